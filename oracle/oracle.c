@@ -1,0 +1,613 @@
+/*
+ * Block-scale quantiser oracle: a plain, slow, obviously correct CPU model of
+ * the hot path (hdiag -> scale choice -> encode -> dequantize -> errors).
+ *
+ * TEST INFRASTRUCTURE ONLY.  The test-suite, the smoke check and the CPU
+ * baseline of the benchmark are the only callers.  It shares no source, header,
+ * table or constant with the GPU library; each side derives its own tables.
+ *
+ * What each part follows (page, then section / table / equation):
+ *   - number formats: LLM-FP4 summary page, "Floating-Point Quantization
+ *     Mechanics" (value of an EeMm code, Q_max); qwantize "Results" page,
+ *     "Exotic Scales" (E4M3 has 126 positive values, the E2M1 codebook);
+ *     "Is Finer Better?" §2.1 (E8M0 power-of-two scales, UE4M3 for NVFP4).
+ *   - element rounding: quantisation-algorithms note, §2 (sorted FP32 codepoint
+ *     table + binary search for the two neighbouring codepoints), rounded to
+ *     nearest with ties to the even code, saturating at the largest code.
+ *   - Naive scale: "Is Finer Better?" §2.1 (s = Q_scale(x_max / C),
+ *     q = Q_elem(x / s), x^ = s q), App. F.3 (the zero-scale bin); qwantize
+ *     "Results", "INT8 (FP8 E4M3 scales)" (amax stored as E4M3, effective scale
+ *     amax_fp8 / 127 divided in float32).
+ *   - SSE-Optimal / H-Optimal: qwantize "Results", INT8 / NVFP4 / MXFP4 tables
+ *     and "Why NVFP4 benefits much more from Hessian-awareness"; the weighted
+ *     objective sum_j h_j (w_j - s Q(w_j / s))^2 with h_j the diagonal of X^T X
+ *     is the diagonal form in the quantisation-algorithms note, §1.  The oracle
+ *     takes the plain definition: the exact argmin over every candidate of the
+ *     scale grid, objective in float64 summed in element order, the first
+ *     (lowest) code on ties.
+ *   - metrics: qwantize "Results", the weight-error and output-error
+ *     definitions at the top of the page.
+ *
+ * Readings where the pages are silent (also listed in the design notes):
+ *   E8M0 Naive snap = nearest power of two in the linear domain, ties upward
+ *   (parity unpinned beyond self-consistency); negative inputs that round to
+ *   zero keep their sign bit in E2M1/E4M3 codes (a convention, parity
+ *   unpinned); E2M1 codes pack element 2i in the low nibble (a convention).
+ *
+ * Build: -O2 -ffp-contract=off, no fast-math, so every float expression below
+ * is one IEEE binary32 operation rounded to nearest-even (fl32).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORC_OK 0
+#define ORC_EINVAL (-1)
+#define ORC_ENOMEM (-2)
+
+/* format ids (same numbering as the public library, kept independently) */
+enum { F_INT8_E4M3 = 0, F_NVFP4 = 1, F_MXFP4 = 2, F_MXFP8 = 3, F_FP8_E4M3S = 4, F_COUNT = 5 };
+enum { M_NAIVE = 0, M_SSE = 1, M_H = 2 };
+enum { DT_F32 = 0, DT_BF16 = 1 };
+
+/* element kinds */
+enum { E_INT8 = 0, E_E2M1 = 1, E_E4M3 = 2 };
+/* scale kinds */
+enum { S_E4M3_OF_AMAX_DIV127 = 0, S_E4M3 = 1, S_E8M0 = 2 };
+
+/* ------------------------------------------------------------------------ */
+/* Number formats                                                            */
+/* ------------------------------------------------------------------------ */
+
+/* Non-negative values of a sign-magnitude binary float format EeMm with
+ * exponent bias `bias`, in increasing bit-pattern order (code k = p*2^m + d).
+ * Exponent field p >= 1 gives 2^(p-bias) * (1 + d/2^m); p = 0 gives the
+ * subnormals 2^(1-bias) * (d/2^m).  reserve = 0: every code is finite;
+ * 1: only the all-ones pattern is NaN (OCP E4M3FN); 2: the whole top exponent
+ * is Inf/NaN (IEEE style).  Returns the count, or ORC_EINVAL if cap is short. */
+int orc_fp_table(int ebits, int mbits, int bias, int reserve, double *out, int cap)
+{
+    int np = 1 << ebits, nd = 1 << mbits, n = 0;
+    for (int p = 0; p < np; p++) {
+        if (reserve == 2 && p == np - 1)
+            break;
+        for (int d = 0; d < nd; d++) {
+            if (reserve == 1 && p == np - 1 && d == nd - 1)
+                break;
+            double frac = (double)d / (double)nd;
+            double v = (p == 0) ? ldexp(frac, 1 - bias) : ldexp(1.0 + frac, p - bias);
+            if (n >= cap)
+                return ORC_EINVAL;
+            out[n++] = v;
+        }
+    }
+    return n;
+}
+
+/* E8M0: 255 finite codes c = 0..254 with value 2^(c-127); 0xFF is NaN. */
+int orc_e8m0_table(double *out, int cap)
+{
+    if (cap < 255)
+        return ORC_EINVAL;
+    for (int c = 0; c < 255; c++)
+        out[c] = ldexp(1.0, c - 127);
+    return 255;
+}
+
+static double T_E2M1[8];
+static double T_E4M3[127];
+static double T_INT8[128];
+static int tables_ready = 0;
+
+static void init_tables(void)
+{
+    if (tables_ready)
+        return;
+    orc_fp_table(2, 1, 1, 0, T_E2M1, 8);    /* {0,.5,1,1.5,2,3,4,6} */
+    orc_fp_table(4, 3, 7, 1, T_E4M3, 127);  /* 0 .. 448, 0x7F is NaN */
+    for (int i = 0; i < 128; i++)
+        T_INT8[i] = (double)i;              /* symmetric INT8 magnitudes */
+    tables_ready = 1;
+}
+
+/* Round a >= 0 onto the sorted table T[0..n-1] (T[0] = 0): saturate at the
+ * top; otherwise take the nearer of T[i] <= a < T[i+1], an exact tie going to
+ * the even index.  The differences are exact in float64 for these tables. */
+int orc_rne_index(const double *T, int n, double a)
+{
+    if (!(a < T[n - 1]))
+        return n - 1;
+    int lo = 0, hi = n - 1; /* T[lo] <= a < T[hi] */
+    while (hi - lo > 1) {
+        int mid = lo + (hi - lo) / 2;
+        if (T[mid] <= a)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    double dl = a - T[lo], dh = T[hi] - a;
+    if (dl < dh)
+        return lo;
+    if (dh < dl)
+        return hi;
+    return (lo % 2 == 0) ? lo : hi;
+}
+
+void orc_rne_index_batch(const double *T, int n, const float *x, int64_t count, int32_t *idx)
+{
+    for (int64_t i = 0; i < count; i++)
+        idx[i] = orc_rne_index(T, n, (double)x[i]);
+}
+
+static int elem_kind(int fmt)
+{
+    switch (fmt) {
+    case F_INT8_E4M3: return E_INT8;
+    case F_NVFP4: case F_MXFP4: return E_E2M1;
+    default: return E_E4M3;
+    }
+}
+
+static int scale_kind(int fmt)
+{
+    switch (fmt) {
+    case F_INT8_E4M3: return S_E4M3_OF_AMAX_DIV127;
+    case F_NVFP4: case F_FP8_E4M3S: return S_E4M3;
+    default: return S_E8M0;
+    }
+}
+
+static const double *elem_table(int fmt, int *n)
+{
+    switch (elem_kind(fmt)) {
+    case E_INT8: *n = 128; return T_INT8;
+    case E_E2M1: *n = 8; return T_E2M1;
+    default: *n = 127; return T_E4M3;
+    }
+}
+
+/* Candidate scale codes of the search, ascending: the 126 positive E4M3 codes
+ * 0x01..0x7E, or all 255 finite E8M0 codes. */
+int orc_candidates(int fmt, int *first, int *last)
+{
+    init_tables();
+    if (fmt < 0 || fmt >= F_COUNT)
+        return ORC_EINVAL;
+    if (scale_kind(fmt) == S_E8M0) {
+        *first = 0;
+        *last = 254;
+    } else {
+        *first = 1;
+        *last = 126;
+    }
+    return *last - *first + 1;
+}
+
+/* The fp32 scale a scale code stands for.  INT8: fl32(val_E4M3(code) / 127);
+ * E4M3 grids: val_E4M3(code) (code 0 is the zero scale); E8M0: 2^(code-127)
+ * (2^-127 is an fp32 subnormal and exact).  Returns NAN for a NaN code. */
+float orc_scale_value(int fmt, int code)
+{
+    init_tables();
+    switch (scale_kind(fmt)) {
+    case S_E4M3_OF_AMAX_DIV127:
+        if (code < 0 || code > 126) return NAN;
+        return (float)T_E4M3[code] / 127.0f;
+    case S_E4M3:
+        if (code < 0 || code > 126) return NAN;
+        return (float)T_E4M3[code];
+    default:
+        if (code < 0 || code > 254) return NAN;
+        return (float)ldexp(1.0, code - 127);
+    }
+}
+
+/* Naive scale code of a block with max |w| = amax. */
+int orc_naive_scale_code(int fmt, float amax)
+{
+    init_tables();
+    int sk = scale_kind(fmt);
+    if (sk == S_E4M3_OF_AMAX_DIV127)
+        return orc_rne_index(T_E4M3, 127, (double)amax); /* amax itself, saturating at 448 */
+    float C = (elem_kind(fmt) == E_E2M1) ? 6.0f : 448.0f; /* largest element magnitude */
+    float v = amax / C;                                   /* fl32 */
+    if (sk == S_E4M3)
+        return orc_rne_index(T_E4M3, 127, (double)v);
+    /* E8M0: nearest power of two in the linear domain, ties upward */
+    if (v == 0.0f)
+        return 0;
+    int e;
+    double f = frexp((double)v, &e); /* v = f * 2^e, f in [0.5, 1) */
+    int E = e - 1;                   /* v = (2f) * 2^E, 2f in [1, 2) */
+    if (2.0 * f >= 1.5)
+        E += 1;
+    if (E < -127)
+        E = -127;
+    if (E > 127)
+        E = 127;
+    return E + 127;
+}
+
+/* Encode one element with scale s; returns the code byte (INT8 two's
+ * complement, E2M1 sign<<3 | index, E4M3 sign<<7 | index) and writes the
+ * dequantised value fl32(s * val(q)) with the element's sign. */
+static int enc_elem(int fmt, float s, float w, float *wq)
+{
+    int n;
+    const double *T = elem_table(fmt, &n);
+    int neg = signbit(w) != 0;
+    float a = fabsf(w);
+    int idx = 0;
+    if (s != 0.0f) {
+        float x = a / s; /* fl32 IEEE division (may overflow to +inf: saturates) */
+        idx = orc_rne_index(T, n, (double)x);
+    }
+    float mag = s * (float)T[idx]; /* fl32 */
+    *wq = neg ? -mag : mag;
+    switch (elem_kind(fmt)) {
+    case E_INT8: return (uint8_t)(int8_t)(neg ? -idx : idx);
+    case E_E2M1: return (neg << 3) | idx;
+    default: return (neg << 7) | idx;
+    }
+}
+
+/* Decode one element code to (sign, index); -1 for an invalid code. */
+static int dec_elem(int fmt, int code, int *neg)
+{
+    switch (elem_kind(fmt)) {
+    case E_INT8: {
+        int v = (int8_t)(uint8_t)code;
+        if (v == -128) return -1;
+        *neg = v < 0;
+        return v < 0 ? -v : v;
+    }
+    case E_E2M1:
+        *neg = (code >> 3) & 1;
+        return code & 7;
+    default:
+        *neg = (code >> 7) & 1;
+        if ((code & 0x7F) == 0x7F) return -1;
+        return code & 0x7F;
+    }
+}
+
+/* Objective of one block at scale s: sum_j om_j (w_j - wq_j)^2 in float64,
+ * j ascending (om == NULL means every om_j = 1). */
+static double block_objective(int fmt, float s, const float *w, const double *om, int B)
+{
+    double obj = 0.0;
+    for (int j = 0; j < B; j++) {
+        float wq;
+        enc_elem(fmt, s, w[j], &wq);
+        double d = (double)w[j] - (double)wq;
+        obj += (om ? om[j] : 1.0) * (d * d);
+    }
+    return obj;
+}
+
+static float widen(const void *p, int dt, int64_t i)
+{
+    if (dt == DT_F32)
+        return ((const float *)p)[i];
+    uint32_t u = (uint32_t)((const uint16_t *)p)[i] << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+static int set_threads(int nthreads)
+{
+#ifdef _OPENMP
+    return nthreads > 0 ? nthreads : omp_get_max_threads();
+#else
+    (void)nthreads;
+    return 1;
+#endif
+}
+
+int orc_max_threads(void) { return set_threads(0); }
+
+/* Every candidate's objective for one block (for brute-force checks).
+ * obj_out / code_out hold orc_candidates() entries. */
+int orc_block_all_objectives(int fmt, int B, const float *w, const float *h, double *obj_out,
+                             int32_t *code_out)
+{
+    init_tables();
+    int c0, c1;
+    if (orc_candidates(fmt, &c0, &c1) < 0 || B <= 0)
+        return ORC_EINVAL;
+    double *om = NULL;
+    if (h) {
+        om = (double *)malloc(sizeof(double) * (size_t)B);
+        if (!om) return ORC_ENOMEM;
+        for (int j = 0; j < B; j++) om[j] = (double)h[j];
+    }
+    for (int c = c0; c <= c1; c++) {
+        obj_out[c - c0] = block_objective(fmt, orc_scale_value(fmt, c), w, om, B);
+        code_out[c - c0] = c;
+    }
+    free(om);
+    return c1 - c0 + 1;
+}
+
+static int check_common(int fmt, int B, int64_t N, int64_t K)
+{
+    if (fmt < 0 || fmt >= F_COUNT || B <= 0 || N < 0 || K < 0 || (K > 0 && K % B != 0))
+        return ORC_EINVAL;
+    if (elem_kind(fmt) == E_E2M1 && (K % 2) != 0)
+        return ORC_EINVAL;
+    return ORC_OK;
+}
+
+static void put_code(int fmt, uint8_t *codes, int64_t N, int64_t K, int64_t n, int64_t k, int code)
+{
+    (void)N;
+    if (elem_kind(fmt) == E_E2M1) {
+        uint8_t *p = codes + n * (K / 2) + k / 2;
+        if (k % 2 == 0)
+            *p = (uint8_t)((*p & 0xF0) | (code & 0xF));
+        else
+            *p = (uint8_t)((*p & 0x0F) | ((code & 0xF) << 4));
+    } else {
+        codes[n * K + k] = (uint8_t)code;
+    }
+}
+
+static int get_code(int fmt, const uint8_t *codes, int64_t K, int64_t n, int64_t k)
+{
+    if (elem_kind(fmt) == E_E2M1) {
+        uint8_t b = codes[n * (K / 2) + k / 2];
+        return (k % 2 == 0) ? (b & 0xF) : (b >> 4);
+    }
+    return codes[n * K + k];
+}
+
+/* quantize_blocks.  method: Naive / SSE-Optimal / H-Optimal.  scales_in, when
+ * not NULL, fixes every block's scale code (encode only: method is ignored).
+ * h is required for H-Optimal; for Naive and for a fixed scale it only weights
+ * the reported objective.  codes: [N][K] bytes (INT8, E4M3) or [N][K/2]
+ * (E2M1); scales: [N][K/B]; block_obj: [N][K/B] float64 or NULL. */
+int orc_quantize(int method, int fmt, int B, const void *W, int wdt, int64_t N, int64_t K,
+                 const float *h, const uint8_t *scales_in, uint8_t *codes, uint8_t *scales,
+                 double *block_obj, int nthreads)
+{
+    init_tables();
+    if (check_common(fmt, B, N, K) != ORC_OK || (wdt != DT_F32 && wdt != DT_BF16))
+        return ORC_EINVAL;
+    if (!scales_in && method == M_H && !h)
+        return ORC_EINVAL;
+    if (!scales_in && (method < M_NAIVE || method > M_H))
+        return ORC_EINVAL;
+    if (N == 0 || K == 0)
+        return ORC_OK;
+    int c0, c1;
+    orc_candidates(fmt, &c0, &c1);
+    const int64_t nb = K / B;
+    int use_h = h != NULL && (scales_in != NULL || method != M_SSE);
+    double *om_all = NULL;
+    if (use_h) {
+        om_all = (double *)malloc(sizeof(double) * (size_t)K);
+        if (!om_all) return ORC_ENOMEM;
+        for (int64_t k = 0; k < K; k++) om_all[k] = (double)h[k];
+    }
+    int err = ORC_OK;
+    int nt = set_threads(nthreads);
+#pragma omp parallel num_threads(nt)
+    {
+        float *w = (float *)malloc(sizeof(float) * (size_t)B);
+        if (!w) {
+#pragma omp atomic write
+            err = ORC_ENOMEM;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t n = 0; n < N; n++) {
+            if (!w) continue;
+            for (int64_t b = 0; b < nb; b++) {
+                const double *om = use_h ? om_all + b * B : NULL;
+                float amax = 0.0f;
+                for (int j = 0; j < B; j++) {
+                    w[j] = widen(W, wdt, n * K + b * B + j);
+                    float a = fabsf(w[j]);
+                    if (a > amax) amax = a;
+                }
+                int code;
+                double best;
+                if (scales_in) {
+                    code = scales_in[n * nb + b];
+                    float s = orc_scale_value(fmt, code);
+                    if (isnan(s)) {
+#pragma omp atomic write
+                        err = ORC_EINVAL;
+                        continue;
+                    }
+                    best = block_objective(fmt, s, w, om, B);
+                } else if (method == M_NAIVE) {
+                    code = orc_naive_scale_code(fmt, amax);
+                    best = block_objective(fmt, orc_scale_value(fmt, code), w, om, B);
+                } else {
+                    code = c0;
+                    best = block_objective(fmt, orc_scale_value(fmt, c0), w, om, B);
+                    for (int c = c0 + 1; c <= c1; c++) {
+                        double o = block_objective(fmt, orc_scale_value(fmt, c), w, om, B);
+                        if (o < best) {
+                            best = o;
+                            code = c;
+                        }
+                    }
+                }
+                float s = orc_scale_value(fmt, code);
+                if (scales) scales[n * nb + b] = (uint8_t)code;
+                if (block_obj) block_obj[n * nb + b] = best;
+                if (codes) {
+                    for (int j = 0; j < B; j++) {
+                        float wq;
+                        int cb = enc_elem(fmt, s, w[j], &wq);
+                        put_code(fmt, codes, N, K, n, b * B + j, cb);
+                    }
+                }
+            }
+        }
+        free(w);
+    }
+    free(om_all);
+    return err;
+}
+
+/* dequantize: Wq[n][k] = sign * fl32(s_block * val(index)) as float32. */
+int orc_dequantize(int fmt, int B, const uint8_t *codes, const uint8_t *scales, int64_t N, int64_t K,
+                   float *out, int nthreads)
+{
+    init_tables();
+    if (check_common(fmt, B, N, K) != ORC_OK)
+        return ORC_EINVAL;
+    int n_t;
+    const double *T = elem_table(fmt, &n_t);
+    const int64_t nb = K / B;
+    int err = ORC_OK;
+    int nt = set_threads(nthreads);
+#pragma omp parallel for num_threads(nt) schedule(static)
+    for (int64_t n = 0; n < N; n++) {
+        for (int64_t k = 0; k < K; k++) {
+            float s = orc_scale_value(fmt, scales[n * nb + k / B]);
+            int neg = 0;
+            int idx = dec_elem(fmt, get_code(fmt, codes, K, n, k), &neg);
+            if (isnan(s) || idx < 0) {
+#pragma omp atomic write
+                err = ORC_EINVAL;
+                continue;
+            }
+            float mag = s * (float)T[idx];
+            out[n * K + k] = neg ? -mag : mag;
+        }
+    }
+    return err;
+}
+
+/* Per-block objective of W at the given scale codes (om = h, or 1 if NULL). */
+int orc_objectives_at(int fmt, int B, const void *W, int wdt, int64_t N, int64_t K, const float *h,
+                      const uint8_t *scales_in, double *obj_out, int nthreads)
+{
+    return orc_quantize(M_NAIVE, fmt, B, W, wdt, N, K, h, scales_in, NULL, NULL, obj_out, nthreads);
+}
+
+/* hdiag: h_j = sum_t x_tj^2, summed in float64 in row order, stored as fp32. */
+int orc_hdiag(const void *X, int xdt, int64_t M, int64_t K, float *h, int nthreads)
+{
+    if (M < 0 || K < 0 || (xdt != DT_F32 && xdt != DT_BF16))
+        return ORC_EINVAL;
+    double *acc = (double *)calloc((size_t)(K ? K : 1), sizeof(double));
+    if (!acc) return ORC_ENOMEM;
+    int nt = set_threads(nthreads);
+    const int64_t chunk = 64;
+    const int64_t nchunks = (K + chunk - 1) / chunk;
+#pragma omp parallel for num_threads(nt) schedule(dynamic, 1)
+    for (int64_t c = 0; c < nchunks; c++) {
+        int64_t j0 = c * chunk, j1 = j0 + chunk < K ? j0 + chunk : K;
+        for (int64_t t = 0; t < M; t++)
+            for (int64_t j = j0; j < j1; j++) {
+                double x = (double)widen(X, xdt, t * K + j);
+                acc[j] += x * x;
+            }
+    }
+    for (int64_t j = 0; j < K; j++)
+        h[j] = (float)acc[j];
+    free(acc);
+    return ORC_OK;
+}
+
+/* Weight error ||Wq - W||_F / ||W||_F in float64 (row partials summed in row
+ * order).  Also returns the two sums of squares when the pointers are set. */
+double orc_weight_error(const void *W, int wdt, const void *Wq, int qdt, int64_t N, int64_t K,
+                        double *num_out, double *den_out, int nthreads)
+{
+    double *rn = (double *)calloc((size_t)(N ? N : 1), sizeof(double));
+    double *rd = (double *)calloc((size_t)(N ? N : 1), sizeof(double));
+    if (!rn || !rd) {
+        free(rn);
+        free(rd);
+        return NAN;
+    }
+    int nt = set_threads(nthreads);
+#pragma omp parallel for num_threads(nt) schedule(static)
+    for (int64_t n = 0; n < N; n++) {
+        double a = 0.0, b = 0.0;
+        for (int64_t k = 0; k < K; k++) {
+            double w = (double)widen(W, wdt, n * K + k);
+            double q = (double)widen(Wq, qdt, n * K + k);
+            a += (q - w) * (q - w);
+            b += w * w;
+        }
+        rn[n] = a;
+        rd[n] = b;
+    }
+    double num = 0.0, den = 0.0;
+    for (int64_t n = 0; n < N; n++) {
+        num += rn[n];
+        den += rd[n];
+    }
+    free(rn);
+    free(rd);
+    if (num_out) *num_out = num;
+    if (den_out) *den_out = den;
+    return sqrt(num) / sqrt(den);
+}
+
+/* Output error ||X Wq^T - X W^T||_F / ||X W^T||_F in float64:
+ * Y = X W^T and D = X (Wq - W)^T from the exact inputs, every dot product
+ * summed in k order, squares summed per row of X and then in row order. */
+double orc_output_error(const void *X, int xdt, int64_t M, const void *W, int wdt, const void *Wq,
+                        int qdt, int64_t N, int64_t K, double *dsq_out, double *ysq_out, int nthreads)
+{
+    const size_t nk = (size_t)(N * K) + 1;
+    double *Wd = (double *)malloc(sizeof(double) * nk);
+    double *Dd = (double *)malloc(sizeof(double) * nk);
+    double *rd = (double *)calloc((size_t)(M ? M : 1), sizeof(double));
+    double *ry = (double *)calloc((size_t)(M ? M : 1), sizeof(double));
+    if (!Wd || !Dd || !rd || !ry) {
+        free(Wd); free(Dd); free(rd); free(ry);
+        return NAN;
+    }
+    for (int64_t i = 0; i < N * K; i++) {
+        double w = (double)widen(W, wdt, i);
+        Wd[i] = w;
+        Dd[i] = (double)widen(Wq, qdt, i) - w;
+    }
+    int nt = set_threads(nthreads);
+#pragma omp parallel num_threads(nt)
+    {
+        double *x = (double *)malloc(sizeof(double) * (size_t)(K ? K : 1));
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t t = 0; t < M; t++) {
+            if (!x) continue;
+            for (int64_t k = 0; k < K; k++)
+                x[k] = (double)widen(X, xdt, t * K + k);
+            double sd = 0.0, sy = 0.0;
+            for (int64_t n = 0; n < N; n++) {
+                const double *wr = Wd + n * K, *dr = Dd + n * K;
+                double y = 0.0, d = 0.0;
+                for (int64_t k = 0; k < K; k++) {
+                    y += x[k] * wr[k];
+                    d += x[k] * dr[k];
+                }
+                sy += y * y;
+                sd += d * d;
+            }
+            rd[t] = sd;
+            ry[t] = sy;
+        }
+        free(x);
+    }
+    double dsq = 0.0, ysq = 0.0;
+    for (int64_t t = 0; t < M; t++) {
+        dsq += rd[t];
+        ysq += ry[t];
+    }
+    free(Wd); free(Dd); free(rd); free(ry);
+    if (dsq_out) *dsq_out = dsq;
+    if (ysq_out) *ysq_out = ysq;
+    return sqrt(dsq) / sqrt(ysq);
+}
