@@ -1,0 +1,237 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-scale quantiser hot path on one MI355X.
+
+Workload (one "step"): the INT8 / E4M3-scale case on the qwantize "Results"
+page's layer shape -- W 2560 x 9728 bf16 (a seeded Student-t(4) x 0.02 stand-in
+with per-row lognormal gain for the down_proj weight) and calibration X
+16384 x 9728 bf16 (N(0,1), 8 outlier channels x 50):
+    hdiag(X), then for B in {32, 64, 128, 256} and each of Naive, SSE-Optimal,
+    H-Optimal: quantize_blocks (scale choice + encode), dequantize, weight
+    error and output error.
+value = 12 quantisations x 2560 x 9728 weights / step time, in Gweights/s.
+Inputs are resident in HBM before timing starts.  Per-call GPU times come from
+HIP events recorded on the stream the kernels run on, over the timed steps.
+
+Prints one JSON line (the metric, per-stage figures, the roofline of the
+dominant kernel and the CPU oracle timed on a bounded sample).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Gweights/s for SSE/H-Optimal block-scale search; % of VALU & HBM peak"
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+# 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz: VALU lane-operations per second
+# without packed FP32 (which this build does not use).
+VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+# counting convention for the search: VALU lane-ops per (weight, candidate)
+SEARCH_OPS = {"sse": 6, "h": 7}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-rows", type=int, default=8, help="rows of W in the CPU sample")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the work shards by rows "
+              "of W and X; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import block_scaled_precision_hdiag_amd as hd
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    hd.lib()
+
+    cfg = synth.CONFIGS[2]
+    W_cpu, X_cpu = synth.config_inputs(2)
+    N, K = W_cpu.shape
+    M = X_cpu.shape[0]
+    W = W_cpu.to(dev)
+    X = X_cpu.to(dev)
+    fmt = hd.INT8_E4M3
+    blocks = cfg["blocks"]
+    methods = [("naive", hd.NAIVE), ("sse", hd.SSE_OPT), ("h", hd.H_OPT)]
+    n_cand = hd.hdiag_format_info(fmt, 32)[2]
+
+    # outputs and workspaces, allocated once outside the timed region
+    h = torch.empty(K, dtype=torch.float32, device=dev)
+    ws_h = torch.empty(hd.hdiag_workspace_size(M, K), dtype=torch.uint8, device=dev)
+    ws_w = torch.empty(hd.lib().weight_error_workspace_size(N, K), dtype=torch.uint8, device=dev)
+    ws_o = torch.empty(hd.output_error_workspace_size(M, N, K), dtype=torch.uint8, device=dev)
+    codes = {B: torch.empty((N, K), dtype=torch.uint8, device=dev) for B in blocks}
+    scales = {B: torch.empty((N, K // B), dtype=torch.uint8, device=dev) for B in blocks}
+    Wq = torch.empty((N, K), dtype=torch.float32, device=dev)
+    werr = torch.empty((len(blocks), 3), dtype=torch.float64, device=dev)
+    oerr = torch.empty((len(blocks), 3), dtype=torch.float64, device=dev)
+
+    events = []  # (stage, B, start, end) during timed steps
+
+    def timed(stage, B, fn, rec):
+        if rec:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            events.append((stage, B, a, b))
+        else:
+            fn()
+
+    def step(rec):
+        timed("hdiag", 0, lambda: hd.hdiag(X, out=h, workspace=ws_h), rec)
+        for bi, B in enumerate(blocks):
+            for mi, (mname, m) in enumerate(methods):
+                stage = "naive" if m == hd.NAIVE else "search_" + mname
+                timed(stage, B, lambda: hd.quantize_blocks(m, fmt, B, W, h=h, codes=codes[B], scales=scales[B]),
+                      rec)
+                timed("dequantize", B, lambda: hd.dequantize(fmt, B, codes[B], scales[B], N, K, out=Wq), rec)
+                timed("weight_error", B, lambda: werr[bi, mi].copy_(hd.weight_error(W, Wq, workspace=ws_w)[0]),
+                      rec)
+                timed("output_error", B, lambda: oerr[bi, mi].copy_(hd.output_error(X, W, Wq, workspace=ws_o)[0]),
+                      rec)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    value = len(blocks) * len(methods) * N * K / (ms_per_step * 1e-3) / 1e9
+
+    # per-stage GPU times (ms per launch), from the events
+    stage_ms = {}
+    for stage, B, a, b in events:
+        stage_ms.setdefault(stage, []).append(a.elapsed_time(b))
+    per_step = {s: sum(v) / args.steps for s, v in stage_ms.items()}
+    avg = {s: sum(v) / len(v) for s, v in stage_ms.items()}
+
+    # algorithmic work per launch of each stage
+    bytes_w = N * K * 2
+    work = {
+        "hdiag": ("hbm", M * K * 2 + K * 4),
+        "naive": ("hbm", sum(bytes_w + N * K + N * K // B for B in blocks) / len(blocks)),
+        "dequantize": ("hbm", sum(N * K + N * K // B + N * K * 4 for B in blocks) / len(blocks)),
+        "weight_error": ("hbm", bytes_w + N * K * 4),
+        "output_error": ("mfma", 4.0 * M * N * K),
+        "search_sse": ("alu", N * K * n_cand * SEARCH_OPS["sse"]),
+        "search_h": ("alu", N * K * n_cand * SEARCH_OPS["h"]),
+    }
+
+    def roof(stage):
+        bound, units = work[stage]
+        t = avg[stage] * 1e-3
+        if bound == "hbm":
+            ach, peak, unit = units / t / 1e9, HBM_PEAK_GBS, "GB/s"
+        elif bound == "mfma":
+            ach, peak, unit = units / t / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
+        else:
+            ach, peak, unit = units / t / 1e12, VALU_PEAK_TOPS, "Tops/s"
+        return {"bound": bound, "achieved": round(ach, 3), "peak": round(peak, 3), "unit": unit,
+                "frac": round(ach / peak, 4), "avg_ms": round(avg[stage], 4)}
+
+    stages = {s: roof(s) for s in avg}
+    dominant = max(per_step, key=per_step.get)
+    roofline = dict(stages[dominant])
+    roofline["kernel"] = dominant
+    roofline["traffic"] = None
+    roofline.pop("avg_ms")
+
+    search_gwps = {s: round(N * K / (avg[s] * 1e-3) / 1e9, 3) for s in avg if s.startswith("search") or s == "naive"}
+
+    errs = {}
+    we, oe = werr.cpu().numpy(), oerr.cpu().numpy()
+    for bi, B in enumerate(blocks):
+        for mi, (mname, _) in enumerate(methods):
+            errs["B%d_%s" % (B, mname)] = {"weight_error": round(float(we[bi, mi]), 6),
+                                           "output_error": round(float(oe[bi, mi]), 6)}
+
+    out = {
+        "metric": METRIC, "value": round(value, 3), "unit": "Gweights/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "INT8 (E4M3 scales) on W 2560x9728 bf16, h from X 16384x9728 bf16; "
+                               "B in {32,64,128,256}; Naive + SSE-Optimal + H-Optimal; hdiag, quantize, "
+                               "dequantize, weight and output error per step",
+                   "W": [N, K], "X": [M, K], "format": "INT8_E4M3", "blocks": blocks,
+                   "quantizations_per_step": len(blocks) * len(methods)},
+        "roofline": roofline,
+        "stages_ms_per_step": {s: round(v, 4) for s, v in per_step.items()},
+        "stages": stages,
+        "kernel_gweights_per_s": search_gwps,
+        "errors": errs,
+    }
+
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(W_cpu, X_cpu, blocks, methods, fmt, args.cpu_rows, value)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(W_cpu, X_cpu, blocks, methods, fmt, rows, gpu_value):
+    """The CPU oracle on a bounded sample of the same step, extrapolated stage
+    by stage to the full workload (blocks are independent, so each stage's
+    time is linear in the rows it covers)."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    N, K = W_cpu.shape
+    M = X_cpu.shape[0]
+    nt = oracle.max_threads()
+    Wb = synth.bits(W_cpu)
+    Xb = synth.bits(X_cpu)
+    xr_h = 2048          # rows of X for hdiag
+    xr_o = 4             # rows of X for the output error
+    Ws = Wb[:rows]
+    t = time.perf_counter()
+    h = oracle.hdiag(Xb[:xr_h])
+    t_hdiag = (time.perf_counter() - t) * (M / xr_h)
+    h_full = h  # the sample's h weights the sample's search; the cost does not depend on its values
+    total = t_hdiag
+    for B in blocks:
+        for _, m in methods:
+            t = time.perf_counter()
+            c, s, _ = oracle.quantize(m, fmt, B, Ws, h=h_full if m == oracle.H_OPT else None)
+            t_q = time.perf_counter() - t
+            t = time.perf_counter()
+            Wq = oracle.dequantize(fmt, B, c, s, rows, K)
+            oracle.weight_error(Ws, Wq)
+            t_d = time.perf_counter() - t
+            t = time.perf_counter()
+            oracle.output_error(Xb[:xr_o], Ws, Wq)
+            t_o = time.perf_counter() - t
+            total += (t_q + t_d) * (N / rows) + t_o * (M / xr_o) * (N / rows)
+    value = len(blocks) * len(methods) * N * K / total / 1e9
+    return {"value": value, "unit": "Gweights/s", "cores": nt, "kind": "oracle",
+            "sample": "oracle (C, fp64, OpenMP %d threads) on W rows 0..%d, X rows 0..%d for hdiag and 0..%d "
+                      "for the output error, every stage of the step, extrapolated linearly to the full "
+                      "2560x9728 / 16384-row workload: %.1f s per step" % (nt, rows - 1, xr_h - 1, xr_o - 1, total),
+            "gpu_over_cpu": gpu_value / value}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,202 @@
+"""MI355X (gfx950) block-scale quantiser: a thin Python binding of libhdiag.so.
+
+Every function here only marshals arguments (device pointers of torch tensors,
+sizes, the current HIP stream) to the C ABI declared in ``include/hdiag.h``;
+all arithmetic runs in the library's HIP kernels.  torch supplies device memory
+and streams.  If the library has not been built the binding raises instead of
+computing anything some other way: build it with
+``python block_scaled_precision_hdiag_amd/build.py`` (or ``__graft_entry__.build()``).
+
+Names follow the C ABI: ``hdiag``, ``quantize_blocks``, ``encode_blocks``,
+``dequantize``, ``weight_error``, ``output_error``, ``hdiag_format_info``.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhdiag.so")
+
+# enums of include/hdiag.h
+HD_OK, HD_ERR_INVALID_ARG, HD_ERR_UNSUPPORTED, HD_ERR_HIP = 0, -1, -2, -3
+HD_F32, HD_BF16 = 0, 1
+NAIVE, SSE_OPT, H_OPT = 0, 1, 2
+INT8_E4M3, NVFP4, MXFP4, MXFP8, FP8_E4M3S = 0, 1, 2, 3, 4
+FORMATS = {"INT8_E4M3": INT8_E4M3, "NVFP4": NVFP4, "MXFP4": MXFP4, "MXFP8": MXFP8, "FP8_E4M3S": FP8_E4M3S}
+METHODS = {"naive": NAIVE, "sse": SSE_OPT, "h": H_OPT}
+
+EXPORTS = ["hdiag", "hdiag_workspace_size", "quantize_blocks", "encode_blocks", "dequantize",
+           "weight_error", "weight_error_workspace_size", "output_error", "output_error_workspace_size",
+           "hdiag_strerror", "hdiag_last_error", "hdiag_format_info", "hdiag_version"]
+
+
+class HdiagError(RuntimeError):
+    def __init__(self, status, what, detail):
+        super().__init__("%s failed: %s (%d): %s" % (what, _strerror(status), status, detail))
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libhdiag.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libhdiag.so is not built (%s); run block_scaled_precision_hdiag_amd/build.py"
+                               % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+        L.hdiag.argtypes = [P, i32, i64, i64, P, P, sz, P]
+        L.hdiag_workspace_size.argtypes = [i64, i64]
+        L.hdiag_workspace_size.restype = sz
+        L.quantize_blocks.argtypes = [i32, i32, i32, P, i32, i64, i64, P, P, P, P, P]
+        L.encode_blocks.argtypes = [i32, i32, P, i32, i64, i64, P, P, P, P, P]
+        L.dequantize.argtypes = [i32, i32, P, P, i64, i64, P, i32, P]
+        L.weight_error_workspace_size.argtypes = [i64, i64]
+        L.weight_error_workspace_size.restype = sz
+        L.weight_error.argtypes = [P, i32, P, i32, i64, i64, P, P, P, sz, P]
+        L.output_error_workspace_size.argtypes = [i64, i64, i64]
+        L.output_error_workspace_size.restype = sz
+        L.output_error.argtypes = [P, i32, i64, P, i32, P, i32, i64, i64, P, P, P, sz, P]
+        L.hdiag_strerror.argtypes = [i32]
+        L.hdiag_strerror.restype = ctypes.c_char_p
+        L.hdiag_last_error.argtypes = []
+        L.hdiag_last_error.restype = ctypes.c_char_p
+        L.hdiag_format_info.argtypes = [i32, i32, P, P, P, P]
+        L.hdiag_version.argtypes = []
+        L.hdiag_version.restype = ctypes.c_char_p
+        for name in ("hdiag", "quantize_blocks", "encode_blocks", "dequantize", "weight_error",
+                     "output_error", "hdiag_format_info"):
+            getattr(L, name).restype = i32
+        _lib = L
+    return _lib
+
+
+def _strerror(status):
+    return lib().hdiag_strerror(status).decode()
+
+
+def _check(status, what):
+    if status != HD_OK:
+        raise HdiagError(status, what, lib().hdiag_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dt(t):
+    if t.dtype == torch.bfloat16:
+        return HD_BF16
+    if t.dtype == torch.float32:
+        return HD_F32
+    raise TypeError("expected a float32 or bfloat16 tensor, got %s" % t.dtype)
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dev(t):
+    if not t.is_cuda:
+        raise ValueError("tensors must be on a GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.device
+
+
+def codes_shape(fmt, N, K):
+    return (N, K // 2) if fmt in (NVFP4, MXFP4) else (N, K)
+
+
+def hdiag_workspace_size(M, K):
+    return int(lib().hdiag_workspace_size(M, K))
+
+
+def hdiag(X, out=None, workspace=None):
+    """h[j] = sum_t X[t, j]^2 (float32 [K]) for X [M, K] float32 / bfloat16."""
+    d = _dev(X)
+    M, K = X.shape
+    h = out if out is not None else torch.empty(K, dtype=torch.float32, device=d)
+    need = hdiag_workspace_size(M, K)
+    ws = workspace if workspace is not None else torch.empty(max(need, 16), dtype=torch.uint8, device=d)
+    _check(lib().hdiag(_ptr(X), _dt(X), M, K, _ptr(h), _ptr(ws), ws.numel(), _stream(d)), "hdiag")
+    return h
+
+
+def quantize_blocks(method, fmt, B, W, h=None, block_obj=False, codes=None, scales=None):
+    """Scale choice + encode.  Returns (codes uint8, scales uint8 [N, K/B], block_obj or None)."""
+    d = _dev(W)
+    N, K = W.shape
+    codes = codes if codes is not None else torch.empty(codes_shape(fmt, N, K), dtype=torch.uint8, device=d)
+    scales = scales if scales is not None else torch.empty((N, K // B if B else 0), dtype=torch.uint8, device=d)
+    obj = torch.empty((N, K // B if B else 0), dtype=torch.float32, device=d) if block_obj else None
+    _check(lib().quantize_blocks(method, fmt, B, _ptr(W), _dt(W), N, K, _ptr(h), _ptr(codes), _ptr(scales),
+                                 _ptr(obj), _stream(d)), "quantize_blocks")
+    return codes, scales, obj
+
+
+def encode_blocks(fmt, B, W, scales, h=None, block_obj=False):
+    """Encode W with given scale codes.  Returns (codes, block_obj or None)."""
+    d = _dev(W)
+    N, K = W.shape
+    codes = torch.empty(codes_shape(fmt, N, K), dtype=torch.uint8, device=d)
+    obj = torch.empty((N, K // B), dtype=torch.float32, device=d) if block_obj else None
+    _check(lib().encode_blocks(fmt, B, _ptr(W), _dt(W), N, K, _ptr(scales), _ptr(h), _ptr(codes), _ptr(obj),
+                               _stream(d)), "encode_blocks")
+    return codes, obj
+
+
+def dequantize(fmt, B, codes, scales, N, K, dtype=torch.float32, out=None):
+    d = _dev(codes)
+    out = out if out is not None else torch.empty((N, K), dtype=dtype, device=d)
+    _check(lib().dequantize(fmt, B, _ptr(codes), _ptr(scales), N, K, _ptr(out), _dt(out), _stream(d)),
+           "dequantize")
+    return out
+
+
+def weight_error(W, Wq, sums=False, workspace=None):
+    """||Wq - W||_F / ||W||_F as a float64 device tensor of shape [1] (and [2] sums)."""
+    d = _dev(W)
+    N, K = W.shape
+    out = torch.empty(1, dtype=torch.float64, device=d)
+    s = torch.empty(2, dtype=torch.float64, device=d) if sums else None
+    need = int(lib().weight_error_workspace_size(N, K))
+    ws = workspace if workspace is not None else torch.empty(max(need, 16), dtype=torch.uint8, device=d)
+    _check(lib().weight_error(_ptr(W), _dt(W), _ptr(Wq), _dt(Wq), N, K, _ptr(out), _ptr(s), _ptr(ws),
+                              ws.numel(), _stream(d)), "weight_error")
+    return (out, s) if sums else out
+
+
+def output_error_workspace_size(M, N, K):
+    return int(lib().output_error_workspace_size(M, N, K))
+
+
+def output_error(X, W, Wq, sums=False, workspace=None):
+    """||X Wq^T - X W^T||_F / ||X W^T||_F as a float64 device tensor [1] (and [2] sums)."""
+    d = _dev(X)
+    M, K = X.shape
+    N = W.shape[0]
+    out = torch.empty(1, dtype=torch.float64, device=d)
+    s = torch.empty(2, dtype=torch.float64, device=d) if sums else None
+    need = output_error_workspace_size(M, N, K)
+    ws = workspace if workspace is not None else torch.empty(max(need, 16), dtype=torch.uint8, device=d)
+    _check(lib().output_error(_ptr(X), _dt(X), M, _ptr(W), _dt(W), _ptr(Wq), _dt(Wq), N, K, _ptr(out), _ptr(s),
+                              _ptr(ws), ws.numel(), _stream(d)), "output_error")
+    return (out, s) if sums else out
+
+
+def hdiag_format_info(fmt, B):
+    """(elem_bits, scale_bits, n_candidates, bits_per_weight); host-only."""
+    e, s, n = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    bpw = ctypes.c_double()
+    _check(lib().hdiag_format_info(fmt, B, ctypes.byref(e), ctypes.byref(s), ctypes.byref(n),
+                                   ctypes.byref(bpw)), "hdiag_format_info")
+    return e.value, s.value, n.value, bpw.value
+
+
+def version():
+    return lib().hdiag_version().decode()

@@ -1,0 +1,243 @@
+// abi.cpp - the C ABI of libhdiag.so: argument validation, error reporting and
+// dispatch to the kernel launchers.  Nothing here allocates device memory.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <hip/hip_runtime.h>
+
+#include "hdiag.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+hd_status fail(hd_status s, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+hd_status ok()
+{
+    g_last_error[0] = '\0';
+    return HD_OK;
+}
+
+hd_status hip_status(hipError_t e, const char *what)
+{
+    if (e == hipSuccess) return ok();
+    return fail(HD_ERR_HIP, "%s: %s (%s)", what, hipGetErrorName(e), hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+bool valid_dtype(int d) { return d == HD_F32 || d == HD_BF16; }
+bool valid_fmt(int f) { return f >= HD_INT8_E4M3 && f <= HD_FP8_E4M3S; }
+bool valid_block(int32_t B) { return B == 8 || B == 16 || B == 32 || B == 64 || B == 128 || B == 256; }
+bool is_fp4(int f) { return f == HD_NVFP4 || f == HD_MXFP4; }
+
+#define HD_REQUIRE(cond, ...) \
+    do {                      \
+        if (!(cond)) return fail(HD_ERR_INVALID_ARG, __VA_ARGS__); \
+    } while (0)
+
+hd_status check_ptr(const void *p, const char *name, bool needed)
+{
+    if (!needed) return HD_OK;
+    if (p == nullptr) return fail(HD_ERR_INVALID_ARG, "%s is NULL", name);
+    if (!aligned16(p)) return fail(HD_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+    return HD_OK;
+}
+
+#define HD_CHECK_PTR(p, needed)                                       \
+    do {                                                              \
+        hd_status s_ = check_ptr((const void *)(p), #p, (needed));    \
+        if (s_ != HD_OK) return s_;                                   \
+    } while (0)
+
+hd_status check_quant_shape(int fmt, int32_t B, int64_t N, int64_t K)
+{
+    HD_REQUIRE(valid_fmt(fmt), "unknown format %d", fmt);
+    HD_REQUIRE(valid_block(B), "block size %d is not one of 8, 16, 32, 64, 128, 256", (int)B);
+    HD_REQUIRE(N >= 0 && K >= 0, "negative size N=%lld K=%lld", (long long)N, (long long)K);
+    HD_REQUIRE(K % B == 0, "K=%lld is not a multiple of B=%d", (long long)K, (int)B);
+    HD_REQUIRE(N <= (int64_t)1 << 40 && K <= (int64_t)1 << 31, "size too large");
+    HD_REQUIRE(N * K / B <= (int64_t)1 << 40, "size too large");
+    return HD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *hdiag_version(void) { return "hdiag 0.1 (gfx950)"; }
+
+const char *hdiag_strerror(hd_status s)
+{
+    switch (s) {
+    case HD_OK: return "success";
+    case HD_ERR_INVALID_ARG: return "invalid argument";
+    case HD_ERR_UNSUPPORTED: return "unsupported combination";
+    case HD_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char *hdiag_last_error(void) { return g_last_error; }
+
+hd_status hdiag_format_info(hd_format fmt, int32_t B, int *elem_bits, int *scale_bits, int *n_candidates,
+                            double *bits_per_weight)
+{
+    HD_REQUIRE(valid_fmt(fmt), "unknown format %d", (int)fmt);
+    HD_REQUIRE(B > 0, "block size must be positive");
+    const int eb = is_fp4(fmt) ? 4 : 8;
+    const int sb = 8;
+    const int nc = (fmt == HD_MXFP4 || fmt == HD_MXFP8) ? 255 : 126;
+    if (elem_bits) *elem_bits = eb;
+    if (scale_bits) *scale_bits = sb;
+    if (n_candidates) *n_candidates = nc;
+    if (bits_per_weight) *bits_per_weight = (double)eb + (double)sb / (double)B;
+    return ok();
+}
+
+size_t hdiag_workspace_size(int64_t M, int64_t K)
+{
+    if (M < 0 || K <= 0) return 0;
+    return hd::hdiag_ws(M, K);
+}
+
+hd_status hdiag(const void *X, hd_dtype xt, int64_t M, int64_t K, float *h, void *ws, size_t ws_bytes,
+                void *stream)
+{
+    HD_REQUIRE(valid_dtype(xt), "unknown dtype %d", (int)xt);
+    HD_REQUIRE(M >= 0 && K >= 0, "negative size M=%lld K=%lld", (long long)M, (long long)K);
+    if (K == 0) return ok();
+    HD_CHECK_PTR(h, true);
+    HD_CHECK_PTR(X, M > 0);
+    HD_CHECK_PTR(ws, true);
+    const size_t need = hd::hdiag_ws(M, K);
+    HD_REQUIRE(ws_bytes >= need, "workspace of %zu bytes is short of %zu", ws_bytes, need);
+    return hip_status(hd::launch_hdiag(X, xt, M, K, h, ws, (hipStream_t)stream), "hdiag");
+}
+
+hd_status quantize_blocks(hd_method method, hd_format fmt, int32_t B, const void *W, hd_dtype wt, int64_t N,
+                          int64_t K, const float *h, uint8_t *codes, uint8_t *scales, float *block_obj,
+                          void *stream)
+{
+    HD_REQUIRE(method >= HD_NAIVE && method <= HD_H_OPT, "unknown method %d", (int)method);
+    HD_REQUIRE(valid_dtype(wt), "unknown dtype %d", (int)wt);
+    hd_status s = check_quant_shape(fmt, B, N, K);
+    if (s != HD_OK) return s;
+    HD_REQUIRE(method != HD_H_OPT || h != nullptr, "H-Optimal needs h");
+    if (N == 0 || K == 0) return ok();
+    HD_CHECK_PTR(W, true);
+    HD_CHECK_PTR(codes, true);
+    if (scales == nullptr) return fail(HD_ERR_INVALID_ARG, "scales is NULL");
+    if (h != nullptr && !aligned16(h)) return fail(HD_ERR_INVALID_ARG, "h is not 16-byte aligned");
+    if (block_obj != nullptr && ((uintptr_t)block_obj & 3u)) return fail(HD_ERR_INVALID_ARG, "block_obj misaligned");
+    hipStream_t st = (hipStream_t)stream;
+    if (method == HD_NAIVE)
+        return hip_status(hd::launch_encode(fmt, B, W, wt, N, K, h, nullptr, codes, scales, block_obj, st),
+                          "quantize_blocks(naive)");
+    const float *hh = method == HD_H_OPT ? h : nullptr;
+    return hip_status(hd::launch_search(fmt, B, W, wt, N, K, hh, codes, scales, block_obj, st),
+                      "quantize_blocks(search)");
+}
+
+hd_status encode_blocks(hd_format fmt, int32_t B, const void *W, hd_dtype wt, int64_t N, int64_t K,
+                        const uint8_t *scales_in, const float *h, uint8_t *codes, float *block_obj, void *stream)
+{
+    HD_REQUIRE(valid_dtype(wt), "unknown dtype %d", (int)wt);
+    hd_status s = check_quant_shape(fmt, B, N, K);
+    if (s != HD_OK) return s;
+    if (N == 0 || K == 0) return ok();
+    HD_CHECK_PTR(W, true);
+    HD_CHECK_PTR(codes, true);
+    if (scales_in == nullptr) return fail(HD_ERR_INVALID_ARG, "scales_in is NULL");
+    if (h != nullptr && !aligned16(h)) return fail(HD_ERR_INVALID_ARG, "h is not 16-byte aligned");
+    if (block_obj != nullptr && ((uintptr_t)block_obj & 3u)) return fail(HD_ERR_INVALID_ARG, "block_obj misaligned");
+    return hip_status(hd::launch_encode(fmt, B, W, wt, N, K, h, scales_in, codes, nullptr, block_obj,
+                                        (hipStream_t)stream),
+                      "encode_blocks");
+}
+
+hd_status dequantize(hd_format fmt, int32_t B, const uint8_t *codes, const uint8_t *scales, int64_t N, int64_t K,
+                     void *Wq, hd_dtype out_t, void *stream)
+{
+    HD_REQUIRE(valid_dtype(out_t), "unknown dtype %d", (int)out_t);
+    hd_status s = check_quant_shape(fmt, B, N, K);
+    if (s != HD_OK) return s;
+    if (N == 0 || K == 0) return ok();
+    HD_CHECK_PTR(codes, true);
+    HD_CHECK_PTR(Wq, true);
+    if (scales == nullptr) return fail(HD_ERR_INVALID_ARG, "scales is NULL");
+    return hip_status(hd::launch_dequant(fmt, B, codes, scales, N, K, Wq, out_t, (hipStream_t)stream),
+                      "dequantize");
+}
+
+size_t weight_error_workspace_size(int64_t N, int64_t K) { return hd::weight_error_ws(N, K); }
+
+hd_status weight_error(const void *W, hd_dtype wt, const void *Wq, hd_dtype qt, int64_t N, int64_t K, double *out,
+                       double *sums, void *ws, size_t ws_bytes, void *stream)
+{
+    HD_REQUIRE(valid_dtype(wt) && valid_dtype(qt), "unknown dtype");
+    HD_REQUIRE(N >= 0 && K >= 0, "negative size");
+    HD_REQUIRE(K % 8 == 0, "K=%lld must be a multiple of 8", (long long)K);
+    HD_REQUIRE(out != nullptr, "out is NULL");
+    HD_CHECK_PTR(ws, true);
+    HD_REQUIRE(ws_bytes >= hd::weight_error_ws(N, K), "workspace too small");
+    HD_CHECK_PTR(W, N * K > 0);
+    HD_CHECK_PTR(Wq, N * K > 0);
+    return hip_status(hd::launch_weight_error(W, wt, Wq, qt, N, K, out, sums, ws, (hipStream_t)stream),
+                      "weight_error");
+}
+
+size_t output_error_workspace_size(int64_t M, int64_t N, int64_t K)
+{
+    if (M < 0 || N < 0 || K < 0) return 0;
+    // the larger of the two paths, so a caller need not know which one runs
+    const size_t a = hd::output_error_ws(M, N, K, true), b = hd::output_error_ws(M, N, K, false);
+    return a > b ? a : b;
+}
+
+hd_status output_error(const void *X, hd_dtype xt, int64_t M, const void *W, hd_dtype wt, const void *Wq,
+                       hd_dtype qt, int64_t N, int64_t K, double *out, double *sums, void *ws, size_t ws_bytes,
+                       void *stream)
+{
+    HD_REQUIRE(valid_dtype(xt) && valid_dtype(wt) && valid_dtype(qt), "unknown dtype");
+    HD_REQUIRE(M >= 0 && N >= 0 && K >= 0, "negative size");
+    HD_REQUIRE(K % 8 == 0, "K=%lld must be a multiple of 8", (long long)K);
+    HD_REQUIRE(M <= (int64_t)1 << 31 && N <= (int64_t)1 << 31, "size too large");
+    HD_REQUIRE(out != nullptr, "out is NULL");
+    HD_CHECK_PTR(ws, true);
+    const bool mfma = hd::output_error_uses_mfma(xt, wt, K);
+    HD_REQUIRE(ws_bytes >= hd::output_error_ws(M, N, K, mfma), "workspace too small");
+    HD_CHECK_PTR(X, M * K > 0);
+    HD_CHECK_PTR(W, N * K > 0);
+    HD_CHECK_PTR(Wq, N * K > 0);
+    return hip_status(hd::launch_output_error(X, xt, M, W, wt, Wq, qt, N, K, out, sums, ws, (hipStream_t)stream),
+                      "output_error");
+}
+
+}  // extern "C"
+
+namespace hd {
+
+hipError_t launch_search(int fmt, int B, const void *W, int wdt, int64_t N, int64_t K, const float *h,
+                         uint8_t *codes, uint8_t *scales, float *block_obj, hipStream_t st)
+{
+    switch (fmt) {
+    case HD_INT8_E4M3: return launch_search_int8(B, W, wdt, N, K, h, codes, scales, block_obj, st);
+    case HD_NVFP4: return launch_search_nvfp4(B, W, wdt, N, K, h, codes, scales, block_obj, st);
+    case HD_MXFP4: return launch_search_mxfp4(B, W, wdt, N, K, h, codes, scales, block_obj, st);
+    case HD_MXFP8: return launch_search_mxfp8(B, W, wdt, N, K, h, codes, scales, block_obj, st);
+    case HD_FP8_E4M3S: return launch_search_fp8s(B, W, wdt, N, K, h, codes, scales, block_obj, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace hd

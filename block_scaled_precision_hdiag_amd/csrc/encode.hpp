@@ -1,0 +1,48 @@
+// encode.hpp - per-element encode with a known scale, shared by the Naive /
+// encode kernel and the final encode of the search kernel.
+#pragma once
+#include "common.hpp"
+#include "formats.hpp"
+
+namespace hd {
+
+// Encode 8 elements w[0..7] with scale s (s == 0: the zero scale) and
+// r = fl32(1/s).  Writes the code of each element (sign included) and returns
+// the objective sum_j om_j (w_j - fl32(s q_j))^2 of the eight, in float64 and
+// element order (om == NULL: unweighted).
+template <int EK, int SK, bool ONE_STEP>
+__device__ __forceinline__ double encode8(const float *w, float s, float r, const double *om,
+                                          uint32_t *code)
+{
+    double obj = 0.0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const float a = fabsf(w[j]);
+        const float x = (s != 0.0f) ? quotient<SK, ONE_STEP>(a, s, r) : 0.0f;
+        const float y = round_elem<EK>(x);
+        code[j] = elem_code<EK>(elem_index<EK>(y), __builtin_signbitf(w[j]) != 0);
+        const float wq = s * y;  // fl32(s * val(q))
+        const double d = (double)a - (double)wq;
+        obj += (om ? om[j] : 1.0) * (d * d);
+    }
+    return obj;
+}
+
+// Store the 8 codes of elements e0..e0+7 (e0 % 8 == 0).
+template <int EK>
+__device__ __forceinline__ void store_codes8(uint8_t *codes, int64_t e0, const uint32_t *c)
+{
+    if (EK == ELEM_E2M1) {
+        const uint32_t v = (c[0] & 15u) | ((c[1] & 15u) << 4) | ((c[2] & 15u) << 8) | ((c[3] & 15u) << 12) |
+                           ((c[4] & 15u) << 16) | ((c[5] & 15u) << 20) | ((c[6] & 15u) << 24) |
+                           ((c[7] & 15u) << 28);
+        *reinterpret_cast<uint32_t *>(codes + e0 / 2) = v;
+    } else {
+        uint2 v;
+        v.x = (c[0] & 255u) | ((c[1] & 255u) << 8) | ((c[2] & 255u) << 16) | ((c[3] & 255u) << 24);
+        v.y = (c[4] & 255u) | ((c[5] & 255u) << 8) | ((c[6] & 255u) << 16) | ((c[7] & 255u) << 24);
+        *reinterpret_cast<uint2 *>(codes + e0) = v;
+    }
+}
+
+}  // namespace hd

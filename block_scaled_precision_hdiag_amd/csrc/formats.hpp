@@ -1,0 +1,189 @@
+// formats.hpp - number formats, scale grids and exact rounding for the gfx950
+// kernels of libhdiag.so.
+//
+// Element formats: INT8 [-127, 127]; E2M1 {0,.5,1,1.5,2,3,4,6} (qwantize
+// "Results", Exotic Scales); OCP E4M3 (126 positive finite codes, max 448;
+// 0x7F/0xFF NaN).  Scale grids: E4M3 codes 0x01..0x7E; INT8's fl32(E4M3 / 127)
+// (qwantize "Results", INT8 section); E8M0 2^(c-127), c = 0..254 ("Is Finer
+// Better?" §2.1).  Values follow the EeMm formula of the LLM-FP4 summary page
+// ("Floating-Point Quantization Mechanics").
+//
+// Rounding: q = RNE(fl32(|w| / s)) onto the element grid, ties to the even
+// code, saturating.  Every helper here is exact in IEEE binary32 with
+// round-to-nearest-even and preserved denormals (the HIP default on gfx950);
+// the library is built with -ffp-contract=off so no expression is fused behind
+// our back.
+#pragma once
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "hdiag.h"
+
+namespace hd {
+
+enum ElemKind { ELEM_INT8 = 0, ELEM_E2M1 = 1, ELEM_E4M3 = 2 };
+enum ScaleKind { SCALE_INT8 = 0, SCALE_E4M3 = 1, SCALE_E8M0 = 2 };
+
+__host__ __device__ constexpr int elem_kind(int fmt)
+{
+    return fmt == HD_INT8_E4M3 ? ELEM_INT8 : (fmt == HD_NVFP4 || fmt == HD_MXFP4) ? ELEM_E2M1 : ELEM_E4M3;
+}
+__host__ __device__ constexpr int scale_kind(int fmt)
+{
+    return fmt == HD_INT8_E4M3 ? SCALE_INT8 : (fmt == HD_NVFP4 || fmt == HD_FP8_E4M3S) ? SCALE_E4M3 : SCALE_E8M0;
+}
+// First / last search candidate code of a scale grid.
+__host__ __device__ constexpr int cand_first(int sk) { return sk == SCALE_E8M0 ? 0 : 1; }
+__host__ __device__ constexpr int cand_last(int sk) { return sk == SCALE_E8M0 ? 254 : 126; }
+// Largest element magnitude (the C of s = Q_scale(amax / C)).
+__host__ __device__ constexpr float elem_max(int ek)
+{
+    return ek == ELEM_INT8 ? 127.0f : ek == ELEM_E2M1 ? 6.0f : 448.0f;
+}
+
+__host__ __device__ inline float bits_f(uint32_t u)
+{
+    union { uint32_t u; float f; } v;
+    v.u = u;
+    return v.f;
+}
+__host__ __device__ inline uint32_t f_bits(float f)
+{
+    union { uint32_t u; float f; } v;
+    v.f = f;
+    return v.u;
+}
+
+// Magnitude of the E4M3 code c in 0..126 (exact in fp32): exponent field
+// e = c >> 3 and mantissa m = c & 7 give (8 + m) 2^(e - 10), or m 2^-9 when
+// e = 0 (subnormal).  Both cases are m' * 2^-9 * 2^(max(e,1) - 1) with
+// m' = m + 8 [e > 0], built here from bits.
+__host__ __device__ inline float e4m3_value(int c)
+{
+    const int e = c >> 3, m = c & 7;
+    const float mant = (float)(e ? 8 + m : m);           // exact small integer
+    const int pw = (e ? e : 1) - 10;                     // power of two of one mantissa step
+    return mant * bits_f((uint32_t)(127 + pw) << 23);    // exact product
+}
+
+// 2^(c - 127) for c in 0..254; 2^-127 is the fp32 subnormal 0x00400000.
+__host__ __device__ inline float e8m0_value(int c)
+{
+    return c == 0 ? bits_f(0x00400000u) : bits_f((uint32_t)c << 23);
+}
+
+// The fp32 scale of scale code c on grid sk (c = 0 on an E4M3 grid is 0).
+__host__ __device__ inline float scale_value(int sk, int c)
+{
+    if (sk == SCALE_E8M0) return e8m0_value(c);
+    const float v = e4m3_value(c);
+    return sk == SCALE_INT8 ? v / 127.0f : v;  // IEEE division (INT8 section)
+}
+
+// fl32(a / s) for a >= 0, s > 0, given r = fl32(1 / s).
+//  - E8M0 grids: s is a power of two, so a * r is the exactly rounded quotient.
+//  - Otherwise: q0 = fl32(a r) is within two ulps of a/s; one correction
+//    q1 = fl32(q0 + fl32(a - s q0) r) (Markstein's residual step, both FMAs)
+//    lands within one ulp, and a second correction, now with an exact
+//    residual, returns the correctly rounded quotient.  bfloat16 inputs need
+//    only the first correction: checked exhaustively (every bf16 value against
+//    every candidate scale) by the encode parity test, which runs this code.
+//  - a is clamped to 2^100 first: any quotient that large saturates the
+//    element grid for every E4M3-grid scale, and the FMAs stay finite.
+template <int SK, bool ONE_STEP>
+__device__ __forceinline__ float quotient(float a, float s, float r)
+{
+    if (SK == SCALE_E8M0) return a * r;
+    a = fminf(a, 0x1p100f);
+    float q = a * r;
+    float e = __builtin_fmaf(-q, s, a);
+    q = __builtin_fmaf(e, r, q);
+    if (!ONE_STEP) {
+        e = __builtin_fmaf(-q, s, a);
+        q = __builtin_fmaf(e, r, q);
+    }
+    return q;
+}
+
+// Round x >= 0 onto the element grid, saturating; returns the grid VALUE.
+// E2M1 / E4M3: add and subtract C = 2^(e + 23 - mbits) where e is the binade
+// of x floored at the smallest normal; the add rounds x to a multiple of that
+// binade's step with ties to even (the even multiple is the even code).
+template <int EK>
+__device__ __forceinline__ float round_elem(float x)
+{
+    if (EK == ELEM_INT8) return __builtin_rintf(fminf(x, 127.0f));
+    if (EK == ELEM_E2M1) {
+        const float xc = fminf(x, 6.0f);
+        const float C = bits_f((f_bits(fmaxf(xc, 1.0f)) & 0x7F800000u) + (22u << 23));
+        return (xc + C) - C;
+    }
+    const float xc = fminf(x, 448.0f);
+    const float C = bits_f((f_bits(fmaxf(xc, 0x1p-6f)) & 0x7F800000u) + (20u << 23));
+    return (xc + C) - C;
+}
+
+// Element code (magnitude index, no sign) of a grid value y.
+template <int EK>
+__device__ __forceinline__ uint32_t elem_index(float y)
+{
+    if (EK == ELEM_INT8) return (uint32_t)y;
+    if (EK == ELEM_E2M1) {
+        // 0, .5 -> 0, 1 ; 1, 1.5 -> 2, 3 ; 2, 3 -> 4, 5 ; 4, 6 -> 6, 7
+        if (y < 1.0f) return y > 0.0f ? 1u : 0u;
+        const uint32_t u = f_bits(y);
+        return 2u + 2u * ((u >> 23) - 127u) + ((u >> 22) & 1u);
+    }
+    if (y < 0x1p-6f) return (uint32_t)(y * 512.0f);     // subnormal codes 0..7
+    const uint32_t u = f_bits(y);
+    return (((u >> 23) - 120u) << 3) | ((u >> 20) & 7u); // (e + 7) << 3 | mantissa
+}
+
+// Grid value of a magnitude index.
+template <int EK>
+__device__ __forceinline__ float elem_value(uint32_t idx)
+{
+    if (EK == ELEM_INT8) return (float)idx;
+    if (EK == ELEM_E2M1) {
+        // 0 .5 1 1.5 2 3 4 6: (2 + (idx & 1)) * 2^((idx >> 1) - 2), idx 1 is subnormal
+        if (idx < 2) return idx ? 0.5f : 0.0f;
+        return (float)(2 + (idx & 1)) * bits_f((uint32_t)(127 + (int)(idx >> 1) - 2) << 23);
+    }
+    return e4m3_value((int)idx);
+}
+
+// Full code byte (INT8 two's complement / E2M1 nibble / E4M3 byte) of a signed element.
+template <int EK>
+__device__ __forceinline__ uint32_t elem_code(uint32_t idx, bool neg)
+{
+    if (EK == ELEM_INT8) return (uint32_t)(uint8_t)(neg ? -(int)idx : (int)idx);
+    if (EK == ELEM_E2M1) return idx | (neg ? 8u : 0u);
+    return idx | (neg ? 0x80u : 0u);
+}
+
+// Naive scale code of a block with max |w| = amax ("Is Finer Better?" §2.1,
+// s = Q_scale(amax / C) with round-to-nearest scale quantisation; INT8 stores
+// amax itself as E4M3).  E4M3 grids may return code 0 (the zero scale).
+// E8M0: nearest power of two in the linear domain, ties upward, clamped to
+// 2^[-127, 127].
+template <int EK, int SK>
+__device__ __forceinline__ int naive_code(float amax)
+{
+    if (SK == SCALE_INT8 || SK == SCALE_E4M3) {
+        const float v = (SK == SCALE_INT8) ? amax : amax / elem_max(EK);  // IEEE division
+        const float y = round_elem<ELEM_E4M3>(v);
+        return (int)elem_index<ELEM_E4M3>(y);
+    }
+    const float v = amax / elem_max(EK);
+    if (v == 0.0f) return 0;
+    // v = f 2^E with f in [1, 2); frexp gives the exponent for subnormals too
+    int ex;
+    const float f = __builtin_frexpf(v, &ex);   // v = f 2^ex, f in [0.5, 1)
+    int E = ex - 1;
+    if (f >= 0.75f) E += 1;                     // 2f >= 1.5: round up (ties up)
+    E = E < -127 ? -127 : (E > 127 ? 127 : E);
+    return E + 127;
+}
+
+}  // namespace hd

@@ -1,0 +1,139 @@
+// hdiag.hip - h_j = sum_t X[t][j]^2, the diagonal of X^T X that weights the
+// H-Optimal objective (quantisation algorithms note, §1).  HBM-bound column
+// reduction over a row-major X [M, K].
+//
+// Pass 1: the rows are cut into R chunks; a 256-thread workgroup owns a
+// 512-column strip of one chunk.  Each lane streams 16-byte row segments
+// (8 columns) down the chunk, one row in four per wave, and keeps 8 float64
+// sums (a bf16 square is exact in fp32, an fp32 square in fp64), so the only
+// rounding is float64 addition.  The four waves' sums are added through LDS
+// in a fixed order and stored as a float64 partial [R][K] in the workspace.
+// Pass 2: h[j] = fl32(sum over the R partials, in chunk order).
+// A one-column-per-lane variant covers K % 8 != 0.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace hd {
+
+static constexpr int HD_COLS = 512;  // columns per workgroup (64 lanes x 8)
+
+static void hdiag_shape(int64_t M, int64_t K, int64_t *col_tiles, int64_t *chunks)
+{
+    const int64_t cols = (K % 8 == 0) ? HD_COLS : 256;
+    int64_t ct = (K + cols - 1) / cols;
+    if (ct < 1) ct = 1;
+    int64_t r = (M + 63) / 64;                 // at least 64 rows per chunk
+    const int64_t want = (4096 + ct - 1) / ct; // ~4096 workgroups in flight
+    if (r > want) r = want;
+    if (r < 1) r = 1;
+    *col_tiles = ct;
+    *chunks = r;
+}
+
+size_t hdiag_ws(int64_t M, int64_t K)
+{
+    int64_t ct, r;
+    hdiag_shape(M, K, &ct, &r);
+    return (size_t)r * (size_t)K * sizeof(double);
+}
+
+template <typename T>
+__device__ __forceinline__ double sq(float x)
+{
+    if (sizeof(T) == 2) return (double)(x * x);  // bf16: 8-bit significand, the fp32 square is exact
+    return (double)x * (double)x;                // fp32: exact in float64
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void hdiag_vec(const T *__restrict__ X, int64_t M, int64_t K,
+                                                 int64_t rows_per_chunk, double *__restrict__ part)
+{
+    __shared__ double red[3][64][8];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int64_t col = (int64_t)blockIdx.x * HD_COLS + lane * 8;
+    const int64_t t0 = (int64_t)blockIdx.y * rows_per_chunk;
+    int64_t t1 = t0 + rows_per_chunk;
+    if (t1 > M) t1 = M;
+    double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (col < K) {
+        const T *p = X + col;
+        int64_t t = t0 + wv;
+        // four rows in flight per lane
+        for (; t + 12 < t1; t += 16) {
+            float v0[8], v1[8], v2[8], v3[8];
+            load8<T>(p + t * K, v0);
+            load8<T>(p + (t + 4) * K, v1);
+            load8<T>(p + (t + 8) * K, v2);
+            load8<T>(p + (t + 12) * K, v3);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[j] += ((sq<T>(v0[j]) + sq<T>(v1[j])) + sq<T>(v2[j])) + sq<T>(v3[j]);
+        }
+        for (; t < t1; t += 4) {
+            float v0[8];
+            load8<T>(p + t * K, v0);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[j] += sq<T>(v0[j]);
+        }
+    }
+    if (wv > 0) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) red[wv - 1][lane][j] = acc[j];
+    }
+    __syncthreads();
+    if (wv == 0 && col < K) {
+        double *o = part + (int64_t)blockIdx.y * K + col;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[j] = ((acc[j] + red[0][lane][j]) + red[1][lane][j]) + red[2][lane][j];
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void hdiag_col(const T *__restrict__ X, int64_t M, int64_t K,
+                                                 int64_t rows_per_chunk, double *__restrict__ part)
+{
+    const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (col >= K) return;
+    const int64_t t0 = (int64_t)blockIdx.y * rows_per_chunk;
+    int64_t t1 = t0 + rows_per_chunk;
+    if (t1 > M) t1 = M;
+    double acc = 0.0;
+    for (int64_t t = t0; t < t1; ++t) {
+        const float x = sizeof(T) == 2 ? bf16_to_f32(((const bf16_t *)X)[t * K + col]) : ((const float *)X)[t * K + col];
+        acc += sq<T>(x);
+    }
+    part[(int64_t)blockIdx.y * K + col] = acc;
+}
+
+__global__ __launch_bounds__(256) void hdiag_final(const double *__restrict__ part, int64_t R, int64_t K,
+                                                   float *__restrict__ h)
+{
+    const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (col >= K) return;
+    double s = 0.0;
+    for (int64_t r = 0; r < R; ++r) s += part[r * K + col];
+    h[col] = (float)s;
+}
+
+hipError_t launch_hdiag(const void *X, int xdt, int64_t M, int64_t K, float *h, void *ws, hipStream_t st)
+{
+    int64_t ct, R;
+    hdiag_shape(M, K, &ct, &R);
+    const int64_t rpc = (M + R - 1) / R;
+    double *part = static_cast<double *>(ws);
+    const dim3 grid((unsigned)ct, (unsigned)R);
+    if (K % 8 == 0) {
+        if (xdt == 1)
+            hdiag_vec<bf16_t><<<grid, 256, 0, st>>>((const bf16_t *)X, M, K, rpc, part);
+        else
+            hdiag_vec<float><<<grid, 256, 0, st>>>((const float *)X, M, K, rpc, part);
+    } else {
+        if (xdt == 1)
+            hdiag_col<bf16_t><<<grid, 256, 0, st>>>((const bf16_t *)X, M, K, rpc, part);
+        else
+            hdiag_col<float><<<grid, 256, 0, st>>>((const float *)X, M, K, rpc, part);
+    }
+    hdiag_final<<<(unsigned)((K + 255) / 256), 256, 0, st>>>(part, R, K, h);
+    return hipGetLastError();
+}
+
+}  // namespace hd

@@ -1,0 +1,46 @@
+// kernels.hpp - launchers behind the C ABI (arguments already validated).
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+namespace hd {
+
+// Naive scale + encode (scales_in == NULL), or encode with given scale codes.
+hipError_t launch_encode(int fmt, int B, const void *W, int wdt, int64_t N, int64_t K, const float *h,
+                         const uint8_t *scales_in, uint8_t *codes, uint8_t *scales, float *block_obj,
+                         hipStream_t st);
+
+// SSE-Optimal (h == NULL) or H-Optimal search + encode.
+hipError_t launch_search(int fmt, int B, const void *W, int wdt, int64_t N, int64_t K, const float *h,
+                         uint8_t *codes, uint8_t *scales, float *block_obj, hipStream_t st);
+// per-format instantiations (one translation unit each)
+hipError_t launch_search_int8(int B, const void *W, int wdt, int64_t N, int64_t K, const float *h,
+                              uint8_t *codes, uint8_t *scales, float *block_obj, hipStream_t st);
+hipError_t launch_search_nvfp4(int B, const void *W, int wdt, int64_t N, int64_t K, const float *h,
+                               uint8_t *codes, uint8_t *scales, float *block_obj, hipStream_t st);
+hipError_t launch_search_mxfp4(int B, const void *W, int wdt, int64_t N, int64_t K, const float *h,
+                               uint8_t *codes, uint8_t *scales, float *block_obj, hipStream_t st);
+hipError_t launch_search_mxfp8(int B, const void *W, int wdt, int64_t N, int64_t K, const float *h,
+                               uint8_t *codes, uint8_t *scales, float *block_obj, hipStream_t st);
+hipError_t launch_search_fp8s(int B, const void *W, int wdt, int64_t N, int64_t K, const float *h,
+                              uint8_t *codes, uint8_t *scales, float *block_obj, hipStream_t st);
+
+hipError_t launch_dequant(int fmt, int B, const uint8_t *codes, const uint8_t *scales, int64_t N, int64_t K,
+                          void *out, int out_t, hipStream_t st);
+
+size_t weight_error_ws(int64_t N, int64_t K);
+hipError_t launch_weight_error(const void *W, int wdt, const void *Wq, int qdt, int64_t N, int64_t K,
+                               double *out, double *sums, void *ws, hipStream_t st);
+
+size_t hdiag_ws(int64_t M, int64_t K);
+hipError_t launch_hdiag(const void *X, int xdt, int64_t M, int64_t K, float *h, void *ws, hipStream_t st);
+
+size_t output_error_ws(int64_t M, int64_t N, int64_t K, bool mfma);
+bool output_error_uses_mfma(int xdt, int wdt, int64_t K);
+hipError_t launch_output_error(const void *X, int xdt, int64_t M, const void *W, int wdt, const void *Wq,
+                               int qdt, int64_t N, int64_t K, double *out, double *sums, void *ws,
+                               hipStream_t st);
+
+}  // namespace hd

@@ -1,0 +1,277 @@
+// quant.hip - Naive scale + encode, encode with given scales, dequantize and
+// the weight error.  All HBM-bound streaming kernels: each thread owns 8
+// consecutive weights (one 16-byte bf16 load), a block of B weights is B/8
+// consecutive lanes, and its amax / objective are combined with lane shuffles.
+#include "encode.hpp"
+#include "kernels.hpp"
+
+namespace hd {
+
+// ---------------------------------------------------------------- encode ---
+// Naive ("Is Finer Better?" §2.1: s = Q_scale(amax / C); qwantize "Results",
+// INT8: the amax itself stored as E4M3 and divided by 127) when GIVEN is false;
+// otherwise the scale code of each block comes from scales_in.
+template <int EK, int SK, typename T, int B, bool GIVEN>
+__global__ __launch_bounds__(256) void encode_kernel(const T *__restrict__ W, int64_t total, int64_t K,
+                                                     const float *__restrict__ h,
+                                                     const uint8_t *__restrict__ scales_in,
+                                                     uint8_t *__restrict__ codes, uint8_t *__restrict__ scales,
+                                                     float *__restrict__ block_obj)
+{
+    constexpr int TPB = B / 8;
+    constexpr bool ONE_STEP = sizeof(T) == 2;
+    const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+    const bool active = e0 < total;  // total % B == 0: a block's lanes agree
+    float w[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (active) load8<T>(W + e0, w);
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(w[j]));
+    amax = group_max<TPB>(amax);
+    const int64_t blk = e0 / B;
+    int code;
+    float s;
+    if (GIVEN) {
+        code = active ? (int)scales_in[blk] : 0;
+        const bool valid = SK == SCALE_E8M0 ? code <= 254 : code <= 126;
+        s = valid ? scale_value(SK, code) : 0.0f;
+    } else {
+        code = naive_code<EK, SK>(amax);
+        s = scale_value(SK, code);
+    }
+    const float r = (s != 0.0f) ? 1.0f / s : 0.0f;
+    double om[8];
+    const double *omp = nullptr;
+    if (h != nullptr && active) {
+        const int64_t k0 = e0 % K;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) om[j] = (double)h[k0 + j];
+        omp = om;
+    }
+    uint32_t c[8];
+    double obj = encode8<EK, SK, ONE_STEP>(w, s, r, omp, c);
+    obj = group_sum<TPB>(obj);
+    if (!active) return;
+    store_codes8<EK>(codes, e0, c);
+    if ((threadIdx.x % TPB) == 0) {
+        if (!GIVEN) scales[blk] = (uint8_t)code;
+        if (block_obj) block_obj[blk] = (float)obj;
+    }
+}
+
+template <int EK, int SK, typename T, bool GIVEN>
+static hipError_t encode_b(int B, const void *W, int64_t N, int64_t K, const float *h, const uint8_t *si,
+                           uint8_t *codes, uint8_t *scales, float *bo, hipStream_t st)
+{
+    const int64_t total = N * K;
+    const dim3 grid((unsigned)((total / 8 + 255) / 256));
+    const T *w = static_cast<const T *>(W);
+#define HD_ENC_CASE(BB)                                                                                  \
+    case BB:                                                                                             \
+        encode_kernel<EK, SK, T, BB, GIVEN><<<grid, 256, 0, st>>>(w, total, K, h, si, codes, scales, bo); \
+        break;
+    switch (B) {
+        HD_ENC_CASE(8)
+        HD_ENC_CASE(16)
+        HD_ENC_CASE(32)
+        HD_ENC_CASE(64)
+        HD_ENC_CASE(128)
+        HD_ENC_CASE(256)
+    default: return hipErrorInvalidValue;
+    }
+#undef HD_ENC_CASE
+    return hipGetLastError();
+}
+
+template <int EK, int SK>
+static hipError_t encode_f(int B, const void *W, int wdt, int64_t N, int64_t K, const float *h,
+                           const uint8_t *si, uint8_t *codes, uint8_t *scales, float *bo, hipStream_t st)
+{
+    if (si) {
+        return wdt == 1 ? encode_b<EK, SK, bf16_t, true>(B, W, N, K, h, si, codes, scales, bo, st)
+                        : encode_b<EK, SK, float, true>(B, W, N, K, h, si, codes, scales, bo, st);
+    }
+    return wdt == 1 ? encode_b<EK, SK, bf16_t, false>(B, W, N, K, h, si, codes, scales, bo, st)
+                    : encode_b<EK, SK, float, false>(B, W, N, K, h, si, codes, scales, bo, st);
+}
+
+hipError_t launch_encode(int fmt, int B, const void *W, int wdt, int64_t N, int64_t K, const float *h,
+                         const uint8_t *scales_in, uint8_t *codes, uint8_t *scales, float *block_obj,
+                         hipStream_t st)
+{
+    switch (fmt) {
+    case HD_INT8_E4M3:
+        return encode_f<ELEM_INT8, SCALE_INT8>(B, W, wdt, N, K, h, scales_in, codes, scales, block_obj, st);
+    case HD_NVFP4:
+        return encode_f<ELEM_E2M1, SCALE_E4M3>(B, W, wdt, N, K, h, scales_in, codes, scales, block_obj, st);
+    case HD_MXFP4:
+        return encode_f<ELEM_E2M1, SCALE_E8M0>(B, W, wdt, N, K, h, scales_in, codes, scales, block_obj, st);
+    case HD_MXFP8:
+        return encode_f<ELEM_E4M3, SCALE_E8M0>(B, W, wdt, N, K, h, scales_in, codes, scales, block_obj, st);
+    case HD_FP8_E4M3S:
+        return encode_f<ELEM_E4M3, SCALE_E4M3>(B, W, wdt, N, K, h, scales_in, codes, scales, block_obj, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+// ------------------------------------------------------------ dequantize ---
+// x^ = s q ("Is Finer Better?" §2.1): sign * fl32(s * val(index)).
+template <int EK, int SK, int OUT_BF16>
+__global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict__ codes,
+                                                      const uint8_t *__restrict__ scales, int64_t total,
+                                                      int B, void *__restrict__ out)
+{
+    const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+    if (e0 >= total) return;
+    const int sc = scales[e0 / B];
+    const bool sval = SK == SCALE_E8M0 ? sc <= 254 : sc <= 126;
+    const float s = sval ? scale_value(SK, sc) : 0.0f;
+    uint32_t c[8];
+    if (EK == ELEM_E2M1) {
+        const uint32_t v = *reinterpret_cast<const uint32_t *>(codes + e0 / 2);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) c[j] = (v >> (4 * j)) & 15u;
+    } else {
+        const uint2 v = *reinterpret_cast<const uint2 *>(codes + e0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            c[j] = (v.x >> (8 * j)) & 255u;
+            c[4 + j] = (v.y >> (8 * j)) & 255u;
+        }
+    }
+    float o[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        uint32_t idx;
+        bool neg, ok = true;
+        if (EK == ELEM_INT8) {
+            const int q = (int)(int8_t)(uint8_t)c[j];
+            ok = q != -128;
+            neg = q < 0;
+            idx = (uint32_t)(q < 0 ? -q : q);
+        } else if (EK == ELEM_E2M1) {
+            neg = (c[j] & 8u) != 0;
+            idx = c[j] & 7u;
+        } else {
+            neg = (c[j] & 0x80u) != 0;
+            idx = c[j] & 0x7Fu;
+            ok = idx != 0x7Fu;
+        }
+        const float mag = ok ? s * elem_value<EK>(idx) : 0.0f;
+        o[j] = neg ? -mag : mag;
+    }
+    if (OUT_BF16) {
+        uint4 v;
+        v.x = f32_to_bf16(o[0]) | (f32_to_bf16(o[1]) << 16);
+        v.y = f32_to_bf16(o[2]) | (f32_to_bf16(o[3]) << 16);
+        v.z = f32_to_bf16(o[4]) | (f32_to_bf16(o[5]) << 16);
+        v.w = f32_to_bf16(o[6]) | (f32_to_bf16(o[7]) << 16);
+        *reinterpret_cast<uint4 *>(static_cast<bf16_t *>(out) + e0) = v;
+    } else {
+        float4 *p = reinterpret_cast<float4 *>(static_cast<float *>(out) + e0);
+        p[0] = make_float4(o[0], o[1], o[2], o[3]);
+        p[1] = make_float4(o[4], o[5], o[6], o[7]);
+    }
+}
+
+template <int EK, int SK>
+static hipError_t dequant_f(int B, const uint8_t *codes, const uint8_t *scales, int64_t total, void *out,
+                            int out_t, hipStream_t st)
+{
+    const dim3 grid((unsigned)((total / 8 + 255) / 256));
+    if (out_t == 1)
+        dequant_kernel<EK, SK, 1><<<grid, 256, 0, st>>>(codes, scales, total, B, out);
+    else
+        dequant_kernel<EK, SK, 0><<<grid, 256, 0, st>>>(codes, scales, total, B, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_dequant(int fmt, int B, const uint8_t *codes, const uint8_t *scales, int64_t N, int64_t K,
+                          void *out, int out_t, hipStream_t st)
+{
+    const int64_t total = N * K;
+    switch (fmt) {
+    case HD_INT8_E4M3: return dequant_f<ELEM_INT8, SCALE_INT8>(B, codes, scales, total, out, out_t, st);
+    case HD_NVFP4: return dequant_f<ELEM_E2M1, SCALE_E4M3>(B, codes, scales, total, out, out_t, st);
+    case HD_MXFP4: return dequant_f<ELEM_E2M1, SCALE_E8M0>(B, codes, scales, total, out, out_t, st);
+    case HD_MXFP8: return dequant_f<ELEM_E4M3, SCALE_E8M0>(B, codes, scales, total, out, out_t, st);
+    case HD_FP8_E4M3S: return dequant_f<ELEM_E4M3, SCALE_E4M3>(B, codes, scales, total, out, out_t, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------- weight error ---
+// ||Wq - W||_F / ||W||_F (qwantize "Results", metric definitions): each
+// workgroup sums its grid-stride share in float64, the partials are combined
+// in a fixed order by one workgroup.
+static constexpr int WE_GRID = 2048;
+
+template <typename TW, typename TQ>
+__global__ __launch_bounds__(256) void werr_partial(const TW *__restrict__ W, const TQ *__restrict__ Wq,
+                                                    int64_t total, double *__restrict__ part)
+{
+    __shared__ double sh[4];
+    double num = 0.0, den = 0.0;
+    for (int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8; e0 < total;
+         e0 += (int64_t)gridDim.x * 256 * 8) {
+        float w[8], q[8];
+        load8<TW>(W + e0, w);
+        load8<TQ>(Wq + e0, q);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const double d = (double)q[j] - (double)w[j];
+            num += d * d;
+            den += (double)w[j] * (double)w[j];
+        }
+    }
+    num = block_sum_256(num, sh);
+    den = block_sum_256(den, sh);
+    if (threadIdx.x == 0) {
+        part[2 * blockIdx.x] = num;
+        part[2 * blockIdx.x + 1] = den;
+    }
+}
+
+// Sum `n` (num, den) partials in a fixed order; out = sqrt(num) / sqrt(den).
+__global__ __launch_bounds__(256) void ratio_final(const double *__restrict__ part, int n,
+                                                   double *__restrict__ out, double *__restrict__ sums)
+{
+    __shared__ double sh[4];
+    double a = 0.0, b = 0.0;
+    for (int i = threadIdx.x; i < n; i += 256) {
+        a += part[2 * i];
+        b += part[2 * i + 1];
+    }
+    a = block_sum_256(a, sh);
+    b = block_sum_256(b, sh);
+    if (threadIdx.x == 0) {
+        *out = sqrt(a) / sqrt(b);
+        if (sums) {
+            sums[0] = a;
+            sums[1] = b;
+        }
+    }
+}
+
+size_t weight_error_ws(int64_t, int64_t) { return sizeof(double) * 2 * WE_GRID; }
+
+hipError_t launch_weight_error(const void *W, int wdt, const void *Wq, int qdt, int64_t N, int64_t K,
+                               double *out, double *sums, void *ws, hipStream_t st)
+{
+    const int64_t total = N * K;
+    int64_t g = (total / 8 + 255) / 256;
+    const int grid = (int)(g < WE_GRID ? (g > 0 ? g : 1) : WE_GRID);
+    double *part = static_cast<double *>(ws);
+    if (wdt == 1 && qdt == 1)
+        werr_partial<bf16_t, bf16_t><<<grid, 256, 0, st>>>((const bf16_t *)W, (const bf16_t *)Wq, total, part);
+    else if (wdt == 1)
+        werr_partial<bf16_t, float><<<grid, 256, 0, st>>>((const bf16_t *)W, (const float *)Wq, total, part);
+    else if (qdt == 1)
+        werr_partial<float, bf16_t><<<grid, 256, 0, st>>>((const float *)W, (const bf16_t *)Wq, total, part);
+    else
+        werr_partial<float, float><<<grid, 256, 0, st>>>((const float *)W, (const float *)Wq, total, part);
+    ratio_final<<<1, 256, 0, st>>>(part, grid, out, sums);
+    return hipGetLastError();
+}
+
+}  // namespace hd

@@ -1,0 +1,191 @@
+/*
+ * hdiag.h - C ABI of the MI355X (gfx950) block-scale quantiser library
+ * (libhdiag.so).
+ *
+ * For every contiguous block of B weights along K in each row of W [N, K] the
+ * library picks one scale from a quantised grid and encodes the block to an
+ * element format, as the qwantize "Results" page describes it (sections
+ * "INT8 (FP8 E4M3 scales)", "NVFP4 (FP8 E4M3 scales)" and "MXFP4 (UE8M0
+ * power-of-2 scales)"), following the generic microscaling quantiser of
+ * "Is Finer Better? The Limits of Microscaling Formats in LLMs", §2.1:
+ * s = Q_scale(x_max / C), q_i = Q_elem(x_i / s), x^_i = s q_i.
+ *
+ * Conventions shared by every call
+ *   - Every array argument is a DEVICE pointer owned by the caller, 16-byte
+ *     aligned, row-major and densely packed.  The library allocates nothing;
+ *     calls that need scratch memory take a caller-owned workspace whose size
+ *     the matching *_workspace_size() function returns.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *     calls only enqueue work on that stream and return; results (including the
+ *     double scalars written by the error metrics) are valid once the stream has
+ *     been synchronised.  Calls on different streams may run concurrently as
+ *     long as they do not share output or workspace memory.
+ *   - Arguments are validated on the host before anything is launched; an
+ *     invalid call returns an error and touches no memory.  Nothing is printed
+ *     and no exception crosses the ABI.  hdiag_last_error() returns a
+ *     thread-local description of the last failure on the calling thread.
+ *   - Inputs must be finite; NaN / Inf inputs give unspecified (but
+ *     memory-safe) codes.
+ *   - Sizes of 0 (N, K or M) are valid and enqueue nothing, except where a
+ *     metric would divide by zero (see the metric functions).
+ */
+#ifndef HDIAG_H
+#define HDIAG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    HD_OK = 0,
+    HD_ERR_INVALID_ARG = -1, /* bad pointer, size, alignment, enum or block size */
+    HD_ERR_UNSUPPORTED = -2, /* a valid but unimplemented combination */
+    HD_ERR_HIP = -3          /* the HIP runtime reported an error (see hdiag_last_error) */
+} hd_status;
+
+typedef enum { HD_F32 = 0, HD_BF16 = 1 } hd_dtype;
+
+/* Scale choice (qwantize "Results", all three format tables):
+ *   HD_NAIVE   - amax of the block snapped onto the scale grid;
+ *   HD_SSE_OPT - the candidate minimising sum_j (w_j - s Q(w_j / s))^2;
+ *   HD_H_OPT   - the candidate minimising sum_j h_j (w_j - s Q(w_j / s))^2, the
+ *                diagonal-Hessian form of the output error (quantisation
+ *                algorithms note, §1).
+ * The search methods evaluate every candidate of the grid and return the first
+ * (lowest) scale code among equal minima. */
+typedef enum { HD_NAIVE = 0, HD_SSE_OPT = 1, HD_H_OPT = 2 } hd_method;
+
+/* Element format x scale grid.
+ *   HD_INT8_E4M3 - symmetric INT8 elements in [-127, 127]; the block's amax is
+ *                  stored as an E4M3 code and the effective scale is
+ *                  fl32(val(code) / 127) (qwantize "Results", INT8 section).
+ *   HD_NVFP4     - E2M1 elements {0,.5,1,1.5,2,3,4,6}, E4M3 scale ("Is Finer
+ *                  Better?" §2.1, NVFP4 with a UE4M3 scale; any B here).
+ *   HD_MXFP4     - E2M1 elements, E8M0 power-of-two scale (OCP MX, §2.1).
+ *   HD_MXFP8     - E4M3 elements, E8M0 scale.
+ *   HD_FP8_E4M3S - E4M3 elements, E4M3 scale.
+ * Search candidates: the 126 positive finite E4M3 codes 0x01..0x7E (E4M3 and
+ * INT8 grids; max 448), or all 255 finite E8M0 codes 0x00..0xFE (2^-127 ..
+ * 2^127).  Naive may also return E4M3 code 0 (the zero scale: every element
+ * encodes to 0), when amax / C rounds into the zero bin ("Is Finer Better?",
+ * App. F.3). */
+typedef enum {
+    HD_INT8_E4M3 = 0,
+    HD_NVFP4 = 1,
+    HD_MXFP4 = 2,
+    HD_MXFP8 = 3,
+    HD_FP8_E4M3S = 4
+} hd_format;
+
+/* ---------------------------------------------------------------- hdiag --- */
+
+/* Bytes of workspace hdiag() needs for X [M, K]. */
+size_t hdiag_workspace_size(int64_t M, int64_t K);
+
+/* h[j] = sum_{t<M} X[t][j]^2: the diagonal of X^T X, i.e. the per-input-channel
+ * weight of the H-Optimal objective (quantisation algorithms note, §1, which
+ * writes it as the mean E[x_j^2]; the sum differs by the factor M, which does
+ * not move the argmin).  X: [M, K] of dtype xt.  h: [K] float32 output.
+ * Summed in float64 (squares are exact), rounded once to float32.
+ * workspace: ws_bytes >= hdiag_workspace_size(M, K).
+ * Errors: HD_ERR_INVALID_ARG for NULL X / h (when M*K > 0), M or K < 0, a bad
+ * dtype, a misaligned pointer or a short workspace. */
+hd_status hdiag(const void *X, hd_dtype xt, int64_t M, int64_t K, float *h, void *ws,
+                size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------ quantize_blocks --- */
+
+/* Choose the scale of every block and encode W with it.
+ *   W      : [N, K] of dtype wt (float32 or bfloat16).
+ *   B      : block size along K, one of 8, 16, 32, 64, 128, 256; K % B == 0.
+ *   h      : [K] float32, required for HD_H_OPT.  For HD_NAIVE it only weights
+ *            the reported block objective (NULL: unweighted); ignored by
+ *            HD_SSE_OPT.
+ *   codes  : element codes.  HD_INT8_E4M3: [N, K] int8 two's complement.
+ *            HD_MXFP8 / HD_FP8_E4M3S: [N, K] E4M3 bytes (sign bit 7).
+ *            HD_NVFP4 / HD_MXFP4: [N, K/2] bytes of two E2M1 nibbles (sign bit
+ *            3), element 2i in the low nibble.  A negative input that rounds to
+ *            zero keeps its sign bit (E2M1 0x8, E4M3 0x80).
+ *   scales : [N, K/B] scale codes (E4M3 or E8M0 bytes).
+ *   block_obj: optional [N, K/B] float32: the block's objective at the chosen
+ *            scale (weighted by h when h is used), computed in float64 and
+ *            rounded; may be NULL.
+ * Encoding: q = RNE_T(fl32(|w| / s)) onto the element table T with ties to the
+ * even code and saturation at the largest element; dequantised value
+ * fl32(s * val(q)).  Division is IEEE round-to-nearest (qwantize "Results",
+ * Correctness notes, on why a reciprocal-multiply moves boundary ties).
+ * Errors: HD_ERR_INVALID_ARG for NULL W / codes / scales (when N*K > 0), bad
+ * enums, an unsupported B, K % B != 0, N or K < 0, H_OPT without h, misaligned
+ * pointers. */
+hd_status quantize_blocks(hd_method method, hd_format fmt, int32_t B, const void *W, hd_dtype wt,
+                          int64_t N, int64_t K, const float *h, uint8_t *codes, uint8_t *scales,
+                          float *block_obj, void *stream);
+
+/* Encode W with caller-given scale codes (the encode step alone).  Arguments
+ * as quantize_blocks; scales_in [N, K/B] is read, not written.  A NaN scale
+ * code (E4M3 0x7F..., E8M0 0xFF) encodes its block with the zero scale. */
+hd_status encode_blocks(hd_format fmt, int32_t B, const void *W, hd_dtype wt, int64_t N, int64_t K,
+                        const uint8_t *scales_in, const float *h, uint8_t *codes, float *block_obj,
+                        void *stream);
+
+/* ----------------------------------------------------------- dequantize --- */
+
+/* Wq[n][k] = sign * fl32(s_block * val(q)) ("Is Finer Better?" §2.1,
+ * x^ = s q), written as float32 or as bfloat16 (round-to-nearest-even of the
+ * float32 value).  codes / scales laid out as quantize_blocks writes them.
+ * Invalid codes (INT8 -128, E4M3 0x7F / 0xFF, E8M0 0xFF) decode to 0. */
+hd_status dequantize(hd_format fmt, int32_t B, const uint8_t *codes, const uint8_t *scales,
+                     int64_t N, int64_t K, void *Wq, hd_dtype out_t, void *stream);
+
+/* --------------------------------------------------------------- errors --- */
+
+/* Weight error ||Wq - W||_F / ||W||_F (qwantize "Results", metric
+ * definitions), in float64, written to the device scalar *out.
+ * sums (optional, device, 2 doubles): {sum (Wq-W)^2, sum W^2}.
+ * If ||W||_F = 0 the result is the IEEE quotient (NaN or Inf). */
+size_t weight_error_workspace_size(int64_t N, int64_t K);
+hd_status weight_error(const void *W, hd_dtype wt, const void *Wq, hd_dtype qt, int64_t N, int64_t K,
+                       double *out, double *sums, void *ws, size_t ws_bytes, void *stream);
+
+/* Output error ||X Wq^T - X W^T||_F / ||X W^T||_F (qwantize "Results", metric
+ * definitions), written to the device scalar *out (float64).
+ * sums (optional, device, 2 doubles): {||X (Wq-W)^T||^2, ||X W^T||^2}.
+ * With X and W in bfloat16 and K % 32 == 0 the products run on the bf16 MFMA
+ * units with float32 accumulation: Y = X W^T and D = X dW^T with
+ * dW = fl32(Wq - W) split into two bfloat16 terms hi + lo (the difference, not
+ * Wq, is rounded, so INT8 codes that bf16 cannot hold do not move the metric);
+ * the squares of each output tile are summed in float64.  Other inputs use a
+ * float32 vector path.
+ * workspace: ws_bytes >= output_error_workspace_size(M, N, K). */
+size_t output_error_workspace_size(int64_t M, int64_t N, int64_t K);
+hd_status output_error(const void *X, hd_dtype xt, int64_t M, const void *W, hd_dtype wt,
+                       const void *Wq, hd_dtype qt, int64_t N, int64_t K, double *out, double *sums,
+                       void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------ utilities --- */
+
+/* Static description of a status code. */
+const char *hdiag_strerror(hd_status s);
+
+/* Thread-local description of the last failure on this thread ("" if none). */
+const char *hdiag_last_error(void);
+
+/* Format facts: bits of one element code, bits of one scale, number of search
+ * candidates, and total bits per weight = elem_bits + scale_bits / B
+ * (qwantize "Results", "Larger blocks" layout table: 4.5 / 4.25 / 4.125 for
+ * FP4 with an 8-bit scale at B = 16 / 32 / 64).  Any output pointer may be
+ * NULL.  Host-only; needs no GPU. */
+hd_status hdiag_format_info(hd_format fmt, int32_t B, int *elem_bits, int *scale_bits,
+                            int *n_candidates, double *bits_per_weight);
+
+/* Library version string.  Host-only. */
+const char *hdiag_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HDIAG_H */

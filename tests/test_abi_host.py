@@ -1,0 +1,91 @@
+"""Host-side checks of libhdiag.so (no GPU needed, no kernel is launched).
+
+- the library loads and exports every function include/hdiag.h declares;
+- hdiag_format_info reports the bits/weight the pages print;
+- argument validation rejects bad calls before touching any memory.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_scaled_precision_hdiag_amd as hd
+from conftest import ROOT, golden_rows
+
+HEADER = os.path.join(ROOT, "include", "hdiag.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([A-Za-z_][A-Za-z0-9_]*)\s*\(",
+                       src, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "while")))
+
+
+def test_header_declares_the_binding_exports():
+    assert sorted(declared_functions()) == sorted(hd.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = hd.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert "gfx950" in hd.version()
+
+
+def test_format_info_bits_per_weight():
+    # qwantize "Results", "Larger blocks" layout table (FP4 + 8-bit scale)
+    for B, scale_bpw, total in golden_rows("bits_per_weight.txt"):
+        e, s, n, bpw = hd.hdiag_format_info(hd.NVFP4, int(B))
+        assert (e, s, n) == (4, 8, 126)
+        assert bpw == float(total) and s / int(B) == float(scale_bpw)
+    assert hd.hdiag_format_info(hd.MXFP4, 32)[2] == 255
+    assert hd.hdiag_format_info(hd.MXFP8, 32)[:3] == (8, 8, 255)
+    assert hd.hdiag_format_info(hd.INT8_E4M3, 32)[3] == 8.25
+
+
+def test_strerror():
+    assert hd._strerror(hd.HD_ERR_INVALID_ARG) == "invalid argument"
+    assert hd._strerror(hd.HD_OK) == "success"
+
+
+# fake, never-dereferenced device addresses (validation must fail first)
+A = ctypes.c_void_p(1 << 20)
+MIS = ctypes.c_void_p((1 << 20) + 4)
+
+
+@pytest.mark.parametrize("args,needle", [
+    ((hd.SSE_OPT, hd.NVFP4, 12, A, hd.HD_BF16, 4, 48, None, A, A, None, None), "block size"),
+    ((hd.SSE_OPT, hd.NVFP4, 16, A, hd.HD_BF16, 4, 40, None, A, A, None, None), "multiple of B"),
+    ((7, hd.NVFP4, 16, A, hd.HD_BF16, 4, 32, None, A, A, None, None), "unknown method"),
+    ((hd.SSE_OPT, 9, 16, A, hd.HD_BF16, 4, 32, None, A, A, None, None), "unknown format"),
+    ((hd.SSE_OPT, hd.NVFP4, 16, A, 5, 4, 32, None, A, A, None, None), "unknown dtype"),
+    ((hd.H_OPT, hd.NVFP4, 16, A, hd.HD_BF16, 4, 32, None, A, A, None, None), "needs h"),
+    ((hd.SSE_OPT, hd.NVFP4, 16, None, hd.HD_BF16, 4, 32, None, A, A, None, None), "W is NULL"),
+    ((hd.SSE_OPT, hd.NVFP4, 16, MIS, hd.HD_BF16, 4, 32, None, A, A, None, None), "aligned"),
+    ((hd.SSE_OPT, hd.NVFP4, 16, A, hd.HD_BF16, -1, 32, None, A, A, None, None), "negative"),
+])
+def test_quantize_blocks_rejects(args, needle):
+    rc = hd.lib().quantize_blocks(*args, None)
+    assert rc == hd.HD_ERR_INVALID_ARG
+    assert needle in hd.lib().hdiag_last_error().decode()
+
+
+def test_empty_inputs_are_noops():
+    L = hd.lib()
+    assert L.quantize_blocks(hd.SSE_OPT, hd.NVFP4, 16, None, hd.HD_BF16, 0, 32, None, None, None, None, None) == 0
+    assert L.quantize_blocks(hd.NAIVE, hd.MXFP4, 32, None, hd.HD_F32, 5, 0, None, None, None, None, None) == 0
+    assert L.dequantize(hd.NVFP4, 16, None, None, 0, 16, None, hd.HD_F32, None) == 0
+    assert L.hdiag(None, hd.HD_BF16, 10, 0, None, None, 0, None) == 0
+
+
+def test_workspace_queries():
+    assert hd.hdiag_workspace_size(244449, 9728) >= 9728 * 8
+    assert hd.lib().hdiag_workspace_size(-1, 5) == 0
+    ws = hd.output_error_workspace_size(16384, 2560, 9728)
+    assert ws >= 2560 * 9728 * 2  # holds bf16(Wq - W)
+    L = hd.lib()
+    rc = L.hdiag(A, hd.HD_BF16, 1000, 64, A, A, 8, None)
+    assert rc == hd.HD_ERR_INVALID_ARG and "workspace" in L.hdiag_last_error().decode()

@@ -1,0 +1,258 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle on the GPU.
+
+Bars (stated per test): bit-exact codes and scales for Naive and for encode
+with given scales; for the searches, identical scale codes on >= 99.99% of
+blocks and, on any block that differs, the oracle's objective at the GPU's
+scale within 1e-6 relative of the oracle's minimum (several scales can be
+correct at a tie); element codes bit-exact at the scale the GPU chose;
+hdiag within 1e-6 relative (both sum exact squares in float64); the error
+metrics within 1e-4 relative (the output error runs on bf16 MFMA).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import block_scaled_precision_hdiag_amd as hd
+
+pytestmark = pytest.mark.gpu
+
+FMTS = [hd.INT8_E4M3, hd.NVFP4, hd.MXFP4, hd.MXFP8, hd.FP8_E4M3S]
+BLOCKS = [8, 16, 32, 64, 128, 256]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    hd.lib()
+
+
+def dev(t):
+    return t.contiguous().cuda()
+
+
+def npy(t):
+    return t.detach().cpu().numpy()
+
+
+def weights_for(fmt, N, K, seed, dtype=torch.bfloat16):
+    # magnitudes that keep every format's competitive scales away from the grid ends
+    std = {hd.FP8_E4M3S: 4.0, hd.MXFP8: 0.05}.get(fmt, 0.02)
+    return synth.weights("t4", N, K, std=std, seed=seed, gain_seed=seed + 1, dtype=dtype)
+
+
+def h_for(K, seed):
+    X = synth.activations(512, K, seed, n_out=4, out_gain=50.0, idx_seed=seed + 1, dtype=torch.float32)
+    return oracle.hdiag(synth.bits(X))
+
+
+def check_search(fmt, B, W, h, method, frac=0.9999):
+    Wo = synth.bits(W)
+    hh = h if method == hd.H_OPT else None
+    c_o, s_o, obj_o = oracle.quantize(method, fmt, B, Wo, h=hh)
+    hdev = dev(torch.from_numpy(h)) if hh is not None else None
+    c_g, s_g, obj_g = hd.quantize_blocks(method, fmt, B, dev(W), h=hdev, block_obj=True)
+    torch.cuda.synchronize()
+    s_g, c_g, obj_g = npy(s_g), npy(c_g), npy(obj_g)
+    same = s_g == s_o
+    assert same.mean() >= frac, "scale agreement %.6f" % same.mean()
+    if not same.all():
+        at = oracle.objectives_at(fmt, B, Wo, s_g, h=hh)
+        rel = (at - obj_o) / np.maximum(obj_o, 1e-300)
+        assert np.all(rel[~same] <= 1e-6), rel[~same].max()
+    # element codes: bit-exact at the scales the GPU chose
+    c_ref, _, _ = oracle.quantize(hd.NAIVE, fmt, B, Wo, scales_in=s_g)
+    np.testing.assert_array_equal(c_g, c_ref)
+    np.testing.assert_allclose(obj_g, obj_o.astype(np.float32), rtol=2e-6, atol=0)
+    return same.mean()
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("B", BLOCKS)
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_naive_bit_exact(fmt, B, dtype):
+    N, K = 37, 3 * 256 + B * (1 if B < 256 else 0)  # ragged row count, several column tiles
+    K = (K // B) * B
+    W = weights_for(fmt, N, K, 1000 + fmt * 10 + B, dtype)
+    h = h_for(K, 7)
+    c_o, s_o, obj_o = oracle.quantize(hd.NAIVE, fmt, B, synth.bits(W), h=h)
+    c_g, s_g, obj_g = hd.quantize_blocks(hd.NAIVE, fmt, B, dev(W), h=dev(torch.from_numpy(h)), block_obj=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(npy(s_g), s_o)
+    np.testing.assert_array_equal(npy(c_g), c_o)
+    np.testing.assert_allclose(npy(obj_g), obj_o.astype(np.float32), rtol=2e-6)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_encode_every_bf16_at_every_scale(fmt):
+    """Every finite bf16 value (both signs) encoded at every candidate scale:
+    bit-exact codes.  This runs the quotient / rounding helpers of the search."""
+    pos = np.arange(0, 0x7F80, dtype=np.uint32)
+    allbits = np.concatenate([pos, pos | 0x8000]).astype(np.uint16)
+    B = 8
+    K = (allbits.size // B) * B
+    x = allbits[:K]
+    cands = oracle.candidates(fmt)
+    W = np.tile(x, (cands.size, 1))
+    scales = np.repeat(cands.astype(np.uint8)[:, None], K // B, axis=1)
+    c_o, _, _ = oracle.quantize(hd.NAIVE, fmt, B, W, scales_in=scales)
+    Wt = torch.from_numpy(W.view(np.int16)).view(torch.bfloat16)
+    c_g, _ = hd.encode_blocks(fmt, B, dev(Wt), dev(torch.from_numpy(scales)))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(npy(c_g), c_o)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_encode_fp32_random_at_every_scale(fmt):
+    rng = np.random.default_rng(3 + fmt)
+    cands = oracle.candidates(fmt)
+    K = 4096
+    # log-uniform magnitudes over the range where the element codes change
+    W = (np.exp(rng.uniform(-25, 12, (cands.size, K))) * rng.choice([-1, 1], (cands.size, K))).astype(np.float32)
+    scales = np.repeat(cands.astype(np.uint8)[:, None], K // 8, axis=1)
+    c_o, _, _ = oracle.quantize(hd.NAIVE, fmt, 8, W, scales_in=scales)
+    c_g, _ = hd.encode_blocks(fmt, 8, dev(torch.from_numpy(W)), dev(torch.from_numpy(scales)))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(npy(c_g), c_o)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("B", BLOCKS)
+@pytest.mark.parametrize("method", [hd.SSE_OPT, hd.H_OPT])
+def test_search_parity(fmt, B, method):
+    N, K = 300, 1024  # 2 row tiles (ragged), 4..128 block columns
+    W = weights_for(fmt, N, K, 2000 + fmt * 10 + B)
+    check_search(fmt, B, W, h_for(K, 11), method)
+
+
+@pytest.mark.parametrize("fmt", [hd.INT8_E4M3, hd.NVFP4])
+def test_search_parity_fp32_inputs(fmt):
+    W = weights_for(fmt, 100, 512, 31, dtype=torch.float32)
+    for m in (hd.SSE_OPT, hd.H_OPT):
+        check_search(fmt, 32, W, h_for(512, 12), m)
+
+
+def test_config1_tiny_end_to_end():
+    W, X = synth.config_inputs(1)
+    h_o = oracle.hdiag(synth.bits(X))
+    h_g = hd.hdiag(dev(X))
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(npy(h_g), h_o, rtol=1e-6)
+    for m in (hd.NAIVE, hd.SSE_OPT, hd.H_OPT):
+        if m == hd.NAIVE:
+            c_o, s_o, _ = oracle.quantize(m, hd.INT8_E4M3, 32, synth.bits(W))
+            c_g, s_g, _ = hd.quantize_blocks(m, hd.INT8_E4M3, 32, dev(W))
+            np.testing.assert_array_equal(npy(s_g), s_o)
+        else:
+            check_search(hd.INT8_E4M3, 32, W, h_o, m, frac=1.0)
+            c_g, s_g, _ = hd.quantize_blocks(m, hd.INT8_E4M3, 32, dev(W), h=dev(torch.from_numpy(h_o)))
+        Wq_g = hd.dequantize(hd.INT8_E4M3, 32, c_g, s_g, 64, 256)
+        Wq_o = oracle.dequantize(hd.INT8_E4M3, 32, npy(c_g), npy(s_g), 64, 256)
+        np.testing.assert_array_equal(npy(Wq_g), Wq_o)
+        we_g = hd.weight_error(dev(W), Wq_g).item()
+        we_o = oracle.weight_error(synth.bits(W), Wq_o)
+        assert we_g == pytest.approx(we_o, rel=1e-9)
+        oe_g = hd.output_error(dev(X), dev(W), Wq_g).item()
+        oe_o = oracle.output_error(synth.bits(X), synth.bits(W), Wq_o)
+        assert oe_g == pytest.approx(oe_o, rel=1e-4)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("M,K", [(1, 8), (257, 1000), (3001, 1536), (700, 37), (64, 4096)])
+def test_hdiag_parity(dtype, M, K):
+    X = synth.activations(M, K, 5 + M, n_out=2 if K > 2 else 0, out_gain=30.0, idx_seed=9, dtype=dtype)
+    h_o = oracle.hdiag(synth.bits(X))
+    h_g = hd.hdiag(dev(X))
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(npy(h_g), h_o, rtol=1e-6)
+
+
+def test_hdiag_exact_cases():
+    X = torch.ones(5000, 520, dtype=torch.bfloat16)
+    assert torch.equal(hd.hdiag(dev(X)).cpu(), torch.full((520,), 5000.0))
+    Xi = torch.randint(-3, 4, (2049, 64), generator=torch.Generator().manual_seed(1)).float()
+    want = (Xi.double() ** 2).sum(0).float()
+    assert torch.equal(hd.hdiag(dev(Xi)).cpu(), want)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("B", [16, 128])
+def test_dequantize_and_weight_error(fmt, B):
+    N, K = 77, 2048
+    W = weights_for(fmt, N, K, 4000 + fmt)
+    c_g, s_g, _ = hd.quantize_blocks(hd.SSE_OPT, fmt, B, dev(W))
+    deq_o = oracle.dequantize(fmt, B, npy(c_g), npy(s_g), N, K)
+    deq_g = hd.dequantize(fmt, B, c_g, s_g, N, K)
+    deq_b = hd.dequantize(fmt, B, c_g, s_g, N, K, dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(npy(deq_g), deq_o)
+    assert torch.equal(deq_b.cpu(), torch.from_numpy(deq_o).to(torch.bfloat16))
+    we_o, num_o, den_o = oracle.weight_error(synth.bits(W), deq_o, sums=True)
+    we_g, sums = hd.weight_error(dev(W), deq_g, sums=True)
+    assert we_g.item() == pytest.approx(we_o, rel=1e-9)
+    np.testing.assert_allclose(npy(sums), [num_o, den_o], rtol=1e-9)
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 200, 512), (129, 131, 96), (1000, 256, 1024), (64, 64, 8)])
+def test_output_error_parity(M, N, K):
+    W = weights_for(hd.NVFP4, N, K, 5000 + M)
+    X = synth.activations(M, K, 77 + N, n_out=2, out_gain=50.0, idx_seed=3, dtype=torch.bfloat16)
+    c_g, s_g, _ = hd.quantize_blocks(hd.SSE_OPT, hd.INT8_E4M3, 8, dev(W))
+    Wq = hd.dequantize(hd.INT8_E4M3, 8, c_g, s_g, N, K)
+    oe_o, d_o, y_o = oracle.output_error(synth.bits(X), synth.bits(W), npy(Wq), sums=True)
+    oe_g, sums = hd.output_error(dev(X), dev(W), Wq, sums=True)
+    torch.cuda.synchronize()
+    assert oe_g.item() == pytest.approx(oe_o, rel=1e-4)
+    np.testing.assert_allclose(npy(sums), [d_o, y_o], rtol=1e-4)
+
+
+def test_output_error_identity_equals_weight_error():
+    K, N = 256, 96
+    W = weights_for(hd.NVFP4, N, K, 6000)
+    X = torch.eye(K, dtype=torch.bfloat16)
+    c_g, s_g, _ = hd.quantize_blocks(hd.SSE_OPT, hd.NVFP4, 16, dev(W))
+    Wq = hd.dequantize(hd.NVFP4, 16, c_g, s_g, N, K, dtype=torch.bfloat16)
+    oe = hd.output_error(dev(X), dev(W), Wq).item()
+    we = hd.weight_error(dev(W), Wq).item()
+    assert oe == pytest.approx(we, rel=1e-5)
+
+
+def test_determinism():
+    W = weights_for(hd.NVFP4, 300, 1024, 7000)
+    h = dev(torch.from_numpy(h_for(1024, 13)))
+    a = hd.quantize_blocks(hd.H_OPT, hd.NVFP4, 16, dev(W), h=h, block_obj=True)
+    b = hd.quantize_blocks(hd.H_OPT, hd.NVFP4, 16, dev(W), h=h, block_obj=True)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    X = synth.activations(3000, 1024, 1, dtype=torch.bfloat16)
+    assert torch.equal(hd.hdiag(dev(X)), hd.hdiag(dev(X)))
+
+
+def test_edge_blocks():
+    # all-zero block, a single non-zero, negative zeros, values far above the
+    # largest scale, subnormal bf16 values, and a block on a grid point
+    rows = [
+        [0.0] * 32,
+        [0.0] * 31 + [0.013],
+        [-0.0] * 16 + [0.0] * 16,
+        [3e30, -2e30] + [1.0] * 30,
+        [1e-40, -3e-39, 2e-38] + [0.0] * 29,
+        [0.0078125 * q for q in ([0, 0.5, 1, 1.5, 2, 3, 4, 6] * 4)],
+    ]
+    W = torch.tensor(rows, dtype=torch.float32).to(torch.bfloat16)
+    h = np.ones(32, np.float32)
+    for fmt in FMTS:
+        for m in (hd.NAIVE, hd.SSE_OPT, hd.H_OPT):
+            c_o, s_o, _ = oracle.quantize(m, fmt, 32, synth.bits(W), h=h)
+            c_g, s_g, _ = hd.quantize_blocks(m, fmt, 32, dev(W), h=dev(torch.from_numpy(h)))
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(npy(s_g), s_o, err_msg="fmt %d method %d" % (fmt, m))
+            np.testing.assert_array_equal(npy(c_g), c_o, err_msg="fmt %d method %d" % (fmt, m))
+
+
+def test_invalid_call_raises():
+    W = dev(torch.zeros(4, 40, dtype=torch.bfloat16))
+    with pytest.raises(hd.HdiagError):
+        hd.quantize_blocks(hd.SSE_OPT, hd.NVFP4, 16, W)
