@@ -10,13 +10,13 @@
 //   reduced in a fixed order by a final one-workgroup kernel.
 //
 // GEMM tiling (gfx950, v_mfma_f32_32x32x16_bf16, wave64):
-//   - workgroup = 4 waves, macro tile 128 rows of X x 128 rows of W, and the
+//   - workgroup = 8 waves, macro tile 256 rows of X x 128 rows of W, and the
 //     same 128 rows of dW-hi and dW-lo: the X tile is loaded once and feeds
-//     all three products;
+//     all three products (640 staged rows per 256 x 128 x 3 products);
 //   - wave (wm, wn): 64 rows of X x 64 rows of W, as 2 x 2 MFMA tiles of
 //     32 x 32 for Y and 2 x 2 for D (hi and lo accumulate into the same D
 //     tiles) -> 128 fp32 accumulators per lane, 12 MFMAs per 16 of K;
-//   - K is walked 32 at a time through two LDS stages (80 KB, dynamic; global
+//   - K is walked 32 at a time through two LDS stages (100 KB, dynamic; global
 //     loads for step k+1 are in flight while step k multiplies); LDS rows are
 //     padded to 80 bytes so the 16-byte fragment reads of 8 consecutive lanes
 //     hit distinct bank groups;
@@ -31,7 +31,7 @@ namespace hd {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-static constexpr int OE_TM = 128;     // X rows per tile
+static constexpr int OE_TM = 256;     // X rows per tile
 static constexpr int OE_TN = 128;     // W rows per tile (and as many dW rows)
 static constexpr int OE_TK = 32;      // K per stage
 static constexpr int OE_PITCH = 40;   // bf16 per LDS row (32 + 8 padding)
@@ -74,15 +74,16 @@ __global__ __launch_bounds__(256) void delta_kernel(const bf16_t *__restrict__ W
 // --------------------------------------------------------------- MFMA GEMM --
 static constexpr int OE_BROWS = 3 * OE_TN;                         // W, hi, lo panels
 static constexpr int OE_STAGE = (OE_TM + OE_BROWS) * OE_PITCH;     // bf16 per LDS stage
+static constexpr int OE_THREADS = 512;                             // 8 waves: 4 (X rows) x 2 (W rows)
 static constexpr size_t OE_LDS_BYTES = 2 * OE_STAGE * sizeof(bf16_t);
 
-__global__ __launch_bounds__(256) void outerr_mfma(const bf16_t *__restrict__ X, const bf16_t *__restrict__ W,
+__global__ __launch_bounds__(OE_THREADS, 1) void outerr_mfma(const bf16_t *__restrict__ X, const bf16_t *__restrict__ W,
                                                    const bf16_t *__restrict__ dhi, const bf16_t *__restrict__ dlo,
                                                    int64_t M, int64_t N, int64_t K, int mt, int nt,
                                                    double *__restrict__ part)
 {
     extern __shared__ __attribute__((aligned(16))) bf16_t lds[];
-    __shared__ double red[2][4];
+    __shared__ double red[2][8];
 
     // tile index: XCD-aware remap, then 8 X tiles per W tile
     const int nblk = mt * nt;
@@ -98,40 +99,36 @@ __global__ __launch_bounds__(256) void outerr_mfma(const bf16_t *__restrict__ X,
     const int64_t m0 = (int64_t)tm * OE_TM, n0 = (int64_t)tn * OE_TN;
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int wm = wv & 1, wn = wv >> 1;  // 64 rows of X x 64 rows of W / dW
+    const int wm = wv & 3, wn = wv >> 2;  // 64 rows of X x 64 rows of W / dW
 
-    // global -> register staging, 16-byte chunks: X tile 128 x 32 (2 per
-    // thread), the three 128 x 32 B panels (6 per thread)
-    uint4 ra[2], rb[6];
-    auto gload = [&](int64_t k0) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int q = tid + 256 * i, r = q >> 2, kc = q & 3;
-            const int64_t m = m0 + r;
-            ra[i] = m < M ? *reinterpret_cast<const uint4 *>(X + m * K + k0 + kc * 8) : make_uint4(0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < 6; ++i) {
-            const int q = tid + 256 * i, r = q >> 2, kc = q & 3;
-            const int p = r / OE_TN, rr = r % OE_TN;
-            const int64_t n = n0 + rr;
-            const bf16_t *src = p == 0 ? W : (p == 1 ? dhi : dlo);
-            rb[i] = n < N ? *reinterpret_cast<const uint4 *>(src + n * K + k0 + kc * 8) : make_uint4(0, 0, 0, 0);
-        }
-    };
-    auto swrite = [&](int buf) {
-        bf16_t *base = lds + buf * OE_STAGE;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int q = tid + 256 * i, r = q >> 2, kc = q & 3;
-            *reinterpret_cast<uint4 *>(base + r * OE_PITCH + kc * 8) = ra[i];
-        }
-#pragma unroll
-        for (int i = 0; i < 6; ++i) {
-            const int q = tid + 256 * i, r = q >> 2, kc = q & 3;
-            *reinterpret_cast<uint4 *>(base + (OE_TM + r) * OE_PITCH + kc * 8) = rb[i];
-        }
-    };
+    // global -> register staging, 16-byte chunks: X tile 256 x 32 (2 per
+    // thread), the three 128 x 32 B panels (3 per thread; chunk i of a thread
+    // is row 128 i + tid / 4 of the 384 B rows, i.e. panel i)
+    const int sr = tid >> 2, sk = (tid & 3) * 8;
+    const bf16_t *const panel[3] = {W, dhi, dlo};
+    uint4 ra[2], rb[3];
+#define OE_GLOAD(k0)                                                                                       \
+    do {                                                                                                   \
+        _Pragma("unroll") for (int i = 0; i < 2; ++i)                                                      \
+        {                                                                                                  \
+            const int64_t m = m0 + 128 * i + sr;                                                           \
+            ra[i] = m < M ? *reinterpret_cast<const uint4 *>(X + m * K + (k0) + sk) : make_uint4(0, 0, 0, 0); \
+        }                                                                                                  \
+        _Pragma("unroll") for (int i = 0; i < 3; ++i)                                                      \
+        {                                                                                                  \
+            const int64_t n = n0 + sr;                                                                     \
+            rb[i] = n < N ? *reinterpret_cast<const uint4 *>(panel[i] + n * K + (k0) + sk)                 \
+                          : make_uint4(0, 0, 0, 0);                                                        \
+        }                                                                                                  \
+    } while (0)
+#define OE_SWRITE(buf)                                                                                     \
+    do {                                                                                                   \
+        bf16_t *base_ = lds + (buf) * OE_STAGE;                                                            \
+        _Pragma("unroll") for (int i = 0; i < 2; ++i)                                                      \
+            *reinterpret_cast<uint4 *>(base_ + (128 * i + sr) * OE_PITCH + sk) = ra[i];                    \
+        _Pragma("unroll") for (int i = 0; i < 3; ++i)                                                      \
+            *reinterpret_cast<uint4 *>(base_ + (OE_TM + 128 * i + sr) * OE_PITCH + sk) = rb[i];            \
+    } while (0)
 
     f32x16_t accy[2][2], accd[2][2];
 #pragma unroll
@@ -145,13 +142,13 @@ __global__ __launch_bounds__(256) void outerr_mfma(const bf16_t *__restrict__ X,
             }
 
     const int ksteps = (int)(K / OE_TK);
-    gload(0);
-    swrite(0);
+    OE_GLOAD(0);
+    OE_SWRITE(0);
     __syncthreads();
     const int fr = lane & 31, fk = (lane >> 5) * 8;
     for (int ks = 0; ks < ksteps; ++ks) {
         const int buf = ks & 1;
-        if (ks + 1 < ksteps) gload((int64_t)(ks + 1) * OE_TK);
+        if (ks + 1 < ksteps) OE_GLOAD((int64_t)(ks + 1) * OE_TK);
         const bf16_t *base = lds + buf * OE_STAGE;
 #pragma unroll
         for (int kk = 0; kk < OE_TK; kk += 16) {
@@ -175,7 +172,7 @@ __global__ __launch_bounds__(256) void outerr_mfma(const bf16_t *__restrict__ X,
                     accd[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bl[j], accd[i][j], 0, 0, 0);
                 }
         }
-        if (ks + 1 < ksteps) swrite(buf ^ 1);
+        if (ks + 1 < ksteps) OE_SWRITE(buf ^ 1);
         __syncthreads();
     }
 
@@ -201,9 +198,16 @@ __global__ __launch_bounds__(256) void outerr_mfma(const bf16_t *__restrict__ X,
     }
     __syncthreads();
     if (tid == 0) {
-        part[2 * (int64_t)blockIdx.x] = (red[0][0] + red[0][1]) + (red[0][2] + red[0][3]);
-        part[2 * (int64_t)blockIdx.x + 1] = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
+        double a = 0.0, b = 0.0;
+        for (int w = 0; w < 8; ++w) {
+            a += red[0][w];
+            b += red[1][w];
+        }
+        part[2 * (int64_t)blockIdx.x] = a;
+        part[2 * (int64_t)blockIdx.x + 1] = b;
     }
+#undef OE_GLOAD
+#undef OE_SWRITE
 }
 
 // ------------------------------------------------------ float32 VALU path --
@@ -298,7 +302,7 @@ hipError_t launch_output_error(const void *X, int xdt, int64_t M, const void *W,
             hipError_t e = hipFuncSetAttribute((const void *)outerr_mfma, hipFuncAttributeMaxDynamicSharedMemorySize,
                                                (int)OE_LDS_BYTES);
             if (e != hipSuccess) return e;
-            outerr_mfma<<<(unsigned)nb, 256, OE_LDS_BYTES, st>>>((const bf16_t *)X, (const bf16_t *)W, dhi, dlo, M,
+            outerr_mfma<<<(unsigned)nb, OE_THREADS, OE_LDS_BYTES, st>>>((const bf16_t *)X, (const bf16_t *)W, dhi, dlo, M,
                                                                   N, K, mt, nt, part);
         }
         outerr_final<<<1, 256, 0, st>>>(part, nb, out, sums);
