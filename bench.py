@@ -7,7 +7,8 @@ with per-row lognormal gain for the down_proj weight) and calibration X
 16384 x 9728 bf16 (N(0,1), 8 outlier channels x 50):
     hdiag(X), then for B in {32, 64, 128, 256} and each of Naive, SSE-Optimal,
     H-Optimal: quantize_blocks (scale choice + encode), dequantize, weight
-    error and output error.
+    error and output error (||X W^T|| is computed by the first output error of
+    the step and passed to the other eleven).
 value = 12 quantisations x 2560 x 9728 weights / step time, in Gweights/s.
 Inputs are resident in HBM before timing starts.  Per-call GPU times come from
 HIP events recorded on the stream the kernels run on, over the timed steps.
@@ -34,6 +35,36 @@ VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 SEARCH_OPS = {"sse": 6, "h": 7}
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "int8_down_proj_2560x9728_hbm_traffic.md")
+
+
+def source_hash():
+    """Hash of the HIP sources; counter-derived traffic is valid only for the
+    kernels it was measured on."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "block_scaled_precision_hdiag_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """Per-stage HBM bytes from the committed rocprofv3 --pmc record, or {} if
+    the kernels changed since it was taken."""
+    try:
+        with open(TRAFFIC_PROFILE) as f:
+            for line in f:
+                if line.startswith("traffic-json:"):
+                    rec = json.loads(line.split(":", 1)[1])
+                    return rec["stages"] if rec.get("source_hash") == source_hash() else {}
+    except OSError:
+        pass
+    return {}
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -41,6 +72,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=8, help="rows of W in the CPU sample")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="before timing, run one device copy of this many MB (a known-size kernel that "
+                         "calibrates HBM byte counters)")
     return ap.parse_args()
 
 
@@ -83,6 +117,17 @@ def main():
     Wq = torch.empty((N, K), dtype=torch.float32, device=dev)
     werr = torch.empty((len(blocks), 3), dtype=torch.float64, device=dev)
     oerr = torch.empty((len(blocks), 3), dtype=torch.float64, device=dev)
+    osums = torch.empty(2, dtype=torch.float64, device=dev)  # ||X Wq^T - X W^T||^2, ||X W^T||^2
+
+    if args.copy_probe_mb:
+        # a plain device-to-device copy of a known size (hipMemcpyAsync runs it
+        # as one copy kernel): reads and writes args.copy_probe_mb MiB
+        src = torch.empty(args.copy_probe_mb << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     events = []  # (stage, B, start, end) during timed steps
 
@@ -107,8 +152,18 @@ def main():
                 timed("dequantize", B, lambda: hd.dequantize(fmt, B, codes[B], scales[B], N, K, out=Wq), rec)
                 timed("weight_error", B, lambda: werr[bi, mi].copy_(hd.weight_error(W, Wq, workspace=ws_w)[0]),
                       rec)
-                timed("output_error", B, lambda: oerr[bi, mi].copy_(hd.output_error(X, W, Wq, workspace=ws_o)[0]),
-                      rec)
+                if bi == 0 and mi == 0:
+                    # ||X W^T||^2 depends on X and W only: the step's first
+                    # output error computes it, the other eleven reuse it
+                    def oe_first():
+                        o, sm = hd.output_error(X, W, Wq, sums=True, workspace=ws_o)
+                        oerr[bi, mi].copy_(o[0])
+                        osums.copy_(sm)
+                    timed("output_error", B, oe_first, rec)
+                else:
+                    timed("output_error_given_ref", B,
+                          lambda: oerr[bi, mi].copy_(hd.output_error_given_ref(X, W, Wq, osums[1:2],
+                                                                               workspace=ws_o)[0]), rec)
 
     for _ in range(args.warmup):
         step(False)
@@ -136,6 +191,7 @@ def main():
         "dequantize": ("hbm", sum(N * K + N * K // B + N * K * 4 for B in blocks) / len(blocks)),
         "weight_error": ("hbm", bytes_w + N * K * 4),
         "output_error": ("mfma", 4.0 * M * N * K),
+        "output_error_given_ref": ("mfma", 2.0 * M * N * K),
         "search_sse": ("alu", N * K * n_cand * SEARCH_OPS["sse"]),
         "search_h": ("alu", N * K * n_cand * SEARCH_OPS["h"]),
     }
@@ -156,7 +212,9 @@ def main():
     dominant = max(per_step, key=per_step.get)
     roofline = dict(stages[dominant])
     roofline["kernel"] = dominant
-    roofline["traffic"] = None
+    tr = measured_traffic().get(dominant)
+    roofline["traffic"] = round(tr["read_bytes"] + tr["write_bytes"]) if tr else None
+    roofline["traffic_unit"] = "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated)"
     roofline.pop("avg_ms")
 
     search_gwps = {s: round(N * K / (avg[s] * 1e-3) / 1e9, 3) for s in avg if s.startswith("search") or s == "naive"}

@@ -28,6 +28,7 @@ METHODS = {"naive": NAIVE, "sse": SSE_OPT, "h": H_OPT}
 
 EXPORTS = ["hdiag", "hdiag_workspace_size", "quantize_blocks", "encode_blocks", "dequantize",
            "weight_error", "weight_error_workspace_size", "output_error", "output_error_workspace_size",
+           "output_error_given_ref",
            "hdiag_strerror", "hdiag_last_error", "hdiag_format_info", "hdiag_version"]
 
 
@@ -61,6 +62,7 @@ def lib():
         L.output_error_workspace_size.argtypes = [i64, i64, i64]
         L.output_error_workspace_size.restype = sz
         L.output_error.argtypes = [P, i32, i64, P, i32, P, i32, i64, i64, P, P, P, sz, P]
+        L.output_error_given_ref.argtypes = [P, i32, i64, P, i32, P, i32, i64, i64, P, P, P, P, sz, P]
         L.hdiag_strerror.argtypes = [i32]
         L.hdiag_strerror.restype = ctypes.c_char_p
         L.hdiag_last_error.argtypes = []
@@ -69,7 +71,7 @@ def lib():
         L.hdiag_version.argtypes = []
         L.hdiag_version.restype = ctypes.c_char_p
         for name in ("hdiag", "quantize_blocks", "encode_blocks", "dequantize", "weight_error",
-                     "output_error", "hdiag_format_info"):
+                     "output_error", "output_error_given_ref", "hdiag_format_info"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -186,6 +188,22 @@ def output_error(X, W, Wq, sums=False, workspace=None):
     ws = workspace if workspace is not None else torch.empty(max(need, 16), dtype=torch.uint8, device=d)
     _check(lib().output_error(_ptr(X), _dt(X), M, _ptr(W), _dt(W), _ptr(Wq), _dt(Wq), N, K, _ptr(out), _ptr(s),
                               _ptr(ws), ws.numel(), _stream(d)), "output_error")
+    return (out, s) if sums else out
+
+
+def output_error_given_ref(X, W, Wq, ysq, sums=False, workspace=None):
+    """output_error with ||X W^T||^2 given as the float64 device scalar ysq
+    (e.g. sums[1] of an earlier output_error on the same X and W)."""
+    d = _dev(X)
+    M, K = X.shape
+    N = W.shape[0]
+    out = torch.empty(1, dtype=torch.float64, device=d)
+    s = torch.empty(2, dtype=torch.float64, device=d) if sums else None
+    need = output_error_workspace_size(M, N, K)
+    ws = workspace if workspace is not None else torch.empty(max(need, 16), dtype=torch.uint8, device=d)
+    _check(lib().output_error_given_ref(_ptr(X), _dt(X), M, _ptr(W), _dt(W), _ptr(Wq), _dt(Wq), N, K, _ptr(ysq),
+                                        _ptr(out), _ptr(s), _ptr(ws), ws.numel(), _stream(d)),
+           "output_error_given_ref")
     return (out, s) if sums else out
 
 

@@ -137,6 +137,7 @@ hd_status quantize_blocks(hd_method method, hd_format fmt, int32_t B, const void
     HD_CHECK_PTR(W, true);
     HD_CHECK_PTR(codes, true);
     if (scales == nullptr) return fail(HD_ERR_INVALID_ARG, "scales is NULL");
+    if ((uintptr_t)scales & 3u) return fail(HD_ERR_INVALID_ARG, "scales is not 4-byte aligned");
     if (h != nullptr && !aligned16(h)) return fail(HD_ERR_INVALID_ARG, "h is not 16-byte aligned");
     if (block_obj != nullptr && ((uintptr_t)block_obj & 3u)) return fail(HD_ERR_INVALID_ARG, "block_obj misaligned");
     hipStream_t st = (hipStream_t)stream;
@@ -204,9 +205,10 @@ size_t output_error_workspace_size(int64_t M, int64_t N, int64_t K)
     return a > b ? a : b;
 }
 
-hd_status output_error(const void *X, hd_dtype xt, int64_t M, const void *W, hd_dtype wt, const void *Wq,
-                       hd_dtype qt, int64_t N, int64_t K, double *out, double *sums, void *ws, size_t ws_bytes,
-                       void *stream)
+static hd_status output_error_common(const void *X, hd_dtype xt, int64_t M, const void *W, hd_dtype wt,
+                                     const void *Wq, hd_dtype qt, int64_t N, int64_t K, const double *ysq,
+                                     double *out, double *sums, void *ws, size_t ws_bytes, void *stream,
+                                     const char *what)
 {
     HD_REQUIRE(valid_dtype(xt) && valid_dtype(wt) && valid_dtype(qt), "unknown dtype");
     HD_REQUIRE(M >= 0 && N >= 0 && K >= 0, "negative size");
@@ -219,8 +221,25 @@ hd_status output_error(const void *X, hd_dtype xt, int64_t M, const void *W, hd_
     HD_CHECK_PTR(X, M * K > 0);
     HD_CHECK_PTR(W, N * K > 0);
     HD_CHECK_PTR(Wq, N * K > 0);
-    return hip_status(hd::launch_output_error(X, xt, M, W, wt, Wq, qt, N, K, out, sums, ws, (hipStream_t)stream),
-                      "output_error");
+    return hip_status(
+        hd::launch_output_error(X, xt, M, W, wt, Wq, qt, N, K, ysq, out, sums, ws, (hipStream_t)stream), what);
+}
+
+hd_status output_error(const void *X, hd_dtype xt, int64_t M, const void *W, hd_dtype wt, const void *Wq,
+                       hd_dtype qt, int64_t N, int64_t K, double *out, double *sums, void *ws, size_t ws_bytes,
+                       void *stream)
+{
+    return output_error_common(X, xt, M, W, wt, Wq, qt, N, K, nullptr, out, sums, ws, ws_bytes, stream,
+                               "output_error");
+}
+
+hd_status output_error_given_ref(const void *X, hd_dtype xt, int64_t M, const void *W, hd_dtype wt,
+                                 const void *Wq, hd_dtype qt, int64_t N, int64_t K, const double *ysq,
+                                 double *out, double *sums, void *ws, size_t ws_bytes, void *stream)
+{
+    HD_REQUIRE(ysq != nullptr, "ysq is NULL");
+    return output_error_common(X, xt, M, W, wt, Wq, qt, N, K, ysq, out, sums, ws, ws_bytes, stream,
+                               "output_error_given_ref");
 }
 
 }  // extern "C"

@@ -10,7 +10,7 @@ namespace hd {
 // r = fl32(1/s).  Writes the code of each element (sign included) and returns
 // the objective sum_j om_j (w_j - fl32(s q_j))^2 of the eight, in float64 and
 // element order (om == NULL: unweighted).
-template <int EK, int SK, bool ONE_STEP>
+template <int EK, int SK, bool ONE_STEP, bool WANT_OBJ = true>
 __device__ __forceinline__ double encode8(const float *w, float s, float r, const double *om,
                                           uint32_t *code)
 {
@@ -21,9 +21,11 @@ __device__ __forceinline__ double encode8(const float *w, float s, float r, cons
         const float x = (s != 0.0f) ? quotient<SK, ONE_STEP>(a, s, r) : 0.0f;
         const float y = round_elem<EK>(x);
         code[j] = elem_code<EK>(elem_index<EK>(y), __builtin_signbitf(w[j]) != 0);
-        const float wq = s * y;  // fl32(s * val(q))
-        const double d = (double)a - (double)wq;
-        obj += (om ? om[j] : 1.0) * (d * d);
+        if (WANT_OBJ) {
+            const float wq = s * y;  // fl32(s * val(q))
+            const double d = (double)a - (double)wq;
+            obj += (om ? om[j] : 1.0) * (d * d);
+        }
     }
     return obj;
 }

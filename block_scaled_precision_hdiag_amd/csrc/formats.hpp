@@ -130,10 +130,10 @@ __device__ __forceinline__ uint32_t elem_index(float y)
 {
     if (EK == ELEM_INT8) return (uint32_t)y;
     if (EK == ELEM_E2M1) {
-        // 0, .5 -> 0, 1 ; 1, 1.5 -> 2, 3 ; 2, 3 -> 4, 5 ; 4, 6 -> 6, 7
-        if (y < 1.0f) return y > 0.0f ? 1u : 0u;
-        const uint32_t u = f_bits(y);
-        return 2u + 2u * ((u >> 23) - 127u) + ((u >> 22) & 1u);
+        // the top 10 bits of 1, 1.5, 2, 3, 4, 6 are 0xFE..0x103, i.e. the code
+        // plus 0xFC; 0.5 (0xFC) and 0 need the floor of 1 / 0
+        const int hi = (int)(f_bits(y) >> 22) - 0xFC;
+        return (uint32_t)max(hi, y > 0.0f ? 1 : 0);
     }
     if (y < 0x1p-6f) return (uint32_t)(y * 512.0f);     // subnormal codes 0..7
     const uint32_t u = f_bits(y);

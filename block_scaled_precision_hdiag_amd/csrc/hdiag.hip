@@ -23,7 +23,7 @@ static void hdiag_shape(int64_t M, int64_t K, int64_t *col_tiles, int64_t *chunk
     int64_t ct = (K + cols - 1) / cols;
     if (ct < 1) ct = 1;
     int64_t r = (M + 63) / 64;                 // at least 64 rows per chunk
-    const int64_t want = (4096 + ct - 1) / ct; // ~4096 workgroups in flight
+    const int64_t want = (1024 + ct - 1) / ct; // ~1024 workgroups (16 waves per CU): few partials
     if (r > want) r = want;
     if (r < 1) r = 1;
     *col_tiles = ct;

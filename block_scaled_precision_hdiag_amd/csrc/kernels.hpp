@@ -39,8 +39,9 @@ hipError_t launch_hdiag(const void *X, int xdt, int64_t M, int64_t K, float *h, 
 
 size_t output_error_ws(int64_t M, int64_t N, int64_t K, bool mfma);
 bool output_error_uses_mfma(int xdt, int wdt, int64_t K);
+// ysq: optional device double holding ||X W^T||^2; when given, Y is not computed.
 hipError_t launch_output_error(const void *X, int xdt, int64_t M, const void *W, int wdt, const void *Wq,
-                               int qdt, int64_t N, int64_t K, double *out, double *sums, void *ws,
-                               hipStream_t st);
+                               int qdt, int64_t N, int64_t K, const double *ysq, double *out, double *sums,
+                               void *ws, hipStream_t st);
 
 }  // namespace hd

@@ -72,11 +72,13 @@ __global__ __launch_bounds__(256) void delta_kernel(const bf16_t *__restrict__ W
 }
 
 // --------------------------------------------------------------- MFMA GEMM --
-static constexpr int OE_BROWS = 3 * OE_TN;                         // W, hi, lo panels
-static constexpr int OE_STAGE = (OE_TM + OE_BROWS) * OE_PITCH;     // bf16 per LDS stage
-static constexpr int OE_THREADS = 512;                             // 8 waves: 4 (X rows) x 2 (W rows)
-static constexpr size_t OE_LDS_BYTES = 2 * OE_STAGE * sizeof(bf16_t);
+static constexpr int OE_THREADS = 512;  // 8 waves: 4 (X rows) x 2 (W rows)
+// LDS stage: the X tile and NP panels of 128 B rows (W, hi, lo; or hi, lo
+// when ||X W^T||^2 is given and Y is not needed)
+__host__ __device__ constexpr int oe_stage(int np) { return (OE_TM + np * OE_TN) * OE_PITCH; }
+constexpr size_t oe_lds_bytes(int np) { return 2 * (size_t)oe_stage(np) * sizeof(bf16_t); }
 
+template <bool WITH_Y>
 __global__ __launch_bounds__(OE_THREADS, 1) void outerr_mfma(const bf16_t *__restrict__ X, const bf16_t *__restrict__ W,
                                                    const bf16_t *__restrict__ dhi, const bf16_t *__restrict__ dlo,
                                                    int64_t M, int64_t N, int64_t K, int mt, int nt,
@@ -102,11 +104,14 @@ __global__ __launch_bounds__(OE_THREADS, 1) void outerr_mfma(const bf16_t *__res
     const int wm = wv & 3, wn = wv >> 2;  // 64 rows of X x 64 rows of W / dW
 
     // global -> register staging, 16-byte chunks: X tile 256 x 32 (2 per
-    // thread), the three 128 x 32 B panels (3 per thread; chunk i of a thread
-    // is row 128 i + tid / 4 of the 384 B rows, i.e. panel i)
+    // thread), the NP 128 x 32 B panels (one chunk per thread and panel: row
+    // tid / 4 of panel i)
+    constexpr int NP = WITH_Y ? 3 : 2;
+    constexpr int OE_STAGE = oe_stage(NP);
+    constexpr int PH = WITH_Y ? 1 : 0;  // LDS panel index of dW-hi
     const int sr = tid >> 2, sk = (tid & 3) * 8;
-    const bf16_t *const panel[3] = {W, dhi, dlo};
-    uint4 ra[2], rb[3];
+    const bf16_t *const panel[3] = {WITH_Y ? W : dhi, WITH_Y ? dhi : dlo, dlo};
+    uint4 ra[2], rb[NP];
 #define OE_GLOAD(k0)                                                                                       \
     do {                                                                                                   \
         _Pragma("unroll") for (int i = 0; i < 2; ++i)                                                      \
@@ -114,7 +119,7 @@ __global__ __launch_bounds__(OE_THREADS, 1) void outerr_mfma(const bf16_t *__res
             const int64_t m = m0 + 128 * i + sr;                                                           \
             ra[i] = m < M ? *reinterpret_cast<const uint4 *>(X + m * K + (k0) + sk) : make_uint4(0, 0, 0, 0); \
         }                                                                                                  \
-        _Pragma("unroll") for (int i = 0; i < 3; ++i)                                                      \
+        _Pragma("unroll") for (int i = 0; i < NP; ++i)                                                     \
         {                                                                                                  \
             const int64_t n = n0 + sr;                                                                     \
             rb[i] = n < N ? *reinterpret_cast<const uint4 *>(panel[i] + n * K + (k0) + sk)                 \
@@ -126,7 +131,7 @@ __global__ __launch_bounds__(OE_THREADS, 1) void outerr_mfma(const bf16_t *__res
         bf16_t *base_ = lds + (buf) * OE_STAGE;                                                            \
         _Pragma("unroll") for (int i = 0; i < 2; ++i)                                                      \
             *reinterpret_cast<uint4 *>(base_ + (128 * i + sr) * OE_PITCH + sk) = ra[i];                    \
-        _Pragma("unroll") for (int i = 0; i < 3; ++i)                                                      \
+        _Pragma("unroll") for (int i = 0; i < NP; ++i)                                                     \
             *reinterpret_cast<uint4 *>(base_ + (OE_TM + 128 * i + sr) * OE_PITCH + sk) = rb[i];            \
     } while (0)
 
@@ -159,15 +164,16 @@ __global__ __launch_bounds__(OE_THREADS, 1) void outerr_mfma(const bf16_t *__res
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const int br = OE_TM + wn * 64 + j * 32 + fr;
-                bw[j] = *reinterpret_cast<const bf16x8_t *>(base + br * OE_PITCH + kk + fk);
-                bh[j] = *reinterpret_cast<const bf16x8_t *>(base + (br + OE_TN) * OE_PITCH + kk + fk);
-                bl[j] = *reinterpret_cast<const bf16x8_t *>(base + (br + 2 * OE_TN) * OE_PITCH + kk + fk);
+                if (WITH_Y) bw[j] = *reinterpret_cast<const bf16x8_t *>(base + br * OE_PITCH + kk + fk);
+                bh[j] = *reinterpret_cast<const bf16x8_t *>(base + (br + PH * OE_TN) * OE_PITCH + kk + fk);
+                bl[j] = *reinterpret_cast<const bf16x8_t *>(base + (br + (PH + 1) * OE_TN) * OE_PITCH + kk + fk);
             }
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
-                    accy[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bw[j], accy[i][j], 0, 0, 0);
+                    if (WITH_Y)
+                        accy[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bw[j], accy[i][j], 0, 0, 0);
                     accd[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bh[j], accd[i][j], 0, 0, 0);
                     accd[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bl[j], accd[i][j], 0, 0, 0);
                 }
@@ -184,7 +190,7 @@ __global__ __launch_bounds__(OE_THREADS, 1) void outerr_mfma(const bf16_t *__res
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const double y = (double)accy[i][j][v], d = (double)accd[i][j][v];
-                sy = __builtin_fma(y, y, sy);
+                if (WITH_Y) sy = __builtin_fma(y, y, sy);
                 sd = __builtin_fma(d, d, sd);
             }
 #pragma unroll
@@ -242,7 +248,8 @@ __global__ __launch_bounds__(256) void outerr_valu(const TX *__restrict__ X, con
 }
 
 __global__ __launch_bounds__(256) void outerr_final(const double *__restrict__ part, int64_t n,
-                                                    double *__restrict__ out, double *__restrict__ sums)
+                                                    const double *__restrict__ ysq, double *__restrict__ out,
+                                                    double *__restrict__ sums)
 {
     __shared__ double sh[4];
     double a = 0.0, b = 0.0;
@@ -253,6 +260,7 @@ __global__ __launch_bounds__(256) void outerr_final(const double *__restrict__ p
     a = block_sum_256(a, sh);
     b = block_sum_256(b, sh);
     if (threadIdx.x == 0) {
+        if (ysq) b = *ysq;
         *out = sqrt(a) / sqrt(b);
         if (sums) {
             sums[0] = a;
@@ -279,8 +287,8 @@ size_t output_error_ws(int64_t M, int64_t N, int64_t K, bool mfma)
 }
 
 hipError_t launch_output_error(const void *X, int xdt, int64_t M, const void *W, int wdt, const void *Wq,
-                               int qdt, int64_t N, int64_t K, double *out, double *sums, void *ws,
-                               hipStream_t st)
+                               int qdt, int64_t N, int64_t K, const double *ysq, double *out, double *sums,
+                               void *ws, hipStream_t st)
 {
     const bool mfma = output_error_uses_mfma(xdt, wdt, K);
     int64_t nb = oe_blocks(M, N, K, mfma);
@@ -299,13 +307,23 @@ hipError_t launch_output_error(const void *X, int xdt, int64_t M, const void *W,
         }
         const int mt = (int)((M + OE_TM - 1) / OE_TM), nt = (int)((N + OE_TN - 1) / OE_TN);
         if (nb > 0) {
-            hipError_t e = hipFuncSetAttribute((const void *)outerr_mfma, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               (int)OE_LDS_BYTES);
-            if (e != hipSuccess) return e;
-            outerr_mfma<<<(unsigned)nb, OE_THREADS, OE_LDS_BYTES, st>>>((const bf16_t *)X, (const bf16_t *)W, dhi, dlo, M,
-                                                                  N, K, mt, nt, part);
+            if (ysq) {
+                const size_t lds = oe_lds_bytes(2);
+                hipError_t e = hipFuncSetAttribute((const void *)outerr_mfma<false>,
+                                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+                if (e != hipSuccess) return e;
+                outerr_mfma<false><<<(unsigned)nb, OE_THREADS, lds, st>>>((const bf16_t *)X, (const bf16_t *)W, dhi,
+                                                                          dlo, M, N, K, mt, nt, part);
+            } else {
+                const size_t lds = oe_lds_bytes(3);
+                hipError_t e = hipFuncSetAttribute((const void *)outerr_mfma<true>,
+                                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+                if (e != hipSuccess) return e;
+                outerr_mfma<true><<<(unsigned)nb, OE_THREADS, lds, st>>>((const bf16_t *)X, (const bf16_t *)W, dhi,
+                                                                         dlo, M, N, K, mt, nt, part);
+            }
         }
-        outerr_final<<<1, 256, 0, st>>>(part, nb, out, sums);
+        outerr_final<<<1, 256, 0, st>>>(part, nb, ysq, out, sums);
         return hipGetLastError();
     }
     double *part = reinterpret_cast<double *>(wsb);
@@ -322,7 +340,7 @@ hipError_t launch_output_error(const void *X, int xdt, int64_t M, const void *W,
         }
     }
 #undef HD_OE_VALU
-    outerr_final<<<1, 256, 0, st>>>(part, nb, out, sums);
+    outerr_final<<<1, 256, 0, st>>>(part, nb, ysq, out, sums);
     return hipGetLastError();
 }
 

@@ -1,7 +1,5 @@
 // quant.hip - Naive scale + encode, encode with given scales, dequantize and
-// the weight error.  All HBM-bound streaming kernels: each thread owns 8
-// consecutive weights (one 16-byte bf16 load), a block of B weights is B/8
-// consecutive lanes, and its amax / objective are combined with lane shuffles.
+// the weight error: the HBM-bound streaming kernels of the path.
 #include "encode.hpp"
 #include "kernels.hpp"
 
@@ -11,51 +9,126 @@ namespace hd {
 // Naive ("Is Finer Better?" §2.1: s = Q_scale(amax / C); qwantize "Results",
 // INT8: the amax itself stored as E4M3 and divided by 127) when GIVEN is false;
 // otherwise the scale code of each block comes from scales_in.
-template <int EK, int SK, typename T, int B, bool GIVEN>
+//
+// Each thread owns 32 consecutive weights (four 16-byte bf16 loads) and writes
+// their codes as whole 16-byte stores (32 bytes for INT8 / E4M3, 16 for E2M1):
+// narrower per-lane stores were measured to multiply the bytes written to HBM.
+// Blocks of B <= 32 lie inside one thread (32 / B of them); a block of B > 32
+// spans B / 32 adjacent lanes, combined with shuffles.
+static constexpr int ENC_EPT = 32;
+
+template <int EK, int SK, typename T, int B, bool GIVEN, bool OBJ>
 __global__ __launch_bounds__(256) void encode_kernel(const T *__restrict__ W, int64_t total, int64_t K,
                                                      const float *__restrict__ h,
                                                      const uint8_t *__restrict__ scales_in,
                                                      uint8_t *__restrict__ codes, uint8_t *__restrict__ scales,
                                                      float *__restrict__ block_obj)
 {
-    constexpr int TPB = B / 8;
+    constexpr int TPB = B > ENC_EPT ? B / ENC_EPT : 1;  // lanes per block
+    constexpr int NBT = B < ENC_EPT ? ENC_EPT / B : 1;  // blocks per lane
+    constexpr int EB = B < ENC_EPT ? B : ENC_EPT;       // weights of one block in this lane
     constexpr bool ONE_STEP = sizeof(T) == 2;
-    const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
-    const bool active = e0 < total;  // total % B == 0: a block's lanes agree
-    float w[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (active) load8<T>(W + e0, w);
-    float amax = 0.0f;
+    const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * ENC_EPT;
+    // total % 8 == 0 and total % B == 0: the last thread may own fewer than 32
+    // weights, but whole blocks (and for B > 32 every lane of a block agrees)
+    const int64_t left = total - e0;
+    const bool active = left > 0;
+    const int nv8 = left >= ENC_EPT ? ENC_EPT / 8 : (left > 0 ? (int)(left / 8) : 0);  // valid 8-chunks
+    float w[ENC_EPT];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(w[j]));
-    amax = group_max<TPB>(amax);
-    const int64_t blk = e0 / B;
-    int code;
-    float s;
-    if (GIVEN) {
-        code = active ? (int)scales_in[blk] : 0;
-        const bool valid = SK == SCALE_E8M0 ? code <= 254 : code <= 126;
-        s = valid ? scale_value(SK, code) : 0.0f;
-    } else {
-        code = naive_code<EK, SK>(amax);
-        s = scale_value(SK, code);
+    for (int c = 0; c < ENC_EPT / 8; ++c) {
+        if (c < nv8)
+            load8<T>(W + e0 + 8 * c, w + 8 * c);
+        else
+            for (int j = 0; j < 8; ++j) w[8 * c + j] = 0.0f;
     }
-    const float r = (s != 0.0f) ? 1.0f / s : 0.0f;
-    double om[8];
-    const double *omp = nullptr;
-    if (h != nullptr && active) {
-        const int64_t k0 = e0 % K;
+    double om[OBJ ? ENC_EPT : 1];
+    const bool weighted = OBJ && h != nullptr;
+    if (OBJ && weighted && active) {
+        // rows hold K % 8 == 0 weights: an 8-chunk never crosses a row end
 #pragma unroll
-        for (int j = 0; j < 8; ++j) om[j] = (double)h[k0 + j];
-        omp = om;
+        for (int c = 0; c < ENC_EPT / 8; ++c) {
+            const int64_t k0 = (e0 + 8 * c) % K;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) om[OBJ ? 8 * c + j : 0] = c < nv8 ? (double)h[k0 + j] : 0.0;
+        }
     }
-    uint32_t c[8];
-    double obj = encode8<EK, SK, ONE_STEP>(w, s, r, omp, c);
-    obj = group_sum<TPB>(obj);
+    uint32_t c[ENC_EPT];
+    int code[NBT];
+    double obj[NBT];
+#pragma unroll
+    for (int bb = 0; bb < NBT; ++bb) {
+        float amax = 0.0f;
+#pragma unroll
+        for (int j = 0; j < EB; ++j) amax = fmaxf(amax, fabsf(w[bb * EB + j]));
+        amax = group_max<TPB>(amax);
+        const int64_t blk = (e0 + bb * EB) / B;
+        float s;
+        if (GIVEN) {
+            code[bb] = (bb * EB < 8 * nv8) ? (int)scales_in[blk] : 0;
+            const bool valid = SK == SCALE_E8M0 ? code[bb] <= 254 : code[bb] <= 126;
+            s = valid ? scale_value(SK, code[bb]) : 0.0f;
+        } else {
+            code[bb] = naive_code<EK, SK>(amax);
+            s = scale_value(SK, code[bb]);
+        }
+        const float r = (s != 0.0f) ? 1.0f / s : 0.0f;
+        double o = 0.0;
+#pragma unroll
+        for (int q = 0; q < EB / 8; ++q) {
+            const int j0 = bb * EB + 8 * q;
+            o += encode8<EK, SK, ONE_STEP, OBJ>(w + j0, s, r, (weighted && active) ? om + (OBJ ? j0 : 0) : nullptr,
+                                                c + j0);
+        }
+        obj[bb] = OBJ ? group_sum<TPB>(o) : 0.0;
+    }
     if (!active) return;
-    store_codes8<EK>(codes, e0, c);
+    if (nv8 < ENC_EPT / 8) {  // tail thread: 8-weight stores, then its whole blocks
+        for (int cc = 0; cc < nv8; ++cc) store_codes8<EK>(codes, e0 + 8 * cc, c + 8 * cc);
+        for (int bb = 0; bb < NBT; ++bb) {
+            if (bb * EB >= 8 * nv8) break;
+            const int64_t blk = (e0 + bb * EB) / B;
+            if (!GIVEN) scales[blk] = (uint8_t)code[bb];
+            if (OBJ) block_obj[blk] = (float)obj[bb];
+        }
+        return;
+    }
+    if (EK == ELEM_E2M1) {
+        uint32_t v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[i] = 0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[i] |= (c[8 * i + j] & 15u) << (4 * j);
+        }
+        *reinterpret_cast<uint4 *>(codes + e0 / 2) = make_uint4(v[0], v[1], v[2], v[3]);
+    } else {
+        uint32_t v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            v[i] = (c[4 * i] & 255u) | ((c[4 * i + 1] & 255u) << 8) | ((c[4 * i + 2] & 255u) << 16) |
+                   ((c[4 * i + 3] & 255u) << 24);
+        uint4 *p = reinterpret_cast<uint4 *>(codes + e0);
+        p[0] = make_uint4(v[0], v[1], v[2], v[3]);
+        p[1] = make_uint4(v[4], v[5], v[6], v[7]);
+    }
     if ((threadIdx.x % TPB) == 0) {
-        if (!GIVEN) scales[blk] = (uint8_t)code;
-        if (block_obj) block_obj[blk] = (float)obj;
+        const int64_t blk0 = e0 / B;
+        if (!GIVEN) {
+            if (NBT == 4)
+                *reinterpret_cast<uint32_t *>(scales + blk0) =
+                    (uint32_t)code[0] | ((uint32_t)code[NBT > 1 ? 1 : 0] << 8) |
+                    ((uint32_t)code[NBT > 2 ? 2 : 0] << 16) | ((uint32_t)code[NBT > 3 ? 3 : 0] << 24);
+            else if (NBT == 2)
+                *reinterpret_cast<uint16_t *>(scales + blk0) =
+                    (uint16_t)((uint32_t)code[0] | ((uint32_t)code[NBT > 1 ? 1 : 0] << 8));
+            else
+                scales[blk0] = (uint8_t)code[0];
+        }
+        if (OBJ) {
+#pragma unroll
+            for (int bb = 0; bb < NBT; ++bb) block_obj[blk0 + bb] = (float)obj[bb];
+        }
     }
 }
 
@@ -64,11 +137,14 @@ static hipError_t encode_b(int B, const void *W, int64_t N, int64_t K, const flo
                            uint8_t *codes, uint8_t *scales, float *bo, hipStream_t st)
 {
     const int64_t total = N * K;
-    const dim3 grid((unsigned)((total / 8 + 255) / 256));
+    const dim3 grid((unsigned)((total / ENC_EPT + 255) / 256));
     const T *w = static_cast<const T *>(W);
-#define HD_ENC_CASE(BB)                                                                                  \
-    case BB:                                                                                             \
-        encode_kernel<EK, SK, T, BB, GIVEN><<<grid, 256, 0, st>>>(w, total, K, h, si, codes, scales, bo); \
+#define HD_ENC_CASE(BB)                                                                                      \
+    case BB:                                                                                                 \
+        if (bo)                                                                                              \
+            encode_kernel<EK, SK, T, BB, GIVEN, true><<<grid, 256, 0, st>>>(w, total, K, h, si, codes, scales, bo);  \
+        else                                                                                                 \
+            encode_kernel<EK, SK, T, BB, GIVEN, false><<<grid, 256, 0, st>>>(w, total, K, h, si, codes, scales, bo); \
         break;
     switch (B) {
         HD_ENC_CASE(8)

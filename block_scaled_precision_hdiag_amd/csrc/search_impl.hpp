@@ -141,7 +141,7 @@ __global__ __launch_bounds__(256) void search_kernel(const T *__restrict__ W, in
 #pragma unroll
         for (int j = 0; j < 8; ++j) w[j] = ((negmask >> (8 * c8 + j)) & 1u) ? -a[8 * c8 + j] : a[8 * c8 + j];
         uint32_t cd[8];
-        encode8<EK, SK, ONE_STEP>(w, s, r, nullptr, cd);
+        encode8<EK, SK, ONE_STEP, false>(w, s, r, nullptr, cd);
         store_codes8<EK>(codes, e0 + 8 * c8, cd);
     }
     if (seg == 0) {

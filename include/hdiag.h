@@ -165,6 +165,17 @@ hd_status output_error(const void *X, hd_dtype xt, int64_t M, const void *W, hd_
                        const void *Wq, hd_dtype qt, int64_t N, int64_t K, double *out, double *sums,
                        void *ws, size_t ws_bytes, void *stream);
 
+/* output_error with ||X W^T||_F^2 already known: ysq is a device double
+ * holding it (e.g. sums[1] of an earlier output_error on the same X and W).
+ * Only D = X dW^T is computed (two of the three bf16 products); the result is
+ * sqrt(sum D^2) / sqrt(*ysq), and sums (optional) receives {sum D^2, *ysq}.
+ * Arguments, workspace and errors as output_error, plus HD_ERR_INVALID_ARG for
+ * a NULL ysq.  For callers that score several quantisations of one W against
+ * the same X. */
+hd_status output_error_given_ref(const void *X, hd_dtype xt, int64_t M, const void *W, hd_dtype wt,
+                                 const void *Wq, hd_dtype qt, int64_t N, int64_t K, const double *ysq,
+                                 double *out, double *sums, void *ws, size_t ws_bytes, void *stream);
+
 /* ------------------------------------------------------------ utilities --- */
 
 /* Static description of a status code. */

@@ -208,6 +208,22 @@ def test_output_error_parity(M, N, K):
     np.testing.assert_allclose(npy(sums), [d_o, y_o], rtol=1e-4)
 
 
+@pytest.mark.parametrize("M,N,K", [(300, 200, 512), (64, 64, 16)])
+def test_output_error_given_ref(M, N, K):
+    """Given ||X W^T||^2 from a first call, the D-only path returns the same
+    sums: its D products are the same MFMAs in the same order."""
+    W = weights_for(hd.NVFP4, N, K, 5100 + M)
+    X = synth.activations(M, K, 78 + N, n_out=2, out_gain=50.0, idx_seed=3, dtype=torch.bfloat16)
+    c_g, s_g, _ = hd.quantize_blocks(hd.H_OPT, hd.NVFP4, 16, dev(W), h=hd.hdiag(dev(X)))
+    Wq = hd.dequantize(hd.NVFP4, 16, c_g, s_g, N, K)
+    oe, sums = hd.output_error(dev(X), dev(W), Wq, sums=True)
+    oe2, sums2 = hd.output_error_given_ref(dev(X), dev(W), Wq, sums[1:2].clone(), sums=True)
+    torch.cuda.synchronize()
+    assert torch.equal(sums, sums2) and torch.equal(oe, oe2)
+    oe_o = oracle.output_error(synth.bits(X), synth.bits(W), npy(Wq))
+    assert oe2.item() == pytest.approx(oe_o, rel=1e-4)
+
+
 def test_output_error_identity_equals_weight_error():
     K, N = 256, 96
     W = weights_for(hd.NVFP4, N, K, 6000)
