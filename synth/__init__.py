@@ -104,7 +104,8 @@ CONFIGS = {
 
 def config_inputs(i: int, rows=None, x_rows=None):
     """(W, X) of configuration i; rows / x_rows cut W / X to their first rows
-    (the draws of the kept rows are the same as in the full tensors)."""
+    (the draws of the kept rows are the same as in the full tensors);
+    x_rows=0 skips X (returned as None)."""
     c = CONFIGS[i]
     wp = dict(c["W"])
     N = wp.pop("N")
@@ -114,7 +115,7 @@ def config_inputs(i: int, rows=None, x_rows=None):
     if rows is not None:
         W = W[:rows].contiguous()
     X = None
-    if c["X"] is not None:
+    if c["X"] is not None and x_rows != 0:
         xp = dict(c["X"])
         M = xp.pop("M") if x_rows is None else min(x_rows, xp.pop("M"))
         xp.pop("M", None)
