@@ -15,16 +15,45 @@ __device__ __forceinline__ double encode8(const float *w, float s, float r, cons
                                           uint32_t *code)
 {
     double obj = 0.0;
+    if (EK == ELEM_INT8) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float a = fabsf(w[j]);
+            const float x = (s != 0.0f) ? quotient<SK, ONE_STEP>(a, s, r) : 0.0f;
+            const float y = round_elem<EK>(x);
+            code[j] = elem_code<EK>(elem_index<EK>(y), __builtin_signbitf(w[j]) != 0);
+            if (WANT_OBJ) {
+                const float wq = s * y;  // fl32(s * val(q))
+                const double d = (double)a - (double)wq;
+                obj += (om ? om[j] : 1.0) * (d * d);
+            }
+        }
+        return obj;
+    }
+    // E2M1 / E4M3 elements: fl32(|w| / m) into the conversion instruction with
+    // the power of two p2 (s = m p2); the same arithmetic as the search
+    const ScaleParts sp = scale_parts<SK>(s);
+    float x[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const float a = fabsf(w[j]);
-        const float x = (s != 0.0f) ? quotient<SK, ONE_STEP>(a, s, r) : 0.0f;
-        const float y = round_elem<EK>(x);
-        code[j] = elem_code<EK>(elem_index<EK>(y), __builtin_signbitf(w[j]) != 0);
+        float v = (s == 0.0f) ? 0.0f : (SK == SCALE_E8M0 ? a : quotient<SCALE_E4M3, ONE_STEP>(a, sp.m, sp.rm));
+        if (EK == ELEM_E4M3) v = fminf(v, 448.0f * sp.p2);
+        x[j] = v;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+        const uint32_t c2 = EK == ELEM_E2M1 ? fp4x2(x[j], x[j + 1], sp.p2) : fp8x2(x[j], x[j + 1], sp.p2);
+        const uint32_t sh = EK == ELEM_E2M1 ? 4u : 8u, mask = EK == ELEM_E2M1 ? 7u : 0x7Fu;
+        const uint32_t sb = EK == ELEM_E2M1 ? 8u : 0x80u;
+        code[j] = (c2 & mask) | (__builtin_signbitf(w[j]) ? sb : 0u);
+        code[j + 1] = ((c2 >> sh) & mask) | (__builtin_signbitf(w[j + 1]) ? sb : 0u);
         if (WANT_OBJ) {
-            const float wq = s * y;  // fl32(s * val(q))
-            const double d = (double)a - (double)wq;
-            obj += (om ? om[j] : 1.0) * (d * d);
+            const hd_v2f v = EK == ELEM_E2M1 ? fp4x2_val(c2) : fp8x2_val(c2);
+            const double d0 = (double)fabsf(w[j]) - (double)(s * v.x);
+            const double d1 = (double)fabsf(w[j + 1]) - (double)(s * v.y);
+            obj += (om ? om[j] : 1.0) * (d0 * d0);
+            obj += (om ? om[j + 1] : 1.0) * (d1 * d1);
         }
     }
     return obj;

@@ -35,12 +35,18 @@ __global__ __launch_bounds__(256) void encode_kernel(const T *__restrict__ W, in
     const bool active = left > 0;
     const int nv8 = left >= ENC_EPT ? ENC_EPT / 8 : (left > 0 ? (int)(left / 8) : 0);  // valid 8-chunks
     float w[ENC_EPT];
+    if (nv8 == ENC_EPT / 8) {
+        // all four 16-byte loads issued back to back (no per-chunk branch)
 #pragma unroll
-    for (int c = 0; c < ENC_EPT / 8; ++c) {
-        if (c < nv8)
-            load8<T>(W + e0 + 8 * c, w + 8 * c);
-        else
-            for (int j = 0; j < 8; ++j) w[8 * c + j] = 0.0f;
+        for (int c = 0; c < ENC_EPT / 8; ++c) load8<T>(W + e0 + 8 * c, w + 8 * c);
+    } else {
+#pragma unroll
+        for (int c = 0; c < ENC_EPT / 8; ++c) {
+            if (c < nv8)
+                load8<T>(W + e0 + 8 * c, w + 8 * c);
+            else
+                for (int j = 0; j < 8; ++j) w[8 * c + j] = 0.0f;
+        }
     }
     double om[OBJ ? ENC_EPT : 1];
     const bool weighted = OBJ && h != nullptr;

@@ -22,12 +22,59 @@
 //   - candidates at and above the first scale that rounds the block's amax to
 //     zero all give sum_j om_j w_j^2 (every element encodes to 0), so the wave
 //     stops at the largest such first-zero code over its lanes: the skipped
-//     codes could only tie, and ties keep the lower code.
+//     codes could only tie, and ties keep the lower code;
+//   - the wave starts from a window around its Naive codes and widens it only
+//     while some lane cannot prove the candidates outside it strictly worse
+//     than its best so far: below the window every element above fl32(Q s)
+//     saturates (sat_lower_bound), above it every element that rounds to zero
+//     stays zero (zero_lower_bound).  Both bounds hold for the objective as the
+//     kernel computes it, so the chosen code is the one the full scan picks.
 #pragma once
 #include "encode.hpp"
 #include "kernels.hpp"
 
 namespace hd {
+
+// Lower bound, valid for every candidate scale s' <= s, of the objective the
+// kernel computes: an element with a > fl32(Q s) saturates at every s' <= s
+// (fl32(a / s') >= Q), its dequantised value is at most fl32(Q s'), and the
+// fp32 residual is >= (a - fl32(Q s)) (1 - 2^-24); the other elements add
+// >= 0.  The bound is summed in float64 from exact differences, so
+// LB (1 - 2^-20) > best proves every such candidate strictly worse.
+template <int EK, int SEG, int LPB, bool WEIGHTED>
+__device__ __forceinline__ double sat_lower_bound(const float *a, const double *om, float s)
+{
+    const float qs = elem_max(EK) * s;  // fl32(Q s): what a saturated element dequantises to
+    double lb = 0.0;
+#pragma unroll
+    for (int j = 0; j < SEG; ++j) {
+        double t = (double)a[j] - (double)qs;
+        t = t > 0.0 ? t : 0.0;
+        lb += (WEIGHTED ? om[j] : 1.0) * (t * t);
+    }
+    return group_sum<LPB>(lb);
+}
+
+// Lower bound, valid for every candidate scale s' >= s, of the objective the
+// kernel computes: an element that rounds to code 0 at s rounds to 0 at every
+// larger scale (quotients only fall), where its residual is exactly a, so it
+// adds exactly om a^2; the other elements add >= 0.
+template <int EK, int SK, bool ONE_STEP, int SEG, int LPB, bool WEIGHTED>
+__device__ __forceinline__ double zero_lower_bound(const float *a, const double *om, float s)
+{
+    const float r = 1.0f / s;
+    double lb = 0.0;
+#pragma unroll
+    for (int j = 0; j < SEG; ++j) {
+        const bool zero = round_elem<EK>(quotient<SK, ONE_STEP>(a[j], s, r)) == 0.0f;
+        const double aj = (double)a[j];
+        lb += zero ? (WEIGHTED ? om[j] : 1.0) * (aj * aj) : 0.0;
+    }
+    return group_sum<LPB>(lb);
+}
+
+// true on every lane when no active lane needs more candidates
+__device__ __forceinline__ bool wave_all(bool p) { return __ballot(!p) == 0; }
 
 template <int EK, int SK, bool ONE_STEP>
 __device__ __forceinline__ float search_resid(float a, float s, float r)
@@ -109,26 +156,52 @@ __global__ __launch_bounds__(256) void search_kernel(const T *__restrict__ W, in
 
     double best = __builtin_huge_val();
     int best_c = 0;
-    for (int c = 0; c <= cend; ++c) {
-        const float2 sr = cand[c];
-        double acc0 = 0.0, acc1 = 0.0;
+    auto eval_range = [&](int lo, int hi) {
+        for (int c = lo; c <= hi; ++c) {
+            const float2 sr = cand[c];
+            double acc0 = 0.0, acc1 = 0.0;
 #pragma unroll
-        for (int j = 0; j < SEG; j += 2) {
-            const double d0 = (double)search_resid<EK, SK, ONE_STEP>(a[j], sr.x, sr.y);
-            const double d1 = (double)search_resid<EK, SK, ONE_STEP>(a[j + 1], sr.x, sr.y);
-            if (WEIGHTED) {
-                acc0 = __builtin_fma(om[j], d0 * d0, acc0);
-                acc1 = __builtin_fma(om[j + 1], d1 * d1, acc1);
-            } else {
-                acc0 = __builtin_fma(d0, d0, acc0);
-                acc1 = __builtin_fma(d1, d1, acc1);
+            for (int j = 0; j < SEG; j += 2) {
+                const double d0 = (double)search_resid<EK, SK, ONE_STEP>(a[j], sr.x, sr.y);
+                const double d1 = (double)search_resid<EK, SK, ONE_STEP>(a[j + 1], sr.x, sr.y);
+                if (WEIGHTED) {
+                    acc0 = __builtin_fma(om[j], d0 * d0, acc0);
+                    acc1 = __builtin_fma(om[j + 1], d1 * d1, acc1);
+                } else {
+                    acc0 = __builtin_fma(d0, d0, acc0);
+                    acc1 = __builtin_fma(d1, d1, acc1);
+                }
+            }
+            const double acc = group_sum<LPB>(acc0 + acc1);
+            if (acc < best || (acc == best && c < best_c)) {
+                best = acc;
+                best_c = c;
             }
         }
-        const double acc = group_sum<LPB>(acc0 + acc1);
-        if (acc < best) {
-            best = acc;
-            best_c = c;
-        }
+    };
+    // start from a binade below the lowest to two binades above the highest
+    // Naive code of the wave; extend either way only while some lane cannot
+    // prove the candidates beyond the window worse than its best so far
+    const int cn = naive_code<EK, SK>(amax) - C0;
+    int clo = cn - 8, chi = cn + 16;
+    clo = __builtin_amdgcn_readfirstlane(-wave_max_int(-(clo < 0 ? 0 : clo)));
+    chi = __builtin_amdgcn_readfirstlane(wave_max_int(chi));
+    if (chi > cend) chi = cend;
+    if (clo > chi) clo = chi;
+    eval_range(clo, chi);
+    while (chi < cend) {
+        const double lb = zero_lower_bound<EK, SK, ONE_STEP, SEG, LPB, WEIGHTED>(a, om, cand[chi + 1].x);
+        if (wave_all(!active || lb * (1.0 - 0x1p-20) > best)) break;
+        const int nhi = chi + 16 < cend ? chi + 16 : cend;
+        eval_range(chi + 1, nhi);
+        chi = nhi;
+    }
+    while (clo > 0) {
+        const double lb = sat_lower_bound<EK, SEG, LPB, WEIGHTED>(a, om, cand[clo - 1].x);
+        if (wave_all(!active || lb * (1.0 - 0x1p-20) > best)) break;
+        const int nlo = clo > 16 ? clo - 16 : 0;
+        eval_range(nlo, clo - 1);
+        clo = nlo;
     }
 
     // encode the segment with the chosen scale
@@ -151,6 +224,178 @@ __global__ __launch_bounds__(256) void search_kernel(const T *__restrict__ W, in
     }
 }
 
+// E2M1 / E4M3 elements: the candidate's quantise-dequantise is two gfx950
+// conversions per pair of weights.  With s = m * p2 (m one of the eight E4M3
+// mantissas, p2 a power of two; m = 1 for E8M0), fl32(a / s) = fl32(a / m) / p2
+// (exact scaling), so fl32(a / m) is computed once per mantissa and the
+// candidates are walked grouped by mantissa: per weight and candidate that
+// leaves one conversion to codes, one back to grid values (both per pair), the
+// residual a - s v as one FMA (s v is exact) and the float64 square-add.
+// Ties keep the lowest code (candidates are not visited in code order).
+template <int EK, int SK, typename T, int SEG, int LPB, bool WEIGHTED>
+__global__ __launch_bounds__(256) void search_hw_kernel(const T *__restrict__ W, int64_t N, int64_t K,
+                                                        const float *__restrict__ h, uint8_t *__restrict__ codes,
+                                                        uint8_t *__restrict__ scales, float *__restrict__ block_obj)
+{
+    constexpr int B = SEG * LPB;
+    constexpr int ROWS = 256 / LPB;
+    constexpr int C0 = cand_first(SK);
+    constexpr int NC = cand_last(SK) - C0 + 1;
+    constexpr bool ONE_STEP = sizeof(T) == 2;
+    __shared__ float4 cand[256];  // (s, p2, m, 1/m) in (mantissa, exponent) order
+    __shared__ int cidx[256];     // candidate index c - C0
+    __shared__ int cmant[256];    // mantissa group
+
+    const int tid = threadIdx.x;
+    if (tid < NC) {
+        int g = 0, rank = tid;  // E8M0: one mantissa, code order
+        if (SK != SCALE_E8M0) rank = e4m3_mantissa_rank(tid, &g);
+        const ScaleParts sp = scale_parts<SK>(scale_value(SK, C0 + tid));
+        cand[rank] = make_float4(sp.s, sp.p2, sp.m, sp.rm);
+        cidx[rank] = tid;
+        cmant[rank] = g;
+    }
+    __syncthreads();
+
+    const int64_t row = (int64_t)blockIdx.x * ROWS + tid / LPB;
+    const int seg = tid % LPB;
+    const int64_t col0 = (int64_t)blockIdx.y * B + (int64_t)seg * SEG;
+    const bool active = row < N;
+
+    float a[SEG];
+    uint32_t negmask = 0;
+    {
+        float w[8];
+#pragma unroll
+        for (int c8 = 0; c8 < SEG / 8; ++c8) {
+            if (active)
+                load8<T>(W + row * K + col0 + 8 * c8, w);
+            else
+                for (int j = 0; j < 8; ++j) w[j] = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                a[8 * c8 + j] = fabsf(w[j]);
+                negmask |= (uint32_t)(__builtin_signbitf(w[j]) != 0) << (8 * c8 + j);
+            }
+        }
+    }
+    double om[WEIGHTED ? SEG : 1];
+    if (WEIGHTED) {
+#pragma unroll
+        for (int j = 0; j < SEG; ++j) om[j] = (double)h[col0 + j];
+    }
+
+    // first candidate (in code order) that rounds the block's amax to zero
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < SEG; ++j) amax = fmaxf(amax, a[j]);
+    amax = group_max<LPB>(amax);
+    int lo = 0, hi = NC;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        const float sm = scale_value(SK, C0 + mid);
+        if (round_elem<EK>(quotient<SK, ONE_STEP>(amax, sm, 1.0f / sm)) == 0.0f)
+            hi = mid;
+        else
+            lo = mid + 1;
+    }
+    const int cend = __builtin_amdgcn_readfirstlane(wave_max_int(lo < NC ? lo : NC - 1));
+
+    double best = __builtin_huge_val();
+    int best_c = 0;
+    float am[SEG];
+    auto eval_range = [&](int lo, int hi) {
+        int cur_m = -1;
+        for (int k = 0; k < NC; ++k) {
+            const int ci = cidx[k];
+            if (ci > hi || ci < lo) continue;  // uniform: every lane skips it
+            const float4 cd = cand[k];
+            const int mg = cmant[k];
+            if (mg != cur_m) {  // uniform
+                cur_m = mg;
+#pragma unroll
+                for (int j = 0; j < SEG; ++j)
+                    am[j] = SK == SCALE_E8M0 ? a[j] : quotient<SCALE_E4M3, ONE_STEP>(a[j], cd.z, cd.w);
+            }
+            const float lim = 448.0f * cd.y;
+            double acc0 = 0.0, acc1 = 0.0;
+#pragma unroll
+            for (int j0 = 0; j0 < SEG; j0 += 8) {
+                float x[8], v[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) x[j] = EK == ELEM_E4M3 ? fminf(am[j0 + j], lim) : am[j0 + j];
+                quant8_vals<EK>(x, cd.y, v);
+#pragma unroll
+                for (int j = 0; j < 8; j += 2) {
+                    const double d0 = (double)__builtin_fmaf(-v[j], cd.x, a[j0 + j]);
+                    const double d1 = (double)__builtin_fmaf(-v[j + 1], cd.x, a[j0 + j + 1]);
+                    if (WEIGHTED) {
+                        acc0 = __builtin_fma(om[j0 + j], d0 * d0, acc0);
+                        acc1 = __builtin_fma(om[j0 + j + 1], d1 * d1, acc1);
+                    } else {
+                        acc0 = __builtin_fma(d0, d0, acc0);
+                        acc1 = __builtin_fma(d1, d1, acc1);
+                    }
+                }
+            }
+            const double acc = group_sum<LPB>(acc0 + acc1);
+            if (acc < best || (acc == best && ci < best_c)) {
+                best = acc;
+                best_c = ci;
+            }
+        }
+    };
+    // start below the lowest Naive code of the wave (a binade for E4M3 grids,
+    // two powers of two for E8M0); extend downward only while some lane cannot
+    // prove the lower candidates worse
+    // No zero bound here: E8M0 grids stop within a few codes of Naive anyway,
+    // E4M3 elements zero almost nothing until the very top, and for E2M1 on
+    // the E4M3 grid the extra passes (each re-divides by every mantissa) cost
+    // more than the candidates they save (measured).  INT8 uses it.
+    constexpr bool UP_PRUNE = false;
+    constexpr int MARGIN = SK == SCALE_E8M0 ? 2 : 8, UP = 16;
+    constexpr int STEP = SK == SCALE_E8M0 ? 4 : 16;
+    const int cn = naive_code<EK, SK>(amax) - C0;
+    int clo = cn - MARGIN, chi = UP_PRUNE ? cn + UP : cend;
+    clo = __builtin_amdgcn_readfirstlane(-wave_max_int(-(clo < 0 ? 0 : clo)));
+    chi = __builtin_amdgcn_readfirstlane(wave_max_int(chi));
+    if (chi > cend) chi = cend;
+    if (clo > chi) clo = chi;
+    eval_range(clo, chi);
+    while (UP_PRUNE && chi < cend) {
+        const double lb = zero_lower_bound<EK, SK, ONE_STEP, SEG, LPB, WEIGHTED>(a, om, scale_value(SK, C0 + chi + 1));
+        if (wave_all(!active || lb * (1.0 - 0x1p-20) > best)) break;
+        const int nhi = chi + STEP < cend ? chi + STEP : cend;
+        eval_range(chi + 1, nhi);
+        chi = nhi;
+    }
+    while (clo > 0) {
+        const double lb = sat_lower_bound<EK, SEG, LPB, WEIGHTED>(a, om, scale_value(SK, C0 + clo - 1));
+        if (wave_all(!active || lb * (1.0 - 0x1p-20) > best)) break;
+        const int nlo = clo > STEP ? clo - STEP : 0;
+        eval_range(nlo, clo - 1);
+        clo = nlo;
+    }
+
+    const float s = scale_value(SK, C0 + best_c);
+    if (!active) return;
+    const int64_t e0 = row * K + col0;
+#pragma unroll
+    for (int c8 = 0; c8 < SEG / 8; ++c8) {
+        float w[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) w[j] = ((negmask >> (8 * c8 + j)) & 1u) ? -a[8 * c8 + j] : a[8 * c8 + j];
+        uint32_t cdd[8];
+        encode8<EK, SK, ONE_STEP, false>(w, s, 1.0f / s, nullptr, cdd);
+        store_codes8<EK>(codes, e0 + 8 * c8, cdd);
+    }
+    if (seg == 0) {
+        const int64_t blk = row * (K / B) + blockIdx.y;
+        scales[blk] = (uint8_t)(C0 + best_c);
+        if (block_obj) block_obj[blk] = (float)best;
+    }
+}
+
 template <int EK, int SK, typename T, int SEG, int LPB>
 static hipError_t search_go(const void *W, int64_t N, int64_t K, const float *h, uint8_t *codes,
                             uint8_t *scales, float *bo, hipStream_t st)
@@ -158,17 +403,46 @@ static hipError_t search_go(const void *W, int64_t N, int64_t K, const float *h,
     constexpr int ROWS = 256 / LPB;
     const dim3 grid((unsigned)((N + ROWS - 1) / ROWS), (unsigned)(K / (SEG * LPB)));
     const T *w = static_cast<const T *>(W);
-    if (h)
-        search_kernel<EK, SK, T, SEG, LPB, true><<<grid, 256, 0, st>>>(w, N, K, h, codes, scales, bo);
-    else
-        search_kernel<EK, SK, T, SEG, LPB, false><<<grid, 256, 0, st>>>(w, N, K, h, codes, scales, bo);
+    // (SEG, LPB) = (32, *) serves only the unweighted search, (16, > 1) only the weighted one
+    constexpr bool MAY_W = SEG <= 16, MAY_U = !(SEG == 16 && LPB > 1);
+    if constexpr (EK == ELEM_INT8) {
+        if constexpr (MAY_W) {
+            if (h) {
+                search_kernel<EK, SK, T, SEG, LPB, true><<<grid, 256, 0, st>>>(w, N, K, h, codes, scales, bo);
+                return hipGetLastError();
+            }
+        }
+        if constexpr (MAY_U) search_kernel<EK, SK, T, SEG, LPB, false><<<grid, 256, 0, st>>>(w, N, K, h, codes, scales, bo);
+    } else {
+        if constexpr (MAY_W) {
+            if (h) {
+                search_hw_kernel<EK, SK, T, SEG, LPB, true><<<grid, 256, 0, st>>>(w, N, K, h, codes, scales, bo);
+                return hipGetLastError();
+            }
+        }
+        if constexpr (MAY_U)
+            search_hw_kernel<EK, SK, T, SEG, LPB, false><<<grid, 256, 0, st>>>(w, N, K, h, codes, scales, bo);
+    }
     return hipGetLastError();
 }
 
+// Lane segments: 32 weights, or 16 when the float64 weights h_j also live in
+// registers (so the H kernels keep two waves per SIMD).
 template <int EK, int SK, typename T>
 static hipError_t search_b(int B, const void *W, int64_t N, int64_t K, const float *h, uint8_t *codes,
                            uint8_t *scales, float *bo, hipStream_t st)
 {
+    if (h) {
+        switch (B) {
+        case 8: return search_go<EK, SK, T, 8, 1>(W, N, K, h, codes, scales, bo, st);
+        case 16: return search_go<EK, SK, T, 16, 1>(W, N, K, h, codes, scales, bo, st);
+        case 32: return search_go<EK, SK, T, 16, 2>(W, N, K, h, codes, scales, bo, st);
+        case 64: return search_go<EK, SK, T, 16, 4>(W, N, K, h, codes, scales, bo, st);
+        case 128: return search_go<EK, SK, T, 16, 8>(W, N, K, h, codes, scales, bo, st);
+        case 256: return search_go<EK, SK, T, 16, 16>(W, N, K, h, codes, scales, bo, st);
+        }
+        return hipErrorInvalidValue;
+    }
     switch (B) {
     case 8: return search_go<EK, SK, T, 8, 1>(W, N, K, h, codes, scales, bo, st);
     case 16: return search_go<EK, SK, T, 16, 1>(W, N, K, h, codes, scales, bo, st);
