@@ -53,6 +53,8 @@ def lib():
         L.orc_weight_error.restype = dbl
         L.orc_output_error.argtypes = [P, i32, i64, P, i32, P, i32, i64, i64, P, P, i32]
         L.orc_output_error.restype = dbl
+        L.orc_matmul_nt.argtypes = [P, i32, i64, P, i32, i64, i64, P, i32]
+        L.orc_matmul_nt.restype = None
         L.orc_max_threads.argtypes = []
         _lib = L
     return _lib
@@ -184,6 +186,17 @@ def weight_error(W, Wq, nthreads=0, sums=False):
     r = lib().orc_weight_error(_ptr(W), _dt(W), _ptr(Wq), _dt(Wq), N, K,
                                ctypes.byref(a), ctypes.byref(b), nthreads)
     return (r, a.value, b.value) if sums else r
+
+
+def matmul_nt(X, W, nthreads=0):
+    """Y = X W^T in float64 ([M, N]), each entry summed in k order."""
+    X = np.ascontiguousarray(X)
+    W = np.ascontiguousarray(W)
+    M, K = X.shape
+    N = W.shape[0]
+    Y = np.empty((M, N), dtype=np.float64)
+    lib().orc_matmul_nt(_ptr(X), _dt(X), M, _ptr(W), _dt(W), N, K, _ptr(Y), nthreads)
+    return Y
 
 
 def output_error(X, W, Wq, nthreads=0, sums=False):

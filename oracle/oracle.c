@@ -611,3 +611,20 @@ double orc_output_error(const void *X, int xdt, int64_t M, const void *W, int wd
     if (ysq_out) *ysq_out = ysq;
     return sqrt(dsq) / sqrt(ysq);
 }
+
+/* Y = X W^T in float64 from the exact inputs, each entry summed in k order
+ * (the product behind the output error's reference term ||X W^T||). */
+void orc_matmul_nt(const void *X, int xdt, int64_t M, const void *W, int wdt, int64_t N, int64_t K, double *Y,
+                   int nthreads)
+{
+    int nt = set_threads(nthreads);
+#pragma omp parallel for num_threads(nt) schedule(dynamic, 1)
+    for (int64_t t = 0; t < M; t++) {
+        for (int64_t n = 0; n < N; n++) {
+            double y = 0.0;
+            for (int64_t k = 0; k < K; k++)
+                y += (double)widen(X, xdt, t * K + k) * (double)widen(W, wdt, n * K + k);
+            Y[t * N + n] = y;
+        }
+    }
+}

@@ -10,8 +10,10 @@ checks the qualitative ordering the qwantize "Results" tables report
 import numpy as np
 import pytest
 import scipy.linalg
+import torch
 
 import oracle
+import synth
 from oracle import NAIVE, SSE_OPT, H_OPT, INT8_E4M3, NVFP4, MXFP4
 
 
@@ -114,3 +116,25 @@ def test_published_ordering_on_stand_in_data():
         assert we[SSE_OPT] <= we[H_OPT], (fmt, we)
         gain[fmt] = 1 - oe[H_OPT] / oe[SSE_OPT]
     assert gain[MXFP4] < gain[NVFP4]
+
+
+def test_matmul_nt_identity_and_integers():
+    """Y = X W^T: X = I gives W^T exactly; small integers give the exact
+    integer product (brute force in Python integers); bf16 inputs are widened
+    exactly; sum Y^2 is the ||X W^T||^2 the output error divides by."""
+    rng = np.random.default_rng(7)
+    W = rng.standard_normal((5, 12)).astype(np.float32)
+    Y = oracle.matmul_nt(np.eye(12, dtype=np.float32), W)
+    np.testing.assert_array_equal(Y, W.T.astype(np.float64))
+    Xi = rng.integers(-50, 51, (7, 9))
+    Wi = rng.integers(-50, 51, (4, 9))
+    Y = oracle.matmul_nt(Xi.astype(np.float32), Wi.astype(np.float32))
+    exact = [[sum(int(Xi[t, k]) * int(Wi[n, k]) for k in range(9)) for n in range(4)] for t in range(7)]
+    np.testing.assert_array_equal(Y, np.array(exact, dtype=np.float64))
+    Xb = torch.from_numpy(Xi.astype(np.float32)).to(torch.bfloat16)
+    Wb = torch.from_numpy(Wi.astype(np.float32)).to(torch.bfloat16)
+    np.testing.assert_array_equal(oracle.matmul_nt(synth.bits(Xb), synth.bits(Wb)), Y)
+    X = rng.standard_normal((6, 12)).astype(np.float32)
+    _, _, ysq = oracle.output_error(X, W, W, sums=True)
+    assert (oracle.matmul_nt(X, W) ** 2).sum() == pytest.approx(ysq, rel=1e-14)
+    assert oracle.matmul_nt(np.zeros((0, 12), np.float32), W).shape == (0, 5)
