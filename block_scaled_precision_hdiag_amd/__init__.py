@@ -28,7 +28,8 @@ METHODS = {"naive": NAIVE, "sse": SSE_OPT, "h": H_OPT}
 
 EXPORTS = ["hdiag", "hdiag_workspace_size", "quantize_blocks", "encode_blocks", "dequantize",
            "weight_error", "weight_error_workspace_size", "output_error", "output_error_workspace_size",
-           "output_error_given_ref",
+           "output_error_given_ref", "output_reference", "output_reference_size", "output_error_codes",
+           "output_error_codes_workspace_size",
            "hdiag_strerror", "hdiag_last_error", "hdiag_format_info", "hdiag_version"]
 
 
@@ -63,6 +64,12 @@ def lib():
         L.output_error_workspace_size.restype = sz
         L.output_error.argtypes = [P, i32, i64, P, i32, P, i32, i64, i64, P, P, P, sz, P]
         L.output_error_given_ref.argtypes = [P, i32, i64, P, i32, P, i32, i64, i64, P, P, P, P, sz, P]
+        L.output_reference_size.argtypes = [i64, i64, i64]
+        L.output_reference_size.restype = sz
+        L.output_reference.argtypes = [P, i32, i64, P, i32, i64, i64, P, sz, P]
+        L.output_error_codes_workspace_size.argtypes = [i64, i64, i64]
+        L.output_error_codes_workspace_size.restype = sz
+        L.output_error_codes.argtypes = [i32, i32, P, i32, i64, P, P, i64, i64, P, sz, P, P, P, sz, P]
         L.hdiag_strerror.argtypes = [i32]
         L.hdiag_strerror.restype = ctypes.c_char_p
         L.hdiag_last_error.argtypes = []
@@ -71,7 +78,8 @@ def lib():
         L.hdiag_version.argtypes = []
         L.hdiag_version.restype = ctypes.c_char_p
         for name in ("hdiag", "quantize_blocks", "encode_blocks", "dequantize", "weight_error",
-                     "output_error", "output_error_given_ref", "hdiag_format_info"):
+                     "output_error", "output_error_given_ref", "output_reference", "output_error_codes",
+                     "hdiag_format_info"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -204,6 +212,58 @@ def output_error_given_ref(X, W, Wq, ysq, sums=False, workspace=None):
     _check(lib().output_error_given_ref(_ptr(X), _dt(X), M, _ptr(W), _dt(W), _ptr(Wq), _dt(Wq), N, K, _ptr(ysq),
                                         _ptr(out), _ptr(s), _ptr(ws), ws.numel(), _stream(d)),
            "output_error_given_ref")
+    return (out, s) if sums else out
+
+
+REF_Y_OFFSET = 256  # HD_REF_Y_OFFSET
+
+
+def output_reference_size(M, N, K):
+    return int(lib().output_reference_size(M, N, K))
+
+
+def output_reference(X, W, ref=None):
+    """Fill (or allocate) the reference buffer of (X, W) for output_error_codes:
+    ||X W^T||^2 and Y = X W^T (see reference_ysq / reference_y).  Returns it
+    as a uint8 device tensor."""
+    d = _dev(X)
+    M, K = X.shape
+    N = W.shape[0]
+    need = output_reference_size(M, N, K)
+    if ref is None:
+        ref = torch.empty(need, dtype=torch.uint8, device=d)
+    _check(lib().output_reference(_ptr(X), _dt(X), M, _ptr(W), _dt(W), N, K, _ptr(ref), ref.numel(), _stream(d)),
+           "output_reference")
+    return ref
+
+
+def reference_ysq(ref):
+    """||X W^T||^2 of a reference buffer, as a float64 device tensor [1] (a view)."""
+    return ref[:8].view(torch.float64)
+
+
+def reference_y(ref, M, N):
+    """Y = X W^T of a reference buffer, as a float32 device tensor [M, N] (a view)."""
+    return ref[REF_Y_OFFSET:REF_Y_OFFSET + M * N * 4].view(torch.float32).view(M, N)
+
+
+def output_error_codes_workspace_size(M, N, K):
+    return int(lib().output_error_codes_workspace_size(M, N, K))
+
+
+def output_error_codes(fmt, B, X, codes, scales, ref, N, K, sums=False, workspace=None, out=None):
+    """||X Wq^T - X W^T||_F / ||X W^T||_F for Wq = dequantize(fmt, B, codes,
+    scales), against the reference buffer of (X, W)."""
+    d = _dev(X)
+    M = X.shape[0]
+    if out is None:
+        out = torch.empty(1, dtype=torch.float64, device=d)
+    s = torch.empty(2, dtype=torch.float64, device=d) if sums else None
+    need = output_error_codes_workspace_size(M, N, K)
+    ws = workspace if workspace is not None else torch.empty(max(need, 16), dtype=torch.uint8, device=d)
+    _check(lib().output_error_codes(fmt, B, _ptr(X), _dt(X), M, _ptr(codes), _ptr(scales), N, K, _ptr(ref),
+                                    ref.numel(), _ptr(out), _ptr(s), _ptr(ws), ws.numel(), _stream(d)),
+           "output_error_codes")
     return (out, s) if sums else out
 
 

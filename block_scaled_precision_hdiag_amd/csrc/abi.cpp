@@ -242,6 +242,57 @@ hd_status output_error_given_ref(const void *X, hd_dtype xt, int64_t M, const vo
                                "output_error_given_ref");
 }
 
+size_t output_reference_size(int64_t M, int64_t N, int64_t K)
+{
+    if (M < 0 || N < 0 || K < 0) return 0;
+    return (size_t)hd::output_reference_layout(M, N, K).bytes;
+}
+
+hd_status output_reference(const void *X, hd_dtype xt, int64_t M, const void *W, hd_dtype wt, int64_t N, int64_t K,
+                           void *ref, size_t ref_bytes, void *stream)
+{
+    HD_REQUIRE(valid_dtype(xt) && valid_dtype(wt), "unknown dtype");
+    HD_REQUIRE(M >= 0 && N >= 0 && K >= 0, "negative size");
+    HD_REQUIRE(K % 8 == 0, "K=%lld must be a multiple of 8", (long long)K);
+    HD_REQUIRE(M <= (int64_t)1 << 31 && N <= (int64_t)1 << 31 && K <= (int64_t)1 << 31, "size too large");
+    if (xt != HD_BF16 || wt != HD_BF16)
+        return fail(HD_ERR_UNSUPPORTED, "output_reference needs bfloat16 X and W (output_error takes float32)");
+    HD_CHECK_PTR(ref, true);
+    HD_REQUIRE(ref_bytes >= (size_t)hd::output_reference_layout(M, N, K).bytes, "reference buffer too small");
+    HD_CHECK_PTR(X, M * K > 0);
+    HD_CHECK_PTR(W, N * K > 0);
+    return hip_status(hd::launch_output_reference(X, M, W, N, K, ref, (hipStream_t)stream), "output_reference");
+}
+
+size_t output_error_codes_workspace_size(int64_t M, int64_t N, int64_t K)
+{
+    if (M < 0 || N < 0 || K < 0) return 0;
+    return hd::output_error_codes_ws(M, N, K);
+}
+
+hd_status output_error_codes(hd_format fmt, int32_t B, const void *X, hd_dtype xt, int64_t M, const uint8_t *codes,
+                             const uint8_t *scales, int64_t N, int64_t K, const void *ref, size_t ref_bytes,
+                             double *out, double *sums, void *ws, size_t ws_bytes, void *stream)
+{
+    hd_status s = check_quant_shape(fmt, B, N, K);
+    if (s != HD_OK) return s;
+    HD_REQUIRE(valid_dtype(xt), "unknown dtype %d", (int)xt);
+    HD_REQUIRE(M >= 0, "negative size");
+    HD_REQUIRE(M <= (int64_t)1 << 31 && N <= (int64_t)1 << 31 && K <= (int64_t)1 << 31, "size too large");
+    if (xt != HD_BF16) return fail(HD_ERR_UNSUPPORTED, "output_error_codes needs bfloat16 X");
+    HD_REQUIRE(out != nullptr, "out is NULL");
+    HD_CHECK_PTR(ref, true);
+    HD_REQUIRE(ref_bytes >= (size_t)hd::output_reference_layout(M, N, K).bytes, "reference buffer too small");
+    HD_CHECK_PTR(ws, true);
+    HD_REQUIRE(ws_bytes >= hd::output_error_codes_ws(M, N, K), "workspace too small");
+    HD_CHECK_PTR(X, M * K > 0);
+    HD_CHECK_PTR(codes, N * K > 0);
+    if (N * K > 0 && scales == nullptr) return fail(HD_ERR_INVALID_ARG, "scales is NULL");
+    return hip_status(hd::launch_output_error_codes(fmt, B, X, M, codes, scales, N, K, ref, out, sums, ws,
+                                                    (hipStream_t)stream),
+                      "output_error_codes");
+}
+
 }  // extern "C"
 
 namespace hd {

@@ -44,4 +44,19 @@ hipError_t launch_output_error(const void *X, int xdt, int64_t M, const void *W,
                                int qdt, int64_t N, int64_t K, const double *ysq, double *out, double *sums,
                                void *ws, hipStream_t st);
 
+// Output error against a stored reference (outref.hip).  The reference buffer
+// holds, at these byte offsets: ||X W^T||^2 (double, offset 0), Y = X W^T
+// (float [M][N], offset y), the per-row exponents of X' (int [M], offset e),
+// X' (fp16 [M][K], offset x) and the GEMM's workgroup partials (offset part).
+struct RefLayout {
+    int64_t y, e, x, part, bytes;
+};
+RefLayout output_reference_layout(int64_t M, int64_t N, int64_t K);
+hipError_t launch_output_reference(const void *X, int64_t M, const void *W, int64_t N, int64_t K, void *ref,
+                                   hipStream_t st);
+size_t output_error_codes_ws(int64_t M, int64_t N, int64_t K);
+hipError_t launch_output_error_codes(int fmt, int B, const void *X, int64_t M, const uint8_t *codes,
+                                     const uint8_t *scales, int64_t N, int64_t K, const void *ref, double *out,
+                                     double *sums, void *ws, hipStream_t st);
+
 }  // namespace hd

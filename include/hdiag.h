@@ -176,6 +176,51 @@ hd_status output_error_given_ref(const void *X, hd_dtype xt, int64_t M, const vo
                                  const void *Wq, hd_dtype qt, int64_t N, int64_t K, const double *ysq,
                                  double *out, double *sums, void *ws, size_t ws_bytes, void *stream);
 
+/* ------------------------------------- output error against a reference --- */
+
+/* For callers that score several quantisations of one W against one X: the
+ * output error of each quantisation then costs one MFMA product instead of two.
+ *
+ * output_reference() fills a caller-allocated device buffer `ref` of at least
+ * output_reference_size(M, N, K) bytes (16-byte aligned) with:
+ *   byte 0                : double ||X W^T||_F^2;
+ *   byte HD_REF_Y_OFFSET  : float Y[M][N] = X W^T (row-major), products of the
+ *                           bf16 inputs accumulated in float32 on the MFMA units;
+ *   after Y               : data private to the library (a float16 copy of X
+ *                           with one power-of-two scale per row, used for INT8).
+ * X and W must be bfloat16 (HD_ERR_UNSUPPORTED otherwise: use output_error);
+ * K % 8 == 0.  The buffer stays valid as long as X and W are unchanged.
+ *
+ * output_error_codes() returns ||X Wq^T - X W^T||_F / ||X W^T||_F for
+ * Wq = dequantize(fmt, B, codes, scales) without forming Wq:
+ *   - E2M1 / E4M3 elements: the dequantised values s val(q) are exact in
+ *     bfloat16, so X Wq^T is one bf16 MFMA product (float32 accumulation);
+ *   - INT8: val(a8) q (E4M3 scale value times the integer code) is exact in
+ *     float16 and is multiplied with the float16 copy of X; the factor
+ *     2^e_row / 127 is applied in float64 afterwards.  This uses val q / 127
+ *     for fl32(fl32(val / 127) q), a difference of at most two float32
+ *     roundings (2^-23 relative) per weight;
+ *   - D = X Wq^T - Y is formed and squared in float64, so D is carried to
+ *     float32 accumulation accuracy relative to Y (about 1e-6 of ||Y|| per
+ *     element): the metric is accurate to ~1e-4 relative while it is above
+ *     ~1e-3.  output_error() computes D directly and has no such floor.
+ * X is the same bfloat16 [M, K] given to output_reference, ref its buffer.
+ * sums (optional, device, 2 doubles): {||D||^2, ||X W^T||^2}.
+ * workspace: ws_bytes >= output_error_codes_workspace_size(M, N, K).
+ * Errors: HD_ERR_INVALID_ARG as quantize_blocks for fmt / B / N / K, NULL or
+ * misaligned pointers, a short ref or workspace; HD_ERR_UNSUPPORTED for a
+ * float32 X.  Calls that share `ref` may run concurrently (it is only read);
+ * each needs its own workspace. */
+#define HD_REF_Y_OFFSET 256
+size_t output_reference_size(int64_t M, int64_t N, int64_t K);
+hd_status output_reference(const void *X, hd_dtype xt, int64_t M, const void *W, hd_dtype wt, int64_t N,
+                           int64_t K, void *ref, size_t ref_bytes, void *stream);
+size_t output_error_codes_workspace_size(int64_t M, int64_t N, int64_t K);
+hd_status output_error_codes(hd_format fmt, int32_t B, const void *X, hd_dtype xt, int64_t M,
+                             const uint8_t *codes, const uint8_t *scales, int64_t N, int64_t K,
+                             const void *ref, size_t ref_bytes, double *out, double *sums, void *ws,
+                             size_t ws_bytes, void *stream);
+
 /* ------------------------------------------------------------ utilities --- */
 
 /* Static description of a status code. */

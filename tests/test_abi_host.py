@@ -89,3 +89,42 @@ def test_workspace_queries():
     L = hd.lib()
     rc = L.hdiag(A, hd.HD_BF16, 1000, 64, A, A, 8, None)
     assert rc == hd.HD_ERR_INVALID_ARG and "workspace" in L.hdiag_last_error().decode()
+
+
+def test_output_reference_validation():
+    L = hd.lib()
+    M, N, K = 300, 200, 512
+    need = hd.output_reference_size(M, N, K)
+    # Y (float32 M x N) and the float16 copy of X fit, after the 256-byte header
+    assert need >= hd.REF_Y_OFFSET + M * N * 4 + M * K * 2
+    assert L.output_reference_size(-1, 2, 3) == 0
+    rc = L.output_reference(A, hd.HD_F32, M, A, hd.HD_BF16, N, K, A, need, None)
+    assert rc == hd.HD_ERR_UNSUPPORTED and "bfloat16" in L.hdiag_last_error().decode()
+    rc = L.output_reference(A, hd.HD_BF16, M, A, hd.HD_BF16, N, 12, A, need, None)
+    assert rc == hd.HD_ERR_INVALID_ARG and "multiple of 8" in L.hdiag_last_error().decode()
+    rc = L.output_reference(A, hd.HD_BF16, M, A, hd.HD_BF16, N, K, A, need - 1, None)
+    assert rc == hd.HD_ERR_INVALID_ARG and "too small" in L.hdiag_last_error().decode()
+    rc = L.output_reference(A, hd.HD_BF16, M, A, hd.HD_BF16, N, K, MIS, need, None)
+    assert rc == hd.HD_ERR_INVALID_ARG and "aligned" in L.hdiag_last_error().decode()
+
+
+def test_output_error_codes_validation():
+    L = hd.lib()
+    M, N, K = 300, 200, 512
+    rb = hd.output_reference_size(M, N, K)
+    ws = hd.output_error_codes_workspace_size(M, N, K)
+    assert ws >= N * K * 2  # the 16-bit weight operand
+    args = [hd.INT8_E4M3, 32, A, hd.HD_BF16, M, A, A, N, K, A, rb, A, None, A, ws, None]
+    bad = list(args); bad[1] = 12
+    assert L.output_error_codes(*bad) == hd.HD_ERR_INVALID_ARG
+    assert "block size" in L.hdiag_last_error().decode()
+    bad = list(args); bad[3] = hd.HD_F32
+    assert L.output_error_codes(*bad) == hd.HD_ERR_UNSUPPORTED
+    bad = list(args); bad[10] = rb - 8
+    assert L.output_error_codes(*bad) == hd.HD_ERR_INVALID_ARG
+    bad = list(args); bad[14] = ws - 8
+    assert L.output_error_codes(*bad) == hd.HD_ERR_INVALID_ARG
+    assert "workspace" in L.hdiag_last_error().decode()
+    bad = list(args); bad[11] = None
+    assert L.output_error_codes(*bad) == hd.HD_ERR_INVALID_ARG
+    assert "out is NULL" in L.hdiag_last_error().decode()
