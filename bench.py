@@ -5,10 +5,11 @@ Workload (one "step"): the INT8 / E4M3-scale case on the qwantize "Results"
 page's layer shape -- W 2560 x 9728 bf16 (a seeded Student-t(4) x 0.02 stand-in
 with per-row lognormal gain for the down_proj weight) and calibration X
 16384 x 9728 bf16 (N(0,1), 8 outlier channels x 50):
-    hdiag(X), then for B in {32, 64, 128, 256} and each of Naive, SSE-Optimal,
-    H-Optimal: quantize_blocks (scale choice + encode), dequantize, weight
-    error and output error (||X W^T|| is computed by the first output error of
-    the step and passed to the other eleven).
+    hdiag(X) and output_reference(X, W) (Y = X W^T and ||Y||^2, which every
+    output error of the step is measured against), then for B in
+    {32, 64, 128, 256} and each of Naive, SSE-Optimal, H-Optimal:
+    quantize_blocks (scale choice + encode), dequantize, weight error and
+    output error (output_error_codes: one MFMA product from the codes).
 value = 12 quantisations x 2560 x 9728 weights / step time, in Gweights/s.
 Inputs are resident in HBM before timing starts.  Per-call GPU times come from
 HIP events recorded on the stream the kernels run on, over the timed steps.
@@ -111,13 +112,13 @@ def main():
     h = torch.empty(K, dtype=torch.float32, device=dev)
     ws_h = torch.empty(hd.hdiag_workspace_size(M, K), dtype=torch.uint8, device=dev)
     ws_w = torch.empty(hd.lib().weight_error_workspace_size(N, K), dtype=torch.uint8, device=dev)
-    ws_o = torch.empty(hd.output_error_workspace_size(M, N, K), dtype=torch.uint8, device=dev)
+    ref = torch.empty(hd.output_reference_size(M, N, K), dtype=torch.uint8, device=dev)
+    ws_o = torch.empty(hd.output_error_codes_workspace_size(M, N, K), dtype=torch.uint8, device=dev)
     codes = {B: torch.empty((N, K), dtype=torch.uint8, device=dev) for B in blocks}
     scales = {B: torch.empty((N, K // B), dtype=torch.uint8, device=dev) for B in blocks}
     Wq = torch.empty((N, K), dtype=torch.float32, device=dev)
     werr = torch.empty((len(blocks), 3), dtype=torch.float64, device=dev)
     oerr = torch.empty((len(blocks), 3), dtype=torch.float64, device=dev)
-    osums = torch.empty(2, dtype=torch.float64, device=dev)  # ||X Wq^T - X W^T||^2, ||X W^T||^2
 
     if args.copy_probe_mb:
         # a plain device-to-device copy of a known size (hipMemcpyAsync runs it
@@ -144,26 +145,18 @@ def main():
 
     def step(rec):
         timed("hdiag", 0, lambda: hd.hdiag(X, out=h, workspace=ws_h), rec)
+        timed("output_reference", 0, lambda: hd.output_reference(X, W, ref=ref), rec)
         for bi, B in enumerate(blocks):
             for mi, (mname, m) in enumerate(methods):
                 stage = "naive" if m == hd.NAIVE else "search_" + mname
                 timed(stage, B, lambda: hd.quantize_blocks(m, fmt, B, W, h=h, codes=codes[B], scales=scales[B]),
                       rec)
                 timed("dequantize", B, lambda: hd.dequantize(fmt, B, codes[B], scales[B], N, K, out=Wq), rec)
-                timed("weight_error", B, lambda: werr[bi, mi].copy_(hd.weight_error(W, Wq, workspace=ws_w)[0]),
+                timed("weight_error", B, lambda: hd.weight_error(W, Wq, workspace=ws_w, out=werr[bi, mi:mi + 1]),
                       rec)
-                if bi == 0 and mi == 0:
-                    # ||X W^T||^2 depends on X and W only: the step's first
-                    # output error computes it, the other eleven reuse it
-                    def oe_first():
-                        o, sm = hd.output_error(X, W, Wq, sums=True, workspace=ws_o)
-                        oerr[bi, mi].copy_(o[0])
-                        osums.copy_(sm)
-                    timed("output_error", B, oe_first, rec)
-                else:
-                    timed("output_error_given_ref", B,
-                          lambda: oerr[bi, mi].copy_(hd.output_error_given_ref(X, W, Wq, osums[1:2],
-                                                                               workspace=ws_o)[0]), rec)
+                timed("output_error", B,
+                      lambda: hd.output_error_codes(fmt, B, X, codes[B], scales[B], ref, N, K, workspace=ws_o,
+                                                    out=oerr[bi, mi:mi + 1]), rec)
 
     for _ in range(args.warmup):
         step(False)
@@ -190,8 +183,8 @@ def main():
         "naive": ("hbm", sum(bytes_w + N * K + N * K // B for B in blocks) / len(blocks)),
         "dequantize": ("hbm", sum(N * K + N * K // B + N * K * 4 for B in blocks) / len(blocks)),
         "weight_error": ("hbm", bytes_w + N * K * 4),
-        "output_error": ("mfma", 4.0 * M * N * K),
-        "output_error_given_ref": ("mfma", 2.0 * M * N * K),
+        "output_reference": ("mfma", 2.0 * M * N * K),
+        "output_error": ("mfma", 2.0 * M * N * K),
         "search_sse": ("alu", N * K * n_cand * SEARCH_OPS["sse"]),
         "search_h": ("alu", N * K * n_cand * SEARCH_OPS["h"]),
     }
@@ -232,8 +225,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "INT8 (E4M3 scales) on W 2560x9728 bf16, h from X 16384x9728 bf16; "
-                               "B in {32,64,128,256}; Naive + SSE-Optimal + H-Optimal; hdiag, quantize, "
-                               "dequantize, weight and output error per step",
+                               "B in {32,64,128,256}; Naive + SSE-Optimal + H-Optimal; hdiag, X W^T reference, "
+                               "quantize, dequantize, weight and output error per step",
                    "W": [N, K], "X": [M, K], "format": "INT8_E4M3", "blocks": blocks,
                    "quantizations_per_step": len(blocks) * len(methods)},
         "roofline": roofline,

@@ -8,7 +8,8 @@ computing anything some other way: build it with
 ``python block_scaled_precision_hdiag_amd/build.py`` (or ``__graft_entry__.build()``).
 
 Names follow the C ABI: ``hdiag``, ``quantize_blocks``, ``encode_blocks``,
-``dequantize``, ``weight_error``, ``output_error``, ``hdiag_format_info``.
+``dequantize``, ``weight_error``, ``output_error``, ``output_error_given_ref``,
+``output_reference``, ``output_error_codes``, ``hdiag_format_info``.
 """
 import ctypes
 import os
@@ -168,11 +169,12 @@ def dequantize(fmt, B, codes, scales, N, K, dtype=torch.float32, out=None):
     return out
 
 
-def weight_error(W, Wq, sums=False, workspace=None):
+def weight_error(W, Wq, sums=False, workspace=None, out=None):
     """||Wq - W||_F / ||W||_F as a float64 device tensor of shape [1] (and [2] sums)."""
     d = _dev(W)
     N, K = W.shape
-    out = torch.empty(1, dtype=torch.float64, device=d)
+    if out is None:
+        out = torch.empty(1, dtype=torch.float64, device=d)
     s = torch.empty(2, dtype=torch.float64, device=d) if sums else None
     need = int(lib().weight_error_workspace_size(N, K))
     ws = workspace if workspace is not None else torch.empty(max(need, 16), dtype=torch.uint8, device=d)

@@ -42,12 +42,31 @@ typedef _Float16 oh16x8_t __attribute__((ext_vector_type(8)));
 typedef float of32x16_t __attribute__((ext_vector_type(16)));
 
 static constexpr int GE_TM = 256;      // X rows per tile
-static constexpr int GE_TN = 256;      // weight rows per tile
-static constexpr int GE_TK = 64;       // K per LDS stage
+static constexpr int GE_TN = 256;      // weight rows per full tile
 static constexpr int GE_THREADS = 256;
 static constexpr int GE_GROUP_M = 8;
-static constexpr int GE_STAGE = (GE_TM + GE_TN) * GE_TK;  // 16-bit elements per LDS stage
-static constexpr size_t GE_LDS = 2 * (size_t)GE_STAGE * 2;
+#ifndef HD_GE_TK
+#define HD_GE_TK 64                    // K per LDS stage (32 or 64)
+#endif
+#ifndef HD_GE_STAGES
+#define HD_GE_STAGES 2                 // LDS stages (copies run STAGES - 1 stages ahead)
+#endif
+
+// Tile geometry for K step TK, S LDS stages and NJ 32-wide MFMA tiles per wave
+// along the weight rows (NJ = 4: 256 x 256 tiles; NJ = 2: 256 x 128 halves).
+template <int TK, int S, int NJ>
+struct GeCfg {
+    static constexpr int TN = 2 * 32 * NJ;           // weight rows of the tile
+    static constexpr int CPR = TK / 8;               // 16-byte chunks per LDS row
+    static constexpr int RPI = 64 / CPR;             // rows one copy instruction fills
+    static constexpr int SWZ = 16 / CPR;             // consecutive rows sharing one XOR value
+    static constexpr int STAGE = (GE_TM + TN) * TK;  // 16-bit elements per stage
+    static constexpr int DA = GE_TM / RPI / 4;       // copy instructions per wave and stage, X tile
+    static constexpr int DB = TN / RPI / 4;          // same, weight tile
+    static constexpr size_t LDS = (size_t)S * STAGE * 2;
+    static_assert(TK == 32 || TK == 64, "TK");
+    static_assert(LDS <= 160 * 1024, "LDS");
+};
 
 enum { GE_STORE_Y = 0, GE_SUB_Y = 1 };
 
@@ -83,120 +102,156 @@ __device__ __attribute__((aligned(16))) uint32_t ge_zero16[4] = {0u, 0u, 0u, 0u}
 typedef __attribute__((address_space(3))) void ge_lds_void;
 typedef __attribute__((address_space(1))) const void ge_gbl_void;
 
-template <bool F16, int MODE>
+// s_waitcnt vmcnt(n) for a small run-time n (the copies still allowed in flight).
+__device__ __forceinline__ void ge_wait_copies(int n)
+{
+    switch (n) {
+    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
+    case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+    case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+    case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+    case 12: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
+    case 16: asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
+    case 24: asm volatile("s_waitcnt vmcnt(24)" ::: "memory"); break;
+    case 32: asm volatile("s_waitcnt vmcnt(32)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    }
+}
+
+// Tiles: the X x W product is cut into 256 x 256 tiles, numbered in a grouped
+// order (GE_GROUP_M X tiles per weight tile).  A launch covers the tile
+// numbers lin0 .. lin0 + nlin - 1: one workgroup per tile, with an XCD-aware
+// remap of the workgroup index (consecutive workgroups go to different XCDs;
+// the remap gives each XCD a contiguous run of tile numbers), or, when
+// `split` is set (NJ = 2), two workgroups per tile, each taking 128 of its
+// 256 weight rows (the last, partial round of tiles then fills twice as
+// many CUs).  Workgroup w writes part[2 (pbase + w) .. + 1].
+template <bool F16, int MODE, int TK, int S, int NJ>
 __global__ __launch_bounds__(GE_THREADS, 1) void gemm_err_kernel(const uint16_t *__restrict__ A,
                                                                  const uint16_t *__restrict__ Bm, int64_t M,
-                                                                 int64_t N, int64_t K, int mt, int nt,
-                                                                 float *__restrict__ Y,
+                                                                 int64_t N, int64_t K, int mt, int nt, int lin0,
+                                                                 int nlin, int split, float *__restrict__ Y,
                                                                  const int *__restrict__ erow, double fscale,
-                                                                 double *__restrict__ part)
+                                                                 double *__restrict__ part, int pbase)
 {
+    typedef GeCfg<TK, S, NJ> C;
     typedef typename Mfma16<F16>::v V;
     extern __shared__ __attribute__((aligned(16))) uint16_t glds[];
     __shared__ double red[2][4];
 
-    // tile index: XCD-aware remap, then GE_GROUP_M X tiles per weight tile
-    const int nblk = mt * nt;
     const int hw = blockIdx.x;
-    const int per = nblk / 8;
-    const int lin = hw < per * 8 ? (hw % 8) * per + hw / 8 : hw;
+    int lin, half = 0;
+    if (split) {
+        lin = lin0 + hw / 2;
+        half = hw & 1;
+    } else {
+        const int per = nlin / 8;
+        lin = lin0 + (hw < per * 8 ? (hw % 8) * per + hw / 8 : hw);
+    }
     const int group = lin / (GE_GROUP_M * nt);
     const int first_m = group * GE_GROUP_M;
     const int gm = min(mt - first_m, GE_GROUP_M);
     const int within = lin % (GE_GROUP_M * nt);
     const int tm = first_m + within % gm;
     const int tn = within / gm;
-    const int64_t m0 = (int64_t)tm * GE_TM, n0 = (int64_t)tn * GE_TN;
+    const int64_t m0 = (int64_t)tm * GE_TM, n0 = (int64_t)tn * GE_TN + (int64_t)half * C::TN;
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int wm = wv & 1, wn = wv >> 1;
 
-    // Staging: global -> LDS by the copy path of global_load_lds_dwordx4 (no
-    // registers).  One instruction of a wave fills 1 KB of LDS, 16 bytes per
-    // lane in lane order: 8 rows of 128 bytes (64 K-elements).  Lane l of the
-    // wave's i-th instruction fills LDS row r = 32 i + 8 wv + l / 8, slot
-    // l % 8, and fetches the 16-byte chunk c = slot ^ ((r >> 1) & 7) of that
-    // row: the XOR swizzle spreads the 16 rows of one fragment read over all
-    // 64 banks.  Chunks past K come from ge_zero16; rows past M / N are
-    // clamped to the last row (their outputs are never read).
-    const int lr = 8 * wv + (lane >> 3), slot = lane & 7;
-    int64_t aoff[8], boff[8];
-    int csw[8];
+    // Staging: global -> LDS by global_load_lds_dwordx4 (no registers).  One
+    // instruction of a wave fills 1 KB of LDS, 16 bytes per lane in lane
+    // order: RPI rows of TK elements.  Lane l of the wave's i-th instruction
+    // fills row r = (4 i + wv) RPI + l / CPR, slot l % CPR, and fetches the
+    // 16-byte chunk c = slot ^ ((r / SWZ) % CPR) of that row: the XOR swizzle
+    // spreads the 16 rows of one fragment read over all 64 banks.  Chunks past
+    // K come from ge_zero16; rows past M / N are clamped to the last row
+    // (their outputs are never read).
+    const int lrow = lane / C::CPR, slot = lane % C::CPR;
+    int64_t aoff[C::DA], boff[C::DB];
+    int acs[C::DA], bcs[C::DB];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int r = 32 * i + lr;
-        csw[i] = (slot ^ ((r >> 1) & 7)) * 8;
-        aoff[i] = min(m0 + r, M - 1) * K + csw[i];
-        boff[i] = min(n0 + r, N - 1) * K + csw[i];
+    for (int i = 0; i < C::DA; ++i) {
+        const int r = (4 * i + wv) * C::RPI + lrow;
+        acs[i] = (slot ^ ((r / C::SWZ) % C::CPR)) * 8;
+        aoff[i] = min(m0 + r, M - 1) * K + acs[i];
+    }
+#pragma unroll
+    for (int i = 0; i < C::DB; ++i) {
+        const int r = (4 * i + wv) * C::RPI + lrow;
+        bcs[i] = (slot ^ ((r / C::SWZ) % C::CPR)) * 8;
+        boff[i] = min(n0 + r, N - 1) * K + bcs[i];
     }
 #define GE_ISSUE(k0, buf)                                                                              \
     do {                                                                                               \
-        uint16_t *sa_ = glds + (buf) * GE_STAGE + (8 * wv) * GE_TK;                                    \
-        uint16_t *sb_ = sa_ + GE_TM * GE_TK;                                                           \
-        _Pragma("unroll") for (int i = 0; i < 8; ++i)                                                  \
+        uint16_t *sa_ = glds + (buf) * C::STAGE + wv * C::RPI * TK;                                    \
+        uint16_t *sb_ = sa_ + GE_TM * TK;                                                              \
+        _Pragma("unroll") for (int i = 0; i < C::DA; ++i)                                              \
         {                                                                                              \
-            const bool in_ = (k0) + csw[i] < K;                                                        \
-            const void *pa_ = in_ ? (const void *)(A + aoff[i] + (k0)) : (const void *)ge_zero16;      \
-            const void *pb_ = in_ ? (const void *)(Bm + boff[i] + (k0)) : (const void *)ge_zero16;     \
-            __builtin_amdgcn_global_load_lds((ge_gbl_void *)pa_, (ge_lds_void *)(sa_ + 32 * i * GE_TK), 16, 0, 0); \
-            __builtin_amdgcn_global_load_lds((ge_gbl_void *)pb_, (ge_lds_void *)(sb_ + 32 * i * GE_TK), 16, 0, 0); \
+            const void *p_ = (k0) + acs[i] < K ? (const void *)(A + aoff[i] + (k0)) : (const void *)ge_zero16; \
+            __builtin_amdgcn_global_load_lds((ge_gbl_void *)p_, (ge_lds_void *)(sa_ + 4 * i * C::RPI * TK), 16, 0, 0); \
+        }                                                                                              \
+        _Pragma("unroll") for (int i = 0; i < C::DB; ++i)                                              \
+        {                                                                                              \
+            const void *p_ = (k0) + bcs[i] < K ? (const void *)(Bm + boff[i] + (k0)) : (const void *)ge_zero16; \
+            __builtin_amdgcn_global_load_lds((ge_gbl_void *)p_, (ge_lds_void *)(sb_ + 4 * i * C::RPI * TK), 16, 0, 0); \
         }                                                                                              \
     } while (0)
 
-    of32x16_t acc[4][4];
+    of32x16_t acc[4][NJ];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-    // Fragments of one 16-wide K slice: a[4] (X rows) and b[4] (weight rows),
-    // double-buffered so the slice after the current one is read from LDS
-    // while the current one multiplies.  The last slice of a stage is read
-    // before the barrier, so the first slice of the next stage can be read
-    // right after it, behind the last 16 MFMAs of this stage.
+    // Fragments of one 16-wide K slice: fa[4] (X rows), fb[NJ] (weight rows),
+    // double-buffered so the next slice is read from LDS while the current one
+    // multiplies.
     const int fr = lane & 31, fh = lane >> 5;
-    V fa[2][4], fb[2][4];
+    V fa[2][4], fb[2][NJ];
 #define GE_FRAG(set, bufp, kk)                                                                         \
     do {                                                                                               \
         const int c_ = 2 * (kk) + fh;                                                                  \
         _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                  \
         {                                                                                              \
             const int r_ = wm * 128 + i * 32 + fr;                                                     \
-            fa[set][i] = *reinterpret_cast<const V *>((bufp) + r_ * GE_TK + ((c_ ^ ((r_ >> 1) & 7)) * 8)); \
+            fa[set][i] = *reinterpret_cast<const V *>((bufp) + r_ * TK + ((c_ ^ ((r_ / C::SWZ) % C::CPR)) * 8)); \
         }                                                                                              \
-        _Pragma("unroll") for (int j = 0; j < 4; ++j)                                                  \
+        _Pragma("unroll") for (int j = 0; j < NJ; ++j)                                                 \
         {                                                                                              \
-            const int r_ = GE_TM + wn * 128 + j * 32 + fr;                                             \
-            fb[set][j] = *reinterpret_cast<const V *>((bufp) + r_ * GE_TK + ((c_ ^ ((r_ >> 1) & 7)) * 8)); \
+            const int r_ = wn * 32 * NJ + j * 32 + fr;                                                 \
+            fb[set][j] = *reinterpret_cast<const V *>((bufp) + (GE_TM + r_) * TK + ((c_ ^ ((r_ / C::SWZ) % C::CPR)) * 8)); \
         }                                                                                              \
     } while (0)
 
-    const int ksteps = (int)((K + GE_TK - 1) / GE_TK);
-    GE_ISSUE((int64_t)0, 0);
-    __syncthreads();  // waits for the copies (vmcnt) and publishes them
-    GE_FRAG(0, glds, 0);
-    for (int ks = 0; ks < ksteps; ++ks) {
-        const int buf = ks & 1;
-        const bool more = ks + 1 < ksteps;
-        if (more) GE_ISSUE((int64_t)(ks + 1) * GE_TK, buf ^ 1);
-        const uint16_t *base = glds + buf * GE_STAGE;
+    // Pipeline: the copies of stage ks + S - 1 are issued right after the
+    // barrier that opens stage ks (that barrier also certifies that every wave
+    // has finished reading the buffer they overwrite, the one of stage ks - 1).
+    // Before the barrier each wave waits for its own copies of stage ks (the
+    // copies of later stages may stay in flight) and for its LDS reads.
+    const int ksteps = (int)((K + TK - 1) / TK);
+    constexpr int D = C::DA + C::DB;
 #pragma unroll
-        for (int kk = 0; kk < GE_TK / 16; ++kk) {
+    for (int p = 0; p < S - 1; ++p)
+        if (p < ksteps) GE_ISSUE((int64_t)p * TK, p);
+    for (int ks = 0; ks < ksteps; ++ks) {
+        ge_wait_copies(min(S - 2, ksteps - 1 - ks) * D);
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        if (ks + S - 1 < ksteps) GE_ISSUE((int64_t)(ks + S - 1) * TK, (ks + S - 1) % S);
+        const uint16_t *base = glds + (ks % S) * C::STAGE;
+        GE_FRAG(0, base, 0);
+#pragma unroll
+        for (int kk = 0; kk < TK / 16; ++kk) {
             const int cur = kk & 1;
-            if (kk + 1 < GE_TK / 16) {
-                GE_FRAG(cur ^ 1, base, kk + 1);
-            } else {
-                // every read of this stage is issued: wait for the next
-                // stage's copies, then start reading it
-                __syncthreads();
-                if (more) GE_FRAG(cur ^ 1, glds + (buf ^ 1) * GE_STAGE, 0);
-            }
+            if (kk + 1 < TK / 16) GE_FRAG(cur ^ 1, base, kk + 1);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = Mfma16<F16>::op(fa[cur][i], fb[cur][j], acc[i][j]);
+                for (int j = 0; j < NJ; ++j) acc[i][j] = Mfma16<F16>::op(fa[cur][i], fb[cur][j], acc[i][j]);
         }
     }
 #undef GE_FRAG
@@ -205,39 +260,41 @@ __global__ __launch_bounds__(GE_THREADS, 1) void gemm_err_kernel(const uint16_t 
     // epilogue: accumulator v of lane l in a 32 x 32 tile is row
     // 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32
     double sd = 0.0, sy = 0.0;
-    const int64_t nb0 = n0 + wn * 128 + (lane & 31);
+    const int64_t nb0 = n0 + wn * 32 * NJ + (lane & 31);
+    const int64_t mb0 = m0 + wm * 128 + 4 * (lane >> 5);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        int64_t mrow[16];
-        double f[16];
+        // row exponents of this lane's 16 rows in tile row i (SUB with erow)
+        int ev[16];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            mrow[v] = m0 + wm * 128 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-            f[v] = 1.0;
-            if (MODE == GE_SUB_Y && erow != nullptr) f[v] = ldexp(fscale, erow[min(mrow[v], M - 1)]);
-        }
+        for (int v = 0; v < 16; ++v)
+            ev[v] = (MODE == GE_SUB_Y && erow != nullptr) ? erow[min(mb0 + i * 32 + 8 * (v >> 2) + (v & 3), M - 1)] : 0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < NJ; ++j) {
             const int64_t n = nb0 + j * 32;
-            const int64_t nc = min(n, N - 1);
+            const bool nin = n < N;
             if (MODE == GE_STORE_Y) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
-                    if (mrow[v] < M && n < N) {
+                    const int64_t m = mb0 + i * 32 + 8 * (v >> 2) + (v & 3);
+                    if (m < M && nin) {
                         const float a = acc[i][j][v];
-                        Y[mrow[v] * N + n] = a;
+                        Y[m * N + n] = a;
                         sy = __builtin_fma((double)a, (double)a, sy);
                     }
                 }
             } else {
-                // all 16 reads of Y in flight before the first use
+                // the 16 reads of Y for this 32 x 32 tile are in flight together
+                const int64_t nc = min(n, N - 1);
                 float yv[16];
 #pragma unroll
-                for (int v = 0; v < 16; ++v) yv[v] = Y[min(mrow[v], M - 1) * N + nc];
+                for (int v = 0; v < 16; ++v) yv[v] = Y[min(mb0 + i * 32 + 8 * (v >> 2) + (v & 3), M - 1) * N + nc];
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
-                    const double d = (double)acc[i][j][v] * f[v] - (double)yv[v];
-                    sd = (mrow[v] < M && n < N) ? __builtin_fma(d, d, sd) : sd;
+                    const int64_t m = mb0 + i * 32 + 8 * (v >> 2) + (v & 3);
+                    const double f = ldexp(fscale, ev[v]);
+                    const double d = (double)acc[i][j][v] * f - (double)yv[v];
+                    sd = (m < M && nin) ? __builtin_fma(d, d, sd) : sd;
                 }
             }
         }
@@ -253,8 +310,8 @@ __global__ __launch_bounds__(GE_THREADS, 1) void gemm_err_kernel(const uint16_t 
     }
     __syncthreads();
     if (tid == 0) {
-        part[2 * (int64_t)blockIdx.x] = (red[0][0] + red[0][1]) + (red[0][2] + red[0][3]);
-        part[2 * (int64_t)blockIdx.x + 1] = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
+        part[2 * (int64_t)(pbase + hw)] = (red[0][0] + red[0][1]) + (red[0][2] + red[0][3]);
+        part[2 * (int64_t)(pbase + hw) + 1] = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
     }
 }
 
@@ -387,7 +444,7 @@ __global__ __launch_bounds__(256) void outref_final(const double *__restrict__ p
 // ---------------------------------------------------------------- layout --
 static int64_t al256(int64_t x) { return (x + 255) / 256 * 256; }
 static int64_t ge_tiles(int64_t M, int64_t N) { return ((M + GE_TM - 1) / GE_TM) * ((N + GE_TN - 1) / GE_TN); }
-static int64_t at_least1(int64_t x) { return x > 0 ? x : 1; }
+static int64_t ge_parts(int64_t M, int64_t N) { return ge_tiles(M, N) + 1024; }  // tiles + split halves
 
 RefLayout output_reference_layout(int64_t M, int64_t N, int64_t K)
 {
@@ -396,27 +453,65 @@ RefLayout output_reference_layout(int64_t M, int64_t N, int64_t K)
     L.e = L.y + al256(M * N * 4);
     L.x = L.e + al256(M * 4);
     L.part = L.x + al256(M * K * 2);
-    L.bytes = L.part + al256(at_least1(ge_tiles(M, N)) * 16);
+    L.bytes = L.part + al256(ge_parts(M, N) * 16);
     return L;
 }
 
 size_t output_error_codes_ws(int64_t M, int64_t N, int64_t K)
 {
-    return (size_t)(al256(N * K * 2) + al256(at_least1(ge_tiles(M, N)) * 16));
+    return (size_t)(al256(N * K * 2) + al256(ge_parts(M, N) * 16));
 }
 
+// CUs of the current device (cached per device).
+static int device_cus()
+{
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
+// Launch plan: T full tiles on `cus` CUs run in ceil(T / cus) rounds; when
+// the last round would fill at most half of the CUs, its tiles run as
+// 256 x 128 halves instead (the round then takes half a tile's time).
+// Returns the number of workgroup partials written.
 template <bool F16, int MODE>
 static hipError_t launch_gemm_err(const uint16_t *A, const uint16_t *Bm, int64_t M, int64_t N, int64_t K,
-                                  float *Y, const int *erow, double fscale, double *part, hipStream_t st)
+                                  float *Y, const int *erow, double fscale, double *part, int64_t *nparts,
+                                  hipStream_t st)
 {
+    constexpr int TK = HD_GE_TK, S = HD_GE_STAGES;
+    typedef GeCfg<TK, S, 4> CF;
+    typedef GeCfg<TK, S, 2> CH;
     const int mt = (int)((M + GE_TM - 1) / GE_TM), nt = (int)((N + GE_TN - 1) / GE_TN);
-    const int64_t nb = (int64_t)mt * nt;
-    if (nb == 0) return hipSuccess;
-    hipError_t e = hipFuncSetAttribute((const void *)gemm_err_kernel<F16, MODE>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)GE_LDS);
-    if (e != hipSuccess) return e;
-    gemm_err_kernel<F16, MODE><<<(unsigned)nb, GE_THREADS, GE_LDS, st>>>(A, Bm, M, N, K, mt, nt, Y, erow, fscale,
-                                                                         part);
+    const int64_t T = (int64_t)mt * nt;
+    *nparts = 0;
+    if (T == 0) return hipSuccess;
+    const int cus = device_cus();
+    const int64_t rem = T % cus;
+    const bool split = rem > 0 && 2 * rem <= cus;
+    const int64_t nfull = split ? T - rem : T;
+    hipError_t e;
+    if (nfull > 0) {
+        e = hipFuncSetAttribute((const void *)gemm_err_kernel<F16, MODE, TK, S, 4>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)CF::LDS);
+        if (e != hipSuccess) return e;
+        gemm_err_kernel<F16, MODE, TK, S, 4><<<(unsigned)nfull, GE_THREADS, CF::LDS, st>>>(
+            A, Bm, M, N, K, mt, nt, 0, (int)nfull, 0, Y, erow, fscale, part, 0);
+    }
+    if (split) {
+        e = hipFuncSetAttribute((const void *)gemm_err_kernel<F16, MODE, TK, S, 2>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)CH::LDS);
+        if (e != hipSuccess) return e;
+        gemm_err_kernel<F16, MODE, TK, S, 2><<<(unsigned)(2 * rem), GE_THREADS, CH::LDS, st>>>(
+            A, Bm, M, N, K, mt, nt, (int)nfull, (int)rem, 1, Y, erow, fscale, part, (int)nfull);
+    }
+    *nparts = nfull + (split ? 2 * rem : 0);
     return hipGetLastError();
 }
 
@@ -431,10 +526,11 @@ hipError_t launch_output_reference(const void *X, int64_t M, const void *W, int6
     uint16_t *Xh = reinterpret_cast<uint16_t *>(r + L.x);
     double *part = reinterpret_cast<double *>(r + L.part);
     if (M > 0 && K > 0) xprep_kernel<<<(unsigned)M, 256, 0, st>>>((const bf16_t *)X, K, Xh, erow);
+    int64_t np = 0;
     hipError_t e = launch_gemm_err<false, GE_STORE_Y>((const uint16_t *)X, (const uint16_t *)W, M, N, K, Y, nullptr,
-                                                      1.0, part, st);
+                                                      1.0, part, &np, st);
     if (e != hipSuccess) return e;
-    outref_final<<<1, 256, 0, st>>>(part, ge_tiles(M, N), nullptr, ysq, nullptr, nullptr);
+    outref_final<<<1, 256, 0, st>>>(part, np, nullptr, ysq, nullptr, nullptr);
     return hipGetLastError();
 }
 
@@ -471,12 +567,13 @@ hipError_t launch_output_error_codes(int fmt, int B, const void *X, int64_t M, c
         default: return hipErrorInvalidValue;
         }
     }
+    int64_t np = 0;
     if (fmt == HD_INT8_E4M3)
-        e = launch_gemm_err<true, GE_SUB_Y>(Xh, opnd, M, N, K, Y, erow, 1.0 / 127.0, part, st);
+        e = launch_gemm_err<true, GE_SUB_Y>(Xh, opnd, M, N, K, Y, erow, 1.0 / 127.0, part, &np, st);
     else
-        e = launch_gemm_err<false, GE_SUB_Y>((const uint16_t *)X, opnd, M, N, K, Y, nullptr, 1.0, part, st);
+        e = launch_gemm_err<false, GE_SUB_Y>((const uint16_t *)X, opnd, M, N, K, Y, nullptr, 1.0, part, &np, st);
     if (e != hipSuccess) return e;
-    outref_final<<<1, 256, 0, st>>>(part, ge_tiles(M, N), ysq, nullptr, out, sums);
+    outref_final<<<1, 256, 0, st>>>(part, np, ysq, nullptr, out, sums);
     return hipGetLastError();
 }
 
