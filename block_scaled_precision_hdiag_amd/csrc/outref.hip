@@ -21,16 +21,21 @@
 //     in a fixed order by a one-workgroup final kernel.
 //
 // GEMM tiling (gfx950, v_mfma_f32_32x32x16_{bf16,f16}, wave64):
-//   - 256 threads = 4 waves in a 2 x 2 grid; workgroup tile 256 rows of X x
-//     256 rows of the weight operand; each wave owns 128 x 128 outputs as
-//     4 x 4 MFMA tiles (256 float accumulators per lane), so every 16-B LDS
-//     fragment read feeds four MFMAs;
-//   - K is walked 64 at a time through two LDS stages (144 KB, dynamic): the
-//     global loads for step k+1 are in flight while step k multiplies; LDS rows
-//     are padded to 144 bytes so the 16-byte fragment reads of 16 consecutive
-//     rows hit distinct banks;
+//   - workgroup tile 256 rows of X x 256 rows of the weight operand, 8 waves
+//     in a 2 x 4 grid, each owning 128 x 64 outputs as 4 x 2 MFMA tiles (128
+//     float accumulators per lane); two waves per SIMD, so one wave's LDS and
+//     barrier waits hide behind the other's MFMAs;
+//   - K is walked 64 at a time through two 64 KB LDS stages filled by
+//     global_load_lds_dwordx4 (global -> LDS without registers), one stage
+//     ahead of the MFMAs; the LDS image of every 128-byte row slice is
+//     XOR-swizzled so the 16-byte fragment reads of 16 consecutive rows hit all
+//     64 banks (no conflicts, checked with SQ_LDS_BANK_CONFLICT); the fragments
+//     of the next 16-wide K slice are read while the current one multiplies;
 //   - tile order: the workgroups one XCD runs at once cover 8 X tiles for each
-//     weight tile, so they share X and W panels in that XCD's L2.
+//     weight tile, so they share X and weight panels in that XCD's L2;
+//   - when the last round of tiles would fill at most half of the CUs, those
+//     tiles run as 256 x 128 halves (a second launch), so that round takes
+//     about half a tile's time.
 #include "common.hpp"
 #include "formats.hpp"
 #include "kernels.hpp"
@@ -43,7 +48,6 @@ typedef float of32x16_t __attribute__((ext_vector_type(16)));
 
 static constexpr int GE_TM = 256;      // X rows per tile
 static constexpr int GE_TN = 256;      // weight rows per full tile
-static constexpr int GE_THREADS = 256;
 static constexpr int GE_GROUP_M = 8;
 #ifndef HD_GE_TK
 #define HD_GE_TK 64                    // K per LDS stage (32 or 64)
@@ -51,20 +55,27 @@ static constexpr int GE_GROUP_M = 8;
 #ifndef HD_GE_STAGES
 #define HD_GE_STAGES 2                 // LDS stages (copies run STAGES - 1 stages ahead)
 #endif
+#ifndef HD_GE_WN
+#define HD_GE_WN 4                     // waves along the weight rows (4: 8 waves of 128 x 64; 2: 4 of 128 x 128)
+#endif
 
-// Tile geometry for K step TK, S LDS stages and NJ 32-wide MFMA tiles per wave
-// along the weight rows (NJ = 4: 256 x 256 tiles; NJ = 2: 256 x 128 halves).
-template <int TK, int S, int NJ>
+// Tile geometry for K step TK, S LDS stages, 2 x WN waves and NJ 32-wide MFMA
+// tiles per wave along the weight rows (WN NJ = 8: 256 x 256 tiles; 4: the
+// 256 x 128 halves).  Each wave owns 128 X rows x 32 NJ weight rows.
+template <int TK, int S, int WN, int NJ>
 struct GeCfg {
-    static constexpr int TN = 2 * 32 * NJ;           // weight rows of the tile
+    static constexpr int NW = 2 * WN;                // waves per workgroup
+    static constexpr int THREADS = 64 * NW;
+    static constexpr int TN = WN * 32 * NJ;          // weight rows of the tile
     static constexpr int CPR = TK / 8;               // 16-byte chunks per LDS row
     static constexpr int RPI = 64 / CPR;             // rows one copy instruction fills
     static constexpr int SWZ = 16 / CPR;             // consecutive rows sharing one XOR value
     static constexpr int STAGE = (GE_TM + TN) * TK;  // 16-bit elements per stage
-    static constexpr int DA = GE_TM / RPI / 4;       // copy instructions per wave and stage, X tile
-    static constexpr int DB = TN / RPI / 4;          // same, weight tile
+    static constexpr int DA = GE_TM / RPI / NW;      // copy instructions per wave and stage, X tile
+    static constexpr int DB = TN / RPI / NW;         // same, weight tile
     static constexpr size_t LDS = (size_t)S * STAGE * 2;
     static_assert(TK == 32 || TK == 64, "TK");
+    static_assert(DA * RPI * NW == GE_TM && DB * RPI * NW == TN, "copy split");
     static_assert(LDS <= 160 * 1024, "LDS");
 };
 
@@ -90,10 +101,6 @@ struct Mfma16<true> {
 };
 
 // ------------------------------------------------------------------ GEMM --
-// acc = A B^T for one 256 x 256 tile (A [M][K], B [N][K], 16-bit, K % 8 == 0),
-// then MODE GE_STORE_Y: Y[m][n] = acc, part = {0, sum acc^2};
-//      MODE GE_SUB_Y:   d = acc f_m - Y[m][n] with f_m = 2^erow[m] * fscale
-//                       (f_m = 1 when erow is NULL), part = {sum d^2, 0}.
 // A 16-byte block of zeros in global memory: the source of every staged chunk
 // that lies past K (its LDS slot must hold zeros; the copy engine cannot
 // select).
@@ -125,21 +132,27 @@ __device__ __forceinline__ void ge_wait_copies(int n)
 // numbers lin0 .. lin0 + nlin - 1: one workgroup per tile, with an XCD-aware
 // remap of the workgroup index (consecutive workgroups go to different XCDs;
 // the remap gives each XCD a contiguous run of tile numbers), or, when
-// `split` is set (NJ = 2), two workgroups per tile, each taking 128 of its
-// 256 weight rows (the last, partial round of tiles then fills twice as
-// many CUs).  Workgroup w writes part[2 (pbase + w) .. + 1].
-template <bool F16, int MODE, int TK, int S, int NJ>
-__global__ __launch_bounds__(GE_THREADS, 1) void gemm_err_kernel(const uint16_t *__restrict__ A,
+// `split` is set (half-width configuration), two workgroups per tile, each
+// taking 128 of its 256 weight rows (the last, partial round of tiles then
+// fills twice as many CUs).
+// Each workgroup computes acc = A B^T for its tile (A [M][K], B [N][K],
+// 16-bit, K % 8 == 0), then
+//   MODE GE_STORE_Y: Y[m][n] = acc, partial {0, sum acc^2};
+//   MODE GE_SUB_Y:   d = acc f_m - Y[m][n] with f_m = fscale 2^erow[m]
+//                    (f_m = 1 when erow is NULL), partial {sum d^2, 0};
+// workgroup w writes its partial to part[2 (pbase + w) .. + 1].
+template <bool F16, int MODE, int TK, int S, int WN, int NJ>
+__global__ __launch_bounds__(128 * WN, 1) void gemm_err_kernel(const uint16_t *__restrict__ A,
                                                                  const uint16_t *__restrict__ Bm, int64_t M,
                                                                  int64_t N, int64_t K, int mt, int nt, int lin0,
                                                                  int nlin, int split, float *__restrict__ Y,
                                                                  const int *__restrict__ erow, double fscale,
                                                                  double *__restrict__ part, int pbase)
 {
-    typedef GeCfg<TK, S, NJ> C;
+    typedef GeCfg<TK, S, WN, NJ> C;
     typedef typename Mfma16<F16>::v V;
     extern __shared__ __attribute__((aligned(16))) uint16_t glds[];
-    __shared__ double red[2][4];
+    __shared__ double red[2][C::NW];
 
     const int hw = blockIdx.x;
     int lin, half = 0;
@@ -174,13 +187,13 @@ __global__ __launch_bounds__(GE_THREADS, 1) void gemm_err_kernel(const uint16_t 
     int acs[C::DA], bcs[C::DB];
 #pragma unroll
     for (int i = 0; i < C::DA; ++i) {
-        const int r = (4 * i + wv) * C::RPI + lrow;
+        const int r = (C::NW * i + wv) * C::RPI + lrow;
         acs[i] = (slot ^ ((r / C::SWZ) % C::CPR)) * 8;
         aoff[i] = min(m0 + r, M - 1) * K + acs[i];
     }
 #pragma unroll
     for (int i = 0; i < C::DB; ++i) {
-        const int r = (4 * i + wv) * C::RPI + lrow;
+        const int r = (C::NW * i + wv) * C::RPI + lrow;
         bcs[i] = (slot ^ ((r / C::SWZ) % C::CPR)) * 8;
         boff[i] = min(n0 + r, N - 1) * K + bcs[i];
     }
@@ -191,12 +204,12 @@ __global__ __launch_bounds__(GE_THREADS, 1) void gemm_err_kernel(const uint16_t 
         _Pragma("unroll") for (int i = 0; i < C::DA; ++i)                                              \
         {                                                                                              \
             const void *p_ = (k0) + acs[i] < K ? (const void *)(A + aoff[i] + (k0)) : (const void *)ge_zero16; \
-            __builtin_amdgcn_global_load_lds((ge_gbl_void *)p_, (ge_lds_void *)(sa_ + 4 * i * C::RPI * TK), 16, 0, 0); \
+            __builtin_amdgcn_global_load_lds((ge_gbl_void *)p_, (ge_lds_void *)(sa_ + C::NW * i * C::RPI * TK), 16, 0, 0); \
         }                                                                                              \
         _Pragma("unroll") for (int i = 0; i < C::DB; ++i)                                              \
         {                                                                                              \
             const void *p_ = (k0) + bcs[i] < K ? (const void *)(Bm + boff[i] + (k0)) : (const void *)ge_zero16; \
-            __builtin_amdgcn_global_load_lds((ge_gbl_void *)p_, (ge_lds_void *)(sb_ + 4 * i * C::RPI * TK), 16, 0, 0); \
+            __builtin_amdgcn_global_load_lds((ge_gbl_void *)p_, (ge_lds_void *)(sb_ + C::NW * i * C::RPI * TK), 16, 0, 0); \
         }                                                                                              \
     } while (0)
 
@@ -310,8 +323,14 @@ __global__ __launch_bounds__(GE_THREADS, 1) void gemm_err_kernel(const uint16_t 
     }
     __syncthreads();
     if (tid == 0) {
-        part[2 * (int64_t)(pbase + hw)] = (red[0][0] + red[0][1]) + (red[0][2] + red[0][3]);
-        part[2 * (int64_t)(pbase + hw) + 1] = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
+        double a = 0.0, b = 0.0;
+#pragma unroll
+        for (int w = 0; w < C::NW; ++w) {
+            a += red[0][w];
+            b += red[1][w];
+        }
+        part[2 * (int64_t)(pbase + hw)] = a;
+        part[2 * (int64_t)(pbase + hw) + 1] = b;
     }
 }
 
@@ -485,9 +504,10 @@ static hipError_t launch_gemm_err(const uint16_t *A, const uint16_t *Bm, int64_t
                                   float *Y, const int *erow, double fscale, double *part, int64_t *nparts,
                                   hipStream_t st)
 {
-    constexpr int TK = HD_GE_TK, S = HD_GE_STAGES;
-    typedef GeCfg<TK, S, 4> CF;
-    typedef GeCfg<TK, S, 2> CH;
+    constexpr int TK = HD_GE_TK, S = HD_GE_STAGES, WN = HD_GE_WN, NJF = 8 / WN, NJH = 4 / WN;
+    typedef GeCfg<TK, S, WN, NJF> CF;
+    typedef GeCfg<TK, S, WN, NJH> CH;
+    static_assert(CF::TN == GE_TN && 2 * CH::TN == GE_TN, "tile widths");
     const int mt = (int)((M + GE_TM - 1) / GE_TM), nt = (int)((N + GE_TN - 1) / GE_TN);
     const int64_t T = (int64_t)mt * nt;
     *nparts = 0;
@@ -498,17 +518,17 @@ static hipError_t launch_gemm_err(const uint16_t *A, const uint16_t *Bm, int64_t
     const int64_t nfull = split ? T - rem : T;
     hipError_t e;
     if (nfull > 0) {
-        e = hipFuncSetAttribute((const void *)gemm_err_kernel<F16, MODE, TK, S, 4>,
+        e = hipFuncSetAttribute((const void *)gemm_err_kernel<F16, MODE, TK, S, WN, NJF>,
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)CF::LDS);
         if (e != hipSuccess) return e;
-        gemm_err_kernel<F16, MODE, TK, S, 4><<<(unsigned)nfull, GE_THREADS, CF::LDS, st>>>(
+        gemm_err_kernel<F16, MODE, TK, S, WN, NJF><<<(unsigned)nfull, CF::THREADS, CF::LDS, st>>>(
             A, Bm, M, N, K, mt, nt, 0, (int)nfull, 0, Y, erow, fscale, part, 0);
     }
     if (split) {
-        e = hipFuncSetAttribute((const void *)gemm_err_kernel<F16, MODE, TK, S, 2>,
+        e = hipFuncSetAttribute((const void *)gemm_err_kernel<F16, MODE, TK, S, WN, NJH>,
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)CH::LDS);
         if (e != hipSuccess) return e;
-        gemm_err_kernel<F16, MODE, TK, S, 2><<<(unsigned)(2 * rem), GE_THREADS, CH::LDS, st>>>(
+        gemm_err_kernel<F16, MODE, TK, S, WN, NJH><<<(unsigned)(2 * rem), CH::THREADS, CH::LDS, st>>>(
             A, Bm, M, N, K, mt, nt, (int)nfull, (int)rem, 1, Y, erow, fscale, part, (int)nfull);
     }
     *nparts = nfull + (split ? 2 * rem : 0);

@@ -10,25 +10,28 @@
 //
 // Mapping (the work is FP32-VALU bound, ~10 instructions per weight and
 // candidate):
-//   - one lane owns one block segment of SEG = min(B, 32) weights held in
-//     registers; a block of B > 32 spans LPB = B / 32 adjacent lanes whose
-//     partial objectives are combined with lane shuffles;
+//   - one lane owns one block segment of SEG weights held in registers (32,
+//     or 16 for the weighted search, which also holds h); a block of B > SEG
+//     spans LPB = B / SEG adjacent lanes whose partial objectives are combined
+//     with lane shuffles;
 //   - all lanes of a workgroup share one block column (so h_j is the same for
-//     every lane of a wave and is loaded once), and walk the candidates in
-//     lock-step: the candidate (s, 1/s) pair is a broadcast read from LDS and
-//     the running argmin needs no cross-lane reduction;
+//     every lane of a wave and is loaded once) and walk the candidates in
+//     lock-step, reading each candidate's (s, 1/s) from an LDS table; the
+//     running argmin is per lane and needs no cross-lane reduction;
 //   - each residual is exact in fp32 and squared / accumulated in float64, so
 //     the objective differs from its exact value only by float64 rounding;
 //   - candidates at and above the first scale that rounds the block's amax to
-//     zero all give sum_j om_j w_j^2 (every element encodes to 0), so the wave
-//     stops at the largest such first-zero code over its lanes: the skipped
-//     codes could only tie, and ties keep the lower code;
-//   - the wave starts from a window around its Naive codes and widens it only
-//     while some lane cannot prove the candidates outside it strictly worse
-//     than its best so far: below the window every element above fl32(Q s)
-//     saturates (sat_lower_bound), above it every element that rounds to zero
-//     stays zero (zero_lower_bound).  Both bounds hold for the objective as the
-//     kernel computes it, so the chosen code is the one the full scan picks.
+//     zero all give sum_j om_j w_j^2 (every element encodes to 0): they could
+//     only tie, and ties keep the lower code, so they are never evaluated;
+//   - INT8: each lane walks candidate offsets from its own block's Naive
+//     code (the optimum lies within a binade above it for nearly every
+//     block), so the rows of different magnitude that share a wave share
+//     offsets, not codes; the window widens only while some lane cannot prove
+//     the candidates outside it strictly worse than its best so far: below it
+//     every element above fl32(Q s) saturates (sat_lower_bound), above it
+//     every element a <= s stays at code 0 or 1 (small_lower_bound).  Both
+//     bounds hold for the objective as the kernel computes it, so the chosen
+//     code is the one the full scan picks.
 #pragma once
 #include "encode.hpp"
 #include "kernels.hpp"
@@ -55,20 +58,22 @@ __device__ __forceinline__ double sat_lower_bound(const float *a, const double *
     return group_sum<LPB>(lb);
 }
 
-// Lower bound, valid for every candidate scale s' >= s, of the objective the
-// kernel computes: an element that rounds to code 0 at s rounds to 0 at every
-// larger scale (quotients only fall), where its residual is exactly a, so it
-// adds exactly om a^2; the other elements add >= 0.
-template <int EK, int SK, bool ONE_STEP, int SEG, int LPB, bool WEIGHTED>
-__device__ __forceinline__ double zero_lower_bound(const float *a, const double *om, float s)
+// Lower bound, valid for every INT8 candidate scale s' >= s, of the
+// objective the kernel computes: an element with a <= s has a / s' <= 1, so it
+// encodes to q = 0 (residual a) or q = 1 (residual s' - a >= s - a, exact in
+// fp32 by Sterbenz's lemma); it adds >= om min(a, s - a)^2, the others >= 0.
+// (For a < s / 2 this is the zero-code term a^2; the s - a branch also bounds
+// the elements that round to 1.)
+template <int SEG, int LPB, bool WEIGHTED>
+__device__ __forceinline__ double small_lower_bound(const float *a, const double *om, float s)
 {
-    const float r = 1.0f / s;
+    const double sd = (double)s;
     double lb = 0.0;
 #pragma unroll
     for (int j = 0; j < SEG; ++j) {
-        const bool zero = round_elem<EK>(quotient<SK, ONE_STEP>(a[j], s, r)) == 0.0f;
         const double aj = (double)a[j];
-        lb += zero ? (WEIGHTED ? om[j] : 1.0) * (aj * aj) : 0.0;
+        const double t = aj <= sd ? fmin(aj, sd - aj) : 0.0;
+        lb += (WEIGHTED ? om[j] : 1.0) * (t * t);
     }
     return group_sum<LPB>(lb);
 }
@@ -152,12 +157,20 @@ __global__ __launch_bounds__(256) void search_kernel(const T *__restrict__ W, in
         else
             lo = mid + 1;
     }
-    const int cend = __builtin_amdgcn_readfirstlane(wave_max_int(lo < NC ? lo : NC - 1));
+    // every candidate from cendl on gives sum om a^2 (all elements encode to 0)
+    const int cendl = lo < NC ? lo : NC - 1;
+    // the lane's Naive candidate: each lane walks offsets from its own Naive
+    // code, so rows of different magnitude in one wave share the offsets, not
+    // the codes
+    const int cb = min(max(naive_code<EK, SK>(amax) - C0, 0), cendl);
 
     double best = __builtin_huge_val();
     int best_c = 0;
-    auto eval_range = [&](int lo, int hi) {
-        for (int c = lo; c <= hi; ++c) {
+    // evaluate offsets o0..o1 from cb; indices are clamped to [0, cendl]:
+    // a repeated candidate cannot change the argmin (ties keep the lower code)
+    auto eval_range = [&](int o0, int o1) {
+        for (int o = o0; o <= o1; ++o) {
+            const int c = min(max(cb + o, 0), cendl);
             const float2 sr = cand[c];
             double acc0 = 0.0, acc1 = 0.0;
 #pragma unroll
@@ -179,29 +192,28 @@ __global__ __launch_bounds__(256) void search_kernel(const T *__restrict__ W, in
             }
         }
     };
-    // start from a binade below the lowest to two binades above the highest
-    // Naive code of the wave; extend either way only while some lane cannot
-    // prove the candidates beyond the window worse than its best so far
-    const int cn = naive_code<EK, SK>(amax) - C0;
-    int clo = cn - 8, chi = cn + 16;
-    clo = __builtin_amdgcn_readfirstlane(-wave_max_int(-(clo < 0 ? 0 : clo)));
-    chi = __builtin_amdgcn_readfirstlane(wave_max_int(chi));
-    if (chi > cend) chi = cend;
-    if (clo > chi) clo = chi;
-    eval_range(clo, chi);
-    while (chi < cend) {
-        const double lb = zero_lower_bound<EK, SK, ONE_STEP, SEG, LPB, WEIGHTED>(a, om, cand[chi + 1].x);
-        if (wave_all(!active || lb * (1.0 - 0x1p-20) > best)) break;
-        const int nhi = chi + 16 < cend ? chi + 16 : cend;
-        eval_range(chi + 1, nhi);
-        chi = nhi;
+    // start one code below Naive to one binade above it (where the optimum
+    // lies for nearly every block); widen by SEARCH_STEP codes while some
+    // lane cannot prove the candidates beyond its window strictly worse than
+    // its best so far (above: small_lower_bound; below: sat_lower_bound)
+    constexpr int SEARCH_STEP = 4;
+    int olo = -1, ohi = 8;
+    eval_range(olo, ohi);
+    for (;;) {
+        const int c1 = cb + ohi + 1;
+        const double lb = small_lower_bound<SEG, LPB, WEIGHTED>(a, om, cand[min(c1, NC - 1)].x);
+        const bool need = active && c1 <= cendl && !(lb * (1.0 - 0x1p-20) > best);
+        if (wave_all(!need)) break;
+        eval_range(ohi + 1, ohi + SEARCH_STEP);
+        ohi += SEARCH_STEP;
     }
-    while (clo > 0) {
-        const double lb = sat_lower_bound<EK, SEG, LPB, WEIGHTED>(a, om, cand[clo - 1].x);
-        if (wave_all(!active || lb * (1.0 - 0x1p-20) > best)) break;
-        const int nlo = clo > 16 ? clo - 16 : 0;
-        eval_range(nlo, clo - 1);
-        clo = nlo;
+    for (;;) {
+        const int c1 = cb + olo - 1;
+        const double lb = sat_lower_bound<EK, SEG, LPB, WEIGHTED>(a, om, cand[max(c1, 0)].x);
+        const bool need = active && c1 >= 0 && !(lb * (1.0 - 0x1p-20) > best);
+        if (wave_all(!need)) break;
+        eval_range(olo - SEARCH_STEP, olo - 1);
+        olo -= SEARCH_STEP;
     }
 
     // encode the segment with the chosen scale
@@ -346,29 +358,19 @@ __global__ __launch_bounds__(256) void search_hw_kernel(const T *__restrict__ W,
         }
     };
     // start below the lowest Naive code of the wave (a binade for E4M3 grids,
-    // two powers of two for E8M0); extend downward only while some lane cannot
-    // prove the lower candidates worse
-    // No zero bound here: E8M0 grids stop within a few codes of Naive anyway,
-    // E4M3 elements zero almost nothing until the very top, and for E2M1 on
-    // the E4M3 grid the extra passes (each re-divides by every mantissa) cost
-    // more than the candidates they save (measured).  INT8 uses it.
-    constexpr bool UP_PRUNE = false;
-    constexpr int MARGIN = SK == SCALE_E8M0 ? 2 : 8, UP = 16;
+    // two powers of two for E8M0) and run up to the first all-zero code;
+    // extend downward only while some lane cannot prove the lower candidates
+    // worse.  (No upper bound here: E8M0 grids stop within a few codes of
+    // Naive anyway, and for the E2M1 / E4M3 element grids the bound passes,
+    // each re-dividing by every mantissa, cost more than the candidates they
+    // save.)
+    constexpr int MARGIN = SK == SCALE_E8M0 ? 2 : 8;
     constexpr int STEP = SK == SCALE_E8M0 ? 4 : 16;
     const int cn = naive_code<EK, SK>(amax) - C0;
-    int clo = cn - MARGIN, chi = UP_PRUNE ? cn + UP : cend;
+    int clo = cn - MARGIN, chi = cend;
     clo = __builtin_amdgcn_readfirstlane(-wave_max_int(-(clo < 0 ? 0 : clo)));
-    chi = __builtin_amdgcn_readfirstlane(wave_max_int(chi));
-    if (chi > cend) chi = cend;
     if (clo > chi) clo = chi;
     eval_range(clo, chi);
-    while (UP_PRUNE && chi < cend) {
-        const double lb = zero_lower_bound<EK, SK, ONE_STEP, SEG, LPB, WEIGHTED>(a, om, scale_value(SK, C0 + chi + 1));
-        if (wave_all(!active || lb * (1.0 - 0x1p-20) > best)) break;
-        const int nhi = chi + STEP < cend ? chi + STEP : cend;
-        eval_range(chi + 1, nhi);
-        chi = nhi;
-    }
     while (clo > 0) {
         const double lb = sat_lower_bound<EK, SEG, LPB, WEIGHTED>(a, om, scale_value(SK, C0 + clo - 1));
         if (wave_all(!active || lb * (1.0 - 0x1p-20) > best)) break;
