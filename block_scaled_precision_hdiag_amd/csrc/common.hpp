@@ -42,6 +42,38 @@ __device__ __forceinline__ void load8<float>(const float *p, float *v)
     v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
+// load8 with the non-temporal hint: for data streamed once (the copy of it
+// need not stay in L2 / MALL); measured ~10% more read bandwidth on gfx950.
+typedef uint32_t hd_u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load16_nt(const void *p)
+{
+    const hd_u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const hd_u32x4 *>(p));
+    return make_uint4(t.x, t.y, t.z, t.w);
+}
+
+template <typename T>
+__device__ __forceinline__ void load8_nt(const T *p, float *v);
+
+template <>
+__device__ __forceinline__ void load8_nt<bf16_t>(const bf16_t *p, float *v)
+{
+    const uint4 q = load16_nt(p);
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(w[i] << 16);
+        v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+}
+
+template <>
+__device__ __forceinline__ void load8_nt<float>(const float *p, float *v)
+{
+    const uint4 a = load16_nt(p), b = load16_nt(p + 4);
+    v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y); v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
+    v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y); v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
+}
+
 // Sum over the `width` consecutive lanes of an aligned lane group (butterfly:
 // every lane of the group ends with the same value, added in the same order).
 template <int WIDTH>

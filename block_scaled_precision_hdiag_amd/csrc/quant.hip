@@ -5,6 +5,7 @@
 
 namespace hd {
 
+
 // ---------------------------------------------------------------- encode ---
 // Naive ("Is Finer Better?" §2.1: s = Q_scale(amax / C); qwantize "Results",
 // INT8: the amax itself stored as E4M3 and divided by 127) when GIVEN is false;
@@ -107,16 +108,17 @@ __global__ __launch_bounds__(256) void encode_kernel(const T *__restrict__ W, in
 #pragma unroll
             for (int j = 0; j < 8; ++j) v[i] |= (c[8 * i + j] & 15u) << (4 * j);
         }
-        *reinterpret_cast<uint4 *>(codes + e0 / 2) = make_uint4(v[0], v[1], v[2], v[3]);
+        // non-temporal stores: the codes are not read again by this kernel
+        __builtin_nontemporal_store(hd_u32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<hd_u32x4 *>(codes + e0 / 2));
     } else {
         uint32_t v[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i)
             v[i] = (c[4 * i] & 255u) | ((c[4 * i + 1] & 255u) << 8) | ((c[4 * i + 2] & 255u) << 16) |
                    ((c[4 * i + 3] & 255u) << 24);
-        uint4 *p = reinterpret_cast<uint4 *>(codes + e0);
-        p[0] = make_uint4(v[0], v[1], v[2], v[3]);
-        p[1] = make_uint4(v[4], v[5], v[6], v[7]);
+        hd_u32x4 *p = reinterpret_cast<hd_u32x4 *>(codes + e0);
+        __builtin_nontemporal_store(hd_u32x4{v[0], v[1], v[2], v[3]}, p);
+        __builtin_nontemporal_store(hd_u32x4{v[4], v[5], v[6], v[7]}, p + 1);
     }
     if ((threadIdx.x % TPB) == 0) {
         const int64_t blk0 = e0 / B;
@@ -288,22 +290,38 @@ hipError_t launch_dequant(int fmt, int B, const uint8_t *codes, const uint8_t *s
 // in a fixed order by one workgroup.
 static constexpr int WE_GRID = 2048;
 
+
 template <typename TW, typename TQ>
 __global__ __launch_bounds__(256) void werr_partial(const TW *__restrict__ W, const TQ *__restrict__ Wq,
                                                     int64_t total, double *__restrict__ part)
 {
     __shared__ double sh[4];
     double num = 0.0, den = 0.0;
-    for (int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8; e0 < total;
-         e0 += (int64_t)gridDim.x * 256 * 8) {
-        float w[8], q[8];
-        load8<TW>(W + e0, w);
-        load8<TQ>(Wq + e0, q);
+    // two 8-weight chunks per lane and iteration: four loads in flight
+    const int64_t stride = (int64_t)gridDim.x * 256 * 8;
+    for (int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8; e0 < total; e0 += 2 * stride) {
+        const int64_t e1 = e0 + stride;
+        const bool two = e1 < total;
+        float w[16], q[16];
+        load8_nt<TW>(W + e0, w);  // non-temporal: each weight is read once here
+        load8_nt<TQ>(Wq + e0, q);
+        if (two) {
+            load8_nt<TW>(W + e1, w + 8);
+            load8_nt<TQ>(Wq + e1, q + 8);
+        }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const double d = (double)q[j] - (double)w[j];
             num += d * d;
             den += (double)w[j] * (double)w[j];
+        }
+        if (two) {
+#pragma unroll
+            for (int j = 8; j < 16; ++j) {
+                const double d = (double)q[j] - (double)w[j];
+                num += d * d;
+                den += (double)w[j] * (double)w[j];
+            }
         }
     }
     num = block_sum_256(num, sh);
