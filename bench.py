@@ -37,6 +37,7 @@ SEARCH_OPS = {"sse": 6, "h": 7}
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "int8_down_proj_2560x9728_hbm_traffic.md")
+COUNTERS_PROFILE = os.path.join(ROOT, "profiles", "int8_down_proj_2560x9728_counters.md")
 
 
 def source_hash():
@@ -52,18 +53,28 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """Per-stage HBM bytes from the committed rocprofv3 --pmc record, or {} if
-    the kernels changed since it was taken."""
+def _profile_record(path, tag):
+    """Per-stage figures from a committed rocprofv3 --pmc record, or {} if the
+    kernels changed since it was taken."""
     try:
-        with open(TRAFFIC_PROFILE) as f:
+        with open(path) as f:
             for line in f:
-                if line.startswith("traffic-json:"):
+                if line.startswith(tag + ":"):
                     rec = json.loads(line.split(":", 1)[1])
                     return rec["stages"] if rec.get("source_hash") == source_hash() else {}
     except OSError:
         pass
     return {}
+
+
+def measured_traffic():
+    """Per-stage HBM bytes (FETCH_SIZE / WRITE_SIZE, calibrated)."""
+    return _profile_record(TRAFFIC_PROFILE, "traffic-json")
+
+
+def measured_counters():
+    """Per-stage executed VALU instructions and MFMA-busy cycles."""
+    return _profile_record(COUNTERS_PROFILE, "counters-json")
 
 
 def parse():
@@ -189,6 +200,8 @@ def main():
         "search_h": ("alu", N * K * n_cand * SEARCH_OPS["h"]),
     }
 
+    counters = measured_counters()
+
     def roof(stage):
         bound, units = work[stage]
         t = avg[stage] * 1e-3
@@ -198,8 +211,20 @@ def main():
             ach, peak, unit = units / t / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
         else:
             ach, peak, unit = units / t / 1e12, VALU_PEAK_TOPS, "Tops/s"
-        return {"bound": bound, "achieved": round(ach, 3), "peak": round(peak, 3), "unit": unit,
-                "frac": round(ach / peak, 4), "avg_ms": round(avg[stage], 4)}
+        r = {"bound": bound, "achieved": round(ach, 3), "peak": round(peak, 3), "unit": unit,
+             "frac": round(ach / peak, 4), "avg_ms": round(avg[stage], 4)}
+        c = counters.get(stage)
+        if bound == "alu":
+            # the full-grid count above is a convention (the search evaluates a
+            # fraction of the grid); the executed VALU rate comes from counters
+            r["basis"] = "full-grid equivalent (%d lane-ops per weight and candidate)" % SEARCH_OPS[stage[7:]]
+            if c:
+                ex = c["SQ_INSTS_VALU"] * 64 / t / 1e12
+                r["executed_valu_tops"] = round(ex, 3)
+                r["executed_valu_frac"] = round(ex / VALU_PEAK_TOPS, 4)
+        elif bound == "mfma" and c:
+            r["mfma_busy_frac"] = round(c["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * t * 2.4e9), 4)
+        return r
 
     stages = {s: roof(s) for s in avg}
     dominant = max(per_step, key=per_step.get)
