@@ -16,12 +16,15 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(HERE, "liboracle.so")
 
-NAIVE, SSE_OPT, H_OPT = 0, 1, 2
+NAIVE, SSE_OPT, H_OPT, NAIVE_OCP = 0, 1, 2, 3
 INT8_E4M3, NVFP4, MXFP4, MXFP8, FP8_E4M3S = 0, 1, 2, 3, 4
+NVFP4_UE4M4, NVFP4_UE5M3, NVINT4 = 5, 6, 7
+FOUR_BIT = (NVFP4, MXFP4, NVFP4_UE4M4, NVFP4_UE5M3, NVINT4)
 F32, BF16 = 0, 1
 
 FORMAT_NAMES = {INT8_E4M3: "INT8_E4M3", NVFP4: "NVFP4", MXFP4: "MXFP4",
-                MXFP8: "MXFP8", FP8_E4M3S: "FP8_E4M3S"}
+                MXFP8: "MXFP8", FP8_E4M3S: "FP8_E4M3S", NVFP4_UE4M4: "NVFP4_UE4M4",
+                NVFP4_UE5M3: "NVFP4_UE5M3", NVINT4: "NVINT4"}
 
 _lib = None
 
@@ -44,6 +47,7 @@ def lib():
         L.orc_scale_value.argtypes = [i32, i32]
         L.orc_scale_value.restype = ctypes.c_float
         L.orc_naive_scale_code.argtypes = [i32, ctypes.c_float]
+        L.orc_naive_ocp_code.argtypes = [i32, ctypes.c_float]
         L.orc_block_all_objectives.argtypes = [i32, i32, P, P, P, P]
         L.orc_quantize.argtypes = [i32, i32, i32, P, i32, i64, i64, P, P, P, P, P, i32]
         L.orc_dequantize.argtypes = [i32, i32, P, P, i64, i64, P, i32]
@@ -118,6 +122,11 @@ def naive_scale_code(fmt, amax):
     return int(lib().orc_naive_scale_code(fmt, float(np.float32(amax))))
 
 
+def naive_ocp_code(fmt, amax):
+    """OCP MX rule 2^(floor(log2 amax) - emax) as an E8M0 code (-1: not an E8M0 format)."""
+    return int(lib().orc_naive_ocp_code(fmt, float(np.float32(amax))))
+
+
 def block_all_objectives(fmt, w, h=None):
     """(codes, objectives) of one block over every candidate scale."""
     w = np.ascontiguousarray(w, np.float32)
@@ -131,7 +140,7 @@ def block_all_objectives(fmt, w, h=None):
 
 
 def codes_shape(fmt, N, K):
-    return (N, K // 2) if fmt in (NVFP4, MXFP4) else (N, K)
+    return (N, K // 2) if fmt in FOUR_BIT else (N, K)
 
 
 def quantize(method, fmt, B, W, h=None, scales_in=None, nthreads=0):

@@ -28,11 +28,22 @@
  *   - metrics: qwantize "Results", the weight-error and output-error
  *     definitions at the top of the page.
  *
+ *   - more grids (qwantize "Results", "Exotic Scales"; "Is Finer Better?"
+ *     §5.2): the unsigned UE4M4 (bias 7) and UE5M3 (bias 15) scale grids,
+ *     every code finite, 255 positive values, with E2M1 elements; NVINT4
+ *     (the "GPTQ Quantization" tables) read as symmetric INT4 elements
+ *     [-7, 7] with an E4M3 block scale s = Q_E4M3(amax / 7), the generic
+ *     rule of "Is Finer Better?" §2.1 with C = 7; the OCP MX rule for
+ *     power-of-two scales, 2^(floor(log2 amax) - emax_elem) (the OCP
+ *     microscaling specification the same section cites), as an alternative
+ *     Naive for MXFP4 / MXFP8.
+ *
  * Readings where the pages are silent (also listed in the design notes):
  *   E8M0 Naive snap = nearest power of two in the linear domain, ties upward
  *   (parity unpinned beyond self-consistency); negative inputs that round to
  *   zero keep their sign bit in E2M1/E4M3 codes (a convention, parity
- *   unpinned); E2M1 codes pack element 2i in the low nibble (a convention).
+ *   unpinned); E2M1 codes pack element 2i in the low nibble (a convention);
+ *   INT4 codes are two's complement nibbles, packed the same way.
  *
  * Build: -O2 -ffp-contract=off, no fast-math, so every float expression below
  * is one IEEE binary32 operation rounded to nearest-even (fl32).
@@ -50,14 +61,15 @@
 #define ORC_ENOMEM (-2)
 
 /* format ids (same numbering as the public library, kept independently) */
-enum { F_INT8_E4M3 = 0, F_NVFP4 = 1, F_MXFP4 = 2, F_MXFP8 = 3, F_FP8_E4M3S = 4, F_COUNT = 5 };
-enum { M_NAIVE = 0, M_SSE = 1, M_H = 2 };
+enum { F_INT8_E4M3 = 0, F_NVFP4 = 1, F_MXFP4 = 2, F_MXFP8 = 3, F_FP8_E4M3S = 4,
+       F_NVFP4_UE4M4 = 5, F_NVFP4_UE5M3 = 6, F_NVINT4 = 7, F_COUNT = 8 };
+enum { M_NAIVE = 0, M_SSE = 1, M_H = 2, M_NAIVE_OCP = 3 };
 enum { DT_F32 = 0, DT_BF16 = 1 };
 
 /* element kinds */
-enum { E_INT8 = 0, E_E2M1 = 1, E_E4M3 = 2 };
+enum { E_INT8 = 0, E_E2M1 = 1, E_E4M3 = 2, E_INT4 = 3 };
 /* scale kinds */
-enum { S_E4M3_OF_AMAX_DIV127 = 0, S_E4M3 = 1, S_E8M0 = 2 };
+enum { S_E4M3_OF_AMAX_DIV127 = 0, S_E4M3 = 1, S_E8M0 = 2, S_UE4M4 = 3, S_UE5M3 = 4 };
 
 /* ------------------------------------------------------------------------ */
 /* Number formats                                                            */
@@ -101,16 +113,23 @@ int orc_e8m0_table(double *out, int cap)
 static double T_E2M1[8];
 static double T_E4M3[127];
 static double T_INT8[128];
+static double T_INT4[8];
+static double T_UE4M4[256];
+static double T_UE5M3[256];
 static int tables_ready = 0;
 
 static void init_tables(void)
 {
     if (tables_ready)
         return;
-    orc_fp_table(2, 1, 1, 0, T_E2M1, 8);    /* {0,.5,1,1.5,2,3,4,6} */
-    orc_fp_table(4, 3, 7, 1, T_E4M3, 127);  /* 0 .. 448, 0x7F is NaN */
+    orc_fp_table(2, 1, 1, 0, T_E2M1, 8);      /* {0,.5,1,1.5,2,3,4,6} */
+    orc_fp_table(4, 3, 7, 1, T_E4M3, 127);    /* 0 .. 448, 0x7F is NaN */
+    orc_fp_table(4, 4, 7, 0, T_UE4M4, 256);   /* unsigned, every code finite: 0 .. 496 */
+    orc_fp_table(5, 3, 15, 0, T_UE5M3, 256);  /* unsigned, every code finite: 0 .. 122880 */
     for (int i = 0; i < 128; i++)
-        T_INT8[i] = (double)i;              /* symmetric INT8 magnitudes */
+        T_INT8[i] = (double)i;                /* symmetric INT8 magnitudes */
+    for (int i = 0; i < 8; i++)
+        T_INT4[i] = (double)i;                /* symmetric INT4 magnitudes 0..7 */
     tables_ready = 1;
 }
 
@@ -147,7 +166,8 @@ static int elem_kind(int fmt)
 {
     switch (fmt) {
     case F_INT8_E4M3: return E_INT8;
-    case F_NVFP4: case F_MXFP4: return E_E2M1;
+    case F_NVFP4: case F_MXFP4: case F_NVFP4_UE4M4: case F_NVFP4_UE5M3: return E_E2M1;
+    case F_NVINT4: return E_INT4;
     default: return E_E4M3;
     }
 }
@@ -156,22 +176,39 @@ static int scale_kind(int fmt)
 {
     switch (fmt) {
     case F_INT8_E4M3: return S_E4M3_OF_AMAX_DIV127;
-    case F_NVFP4: case F_FP8_E4M3S: return S_E4M3;
+    case F_NVFP4: case F_FP8_E4M3S: case F_NVINT4: return S_E4M3;
+    case F_NVFP4_UE4M4: return S_UE4M4;
+    case F_NVFP4_UE5M3: return S_UE5M3;
     default: return S_E8M0;
     }
 }
+
+/* elements stored as 4-bit codes, two per byte */
+static int four_bit(int fmt) { return elem_kind(fmt) == E_E2M1 || elem_kind(fmt) == E_INT4; }
 
 static const double *elem_table(int fmt, int *n)
 {
     switch (elem_kind(fmt)) {
     case E_INT8: *n = 128; return T_INT8;
+    case E_INT4: *n = 8; return T_INT4;
     case E_E2M1: *n = 8; return T_E2M1;
     default: *n = 127; return T_E4M3;
     }
 }
 
+/* largest element magnitude C of the Naive rule s = Q_scale(amax / C) */
+static float elem_cmax(int fmt)
+{
+    switch (elem_kind(fmt)) {
+    case E_E2M1: return 6.0f;
+    case E_INT4: return 7.0f;
+    default: return 448.0f;
+    }
+}
+
 /* Candidate scale codes of the search, ascending: the 126 positive E4M3 codes
- * 0x01..0x7E, or all 255 finite E8M0 codes. */
+ * 0x01..0x7E, all 255 finite E8M0 codes, or the 255 positive UE4M4 / UE5M3
+ * codes 0x01..0xFF. */
 int orc_candidates(int fmt, int *first, int *last)
 {
     init_tables();
@@ -180,6 +217,9 @@ int orc_candidates(int fmt, int *first, int *last)
     if (scale_kind(fmt) == S_E8M0) {
         *first = 0;
         *last = 254;
+    } else if (scale_kind(fmt) == S_UE4M4 || scale_kind(fmt) == S_UE5M3) {
+        *first = 1;
+        *last = 255;
     } else {
         *first = 1;
         *last = 126;
@@ -200,6 +240,12 @@ float orc_scale_value(int fmt, int code)
     case S_E4M3:
         if (code < 0 || code > 126) return NAN;
         return (float)T_E4M3[code];
+    case S_UE4M4:
+        if (code < 0 || code > 255) return NAN;
+        return (float)T_UE4M4[code];
+    case S_UE5M3:
+        if (code < 0 || code > 255) return NAN;
+        return (float)T_UE5M3[code];
     default:
         if (code < 0 || code > 254) return NAN;
         return (float)ldexp(1.0, code - 127);
@@ -213,10 +259,14 @@ int orc_naive_scale_code(int fmt, float amax)
     int sk = scale_kind(fmt);
     if (sk == S_E4M3_OF_AMAX_DIV127)
         return orc_rne_index(T_E4M3, 127, (double)amax); /* amax itself, saturating at 448 */
-    float C = (elem_kind(fmt) == E_E2M1) ? 6.0f : 448.0f; /* largest element magnitude */
-    float v = amax / C;                                   /* fl32 */
+    float C = elem_cmax(fmt); /* largest element magnitude */
+    float v = amax / C;       /* fl32 */
     if (sk == S_E4M3)
         return orc_rne_index(T_E4M3, 127, (double)v);
+    if (sk == S_UE4M4)
+        return orc_rne_index(T_UE4M4, 256, (double)v);
+    if (sk == S_UE5M3)
+        return orc_rne_index(T_UE5M3, 256, (double)v);
     /* E8M0: nearest power of two in the linear domain, ties upward */
     if (v == 0.0f)
         return 0;
@@ -229,6 +279,26 @@ int orc_naive_scale_code(int fmt, float amax)
         E = -127;
     if (E > 127)
         E = 127;
+    return E + 127;
+}
+
+/* OCP MX rule for power-of-two scales: 2^(floor(log2 amax) - emax), emax the
+ * exponent of the largest element (E2M1: 6 = 1.5 * 2^2; E4M3: 448 = 1.75 * 2^8),
+ * clamped to the E8M0 range; an all-zero block gets code 0.  -1 for a format
+ * without E8M0 scales. */
+int orc_naive_ocp_code(int fmt, float amax)
+{
+    init_tables();
+    if (fmt < 0 || fmt >= F_COUNT || scale_kind(fmt) != S_E8M0)
+        return -1;
+    if (amax == 0.0f)
+        return 0;
+    int e;
+    frexp((double)amax, &e); /* amax = f * 2^e, f in [0.5, 1): floor(log2 amax) = e - 1 */
+    int emax = (elem_kind(fmt) == E_E2M1) ? 2 : 8;
+    int E = e - 1 - emax;
+    if (E < -127) E = -127;
+    if (E > 127) E = 127;
     return E + 127;
 }
 
@@ -250,6 +320,7 @@ static int enc_elem(int fmt, float s, float w, float *wq)
     *wq = neg ? -mag : mag;
     switch (elem_kind(fmt)) {
     case E_INT8: return (uint8_t)(int8_t)(neg ? -idx : idx);
+    case E_INT4: return (neg ? -idx : idx) & 0xF; /* two's complement nibble */
     case E_E2M1: return (neg << 3) | idx;
     default: return (neg << 7) | idx;
     }
@@ -262,6 +333,13 @@ static int dec_elem(int fmt, int code, int *neg)
     case E_INT8: {
         int v = (int8_t)(uint8_t)code;
         if (v == -128) return -1;
+        *neg = v < 0;
+        return v < 0 ? -v : v;
+    }
+    case E_INT4: {
+        int v = code & 0xF;
+        if (v >= 8) v -= 16;
+        if (v == -8) return -1;
         *neg = v < 0;
         return v < 0 ? -v : v;
     }
@@ -338,7 +416,7 @@ static int check_common(int fmt, int B, int64_t N, int64_t K)
 {
     if (fmt < 0 || fmt >= F_COUNT || B <= 0 || N < 0 || K < 0 || (K > 0 && K % B != 0))
         return ORC_EINVAL;
-    if (elem_kind(fmt) == E_E2M1 && (K % 2) != 0)
+    if (four_bit(fmt) && (K % 2) != 0)
         return ORC_EINVAL;
     return ORC_OK;
 }
@@ -346,7 +424,7 @@ static int check_common(int fmt, int B, int64_t N, int64_t K)
 static void put_code(int fmt, uint8_t *codes, int64_t N, int64_t K, int64_t n, int64_t k, int code)
 {
     (void)N;
-    if (elem_kind(fmt) == E_E2M1) {
+    if (four_bit(fmt)) {
         uint8_t *p = codes + n * (K / 2) + k / 2;
         if (k % 2 == 0)
             *p = (uint8_t)((*p & 0xF0) | (code & 0xF));
@@ -359,7 +437,7 @@ static void put_code(int fmt, uint8_t *codes, int64_t N, int64_t K, int64_t n, i
 
 static int get_code(int fmt, const uint8_t *codes, int64_t K, int64_t n, int64_t k)
 {
-    if (elem_kind(fmt) == E_E2M1) {
+    if (four_bit(fmt)) {
         uint8_t b = codes[n * (K / 2) + k / 2];
         return (k % 2 == 0) ? (b & 0xF) : (b >> 4);
     }
@@ -370,7 +448,7 @@ static int get_code(int fmt, const uint8_t *codes, int64_t K, int64_t n, int64_t
  * not NULL, fixes every block's scale code (encode only: method is ignored).
  * h is required for H-Optimal; for Naive and for a fixed scale it only weights
  * the reported objective.  codes: [N][K] bytes (INT8, E4M3) or [N][K/2]
- * (E2M1); scales: [N][K/B]; block_obj: [N][K/B] float64 or NULL. */
+ * (E2M1, INT4: element 2k in the low nibble); scales: [N][K/B]; block_obj: [N][K/B] float64 or NULL. */
 int orc_quantize(int method, int fmt, int B, const void *W, int wdt, int64_t N, int64_t K,
                  const float *h, const uint8_t *scales_in, uint8_t *codes, uint8_t *scales,
                  double *block_obj, int nthreads)
@@ -380,7 +458,9 @@ int orc_quantize(int method, int fmt, int B, const void *W, int wdt, int64_t N, 
         return ORC_EINVAL;
     if (!scales_in && method == M_H && !h)
         return ORC_EINVAL;
-    if (!scales_in && (method < M_NAIVE || method > M_H))
+    if (!scales_in && (method < M_NAIVE || method > M_NAIVE_OCP))
+        return ORC_EINVAL;
+    if (!scales_in && method == M_NAIVE_OCP && scale_kind(fmt) != S_E8M0)
         return ORC_EINVAL;
     if (N == 0 || K == 0)
         return ORC_OK;
@@ -425,8 +505,8 @@ int orc_quantize(int method, int fmt, int B, const void *W, int wdt, int64_t N, 
                         continue;
                     }
                     best = block_objective(fmt, s, w, om, B);
-                } else if (method == M_NAIVE) {
-                    code = orc_naive_scale_code(fmt, amax);
+                } else if (method == M_NAIVE || method == M_NAIVE_OCP) {
+                    code = method == M_NAIVE ? orc_naive_scale_code(fmt, amax) : orc_naive_ocp_code(fmt, amax);
                     best = block_objective(fmt, orc_scale_value(fmt, code), w, om, B);
                 } else {
                     code = c0;

@@ -14,6 +14,10 @@ import numpy as np
 # all-ones code is NaN, so the P4 formula's 480 is one step beyond the range.
 E2M1 = (2, 1, 1, 6.0)
 E4M3 = (4, 3, 7, 448.0)
+# the unsigned scale grids of the qwantize "Exotic Scales" section: every code
+# finite, so Q_max is the P4 formula's value
+UE4M4 = (4, 4, 7, 496.0)
+UE5M3 = (5, 3, 15, 122880.0)
 
 
 def p4_value(ebits, mbits, bias, p, d):

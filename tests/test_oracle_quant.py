@@ -15,25 +15,35 @@ import pytest
 
 import oracle
 import fpref
-from oracle import NAIVE, SSE_OPT, H_OPT, INT8_E4M3, NVFP4, MXFP4, MXFP8, FP8_E4M3S
+from oracle import (NAIVE, SSE_OPT, H_OPT, NAIVE_OCP, INT8_E4M3, NVFP4, MXFP4, MXFP8, FP8_E4M3S,
+                    NVFP4_UE4M4, NVFP4_UE5M3, NVINT4)
 
-ALL_FMTS = [INT8_E4M3, NVFP4, MXFP4, MXFP8, FP8_E4M3S]
+ALL_FMTS = [INT8_E4M3, NVFP4, MXFP4, MXFP8, FP8_E4M3S, NVFP4_UE4M4, NVFP4_UE5M3, NVINT4]
+E2M1_FMTS = (NVFP4, MXFP4, NVFP4_UE4M4, NVFP4_UE5M3)
 E4M3_GRID = fpref.grid(4, 3, 7, True)
+UE4M4_GRID = fpref.grid(4, 4, 7, False)
+UE5M3_GRID = fpref.grid(5, 3, 15, False)
 
 
 def ref_scales(fmt):
     """(code, fp32 scale) of every candidate, derived here independently."""
     if fmt == INT8_E4M3:
         return [(c, np.float32(E4M3_GRID[c]) / np.float32(127)) for c in range(1, 127)]
-    if fmt in (NVFP4, FP8_E4M3S):
+    if fmt in (NVFP4, FP8_E4M3S, NVINT4):
         return [(c, np.float32(E4M3_GRID[c])) for c in range(1, 127)]
+    if fmt == NVFP4_UE4M4:
+        return [(c, np.float32(UE4M4_GRID[c])) for c in range(1, 256)]
+    if fmt == NVFP4_UE5M3:
+        return [(c, np.float32(UE5M3_GRID[c])) for c in range(1, 256)]
     return [(c, np.float32(np.ldexp(1.0, c - 127))) for c in range(255)]
 
 
 def ref_elem_round(fmt, x):
     if fmt == INT8_E4M3:
         return fpref.int_round(x, 127)
-    if fmt in (NVFP4, MXFP4):
+    if fmt == NVINT4:
+        return fpref.int_round(x, 7)
+    if fmt in E2M1_FMTS:
         return fpref.p4_round(x, fpref.E2M1)
     return fpref.p4_round(x, fpref.E4M3)
 
@@ -117,7 +127,7 @@ def test_encode_every_bf16_at_every_scale(fmt):
     K = (x.size // B) * B
     x = x[:K]
     cands = ref_scales(fmt)
-    step = 1 if fmt in (INT8_E4M3, NVFP4, FP8_E4M3S) else 3
+    step = 1 if fmt in (INT8_E4M3, NVFP4, FP8_E4M3S, NVINT4) else 3
     cands = cands[::step]
     W = np.tile(x, (len(cands), 1))
     scales_in = np.array([[c] * (K // B) for c, _ in cands], np.uint8)
@@ -126,7 +136,7 @@ def test_encode_every_bf16_at_every_scale(fmt):
     for r, (c, s) in enumerate(cands):
         ref = ref_dequant_block(fmt, s, x)
         np.testing.assert_array_equal(deq[r], ref)
-        assert np.array_equal(np.signbit(deq[r]), np.signbit(x)) or fmt == INT8_E4M3
+        assert np.array_equal(np.signbit(deq[r]), np.signbit(x)) or fmt in (INT8_E4M3, NVINT4)
 
 
 def _naive_code_ref(fmt, amax):
@@ -134,11 +144,15 @@ def _naive_code_ref(fmt, amax):
     if fmt == INT8_E4M3:
         v = fpref.p4_round(np.array([amax]), fpref.E4M3)[0]
         return int(np.nonzero(E4M3_GRID == v)[0][0])
-    C = np.float32(6) if fmt in (NVFP4, MXFP4) else np.float32(448)
+    C = np.float32(6) if fmt in E2M1_FMTS else (np.float32(7) if fmt == NVINT4 else np.float32(448))
     v = amax / C
-    if fmt in (NVFP4, FP8_E4M3S):
+    if fmt in (NVFP4, FP8_E4M3S, NVINT4):
         r = fpref.p4_round(np.array([v]), fpref.E4M3)[0]
         return int(np.nonzero(E4M3_GRID == r)[0][0])
+    if fmt in (NVFP4_UE4M4, NVFP4_UE5M3):
+        spec, grid = (fpref.UE4M4, UE4M4_GRID) if fmt == NVFP4_UE4M4 else (fpref.UE5M3, UE5M3_GRID)
+        r = fpref.p4_round(np.array([v]), spec)[0]
+        return int(np.nonzero(grid == r)[0][0])
     if v == 0:
         return 0
     fv = Fraction(float(v))
@@ -215,7 +229,8 @@ def mid_h(seed, K=512):
 
 
 @pytest.mark.parametrize("fmt,B", [(INT8_E4M3, 32), (INT8_E4M3, 128), (NVFP4, 16), (MXFP4, 32),
-                                   (MXFP8, 32), (FP8_E4M3S, 16)])
+                                   (MXFP8, 32), (FP8_E4M3S, 16), (NVFP4_UE4M4, 16), (NVFP4_UE5M3, 16),
+                                   (NVINT4, 16)])
 def test_per_block_invariants(fmt, B):
     W = mid_weights(21)
     h = mid_h(22)
@@ -251,7 +266,10 @@ def test_sign_flip(fmt):
         assert np.array_equal(s1, s2) and np.array_equal(o1, o2)
         if fmt == INT8_E4M3:
             assert np.array_equal(c1.view(np.int8), -c2.view(np.int8))
-        elif fmt in (NVFP4, MXFP4):
+        elif fmt == NVINT4:  # two's complement nibbles: negate each
+            neg = lambda c: ((-(c & 15)) & 15) | (((-(c >> 4)) & 15) << 4)
+            assert np.array_equal(neg(c1.astype(int)), c2.astype(int))
+        elif fmt in E2M1_FMTS:
             assert np.array_equal(c1 ^ 0x88, c2)
         else:
             assert np.array_equal(c1 ^ 0x80, c2)
@@ -269,17 +287,19 @@ def test_e8m0_power_of_two_shift(fmt):
             assert np.array_equal(c1, c2)
 
 
-@pytest.mark.parametrize("fmt", [INT8_E4M3, NVFP4, FP8_E4M3S])
-def test_e4m3_scale_binade_shift(fmt):
-    # magnitudes ~1 keep every competitive candidate in the normal E4M3 range,
-    # so doubling W moves the chosen scale up by one binade (8 codes)
+@pytest.mark.parametrize("fmt,step", [(INT8_E4M3, 8), (NVFP4, 8), (FP8_E4M3S, 8), (NVINT4, 8),
+                                      (NVFP4_UE4M4, 16), (NVFP4_UE5M3, 8)])
+def test_e4m3_scale_binade_shift(fmt, step):
+    # magnitudes ~1 keep every competitive candidate in the normal range of
+    # the scale grid, so doubling W moves the chosen scale up by one binade
+    # (8 codes; 16 on the UE4M4 grid)
     rng = np.random.default_rng(61)
     W = (rng.standard_t(4, (16, 256)) * (0.3 if fmt != FP8_E4M3S else 40.0)).astype(np.float32)
     h = mid_h(62, 256)
     for m in (NAIVE, SSE_OPT, H_OPT):
         c1, s1, o1 = oracle.quantize(m, fmt, 32, W, h=h)
         c2, s2, o2 = oracle.quantize(m, fmt, 32, (2 * W).astype(np.float32), h=h)
-        assert np.array_equal(s2.astype(int), s1.astype(int) + 8)
+        assert np.array_equal(s2.astype(int), s1.astype(int) + step)
         assert np.array_equal(c1, c2)
         np.testing.assert_allclose(o2, 4 * o1, rtol=1e-15)
 
@@ -294,7 +314,9 @@ def test_weights_on_a_grid_point(fmt):
         c, s = cands[rng.integers(len(cands) // 4, 3 * len(cands) // 4)]
         if fmt == INT8_E4M3:
             q = rng.integers(-127, 128, B).astype(np.float32)
-        elif fmt in (NVFP4, MXFP4):
+        elif fmt == NVINT4:
+            q = rng.integers(-7, 8, B).astype(np.float32)
+        elif fmt in E2M1_FMTS:
             q = rng.choice([0, .5, 1, 1.5, 2, 3, 4, 6], B) * rng.choice([-1, 1], B)
         else:
             q = rng.choice(E4M3_GRID[1:], B) * rng.choice([-1, 1], B)
@@ -336,3 +358,62 @@ def test_invalid_arguments():
         oracle.quantize(SSE_OPT, NVFP4, 16, W)  # K % B != 0
     with pytest.raises(ValueError):
         oracle.quantize(H_OPT, NVFP4, 2, np.zeros((2, 32), np.float32))  # H-Optimal needs h
+
+
+def test_nvint4_codes_and_packing():
+    # scale 1.0 (E4M3 code 0x38): integers encode as themselves, halves tie to
+    # even, |x| > 7 saturates; two's complement nibbles, element 2i low
+    w = np.array([[7.0, -7.0, 1.0, -1.0, 0.0, 3.4, -3.5, 2.5, 9.0, -0.4, 4.5, -6.5, 0, 0, 0, 0]], np.float32)
+    codes, _, obj = oracle.quantize(NAIVE, NVINT4, 16, w, scales_in=np.array([[0x38]], np.uint8))
+    assert list(codes[0]) == [0x97, 0xF1, 0x30, 0x2C, 0x07, 0xA4, 0x00, 0x00]
+    deq = oracle.dequantize(NVINT4, 16, codes, np.array([[0x38]], np.uint8), 1, 16)
+    np.testing.assert_array_equal(deq[0], [7, -7, 1, -1, 0, 3, -4, 2, 7, -0.0, 4, -6, 0, 0, 0, 0])
+    # Naive: E4M3(amax / 7); amax = 7 -> scale 1.0
+    assert oracle.naive_scale_code(NVINT4, 7.0) == 0x38
+    # the INT4 code -8 (0x8 nibble) is not a symmetric INT4 value
+    with pytest.raises(ValueError):
+        oracle.dequantize(NVINT4, 8, np.array([[0x08, 0, 0, 0]], np.uint8), np.array([[0x38]], np.uint8), 1, 8)
+
+
+def test_unsigned_scale_grids():
+    # 255 positive candidates each; UE4M4 halves the E4M3 step (16 codes per
+    # binade), UE5M3 keeps 8 per binade and reaches 2^-17 .. 122880
+    for fmt, grid in ((NVFP4_UE4M4, UE4M4_GRID), (NVFP4_UE5M3, UE5M3_GRID)):
+        assert oracle.candidates(fmt).tolist() == list(range(1, 256))
+        assert [oracle.scale_value(fmt, c) for c in range(256)] == [np.float32(v) for v in grid]
+    assert oracle.scale_value(NVFP4_UE4M4, 255) == 496.0
+    assert oracle.scale_value(NVFP4_UE5M3, 1) == np.float32(2.0 ** -17)
+    assert oracle.scale_value(NVFP4_UE5M3, 255) == 122880.0
+    # one E4M3 binade [1, 2) holds 8 codes, UE4M4's holds 16
+    assert sum(1 <= v < 2 for v in UE4M4_GRID) == 16 and sum(1 <= v < 2 for v in E4M3_GRID) == 8
+    # Naive zero bin: amax / 6 at or below half the smallest positive scale
+    assert oracle.naive_scale_code(NVFP4_UE5M3, np.float32(6 * 2.0 ** -18)) == 0
+    assert oracle.naive_scale_code(NVFP4_UE5M3, np.nextafter(np.float32(6 * 2.0 ** -18), np.float32(1))) == 1
+    assert oracle.naive_scale_code(NVFP4_UE4M4, np.float32(6 * 496.0 * 2)) == 255  # saturates
+
+
+def test_ocp_floor_naive():
+    # OCP MX: 2^(floor(log2 amax) - emax), emax = 2 (E2M1), 8 (E4M3)
+    assert oracle.naive_ocp_code(MXFP4, 6.0) == 127          # floor(log2 6) = 2
+    assert oracle.naive_ocp_code(MXFP4, np.float32(7.99)) == 127
+    assert oracle.naive_ocp_code(MXFP4, 8.0) == 128
+    assert oracle.naive_ocp_code(MXFP4, np.nextafter(np.float32(4.0), np.float32(0))) == 126
+    assert oracle.naive_ocp_code(MXFP8, 448.0) == 127        # floor(log2 448) = 8
+    assert oracle.naive_ocp_code(MXFP8, 1.0) == 119
+    assert oracle.naive_ocp_code(MXFP4, 0.0) == 0
+    assert oracle.naive_ocp_code(MXFP4, np.float32(2.0 ** -140)) == 0   # clamped at 2^-127
+    assert oracle.naive_ocp_code(NVFP4, 1.0) == -1                      # not an E8M0 format
+    # unlike the nearest-power-of-two snap, the floor rule never rounds up:
+    # amax = 9 (v = 1.5) snaps to 2^1 but floors to 2^1 as well; amax = 7 (v =
+    # 1.17) snaps to 2^0 and floors to 2^0; amax = 11.9 snaps to 2^1, floors to 2^1
+    W = mid_weights(101, N=8, K=256)
+    for fmt in (MXFP4, MXFP8):
+        c, s, o = oracle.quantize(NAIVE_OCP, fmt, 32, W)
+        amax = np.abs(W).reshape(8, 8, 32).max(-1)
+        assert np.array_equal(s, np.vectorize(lambda a: oracle.naive_ocp_code(fmt, a))(amax))
+        # no element of a floor-rule block saturates: amax / s < 2^(emax + 1)
+        emax = 2 if fmt == MXFP4 else 8
+        sv = np.vectorize(lambda cc: float(oracle.scale_value(fmt, cc)))(s)
+        assert np.all(amax / sv < 2.0 ** (emax + 1))
+    with pytest.raises(ValueError):
+        oracle.quantize(NAIVE_OCP, NVFP4, 16, W)
