@@ -22,10 +22,13 @@ LIB_PATH = os.path.join(_HERE, "libhdiag.so")
 # enums of include/hdiag.h
 HD_OK, HD_ERR_INVALID_ARG, HD_ERR_UNSUPPORTED, HD_ERR_HIP = 0, -1, -2, -3
 HD_F32, HD_BF16 = 0, 1
-NAIVE, SSE_OPT, H_OPT = 0, 1, 2
+NAIVE, SSE_OPT, H_OPT, NAIVE_OCP = 0, 1, 2, 3
 INT8_E4M3, NVFP4, MXFP4, MXFP8, FP8_E4M3S = 0, 1, 2, 3, 4
-FORMATS = {"INT8_E4M3": INT8_E4M3, "NVFP4": NVFP4, "MXFP4": MXFP4, "MXFP8": MXFP8, "FP8_E4M3S": FP8_E4M3S}
-METHODS = {"naive": NAIVE, "sse": SSE_OPT, "h": H_OPT}
+NVFP4_UE4M4, NVFP4_UE5M3, NVINT4 = 5, 6, 7
+FORMATS = {"INT8_E4M3": INT8_E4M3, "NVFP4": NVFP4, "MXFP4": MXFP4, "MXFP8": MXFP8, "FP8_E4M3S": FP8_E4M3S,
+           "NVFP4_UE4M4": NVFP4_UE4M4, "NVFP4_UE5M3": NVFP4_UE5M3, "NVINT4": NVINT4}
+METHODS = {"naive": NAIVE, "sse": SSE_OPT, "h": H_OPT, "naive_ocp": NAIVE_OCP}
+FOUR_BIT = (NVFP4, MXFP4, NVFP4_UE4M4, NVFP4_UE5M3, NVINT4)
 
 EXPORTS = ["hdiag", "hdiag_workspace_size", "quantize_blocks", "encode_blocks", "dequantize",
            "weight_error", "weight_error_workspace_size", "output_error", "output_error_workspace_size",
@@ -120,7 +123,7 @@ def _dev(t):
 
 
 def codes_shape(fmt, N, K):
-    return (N, K // 2) if fmt in (NVFP4, MXFP4) else (N, K)
+    return (N, K // 2) if fmt in FOUR_BIT else (N, K)
 
 
 def hdiag_workspace_size(M, K):

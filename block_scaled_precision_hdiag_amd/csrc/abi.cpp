@@ -36,9 +36,13 @@ hd_status hip_status(hipError_t e, const char *what)
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 bool valid_dtype(int d) { return d == HD_F32 || d == HD_BF16; }
-bool valid_fmt(int f) { return f >= HD_INT8_E4M3 && f <= HD_FP8_E4M3S; }
+bool valid_fmt(int f) { return f >= HD_INT8_E4M3 && f <= HD_NVINT4; }
 bool valid_block(int32_t B) { return B == 8 || B == 16 || B == 32 || B == 64 || B == 128 || B == 256; }
-bool is_fp4(int f) { return f == HD_NVFP4 || f == HD_MXFP4; }
+bool is_4bit(int f)
+{
+    return f == HD_NVFP4 || f == HD_MXFP4 || f == HD_NVFP4_UE4M4 || f == HD_NVFP4_UE5M3 || f == HD_NVINT4;
+}
+bool is_e8m0(int f) { return f == HD_MXFP4 || f == HD_MXFP8; }
 
 #define HD_REQUIRE(cond, ...) \
     do {                      \
@@ -94,9 +98,9 @@ hd_status hdiag_format_info(hd_format fmt, int32_t B, int *elem_bits, int *scale
 {
     HD_REQUIRE(valid_fmt(fmt), "unknown format %d", (int)fmt);
     HD_REQUIRE(B > 0, "block size must be positive");
-    const int eb = is_fp4(fmt) ? 4 : 8;
+    const int eb = is_4bit(fmt) ? 4 : 8;
     const int sb = 8;
-    const int nc = (fmt == HD_MXFP4 || fmt == HD_MXFP8) ? 255 : 126;
+    const int nc = (is_e8m0(fmt) || fmt == HD_NVFP4_UE4M4 || fmt == HD_NVFP4_UE5M3) ? 255 : 126;
     if (elem_bits) *elem_bits = eb;
     if (scale_bits) *scale_bits = sb;
     if (n_candidates) *n_candidates = nc;
@@ -128,7 +132,7 @@ hd_status quantize_blocks(hd_method method, hd_format fmt, int32_t B, const void
                           int64_t K, const float *h, uint8_t *codes, uint8_t *scales, float *block_obj,
                           void *stream)
 {
-    HD_REQUIRE(method >= HD_NAIVE && method <= HD_H_OPT, "unknown method %d", (int)method);
+    HD_REQUIRE(method >= HD_NAIVE && method <= HD_NAIVE_OCP, "unknown method %d", (int)method);
     HD_REQUIRE(valid_dtype(wt), "unknown dtype %d", (int)wt);
     hd_status s = check_quant_shape(fmt, B, N, K);
     if (s != HD_OK) return s;
@@ -141,8 +145,10 @@ hd_status quantize_blocks(hd_method method, hd_format fmt, int32_t B, const void
     if (h != nullptr && !aligned16(h)) return fail(HD_ERR_INVALID_ARG, "h is not 16-byte aligned");
     if (block_obj != nullptr && ((uintptr_t)block_obj & 3u)) return fail(HD_ERR_INVALID_ARG, "block_obj misaligned");
     hipStream_t st = (hipStream_t)stream;
-    if (method == HD_NAIVE)
-        return hip_status(hd::launch_encode(fmt, B, W, wt, N, K, h, nullptr, codes, scales, block_obj, st),
+    HD_REQUIRE(method != HD_NAIVE_OCP || is_e8m0(fmt), "the OCP rule needs a power-of-two (E8M0) scale grid");
+    if (method == HD_NAIVE || method == HD_NAIVE_OCP)
+        return hip_status(hd::launch_encode(fmt, B, W, wt, N, K, h, nullptr, codes, scales, block_obj,
+                                            method == HD_NAIVE_OCP, st),
                           "quantize_blocks(naive)");
     const float *hh = method == HD_H_OPT ? h : nullptr;
     return hip_status(hd::launch_search(fmt, B, W, wt, N, K, hh, codes, scales, block_obj, st),
@@ -161,7 +167,7 @@ hd_status encode_blocks(hd_format fmt, int32_t B, const void *W, hd_dtype wt, in
     if (scales_in == nullptr) return fail(HD_ERR_INVALID_ARG, "scales_in is NULL");
     if (h != nullptr && !aligned16(h)) return fail(HD_ERR_INVALID_ARG, "h is not 16-byte aligned");
     if (block_obj != nullptr && ((uintptr_t)block_obj & 3u)) return fail(HD_ERR_INVALID_ARG, "block_obj misaligned");
-    return hip_status(hd::launch_encode(fmt, B, W, wt, N, K, h, scales_in, codes, nullptr, block_obj,
+    return hip_status(hd::launch_encode(fmt, B, W, wt, N, K, h, scales_in, codes, nullptr, block_obj, 0,
                                         (hipStream_t)stream),
                       "encode_blocks");
 }
@@ -306,6 +312,9 @@ hipError_t launch_search(int fmt, int B, const void *W, int wdt, int64_t N, int6
     case HD_MXFP4: return launch_search_mxfp4(B, W, wdt, N, K, h, codes, scales, block_obj, st);
     case HD_MXFP8: return launch_search_mxfp8(B, W, wdt, N, K, h, codes, scales, block_obj, st);
     case HD_FP8_E4M3S: return launch_search_fp8s(B, W, wdt, N, K, h, codes, scales, block_obj, st);
+    case HD_NVFP4_UE4M4: return launch_search_nvfp4_ue4m4(B, W, wdt, N, K, h, codes, scales, block_obj, st);
+    case HD_NVFP4_UE5M3: return launch_search_nvfp4_ue5m3(B, W, wdt, N, K, h, codes, scales, block_obj, st);
+    case HD_NVINT4: return launch_search_nvint4(B, W, wdt, N, K, h, codes, scales, block_obj, st);
     }
     return hipErrorInvalidValue;
 }

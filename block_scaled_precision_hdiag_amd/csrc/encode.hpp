@@ -15,7 +15,7 @@ __device__ __forceinline__ double encode8(const float *w, float s, float r, cons
                                           uint32_t *code)
 {
     double obj = 0.0;
-    if (EK == ELEM_INT8) {
+    if (elem_int(EK)) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const float a = fabsf(w[j]);
@@ -63,7 +63,7 @@ __device__ __forceinline__ double encode8(const float *w, float s, float r, cons
 template <int EK>
 __device__ __forceinline__ void store_codes8(uint8_t *codes, int64_t e0, const uint32_t *c)
 {
-    if (EK == ELEM_E2M1) {
+    if (elem_4bit(EK)) {
         const uint32_t v = (c[0] & 15u) | ((c[1] & 15u) << 4) | ((c[2] & 15u) << 8) | ((c[3] & 15u) << 12) |
                            ((c[4] & 15u) << 16) | ((c[5] & 15u) << 20) | ((c[6] & 15u) << 24) |
                            ((c[7] & 15u) << 28);

@@ -1,11 +1,14 @@
 // formats.hpp - number formats, scale grids and exact rounding for the gfx950
 // kernels of libhdiag.so.
 //
-// Element formats: INT8 [-127, 127]; E2M1 {0,.5,1,1.5,2,3,4,6} (qwantize
-// "Results", Exotic Scales); OCP E4M3 (126 positive finite codes, max 448;
-// 0x7F/0xFF NaN).  Scale grids: E4M3 codes 0x01..0x7E; INT8's fl32(E4M3 / 127)
-// (qwantize "Results", INT8 section); E8M0 2^(c-127), c = 0..254 ("Is Finer
-// Better?" §2.1).  Values follow the EeMm formula of the LLM-FP4 summary page
+// Element formats: INT8 [-127, 127]; INT4 [-7, 7] (the NVINT4 rows of the
+// qwantize "Results" tables, read as symmetric INT4); E2M1
+// {0,.5,1,1.5,2,3,4,6} (qwantize "Results", Exotic Scales); OCP E4M3 (126
+// positive finite codes, max 448; 0x7F/0xFF NaN).  Scale grids: E4M3 codes
+// 0x01..0x7E; INT8's fl32(E4M3 / 127) (qwantize "Results", INT8 section); E8M0
+// 2^(c-127), c = 0..254 ("Is Finer Better?" §2.1); the unsigned UE4M4 (bias 7)
+// and UE5M3 (bias 15) grids of the "Exotic Scales" section, every code finite
+// (0x01..0xFF positive).  Values follow the EeMm formula of the LLM-FP4 summary page
 // ("Floating-Point Quantization Mechanics").
 //
 // Rounding: q = RNE(fl32(|w| / s)) onto the element grid, ties to the even
@@ -22,24 +25,55 @@
 
 namespace hd {
 
-enum ElemKind { ELEM_INT8 = 0, ELEM_E2M1 = 1, ELEM_E4M3 = 2 };
-enum ScaleKind { SCALE_INT8 = 0, SCALE_E4M3 = 1, SCALE_E8M0 = 2 };
+enum ElemKind { ELEM_INT8 = 0, ELEM_E2M1 = 1, ELEM_E4M3 = 2, ELEM_INT4 = 3 };
+enum ScaleKind { SCALE_INT8 = 0, SCALE_E4M3 = 1, SCALE_E8M0 = 2, SCALE_UE4M4 = 3, SCALE_UE5M3 = 4 };
 
 __host__ __device__ constexpr int elem_kind(int fmt)
 {
-    return fmt == HD_INT8_E4M3 ? ELEM_INT8 : (fmt == HD_NVFP4 || fmt == HD_MXFP4) ? ELEM_E2M1 : ELEM_E4M3;
+    return fmt == HD_INT8_E4M3 ? ELEM_INT8
+         : fmt == HD_NVINT4 ? ELEM_INT4
+         : (fmt == HD_NVFP4 || fmt == HD_MXFP4 || fmt == HD_NVFP4_UE4M4 || fmt == HD_NVFP4_UE5M3) ? ELEM_E2M1
+                                                                                                  : ELEM_E4M3;
 }
 __host__ __device__ constexpr int scale_kind(int fmt)
 {
-    return fmt == HD_INT8_E4M3 ? SCALE_INT8 : (fmt == HD_NVFP4 || fmt == HD_FP8_E4M3S) ? SCALE_E4M3 : SCALE_E8M0;
+    return fmt == HD_INT8_E4M3 ? SCALE_INT8
+         : (fmt == HD_NVFP4 || fmt == HD_FP8_E4M3S || fmt == HD_NVINT4) ? SCALE_E4M3
+         : fmt == HD_NVFP4_UE4M4 ? SCALE_UE4M4
+         : fmt == HD_NVFP4_UE5M3 ? SCALE_UE5M3
+                                 : SCALE_E8M0;
 }
+// Integer element grids (exact arithmetic encode) and 4-bit element codes.
+__host__ __device__ constexpr bool elem_int(int ek) { return ek == ELEM_INT8 || ek == ELEM_INT4; }
+__host__ __device__ constexpr bool elem_4bit(int ek) { return ek == ELEM_E2M1 || ek == ELEM_INT4; }
+// Unsigned every-code-finite scale grids.
+__host__ __device__ constexpr bool scale_unsigned(int sk) { return sk == SCALE_UE4M4 || sk == SCALE_UE5M3; }
 // First / last search candidate code of a scale grid.
 __host__ __device__ constexpr int cand_first(int sk) { return sk == SCALE_E8M0 ? 0 : 1; }
-__host__ __device__ constexpr int cand_last(int sk) { return sk == SCALE_E8M0 ? 254 : 126; }
+__host__ __device__ constexpr int cand_last(int sk)
+{
+    return sk == SCALE_E8M0 ? 254 : scale_unsigned(sk) ? 255 : 126;
+}
+// Scale codes that stand for a number (the rest are NaN codes).
+__host__ __device__ constexpr bool scale_code_valid(int sk, int c)
+{
+    return c >= 0 && c <= (sk == SCALE_E8M0 ? 254 : scale_unsigned(sk) ? 255 : 126);
+}
+// Scale codes per binade of the grid (8 for E4M3 / UE5M3 / INT8, 16 for
+// UE4M4, 1 for E8M0).
+__host__ __device__ constexpr int codes_per_binade(int sk)
+{
+    return sk == SCALE_E8M0 ? 1 : sk == SCALE_UE4M4 ? 16 : 8;
+}
 // Largest element magnitude (the C of s = Q_scale(amax / C)).
 __host__ __device__ constexpr float elem_max(int ek)
 {
-    return ek == ELEM_INT8 ? 127.0f : ek == ELEM_E2M1 ? 6.0f : 448.0f;
+    return ek == ELEM_INT8 ? 127.0f : ek == ELEM_INT4 ? 7.0f : ek == ELEM_E2M1 ? 6.0f : 448.0f;
+}
+// Smallest positive element value.
+__host__ __device__ constexpr float elem_min_pos(int ek)
+{
+    return ek == ELEM_E2M1 ? 0.5f : ek == ELEM_E4M3 ? 0x1p-9f : 1.0f;
 }
 
 __host__ __device__ inline float bits_f(uint32_t u)
@@ -73,10 +107,24 @@ __host__ __device__ inline float e8m0_value(int c)
     return c == 0 ? bits_f(0x00400000u) : bits_f((uint32_t)c << 23);
 }
 
+// Magnitude of an unsigned UExMy code c (every code finite): exponent field
+// e = c >> M, mantissa d = c & (2^M - 1); (2^M + d) 2^(e - bias - M), or
+// d 2^(1 - bias - M) when e = 0.
+template <int M, int BIAS>
+__host__ __device__ inline float ue_value(int c)
+{
+    const int e = c >> M, d = c & ((1 << M) - 1);
+    const float mant = (float)(e ? (1 << M) + d : d);
+    const int pw = (e ? e : 1) - BIAS - M;
+    return mant * bits_f((uint32_t)(127 + pw) << 23);  // 2^pw is normal for both grids
+}
+
 // The fp32 scale of scale code c on grid sk (c = 0 on an E4M3 grid is 0).
 __host__ __device__ inline float scale_value(int sk, int c)
 {
     if (sk == SCALE_E8M0) return e8m0_value(c);
+    if (sk == SCALE_UE4M4) return ue_value<4, 7>(c);
+    if (sk == SCALE_UE5M3) return ue_value<3, 15>(c);
     const float v = e4m3_value(c);
     return sk == SCALE_INT8 ? v / 127.0f : v;  // IEEE division (INT8 section)
 }
@@ -114,6 +162,7 @@ template <int EK>
 __device__ __forceinline__ float round_elem(float x)
 {
     if (EK == ELEM_INT8) return __builtin_rintf(fminf(x, 127.0f));
+    if (EK == ELEM_INT4) return __builtin_rintf(fminf(x, 7.0f));
     if (EK == ELEM_E2M1) {
         const float xc = fminf(x, 6.0f);
         const float C = bits_f((f_bits(fmaxf(xc, 1.0f)) & 0x7F800000u) + (22u << 23));
@@ -128,7 +177,7 @@ __device__ __forceinline__ float round_elem(float x)
 template <int EK>
 __device__ __forceinline__ uint32_t elem_index(float y)
 {
-    if (EK == ELEM_INT8) return (uint32_t)y;
+    if (elem_int(EK)) return (uint32_t)y;
     if (EK == ELEM_E2M1) {
         // the top 10 bits of 1, 1.5, 2, 3, 4, 6 are 0xFE..0x103, i.e. the code
         // plus 0xFC; 0.5 (0xFC) and 0 need the floor of 1 / 0
@@ -146,7 +195,7 @@ __device__ __forceinline__ uint32_t elem_index(float y)
 template <int EK>
 __device__ __forceinline__ float elem_value(uint32_t idx)
 {
-    if (EK == ELEM_INT8) return (float)idx;
+    if (elem_int(EK)) return (float)idx;
     if (EK == ELEM_E2M1) {
         // 0 .5 1 1.5 2 3 4 6: (2 + (idx & 1)) * 2^((idx >> 1) - 2), idx 1 is subnormal
         if (idx < 2) return idx ? 0.5f : 0.0f;
@@ -160,6 +209,7 @@ template <int EK>
 __device__ __forceinline__ uint32_t elem_code(uint32_t idx, bool neg)
 {
     if (EK == ELEM_INT8) return (uint32_t)(uint8_t)(neg ? -(int)idx : (int)idx);
+    if (EK == ELEM_INT4) return (uint32_t)(neg ? -(int)idx : (int)idx) & 15u;  // two's complement nibble
     if (EK == ELEM_E2M1) return idx | (neg ? 8u : 0u);
     return idx | (neg ? 0x80u : 0u);
 }
@@ -273,6 +323,39 @@ __device__ __forceinline__ int e4m3_mantissa_rank(int t, int *group)
     return off + pos;
 }
 
+// Round v >= 0 onto an unsigned UExMy grid (saturating at its largest value)
+// and return the code: the add-and-subtract-2^(e + 23 - M) rounding of
+// round_elem with the grid's smallest normal exponent, then the code from the
+// value's bits (subnormal codes are v / 2^(1 - bias - M)).
+template <int M, int BIAS>
+__device__ __forceinline__ int ue_round_code(float v)
+{
+    constexpr int EMIN = 1 - BIAS;  // exponent of the smallest normal
+    const float vmax = ue_value<M, BIAS>(255);  // the largest code
+    const float xc = fminf(v, vmax);
+    const float C = bits_f((f_bits(fmaxf(xc, bits_f((uint32_t)(127 + EMIN) << 23))) & 0x7F800000u) +
+                           ((uint32_t)(23 - M) << 23));
+    const float y = (xc + C) - C;
+    const uint32_t u = f_bits(y);
+    const int sub = (int)(y * bits_f((uint32_t)(127 + BIAS - 1 + M) << 23));
+    const int nrm = ((int)((u >> 23) & 0xFFu) - 127 + BIAS) << M | (int)((u >> (23 - M)) & ((1u << M) - 1));
+    return y < bits_f((uint32_t)(127 + EMIN) << 23) ? sub : nrm;
+}
+
+// OCP MX rule for power-of-two scales: code of 2^(floor(log2 amax) - emax),
+// emax the exponent of the largest element (E2M1 6 = 1.5 2^2, E4M3 448 =
+// 1.75 2^8), clamped to E8M0's 2^[-127, 127]; amax = 0 gives code 0.
+template <int EK>
+__device__ __forceinline__ int ocp_code(float amax)
+{
+    if (amax == 0.0f) return 0;
+    int ex;
+    __builtin_frexpf(amax, &ex);  // amax = f 2^ex, f in [0.5, 1): floor(log2 amax) = ex - 1
+    int E = ex - 1 - (EK == ELEM_E2M1 ? 2 : 8);
+    E = E < -127 ? -127 : (E > 127 ? 127 : E);
+    return E + 127;
+}
+
 // Naive scale code of a block with max |w| = amax ("Is Finer Better?" §2.1,
 // s = Q_scale(amax / C) with round-to-nearest scale quantisation; INT8 stores
 // amax itself as E4M3).  E4M3 grids may return code 0 (the zero scale).
@@ -286,6 +369,8 @@ __device__ __forceinline__ int naive_code(float amax)
         const float y = round_elem<ELEM_E4M3>(v);
         return (int)elem_index<ELEM_E4M3>(y);
     }
+    if (SK == SCALE_UE4M4) return ue_round_code<4, 7>(amax / elem_max(EK));
+    if (SK == SCALE_UE5M3) return ue_round_code<3, 15>(amax / elem_max(EK));
     const float v = amax / elem_max(EK);
     if (v == 0.0f) return 0;
     // v = f 2^E with f in [1, 2); frexp gives the exponent for subnormals too

@@ -8,8 +8,9 @@
 namespace hd {
 
 // Naive scale + encode (scales_in == NULL), or encode with given scale codes.
+// ocp != 0 (E8M0 grids): the OCP MX floor rule instead of the Naive snap.
 hipError_t launch_encode(int fmt, int B, const void *W, int wdt, int64_t N, int64_t K, const float *h,
-                         const uint8_t *scales_in, uint8_t *codes, uint8_t *scales, float *block_obj,
+                         const uint8_t *scales_in, uint8_t *codes, uint8_t *scales, float *block_obj, int ocp,
                          hipStream_t st);
 
 // SSE-Optimal (h == NULL) or H-Optimal search + encode.
@@ -26,6 +27,12 @@ hipError_t launch_search_mxfp8(int B, const void *W, int wdt, int64_t N, int64_t
                                uint8_t *codes, uint8_t *scales, float *block_obj, hipStream_t st);
 hipError_t launch_search_fp8s(int B, const void *W, int wdt, int64_t N, int64_t K, const float *h,
                               uint8_t *codes, uint8_t *scales, float *block_obj, hipStream_t st);
+hipError_t launch_search_nvfp4_ue4m4(int B, const void *W, int wdt, int64_t N, int64_t K, const float *h,
+                                     uint8_t *codes, uint8_t *scales, float *block_obj, hipStream_t st);
+hipError_t launch_search_nvfp4_ue5m3(int B, const void *W, int wdt, int64_t N, int64_t K, const float *h,
+                                     uint8_t *codes, uint8_t *scales, float *block_obj, hipStream_t st);
+hipError_t launch_search_nvint4(int B, const void *W, int wdt, int64_t N, int64_t K, const float *h,
+                                uint8_t *codes, uint8_t *scales, float *block_obj, hipStream_t st);
 
 hipError_t launch_dequant(int fmt, int B, const uint8_t *codes, const uint8_t *scales, int64_t N, int64_t K,
                           void *out, int out_t, hipStream_t st);

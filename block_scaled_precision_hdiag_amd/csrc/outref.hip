@@ -388,11 +388,10 @@ __global__ __launch_bounds__(256) void operand_kernel(const uint8_t *__restrict_
     const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
     if (e0 >= total) return;
     const int sc = scales[e0 / B];
-    const bool sval = SK == SCALE_E8M0 ? sc <= 254 : sc <= 126;
     // INT8 carries the E4M3 value of the scale code; 1/127 goes to the epilogue
-    const float s = !sval ? 0.0f : (EK == ELEM_INT8 ? e4m3_value(sc) : scale_value(SK, sc));
+    const float s = !scale_code_valid(SK, sc) ? 0.0f : (EK == ELEM_INT8 ? e4m3_value(sc) : scale_value(SK, sc));
     uint32_t c[8];
-    if (EK == ELEM_E2M1) {
+    if (elem_4bit(EK)) {
         const uint32_t v = *reinterpret_cast<const uint32_t *>(codes + e0 / 2);
 #pragma unroll
         for (int j = 0; j < 8; ++j) c[j] = (v >> (4 * j)) & 15u;
@@ -411,6 +410,9 @@ __global__ __launch_bounds__(256) void operand_kernel(const uint8_t *__restrict_
             const int q = (int)(int8_t)(uint8_t)c[j];
             const float f = q == -128 ? 0.0f : s * (float)q;  // exact: <= 11 significant bits
             o[j] = __builtin_bit_cast(uint16_t, (_Float16)f);
+        } else if (EK == ELEM_INT4) {
+            const int q = (int)((c[j] ^ 8u) & 15u) - 8;        // two's complement nibble
+            o[j] = f32_to_bf16(q == -8 ? 0.0f : s * (float)q);  // exact: <= 7 significant bits
         } else {
             bool neg, ok = true;
             uint32_t idx;
@@ -584,6 +586,9 @@ hipError_t launch_output_error_codes(int fmt, int B, const void *X, int64_t M, c
         case HD_MXFP4: launch_operand<ELEM_E2M1, SCALE_E8M0>(codes, scales, total, B, opnd, st); break;
         case HD_MXFP8: launch_operand<ELEM_E4M3, SCALE_E8M0>(codes, scales, total, B, opnd, st); break;
         case HD_FP8_E4M3S: launch_operand<ELEM_E4M3, SCALE_E4M3>(codes, scales, total, B, opnd, st); break;
+        case HD_NVFP4_UE4M4: launch_operand<ELEM_E2M1, SCALE_UE4M4>(codes, scales, total, B, opnd, st); break;
+        case HD_NVFP4_UE5M3: launch_operand<ELEM_E2M1, SCALE_UE5M3>(codes, scales, total, B, opnd, st); break;
+        case HD_NVINT4: launch_operand<ELEM_INT4, SCALE_E4M3>(codes, scales, total, B, opnd, st); break;
         default: return hipErrorInvalidValue;
         }
     }

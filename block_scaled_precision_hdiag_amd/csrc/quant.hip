@@ -23,7 +23,7 @@ __global__ __launch_bounds__(256) void encode_kernel(const T *__restrict__ W, in
                                                      const float *__restrict__ h,
                                                      const uint8_t *__restrict__ scales_in,
                                                      uint8_t *__restrict__ codes, uint8_t *__restrict__ scales,
-                                                     float *__restrict__ block_obj)
+                                                     float *__restrict__ block_obj, int ocp)
 {
     constexpr int TPB = B > ENC_EPT ? B / ENC_EPT : 1;  // lanes per block
     constexpr int NBT = B < ENC_EPT ? ENC_EPT / B : 1;  // blocks per lane
@@ -73,10 +73,13 @@ __global__ __launch_bounds__(256) void encode_kernel(const T *__restrict__ W, in
         float s;
         if (GIVEN) {
             code[bb] = (bb * EB < 8 * nv8) ? (int)scales_in[blk] : 0;
-            const bool valid = SK == SCALE_E8M0 ? code[bb] <= 254 : code[bb] <= 126;
-            s = valid ? scale_value(SK, code[bb]) : 0.0f;
+            s = scale_code_valid(SK, code[bb]) ? scale_value(SK, code[bb]) : 0.0f;
         } else {
-            code[bb] = naive_code<EK, SK>(amax);
+            // ocp (E8M0 grids only): the OCP MX floor rule instead of the snap
+            if constexpr (SK == SCALE_E8M0)
+                code[bb] = ocp ? ocp_code<EK>(amax) : naive_code<EK, SK>(amax);
+            else
+                code[bb] = naive_code<EK, SK>(amax);
             s = scale_value(SK, code[bb]);
         }
         const float r = (s != 0.0f) ? 1.0f / s : 0.0f;
@@ -100,7 +103,7 @@ __global__ __launch_bounds__(256) void encode_kernel(const T *__restrict__ W, in
         }
         return;
     }
-    if (EK == ELEM_E2M1) {
+    if (elem_4bit(EK)) {
         uint32_t v[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -142,7 +145,7 @@ __global__ __launch_bounds__(256) void encode_kernel(const T *__restrict__ W, in
 
 template <int EK, int SK, typename T, bool GIVEN>
 static hipError_t encode_b(int B, const void *W, int64_t N, int64_t K, const float *h, const uint8_t *si,
-                           uint8_t *codes, uint8_t *scales, float *bo, hipStream_t st)
+                           uint8_t *codes, uint8_t *scales, float *bo, int ocp, hipStream_t st)
 {
     const int64_t total = N * K;
     const dim3 grid((unsigned)((total / ENC_EPT + 255) / 256));
@@ -150,9 +153,9 @@ static hipError_t encode_b(int B, const void *W, int64_t N, int64_t K, const flo
 #define HD_ENC_CASE(BB)                                                                                      \
     case BB:                                                                                                 \
         if (bo)                                                                                              \
-            encode_kernel<EK, SK, T, BB, GIVEN, true><<<grid, 256, 0, st>>>(w, total, K, h, si, codes, scales, bo);  \
+            encode_kernel<EK, SK, T, BB, GIVEN, true><<<grid, 256, 0, st>>>(w, total, K, h, si, codes, scales, bo, ocp);  \
         else                                                                                                 \
-            encode_kernel<EK, SK, T, BB, GIVEN, false><<<grid, 256, 0, st>>>(w, total, K, h, si, codes, scales, bo); \
+            encode_kernel<EK, SK, T, BB, GIVEN, false><<<grid, 256, 0, st>>>(w, total, K, h, si, codes, scales, bo, ocp); \
         break;
     switch (B) {
         HD_ENC_CASE(8)
@@ -169,32 +172,34 @@ static hipError_t encode_b(int B, const void *W, int64_t N, int64_t K, const flo
 
 template <int EK, int SK>
 static hipError_t encode_f(int B, const void *W, int wdt, int64_t N, int64_t K, const float *h,
-                           const uint8_t *si, uint8_t *codes, uint8_t *scales, float *bo, hipStream_t st)
+                           const uint8_t *si, uint8_t *codes, uint8_t *scales, float *bo, int ocp, hipStream_t st)
 {
     if (si) {
-        return wdt == 1 ? encode_b<EK, SK, bf16_t, true>(B, W, N, K, h, si, codes, scales, bo, st)
-                        : encode_b<EK, SK, float, true>(B, W, N, K, h, si, codes, scales, bo, st);
+        return wdt == 1 ? encode_b<EK, SK, bf16_t, true>(B, W, N, K, h, si, codes, scales, bo, 0, st)
+                        : encode_b<EK, SK, float, true>(B, W, N, K, h, si, codes, scales, bo, 0, st);
     }
-    return wdt == 1 ? encode_b<EK, SK, bf16_t, false>(B, W, N, K, h, si, codes, scales, bo, st)
-                    : encode_b<EK, SK, float, false>(B, W, N, K, h, si, codes, scales, bo, st);
+    return wdt == 1 ? encode_b<EK, SK, bf16_t, false>(B, W, N, K, h, si, codes, scales, bo, ocp, st)
+                    : encode_b<EK, SK, float, false>(B, W, N, K, h, si, codes, scales, bo, ocp, st);
 }
 
 hipError_t launch_encode(int fmt, int B, const void *W, int wdt, int64_t N, int64_t K, const float *h,
-                         const uint8_t *scales_in, uint8_t *codes, uint8_t *scales, float *block_obj,
+                         const uint8_t *scales_in, uint8_t *codes, uint8_t *scales, float *block_obj, int ocp,
                          hipStream_t st)
 {
+#define HD_ENC_FMT(F)                                                                                      \
+    case F:                                                                                                \
+        return encode_f<elem_kind(F), scale_kind(F)>(B, W, wdt, N, K, h, scales_in, codes, scales, block_obj, ocp, st);
     switch (fmt) {
-    case HD_INT8_E4M3:
-        return encode_f<ELEM_INT8, SCALE_INT8>(B, W, wdt, N, K, h, scales_in, codes, scales, block_obj, st);
-    case HD_NVFP4:
-        return encode_f<ELEM_E2M1, SCALE_E4M3>(B, W, wdt, N, K, h, scales_in, codes, scales, block_obj, st);
-    case HD_MXFP4:
-        return encode_f<ELEM_E2M1, SCALE_E8M0>(B, W, wdt, N, K, h, scales_in, codes, scales, block_obj, st);
-    case HD_MXFP8:
-        return encode_f<ELEM_E4M3, SCALE_E8M0>(B, W, wdt, N, K, h, scales_in, codes, scales, block_obj, st);
-    case HD_FP8_E4M3S:
-        return encode_f<ELEM_E4M3, SCALE_E4M3>(B, W, wdt, N, K, h, scales_in, codes, scales, block_obj, st);
+        HD_ENC_FMT(HD_INT8_E4M3)
+        HD_ENC_FMT(HD_NVFP4)
+        HD_ENC_FMT(HD_MXFP4)
+        HD_ENC_FMT(HD_MXFP8)
+        HD_ENC_FMT(HD_FP8_E4M3S)
+        HD_ENC_FMT(HD_NVFP4_UE4M4)
+        HD_ENC_FMT(HD_NVFP4_UE5M3)
+        HD_ENC_FMT(HD_NVINT4)
     }
+#undef HD_ENC_FMT
     return hipErrorInvalidValue;
 }
 
@@ -208,10 +213,9 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict_
     const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
     if (e0 >= total) return;
     const int sc = scales[e0 / B];
-    const bool sval = SK == SCALE_E8M0 ? sc <= 254 : sc <= 126;
-    const float s = sval ? scale_value(SK, sc) : 0.0f;
+    const float s = scale_code_valid(SK, sc) ? scale_value(SK, sc) : 0.0f;
     uint32_t c[8];
-    if (EK == ELEM_E2M1) {
+    if (elem_4bit(EK)) {
         const uint32_t v = *reinterpret_cast<const uint32_t *>(codes + e0 / 2);
 #pragma unroll
         for (int j = 0; j < 8; ++j) c[j] = (v >> (4 * j)) & 15u;
@@ -231,6 +235,11 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict_
         if (EK == ELEM_INT8) {
             const int q = (int)(int8_t)(uint8_t)c[j];
             ok = q != -128;
+            neg = q < 0;
+            idx = (uint32_t)(q < 0 ? -q : q);
+        } else if (EK == ELEM_INT4) {
+            const int q = (int)((c[j] ^ 8u) & 15u) - 8;  // two's complement nibble
+            ok = q != -8;
             neg = q < 0;
             idx = (uint32_t)(q < 0 ? -q : q);
         } else if (EK == ELEM_E2M1) {
@@ -274,13 +283,20 @@ hipError_t launch_dequant(int fmt, int B, const uint8_t *codes, const uint8_t *s
                           void *out, int out_t, hipStream_t st)
 {
     const int64_t total = N * K;
+#define HD_DEQ_FMT(F)                                                                                      \
+    case F:                                                                                                \
+        return dequant_f<elem_kind(F), scale_kind(F)>(B, codes, scales, total, out, out_t, st);
     switch (fmt) {
-    case HD_INT8_E4M3: return dequant_f<ELEM_INT8, SCALE_INT8>(B, codes, scales, total, out, out_t, st);
-    case HD_NVFP4: return dequant_f<ELEM_E2M1, SCALE_E4M3>(B, codes, scales, total, out, out_t, st);
-    case HD_MXFP4: return dequant_f<ELEM_E2M1, SCALE_E8M0>(B, codes, scales, total, out, out_t, st);
-    case HD_MXFP8: return dequant_f<ELEM_E4M3, SCALE_E8M0>(B, codes, scales, total, out, out_t, st);
-    case HD_FP8_E4M3S: return dequant_f<ELEM_E4M3, SCALE_E4M3>(B, codes, scales, total, out, out_t, st);
+        HD_DEQ_FMT(HD_INT8_E4M3)
+        HD_DEQ_FMT(HD_NVFP4)
+        HD_DEQ_FMT(HD_MXFP4)
+        HD_DEQ_FMT(HD_MXFP8)
+        HD_DEQ_FMT(HD_FP8_E4M3S)
+        HD_DEQ_FMT(HD_NVFP4_UE4M4)
+        HD_DEQ_FMT(HD_NVFP4_UE5M3)
+        HD_DEQ_FMT(HD_NVINT4)
     }
+#undef HD_DEQ_FMT
     return hipErrorInvalidValue;
 }
 

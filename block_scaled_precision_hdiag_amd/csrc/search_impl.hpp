@@ -58,16 +58,17 @@ __device__ __forceinline__ double sat_lower_bound(const float *a, const double *
     return group_sum<LPB>(lb);
 }
 
-// Lower bound, valid for every INT8 candidate scale s' >= s, of the
-// objective the kernel computes: an element with a <= s has a / s' <= 1, so it
-// encodes to q = 0 (residual a) or q = 1 (residual s' - a >= s - a, exact in
-// fp32 by Sterbenz's lemma); it adds >= om min(a, s - a)^2, the others >= 0.
-// (For a < s / 2 this is the zero-code term a^2; the s - a branch also bounds
-// the elements that round to 1.)
-template <int SEG, int LPB, bool WEIGHTED>
+// Lower bound, valid for every candidate scale s' >= s, of the objective the
+// kernel computes, for element grids whose smallest positive value v1 (INT8,
+// INT4: 1; E2M1: 0.5) is at most half the next one: an element with
+// a <= v1 s has a / s' <= v1, so it encodes to 0 (residual a) or to v1
+// (residual v1 s' - a >= v1 s - a, exact in fp32 by Sterbenz's lemma); it adds
+// >= om min(a, v1 s - a)^2, the others >= 0.  (For a < v1 s / 2 this is the
+// zero-code term a^2; the other branch also bounds the elements at v1.)
+template <int EK, int SEG, int LPB, bool WEIGHTED>
 __device__ __forceinline__ double small_lower_bound(const float *a, const double *om, float s)
 {
-    const double sd = (double)s;
+    const double sd = (double)elem_min_pos(EK) * (double)s;
     double lb = 0.0;
 #pragma unroll
     for (int j = 0; j < SEG; ++j) {
@@ -86,7 +87,7 @@ __device__ __forceinline__ float search_resid(float a, float s, float r)
 {
     const float x = quotient<SK, ONE_STEP>(a, s, r);
     const float y = round_elem<EK>(x);
-    if (EK == ELEM_INT8) {
+    if (elem_int(EK)) {
         const float wq = s * y;  // fl32(s * q): INT8 scales carry a full fp32 mantissa
         return a - wq;
     }
@@ -192,16 +193,18 @@ __global__ __launch_bounds__(256) void search_kernel(const T *__restrict__ W, in
             }
         }
     };
-    // start one code below Naive to one binade above it (where the optimum
-    // lies for nearly every block); widen by SEARCH_STEP codes while some
-    // lane cannot prove the candidates beyond its window strictly worse than
-    // its best so far (above: small_lower_bound; below: sat_lower_bound)
-    constexpr int SEARCH_STEP = 4;
-    int olo = -1, ohi = 8;
+    // INT8: start one code below Naive to one binade above it (where the
+    // optimum lies for nearly every block); the other grids: half a binade
+    // below to one binade above.  Widen by SEARCH_STEP codes while some lane
+    // cannot prove the candidates beyond its window strictly worse than its
+    // best so far (above: small_lower_bound; below: sat_lower_bound)
+    constexpr int CPB = codes_per_binade(SK);
+    constexpr int SEARCH_STEP = CPB > 8 ? CPB / 2 : 4;
+    int olo = EK == ELEM_INT8 ? -1 : -CPB / 2, ohi = CPB;
     eval_range(olo, ohi);
     for (;;) {
         const int c1 = cb + ohi + 1;
-        const double lb = small_lower_bound<SEG, LPB, WEIGHTED>(a, om, cand[min(c1, NC - 1)].x);
+        const double lb = small_lower_bound<EK, SEG, LPB, WEIGHTED>(a, om, cand[min(c1, NC - 1)].x);
         const bool need = active && c1 <= cendl && !(lb * (1.0 - 0x1p-20) > best);
         if (wave_all(!need)) break;
         eval_range(ohi + 1, ohi + SEARCH_STEP);
@@ -407,7 +410,10 @@ static hipError_t search_go(const void *W, int64_t N, int64_t K, const float *h,
     const T *w = static_cast<const T *>(W);
     // (SEG, LPB) = (32, *) serves only the unweighted search, (16, > 1) only the weighted one
     constexpr bool MAY_W = SEG <= 16, MAY_U = !(SEG == 16 && LPB > 1);
-    if constexpr (EK == ELEM_INT8) {
+    // integer elements and the unsigned scale grids: the generic search kernel
+    // (exact arithmetic quantise-dequantise, per-lane windows); E2M1 / E4M3
+    // elements on E4M3 / E8M0 grids: the conversion-instruction kernel
+    if constexpr (elem_int(EK) || scale_unsigned(SK)) {
         if constexpr (MAY_W) {
             if (h) {
                 search_kernel<EK, SK, T, SEG, LPB, true><<<grid, 256, 0, st>>>(w, N, K, h, codes, scales, bo);

@@ -49,14 +49,19 @@ typedef enum {
 typedef enum { HD_F32 = 0, HD_BF16 = 1 } hd_dtype;
 
 /* Scale choice (qwantize "Results", all three format tables):
- *   HD_NAIVE   - amax of the block snapped onto the scale grid;
- *   HD_SSE_OPT - the candidate minimising sum_j (w_j - s Q(w_j / s))^2;
- *   HD_H_OPT   - the candidate minimising sum_j h_j (w_j - s Q(w_j / s))^2, the
- *                diagonal-Hessian form of the output error (quantisation
- *                algorithms note, §1).
+ *   HD_NAIVE     - amax of the block snapped onto the scale grid;
+ *   HD_SSE_OPT   - the candidate minimising sum_j (w_j - s Q(w_j / s))^2;
+ *   HD_H_OPT     - the candidate minimising sum_j h_j (w_j - s Q(w_j / s))^2,
+ *                  the diagonal-Hessian form of the output error (quantisation
+ *                  algorithms note, §1);
+ *   HD_NAIVE_OCP - power-of-two grids only (HD_MXFP4, HD_MXFP8): the OCP MX
+ *                  rule s = 2^(floor(log2 amax) - emax), emax the exponent of
+ *                  the largest element (2 for E2M1, 8 for E4M3), clamped to
+ *                  E8M0's range; amax = 0 gives code 0 ("Is Finer Better?"
+ *                  §2.1 cites the OCP specification that defines it).
  * The search methods evaluate every candidate of the grid and return the first
  * (lowest) scale code among equal minima. */
-typedef enum { HD_NAIVE = 0, HD_SSE_OPT = 1, HD_H_OPT = 2 } hd_method;
+typedef enum { HD_NAIVE = 0, HD_SSE_OPT = 1, HD_H_OPT = 2, HD_NAIVE_OCP = 3 } hd_method;
 
 /* Element format x scale grid.
  *   HD_INT8_E4M3 - symmetric INT8 elements in [-127, 127]; the block's amax is
@@ -67,9 +72,20 @@ typedef enum { HD_NAIVE = 0, HD_SSE_OPT = 1, HD_H_OPT = 2 } hd_method;
  *   HD_MXFP4     - E2M1 elements, E8M0 power-of-two scale (OCP MX, §2.1).
  *   HD_MXFP8     - E4M3 elements, E8M0 scale.
  *   HD_FP8_E4M3S - E4M3 elements, E4M3 scale.
+ *   HD_NVFP4_UE4M4 - E2M1 elements, unsigned UE4M4 scale (4 exponent bits,
+ *                  bias 7, 4 mantissa bits, every code finite: 0x01..0xFF,
+ *                  2^-10 .. 496) (qwantize "Results", Exotic Scales).
+ *   HD_NVFP4_UE5M3 - E2M1 elements, unsigned UE5M3 scale (bias 15, 3 mantissa
+ *                  bits: 2^-17 .. 122880) (same section; "Is Finer Better?"
+ *                  §5.2).
+ *   HD_NVINT4    - symmetric INT4 elements [-7, 7] (two's complement nibbles,
+ *                  element 2i in the low nibble), E4M3 scale
+ *                  s = Q_E4M3(amax / 7) (the NVINT4 rows of the qwantize
+ *                  "Results" GPTQ tables, read with the generic rule of "Is
+ *                  Finer Better?" §2.1).
  * Search candidates: the 126 positive finite E4M3 codes 0x01..0x7E (E4M3 and
- * INT8 grids; max 448), or all 255 finite E8M0 codes 0x00..0xFE (2^-127 ..
- * 2^127).  Naive may also return E4M3 code 0 (the zero scale: every element
+ * INT8 grids; max 448), all 255 finite E8M0 codes 0x00..0xFE (2^-127 ..
+ * 2^127), or the 255 positive UE4M4 / UE5M3 codes.  Naive may also return E4M3 code 0 (the zero scale: every element
  * encodes to 0), when amax / C rounds into the zero bin ("Is Finer Better?",
  * App. F.3). */
 typedef enum {
@@ -77,7 +93,10 @@ typedef enum {
     HD_NVFP4 = 1,
     HD_MXFP4 = 2,
     HD_MXFP8 = 3,
-    HD_FP8_E4M3S = 4
+    HD_FP8_E4M3S = 4,
+    HD_NVFP4_UE4M4 = 5,
+    HD_NVFP4_UE5M3 = 6,
+    HD_NVINT4 = 7
 } hd_format;
 
 /* ---------------------------------------------------------------- hdiag --- */
@@ -106,8 +125,10 @@ hd_status hdiag(const void *X, hd_dtype xt, int64_t M, int64_t K, float *h, void
  *            HD_SSE_OPT.
  *   codes  : element codes.  HD_INT8_E4M3: [N, K] int8 two's complement.
  *            HD_MXFP8 / HD_FP8_E4M3S: [N, K] E4M3 bytes (sign bit 7).
- *            HD_NVFP4 / HD_MXFP4: [N, K/2] bytes of two E2M1 nibbles (sign bit
- *            3), element 2i in the low nibble.  A negative input that rounds to
+ *            HD_NVFP4 / HD_MXFP4 / HD_NVFP4_UE4M4 / HD_NVFP4_UE5M3: [N, K/2]
+ *            bytes of two E2M1 nibbles (sign bit 3), element 2i in the low
+ *            nibble.  HD_NVINT4: [N, K/2] bytes of two INT4 two's complement
+ *            nibbles, same order.  A negative input that rounds to
  *            zero keeps its sign bit (E2M1 0x8, E4M3 0x80).
  *   scales : [N, K/B] scale codes (E4M3 or E8M0 bytes).
  *   block_obj: optional [N, K/B] float32: the block's objective at the chosen
@@ -118,8 +139,8 @@ hd_status hdiag(const void *X, hd_dtype xt, int64_t M, int64_t K, float *h, void
  * fl32(s * val(q)).  Division is IEEE round-to-nearest (qwantize "Results",
  * Correctness notes, on why a reciprocal-multiply moves boundary ties).
  * Errors: HD_ERR_INVALID_ARG for NULL W / codes / scales (when N*K > 0), bad
- * enums, an unsupported B, K % B != 0, N or K < 0, H_OPT without h, misaligned
- * pointers. */
+ * enums, an unsupported B, K % B != 0, N or K < 0, H_OPT without h,
+ * HD_NAIVE_OCP on a grid that is not E8M0, misaligned pointers. */
 hd_status quantize_blocks(hd_method method, hd_format fmt, int32_t B, const void *W, hd_dtype wt,
                           int64_t N, int64_t K, const float *h, uint8_t *codes, uint8_t *scales,
                           float *block_obj, void *stream);

@@ -44,6 +44,11 @@ def test_format_info_bits_per_weight():
     assert hd.hdiag_format_info(hd.MXFP4, 32)[2] == 255
     assert hd.hdiag_format_info(hd.MXFP8, 32)[:3] == (8, 8, 255)
     assert hd.hdiag_format_info(hd.INT8_E4M3, 32)[3] == 8.25
+    # the unsigned scale grids have 255 candidates (qwantize "Exotic Scales"),
+    # NVINT4 keeps E4M3's 126; all three are 4-bit elements with 8-bit scales
+    assert hd.hdiag_format_info(hd.NVFP4_UE4M4, 16) == (4, 8, 255, 4.5)
+    assert hd.hdiag_format_info(hd.NVFP4_UE5M3, 16) == (4, 8, 255, 4.5)
+    assert hd.hdiag_format_info(hd.NVINT4, 16) == (4, 8, 126, 4.5)
 
 
 def test_strerror():
@@ -71,6 +76,15 @@ def test_quantize_blocks_rejects(args, needle):
     rc = hd.lib().quantize_blocks(*args, None)
     assert rc == hd.HD_ERR_INVALID_ARG
     assert needle in hd.lib().hdiag_last_error().decode()
+
+
+def test_ocp_rule_needs_e8m0():
+    rc = hd.lib().quantize_blocks(hd.NAIVE_OCP, hd.NVFP4, 16, A, hd.HD_BF16, 4, 32, None, A, A, None, None)
+    assert rc == hd.HD_ERR_INVALID_ARG and "E8M0" in hd.lib().hdiag_last_error().decode()
+    rc = hd.lib().quantize_blocks(4, hd.MXFP4, 32, A, hd.HD_BF16, 4, 32, None, A, A, None, None)
+    assert rc == hd.HD_ERR_INVALID_ARG and "unknown method" in hd.lib().hdiag_last_error().decode()
+    rc = hd.lib().quantize_blocks(hd.SSE_OPT, 8, 32, A, hd.HD_BF16, 4, 32, None, A, A, None, None)
+    assert rc == hd.HD_ERR_INVALID_ARG and "unknown format" in hd.lib().hdiag_last_error().decode()
 
 
 def test_empty_inputs_are_noops():

@@ -17,7 +17,7 @@ import block_scaled_precision_hdiag_amd as hd
 
 pytestmark = pytest.mark.gpu
 
-FMTS = [hd.INT8_E4M3, hd.NVFP4, hd.MXFP4, hd.MXFP8, hd.FP8_E4M3S]
+FMTS = [hd.INT8_E4M3, hd.NVFP4, hd.MXFP4, hd.MXFP8, hd.FP8_E4M3S, hd.NVFP4_UE4M4, hd.NVFP4_UE5M3, hd.NVINT4]
 
 
 @pytest.fixture(scope="module", autouse=True)

@@ -18,7 +18,7 @@ import block_scaled_precision_hdiag_amd as hd
 
 pytestmark = pytest.mark.gpu
 
-FMTS = [hd.INT8_E4M3, hd.NVFP4, hd.MXFP4, hd.MXFP8, hd.FP8_E4M3S]
+FMTS = [hd.INT8_E4M3, hd.NVFP4, hd.MXFP4, hd.MXFP8, hd.FP8_E4M3S, hd.NVFP4_UE4M4, hd.NVFP4_UE5M3, hd.NVINT4]
 BLOCKS = [8, 16, 32, 64, 128, 256]
 
 
@@ -83,6 +83,27 @@ def test_naive_bit_exact(fmt, B, dtype):
     np.testing.assert_array_equal(npy(s_g), s_o)
     np.testing.assert_array_equal(npy(c_g), c_o)
     np.testing.assert_allclose(npy(obj_g), obj_o.astype(np.float32), rtol=2e-6)
+
+
+@pytest.mark.parametrize("fmt", [hd.MXFP4, hd.MXFP8])
+@pytest.mark.parametrize("B", [8, 32, 256])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_naive_ocp_bit_exact(fmt, B, dtype):
+    """The OCP MX floor rule for power-of-two scales, bit-exact with the oracle
+    (scales, codes, objectives), including all-zero and tiny blocks."""
+    N, K = 41, 1024
+    W = weights_for(fmt, N, K, 1500 + fmt * 10 + B, dtype).float()
+    W[3, :B] = 0.0
+    W[5, :B] *= 1e-30
+    W = W.to(dtype)
+    c_o, s_o, obj_o = oracle.quantize(oracle.NAIVE_OCP, fmt, B, synth.bits(W))
+    c_g, s_g, obj_g = hd.quantize_blocks(hd.NAIVE_OCP, fmt, B, dev(W), block_obj=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(npy(s_g), s_o)
+    np.testing.assert_array_equal(npy(c_g), c_o)
+    np.testing.assert_allclose(npy(obj_g), obj_o.astype(np.float32), rtol=2e-6)
+    with pytest.raises(hd.HdiagError):
+        hd.quantize_blocks(hd.NAIVE_OCP, hd.NVFP4, 16, dev(W))
 
 
 @pytest.mark.parametrize("fmt", FMTS)
