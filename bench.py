@@ -84,6 +84,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=8, help="rows of W in the CPU sample")
+    ap.add_argument("--suite", choices=["headline", "formats"], default="headline",
+                    help="headline: the step above (one JSON line, the default); formats: every element / "
+                         "scale format x B in {16, 32} x scale choice on the same W and h (one JSON line)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="before timing, run one device copy of this many MB (a known-size kernel that "
                          "calibrates HBM byte counters)")
@@ -107,6 +110,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     hd.lib()
+    if args.suite == "formats":
+        return formats_suite(args, dev)
 
     cfg = synth.CONFIGS[2]
     W_cpu, X_cpu = synth.config_inputs(2)
@@ -264,6 +269,60 @@ def main():
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(W_cpu, X_cpu, blocks, methods, fmt, args.cpu_rows, value)
     print(json.dumps(out), flush=True)
+
+
+def formats_suite(args, dev):
+    """Scale choice for every format on the down_proj stand-in (W 2560x9728,
+    h from X 16384x9728): per (format, B, method) the kernel time of
+    quantize_blocks (median of `steps` launches after `warmup`, HIP events),
+    Gweights/s, and the weight / output error of the result (the output error
+    against one stored X W^T reference)."""
+    import torch
+
+    import block_scaled_precision_hdiag_amd as hd
+    import synth
+
+    W_cpu, X_cpu = synth.config_inputs(2)
+    N, K = W_cpu.shape
+    M = X_cpu.shape[0]
+    W, X = W_cpu.to(dev), X_cpu.to(dev)
+    h = hd.hdiag(X)
+    ref = hd.output_reference(X, W)
+    ws_o = torch.empty(hd.output_error_codes_workspace_size(M, N, K), dtype=torch.uint8, device=dev)
+    rows = []
+    names = {v: k for k, v in hd.FORMATS.items()}
+    for fmt in sorted(names):
+        nc = hd.hdiag_format_info(fmt, 16)[2]
+        meths = [("naive", hd.NAIVE), ("sse", hd.SSE_OPT), ("h", hd.H_OPT)]
+        if fmt in (hd.MXFP4, hd.MXFP8):
+            meths.append(("naive_ocp", hd.NAIVE_OCP))
+        for B in (16, 32):
+            for mname, m in meths:
+                codes = torch.empty(hd.codes_shape(fmt, N, K), dtype=torch.uint8, device=dev)
+                scales = torch.empty((N, K // B), dtype=torch.uint8, device=dev)
+                run = lambda: hd.quantize_blocks(m, fmt, B, W, h=h, codes=codes, scales=scales)
+                for _ in range(max(args.warmup, 1)):
+                    run()
+                ts = []
+                for _ in range(max(args.steps, 1)):
+                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a.record()
+                    run()
+                    b.record()
+                    torch.cuda.synchronize()
+                    ts.append(a.elapsed_time(b))
+                ms = sorted(ts)[len(ts) // 2]
+                Wq = hd.dequantize(fmt, B, codes, scales, N, K)
+                we = hd.weight_error(W, Wq).item()
+                oe = hd.output_error_codes(fmt, B, X, codes, scales, ref, N, K, workspace=ws_o).item()
+                rows.append({"format": names[fmt], "B": B, "method": mname, "candidates": nc,
+                             "ms": round(ms, 4), "gweights_per_s": round(N * K / (ms * 1e-3) / 1e9, 2),
+                             "weight_error": round(we, 6), "output_error": round(oe, 6)})
+    print(json.dumps({"suite": "formats", "unit": "Gweights/s",
+                      "config": {"workload": "scale choice on W 2560x9728 bf16 (Student-t(4) x 0.02, row gains), "
+                                             "h from X 16384x9728 bf16; every format, B in {16, 32}",
+                                 "W": [N, K], "X": [M, K]},
+                      "data": "synthetic", "rows": rows}), flush=True)
 
 
 def cpu_baseline(W_cpu, X_cpu, blocks, methods, fmt, rows, gpu_value):

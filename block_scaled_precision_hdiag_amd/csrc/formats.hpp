@@ -241,37 +241,6 @@ __device__ __forceinline__ uint32_t fp8x2(float a, float b, float p2)
 }
 __device__ __forceinline__ hd_v2f fp8x2_val(uint32_t half) { return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(half, 1.0f, false); }
 
-// Eight elements at once: codes packed into one dword (E2M1, byte i = pair i)
-// or two (E4M3, half i of dword q = pair 2q + i), then the eight grid values.
-// Chaining the partial-write operand avoids clearing and masking per pair.
-template <int EK>
-__device__ __forceinline__ void quant8_vals(const float *x, float p2, float *v)
-{
-    if (EK == ELEM_E2M1) {
-        uint32_t c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, x[0], x[1], p2, 0);
-        c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, x[2], x[3], p2, 1);
-        c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, x[4], x[5], p2, 2);
-        c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, x[6], x[7], p2, 3);
-        const hd_v2f v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 0);
-        const hd_v2f v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 1);
-        const hd_v2f v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 2);
-        const hd_v2f v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 3);
-        v[0] = v0.x; v[1] = v0.y; v[2] = v1.x; v[3] = v1.y;
-        v[4] = v2.x; v[5] = v2.y; v[6] = v3.x; v[7] = v3.y;
-    } else {
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            hd_v2s c = {0, 0};
-            c = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(c, x[4 * q], x[4 * q + 1], p2, false);
-            c = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(c, x[4 * q + 2], x[4 * q + 3], p2, true);
-            const uint32_t u = (uint32_t)(uint16_t)c.x | ((uint32_t)(uint16_t)c.y << 16);
-            const hd_v2f v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(u, 1.0f, false);
-            const hd_v2f v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(u, 1.0f, true);
-            v[4 * q] = v0.x; v[4 * q + 1] = v0.y; v[4 * q + 2] = v1.x; v[4 * q + 3] = v1.y;
-        }
-    }
-}
-
 // A positive E4M3 or E8M0 scale as m * p2 with m in [1, 2) one of the eight
 // E4M3 mantissas (1 for E8M0) and p2 a power of two; rm = fl32(1 / m).
 // fl32(a / s) = fl32(a / m) / p2 whenever the result is an fp32 normal, and
@@ -297,30 +266,6 @@ __device__ __forceinline__ ScaleParts scale_parts(float s)
     r.rm = 1.0f / r.m;
     r.p2 = __builtin_ldexpf(1.0f, ex - 1);
     return r;
-}
-
-// Order of the 126 E4M3 search candidates (index t = code - 1) grouped by
-// mantissa m = (8 + g) / 8, g = 0..7, and by code within a group.  A normal
-// code (e << 3) | g has mantissa g; a subnormal code mm = 1..7 is
-// mm * 2^-9 = ((8 + g) / 8) 2^(k - 9) with k = floor(log2 mm).  Group g holds
-// ctz(8 + g) subnormal codes (g odd: none) and 15 normal ones (14 for g = 7:
-// 0x7F is NaN).  Returns the position and the group.
-__device__ __forceinline__ int e4m3_mantissa_rank(int t, int *group)
-{
-    const int c = t + 1, e = c >> 3, mm = c & 7;
-    int g, pos;
-    if (e) {
-        g = mm;
-        pos = ((g & 1) ? 0 : __builtin_ctz(8 + g)) + e - 1;
-    } else {
-        const int k = 31 - __builtin_clz(mm);
-        g = (mm << (3 - k)) & 7;
-        pos = k - (3 - __builtin_ctz(8 + g));
-    }
-    int off = 0;
-    for (int q = 0; q < g; ++q) off += 15 - (q == 7) + ((q & 1) ? 0 : __builtin_ctz(8 + q));
-    *group = g;
-    return off + pos;
 }
 
 // Round v >= 0 onto an unsigned UExMy grid (saturating at its largest value)

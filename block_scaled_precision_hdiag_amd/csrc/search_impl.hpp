@@ -8,8 +8,8 @@
 // the first strict minimum (the lowest code on ties), then encodes the block
 // with it.  om_j = 1 (SSE) or h_j (H).
 //
-// Mapping (the work is FP32-VALU bound, ~10 instructions per weight and
-// candidate):
+// Mapping (the work is VALU bound: about 10 to 13 instructions per weight and
+// evaluated candidate):
 //   - one lane owns one block segment of SEG weights held in registers (32,
 //     or 16 for the weighted search, which also holds h); a block of B > SEG
 //     spans LPB = B / SEG adjacent lanes whose partial objectives are combined
@@ -23,15 +23,18 @@
 //   - candidates at and above the first scale that rounds the block's amax to
 //     zero all give sum_j om_j w_j^2 (every element encodes to 0): they could
 //     only tie, and ties keep the lower code, so they are never evaluated;
-//   - INT8: each lane walks candidate offsets from its own block's Naive
-//     code (the optimum lies within a binade above it for nearly every
-//     block), so the rows of different magnitude that share a wave share
-//     offsets, not codes; the window widens only while some lane cannot prove
-//     the candidates outside it strictly worse than its best so far: below it
-//     every element above fl32(Q s) saturates (sat_lower_bound), above it
-//     every element a <= s stays at code 0 or 1 (small_lower_bound).  Both
-//     bounds hold for the objective as the kernel computes it, so the chosen
-//     code is the one the full scan picks.
+//   - each lane walks candidate offsets from its own block's Naive code, so
+//     the rows of different magnitude that share a wave share offsets, not
+//     codes (measured: 1.5-1.9x faster than walking common codes, which also
+//     used the gfx950 FP4/FP8 conversions for two weights at a time); the
+//     window widens only while some lane cannot prove the candidates outside
+//     it strictly worse than its best so far: below it every element above
+//     fl32(Q s) saturates (sat_lower_bound), above it every element
+//     a <= v1 s stays at code 0 or v1 (small_lower_bound; v1 the smallest
+//     positive element).  Both bounds hold for the objective as the kernel
+//     computes it, so the chosen code is the one the full scan picks.  For
+//     E4M3 elements v1 = 2^-9 makes the upper bound void: their error is
+//     nearly scale invariant and the scan runs to the zero tail.
 #pragma once
 #include "encode.hpp"
 #include "kernels.hpp"
@@ -239,168 +242,6 @@ __global__ __launch_bounds__(256) void search_kernel(const T *__restrict__ W, in
     }
 }
 
-// E2M1 / E4M3 elements: the candidate's quantise-dequantise is two gfx950
-// conversions per pair of weights.  With s = m * p2 (m one of the eight E4M3
-// mantissas, p2 a power of two; m = 1 for E8M0), fl32(a / s) = fl32(a / m) / p2
-// (exact scaling), so fl32(a / m) is computed once per mantissa and the
-// candidates are walked grouped by mantissa: per weight and candidate that
-// leaves one conversion to codes, one back to grid values (both per pair), the
-// residual a - s v as one FMA (s v is exact) and the float64 square-add.
-// Ties keep the lowest code (candidates are not visited in code order).
-template <int EK, int SK, typename T, int SEG, int LPB, bool WEIGHTED>
-__global__ __launch_bounds__(256) void search_hw_kernel(const T *__restrict__ W, int64_t N, int64_t K,
-                                                        const float *__restrict__ h, uint8_t *__restrict__ codes,
-                                                        uint8_t *__restrict__ scales, float *__restrict__ block_obj)
-{
-    constexpr int B = SEG * LPB;
-    constexpr int ROWS = 256 / LPB;
-    constexpr int C0 = cand_first(SK);
-    constexpr int NC = cand_last(SK) - C0 + 1;
-    constexpr bool ONE_STEP = sizeof(T) == 2;
-    __shared__ float4 cand[256];  // (s, p2, m, 1/m) in (mantissa, exponent) order
-    __shared__ int cidx[256];     // candidate index c - C0
-    __shared__ int cmant[256];    // mantissa group
-
-    const int tid = threadIdx.x;
-    if (tid < NC) {
-        int g = 0, rank = tid;  // E8M0: one mantissa, code order
-        if (SK != SCALE_E8M0) rank = e4m3_mantissa_rank(tid, &g);
-        const ScaleParts sp = scale_parts<SK>(scale_value(SK, C0 + tid));
-        cand[rank] = make_float4(sp.s, sp.p2, sp.m, sp.rm);
-        cidx[rank] = tid;
-        cmant[rank] = g;
-    }
-    __syncthreads();
-
-    const int64_t row = (int64_t)blockIdx.x * ROWS + tid / LPB;
-    const int seg = tid % LPB;
-    const int64_t col0 = (int64_t)blockIdx.y * B + (int64_t)seg * SEG;
-    const bool active = row < N;
-
-    float a[SEG];
-    uint32_t negmask = 0;
-    {
-        float w[8];
-#pragma unroll
-        for (int c8 = 0; c8 < SEG / 8; ++c8) {
-            if (active)
-                load8<T>(W + row * K + col0 + 8 * c8, w);
-            else
-                for (int j = 0; j < 8; ++j) w[j] = 0.0f;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                a[8 * c8 + j] = fabsf(w[j]);
-                negmask |= (uint32_t)(__builtin_signbitf(w[j]) != 0) << (8 * c8 + j);
-            }
-        }
-    }
-    double om[WEIGHTED ? SEG : 1];
-    if (WEIGHTED) {
-#pragma unroll
-        for (int j = 0; j < SEG; ++j) om[j] = (double)h[col0 + j];
-    }
-
-    // first candidate (in code order) that rounds the block's amax to zero
-    float amax = 0.0f;
-#pragma unroll
-    for (int j = 0; j < SEG; ++j) amax = fmaxf(amax, a[j]);
-    amax = group_max<LPB>(amax);
-    int lo = 0, hi = NC;
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        const float sm = scale_value(SK, C0 + mid);
-        if (round_elem<EK>(quotient<SK, ONE_STEP>(amax, sm, 1.0f / sm)) == 0.0f)
-            hi = mid;
-        else
-            lo = mid + 1;
-    }
-    const int cend = __builtin_amdgcn_readfirstlane(wave_max_int(lo < NC ? lo : NC - 1));
-
-    double best = __builtin_huge_val();
-    int best_c = 0;
-    float am[SEG];
-    auto eval_range = [&](int lo, int hi) {
-        int cur_m = -1;
-        for (int k = 0; k < NC; ++k) {
-            const int ci = cidx[k];
-            if (ci > hi || ci < lo) continue;  // uniform: every lane skips it
-            const float4 cd = cand[k];
-            const int mg = cmant[k];
-            if (mg != cur_m) {  // uniform
-                cur_m = mg;
-#pragma unroll
-                for (int j = 0; j < SEG; ++j)
-                    am[j] = SK == SCALE_E8M0 ? a[j] : quotient<SCALE_E4M3, ONE_STEP>(a[j], cd.z, cd.w);
-            }
-            const float lim = 448.0f * cd.y;
-            double acc0 = 0.0, acc1 = 0.0;
-#pragma unroll
-            for (int j0 = 0; j0 < SEG; j0 += 8) {
-                float x[8], v[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) x[j] = EK == ELEM_E4M3 ? fminf(am[j0 + j], lim) : am[j0 + j];
-                quant8_vals<EK>(x, cd.y, v);
-#pragma unroll
-                for (int j = 0; j < 8; j += 2) {
-                    const double d0 = (double)__builtin_fmaf(-v[j], cd.x, a[j0 + j]);
-                    const double d1 = (double)__builtin_fmaf(-v[j + 1], cd.x, a[j0 + j + 1]);
-                    if (WEIGHTED) {
-                        acc0 = __builtin_fma(om[j0 + j], d0 * d0, acc0);
-                        acc1 = __builtin_fma(om[j0 + j + 1], d1 * d1, acc1);
-                    } else {
-                        acc0 = __builtin_fma(d0, d0, acc0);
-                        acc1 = __builtin_fma(d1, d1, acc1);
-                    }
-                }
-            }
-            const double acc = group_sum<LPB>(acc0 + acc1);
-            if (acc < best || (acc == best && ci < best_c)) {
-                best = acc;
-                best_c = ci;
-            }
-        }
-    };
-    // start below the lowest Naive code of the wave (a binade for E4M3 grids,
-    // two powers of two for E8M0) and run up to the first all-zero code;
-    // extend downward only while some lane cannot prove the lower candidates
-    // worse.  (No upper bound here: E8M0 grids stop within a few codes of
-    // Naive anyway, and for the E2M1 / E4M3 element grids the bound passes,
-    // each re-dividing by every mantissa, cost more than the candidates they
-    // save.)
-    constexpr int MARGIN = SK == SCALE_E8M0 ? 2 : 8;
-    constexpr int STEP = SK == SCALE_E8M0 ? 4 : 16;
-    const int cn = naive_code<EK, SK>(amax) - C0;
-    int clo = cn - MARGIN, chi = cend;
-    clo = __builtin_amdgcn_readfirstlane(-wave_max_int(-(clo < 0 ? 0 : clo)));
-    if (clo > chi) clo = chi;
-    eval_range(clo, chi);
-    while (clo > 0) {
-        const double lb = sat_lower_bound<EK, SEG, LPB, WEIGHTED>(a, om, scale_value(SK, C0 + clo - 1));
-        if (wave_all(!active || lb * (1.0 - 0x1p-20) > best)) break;
-        const int nlo = clo > STEP ? clo - STEP : 0;
-        eval_range(nlo, clo - 1);
-        clo = nlo;
-    }
-
-    const float s = scale_value(SK, C0 + best_c);
-    if (!active) return;
-    const int64_t e0 = row * K + col0;
-#pragma unroll
-    for (int c8 = 0; c8 < SEG / 8; ++c8) {
-        float w[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) w[j] = ((negmask >> (8 * c8 + j)) & 1u) ? -a[8 * c8 + j] : a[8 * c8 + j];
-        uint32_t cdd[8];
-        encode8<EK, SK, ONE_STEP, false>(w, s, 1.0f / s, nullptr, cdd);
-        store_codes8<EK>(codes, e0 + 8 * c8, cdd);
-    }
-    if (seg == 0) {
-        const int64_t blk = row * (K / B) + blockIdx.y;
-        scales[blk] = (uint8_t)(C0 + best_c);
-        if (block_obj) block_obj[blk] = (float)best;
-    }
-}
-
 template <int EK, int SK, typename T, int SEG, int LPB>
 static hipError_t search_go(const void *W, int64_t N, int64_t K, const float *h, uint8_t *codes,
                             uint8_t *scales, float *bo, hipStream_t st)
@@ -410,27 +251,13 @@ static hipError_t search_go(const void *W, int64_t N, int64_t K, const float *h,
     const T *w = static_cast<const T *>(W);
     // (SEG, LPB) = (32, *) serves only the unweighted search, (16, > 1) only the weighted one
     constexpr bool MAY_W = SEG <= 16, MAY_U = !(SEG == 16 && LPB > 1);
-    // integer elements and the unsigned scale grids: the generic search kernel
-    // (exact arithmetic quantise-dequantise, per-lane windows); E2M1 / E4M3
-    // elements on E4M3 / E8M0 grids: the conversion-instruction kernel
-    if constexpr (elem_int(EK) || scale_unsigned(SK)) {
-        if constexpr (MAY_W) {
-            if (h) {
-                search_kernel<EK, SK, T, SEG, LPB, true><<<grid, 256, 0, st>>>(w, N, K, h, codes, scales, bo);
-                return hipGetLastError();
-            }
+    if constexpr (MAY_W) {
+        if (h) {
+            search_kernel<EK, SK, T, SEG, LPB, true><<<grid, 256, 0, st>>>(w, N, K, h, codes, scales, bo);
+            return hipGetLastError();
         }
-        if constexpr (MAY_U) search_kernel<EK, SK, T, SEG, LPB, false><<<grid, 256, 0, st>>>(w, N, K, h, codes, scales, bo);
-    } else {
-        if constexpr (MAY_W) {
-            if (h) {
-                search_hw_kernel<EK, SK, T, SEG, LPB, true><<<grid, 256, 0, st>>>(w, N, K, h, codes, scales, bo);
-                return hipGetLastError();
-            }
-        }
-        if constexpr (MAY_U)
-            search_hw_kernel<EK, SK, T, SEG, LPB, false><<<grid, 256, 0, st>>>(w, N, K, h, codes, scales, bo);
     }
+    if constexpr (MAY_U) search_kernel<EK, SK, T, SEG, LPB, false><<<grid, 256, 0, st>>>(w, N, K, h, codes, scales, bo);
     return hipGetLastError();
 }
 
