@@ -19,12 +19,15 @@ _LIB_PATH = os.path.join(HERE, "liboracle.so")
 NAIVE, SSE_OPT, H_OPT, NAIVE_OCP = 0, 1, 2, 3
 INT8_E4M3, NVFP4, MXFP4, MXFP8, FP8_E4M3S = 0, 1, 2, 3, 4
 NVFP4_UE4M4, NVFP4_UE5M3, NVINT4 = 5, 6, 7
-FOUR_BIT = (NVFP4, MXFP4, NVFP4_UE4M4, NVFP4_UE5M3, NVINT4)
+FP4_F16, INT4_F16 = 8, 9
+FOUR_BIT = (NVFP4, MXFP4, NVFP4_UE4M4, NVFP4_UE5M3, NVINT4, FP4_F16, INT4_F16)
+F16_SCALES = (FP4_F16, INT4_F16)
 F32, BF16 = 0, 1
 
 FORMAT_NAMES = {INT8_E4M3: "INT8_E4M3", NVFP4: "NVFP4", MXFP4: "MXFP4",
                 MXFP8: "MXFP8", FP8_E4M3S: "FP8_E4M3S", NVFP4_UE4M4: "NVFP4_UE4M4",
-                NVFP4_UE5M3: "NVFP4_UE5M3", NVINT4: "NVINT4"}
+                NVFP4_UE5M3: "NVFP4_UE5M3", NVINT4: "NVINT4", FP4_F16: "FP4_F16",
+                INT4_F16: "INT4_F16"}
 
 _lib = None
 
@@ -48,6 +51,7 @@ def lib():
         L.orc_scale_value.restype = ctypes.c_float
         L.orc_naive_scale_code.argtypes = [i32, ctypes.c_float]
         L.orc_naive_ocp_code.argtypes = [i32, ctypes.c_float]
+        L.orc_f16_code.argtypes = [dbl]
         L.orc_block_all_objectives.argtypes = [i32, i32, P, P, P, P]
         L.orc_quantize.argtypes = [i32, i32, i32, P, i32, i64, i64, P, P, P, P, P, i32]
         L.orc_dequantize.argtypes = [i32, i32, P, P, i64, i64, P, i32]
@@ -127,6 +131,17 @@ def naive_ocp_code(fmt, amax):
     return int(lib().orc_naive_ocp_code(fmt, float(np.float32(amax))))
 
 
+def f16_code(v):
+    """Binary16 bit pattern of v >= 0 by the oracle's table rounding (RNE,
+    saturating at 65504)."""
+    return int(lib().orc_f16_code(float(v)))
+
+
+def scale_dtype(fmt):
+    """Scale codes are one byte, or binary16 bits (uint16) for FP16 scales."""
+    return np.uint16 if fmt in F16_SCALES else np.uint8
+
+
 def block_all_objectives(fmt, w, h=None):
     """(codes, objectives) of one block over every candidate scale."""
     w = np.ascontiguousarray(w, np.float32)
@@ -144,14 +159,15 @@ def codes_shape(fmt, N, K):
 
 
 def quantize(method, fmt, B, W, h=None, scales_in=None, nthreads=0):
-    """Returns (codes uint8, scales uint8 [N, K/B], block objective float64 [N, K/B])."""
+    """Returns (codes uint8, scales [N, K/B] (uint8, or uint16 for FP16 scales),
+    block objective float64 [N, K/B])."""
     W = np.ascontiguousarray(W)
     N, K = W.shape
     codes = np.zeros(codes_shape(fmt, N, K), np.uint8)
-    scales = np.zeros((N, K // B), np.uint8)
+    scales = np.zeros((N, K // B), scale_dtype(fmt))
     obj = np.zeros((N, K // B), np.float64)
     hh = None if h is None else np.ascontiguousarray(h, np.float32)
-    si = None if scales_in is None else np.ascontiguousarray(scales_in, np.uint8)
+    si = None if scales_in is None else np.ascontiguousarray(scales_in, scale_dtype(fmt))
     rc = lib().orc_quantize(method, fmt, B, _ptr(W), _dt(W), N, K, _ptr(hh), _ptr(si),
                             _ptr(codes), _ptr(scales), _ptr(obj), nthreads)
     _check(rc, "quantize")
@@ -164,7 +180,7 @@ def objectives_at(fmt, B, W, scales_in, h=None, nthreads=0):
     N, K = W.shape
     obj = np.zeros((N, K // B), np.float64)
     hh = None if h is None else np.ascontiguousarray(h, np.float32)
-    si = np.ascontiguousarray(scales_in, np.uint8)
+    si = np.ascontiguousarray(scales_in, scale_dtype(fmt))
     rc = lib().orc_objectives_at(fmt, B, _ptr(W), _dt(W), N, K, _ptr(hh), _ptr(si), _ptr(obj), nthreads)
     _check(rc, "objectives_at")
     return obj
@@ -172,7 +188,7 @@ def objectives_at(fmt, B, W, scales_in, h=None, nthreads=0):
 
 def dequantize(fmt, B, codes, scales, N, K, nthreads=0):
     codes = np.ascontiguousarray(codes, np.uint8)
-    scales = np.ascontiguousarray(scales, np.uint8)
+    scales = np.ascontiguousarray(scales, scale_dtype(fmt))
     out = np.zeros((N, K), np.float32)
     rc = lib().orc_dequantize(fmt, B, _ptr(codes), _ptr(scales), N, K, _ptr(out), nthreads)
     _check(rc, "dequantize")

@@ -37,6 +37,12 @@
  *     power-of-two scales, 2^(floor(log2 amax) - emax_elem) (the OCP
  *     microscaling specification the same section cites), as an alternative
  *     Naive for MXFP4 / MXFP8.
+ *   - FP16 scales (qwantize "Results", "Larger blocks: bs=64 (E4M3 scales) and
+ *     bs=128 (FP16 scales)"): FP4 (E2M1) or INT4 elements with a binary16
+ *     (E5M10, bias 15, top exponent reserved) block scale; Naive is
+ *     fp16(fl32(amax / C)); SSE-Optimal / H-Optimal are found by alternating
+ *     element assignment and the closed-form least-squares scale snapped to
+ *     FP16 (f16_alternation below; its readings are listed there).
  *
  * Readings where the pages are silent (also listed in the design notes):
  *   E8M0 Naive snap = nearest power of two in the linear domain, ties upward
@@ -62,14 +68,18 @@
 
 /* format ids (same numbering as the public library, kept independently) */
 enum { F_INT8_E4M3 = 0, F_NVFP4 = 1, F_MXFP4 = 2, F_MXFP8 = 3, F_FP8_E4M3S = 4,
-       F_NVFP4_UE4M4 = 5, F_NVFP4_UE5M3 = 6, F_NVINT4 = 7, F_COUNT = 8 };
+       F_NVFP4_UE4M4 = 5, F_NVFP4_UE5M3 = 6, F_NVINT4 = 7, F_FP4_F16 = 8, F_INT4_F16 = 9,
+       F_COUNT = 10 };
 enum { M_NAIVE = 0, M_SSE = 1, M_H = 2, M_NAIVE_OCP = 3 };
 enum { DT_F32 = 0, DT_BF16 = 1 };
 
 /* element kinds */
 enum { E_INT8 = 0, E_E2M1 = 1, E_E4M3 = 2, E_INT4 = 3 };
 /* scale kinds */
-enum { S_E4M3_OF_AMAX_DIV127 = 0, S_E4M3 = 1, S_E8M0 = 2, S_UE4M4 = 3, S_UE5M3 = 4 };
+enum { S_E4M3_OF_AMAX_DIV127 = 0, S_E4M3 = 1, S_E8M0 = 2, S_UE4M4 = 3, S_UE5M3 = 4, S_F16 = 5 };
+
+/* rounds of the FP16-scale alternation before it stops without a fixed point */
+#define F16_ALT_MAX_ROUNDS 32
 
 /* ------------------------------------------------------------------------ */
 /* Number formats                                                            */
@@ -116,6 +126,7 @@ static double T_INT8[128];
 static double T_INT4[8];
 static double T_UE4M4[256];
 static double T_UE5M3[256];
+static double T_F16[31744];
 static int tables_ready = 0;
 
 static void init_tables(void)
@@ -126,6 +137,7 @@ static void init_tables(void)
     orc_fp_table(4, 3, 7, 1, T_E4M3, 127);    /* 0 .. 448, 0x7F is NaN */
     orc_fp_table(4, 4, 7, 0, T_UE4M4, 256);   /* unsigned, every code finite: 0 .. 496 */
     orc_fp_table(5, 3, 15, 0, T_UE5M3, 256);  /* unsigned, every code finite: 0 .. 122880 */
+    orc_fp_table(5, 10, 15, 2, T_F16, 31744); /* FP16 E5M10, top exponent Inf/NaN: 0 .. 65504 */
     for (int i = 0; i < 128; i++)
         T_INT8[i] = (double)i;                /* symmetric INT8 magnitudes */
     for (int i = 0; i < 8; i++)
@@ -166,8 +178,8 @@ static int elem_kind(int fmt)
 {
     switch (fmt) {
     case F_INT8_E4M3: return E_INT8;
-    case F_NVFP4: case F_MXFP4: case F_NVFP4_UE4M4: case F_NVFP4_UE5M3: return E_E2M1;
-    case F_NVINT4: return E_INT4;
+    case F_NVFP4: case F_MXFP4: case F_NVFP4_UE4M4: case F_NVFP4_UE5M3: case F_FP4_F16: return E_E2M1;
+    case F_NVINT4: case F_INT4_F16: return E_INT4;
     default: return E_E4M3;
     }
 }
@@ -179,7 +191,28 @@ static int scale_kind(int fmt)
     case F_NVFP4: case F_FP8_E4M3S: case F_NVINT4: return S_E4M3;
     case F_NVFP4_UE4M4: return S_UE4M4;
     case F_NVFP4_UE5M3: return S_UE5M3;
+    case F_FP4_F16: case F_INT4_F16: return S_F16;
     default: return S_E8M0;
+    }
+}
+
+/* bytes per stored scale: 2 for FP16 scales (little-endian binary16 bits), else 1 */
+static int scale_bytes(int fmt) { return scale_kind(fmt) == S_F16 ? 2 : 1; }
+
+static int get_scale(int fmt, const uint8_t *scales, int64_t i)
+{
+    if (scale_bytes(fmt) == 2)
+        return scales[2 * i] | (scales[2 * i + 1] << 8);
+    return scales[i];
+}
+
+static void put_scale(int fmt, uint8_t *scales, int64_t i, int code)
+{
+    if (scale_bytes(fmt) == 2) {
+        scales[2 * i] = (uint8_t)(code & 0xFF);
+        scales[2 * i + 1] = (uint8_t)(code >> 8);
+    } else {
+        scales[i] = (uint8_t)code;
     }
 }
 
@@ -220,6 +253,9 @@ int orc_candidates(int fmt, int *first, int *last)
     } else if (scale_kind(fmt) == S_UE4M4 || scale_kind(fmt) == S_UE5M3) {
         *first = 1;
         *last = 255;
+    } else if (scale_kind(fmt) == S_F16) {
+        *first = 1;
+        *last = 0x7BFF; /* every positive finite binary16 value */
     } else {
         *first = 1;
         *last = 126;
@@ -246,6 +282,9 @@ float orc_scale_value(int fmt, int code)
     case S_UE5M3:
         if (code < 0 || code > 255) return NAN;
         return (float)T_UE5M3[code];
+    case S_F16:
+        if (code < 0 || code > 0x7BFF) return NAN; /* Inf, NaN and negative scales are invalid */
+        return (float)T_F16[code];
     default:
         if (code < 0 || code > 254) return NAN;
         return (float)ldexp(1.0, code - 127);
@@ -267,6 +306,8 @@ int orc_naive_scale_code(int fmt, float amax)
         return orc_rne_index(T_UE4M4, 256, (double)v);
     if (sk == S_UE5M3)
         return orc_rne_index(T_UE5M3, 256, (double)v);
+    if (sk == S_F16)
+        return orc_rne_index(T_F16, 31744, (double)v); /* RNE, saturating at 65504 */
     /* E8M0: nearest power of two in the linear domain, ties upward */
     if (v == 0.0f)
         return 0;
@@ -367,6 +408,60 @@ static double block_objective(int fmt, float s, const float *w, const double *om
     return obj;
 }
 
+/* Binary16 code of v >= 0: round to nearest, ties to the even code,
+ * saturating at 65504 (the FP16 scale snap). */
+int orc_f16_code(double v)
+{
+    init_tables();
+    return orc_rne_index(T_F16, 31744, v);
+}
+
+/* FP16-scale alternation (qwantize "Results", "Larger blocks: bs=64 (E4M3
+ * scales) and bs=128 (FP16 scales)").  For a fixed element assignment q the
+ * objective sum_j om_j (w_j - s q_j)^2 is a quadratic in s with its minimum at
+ * s* = sum_j om_j w_j q_j / sum_j om_j q_j^2 (least squares); the page
+ * alternates between q (encode at the current scale) and s (s* snapped to
+ * FP16).  Readings: the walk starts at the Naive scale; it stops at a fixed
+ * point (the snapped s* is the current scale), when every om_j q_j^2 is 0 (s*
+ * undefined), at the zero scale, or after F16_ALT_MAX_ROUNDS rounds; the scale
+ * returned is the iterate with the smallest objective, the earliest on ties,
+ * so the result is never worse than Naive.  Sums in float64, j ascending; each
+ * product om_j * w_j * q_j is exact in float64 (24 + 24 + 3 bits). */
+static int f16_alternation(int fmt, const float *w, const double *om, int B, float amax, double *best_out)
+{
+    int n_t;
+    const double *T = elem_table(fmt, &n_t);
+    int code = orc_naive_scale_code(fmt, amax);
+    int best_code = code;
+    double best = block_objective(fmt, (float)T_F16[code], w, om, B);
+    for (int round = 0; round < F16_ALT_MAX_ROUNDS && code != 0; round++) {
+        float s = (float)T_F16[code];
+        double num = 0.0, den = 0.0;
+        for (int j = 0; j < B; j++) {
+            float wq;
+            int neg = 0;
+            int idx = dec_elem(fmt, enc_elem(fmt, s, w[j], &wq), &neg);
+            double q = neg ? -T[idx] : T[idx];
+            double o = om ? om[j] : 1.0;
+            num += o * (double)w[j] * q;
+            den += o * q * q;
+        }
+        if (den == 0.0)
+            break;
+        int next = orc_rne_index(T_F16, 31744, num / den);
+        if (next == code)
+            break;
+        code = next;
+        double obj = block_objective(fmt, (float)T_F16[code], w, om, B);
+        if (obj < best) {
+            best = obj;
+            best_code = code;
+        }
+    }
+    *best_out = best;
+    return best_code;
+}
+
 static float widen(const void *p, int dt, int64_t i)
 {
     if (dt == DT_F32)
@@ -444,11 +539,14 @@ static int get_code(int fmt, const uint8_t *codes, int64_t K, int64_t n, int64_t
     return codes[n * K + k];
 }
 
-/* quantize_blocks.  method: Naive / SSE-Optimal / H-Optimal.  scales_in, when
+/* quantize_blocks.  method: Naive / SSE-Optimal / H-Optimal (the exact argmin
+ * over the scale grid; for FP16 scales the alternation above).  scales_in, when
  * not NULL, fixes every block's scale code (encode only: method is ignored).
  * h is required for H-Optimal; for Naive and for a fixed scale it only weights
  * the reported objective.  codes: [N][K] bytes (INT8, E4M3) or [N][K/2]
- * (E2M1, INT4: element 2k in the low nibble); scales: [N][K/B]; block_obj: [N][K/B] float64 or NULL. */
+ * (E2M1, INT4: element 2k in the low nibble); scales: [N][K/B] codes, one byte
+ * each, or two (little-endian binary16 bits) for FP16 scales; block_obj:
+ * [N][K/B] float64 or NULL. */
 int orc_quantize(int method, int fmt, int B, const void *W, int wdt, int64_t N, int64_t K,
                  const float *h, const uint8_t *scales_in, uint8_t *codes, uint8_t *scales,
                  double *block_obj, int nthreads)
@@ -497,7 +595,7 @@ int orc_quantize(int method, int fmt, int B, const void *W, int wdt, int64_t N, 
                 int code;
                 double best;
                 if (scales_in) {
-                    code = scales_in[n * nb + b];
+                    code = get_scale(fmt, scales_in, n * nb + b);
                     float s = orc_scale_value(fmt, code);
                     if (isnan(s)) {
 #pragma omp atomic write
@@ -508,6 +606,8 @@ int orc_quantize(int method, int fmt, int B, const void *W, int wdt, int64_t N, 
                 } else if (method == M_NAIVE || method == M_NAIVE_OCP) {
                     code = method == M_NAIVE ? orc_naive_scale_code(fmt, amax) : orc_naive_ocp_code(fmt, amax);
                     best = block_objective(fmt, orc_scale_value(fmt, code), w, om, B);
+                } else if (scale_kind(fmt) == S_F16) {
+                    code = f16_alternation(fmt, w, om, B, amax, &best);
                 } else {
                     code = c0;
                     best = block_objective(fmt, orc_scale_value(fmt, c0), w, om, B);
@@ -520,7 +620,7 @@ int orc_quantize(int method, int fmt, int B, const void *W, int wdt, int64_t N, 
                     }
                 }
                 float s = orc_scale_value(fmt, code);
-                if (scales) scales[n * nb + b] = (uint8_t)code;
+                if (scales) put_scale(fmt, scales, n * nb + b, code);
                 if (block_obj) block_obj[n * nb + b] = best;
                 if (codes) {
                     for (int j = 0; j < B; j++) {
@@ -552,7 +652,7 @@ int orc_dequantize(int fmt, int B, const uint8_t *codes, const uint8_t *scales, 
 #pragma omp parallel for num_threads(nt) schedule(static)
     for (int64_t n = 0; n < N; n++) {
         for (int64_t k = 0; k < K; k++) {
-            float s = orc_scale_value(fmt, scales[n * nb + k / B]);
+            float s = orc_scale_value(fmt, get_scale(fmt, scales, n * nb + k / B));
             int neg = 0;
             int idx = dec_elem(fmt, get_code(fmt, codes, K, n, k), &neg);
             if (isnan(s) || idx < 0) {
