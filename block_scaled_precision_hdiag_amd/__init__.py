@@ -25,10 +25,14 @@ HD_F32, HD_BF16 = 0, 1
 NAIVE, SSE_OPT, H_OPT, NAIVE_OCP = 0, 1, 2, 3
 INT8_E4M3, NVFP4, MXFP4, MXFP8, FP8_E4M3S = 0, 1, 2, 3, 4
 NVFP4_UE4M4, NVFP4_UE5M3, NVINT4 = 5, 6, 7
+FP4_F16, INT4_F16 = 8, 9
 FORMATS = {"INT8_E4M3": INT8_E4M3, "NVFP4": NVFP4, "MXFP4": MXFP4, "MXFP8": MXFP8, "FP8_E4M3S": FP8_E4M3S,
-           "NVFP4_UE4M4": NVFP4_UE4M4, "NVFP4_UE5M3": NVFP4_UE5M3, "NVINT4": NVINT4}
+           "NVFP4_UE4M4": NVFP4_UE4M4, "NVFP4_UE5M3": NVFP4_UE5M3, "NVINT4": NVINT4, "FP4_F16": FP4_F16,
+           "INT4_F16": INT4_F16}
 METHODS = {"naive": NAIVE, "sse": SSE_OPT, "h": H_OPT, "naive_ocp": NAIVE_OCP}
-FOUR_BIT = (NVFP4, MXFP4, NVFP4_UE4M4, NVFP4_UE5M3, NVINT4)
+FOUR_BIT = (NVFP4, MXFP4, NVFP4_UE4M4, NVFP4_UE5M3, NVINT4, FP4_F16, INT4_F16)
+# formats whose block scales are binary16 values (stored as torch.float16)
+F16_SCALES = (FP4_F16, INT4_F16)
 
 EXPORTS = ["hdiag", "hdiag_workspace_size", "quantize_blocks", "encode_blocks", "dequantize",
            "weight_error", "weight_error_workspace_size", "output_error", "output_error_workspace_size",
@@ -126,6 +130,12 @@ def codes_shape(fmt, N, K):
     return (N, K // 2) if fmt in FOUR_BIT else (N, K)
 
 
+def scale_dtype(fmt):
+    """torch dtype of a scale tensor: float16 (the binary16 scale itself) for
+    the FP16-scale formats, uint8 codes otherwise."""
+    return torch.float16 if fmt in F16_SCALES else torch.uint8
+
+
 def hdiag_workspace_size(M, K):
     return int(lib().hdiag_workspace_size(M, K))
 
@@ -142,11 +152,12 @@ def hdiag(X, out=None, workspace=None):
 
 
 def quantize_blocks(method, fmt, B, W, h=None, block_obj=False, codes=None, scales=None):
-    """Scale choice + encode.  Returns (codes uint8, scales uint8 [N, K/B], block_obj or None)."""
+    """Scale choice + encode.  Returns (codes uint8, scales [N, K/B] (uint8 codes,
+    or float16 for FP16 scales), block_obj or None)."""
     d = _dev(W)
     N, K = W.shape
     codes = codes if codes is not None else torch.empty(codes_shape(fmt, N, K), dtype=torch.uint8, device=d)
-    scales = scales if scales is not None else torch.empty((N, K // B if B else 0), dtype=torch.uint8, device=d)
+    scales = scales if scales is not None else torch.empty((N, K // B if B else 0), dtype=scale_dtype(fmt), device=d)
     obj = torch.empty((N, K // B if B else 0), dtype=torch.float32, device=d) if block_obj else None
     _check(lib().quantize_blocks(method, fmt, B, _ptr(W), _dt(W), N, K, _ptr(h), _ptr(codes), _ptr(scales),
                                  _ptr(obj), _stream(d)), "quantize_blocks")

@@ -36,13 +36,15 @@ hd_status hip_status(hipError_t e, const char *what)
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 bool valid_dtype(int d) { return d == HD_F32 || d == HD_BF16; }
-bool valid_fmt(int f) { return f >= HD_INT8_E4M3 && f <= HD_NVINT4; }
+bool valid_fmt(int f) { return f >= HD_INT8_E4M3 && f <= HD_INT4_F16; }
 bool valid_block(int32_t B) { return B == 8 || B == 16 || B == 32 || B == 64 || B == 128 || B == 256; }
 bool is_4bit(int f)
 {
-    return f == HD_NVFP4 || f == HD_MXFP4 || f == HD_NVFP4_UE4M4 || f == HD_NVFP4_UE5M3 || f == HD_NVINT4;
+    return f == HD_NVFP4 || f == HD_MXFP4 || f == HD_NVFP4_UE4M4 || f == HD_NVFP4_UE5M3 || f == HD_NVINT4 ||
+           f == HD_FP4_F16 || f == HD_INT4_F16;
 }
 bool is_e8m0(int f) { return f == HD_MXFP4 || f == HD_MXFP8; }
+bool is_f16(int f) { return f == HD_FP4_F16 || f == HD_INT4_F16; }
 
 #define HD_REQUIRE(cond, ...) \
     do {                      \
@@ -99,8 +101,8 @@ hd_status hdiag_format_info(hd_format fmt, int32_t B, int *elem_bits, int *scale
     HD_REQUIRE(valid_fmt(fmt), "unknown format %d", (int)fmt);
     HD_REQUIRE(B > 0, "block size must be positive");
     const int eb = is_4bit(fmt) ? 4 : 8;
-    const int sb = 8;
-    const int nc = (is_e8m0(fmt) || fmt == HD_NVFP4_UE4M4 || fmt == HD_NVFP4_UE5M3) ? 255 : 126;
+    const int sb = is_f16(fmt) ? 16 : 8;
+    const int nc = is_f16(fmt) ? 0x7BFF : (is_e8m0(fmt) || fmt == HD_NVFP4_UE4M4 || fmt == HD_NVFP4_UE5M3) ? 255 : 126;
     if (elem_bits) *elem_bits = eb;
     if (scale_bits) *scale_bits = sb;
     if (n_candidates) *n_candidates = nc;
@@ -151,6 +153,9 @@ hd_status quantize_blocks(hd_method method, hd_format fmt, int32_t B, const void
                                             method == HD_NAIVE_OCP, st),
                           "quantize_blocks(naive)");
     const float *hh = method == HD_H_OPT ? h : nullptr;
+    if (is_f16(fmt))
+        return hip_status(hd::launch_alt_f16(fmt, B, W, wt, N, K, hh, codes, scales, block_obj, st),
+                          "quantize_blocks(alternation)");
     return hip_status(hd::launch_search(fmt, B, W, wt, N, K, hh, codes, scales, block_obj, st),
                       "quantize_blocks(search)");
 }
@@ -165,6 +170,7 @@ hd_status encode_blocks(hd_format fmt, int32_t B, const void *W, hd_dtype wt, in
     HD_CHECK_PTR(W, true);
     HD_CHECK_PTR(codes, true);
     if (scales_in == nullptr) return fail(HD_ERR_INVALID_ARG, "scales_in is NULL");
+    if (is_f16(fmt) && ((uintptr_t)scales_in & 1u)) return fail(HD_ERR_INVALID_ARG, "scales_in is not 2-byte aligned");
     if (h != nullptr && !aligned16(h)) return fail(HD_ERR_INVALID_ARG, "h is not 16-byte aligned");
     if (block_obj != nullptr && ((uintptr_t)block_obj & 3u)) return fail(HD_ERR_INVALID_ARG, "block_obj misaligned");
     return hip_status(hd::launch_encode(fmt, B, W, wt, N, K, h, scales_in, codes, nullptr, block_obj, 0,
@@ -182,6 +188,7 @@ hd_status dequantize(hd_format fmt, int32_t B, const uint8_t *codes, const uint8
     HD_CHECK_PTR(codes, true);
     HD_CHECK_PTR(Wq, true);
     if (scales == nullptr) return fail(HD_ERR_INVALID_ARG, "scales is NULL");
+    if (is_f16(fmt) && ((uintptr_t)scales & 1u)) return fail(HD_ERR_INVALID_ARG, "scales is not 2-byte aligned");
     return hip_status(hd::launch_dequant(fmt, B, codes, scales, N, K, Wq, out_t, (hipStream_t)stream),
                       "dequantize");
 }
@@ -286,6 +293,9 @@ hd_status output_error_codes(hd_format fmt, int32_t B, const void *X, hd_dtype x
     HD_REQUIRE(M >= 0, "negative size");
     HD_REQUIRE(M <= (int64_t)1 << 31 && N <= (int64_t)1 << 31 && K <= (int64_t)1 << 31, "size too large");
     if (xt != HD_BF16) return fail(HD_ERR_UNSUPPORTED, "output_error_codes needs bfloat16 X");
+    if (is_f16(fmt))
+        return fail(HD_ERR_UNSUPPORTED, "output_error_codes: FP16 block scales do not give an exact 16-bit operand "
+                                        "(use dequantize + output_error)");
     HD_REQUIRE(out != nullptr, "out is NULL");
     HD_CHECK_PTR(ref, true);
     HD_REQUIRE(ref_bytes >= (size_t)hd::output_reference_layout(M, N, K).bytes, "reference buffer too small");

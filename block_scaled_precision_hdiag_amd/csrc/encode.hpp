@@ -37,7 +37,9 @@ __device__ __forceinline__ double encode8(const float *w, float s, float r, cons
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const float a = fabsf(w[j]);
-        float v = (s == 0.0f) ? 0.0f : (SK == SCALE_E8M0 ? a : quotient<SCALE_E4M3, ONE_STEP>(a, sp.m, sp.rm));
+        // (an FP16 scale's mantissa m is one of 1024: both quotient corrections)
+        float v = (s == 0.0f) ? 0.0f
+                              : (SK == SCALE_E8M0 ? a : quotient<SCALE_E4M3, ONE_STEP && SK != SCALE_F16>(a, sp.m, sp.rm));
         if (EK == ELEM_E4M3) v = fminf(v, 448.0f * sp.p2);
         x[j] = v;
     }
@@ -57,6 +59,22 @@ __device__ __forceinline__ double encode8(const float *w, float s, float r, cons
         }
     }
     return obj;
+}
+
+// Scale code of block `blk`: a byte, or binary16 bits for FP16 scales.
+template <int SK>
+__device__ __forceinline__ int load_scale(const uint8_t *scales, int64_t blk)
+{
+    if (SK == SCALE_F16) return (int)reinterpret_cast<const uint16_t *>(scales)[blk];
+    return (int)scales[blk];
+}
+template <int SK>
+__device__ __forceinline__ void store_scale(uint8_t *scales, int64_t blk, int code)
+{
+    if (SK == SCALE_F16)
+        reinterpret_cast<uint16_t *>(scales)[blk] = (uint16_t)code;
+    else
+        scales[blk] = (uint8_t)code;
 }
 
 // Store the 8 codes of elements e0..e0+7 (e0 % 8 == 0).

@@ -8,8 +8,10 @@
 // 0x01..0x7E; INT8's fl32(E4M3 / 127) (qwantize "Results", INT8 section); E8M0
 // 2^(c-127), c = 0..254 ("Is Finer Better?" §2.1); the unsigned UE4M4 (bias 7)
 // and UE5M3 (bias 15) grids of the "Exotic Scales" section, every code finite
-// (0x01..0xFF positive).  Values follow the EeMm formula of the LLM-FP4 summary page
-// ("Floating-Point Quantization Mechanics").
+// (0x01..0xFF positive); binary16 (FP16 E5M10, 0x0000..0x7BFF) block scales
+// found by alternation (qwantize "Results", "Larger blocks: bs=64 (E4M3 scales)
+// and bs=128 (FP16 scales)").  Values follow the EeMm formula of the LLM-FP4
+// summary page ("Floating-Point Quantization Mechanics").
 //
 // Rounding: q = RNE(fl32(|w| / s)) onto the element grid, ties to the even
 // code, saturating.  Every helper here is exact in IEEE binary32 with
@@ -26,14 +28,16 @@
 namespace hd {
 
 enum ElemKind { ELEM_INT8 = 0, ELEM_E2M1 = 1, ELEM_E4M3 = 2, ELEM_INT4 = 3 };
-enum ScaleKind { SCALE_INT8 = 0, SCALE_E4M3 = 1, SCALE_E8M0 = 2, SCALE_UE4M4 = 3, SCALE_UE5M3 = 4 };
+enum ScaleKind { SCALE_INT8 = 0, SCALE_E4M3 = 1, SCALE_E8M0 = 2, SCALE_UE4M4 = 3, SCALE_UE5M3 = 4, SCALE_F16 = 5 };
 
 __host__ __device__ constexpr int elem_kind(int fmt)
 {
     return fmt == HD_INT8_E4M3 ? ELEM_INT8
-         : fmt == HD_NVINT4 ? ELEM_INT4
-         : (fmt == HD_NVFP4 || fmt == HD_MXFP4 || fmt == HD_NVFP4_UE4M4 || fmt == HD_NVFP4_UE5M3) ? ELEM_E2M1
-                                                                                                  : ELEM_E4M3;
+         : (fmt == HD_NVINT4 || fmt == HD_INT4_F16) ? ELEM_INT4
+         : (fmt == HD_NVFP4 || fmt == HD_MXFP4 || fmt == HD_NVFP4_UE4M4 || fmt == HD_NVFP4_UE5M3 ||
+            fmt == HD_FP4_F16)
+             ? ELEM_E2M1
+             : ELEM_E4M3;
 }
 __host__ __device__ constexpr int scale_kind(int fmt)
 {
@@ -41,8 +45,11 @@ __host__ __device__ constexpr int scale_kind(int fmt)
          : (fmt == HD_NVFP4 || fmt == HD_FP8_E4M3S || fmt == HD_NVINT4) ? SCALE_E4M3
          : fmt == HD_NVFP4_UE4M4 ? SCALE_UE4M4
          : fmt == HD_NVFP4_UE5M3 ? SCALE_UE5M3
+         : (fmt == HD_FP4_F16 || fmt == HD_INT4_F16) ? SCALE_F16
                                  : SCALE_E8M0;
 }
+// Bytes of one stored scale code: binary16 bits for FP16 scales, else a byte.
+__host__ __device__ constexpr int scale_bytes(int sk) { return sk == SCALE_F16 ? 2 : 1; }
 // Integer element grids (exact arithmetic encode) and 4-bit element codes.
 __host__ __device__ constexpr bool elem_int(int ek) { return ek == ELEM_INT8 || ek == ELEM_INT4; }
 __host__ __device__ constexpr bool elem_4bit(int ek) { return ek == ELEM_E2M1 || ek == ELEM_INT4; }
@@ -52,18 +59,19 @@ __host__ __device__ constexpr bool scale_unsigned(int sk) { return sk == SCALE_U
 __host__ __device__ constexpr int cand_first(int sk) { return sk == SCALE_E8M0 ? 0 : 1; }
 __host__ __device__ constexpr int cand_last(int sk)
 {
-    return sk == SCALE_E8M0 ? 254 : scale_unsigned(sk) ? 255 : 126;
+    return sk == SCALE_E8M0 ? 254 : scale_unsigned(sk) ? 255 : sk == SCALE_F16 ? 0x7BFF : 126;
 }
-// Scale codes that stand for a number (the rest are NaN codes).
+// Scale codes that stand for a number (the rest are NaN / Inf codes, or
+// negative binary16 values).
 __host__ __device__ constexpr bool scale_code_valid(int sk, int c)
 {
-    return c >= 0 && c <= (sk == SCALE_E8M0 ? 254 : scale_unsigned(sk) ? 255 : 126);
+    return c >= 0 && c <= cand_last(sk);
 }
 // Scale codes per binade of the grid (8 for E4M3 / UE5M3 / INT8, 16 for
 // UE4M4, 1 for E8M0).
 __host__ __device__ constexpr int codes_per_binade(int sk)
 {
-    return sk == SCALE_E8M0 ? 1 : sk == SCALE_UE4M4 ? 16 : 8;
+    return sk == SCALE_E8M0 ? 1 : sk == SCALE_UE4M4 ? 16 : sk == SCALE_F16 ? 1024 : 8;
 }
 // Largest element magnitude (the C of s = Q_scale(amax / C)).
 __host__ __device__ constexpr float elem_max(int ek)
@@ -120,8 +128,10 @@ __host__ __device__ inline float ue_value(int c)
 }
 
 // The fp32 scale of scale code c on grid sk (c = 0 on an E4M3 grid is 0).
+// Binary16 is the UExMy formula with M = 10, bias 15 (codes up to 0x7BFF).
 __host__ __device__ inline float scale_value(int sk, int c)
 {
+    if (sk == SCALE_F16) return ue_value<10, 15>(c);
     if (sk == SCALE_E8M0) return e8m0_value(c);
     if (sk == SCALE_UE4M4) return ue_value<4, 7>(c);
     if (sk == SCALE_UE5M3) return ue_value<3, 15>(c);
@@ -139,6 +149,8 @@ __host__ __device__ inline float scale_value(int sk, int c)
 //    every candidate scale) by the encode parity test, which runs this code.
 //  - a is clamped to 2^100 first: any quotient that large saturates the
 //    element grid for every E4M3-grid scale, and the FMAs stay finite.
+//  - FP16 scales take both corrections whatever the input type (the one-step
+//    check covered only the scale grids above).
 template <int SK, bool ONE_STEP>
 __device__ __forceinline__ float quotient(float a, float s, float r)
 {
@@ -147,7 +159,7 @@ __device__ __forceinline__ float quotient(float a, float s, float r)
     float q = a * r;
     float e = __builtin_fmaf(-q, s, a);
     q = __builtin_fmaf(e, r, q);
-    if (!ONE_STEP) {
+    if (!ONE_STEP || SK == SCALE_F16) {
         e = __builtin_fmaf(-q, s, a);
         q = __builtin_fmaf(e, r, q);
     }
@@ -287,6 +299,23 @@ __device__ __forceinline__ int ue_round_code(float v)
     return y < bits_f((uint32_t)(127 + EMIN) << 23) ? sub : nrm;
 }
 
+// Binary16 code of v >= 0, rounded to nearest with ties to even and saturated
+// at 65504 (0x7BFF).  With e = max(floor(log2 v), -14) one unit in the last
+// place is 2^(e - 10), so m = rint(v / 2^(e - 10)) (exact scaling, then the
+// hardware's round-to-nearest-even) is the significand as an integer, 1024 ..
+// 2048 for normals and 0 .. 1024 below 2^-14, and the code is
+// (e + 14) * 1024 + m in both cases (m = 2048 carries into the next binade).
+__device__ __forceinline__ int f16_round_code(double v)
+{
+    if (!(v > 0x1p-25)) return 0;   // half the smallest subnormal ties to the even code 0
+    if (v >= 65520.0) return 0x7BFF;  // rounds beyond 65504 (to Inf in IEEE): saturate
+    int ex;
+    __builtin_frexp(v, &ex);  // v = f 2^ex, f in [0.5, 1): floor(log2 v) = ex - 1
+    const int e = max(ex - 1, -14);
+    const double m = __builtin_rint(__builtin_ldexp(v, 10 - e));
+    return (e + 14) * 1024 + (int)m;
+}
+
 // OCP MX rule for power-of-two scales: code of 2^(floor(log2 amax) - emax),
 // emax the exponent of the largest element (E2M1 6 = 1.5 2^2, E4M3 448 =
 // 1.75 2^8), clamped to E8M0's 2^[-127, 127]; amax = 0 gives code 0.
@@ -316,6 +345,7 @@ __device__ __forceinline__ int naive_code(float amax)
     }
     if (SK == SCALE_UE4M4) return ue_round_code<4, 7>(amax / elem_max(EK));
     if (SK == SCALE_UE5M3) return ue_round_code<3, 15>(amax / elem_max(EK));
+    if (SK == SCALE_F16) return f16_round_code((double)(amax / elem_max(EK)));  // fp16(fl32(amax / C))
     const float v = amax / elem_max(EK);
     if (v == 0.0f) return 0;
     // v = f 2^E with f in [1, 2); frexp gives the exponent for subnormals too

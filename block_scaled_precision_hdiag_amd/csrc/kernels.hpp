@@ -34,6 +34,11 @@ hipError_t launch_search_nvfp4_ue5m3(int B, const void *W, int wdt, int64_t N, i
 hipError_t launch_search_nvint4(int B, const void *W, int wdt, int64_t N, int64_t K, const float *h,
                                 uint8_t *codes, uint8_t *scales, float *block_obj, hipStream_t st);
 
+// SSE-Optimal (h == NULL) or H-Optimal binary16 block scales by alternation
+// (HD_FP4_F16, HD_INT4_F16) + encode.
+hipError_t launch_alt_f16(int fmt, int B, const void *W, int wdt, int64_t N, int64_t K, const float *h,
+                          uint8_t *codes, uint8_t *scales, float *block_obj, hipStream_t st);
+
 hipError_t launch_dequant(int fmt, int B, const uint8_t *codes, const uint8_t *scales, int64_t N, int64_t K,
                           void *out, int out_t, hipStream_t st);
 

@@ -72,7 +72,7 @@ __global__ __launch_bounds__(256) void encode_kernel(const T *__restrict__ W, in
         const int64_t blk = (e0 + bb * EB) / B;
         float s;
         if (GIVEN) {
-            code[bb] = (bb * EB < 8 * nv8) ? (int)scales_in[blk] : 0;
+            code[bb] = (bb * EB < 8 * nv8) ? load_scale<SK>(scales_in, blk) : 0;
             s = scale_code_valid(SK, code[bb]) ? scale_value(SK, code[bb]) : 0.0f;
         } else {
             // ocp (E8M0 grids only): the OCP MX floor rule instead of the snap
@@ -98,7 +98,7 @@ __global__ __launch_bounds__(256) void encode_kernel(const T *__restrict__ W, in
         for (int bb = 0; bb < NBT; ++bb) {
             if (bb * EB >= 8 * nv8) break;
             const int64_t blk = (e0 + bb * EB) / B;
-            if (!GIVEN) scales[blk] = (uint8_t)code[bb];
+            if (!GIVEN) store_scale<SK>(scales, blk, code[bb]);
             if (OBJ) block_obj[blk] = (float)obj[bb];
         }
         return;
@@ -125,7 +125,18 @@ __global__ __launch_bounds__(256) void encode_kernel(const T *__restrict__ W, in
     }
     if ((threadIdx.x % TPB) == 0) {
         const int64_t blk0 = e0 / B;
-        if (!GIVEN) {
+        if (!GIVEN && SK == SCALE_F16) {
+            // 2-byte codes
+            uint16_t *p = reinterpret_cast<uint16_t *>(scales) + blk0;
+            if (NBT == 4) {  // two 4-byte stores: the scales need only 4-byte alignment
+                uint32_t *q = reinterpret_cast<uint32_t *>(p);
+                q[0] = (uint32_t)code[0] | ((uint32_t)code[NBT > 1 ? 1 : 0] << 16);
+                q[1] = (uint32_t)code[NBT > 2 ? 2 : 0] | ((uint32_t)code[NBT > 3 ? 3 : 0] << 16);
+            } else if (NBT == 2)
+                *reinterpret_cast<uint32_t *>(p) = (uint32_t)code[0] | ((uint32_t)code[NBT > 1 ? 1 : 0] << 16);
+            else
+                *p = (uint16_t)code[0];
+        } else if (!GIVEN) {
             if (NBT == 4)
                 *reinterpret_cast<uint32_t *>(scales + blk0) =
                     (uint32_t)code[0] | ((uint32_t)code[NBT > 1 ? 1 : 0] << 8) |
@@ -198,6 +209,8 @@ hipError_t launch_encode(int fmt, int B, const void *W, int wdt, int64_t N, int6
         HD_ENC_FMT(HD_NVFP4_UE4M4)
         HD_ENC_FMT(HD_NVFP4_UE5M3)
         HD_ENC_FMT(HD_NVINT4)
+        HD_ENC_FMT(HD_FP4_F16)
+        HD_ENC_FMT(HD_INT4_F16)
     }
 #undef HD_ENC_FMT
     return hipErrorInvalidValue;
@@ -212,7 +225,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict_
 {
     const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
     if (e0 >= total) return;
-    const int sc = scales[e0 / B];
+    const int sc = load_scale<SK>(scales, e0 / B);
     const float s = scale_code_valid(SK, sc) ? scale_value(SK, sc) : 0.0f;
     uint32_t c[8];
     if (elem_4bit(EK)) {
@@ -295,6 +308,8 @@ hipError_t launch_dequant(int fmt, int B, const uint8_t *codes, const uint8_t *s
         HD_DEQ_FMT(HD_NVFP4_UE4M4)
         HD_DEQ_FMT(HD_NVFP4_UE5M3)
         HD_DEQ_FMT(HD_NVINT4)
+        HD_DEQ_FMT(HD_FP4_F16)
+        HD_DEQ_FMT(HD_INT4_F16)
     }
 #undef HD_DEQ_FMT
     return hipErrorInvalidValue;

@@ -60,7 +60,8 @@ typedef enum { HD_F32 = 0, HD_BF16 = 1 } hd_dtype;
  *                  E8M0's range; amax = 0 gives code 0 ("Is Finer Better?"
  *                  §2.1 cites the OCP specification that defines it).
  * The search methods evaluate every candidate of the grid and return the first
- * (lowest) scale code among equal minima. */
+ * (lowest) scale code among equal minima.  On the FP16 scale grids
+ * (HD_FP4_F16, HD_INT4_F16) they alternate instead (see hd_format). */
 typedef enum { HD_NAIVE = 0, HD_SSE_OPT = 1, HD_H_OPT = 2, HD_NAIVE_OCP = 3 } hd_method;
 
 /* Element format x scale grid.
@@ -83,6 +84,20 @@ typedef enum { HD_NAIVE = 0, HD_SSE_OPT = 1, HD_H_OPT = 2, HD_NAIVE_OCP = 3 } hd
  *                  s = Q_E4M3(amax / 7) (the NVINT4 rows of the qwantize
  *                  "Results" GPTQ tables, read with the generic rule of "Is
  *                  Finer Better?" §2.1).
+ *   HD_FP4_F16   - E2M1 elements with a binary16 (FP16 E5M10) block scale, and
+ *   HD_INT4_F16  - INT4 elements [-7, 7] with a binary16 block scale
+ *                  (qwantize "Results", "Larger blocks: bs=64 (E4M3 scales) and
+ *                  bs=128 (FP16 scales)").  Scales are stored as 2-byte
+ *                  binary16 bit patterns; only 0x0000 .. 0x7BFF (0 .. 65504)
+ *                  are produced or accepted.  Naive: s = fp16(fl32(amax / C)),
+ *                  round to nearest even, saturating at 65504.  SSE / H-Optimal
+ *                  alternate, from the Naive scale, between encoding the block
+ *                  at the current scale and the least-squares scale of that
+ *                  assignment, s* = sum w q / sum q^2 (weighted by h for
+ *                  H-Optimal, in float64) snapped to FP16; they stop at a
+ *                  fixed point, at an all-zero assignment or the zero scale,
+ *                  or after 32 rounds, and keep the scale with the smallest
+ *                  objective among those visited (the earliest on ties).
  * Search candidates: the 126 positive finite E4M3 codes 0x01..0x7E (E4M3 and
  * INT8 grids; max 448), all 255 finite E8M0 codes 0x00..0xFE (2^-127 ..
  * 2^127), or the 255 positive UE4M4 / UE5M3 codes.  Naive may also return E4M3 code 0 (the zero scale: every element
@@ -96,7 +111,9 @@ typedef enum {
     HD_FP8_E4M3S = 4,
     HD_NVFP4_UE4M4 = 5,
     HD_NVFP4_UE5M3 = 6,
-    HD_NVINT4 = 7
+    HD_NVINT4 = 7,
+    HD_FP4_F16 = 8,
+    HD_INT4_F16 = 9
 } hd_format;
 
 /* ---------------------------------------------------------------- hdiag --- */
@@ -125,12 +142,14 @@ hd_status hdiag(const void *X, hd_dtype xt, int64_t M, int64_t K, float *h, void
  *            HD_SSE_OPT.
  *   codes  : element codes.  HD_INT8_E4M3: [N, K] int8 two's complement.
  *            HD_MXFP8 / HD_FP8_E4M3S: [N, K] E4M3 bytes (sign bit 7).
- *            HD_NVFP4 / HD_MXFP4 / HD_NVFP4_UE4M4 / HD_NVFP4_UE5M3: [N, K/2]
- *            bytes of two E2M1 nibbles (sign bit 3), element 2i in the low
- *            nibble.  HD_NVINT4: [N, K/2] bytes of two INT4 two's complement
- *            nibbles, same order.  A negative input that rounds to
+ *            HD_NVFP4 / HD_MXFP4 / HD_NVFP4_UE4M4 / HD_NVFP4_UE5M3 /
+ *            HD_FP4_F16: [N, K/2] bytes of two E2M1 nibbles (sign bit 3),
+ *            element 2i in the low nibble.  HD_NVINT4 / HD_INT4_F16: [N, K/2]
+ *            bytes of two INT4 two's complement nibbles, same order.  A negative input that rounds to
  *            zero keeps its sign bit (E2M1 0x8, E4M3 0x80).
- *   scales : [N, K/B] scale codes (E4M3 or E8M0 bytes).
+ *   scales : [N, K/B] scale codes: one byte each (E4M3, E8M0, UE4M4, UE5M3),
+ *            or two (little-endian binary16 bits, 2-byte aligned) for
+ *            HD_FP4_F16 / HD_INT4_F16.
  *   block_obj: optional [N, K/B] float32: the block's objective at the chosen
  *            scale (weighted by h when h is used), computed in float64 and
  *            rounded; may be NULL.
@@ -147,7 +166,8 @@ hd_status quantize_blocks(hd_method method, hd_format fmt, int32_t B, const void
 
 /* Encode W with caller-given scale codes (the encode step alone).  Arguments
  * as quantize_blocks; scales_in [N, K/B] is read, not written.  A NaN scale
- * code (E4M3 0x7F..., E8M0 0xFF) encodes its block with the zero scale. */
+ * code (E4M3 0x7F..., E8M0 0xFF, binary16 above 0x7BFF) encodes its block
+ * with the zero scale. */
 hd_status encode_blocks(hd_format fmt, int32_t B, const void *W, hd_dtype wt, int64_t N, int64_t K,
                         const uint8_t *scales_in, const float *h, uint8_t *codes, float *block_obj,
                         void *stream);
@@ -157,7 +177,8 @@ hd_status encode_blocks(hd_format fmt, int32_t B, const void *W, hd_dtype wt, in
 /* Wq[n][k] = sign * fl32(s_block * val(q)) ("Is Finer Better?" §2.1,
  * x^ = s q), written as float32 or as bfloat16 (round-to-nearest-even of the
  * float32 value).  codes / scales laid out as quantize_blocks writes them.
- * Invalid codes (INT8 -128, E4M3 0x7F / 0xFF, E8M0 0xFF) decode to 0. */
+ * Invalid codes (INT8 -128, E4M3 0x7F / 0xFF, E8M0 0xFF, INT4 -8, binary16
+ * scales above 0x7BFF) decode to 0. */
 hd_status dequantize(hd_format fmt, int32_t B, const uint8_t *codes, const uint8_t *scales,
                      int64_t N, int64_t K, void *Wq, hd_dtype out_t, void *stream);
 
@@ -230,7 +251,8 @@ hd_status output_error_given_ref(const void *X, hd_dtype xt, int64_t M, const vo
  * workspace: ws_bytes >= output_error_codes_workspace_size(M, N, K).
  * Errors: HD_ERR_INVALID_ARG as quantize_blocks for fmt / B / N / K, NULL or
  * misaligned pointers, a short ref or workspace; HD_ERR_UNSUPPORTED for a
- * float32 X.  Calls that share `ref` may run concurrently (it is only read);
+ * float32 X and for the FP16-scale formats (s val(q) needs up to 14
+ * significant bits there: use dequantize + output_error).  Calls that share `ref` may run concurrently (it is only read);
  * each needs its own workspace. */
 #define HD_REF_Y_OFFSET 256
 size_t output_reference_size(int64_t M, int64_t N, int64_t K);
@@ -251,9 +273,11 @@ const char *hdiag_strerror(hd_status s);
 const char *hdiag_last_error(void);
 
 /* Format facts: bits of one element code, bits of one scale, number of search
- * candidates, and total bits per weight = elem_bits + scale_bits / B
- * (qwantize "Results", "Larger blocks" layout table: 4.5 / 4.25 / 4.125 for
- * FP4 with an 8-bit scale at B = 16 / 32 / 64).  Any output pointer may be
+ * candidates (for the FP16 scale grids: the 31743 positive finite values the
+ * alternation may land on), and total bits per weight = elem_bits +
+ * scale_bits / B (qwantize "Results", "Larger blocks" layout table: 4.5 /
+ * 4.25 / 4.125 for FP4 with an 8-bit scale at B = 16 / 32 / 64, and 4.125
+ * with an FP16 scale at B = 128).  Any output pointer may be
  * NULL.  Host-only; needs no GPU. */
 hd_status hdiag_format_info(hd_format fmt, int32_t B, int *elem_bits, int *scale_bits,
                             int *n_candidates, double *bits_per_weight);

@@ -51,6 +51,16 @@ def test_format_info_bits_per_weight():
     assert hd.hdiag_format_info(hd.NVINT4, 16) == (4, 8, 126, 4.5)
 
 
+def test_format_info_fp16_scales():
+    # qwantize "Results", "Larger blocks" layout table: FP16 E5M10 scales at
+    # B = 128 cost 0.125 bits per weight, 4.125 in total with 4-bit elements
+    for B, scale_bpw, total in golden_rows("bits_per_weight_f16.txt"):
+        for f in hd.F16_SCALES:
+            e, s, n, bpw = hd.hdiag_format_info(f, int(B))
+            assert (e, s, n) == (4, 16, 0x7BFF)
+            assert bpw == float(total) and s / int(B) == float(scale_bpw)
+
+
 def test_strerror():
     assert hd._strerror(hd.HD_ERR_INVALID_ARG) == "invalid argument"
     assert hd._strerror(hd.HD_OK) == "success"
@@ -65,7 +75,7 @@ MIS = ctypes.c_void_p((1 << 20) + 4)
     ((hd.SSE_OPT, hd.NVFP4, 12, A, hd.HD_BF16, 4, 48, None, A, A, None, None), "block size"),
     ((hd.SSE_OPT, hd.NVFP4, 16, A, hd.HD_BF16, 4, 40, None, A, A, None, None), "multiple of B"),
     ((7, hd.NVFP4, 16, A, hd.HD_BF16, 4, 32, None, A, A, None, None), "unknown method"),
-    ((hd.SSE_OPT, 9, 16, A, hd.HD_BF16, 4, 32, None, A, A, None, None), "unknown format"),
+    ((hd.SSE_OPT, 10, 16, A, hd.HD_BF16, 4, 32, None, A, A, None, None), "unknown format"),
     ((hd.SSE_OPT, hd.NVFP4, 16, A, 5, 4, 32, None, A, A, None, None), "unknown dtype"),
     ((hd.H_OPT, hd.NVFP4, 16, A, hd.HD_BF16, 4, 32, None, A, A, None, None), "needs h"),
     ((hd.SSE_OPT, hd.NVFP4, 16, None, hd.HD_BF16, 4, 32, None, A, A, None, None), "W is NULL"),
@@ -83,8 +93,11 @@ def test_ocp_rule_needs_e8m0():
     assert rc == hd.HD_ERR_INVALID_ARG and "E8M0" in hd.lib().hdiag_last_error().decode()
     rc = hd.lib().quantize_blocks(4, hd.MXFP4, 32, A, hd.HD_BF16, 4, 32, None, A, A, None, None)
     assert rc == hd.HD_ERR_INVALID_ARG and "unknown method" in hd.lib().hdiag_last_error().decode()
-    rc = hd.lib().quantize_blocks(hd.SSE_OPT, 8, 32, A, hd.HD_BF16, 4, 32, None, A, A, None, None)
+    rc = hd.lib().quantize_blocks(hd.SSE_OPT, 10, 32, A, hd.HD_BF16, 4, 32, None, A, A, None, None)
     assert rc == hd.HD_ERR_INVALID_ARG and "unknown format" in hd.lib().hdiag_last_error().decode()
+    for f in hd.F16_SCALES:
+        rc = hd.lib().quantize_blocks(hd.NAIVE_OCP, f, 128, A, hd.HD_BF16, 4, 128, None, A, A, None, None)
+        assert rc == hd.HD_ERR_INVALID_ARG and "E8M0" in hd.lib().hdiag_last_error().decode()
 
 
 def test_empty_inputs_are_noops():
@@ -142,3 +155,7 @@ def test_output_error_codes_validation():
     bad = list(args); bad[11] = None
     assert L.output_error_codes(*bad) == hd.HD_ERR_INVALID_ARG
     assert "out is NULL" in L.hdiag_last_error().decode()
+    for f in hd.F16_SCALES:  # s val(q) is not an exact 16-bit operand with FP16 scales
+        bad = list(args); bad[0] = f; bad[1] = 128
+        assert L.output_error_codes(*bad) == hd.HD_ERR_UNSUPPORTED
+        assert "FP16" in L.hdiag_last_error().decode()
