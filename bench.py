@@ -276,7 +276,8 @@ def formats_suite(args, dev):
     h from X 16384x9728): per (format, B, method) the kernel time of
     quantize_blocks (median of `steps` launches after `warmup`, HIP events),
     Gweights/s, and the weight / output error of the result (the output error
-    against one stored X W^T reference)."""
+    against one stored X W^T reference: from the codes for 8-bit scales, from
+    the dequantised weights for FP16 scales)."""
     import torch
 
     import block_scaled_precision_hdiag_amd as hd
@@ -289,6 +290,8 @@ def formats_suite(args, dev):
     h = hd.hdiag(X)
     ref = hd.output_reference(X, W)
     ws_o = torch.empty(hd.output_error_codes_workspace_size(M, N, K), dtype=torch.uint8, device=dev)
+    ysq = hd.reference_ysq(ref)
+    ws_g = torch.empty(hd.output_error_workspace_size(M, N, K), dtype=torch.uint8, device=dev)
     rows = []
     names = {v: k for k, v in hd.FORMATS.items()}
     for fmt in sorted(names):
@@ -296,10 +299,13 @@ def formats_suite(args, dev):
         meths = [("naive", hd.NAIVE), ("sse", hd.SSE_OPT), ("h", hd.H_OPT)]
         if fmt in (hd.MXFP4, hd.MXFP8):
             meths.append(("naive_ocp", hd.NAIVE_OCP))
-        for B in (16, 32):
+        # the FP16-scale formats at the pages' B = 128; NVFP4 / NVINT4 also at
+        # B = 64, the E4M3-scale point of the same 4.125 bits per weight
+        blocks = (128,) if fmt in hd.F16_SCALES else (16, 32, 64) if fmt in (hd.NVFP4, hd.NVINT4) else (16, 32)
+        for B in blocks:
             for mname, m in meths:
                 codes = torch.empty(hd.codes_shape(fmt, N, K), dtype=torch.uint8, device=dev)
-                scales = torch.empty((N, K // B), dtype=torch.uint8, device=dev)
+                scales = torch.empty((N, K // B), dtype=hd.scale_dtype(fmt), device=dev)
                 run = lambda: hd.quantize_blocks(m, fmt, B, W, h=h, codes=codes, scales=scales)
                 for _ in range(max(args.warmup, 1)):
                     run()
@@ -314,13 +320,18 @@ def formats_suite(args, dev):
                 ms = sorted(ts)[len(ts) // 2]
                 Wq = hd.dequantize(fmt, B, codes, scales, N, K)
                 we = hd.weight_error(W, Wq).item()
-                oe = hd.output_error_codes(fmt, B, X, codes, scales, ref, N, K, workspace=ws_o).item()
+                if fmt in hd.F16_SCALES:  # no exact 16-bit operand: the generic product
+                    oe = hd.output_error_given_ref(X, W, Wq, ysq, workspace=ws_g).item()
+                else:
+                    oe = hd.output_error_codes(fmt, B, X, codes, scales, ref, N, K, workspace=ws_o).item()
                 rows.append({"format": names[fmt], "B": B, "method": mname, "candidates": nc,
+                             "bits_per_weight": hd.hdiag_format_info(fmt, B)[3],
                              "ms": round(ms, 4), "gweights_per_s": round(N * K / (ms * 1e-3) / 1e9, 2),
                              "weight_error": round(we, 6), "output_error": round(oe, 6)})
     print(json.dumps({"suite": "formats", "unit": "Gweights/s",
                       "config": {"workload": "scale choice on W 2560x9728 bf16 (Student-t(4) x 0.02, row gains), "
-                                             "h from X 16384x9728 bf16; every format, B in {16, 32}",
+                                             "h from X 16384x9728 bf16; every format at B in {16, 32} (NVFP4 and "
+                                             "NVINT4 also 64), the FP16-scale formats at B = 128",
                                  "W": [N, K], "X": [M, K]},
                       "data": "synthetic", "rows": rows}), flush=True)
 
