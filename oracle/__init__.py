@@ -63,6 +63,8 @@ def lib():
         L.orc_output_error.restype = dbl
         L.orc_matmul_nt.argtypes = [P, i32, i64, P, i32, i64, i64, P, i32]
         L.orc_matmul_nt.restype = None
+        L.orc_xtx.argtypes = [P, i32, i64, i64, P, i32]
+        L.orc_gptq.argtypes = [i32, i32, i32, P, i32, i64, i64, P, dbl, i32, P, P, P, i32]
         L.orc_max_threads.argtypes = []
         _lib = L
     return _lib
@@ -234,3 +236,28 @@ def output_error(X, W, Wq, nthreads=0, sums=False):
     r = lib().orc_output_error(_ptr(X), _dt(X), M, _ptr(W), _dt(W), _ptr(Wq), _dt(Wq), N, K,
                                ctypes.byref(d), ctypes.byref(y), nthreads)
     return (r, d.value, y.value) if sums else r
+
+
+def xtx(X, nthreads=0):
+    """H = X^T X in float64 ([K, K])."""
+    X = np.ascontiguousarray(X)
+    M, K = X.shape
+    H = np.empty((K, K), dtype=np.float64)
+    _check(lib().orc_xtx(_ptr(X), _dt(X), M, K, _ptr(H), nthreads), "xtx")
+    return H
+
+
+def gptq(method, fmt, B, W, H, damp=0.01, ordered=False, nthreads=0):
+    """GPTQ-Seq (ordered=False) or GPTQ-Ord on top of `method`'s scale choice,
+    given H = X^T X.  Returns (codes, scales, block_order) like quantize."""
+    W = np.ascontiguousarray(W)
+    N, K = W.shape
+    H = np.ascontiguousarray(H, np.float64)
+    codes = np.zeros(codes_shape(fmt, N, K), np.uint8)
+    scales = np.zeros((N, K // B), scale_dtype(fmt))
+    order = np.zeros(K // B, np.int32)
+    rc = lib().orc_gptq(method, fmt, B, _ptr(W), _dt(W), N, K, _ptr(H), float(damp), int(bool(ordered)),
+                        _ptr(codes), _ptr(scales), _ptr(order), nthreads)
+    _check(rc, "gptq")
+    return codes, scales, order
+

@@ -43,6 +43,11 @@
  *     fp16(fl32(amax / C)); SSE-Optimal / H-Optimal are found by alternating
  *     element assignment and the closed-form least-squares scale snapped to
  *     FP16 (f16_alternation below; its readings are listed there).
+ *   - GPTQ (qwantize "Results", "GPTQ Quantization"; quantisation-algorithms
+ *     note, §1): H = X^T X (orc_xtx), damped, the upper Cholesky factor of its
+ *     inverse, and the column loop of Frantar et al. with the GPTQ block equal
+ *     to the quantisation block, in natural or loss order (orc_gptq; its
+ *     readings are listed there).
  *
  * Readings where the pages are silent (also listed in the design notes):
  *   E8M0 Naive snap = nearest power of two in the linear domain, ties upward
@@ -539,6 +544,34 @@ static int get_code(int fmt, const uint8_t *codes, int64_t K, int64_t n, int64_t
     return codes[n * K + k];
 }
 
+/* The scale code a method picks for one block w[0..B-1] with max |w| = amax,
+ * and its objective (weighted by om, or unweighted if om == NULL): Naive or
+ * the OCP rule; the exact argmin over the scale grid in ascending code order
+ * (the first strict minimum); or, for FP16 scales, the alternation. */
+static int choose_scale(int method, int fmt, const float *w, const double *om, int B, float amax, double *best)
+{
+    if (method == M_NAIVE || method == M_NAIVE_OCP) {
+        int code = method == M_NAIVE ? orc_naive_scale_code(fmt, amax) : orc_naive_ocp_code(fmt, amax);
+        *best = block_objective(fmt, orc_scale_value(fmt, code), w, om, B);
+        return code;
+    }
+    if (scale_kind(fmt) == S_F16)
+        return f16_alternation(fmt, w, om, B, amax, best);
+    int c0, c1;
+    orc_candidates(fmt, &c0, &c1);
+    int code = c0;
+    double b0 = block_objective(fmt, orc_scale_value(fmt, c0), w, om, B);
+    for (int c = c0 + 1; c <= c1; c++) {
+        double o = block_objective(fmt, orc_scale_value(fmt, c), w, om, B);
+        if (o < b0) {
+            b0 = o;
+            code = c;
+        }
+    }
+    *best = b0;
+    return code;
+}
+
 /* quantize_blocks.  method: Naive / SSE-Optimal / H-Optimal (the exact argmin
  * over the scale grid; for FP16 scales the alternation above).  scales_in, when
  * not NULL, fixes every block's scale code (encode only: method is ignored).
@@ -562,8 +595,6 @@ int orc_quantize(int method, int fmt, int B, const void *W, int wdt, int64_t N, 
         return ORC_EINVAL;
     if (N == 0 || K == 0)
         return ORC_OK;
-    int c0, c1;
-    orc_candidates(fmt, &c0, &c1);
     const int64_t nb = K / B;
     int use_h = h != NULL && (scales_in != NULL || method != M_SSE);
     double *om_all = NULL;
@@ -603,21 +634,8 @@ int orc_quantize(int method, int fmt, int B, const void *W, int wdt, int64_t N, 
                         continue;
                     }
                     best = block_objective(fmt, s, w, om, B);
-                } else if (method == M_NAIVE || method == M_NAIVE_OCP) {
-                    code = method == M_NAIVE ? orc_naive_scale_code(fmt, amax) : orc_naive_ocp_code(fmt, amax);
-                    best = block_objective(fmt, orc_scale_value(fmt, code), w, om, B);
-                } else if (scale_kind(fmt) == S_F16) {
-                    code = f16_alternation(fmt, w, om, B, amax, &best);
                 } else {
-                    code = c0;
-                    best = block_objective(fmt, orc_scale_value(fmt, c0), w, om, B);
-                    for (int c = c0 + 1; c <= c1; c++) {
-                        double o = block_objective(fmt, orc_scale_value(fmt, c), w, om, B);
-                        if (o < best) {
-                            best = o;
-                            code = c;
-                        }
-                    }
+                    code = choose_scale(method, fmt, w, om, B, amax, &best);
                 }
                 float s = orc_scale_value(fmt, code);
                 if (scales) put_scale(fmt, scales, n * nb + b, code);
@@ -807,4 +825,246 @@ void orc_matmul_nt(const void *X, int xdt, int64_t M, const void *W, int wdt, in
             Y[t * N + n] = y;
         }
     }
+}
+
+/* ------------------------------------------------------------------------ */
+/* GPTQ                                                                      */
+/* ------------------------------------------------------------------------ */
+
+/* H = X^T X, K x K row-major in float64: H[i][j] = sum_t x_ti x_tj, t in
+ * order (products of bf16 / fp32 values are exact in float64). */
+int orc_xtx(const void *X, int xdt, int64_t M, int64_t K, double *H, int nthreads)
+{
+    if (M < 0 || K < 0 || (xdt != DT_F32 && xdt != DT_BF16))
+        return ORC_EINVAL;
+    int nt = set_threads(nthreads);
+#pragma omp parallel for num_threads(nt) schedule(dynamic, 1)
+    for (int64_t i = 0; i < K; i++) {
+        for (int64_t j = 0; j <= i; j++) {
+            double acc = 0.0;
+            for (int64_t t = 0; t < M; t++)
+                acc += (double)widen(X, xdt, t * K + i) * (double)widen(X, xdt, t * K + j);
+            H[i * K + j] = acc;
+            H[j * K + i] = acc;
+        }
+    }
+    return ORC_OK;
+}
+
+/* Lower Cholesky factor of the symmetric positive definite A (n x n), in
+ * place of L (may alias nothing); returns ORC_EINVAL if A is not positive
+ * definite in float64. */
+static int cholesky_lower(const double *A, double *L, int64_t n)
+{
+    memset(L, 0, sizeof(double) * (size_t)(n * n));
+    for (int64_t j = 0; j < n; j++) {
+        double d = A[j * n + j];
+        for (int64_t k = 0; k < j; k++)
+            d -= L[j * n + k] * L[j * n + k];
+        if (!(d > 0.0))
+            return ORC_EINVAL;
+        const double ljj = sqrt(d);
+        L[j * n + j] = ljj;
+        for (int64_t i = j + 1; i < n; i++) {
+            double v = A[i * n + j];
+            for (int64_t k = 0; k < j; k++)
+                v -= L[i * n + k] * L[j * n + k];
+            L[i * n + j] = v / ljj;
+        }
+    }
+    return ORC_OK;
+}
+
+/* U with H^-1 = U^T U, U upper triangular with positive diagonal, for the
+ * symmetric positive definite H (n x n): the sequence GPTQ (Frantar et al.)
+ * uses - L = chol(H), H^-1 = L^-T L^-1, then the Cholesky factor of H^-1. */
+static int inverse_upper_factor(const double *H, double *U, int64_t n)
+{
+    double *L = (double *)malloc(sizeof(double) * (size_t)(n * n));
+    double *Li = (double *)calloc((size_t)(n * n), sizeof(double));
+    double *Hi = (double *)malloc(sizeof(double) * (size_t)(n * n));
+    int rc = (L && Li && Hi) ? ORC_OK : ORC_ENOMEM;
+    if (rc == ORC_OK)
+        rc = cholesky_lower(H, L, n);
+    if (rc == ORC_OK) {
+        /* L^-1 column by column: forward substitution on the unit vectors */
+        for (int64_t c = 0; c < n; c++) {
+            for (int64_t i = c; i < n; i++) {
+                double v = (i == c) ? 1.0 : 0.0;
+                for (int64_t k = c; k < i; k++)
+                    v -= L[i * n + k] * Li[k * n + c];
+                Li[i * n + c] = v / L[i * n + i];
+            }
+        }
+        /* H^-1 = L^-T L^-1: (i, j) = sum_k Li[k][i] Li[k][j], k >= max(i, j) */
+        for (int64_t i = 0; i < n; i++) {
+            for (int64_t j = 0; j <= i; j++) {
+                double v = 0.0;
+                for (int64_t k = i; k < n; k++)
+                    v += Li[k * n + i] * Li[k * n + j];
+                Hi[i * n + j] = v;
+                Hi[j * n + i] = v;
+            }
+        }
+        rc = cholesky_lower(Hi, L, n); /* H^-1 = L2 L2^T, U = L2^T */
+        if (rc == ORC_OK)
+            for (int64_t i = 0; i < n; i++)
+                for (int64_t j = 0; j < n; j++)
+                    U[i * n + j] = (j >= i) ? L[j * n + i] : 0.0;
+    }
+    free(L);
+    free(Li);
+    free(Hi);
+    return rc;
+}
+
+/* GPTQ on top of a scale choice (qwantize "Results", "GPTQ Quantization": GPTQ
+ * of Frantar et al. with its block size equal to the quantisation block size;
+ * the quantisation-algorithms note, §1: H = X^T X + lambda I, columns quantised
+ * in sequence, each residual propagated through H^-1).
+ *
+ *   H       : X^T X, K x K (orc_xtx); h_j = fl32(H_jj) weights H-Optimal, as
+ *             hdiag would give it.
+ *   damping : lambda = damp * mean_j H_jj (1 if that mean is 0), H + lambda I.
+ *   order   : ordered == 0 (GPTQ-Seq): block columns left to right.
+ *             ordered != 0 (GPTQ-Ord): block columns by descending
+ *             Hessian-weighted loss sum_n sum_{j in b} h_j (w_nj - q_nj)^2 of
+ *             the method's quantisation of W without GPTQ, ties in column
+ *             order; W's and H's columns are permuted by whole blocks.
+ *   loop    : U = the upper Cholesky factor of (H + lambda I)^-1 in the
+ *             processing order.  For each block column in order, every row's
+ *             scale is chosen by `method` from that row's current (already
+ *             compensated) block, rounded to fp32 as the quantiser's input;
+ *             then the block's columns j are encoded one by one at that scale
+ *             and the error e = (w_j - q_j) / U_jj is propagated to every
+ *             later column k: w_k -= e U_jk.  Working weights are float64.
+ * Outputs codes / scales in the original column order; block_order[i] is the
+ * original index of the i-th block column processed (may be NULL). */
+int orc_gptq(int method, int fmt, int B, const void *W, int wdt, int64_t N, int64_t K, const double *H,
+             double damp, int ordered, uint8_t *codes, uint8_t *scales, int32_t *block_order, int nthreads)
+{
+    init_tables();
+    if (check_common(fmt, B, N, K) != ORC_OK || (wdt != DT_F32 && wdt != DT_BF16) || !H || damp < 0.0 || B > 256)
+        return ORC_EINVAL;
+    if (method < M_NAIVE || method > M_NAIVE_OCP || (method == M_NAIVE_OCP && scale_kind(fmt) != S_E8M0))
+        return ORC_EINVAL;
+    if (N == 0 || K == 0)
+        return ORC_OK;
+    const int64_t nb = K / B;
+    int nt = set_threads(nthreads);
+    int rc = ORC_OK;
+    float *h = (float *)malloc(sizeof(float) * (size_t)K);
+    int64_t *perm = (int64_t *)malloc(sizeof(int64_t) * (size_t)nb); /* processing slot -> block */
+    int64_t *col = (int64_t *)malloc(sizeof(int64_t) * (size_t)K);   /* processed column -> original */
+    double *Hp = (double *)malloc(sizeof(double) * (size_t)(K * K));
+    double *U = (double *)malloc(sizeof(double) * (size_t)(K * K));
+    double *Wc = (double *)malloc(sizeof(double) * (size_t)(N * K));
+    double *om = (double *)malloc(sizeof(double) * (size_t)K);
+    if (!h || !perm || !col || !Hp || !U || !Wc || !om) {
+        rc = ORC_ENOMEM;
+        goto done;
+    }
+    double mean = 0.0;
+    for (int64_t j = 0; j < K; j++) {
+        h[j] = (float)H[j * K + j];
+        mean += H[j * K + j];
+    }
+    mean /= (double)K;
+    const double lambda = mean > 0.0 ? damp * mean : 1.0;
+
+    for (int64_t b = 0; b < nb; b++)
+        perm[b] = b;
+    if (ordered) {
+        /* Hessian-weighted loss of each block column without GPTQ */
+        double *loss = (double *)calloc((size_t)nb, sizeof(double));
+        double *bo = (double *)malloc(sizeof(double) * (size_t)(N * nb));
+        if (!loss || !bo) {
+            free(loss);
+            free(bo);
+            rc = ORC_ENOMEM;
+            goto done;
+        }
+        uint8_t *sc = (uint8_t *)malloc((size_t)(N * nb) * (size_t)scale_bytes(fmt));
+        rc = sc ? orc_quantize(method, fmt, B, W, wdt, N, K, h, NULL, NULL, sc, NULL, nthreads) : ORC_ENOMEM;
+        if (rc == ORC_OK)
+            rc = orc_quantize(M_NAIVE, fmt, B, W, wdt, N, K, h, sc, NULL, NULL, bo, nthreads);
+        if (rc == ORC_OK) {
+            for (int64_t n = 0; n < N; n++)
+                for (int64_t b = 0; b < nb; b++)
+                    loss[b] += bo[n * nb + b];
+            /* stable insertion sort by descending loss */
+            for (int64_t i = 1; i < nb; i++) {
+                int64_t v = perm[i], k = i;
+                while (k > 0 && loss[perm[k - 1]] < loss[v]) {
+                    perm[k] = perm[k - 1];
+                    k--;
+                }
+                perm[k] = v;
+            }
+        }
+        free(sc);
+        free(loss);
+        free(bo);
+        if (rc != ORC_OK)
+            goto done;
+    }
+    for (int64_t i = 0; i < nb; i++)
+        for (int j = 0; j < B; j++)
+            col[i * B + j] = perm[i] * B + j;
+    if (block_order)
+        for (int64_t i = 0; i < nb; i++)
+            block_order[i] = (int32_t)perm[i];
+    for (int64_t i = 0; i < K; i++) {
+        for (int64_t j = 0; j < K; j++)
+            Hp[i * K + j] = H[col[i] * K + col[j]];
+        Hp[i * K + i] += lambda;
+        om[i] = (double)h[col[i]];
+    }
+    rc = inverse_upper_factor(Hp, U, K);
+    if (rc != ORC_OK)
+        goto done;
+    for (int64_t n = 0; n < N; n++)
+        for (int64_t i = 0; i < K; i++)
+            Wc[n * K + i] = (double)widen(W, wdt, n * K + col[i]);
+
+#pragma omp parallel num_threads(nt)
+    {
+        float w[256];
+        const double *omw;
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t n = 0; n < N; n++) {
+            double *wr = Wc + n * K;
+            for (int64_t i = 0; i < nb; i++) {
+                const int64_t cs = i * B;
+                float amax = 0.0f;
+                for (int j = 0; j < B; j++) {
+                    w[j] = (float)wr[cs + j];
+                    if (fabsf(w[j]) > amax) amax = fabsf(w[j]);
+                }
+                omw = (method == M_SSE) ? NULL : om + cs;
+                double obj;
+                const int code = choose_scale(method, fmt, w, omw, B, amax, &obj);
+                const float s = orc_scale_value(fmt, code);
+                put_scale(fmt, scales, n * nb + perm[i], code);
+                for (int j = 0; j < B; j++) {
+                    const int64_t c = cs + j;
+                    float wq;
+                    const int cb = enc_elem(fmt, s, (float)wr[c], &wq);
+                    put_code(fmt, codes, N, K, n, col[c], cb);
+                    const double e = (wr[c] - (double)wq) / U[c * K + c];
+                    for (int64_t k = c + 1; k < K; k++)
+                        wr[k] -= e * U[c * K + k];
+                }
+            }
+        }
+    }
+done:
+    free(h);
+    free(perm);
+    free(col);
+    free(Hp);
+    free(U);
+    free(Wc);
+    free(om);
+    return rc;
 }
