@@ -9,7 +9,8 @@ computing anything some other way: build it with
 
 Names follow the C ABI: ``hdiag``, ``quantize_blocks``, ``encode_blocks``,
 ``dequantize``, ``weight_error``, ``output_error``, ``output_error_given_ref``,
-``output_reference``, ``output_error_codes``, ``hdiag_format_info``.
+``output_reference``, ``output_error_codes``, ``gptq_hessian``, ``gptq_quantize``,
+``hdiag_format_info``.
 """
 import ctypes
 import os
@@ -37,7 +38,8 @@ F16_SCALES = (FP4_F16, INT4_F16)
 EXPORTS = ["hdiag", "hdiag_workspace_size", "quantize_blocks", "encode_blocks", "dequantize",
            "weight_error", "weight_error_workspace_size", "output_error", "output_error_workspace_size",
            "output_error_given_ref", "output_reference", "output_reference_size", "output_error_codes",
-           "output_error_codes_workspace_size",
+           "output_error_codes_workspace_size", "gptq_hessian", "gptq_hessian_workspace_size", "gptq_quantize",
+           "gptq_workspace_size",
            "hdiag_strerror", "hdiag_last_error", "hdiag_format_info", "hdiag_version"]
 
 
@@ -85,9 +87,15 @@ def lib():
         L.hdiag_format_info.argtypes = [i32, i32, P, P, P, P]
         L.hdiag_version.argtypes = []
         L.hdiag_version.restype = ctypes.c_char_p
+        L.gptq_hessian_workspace_size.argtypes = [i64, i64]
+        L.gptq_hessian_workspace_size.restype = sz
+        L.gptq_hessian.argtypes = [P, i32, i64, i64, P, P, sz, P]
+        L.gptq_workspace_size.argtypes = [i32, i64, i64]
+        L.gptq_workspace_size.restype = sz
+        L.gptq_quantize.argtypes = [i32, i32, i32, P, i32, i64, i64, P, ctypes.c_double, i32, P, P, P, P, P, sz, P]
         for name in ("hdiag", "quantize_blocks", "encode_blocks", "dequantize", "weight_error",
                      "output_error", "output_error_given_ref", "output_reference", "output_error_codes",
-                     "hdiag_format_info"):
+                     "hdiag_format_info", "gptq_hessian", "gptq_quantize"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -281,6 +289,39 @@ def output_error_codes(fmt, B, X, codes, scales, ref, N, K, sums=False, workspac
                                     ref.numel(), _ptr(out), _ptr(s), _ptr(ws), ws.numel(), _stream(d)),
            "output_error_codes")
     return (out, s) if sums else out
+
+
+def gptq_hessian(X, H=None, workspace=None):
+    """H = X^T X (float32 [K, K]) for bfloat16 X [M, K], on the MFMA units."""
+    d = _dev(X)
+    M, K = X.shape
+    H = H if H is not None else torch.empty((K, K), dtype=torch.float32, device=d)
+    need = int(lib().gptq_hessian_workspace_size(M, K))
+    ws = workspace if workspace is not None else torch.empty(max(need, 16), dtype=torch.uint8, device=d)
+    _check(lib().gptq_hessian(_ptr(X), _dt(X), M, K, _ptr(H), _ptr(ws), ws.numel(), _stream(d)), "gptq_hessian")
+    return H
+
+
+def gptq_workspace_size(B, N, K):
+    return int(lib().gptq_workspace_size(B, N, K))
+
+
+def gptq_quantize(method, fmt, B, W, H, damp=0.01, ordered=False, codes=None, scales=None, workspace=None):
+    """GPTQ-Seq (ordered=False) or GPTQ-Ord on top of `method`'s scale choice,
+    given H = X^T X (float32 [K, K]).  Returns (codes, scales, block_order
+    int32 [K/B], info int32 [1]: 0, or 1 + the first non-positive pivot)."""
+    d = _dev(W)
+    N, K = W.shape
+    codes = codes if codes is not None else torch.empty(codes_shape(fmt, N, K), dtype=torch.uint8, device=d)
+    scales = scales if scales is not None else torch.empty((N, K // B), dtype=scale_dtype(fmt), device=d)
+    order = torch.empty(K // B, dtype=torch.int32, device=d)
+    info = torch.zeros(1, dtype=torch.int32, device=d)
+    need = gptq_workspace_size(B, N, K)
+    ws = workspace if workspace is not None else torch.empty(max(need, 16), dtype=torch.uint8, device=d)
+    _check(lib().gptq_quantize(method, fmt, B, _ptr(W), _dt(W), N, K, _ptr(H), float(damp), int(bool(ordered)),
+                               _ptr(codes), _ptr(scales), _ptr(order), _ptr(info), _ptr(ws), ws.numel(), _stream(d)),
+           "gptq_quantize")
+    return codes, scales, order, info
 
 
 def hdiag_format_info(fmt, B):

@@ -309,6 +309,59 @@ hd_status output_error_codes(hd_format fmt, int32_t B, const void *X, hd_dtype x
                       "output_error_codes");
 }
 
+size_t gptq_hessian_workspace_size(int64_t M, int64_t K)
+{
+    if (M < 0 || K < 0) return 0;
+    return (size_t)hd::gptq_hessian_ws(M, K);
+}
+
+hd_status gptq_hessian(const void *X, hd_dtype xt, int64_t M, int64_t K, float *H, void *ws, size_t ws_bytes,
+                       void *stream)
+{
+    HD_REQUIRE(valid_dtype(xt), "unknown dtype %d", (int)xt);
+    HD_REQUIRE(M >= 0 && K >= 0, "negative size M=%lld K=%lld", (long long)M, (long long)K);
+    HD_REQUIRE(M <= (int64_t)1 << 31 && K <= 65535, "size too large (K <= 65535)");
+    if (xt != HD_BF16) return fail(HD_ERR_UNSUPPORTED, "gptq_hessian needs bfloat16 X (the MFMA product)");
+    if (K == 0) return ok();
+    HD_CHECK_PTR(H, true);
+    HD_CHECK_PTR(ws, true);
+    HD_CHECK_PTR(X, M > 0);
+    HD_REQUIRE(ws_bytes >= (size_t)hd::gptq_hessian_ws(M, K), "workspace too small");
+    return hip_status(hd::launch_gptq_hessian(X, M, K, H, ws, (hipStream_t)stream), "gptq_hessian");
+}
+
+size_t gptq_workspace_size(int32_t B, int64_t N, int64_t K)
+{
+    if (!valid_block(B) || N < 0 || K < 0 || K % B) return 0;
+    return (size_t)hd::gptq_ws(B, N, K);
+}
+
+hd_status gptq_quantize(hd_method method, hd_format fmt, int32_t B, const void *W, hd_dtype wt, int64_t N, int64_t K,
+                        const float *H, double damp, int32_t ordered, uint8_t *codes, uint8_t *scales,
+                        int32_t *block_order, int32_t *info, void *ws, size_t ws_bytes, void *stream)
+{
+    HD_REQUIRE(method >= HD_NAIVE && method <= HD_NAIVE_OCP, "unknown method %d", (int)method);
+    HD_REQUIRE(valid_dtype(wt), "unknown dtype %d", (int)wt);
+    hd_status s = check_quant_shape(fmt, B, N, K);
+    if (s != HD_OK) return s;
+    HD_REQUIRE(K <= 65535 && N <= (int64_t)1 << 31, "size too large (K <= 65535)");
+    HD_REQUIRE(method != HD_NAIVE_OCP || is_e8m0(fmt), "the OCP rule needs a power-of-two (E8M0) scale grid");
+    HD_REQUIRE(damp >= 0.0 && damp < 1e300, "damp must be a finite non-negative number");
+    if (N == 0 || K == 0) return ok();
+    HD_CHECK_PTR(W, true);
+    HD_CHECK_PTR(H, true);
+    HD_CHECK_PTR(codes, true);
+    HD_CHECK_PTR(ws, true);
+    if (scales == nullptr) return fail(HD_ERR_INVALID_ARG, "scales is NULL");
+    if ((uintptr_t)scales & 3u) return fail(HD_ERR_INVALID_ARG, "scales is not 4-byte aligned");
+    if (block_order != nullptr && ((uintptr_t)block_order & 3u)) return fail(HD_ERR_INVALID_ARG, "block_order misaligned");
+    if (info != nullptr && ((uintptr_t)info & 3u)) return fail(HD_ERR_INVALID_ARG, "info misaligned");
+    HD_REQUIRE(ws_bytes >= (size_t)hd::gptq_ws(B, N, K), "workspace too small");
+    return hip_status(hd::launch_gptq(method, fmt, B, W, wt, N, K, H, damp, ordered != 0, codes, scales, block_order,
+                                      info, ws, (hipStream_t)stream),
+                      "gptq_quantize");
+}
+
 }  // extern "C"
 
 namespace hd {

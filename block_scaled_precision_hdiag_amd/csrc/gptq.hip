@@ -1,0 +1,733 @@
+// gptq.hip - GPTQ on top of a scale choice (qwantize "Results", "GPTQ
+// Quantization": GPTQ of Frantar et al. with the GPTQ block equal to the
+// quantisation block, columns in natural order (GPTQ-Seq) or block columns by
+// descending Hessian-weighted loss (GPTQ-Ord); quantisation-algorithms note,
+// §1: H = X^T X + lambda I, columns quantised in sequence, each residual
+// propagated through H^-1).
+//
+// Pipeline (all on the caller's stream, no host synchronisation):
+//   1. H = X^T X (gptq_hessian): X is transposed into the workspace and the
+//      bf16 MFMA product of output_reference computes Xt Xt^T in float32
+//      (bf16 products are exact; the sums carry float32 accumulation).
+//   2. h = diag(H), lambda = damp * mean(h) (1 if the mean is 0).
+//   3. GPTQ-Ord only: the method's own scales on W, the h-weighted loss of
+//      every block column in float64 (fixed summation order), and the
+//      processing order by descending loss (ties: lower block first).
+//   4. P = J (Hp + lambda I) J, Hp = H with rows and columns in processing
+//      order and J the reversal, in float64; a recursive Cholesky gives
+//      L^-1 for P = L L^T directly (leaves of 64 x 64 factored and inverted
+//      in LDS; above them L21 = P21 L11^-T, S22 = P22 - L21 L21^T,
+//      (L^-1)21 = -(L22^-1) L21 (L11^-1), all float64 GEMMs).  Then
+//      (Hp + lambda I)^-1 = U^T U with U = J L^-1 J (upper triangular), and the
+//      loop uses V[c][k] = U[c][k] / U[c][c] in float32.
+//   5. The column loop over panels of BL = 128 (256 for B = 256) columns:
+//      gptq_panel_kernel walks a panel for 16 rows per workgroup (16 lanes per
+//      row, each holding BL / 16 working values in registers): at each
+//      quantisation block it picks every row's scale with the method from the
+//      current values (the full-grid argmin with the lanes splitting the
+//      candidates, or the FP16 alternation), then encodes the block's columns
+//      one by one, broadcasting each error e = w - q to the row's lanes, which
+//      apply w_k -= e V[c][k] inside the panel; gptq_trail_kernel then applies
+//      the panel's errors to every later column (an fp32 tiled GEMM).
+// Codes and scales are written at the original column / block positions.
+#include <algorithm>
+
+#include "encode.hpp"
+#include "kernels.hpp"
+
+namespace hd {
+
+// --------------------------------------------------------------- helpers ---
+
+// Xt[k][m] = X[m][k] for m < M, 0 for M <= m < M8 (bf16 bits).
+__global__ __launch_bounds__(256) void gptq_transpose_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t K,
+                                                             int64_t M8, uint16_t *__restrict__ Xt)
+{
+    __shared__ uint16_t t[64][66];
+    const int64_t m0 = (int64_t)blockIdx.y * 64, k0 = (int64_t)blockIdx.x * 64;
+    const int tx = threadIdx.x % 64, ty = threadIdx.x / 64;
+    for (int r = ty; r < 64; r += 4) {
+        const int64_t m = m0 + r, k = k0 + tx;
+        t[r][tx] = (m < M && k < K) ? X[m * K + k] : (uint16_t)0;
+    }
+    __syncthreads();
+    for (int r = ty; r < 64; r += 4) {
+        const int64_t k = k0 + r, m = m0 + tx;
+        if (k < K && m < M8) Xt[k * M8 + m] = t[tx][r];
+    }
+}
+
+// h[k] = H[k][k]; stat[0] = lambda (damp * mean(h), or 1 when it is 0).
+__global__ __launch_bounds__(256) void gptq_diag_kernel(const float *__restrict__ H, int64_t K, double damp,
+                                                        float *__restrict__ h, double *__restrict__ stat)
+{
+    __shared__ double red[256];
+    double s = 0.0;
+    for (int64_t k = threadIdx.x; k < K; k += 256) {
+        const float v = H[k * K + k];
+        h[k] = v;
+        s += (double)v;
+    }
+    red[threadIdx.x] = s;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+        if ((int)threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        const double mean = red[0] / (double)K;
+        stat[0] = mean > 0.0 ? damp * mean : 1.0;
+    }
+}
+
+// Hessian-weighted loss of block column b: sum over rows of
+// sum_j h_j (|w| - fl32(s q))^2 at the given scales, in float64; each block's
+// sum runs j in order and the rows are reduced in a fixed tree, so the result
+// does not depend on scheduling.
+template <int EK, int SK, typename T>
+__global__ __launch_bounds__(256) void gptq_block_loss_kernel(const T *__restrict__ W, int64_t N, int64_t K, int B,
+                                                              const float *__restrict__ h,
+                                                              const uint8_t *__restrict__ scales,
+                                                              double *__restrict__ loss)
+{
+    __shared__ double red[256];
+    const int64_t b = blockIdx.x, nb = K / B;
+    double acc = 0.0;
+    for (int64_t n = threadIdx.x; n < N; n += 256) {
+        const int code = load_scale<SK>(scales, n * nb + b);
+        const float s = scale_code_valid(SK, code) ? scale_value(SK, code) : 0.0f;
+        const float r = s != 0.0f ? 1.0f / s : 0.0f;
+        double o = 0.0;
+        for (int j = 0; j < B; ++j) {
+            const int64_t e = n * K + b * B + j;
+            const float a = fabsf(sizeof(T) == 2 ? __uint_as_float((uint32_t)((const uint16_t *)W)[e] << 16)
+                                                 : ((const float *)W)[e]);
+            const float x = s != 0.0f ? quotient<SK, false>(a, s, r) : 0.0f;
+            const float wq = s * round_elem<EK>(x);
+            const double d = (double)a - (double)wq;
+            o += (double)h[b * B + j] * (d * d);
+        }
+        acc += o;
+    }
+    red[threadIdx.x] = acc;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+        if ((int)threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) loss[b] = red[0];
+}
+
+// Processing order: slot of block b = number of blocks that go before it
+// (larger loss, or equal loss and lower index); perm[slot] = b (also into
+// order_out when given).  Also clears the factorisation's info word.
+__global__ __launch_bounds__(256) void gptq_rank_kernel(const double *__restrict__ loss, int64_t nb, int ordered,
+                                                        int *__restrict__ perm, int32_t *__restrict__ order_out,
+                                                        int *__restrict__ info)
+{
+    if (threadIdx.x == 0) info[0] = 0;
+    for (int64_t b = threadIdx.x; b < nb; b += 256) {
+        int64_t slot = b;
+        if (ordered) {
+            slot = 0;
+            const double lb = loss[b];
+            for (int64_t o = 0; o < nb; ++o) slot += (loss[o] > lb || (loss[o] == lb && o < b)) ? 1 : 0;
+        }
+        perm[slot] = (int)b;
+        if (order_out) order_out[slot] = (int32_t)b;
+    }
+}
+
+// Processing-order maps: col[i] = original column of processed column i,
+// hp[i] = h[col[i]]; Wp[n][i] = W[n][col[i]] as float32.
+template <typename T>
+__global__ __launch_bounds__(256) void gptq_gather_kernel(const T *__restrict__ W, int64_t N, int64_t K, int B,
+                                                          const int *__restrict__ perm, const float *__restrict__ h,
+                                                          int *__restrict__ col, float *__restrict__ hp,
+                                                          float *__restrict__ Wp)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= K) return;
+    const int64_t c = (int64_t)perm[i / B] * B + i % B;
+    if (blockIdx.y == 0) {
+        col[i] = (int)c;
+        hp[i] = h[c];
+    }
+    for (int64_t n = blockIdx.y; n < N; n += gridDim.y) {
+        const int64_t e = n * K + c;
+        Wp[n * K + i] = sizeof(T) == 2 ? __uint_as_float((uint32_t)((const uint16_t *)W)[e] << 16)
+                                       : ((const float *)W)[e];
+    }
+}
+
+// P[i][j] = Hp[K-1-i][K-1-j] + lambda [i == j] (float64): the reversed,
+// permuted, damped Hessian.
+__global__ __launch_bounds__(256) void gptq_build_p_kernel(const float *__restrict__ H, int64_t K,
+                                                           const int *__restrict__ col,
+                                                           const double *__restrict__ stat, double *__restrict__ P)
+{
+    const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x, i = blockIdx.y;
+    if (j >= K) return;
+    const int64_t ci = col[K - 1 - i], cj = col[K - 1 - j];
+    double v = (double)H[ci * K + cj];
+    if (i == j) v += stat[0];
+    P[i * K + j] = v;
+}
+
+// V[c][k] = U[c][k] / U[c][c] for k > c, U[c][k] = Li[K-1-c][K-1-k] (float32).
+__global__ __launch_bounds__(256) void gptq_build_v_kernel(const double *__restrict__ Li, int64_t K,
+                                                           float *__restrict__ V)
+{
+    const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x, c = blockIdx.y;
+    if (k >= K) return;
+    const int64_t rc = K - 1 - c;
+    V[c * K + k] = k > c ? (float)(Li[rc * K + (K - 1 - k)] / Li[rc * K + rc]) : 0.0f;
+}
+
+// ---------------------------------------------- float64 factorisation ---
+
+// Leaf: L = chol(P block), n <= 64, then Li = L^-1 (lower); only Li is kept.
+// info[0] gets the first non-positive pivot's global index + 1 (the pivot is
+// then replaced by 1 so the factorisation still finishes).
+__global__ __launch_bounds__(256) void gptq_chol_leaf_kernel(const double *__restrict__ P, int64_t ld, int64_t off,
+                                                             int n, double *__restrict__ Li, int *__restrict__ info)
+{
+    __shared__ double a[64][65];
+    __shared__ double li[64][65];
+    const int tid = threadIdx.x;
+    for (int e = tid; e < 64 * 64; e += 256) {
+        const int i = e / 64, j = e % 64;
+        a[i][j] = (i < n && j <= i) ? P[(off + i) * ld + off + j] : 0.0;
+        li[i][j] = 0.0;
+    }
+    __syncthreads();
+    for (int j = 0; j < n; ++j) {
+        if (tid == 0) {
+            double d = a[j][j];
+            if (!(d > 0.0)) {
+                if (info) atomicCAS(info, 0, (int)(off + j + 1));
+                d = 1.0;
+            }
+            a[j][j] = sqrt(d);
+        }
+        __syncthreads();
+        for (int i = j + 1 + tid; i < n; i += 256) a[i][j] /= a[j][j];
+        __syncthreads();
+        for (int e = tid; e < 64 * 64; e += 256) {
+            const int i = e / 64, k = e % 64;
+            if (k > j && i >= k && i < n) a[i][k] -= a[i][j] * a[k][j];
+        }
+        __syncthreads();
+    }
+    // columns of L^-1 are independent: forward substitution per column
+    if (tid < n) {
+        const int c = tid;
+        li[c][c] = 1.0 / a[c][c];
+        for (int i = c + 1; i < n; ++i) {
+            double v = 0.0;
+            for (int k = c; k < i; ++k) v += a[i][k] * li[k][c];
+            li[i][c] = -v / a[i][i];
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e < 64 * 64; e += 256) {
+        const int i = e / 64, j = e % 64;
+        if (i < n && j < n) Li[(off + i) * ld + off + j] = j <= i ? li[i][j] : 0.0;
+    }
+}
+
+// C[m][n] = alpha sum_k A[m][k] Bop[k][n] + beta C[m][n] in float64 (row-major,
+// leading dimensions lda / ldb / ldc; Bop = B or, with TB, B^T).  64 x 64
+// output tile per workgroup, 4 x 4 per thread, k in steps of 16 through LDS.
+template <bool TB>
+__global__ __launch_bounds__(256) void gptq_dgemm_kernel(int64_t M, int64_t N, int64_t K, double alpha,
+                                                         const double *__restrict__ A, int64_t lda,
+                                                         const double *__restrict__ Bm, int64_t ldb, double beta,
+                                                         double *__restrict__ C, int64_t ldc)
+{
+    __shared__ double As[16][64 + 1];
+    __shared__ double Bs[16][64 + 1];
+    const int tid = threadIdx.x, tx = tid % 16, ty = tid / 16;
+    const int64_t m0 = (int64_t)blockIdx.y * 64, n0 = (int64_t)blockIdx.x * 64;
+    double acc[4][4] = {};
+    for (int64_t k0 = 0; k0 < K; k0 += 16) {
+        for (int e = tid; e < 64 * 16; e += 256) {
+            const int mm = e / 16, kk = e % 16;
+            const int64_t m = m0 + mm, k = k0 + kk;
+            As[kk][mm] = (m < M && k < K) ? A[m * lda + k] : 0.0;
+            int nn, kb;
+            if (TB) { nn = e / 16; kb = e % 16; } else { kb = e / 64; nn = e % 64; }
+            const int64_t n = n0 + nn, kq = k0 + kb;
+            Bs[kb][nn] = (n < N && kq < K) ? (TB ? Bm[n * ldb + kq] : Bm[kq * ldb + n]) : 0.0;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) {
+            double av[4], bv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) av[i] = As[kk][ty + 16 * i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) bv[j] = Bs[kk][tx + 16 * j];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fma(av[i], bv[j], acc[i][j]);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t m = m0 + ty + 16 * i;
+        if (m >= M) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t n = n0 + tx + 16 * j;
+            if (n >= N) continue;
+            double *c = C + m * ldc + n;
+            *c = beta == 0.0 ? alpha * acc[i][j] : beta * *c + alpha * acc[i][j];
+        }
+    }
+}
+
+template <bool TB>
+static void dgemm(int64_t M, int64_t N, int64_t K, double alpha, const double *A, int64_t lda, const double *Bm,
+                  int64_t ldb, double beta, double *C, int64_t ldc, hipStream_t st)
+{
+    if (M <= 0 || N <= 0) return;
+    const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 63) / 64));
+    gptq_dgemm_kernel<TB><<<grid, 256, 0, st>>>(M, N, K, alpha, A, lda, Bm, ldb, beta, C, ldc);
+}
+
+// Recursive Cholesky-with-inverse of the n x n diagonal block of P at `off`
+// (row-major, leading dimension ld): writes L^-1 of that block into Li
+// (same position).  P's trailing block is overwritten by its Schur
+// complement.  T (>= (n/2)^2 doubles, free on entry) holds L21; T2 is a stack
+// of temporaries that must survive the recursive calls.
+static void cholinv(double *P, double *Li, int64_t ld, int64_t off, int64_t n, double *T, double *T2, int *info,
+                    hipStream_t st)
+{
+    if (n <= 64) {
+        gptq_chol_leaf_kernel<<<1, 256, 0, st>>>(P, ld, off, (int)n, Li, info);
+        return;
+    }
+    const int64_t n1 = ((n / 2 + 63) / 64) * 64, n2 = n - n1;
+    double *P11 = P + off * ld + off, *P21 = P11 + n1 * ld, *P22 = P21 + n1;
+    double *Li11 = Li + off * ld + off, *Li21 = Li11 + n1 * ld, *Li22 = Li21 + n1;
+    cholinv(P, Li, ld, off, n1, T, T2, info, st);
+    // L21 = P21 L11^-T  (T: n2 x n1)
+    dgemm<true>(n2, n1, n1, 1.0, P21, ld, Li11, ld, 0.0, T, n1, st);
+    // S22 = P22 - L21 L21^T
+    dgemm<true>(n2, n2, n1, -1.0, T, n1, T, n1, 1.0, P22, ld, st);
+    // L21 L11^-1 (T2: n2 x n1), kept across the recursion on S22
+    double *Tm = T2;
+    dgemm<false>(n2, n1, n1, 1.0, T, n1, Li11, ld, 0.0, Tm, n1, st);
+    cholinv(P, Li, ld, off + n1, n2, T, T2 + n2 * n1, info, st);
+    // (L^-1)21 = -L22^-1 (L21 L11^-1)
+    dgemm<false>(n2, n1, n2, -1.0, Li22, ld, Tm, n1, 0.0, Li21, ld, st);
+}
+
+// ------------------------------------------------------- column loop ---
+
+enum { GQ_NAIVE = 0, GQ_GRID = 1, GQ_ALT = 2 };
+
+// Objective of one block (values v[0..B-1] in LDS, fp32) at scale s:
+// sum_j om_j (|v_j| - fl32(s q_j))^2 in float64, j in order - the oracle's
+// block objective, operation for operation.
+template <int EK, int SK, bool WEIGHTED>
+__device__ __forceinline__ double gq_objective(const float *v, const float *om, int B, float s, float r)
+{
+    double o = 0.0;
+    for (int j = 0; j < B; ++j) {
+        const float a = fabsf(v[j]);
+        const float x = s != 0.0f ? quotient<SK, false>(a, s, r) : 0.0f;
+        const float wq = s * round_elem<EK>(x);
+        const double d = (double)a - (double)wq;
+        o += (WEIGHTED ? (double)om[j] : 1.0) * (d * d);
+    }
+    return o;
+}
+
+// The FP16 alternation of alt_f16.hip for one block held in LDS, run by one
+// lane with every sum in element order.
+template <int EK, bool WEIGHTED>
+__device__ int gq_alternation(const float *v, const float *om, int B)
+{
+    float amax = 0.0f;
+    for (int j = 0; j < B; ++j) amax = fmaxf(amax, fabsf(v[j]));
+    int code = naive_code<EK, SCALE_F16>(amax), best_code = code;
+    float s = scale_value(SCALE_F16, code);
+    double best = gq_objective<EK, SCALE_F16, WEIGHTED>(v, om, B, s, s != 0.0f ? 1.0f / s : 0.0f);
+    for (int round = 0; round < 32 && code != 0; ++round) {
+        const float r = 1.0f / s;
+        double num = 0.0, den = 0.0;
+        for (int j = 0; j < B; ++j) {
+            const float a = fabsf(v[j]);
+            const float y = round_elem<EK>(quotient<SCALE_F16, false>(a, s, r));
+            const double o = WEIGHTED ? (double)om[j] : 1.0;
+            num += (o * (double)a) * (double)y;
+            den += (o * (double)y) * (double)y;
+        }
+        if (den == 0.0) break;
+        const int next = f16_round_code(num / den);
+        if (next == code) break;
+        code = next;
+        s = scale_value(SCALE_F16, code);
+        const double obj = gq_objective<EK, SCALE_F16, WEIGHTED>(v, om, B, s, s != 0.0f ? 1.0f / s : 0.0f);
+        if (obj < best) {
+            best = obj;
+            best_code = code;
+        }
+    }
+    return best_code;
+}
+
+// One panel [p0, p0 + 16 SEGP) of the column loop for 16 rows per workgroup.
+template <int EK, int SK, int KIND, bool WEIGHTED, int SEGP>
+__global__ __launch_bounds__(256) void gptq_panel_kernel(float *__restrict__ Wp, const float *__restrict__ V,
+                                                         const float *__restrict__ hp, const int *__restrict__ col,
+                                                         int64_t N, int64_t K, int B, int64_t p0, int ocp,
+                                                         uint8_t *__restrict__ codes, uint8_t *__restrict__ scales,
+                                                         float *__restrict__ E)
+{
+    constexpr int BL = 16 * SEGP;
+    __shared__ float blk[16][256 + 4];
+    __shared__ float oms[256];
+    const int tid = threadIdx.x, r = tid / 16, l = tid % 16;
+    const int64_t n = (int64_t)blockIdx.x * 16 + r;
+    const bool active = n < N;
+    const int64_t pe = min(p0 + BL, K);
+    const int64_t nb = K / B;
+    const int lane0 = (tid & 63) - l;  // the row's first lane within the wave
+
+    float w[SEGP];
+#pragma unroll
+    for (int i = 0; i < SEGP; ++i) {
+        const int64_t c = p0 + l * SEGP + i;
+        w[i] = (active && c < pe) ? Wp[n * K + c] : 0.0f;
+    }
+    for (int64_t cs = p0; cs < pe; cs += B) {
+        // the block's current values, and its h
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < SEGP; ++i) {
+            const int64_t c = p0 + l * SEGP + i;
+            if (c >= cs && c < cs + B) blk[r][c - cs] = w[i];
+        }
+        if (WEIGHTED)
+            for (int j = tid; j < B; j += 256) oms[j] = hp[cs + j];
+        __syncthreads();
+        const float *v = blk[r];
+        int code;
+        if (KIND == GQ_NAIVE) {
+            float amax = 0.0f;
+            for (int j = l; j < B; j += 16) amax = fmaxf(amax, fabsf(v[j]));
+            amax = group_max<16>(amax);
+            if constexpr (SK == SCALE_E8M0)
+                code = ocp ? ocp_code<EK>(amax) : naive_code<EK, SK>(amax);
+            else
+                code = naive_code<EK, SK>(amax);
+        } else if (KIND == GQ_ALT) {
+            code = l == 0 ? gq_alternation<EK, WEIGHTED>(v, oms, B) : 0;
+            code = __shfl(code, lane0, 64);
+        } else {
+            // full-grid argmin: lane l takes candidates c0 + l, c0 + l + 16, ...
+            constexpr int C0 = cand_first(SK), C1 = cand_last(SK);
+            double best = __builtin_huge_val();
+            int bc = C1 + 1;
+            for (int c = C0 + l; c <= C1; c += 16) {
+                const float s = scale_value(SK, c);
+                const double o = gq_objective<EK, SK, WEIGHTED>(v, oms, B, s, 1.0f / s);
+                if (o < best) {
+                    best = o;
+                    bc = c;
+                }
+            }
+            // lexicographic (objective, code) minimum over the row's 16 lanes
+#pragma unroll
+            for (int m = 1; m < 16; m <<= 1) {
+                const double ob = __shfl_xor(best, m, 64);
+                const int oc = __shfl_xor(bc, m, 64);
+                if (ob < best || (ob == best && oc < bc)) {
+                    best = ob;
+                    bc = oc;
+                }
+            }
+            code = bc;
+        }
+        const float s = scale_value(SK, code);
+        const float rs = s != 0.0f ? 1.0f / s : 0.0f;
+        if (active && l == 0) store_scale<SK>(scales, n * nb + col[cs] / B, code);
+        // encode the block's columns in order; each error goes to the later
+        // columns of the panel held by the row's lanes
+        uint32_t lo = 0;
+        for (int64_t c = cs; c < cs + B; ++c) {
+            const int own = (int)((c - p0) / SEGP), slot = (int)((c - p0) % SEGP);
+            float e = 0.0f;
+            if (l == own) {
+                float wv = 0.0f;
+#pragma unroll
+                for (int i = 0; i < SEGP; ++i)
+                    if (i == slot) wv = w[i];
+                const float a = fabsf(wv);
+                const float x = s != 0.0f ? quotient<SK, false>(a, s, rs) : 0.0f;
+                const float y = round_elem<EK>(x);
+                const float wq = s * y;
+                e = wv - (__builtin_signbitf(wv) ? -wq : wq);
+                const uint32_t cd = elem_code<EK>(elem_index<EK>(y), __builtin_signbitf(wv) != 0);
+                if (active) {
+                    E[n * BL + (c - p0)] = e;
+                    const int64_t oc = col[c];
+                    if (elem_4bit(EK)) {
+                        if ((c & 1) == 0)
+                            lo = cd & 15u;
+                        else
+                            codes[n * (K / 2) + oc / 2] = (uint8_t)(lo | ((cd & 15u) << 4));
+                    } else {
+                        codes[n * K + oc] = (uint8_t)cd;
+                    }
+                }
+            }
+            e = __shfl(e, lane0 + own, 64);
+            const float *vr = V + c * K;
+#pragma unroll
+            for (int i = 0; i < SEGP; ++i) {
+                const int64_t k = p0 + l * SEGP + i;
+                if (k > c && k < pe) w[i] = __builtin_fmaf(-e, vr[k], w[i]);
+            }
+        }
+    }
+}
+
+// Wp[n][k] -= sum_{c in panel} E[n][c - p0] V[c][k] for k >= pe (float32):
+// 64 x 64 output tiles, 4 x 4 per thread, the panel in steps of 16 via LDS.
+__global__ __launch_bounds__(256) void gptq_trail_kernel(float *__restrict__ Wp, const float *__restrict__ V,
+                                                         const float *__restrict__ E, int64_t N, int64_t K,
+                                                         int64_t p0, int BL, int64_t pe)
+{
+    __shared__ float Es[16][64 + 1];
+    __shared__ float Vs[16][64 + 1];
+    const int tid = threadIdx.x, tx = tid % 16, ty = tid / 16;
+    const int64_t m0 = (int64_t)blockIdx.y * 64, k0 = pe + (int64_t)blockIdx.x * 64;
+    float acc[4][4] = {};
+    for (int q0 = 0; q0 < BL; q0 += 16) {
+        for (int e = tid; e < 64 * 16; e += 256) {
+            const int mm = e / 16, qq = e % 16;
+            const int64_t m = m0 + mm;
+            Es[qq][mm] = m < N ? E[m * BL + q0 + qq] : 0.0f;
+            const int qv = e / 64, kk = e % 64;
+            const int64_t k = k0 + kk;
+            Vs[qv][kk] = k < K ? V[(p0 + q0 + qv) * K + k] : 0.0f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int qq = 0; qq < 16; ++qq) {
+            float av[4], bv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) av[i] = Es[qq][ty + 16 * i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) bv[j] = Vs[qq][tx + 16 * j];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(av[i], bv[j], acc[i][j]);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t m = m0 + ty + 16 * i;
+        if (m >= N) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t k = k0 + tx + 16 * j;
+            if (k < K) Wp[m * K + k] -= acc[i][j];
+        }
+    }
+}
+
+// ------------------------------------------------------------ launchers ---
+
+static int64_t al256(int64_t x) { return (x + 255) / 256 * 256; }
+
+int64_t gptq_hessian_ws(int64_t M, int64_t K)
+{
+    const int64_t M8 = (M + 7) / 8 * 8;
+    return al256(K * M8 * 2) + al256(output_gemm_parts_bytes(K, K));
+}
+
+__global__ __launch_bounds__(256) void gptq_zero_kernel(float *__restrict__ p, int64_t n)
+{
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.0f;
+}
+
+hipError_t launch_gptq_hessian(const void *X, int64_t M, int64_t K, float *H, void *ws, hipStream_t st)
+{
+    const int64_t M8 = (M + 7) / 8 * 8;
+    if (M8 == 0) {  // no rows: H = 0
+        gptq_zero_kernel<<<1024, 256, 0, st>>>(H, K * K);
+        return hipGetLastError();
+    }
+    uint16_t *Xt = static_cast<uint16_t *>(ws);
+    double *part = reinterpret_cast<double *>(static_cast<char *>(ws) + al256(K * M8 * 2));
+    const dim3 tg((unsigned)((K + 63) / 64), (unsigned)((M8 + 63) / 64));
+    gptq_transpose_kernel<<<tg, 256, 0, st>>>(static_cast<const uint16_t *>(X), M, K, M8, Xt);
+    return launch_gemm_store(Xt, Xt, K, K, M8, H, part, st);
+}
+
+// Workspace of launch_gptq (bytes), carved in this order.
+struct GqLayout {
+    int64_t P, Li, T, T2, V, Wp, E, h, hp, col, perm, loss, stat, info, sc, bytes;
+};
+static GqLayout gq_layout(int B, int64_t N, int64_t K)
+{
+    GqLayout L;
+    const int64_t nb = K / B, BL = B > 128 ? 256 : 128, h1 = (K / 2 + 63) / 64 * 64;
+    int64_t o = 0;
+    L.P = o; o += al256(K * K * 8);
+    L.Li = o; o += al256(K * K * 8);
+    L.T = o; o += al256(h1 * h1 * 8);
+    L.T2 = o; o += al256(K * K * 8 / 2);
+    L.V = o; o += al256(K * K * 4);
+    L.Wp = o; o += al256(N * K * 4);
+    L.E = o; o += al256(N * BL * 4);
+    L.h = o; o += al256(K * 4);
+    L.hp = o; o += al256(K * 4);
+    L.col = o; o += al256(K * 4);
+    L.perm = o; o += al256(nb * 4);
+    L.loss = o; o += al256(nb * 8);
+    L.stat = o; o += 256;
+    L.info = o; o += 256;
+    L.sc = o; o += al256(N * nb * 2);
+    L.bytes = o;
+    return L;
+}
+int64_t gptq_ws(int B, int64_t N, int64_t K) { return gq_layout(B, N, K).bytes; }
+
+template <int EK, int SK, int KIND, bool WEIGHTED>
+static void gq_panel(float *Wp, const float *V, const float *hp, const int *col, int64_t N, int64_t K, int B,
+                     int64_t p0, int ocp, uint8_t *codes, uint8_t *scales, float *E, hipStream_t st)
+{
+    const unsigned g = (unsigned)((N + 15) / 16);
+    if (B > 128)
+        gptq_panel_kernel<EK, SK, KIND, WEIGHTED, 16><<<g, 256, 0, st>>>(Wp, V, hp, col, N, K, B, p0, ocp, codes,
+                                                                          scales, E);
+    else
+        gptq_panel_kernel<EK, SK, KIND, WEIGHTED, 8><<<g, 256, 0, st>>>(Wp, V, hp, col, N, K, B, p0, ocp, codes,
+                                                                         scales, E);
+}
+
+template <int EK, int SK>
+static void gq_panel_m(int method, float *Wp, const float *V, const float *hp, const int *col, int64_t N, int64_t K,
+                       int B, int64_t p0, uint8_t *codes, uint8_t *scales, float *E, hipStream_t st)
+{
+    if (method == HD_NAIVE || method == HD_NAIVE_OCP) {
+        gq_panel<EK, SK, GQ_NAIVE, false>(Wp, V, hp, col, N, K, B, p0, method == HD_NAIVE_OCP, codes, scales, E,
+                                          st);
+        return;
+    }
+    constexpr int KIND = SK == SCALE_F16 ? GQ_ALT : GQ_GRID;
+    if (method == HD_H_OPT)
+        gq_panel<EK, SK, KIND, true>(Wp, V, hp, col, N, K, B, p0, 0, codes, scales, E, st);
+    else
+        gq_panel<EK, SK, KIND, false>(Wp, V, hp, col, N, K, B, p0, 0, codes, scales, E, st);
+}
+
+template <int EK, int SK>
+static void gq_loss(const void *W, int wdt, int64_t N, int64_t K, int B, const float *h, const uint8_t *sc,
+                    double *loss, hipStream_t st)
+{
+    const unsigned nb = (unsigned)(K / B);
+    if (wdt == HD_BF16)
+        gptq_block_loss_kernel<EK, SK, uint16_t><<<nb, 256, 0, st>>>(static_cast<const uint16_t *>(W), N, K, B, h,
+                                                                     sc, loss);
+    else
+        gptq_block_loss_kernel<EK, SK, float><<<nb, 256, 0, st>>>(static_cast<const float *>(W), N, K, B, h, sc,
+                                                                  loss);
+}
+
+template <int EK, int SK>
+static hipError_t gq_run(int method, int B, const void *W, int wdt, int64_t N, int64_t K, const float *H, double damp,
+                         int ordered, uint8_t *codes, uint8_t *scales, int32_t *block_order, int *info_out, void *ws,
+                         int fmt, hipStream_t st)
+{
+    const GqLayout L = gq_layout(B, N, K);
+    char *base = static_cast<char *>(ws);
+    double *P = reinterpret_cast<double *>(base + L.P), *Li = reinterpret_cast<double *>(base + L.Li);
+    double *T = reinterpret_cast<double *>(base + L.T), *T2 = reinterpret_cast<double *>(base + L.T2);
+    float *V = reinterpret_cast<float *>(base + L.V), *Wp = reinterpret_cast<float *>(base + L.Wp);
+    float *E = reinterpret_cast<float *>(base + L.E), *h = reinterpret_cast<float *>(base + L.h);
+    float *hp = reinterpret_cast<float *>(base + L.hp);
+    int *col = reinterpret_cast<int *>(base + L.col), *perm = reinterpret_cast<int *>(base + L.perm);
+    double *loss = reinterpret_cast<double *>(base + L.loss), *stat = reinterpret_cast<double *>(base + L.stat);
+    int *info = info_out ? info_out : reinterpret_cast<int *>(base + L.info);
+    uint8_t *sc = reinterpret_cast<uint8_t *>(base + L.sc);
+    const int64_t nb = K / B;
+
+    gptq_diag_kernel<<<1, 256, 0, st>>>(H, K, damp, h, stat);
+    hipError_t e = hipSuccess;
+    if (ordered) {
+        // the method's own scales on W, then the h-weighted loss per block column
+        const float *hh = method == HD_H_OPT ? h : nullptr;
+        if (method == HD_NAIVE || method == HD_NAIVE_OCP)
+            e = launch_encode(fmt, B, W, wdt, N, K, nullptr, nullptr, codes, sc, nullptr, method == HD_NAIVE_OCP,
+                              st);
+        else if (SK == SCALE_F16)
+            e = launch_alt_f16(fmt, B, W, wdt, N, K, hh, codes, sc, nullptr, st);
+        else
+            e = launch_search(fmt, B, W, wdt, N, K, hh, codes, sc, nullptr, st);
+        if (e != hipSuccess) return e;
+        gq_loss<EK, SK>(W, wdt, N, K, B, h, sc, loss, st);
+    }
+    gptq_rank_kernel<<<1, 256, 0, st>>>(loss, nb, ordered, perm, block_order, info);
+    {
+        const dim3 g((unsigned)((K + 255) / 256), (unsigned)std::min<int64_t>(N > 0 ? N : 1, 4096));
+        if (wdt == HD_BF16)
+            gptq_gather_kernel<uint16_t><<<g, 256, 0, st>>>(static_cast<const uint16_t *>(W), N, K, B, perm, h, col,
+                                                            hp, Wp);
+        else
+            gptq_gather_kernel<float><<<g, 256, 0, st>>>(static_cast<const float *>(W), N, K, B, perm, h, col, hp,
+                                                         Wp);
+    }
+    gptq_build_p_kernel<<<dim3((unsigned)((K + 255) / 256), (unsigned)K), 256, 0, st>>>(H, K, col, stat, P);
+    // the recursion multiplies by whole diagonal blocks of L^-1, whose upper
+    // off-diagonal parts it never writes: they must read as zero
+    gptq_zero_kernel<<<2048, 256, 0, st>>>(reinterpret_cast<float *>(Li), 2 * K * K);
+    cholinv(P, Li, K, 0, K, T, T2, info, st);
+    gptq_build_v_kernel<<<dim3((unsigned)((K + 255) / 256), (unsigned)K), 256, 0, st>>>(Li, K, V);
+    const int BL = B > 128 ? 256 : 128;
+    for (int64_t p0 = 0; p0 < K; p0 += BL) {
+        const int64_t pe = std::min<int64_t>(p0 + BL, K);
+        gq_panel_m<EK, SK>(method, Wp, V, hp, col, N, K, B, p0, codes, scales, E, st);
+        if (pe < K) {
+            const dim3 g((unsigned)((K - pe + 63) / 64), (unsigned)((N + 63) / 64));
+            gptq_trail_kernel<<<g, 256, 0, st>>>(Wp, V, E, N, K, p0, (int)(pe - p0), pe);
+        }
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_gptq(int method, int fmt, int B, const void *W, int wdt, int64_t N, int64_t K, const float *H,
+                       double damp, int ordered, uint8_t *codes, uint8_t *scales, int32_t *block_order, int *info,
+                       void *ws, hipStream_t st)
+{
+#define HD_GQ_FMT(F)                                                                                          \
+    case F:                                                                                                   \
+        return gq_run<elem_kind(F), scale_kind(F)>(method, B, W, wdt, N, K, H, damp, ordered, codes, scales, \
+                                                   block_order, info, ws, F, st);
+    switch (fmt) {
+        HD_GQ_FMT(HD_INT8_E4M3)
+        HD_GQ_FMT(HD_NVFP4)
+        HD_GQ_FMT(HD_MXFP4)
+        HD_GQ_FMT(HD_MXFP8)
+        HD_GQ_FMT(HD_FP8_E4M3S)
+        HD_GQ_FMT(HD_NVFP4_UE4M4)
+        HD_GQ_FMT(HD_NVFP4_UE5M3)
+        HD_GQ_FMT(HD_NVINT4)
+        HD_GQ_FMT(HD_FP4_F16)
+        HD_GQ_FMT(HD_INT4_F16)
+    }
+#undef HD_GQ_FMT
+    return hipErrorInvalidValue;
+}
+
+}  // namespace hd

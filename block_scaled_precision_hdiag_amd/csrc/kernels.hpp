@@ -71,4 +71,20 @@ hipError_t launch_output_error_codes(int fmt, int B, const void *X, int64_t M, c
                                      const uint8_t *scales, int64_t N, int64_t K, const void *ref, double *out,
                                      double *sums, void *ws, hipStream_t st);
 
+// Y = A B^T (bf16 A [M][K], B [N][K], float32 Y [M][N]) on the MFMA product of
+// outref.hip; part: output_gemm_parts_bytes(M, N) bytes of scratch.
+int64_t output_gemm_parts_bytes(int64_t M, int64_t N);
+hipError_t launch_gemm_store(const uint16_t *A, const uint16_t *Bm, int64_t M, int64_t N, int64_t K, float *Y,
+                             double *part, hipStream_t st);
+
+// GPTQ (gptq.hip): H = X^T X (bf16 X), and the column loop on top of a scale
+// choice; info (device int, may be NULL) gets 1 + the index of the first
+// non-positive pivot of the damped Hessian's factorisation, else 0.
+int64_t gptq_hessian_ws(int64_t M, int64_t K);
+hipError_t launch_gptq_hessian(const void *X, int64_t M, int64_t K, float *H, void *ws, hipStream_t st);
+int64_t gptq_ws(int B, int64_t N, int64_t K);
+hipError_t launch_gptq(int method, int fmt, int B, const void *W, int wdt, int64_t N, int64_t K, const float *H,
+                       double damp, int ordered, uint8_t *codes, uint8_t *scales, int32_t *block_order, int *info,
+                       void *ws, hipStream_t st);
+
 }  // namespace hd

@@ -537,6 +537,16 @@ static hipError_t launch_gemm_err(const uint16_t *A, const uint16_t *Bm, int64_t
     return hipGetLastError();
 }
 
+// Y = A B^T in float32 for 16-bit bf16 operands A [M][K], B [N][K] (K % 8 == 0),
+// with `part` holding ge_parts(M, N) pairs of doubles of scratch.
+int64_t output_gemm_parts_bytes(int64_t M, int64_t N) { return ge_parts(M, N) * 2 * 8; }
+hipError_t launch_gemm_store(const uint16_t *A, const uint16_t *Bm, int64_t M, int64_t N, int64_t K, float *Y,
+                             double *part, hipStream_t st)
+{
+    int64_t np = 0;
+    return launch_gemm_err<false, GE_STORE_Y>(A, Bm, M, N, K, Y, nullptr, 1.0, part, &np, st);
+}
+
 hipError_t launch_output_reference(const void *X, int64_t M, const void *W, int64_t N, int64_t K, void *ref,
                                    hipStream_t st)
 {

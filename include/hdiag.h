@@ -264,6 +264,47 @@ hd_status output_error_codes(hd_format fmt, int32_t B, const void *X, hd_dtype x
                              const void *ref, size_t ref_bytes, double *out, double *sums, void *ws,
                              size_t ws_bytes, void *stream);
 
+/* ----------------------------------------------------------------- GPTQ --- */
+
+/* GPTQ on top of a scale choice (qwantize "Results", "GPTQ Quantization": GPTQ
+ * of Frantar et al. with its block size equal to the quantisation block size;
+ * the quantisation-algorithms note, §1: H = X^T X + lambda I, columns
+ * quantised in sequence with each residual propagated through H^-1).
+ *
+ * gptq_hessian: H = X^T X, float32 [K, K] row-major, for bfloat16 X [M, K]
+ * (products exact, float32 accumulation on the MFMA units).  Workspace:
+ * gptq_hessian_workspace_size(M, K) bytes (X^T is staged there).  Errors:
+ * HD_ERR_UNSUPPORTED for float32 X; HD_ERR_INVALID_ARG for K > 65535, NULL or
+ * misaligned pointers, a short workspace.
+ *
+ * gptq_quantize: codes / scales as quantize_blocks writes them, for W [N, K]
+ * quantised with `method` inside the GPTQ column loop:
+ *   - h_j = H_jj weights H-Optimal; lambda = damp * mean_j H_jj (1 if that mean
+ *     is 0; the usual damp is 0.01) is added to the diagonal;
+ *   - ordered == 0 (GPTQ-Seq): block columns left to right; ordered != 0
+ *     (GPTQ-Ord): by descending Hessian-weighted loss sum_n sum_{j in b}
+ *     h_j (w - q)^2 of the method's own quantisation of W (ties: lower block
+ *     first); block_order (optional, device int32 [K/B]) receives the
+ *     processing order as original block indices;
+ *   - with U the upper Cholesky factor of (H + lambda I)^-1 in processing
+ *     order, each block's scales are chosen by `method` from the block's
+ *     current (compensated) values, then its columns are encoded in order and
+ *     each error (w_c - q_c) / U_cc is subtracted, times U_ck, from every later
+ *     column k (the working weights are float32; the factorisation is
+ *     float64);
+ *   - info (optional, device int32): 0, or 1 + the first pivot at which the
+ *     damped Hessian was not positive definite (that pivot is replaced by 1).
+ * Workspace: gptq_workspace_size(B, N, K) bytes, about 2.6 K^2 doubles +
+ * 1.5 K^2 floats + 4 N K bytes (2 GB for K = 9728).  Errors as
+ * quantize_blocks, plus K > 65535 and a negative or non-finite damp. */
+size_t gptq_hessian_workspace_size(int64_t M, int64_t K);
+hd_status gptq_hessian(const void *X, hd_dtype xt, int64_t M, int64_t K, float *H, void *ws, size_t ws_bytes,
+                       void *stream);
+size_t gptq_workspace_size(int32_t B, int64_t N, int64_t K);
+hd_status gptq_quantize(hd_method method, hd_format fmt, int32_t B, const void *W, hd_dtype wt, int64_t N, int64_t K,
+                        const float *H, double damp, int32_t ordered, uint8_t *codes, uint8_t *scales,
+                        int32_t *block_order, int32_t *info, void *ws, size_t ws_bytes, void *stream);
+
 /* ------------------------------------------------------------ utilities --- */
 
 /* Static description of a status code. */
