@@ -84,7 +84,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=8, help="rows of W in the CPU sample")
-    ap.add_argument("--suite", choices=["headline", "formats"], default="headline",
+    ap.add_argument("--suite", choices=["headline", "formats", "gptq"], default="headline",
                     help="headline: the step above (one JSON line, the default); formats: every element / "
                          "scale format x B in {16, 32} x scale choice on the same W and h (one JSON line)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -112,6 +112,8 @@ def main():
     hd.lib()
     if args.suite == "formats":
         return formats_suite(args, dev)
+    if args.suite == "gptq":
+        return gptq_suite(args, dev)
 
     cfg = synth.CONFIGS[2]
     W_cpu, X_cpu = synth.config_inputs(2)
@@ -334,6 +336,63 @@ def formats_suite(args, dev):
                                              "NVINT4 also 64), the FP16-scale formats at B = 128",
                                  "W": [N, K], "X": [M, K]},
                       "data": "synthetic", "rows": rows}), flush=True)
+
+
+def gptq_suite(args, dev):
+    """GPTQ on the down_proj stand-in (W 2560x9728, X 16384x9728): for NVFP4,
+    MXFP4 and NVINT4 at B = 16 and 32, each of Naive / SSE-Optimal /
+    H-Optimal without GPTQ, with GPTQ-Seq and with GPTQ-Ord: the call's time
+    (HIP events, one warm-up) and the weight / output error of the result.
+    H = X^T X is computed once (its time is reported separately)."""
+    import torch
+
+    import block_scaled_precision_hdiag_amd as hd
+    import synth
+
+    W_cpu, X_cpu = synth.config_inputs(2)
+    N, K = W_cpu.shape
+    M = X_cpu.shape[0]
+    W, X = W_cpu.to(dev), X_cpu.to(dev)
+    ref = hd.output_reference(X, W)
+    ysq = hd.reference_ysq(ref)
+    ws_g = torch.empty(hd.output_error_workspace_size(M, N, K), dtype=torch.uint8, device=dev)
+
+    def timed(f):
+        f()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        r = f()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b), r
+
+    ws_h = torch.empty(hd.gptq_hessian_workspace_size(M, K), dtype=torch.uint8, device=dev)
+    H = torch.empty((K, K), dtype=torch.float32, device=dev)
+    h_ms, _ = timed(lambda: hd.gptq_hessian(X, H=H, workspace=ws_h))
+    h = hd.hdiag(X)
+    names = {v: k for k, v in hd.FORMATS.items()}
+    rows = []
+    for fmt in (hd.NVFP4, hd.MXFP4, hd.NVINT4):
+        for B in (16, 32):
+            ws = torch.empty(hd.gptq_workspace_size(B, N, K), dtype=torch.uint8, device=dev)
+            for mname, m in (("naive", hd.NAIVE), ("sse", hd.SSE_OPT), ("h", hd.H_OPT)):
+                for mode in ("none", "seq", "ord"):
+                    if mode == "none":
+                        ms, (c, sc, _) = timed(lambda: hd.quantize_blocks(m, fmt, B, W, h=h))
+                    else:
+                        ms, (c, sc, _, info) = timed(lambda: hd.gptq_quantize(m, fmt, B, W, H, ordered=mode == "ord",
+                                                                              workspace=ws))
+                        assert int(info.item()) == 0
+                    Wq = hd.dequantize(fmt, B, c, sc, N, K)
+                    rows.append({"format": names[fmt], "B": B, "method": mname, "gptq": mode, "ms": round(ms, 3),
+                                 "weight_error": round(hd.weight_error(W, Wq).item(), 6),
+                                 "output_error": round(hd.output_error_given_ref(X, W, Wq, ysq,
+                                                                                  workspace=ws_g).item(), 6)})
+                    print(json.dumps(rows[-1]), file=sys.stderr, flush=True)
+    print(json.dumps({"suite": "gptq", "config": {"workload": "GPTQ on W 2560x9728 bf16 with H = X^T X from X "
+                                                              "16384x9728 bf16 (synthetic stand-ins)",
+                                                  "W": [N, K], "X": [M, K]},
+                      "hessian_ms": round(h_ms, 3), "data": "synthetic", "rows": rows}), flush=True)
 
 
 def cpu_baseline(W_cpu, X_cpu, blocks, methods, fmt, rows, gpu_value):

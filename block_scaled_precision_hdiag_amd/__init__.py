@@ -291,12 +291,16 @@ def output_error_codes(fmt, B, X, codes, scales, ref, N, K, sums=False, workspac
     return (out, s) if sums else out
 
 
+def gptq_hessian_workspace_size(M, K):
+    return int(lib().gptq_hessian_workspace_size(M, K))
+
+
 def gptq_hessian(X, H=None, workspace=None):
     """H = X^T X (float32 [K, K]) for bfloat16 X [M, K], on the MFMA units."""
     d = _dev(X)
     M, K = X.shape
     H = H if H is not None else torch.empty((K, K), dtype=torch.float32, device=d)
-    need = int(lib().gptq_hessian_workspace_size(M, K))
+    need = gptq_hessian_workspace_size(M, K)
     ws = workspace if workspace is not None else torch.empty(max(need, 16), dtype=torch.uint8, device=d)
     _check(lib().gptq_hessian(_ptr(X), _dt(X), M, K, _ptr(H), _ptr(ws), ws.numel(), _stream(d)), "gptq_hessian")
     return H

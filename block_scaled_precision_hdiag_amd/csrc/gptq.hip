@@ -21,8 +21,8 @@
 //      (Hp + lambda I)^-1 = U^T U with U = J L^-1 J (upper triangular), and the
 //      loop uses V[c][k] = U[c][k] / U[c][c] in float32.
 //   5. The column loop over panels of BL = 128 (256 for B = 256) columns:
-//      gptq_panel_kernel walks a panel for 16 rows per workgroup (16 lanes per
-//      row, each holding BL / 16 working values in registers): at each
+//      gptq_panel_kernel walks a panel with one wave per row (each lane
+//      holding BL / 64 working values in registers): at each
 //      quantisation block it picks every row's scale with the method from the
 //      current values (the full-grid argmin with the lanes splitting the
 //      candidates, or the FP16 alternation), then encodes the block's columns
@@ -187,70 +187,147 @@ __global__ __launch_bounds__(256) void gptq_build_v_kernel(const double *__restr
 // ---------------------------------------------- float64 factorisation ---
 
 // Leaf: L = chol(P block), n <= 64, then Li = L^-1 (lower); only Li is kept.
-// info[0] gets the first non-positive pivot's global index + 1 (the pivot is
-// then replaced by 1 so the factorisation still finishes).
+// Thread t owns the 4 x 4 tile rows 4 (t / 16) .., columns 4 (t % 16) .. of
+// the 64 x 64 block in registers; each step publishes one column (or row)
+// through LDS and every thread updates its tile.  Rows / columns >= n are
+// padded with the identity.  info[0] gets the first non-positive pivot's
+// global index + 1 (the pivot is then replaced by 1 so the factorisation
+// still finishes).
 __global__ __launch_bounds__(256) void gptq_chol_leaf_kernel(const double *__restrict__ P, int64_t ld, int64_t off,
                                                              int n, double *__restrict__ Li, int *__restrict__ info)
 {
-    __shared__ double a[64][65];
-    __shared__ double li[64][65];
-    const int tid = threadIdx.x;
-    for (int e = tid; e < 64 * 64; e += 256) {
-        const int i = e / 64, j = e % 64;
-        a[i][j] = (i < n && j <= i) ? P[(off + i) * ld + off + j] : 0.0;
-        li[i][j] = 0.0;
-    }
-    __syncthreads();
-    for (int j = 0; j < n; ++j) {
-        if (tid == 0) {
-            double d = a[j][j];
+    __shared__ double colv[64];     // the current column of L (or row of X)
+    __shared__ double Ls[64][65];   // L, for the inverse
+    const int tid = threadIdx.x, ti = tid / 16, tk = tid % 16;
+    double a[4][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int i = 4 * ti + u, k = 4 * tk + v;
+            a[u][v] = (i < n && k <= i) ? P[(off + i) * ld + off + k] : (i == k ? 1.0 : 0.0);
+        }
+    // Cholesky: step j scales column j below the pivot by 1 / sqrt(pivot) and
+    // subtracts the outer product from the trailing lower triangle
+    for (int j = 0; j < 64; ++j) {
+        const int tj = j / 4, vj = j % 4;
+        if (tk == tj && ti == tj) {
+            double d = a[vj][vj];
             if (!(d > 0.0)) {
-                if (info) atomicCAS(info, 0, (int)(off + j + 1));
+                if (info && j < n) atomicCAS(info, 0, (int)(off + j + 1));
                 d = 1.0;
             }
-            a[j][j] = sqrt(d);
+            colv[j] = sqrt(d);
         }
         __syncthreads();
-        for (int i = j + 1 + tid; i < n; i += 256) a[i][j] /= a[j][j];
+        const double piv = colv[j];
         __syncthreads();
-        for (int e = tid; e < 64 * 64; e += 256) {
-            const int i = e / 64, k = e % 64;
-            if (k > j && i >= k && i < n) a[i][k] -= a[i][j] * a[k][j];
+        if (tk == tj) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int i = 4 * ti + u;
+                if (i > j) a[u][vj] /= piv;
+                if (i == j) a[u][vj] = piv;
+                if (i >= j) colv[i] = i == j ? 0.0 : a[u][vj];
+            }
+        }
+        if (ti < tj) {
+            // rows above the pivot hold nothing of column j
+        }
+        __syncthreads();
+        if (ti >= tj) {
+            double ci[4], ck[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) ci[u] = 4 * ti + u > j ? colv[4 * ti + u] : 0.0;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) ck[v] = 4 * tk + v > j ? colv[4 * tk + v] : 0.0;
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    if (4 * tk + v > j && 4 * tk + v <= 4 * ti + u) a[u][v] -= ci[u] * ck[v];
         }
         __syncthreads();
     }
-    // columns of L^-1 are independent: forward substitution per column
-    if (tid < n) {
-        const int c = tid;
-        li[c][c] = 1.0 / a[c][c];
-        for (int i = c + 1; i < n; ++i) {
-            double v = 0.0;
-            for (int k = c; k < i; ++k) v += a[i][k] * li[k][c];
-            li[i][c] = -v / a[i][i];
+    // L (lower) to LDS; X = identity tile
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int i = 4 * ti + u, k = 4 * tk + v;
+            Ls[i][k] = k <= i ? a[u][v] : 0.0;
+            a[u][v] = i == k ? 1.0 : 0.0;
         }
-    }
     __syncthreads();
-    for (int e = tid; e < 64 * 64; e += 256) {
-        const int i = e / 64, j = e % 64;
-        if (i < n && j < n) Li[(off + i) * ld + off + j] = j <= i ? li[i][j] : 0.0;
+    // L^-1 by a right-looking solve of L X = I: at step k row k of X is final
+    // once divided by L_kk, and every later row subtracts L_ik times it
+    for (int k = 0; k < 64; ++k) {
+        const int tkk = k / 4, uk = k % 4;
+        if (ti == tkk) {
+            const double rk = 1.0 / Ls[k][k];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                a[uk][v] *= rk;
+                colv[4 * tk + v] = a[uk][v];
+            }
+        }
+        __syncthreads();
+        if (ti >= tkk) {
+            double xr[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) xr[v] = colv[4 * tk + v];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int i = 4 * ti + u;
+                if (i > k) {
+                    const double lik = Ls[i][k];
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) a[u][v] -= lik * xr[v];
+                }
+            }
+        }
+        __syncthreads();
     }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int i = 4 * ti + u, k = 4 * tk + v;
+            if (i < n && k < n) Li[(off + i) * ld + off + k] = k <= i ? a[u][v] : 0.0;
+        }
 }
+
+// Structure flags of the float64 GEMM: operands known to be zero outside a
+// triangle let a tile skip those k, and a symmetric result needs only the
+// tiles that touch its lower triangle.
+enum {
+    TRI_B_KGE_N = 1,  // Bop[k][n] = 0 unless k >= n
+    TRI_B_KLE_N = 2,  // Bop[k][n] = 0 unless k <= n
+    TRI_A_KLE_M = 4,  // A[m][k] = 0 unless k <= m
+    TRI_C_LOWER = 8   // only entries with n <= m are needed
+};
 
 // C[m][n] = alpha sum_k A[m][k] Bop[k][n] + beta C[m][n] in float64 (row-major,
 // leading dimensions lda / ldb / ldc; Bop = B or, with TB, B^T).  64 x 64
-// output tile per workgroup, 4 x 4 per thread, k in steps of 16 through LDS.
+// output tile per workgroup, 4 x 4 per thread, k in steps of 16 through LDS;
+// `tri` (TRI_* flags) limits the k range and the tiles.
 template <bool TB>
 __global__ __launch_bounds__(256) void gptq_dgemm_kernel(int64_t M, int64_t N, int64_t K, double alpha,
                                                          const double *__restrict__ A, int64_t lda,
                                                          const double *__restrict__ Bm, int64_t ldb, double beta,
-                                                         double *__restrict__ C, int64_t ldc)
+                                                         double *__restrict__ C, int64_t ldc, int tri)
 {
     __shared__ double As[16][64 + 1];
     __shared__ double Bs[16][64 + 1];
     const int tid = threadIdx.x, tx = tid % 16, ty = tid / 16;
     const int64_t m0 = (int64_t)blockIdx.y * 64, n0 = (int64_t)blockIdx.x * 64;
+    if ((tri & TRI_C_LOWER) && n0 > m0 + 63) return;
+    int64_t kb = 0, ke = K;
+    if (tri & TRI_B_KGE_N) kb = n0;
+    if (tri & TRI_B_KLE_N) ke = min(ke, n0 + 64);
+    if (tri & TRI_A_KLE_M) ke = min(ke, m0 + 64);
     double acc[4][4] = {};
-    for (int64_t k0 = 0; k0 < K; k0 += 16) {
+    for (int64_t k0 = kb; k0 < ke; k0 += 16) {
         for (int e = tid; e < 64 * 16; e += 256) {
             const int mm = e / 16, kk = e % 16;
             const int64_t m = m0 + mm, k = k0 + kk;
@@ -291,11 +368,11 @@ __global__ __launch_bounds__(256) void gptq_dgemm_kernel(int64_t M, int64_t N, i
 
 template <bool TB>
 static void dgemm(int64_t M, int64_t N, int64_t K, double alpha, const double *A, int64_t lda, const double *Bm,
-                  int64_t ldb, double beta, double *C, int64_t ldc, hipStream_t st)
+                  int64_t ldb, double beta, double *C, int64_t ldc, int tri, hipStream_t st)
 {
     if (M <= 0 || N <= 0) return;
     const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 63) / 64));
-    gptq_dgemm_kernel<TB><<<grid, 256, 0, st>>>(M, N, K, alpha, A, lda, Bm, ldb, beta, C, ldc);
+    gptq_dgemm_kernel<TB><<<grid, 256, 0, st>>>(M, N, K, alpha, A, lda, Bm, ldb, beta, C, ldc, tri);
 }
 
 // Recursive Cholesky-with-inverse of the n x n diagonal block of P at `off`
@@ -314,16 +391,16 @@ static void cholinv(double *P, double *Li, int64_t ld, int64_t off, int64_t n, d
     double *P11 = P + off * ld + off, *P21 = P11 + n1 * ld, *P22 = P21 + n1;
     double *Li11 = Li + off * ld + off, *Li21 = Li11 + n1 * ld, *Li22 = Li21 + n1;
     cholinv(P, Li, ld, off, n1, T, T2, info, st);
-    // L21 = P21 L11^-T  (T: n2 x n1)
-    dgemm<true>(n2, n1, n1, 1.0, P21, ld, Li11, ld, 0.0, T, n1, st);
-    // S22 = P22 - L21 L21^T
-    dgemm<true>(n2, n2, n1, -1.0, T, n1, T, n1, 1.0, P22, ld, st);
+    // L21 = P21 L11^-T  (T: n2 x n1; L11^-T is upper triangular)
+    dgemm<true>(n2, n1, n1, 1.0, P21, ld, Li11, ld, 0.0, T, n1, TRI_B_KLE_N, st);
+    // S22 = P22 - L21 L21^T (symmetric: the recursion reads its lower triangle)
+    dgemm<true>(n2, n2, n1, -1.0, T, n1, T, n1, 1.0, P22, ld, TRI_C_LOWER, st);
     // L21 L11^-1 (T2: n2 x n1), kept across the recursion on S22
     double *Tm = T2;
-    dgemm<false>(n2, n1, n1, 1.0, T, n1, Li11, ld, 0.0, Tm, n1, st);
+    dgemm<false>(n2, n1, n1, 1.0, T, n1, Li11, ld, 0.0, Tm, n1, TRI_B_KGE_N, st);
     cholinv(P, Li, ld, off + n1, n2, T, T2 + n2 * n1, info, st);
-    // (L^-1)21 = -L22^-1 (L21 L11^-1)
-    dgemm<false>(n2, n1, n2, -1.0, Li22, ld, Tm, n1, 0.0, Li21, ld, st);
+    // (L^-1)21 = -L22^-1 (L21 L11^-1), L22^-1 lower triangular
+    dgemm<false>(n2, n1, n2, -1.0, Li22, ld, Tm, n1, 0.0, Li21, ld, TRI_A_KLE_M, st);
 }
 
 // ------------------------------------------------------- column loop ---
@@ -381,7 +458,8 @@ __device__ int gq_alternation(const float *v, const float *om, int B)
     return best_code;
 }
 
-// One panel [p0, p0 + 16 SEGP) of the column loop for 16 rows per workgroup.
+// One panel [p0, p0 + 64 SEGP) of the column loop: one wave per row, four
+// rows per workgroup, each lane holding SEGP consecutive working values.
 template <int EK, int SK, int KIND, bool WEIGHTED, int SEGP>
 __global__ __launch_bounds__(256) void gptq_panel_kernel(float *__restrict__ Wp, const float *__restrict__ V,
                                                          const float *__restrict__ hp, const int *__restrict__ col,
@@ -389,15 +467,14 @@ __global__ __launch_bounds__(256) void gptq_panel_kernel(float *__restrict__ Wp,
                                                          uint8_t *__restrict__ codes, uint8_t *__restrict__ scales,
                                                          float *__restrict__ E)
 {
-    constexpr int BL = 16 * SEGP;
-    __shared__ float blk[16][256 + 4];
+    constexpr int BL = 64 * SEGP;
+    __shared__ float blk[4][256 + 4];
     __shared__ float oms[256];
-    const int tid = threadIdx.x, r = tid / 16, l = tid % 16;
-    const int64_t n = (int64_t)blockIdx.x * 16 + r;
+    const int tid = threadIdx.x, r = tid / 64, l = tid % 64;
+    const int64_t n = (int64_t)blockIdx.x * 4 + r;
     const bool active = n < N;
     const int64_t pe = min(p0 + BL, K);
     const int64_t nb = K / B;
-    const int lane0 = (tid & 63) - l;  // the row's first lane within the wave
 
     float w[SEGP];
 #pragma unroll
@@ -420,21 +497,21 @@ __global__ __launch_bounds__(256) void gptq_panel_kernel(float *__restrict__ Wp,
         int code;
         if (KIND == GQ_NAIVE) {
             float amax = 0.0f;
-            for (int j = l; j < B; j += 16) amax = fmaxf(amax, fabsf(v[j]));
-            amax = group_max<16>(amax);
+            for (int j = l; j < B; j += 64) amax = fmaxf(amax, fabsf(v[j]));
+            amax = group_max<64>(amax);
             if constexpr (SK == SCALE_E8M0)
                 code = ocp ? ocp_code<EK>(amax) : naive_code<EK, SK>(amax);
             else
                 code = naive_code<EK, SK>(amax);
         } else if (KIND == GQ_ALT) {
             code = l == 0 ? gq_alternation<EK, WEIGHTED>(v, oms, B) : 0;
-            code = __shfl(code, lane0, 64);
+            code = __shfl(code, 0, 64);
         } else {
-            // full-grid argmin: lane l takes candidates c0 + l, c0 + l + 16, ...
+            // full-grid argmin: lane l takes candidates c0 + l, c0 + l + 64, ...
             constexpr int C0 = cand_first(SK), C1 = cand_last(SK);
             double best = __builtin_huge_val();
             int bc = C1 + 1;
-            for (int c = C0 + l; c <= C1; c += 16) {
+            for (int c = C0 + l; c <= C1; c += 64) {
                 const float s = scale_value(SK, c);
                 const double o = gq_objective<EK, SK, WEIGHTED>(v, oms, B, s, 1.0f / s);
                 if (o < best) {
@@ -442,9 +519,9 @@ __global__ __launch_bounds__(256) void gptq_panel_kernel(float *__restrict__ Wp,
                     bc = c;
                 }
             }
-            // lexicographic (objective, code) minimum over the row's 16 lanes
+            // lexicographic (objective, code) minimum over the wave
 #pragma unroll
-            for (int m = 1; m < 16; m <<= 1) {
+            for (int m = 1; m < 64; m <<= 1) {
                 const double ob = __shfl_xor(best, m, 64);
                 const int oc = __shfl_xor(bc, m, 64);
                 if (ob < best || (ob == best && oc < bc)) {
@@ -487,7 +564,7 @@ __global__ __launch_bounds__(256) void gptq_panel_kernel(float *__restrict__ Wp,
                     }
                 }
             }
-            e = __shfl(e, lane0 + own, 64);
+            e = __shfl(e, own, 64);
             const float *vr = V + c * K;
 #pragma unroll
             for (int i = 0; i < SEGP; ++i) {
@@ -607,12 +684,12 @@ template <int EK, int SK, int KIND, bool WEIGHTED>
 static void gq_panel(float *Wp, const float *V, const float *hp, const int *col, int64_t N, int64_t K, int B,
                      int64_t p0, int ocp, uint8_t *codes, uint8_t *scales, float *E, hipStream_t st)
 {
-    const unsigned g = (unsigned)((N + 15) / 16);
+    const unsigned g = (unsigned)((N + 3) / 4);
     if (B > 128)
-        gptq_panel_kernel<EK, SK, KIND, WEIGHTED, 16><<<g, 256, 0, st>>>(Wp, V, hp, col, N, K, B, p0, ocp, codes,
-                                                                          scales, E);
+        gptq_panel_kernel<EK, SK, KIND, WEIGHTED, 4><<<g, 256, 0, st>>>(Wp, V, hp, col, N, K, B, p0, ocp, codes,
+                                                                         scales, E);
     else
-        gptq_panel_kernel<EK, SK, KIND, WEIGHTED, 8><<<g, 256, 0, st>>>(Wp, V, hp, col, N, K, B, p0, ocp, codes,
+        gptq_panel_kernel<EK, SK, KIND, WEIGHTED, 2><<<g, 256, 0, st>>>(Wp, V, hp, col, N, K, B, p0, ocp, codes,
                                                                          scales, E);
 }
 
