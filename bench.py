@@ -84,7 +84,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=8, help="rows of W in the CPU sample")
-    ap.add_argument("--suite", choices=["headline", "formats", "gptq"], default="headline",
+    ap.add_argument("--suite", choices=["headline", "formats", "gptq", "sigma"], default="headline",
                     help="headline: the step above (one JSON line, the default); formats: every element / "
                          "scale format x B in {16, 32} x scale choice on the same W and h (one JSON line)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -114,6 +114,8 @@ def main():
         return formats_suite(args, dev)
     if args.suite == "gptq":
         return gptq_suite(args, dev)
+    if args.suite == "sigma":
+        return sigma_suite(args, dev)
 
     cfg = synth.CONFIGS[2]
     W_cpu, X_cpu = synth.config_inputs(2)
@@ -393,6 +395,61 @@ def gptq_suite(args, dev):
                                                               "16384x9728 bf16 (synthetic stand-ins)",
                                                   "W": [N, K], "X": [M, K]},
                       "hessian_ms": round(h_ms, 3), "data": "synthetic", "rows": rows}), flush=True)
+
+
+def sigma_suite(args, dev):
+    """Block size against tensor width ("Is Finer Better?", §3.2, §4.3,
+    §5.2): a seeded N(0, 1) tensor of 4096 x 4096 is scaled by sigma (40
+    values, 1e-4 .. 1) and quantised with E2M1 elements and Naive scales on
+    the UE4M3 (E4M3), UE4M4, UE5M3 and binary16 grids at B = 8 .. 64; the
+    per-tensor MSE (from weight_error's sums) is reported as MSE / sigma^2,
+    with the sigma where B = 8 and B = 16 cross for each grid."""
+    import numpy as np
+    import torch
+
+    import block_scaled_precision_hdiag_amd as hd
+    import synth
+
+    N = K = 4096
+    Z = synth.weights("normal", N, K, std=1.0, seed=61, dtype=torch.float32).to(dev)
+    sigmas = [float(x) for x in np.geomspace(1e-4, 1.0, 40)]
+    fmts = (hd.NVFP4, hd.NVFP4_UE4M4, hd.NVFP4_UE5M3, hd.FP4_F16)
+    blocks = (8, 16, 32, 64)
+    names = {v: k for k, v in hd.FORMATS.items()}
+    Wq = torch.empty((N, K), dtype=torch.float32, device=dev)
+    rows = []
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for sg in sigmas:
+        W = (Z * sg).contiguous()  # the synthetic input at this width
+        for fmt in fmts:
+            for B in blocks:
+                c, sc, _ = hd.quantize_blocks(hd.NAIVE, fmt, B, W)
+                hd.dequantize(fmt, B, c, sc, N, K, out=Wq)
+                _, sums = hd.weight_error(W, Wq, sums=True)
+                rows.append((sg, fmt, B, sums))
+    t1.record()
+    torch.cuda.synchronize()
+    out = []
+    for sg, fmt, B, sums in rows:
+        mse = sums[0].item() / (N * K)
+        out.append({"sigma": round(sg, 8), "format": names[fmt], "B": B, "mse": mse, "mse_over_sigma2": mse / sg ** 2})
+    crossings = {}
+    for fmt in fmts:
+        d = [next(r["mse"] for r in out if r["sigma"] == round(sg, 8) and r["format"] == names[fmt] and r["B"] == 8) -
+             next(r["mse"] for r in out if r["sigma"] == round(sg, 8) and r["format"] == names[fmt] and r["B"] == 16)
+             for sg in sigmas]
+        xs = []
+        for i in range(1, len(sigmas)):
+            if d[i - 1] > 0 >= d[i]:  # B = 8 worse below, better above
+                f = d[i - 1] / (d[i - 1] - d[i])
+                xs.append(float(np.exp(np.log(sigmas[i - 1]) + f * (np.log(sigmas[i]) - np.log(sigmas[i - 1])))))
+        crossings[names[fmt]] = xs
+    print(json.dumps({"suite": "sigma", "config": {"workload": "N(0, sigma^2) 4096x4096 fp32 (one seeded draw scaled), "
+                                                               "E2M1 elements, Naive scales", "sigmas": len(sigmas)},
+                      "data": "synthetic", "quantizations": len(rows), "total_ms": round(t0.elapsed_time(t1), 3),
+                      "b8_b16_crossing_sigma": crossings, "rows": out}), flush=True)
 
 
 def cpu_baseline(W_cpu, X_cpu, blocks, methods, fmt, rows, gpu_value):
