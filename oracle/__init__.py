@@ -64,6 +64,10 @@ def lib():
         L.orc_matmul_nt.argtypes = [P, i32, i64, P, i32, i64, i64, P, i32]
         L.orc_matmul_nt.restype = None
         L.orc_xtx.argtypes = [P, i32, i64, i64, P, i32]
+        L.orc_tensor_scale.argtypes = [i32, P, i32, i64]
+        L.orc_tensor_scale.restype = ctypes.c_float
+        L.orc_quantize_tensor_scaled.argtypes = [i32, i32, i32, P, i32, i64, i64, P, P, P, P, P, i32]
+        L.orc_dequantize_tensor_scaled.argtypes = [i32, i32, P, P, ctypes.c_float, i64, i64, P, i32]
         L.orc_gptq.argtypes = [i32, i32, i32, P, i32, i64, i64, P, dbl, i32, P, P, P, i32]
         L.orc_max_threads.argtypes = []
         _lib = L
@@ -260,4 +264,30 @@ def gptq(method, fmt, B, W, H, damp=0.01, ordered=False, nthreads=0):
                         _ptr(codes), _ptr(scales), _ptr(order), nthreads)
     _check(rc, "gptq")
     return codes, scales, order
+
+
+def quantize_tensor_scaled(method, fmt, B, W, h=None, nthreads=0):
+    """Per-tensor scale + E4M3 block scales (see oracle.c).  Returns (codes,
+    scales, tensor_scale float32, block objective of W / tensor_scale)."""
+    W = np.ascontiguousarray(W)
+    N, K = W.shape
+    codes = np.zeros(codes_shape(fmt, N, K), np.uint8)
+    scales = np.zeros((N, K // B), np.uint8)
+    obj = np.zeros((N, K // B), np.float64)
+    st = ctypes.c_float()
+    hh = None if h is None else np.ascontiguousarray(h, np.float32)
+    rc = lib().orc_quantize_tensor_scaled(method, fmt, B, _ptr(W), _dt(W), N, K, _ptr(hh), _ptr(codes), _ptr(scales),
+                                          ctypes.byref(st), _ptr(obj), nthreads)
+    _check(rc, "quantize_tensor_scaled")
+    return codes, scales, np.float32(st.value), obj
+
+
+def dequantize_tensor_scaled(fmt, B, codes, scales, tensor_scale, N, K, nthreads=0):
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = np.ascontiguousarray(scales, np.uint8)
+    out = np.zeros((N, K), np.float32)
+    rc = lib().orc_dequantize_tensor_scaled(fmt, B, _ptr(codes), _ptr(scales), float(np.float32(tensor_scale)), N, K,
+                                            _ptr(out), nthreads)
+    _check(rc, "dequantize_tensor_scaled")
+    return out
 

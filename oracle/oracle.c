@@ -43,6 +43,8 @@
  *     fp16(fl32(amax / C)); SSE-Optimal / H-Optimal are found by alternating
  *     element assignment and the closed-form least-squares scale snapped to
  *     FP16 (f16_alternation below; its readings are listed there).
+ *   - per-tensor scaling over E4M3 block scales ("Is Finer Better?" §5.1,
+ *     UE4M3-S; orc_quantize_tensor_scaled, its reading is listed there).
  *   - GPTQ (qwantize "Results", "GPTQ Quantization"; quantisation-algorithms
  *     note, §1): H = X^T X (orc_xtx), damped, the upper Cholesky factor of its
  *     inverse, and the column loop of Frantar et al. with the GPTQ block equal
@@ -1066,5 +1068,62 @@ done:
     free(U);
     free(Wc);
     free(om);
+    return rc;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Per-tensor scaling on top of E4M3 block scales                            */
+/* ------------------------------------------------------------------------ */
+
+/* "Is Finer Better?" §5.1 / Table 1 (UE4M3-S: per-tensor scaling + UE4M3
+ * block scales; the page's formula for the tensor scale is not legible in
+ * our copy).  Reading: s_T = fl32(amax_T / (C_T * 448)) maps the tensor's
+ * largest block scale onto the top of the E4M3 grid (C_T = the element
+ * maximum, or 1 for INT8, whose block scale is amax itself); 1 when the tensor
+ * is all zero.  The blocks then quantise W' = fl32(W / s_T) exactly as the
+ * format does, and x^ = fl32(s_T * fl32(s q)).  E4M3-scale formats only. */
+float orc_tensor_scale(int fmt, const void *W, int wdt, int64_t n)
+{
+    init_tables();
+    float amax = 0.0f;
+    for (int64_t i = 0; i < n; i++) {
+        const float a = fabsf(widen(W, wdt, i));
+        if (a > amax) amax = a;
+    }
+    if (amax == 0.0f)
+        return 1.0f;
+    const float ct = (scale_kind(fmt) == S_E4M3_OF_AMAX_DIV127) ? 1.0f : elem_cmax(fmt);
+    return amax / (ct * 448.0f); /* ct * 448 is exact */
+}
+
+int orc_quantize_tensor_scaled(int method, int fmt, int B, const void *W, int wdt, int64_t N, int64_t K,
+                               const float *h, uint8_t *codes, uint8_t *scales, float *tensor_scale,
+                               double *block_obj, int nthreads)
+{
+    init_tables();
+    if (fmt < 0 || fmt >= F_COUNT || (scale_kind(fmt) != S_E4M3 && scale_kind(fmt) != S_E4M3_OF_AMAX_DIV127))
+        return ORC_EINVAL;
+    if (wdt != DT_F32 && wdt != DT_BF16)
+        return ORC_EINVAL;
+    const float st = orc_tensor_scale(fmt, W, wdt, N * K);
+    float *Wp = (float *)malloc(sizeof(float) * (size_t)(N * K > 0 ? N * K : 1));
+    if (!Wp)
+        return ORC_ENOMEM;
+    for (int64_t i = 0; i < N * K; i++)
+        Wp[i] = widen(W, wdt, i) / st; /* fl32 IEEE division */
+    const int rc = orc_quantize(method, fmt, B, Wp, DT_F32, N, K, h, NULL, codes, scales, block_obj, nthreads);
+    free(Wp);
+    if (tensor_scale)
+        *tensor_scale = st;
+    return rc;
+}
+
+int orc_dequantize_tensor_scaled(int fmt, int B, const uint8_t *codes, const uint8_t *scales, float tensor_scale,
+                                 int64_t N, int64_t K, float *out, int nthreads)
+{
+    const int rc = orc_dequantize(fmt, B, codes, scales, N, K, out, nthreads);
+    if (rc == ORC_OK)
+        for (int64_t i = 0; i < N * K; i++)
+            out[i] = tensor_scale * out[i]; /* fl32 */
     return rc;
 }
