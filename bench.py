@@ -401,7 +401,8 @@ def sigma_suite(args, dev):
     """Block size against tensor width ("Is Finer Better?", §3.2, §4.3,
     §5.2): a seeded N(0, 1) tensor of 4096 x 4096 is scaled by sigma (40
     values, 1e-4 .. 1) and quantised with E2M1 elements and Naive scales on
-    the UE4M3 (E4M3), UE4M4, UE5M3 and binary16 grids at B = 8 .. 64; the
+    the UE4M3 (E4M3), UE4M4, UE5M3 and binary16 grids and UE4M3 under a
+    per-tensor scale (UE4M3-S, §5.1) at B = 8 .. 64; the
     per-tensor MSE (from weight_error's sums) is reported as MSE / sigma^2,
     with the sigma where B = 8 and B = 16 cross for each grid."""
     import numpy as np
@@ -414,19 +415,26 @@ def sigma_suite(args, dev):
     Z = synth.weights("normal", N, K, std=1.0, seed=61, dtype=torch.float32).to(dev)
     sigmas = [float(x) for x in np.geomspace(1e-4, 1.0, 40)]
     fmts = (hd.NVFP4, hd.NVFP4_UE4M4, hd.NVFP4_UE5M3, hd.FP4_F16)
+    TS = -1  # marker: NVFP4 with a per-tensor scale (UE4M3-S)
     blocks = (8, 16, 32, 64)
     names = {v: k for k, v in hd.FORMATS.items()}
+    names[TS] = "NVFP4_TENSOR_SCALED"
     Wq = torch.empty((N, K), dtype=torch.float32, device=dev)
     rows = []
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
+    ws_t = torch.empty(hd.quantize_blocks_tensor_scaled_workspace_size(N, K), dtype=torch.uint8, device=dev)
     for sg in sigmas:
         W = (Z * sg).contiguous()  # the synthetic input at this width
-        for fmt in fmts:
+        for fmt in fmts + (TS,):
             for B in blocks:
-                c, sc, _ = hd.quantize_blocks(hd.NAIVE, fmt, B, W)
-                hd.dequantize(fmt, B, c, sc, N, K, out=Wq)
+                if fmt == TS:  # UE4M3 block scales under a per-tensor scale
+                    c, sc, ts, _ = hd.quantize_blocks_tensor_scaled(hd.NAIVE, hd.NVFP4, B, W, workspace=ws_t)
+                    hd.dequantize_tensor_scaled(hd.NVFP4, B, c, sc, ts, N, K, out=Wq)
+                else:
+                    c, sc, _ = hd.quantize_blocks(hd.NAIVE, fmt, B, W)
+                    hd.dequantize(fmt, B, c, sc, N, K, out=Wq)
                 _, sums = hd.weight_error(W, Wq, sums=True)
                 rows.append((sg, fmt, B, sums))
     t1.record()
@@ -436,7 +444,7 @@ def sigma_suite(args, dev):
         mse = sums[0].item() / (N * K)
         out.append({"sigma": round(sg, 8), "format": names[fmt], "B": B, "mse": mse, "mse_over_sigma2": mse / sg ** 2})
     crossings = {}
-    for fmt in fmts:
+    for fmt in fmts + (TS,):
         d = [next(r["mse"] for r in out if r["sigma"] == round(sg, 8) and r["format"] == names[fmt] and r["B"] == 8) -
              next(r["mse"] for r in out if r["sigma"] == round(sg, 8) and r["format"] == names[fmt] and r["B"] == 16)
              for sg in sigmas]

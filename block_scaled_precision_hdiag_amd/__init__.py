@@ -38,7 +38,8 @@ F16_SCALES = (FP4_F16, INT4_F16)
 EXPORTS = ["hdiag", "hdiag_workspace_size", "quantize_blocks", "encode_blocks", "dequantize",
            "weight_error", "weight_error_workspace_size", "output_error", "output_error_workspace_size",
            "output_error_given_ref", "output_reference", "output_reference_size", "output_error_codes",
-           "output_error_codes_workspace_size", "gptq_hessian", "gptq_hessian_workspace_size", "gptq_quantize",
+           "output_error_codes_workspace_size", "quantize_blocks_tensor_scaled",
+           "quantize_blocks_tensor_scaled_workspace_size", "dequantize_tensor_scaled", "gptq_hessian", "gptq_hessian_workspace_size", "gptq_quantize",
            "gptq_workspace_size",
            "hdiag_strerror", "hdiag_last_error", "hdiag_format_info", "hdiag_version"]
 
@@ -87,6 +88,10 @@ def lib():
         L.hdiag_format_info.argtypes = [i32, i32, P, P, P, P]
         L.hdiag_version.argtypes = []
         L.hdiag_version.restype = ctypes.c_char_p
+        L.quantize_blocks_tensor_scaled_workspace_size.argtypes = [i64, i64]
+        L.quantize_blocks_tensor_scaled_workspace_size.restype = sz
+        L.quantize_blocks_tensor_scaled.argtypes = [i32, i32, i32, P, i32, i64, i64, P, P, P, P, P, P, sz, P]
+        L.dequantize_tensor_scaled.argtypes = [i32, i32, P, P, P, i64, i64, P, i32, P]
         L.gptq_hessian_workspace_size.argtypes = [i64, i64]
         L.gptq_hessian_workspace_size.restype = sz
         L.gptq_hessian.argtypes = [P, i32, i64, i64, P, P, sz, P]
@@ -95,7 +100,8 @@ def lib():
         L.gptq_quantize.argtypes = [i32, i32, i32, P, i32, i64, i64, P, ctypes.c_double, i32, P, P, P, P, P, sz, P]
         for name in ("hdiag", "quantize_blocks", "encode_blocks", "dequantize", "weight_error",
                      "output_error", "output_error_given_ref", "output_reference", "output_error_codes",
-                     "hdiag_format_info", "gptq_hessian", "gptq_quantize"):
+                     "hdiag_format_info", "gptq_hessian", "gptq_quantize", "quantize_blocks_tensor_scaled",
+                     "dequantize_tensor_scaled"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -289,6 +295,35 @@ def output_error_codes(fmt, B, X, codes, scales, ref, N, K, sums=False, workspac
                                     ref.numel(), _ptr(out), _ptr(s), _ptr(ws), ws.numel(), _stream(d)),
            "output_error_codes")
     return (out, s) if sums else out
+
+
+def quantize_blocks_tensor_scaled_workspace_size(N, K):
+    return int(lib().quantize_blocks_tensor_scaled_workspace_size(N, K))
+
+
+def quantize_blocks_tensor_scaled(method, fmt, B, W, h=None, block_obj=False, workspace=None):
+    """Per-tensor scale + E4M3 block scales.  Returns (codes, scales, tensor_scale
+    float32 [1], block_obj of W / tensor_scale or None)."""
+    d = _dev(W)
+    N, K = W.shape
+    codes = torch.empty(codes_shape(fmt, N, K), dtype=torch.uint8, device=d)
+    scales = torch.empty((N, K // B), dtype=torch.uint8, device=d)
+    ts = torch.empty(1, dtype=torch.float32, device=d)
+    obj = torch.empty((N, K // B), dtype=torch.float32, device=d) if block_obj else None
+    need = quantize_blocks_tensor_scaled_workspace_size(N, K)
+    ws = workspace if workspace is not None else torch.empty(max(need, 16), dtype=torch.uint8, device=d)
+    _check(lib().quantize_blocks_tensor_scaled(method, fmt, B, _ptr(W), _dt(W), N, K, _ptr(h), _ptr(codes),
+                                               _ptr(scales), _ptr(ts), _ptr(obj), _ptr(ws), ws.numel(), _stream(d)),
+           "quantize_blocks_tensor_scaled")
+    return codes, scales, ts, obj
+
+
+def dequantize_tensor_scaled(fmt, B, codes, scales, tensor_scale, N, K, dtype=torch.float32, out=None):
+    d = _dev(codes)
+    out = out if out is not None else torch.empty((N, K), dtype=dtype, device=d)
+    _check(lib().dequantize_tensor_scaled(fmt, B, _ptr(codes), _ptr(scales), _ptr(tensor_scale), N, K, _ptr(out),
+                                          _dt(out), _stream(d)), "dequantize_tensor_scaled")
+    return out
 
 
 def gptq_hessian_workspace_size(M, K):

@@ -189,7 +189,7 @@ hd_status dequantize(hd_format fmt, int32_t B, const uint8_t *codes, const uint8
     HD_CHECK_PTR(Wq, true);
     if (scales == nullptr) return fail(HD_ERR_INVALID_ARG, "scales is NULL");
     if (is_f16(fmt) && ((uintptr_t)scales & 1u)) return fail(HD_ERR_INVALID_ARG, "scales is not 2-byte aligned");
-    return hip_status(hd::launch_dequant(fmt, B, codes, scales, N, K, Wq, out_t, (hipStream_t)stream),
+    return hip_status(hd::launch_dequant(fmt, B, codes, scales, N, K, Wq, out_t, nullptr, (hipStream_t)stream),
                       "dequantize");
 }
 
@@ -307,6 +307,65 @@ hd_status output_error_codes(hd_format fmt, int32_t B, const void *X, hd_dtype x
     return hip_status(hd::launch_output_error_codes(fmt, B, X, M, codes, scales, N, K, ref, out, sums, ws,
                                                     (hipStream_t)stream),
                       "output_error_codes");
+}
+
+bool is_e4m3_scaled(int f) { return f == HD_INT8_E4M3 || f == HD_NVFP4 || f == HD_FP8_E4M3S || f == HD_NVINT4; }
+
+size_t quantize_blocks_tensor_scaled_workspace_size(int64_t N, int64_t K)
+{
+    if (N < 0 || K < 0) return 0;
+    return (size_t)(256 + ((N * K * 4 + 255) / 256) * 256);
+}
+
+hd_status quantize_blocks_tensor_scaled(hd_method method, hd_format fmt, int32_t B, const void *W, hd_dtype wt,
+                                        int64_t N, int64_t K, const float *h, uint8_t *codes, uint8_t *scales,
+                                        float *tensor_scale, float *block_obj, void *ws, size_t ws_bytes,
+                                        void *stream)
+{
+    HD_REQUIRE(method >= HD_NAIVE && method <= HD_H_OPT, "unknown method %d (the OCP rule needs E8M0 scales)",
+               (int)method);
+    HD_REQUIRE(valid_dtype(wt), "unknown dtype %d", (int)wt);
+    hd_status s = check_quant_shape(fmt, B, N, K);
+    if (s != HD_OK) return s;
+    HD_REQUIRE(is_e4m3_scaled(fmt), "per-tensor scaling needs an E4M3 block-scale format");
+    HD_REQUIRE(method != HD_H_OPT || h != nullptr, "H-Optimal needs h");
+    if (N == 0 || K == 0) return ok();
+    HD_CHECK_PTR(W, true);
+    HD_CHECK_PTR(codes, true);
+    HD_CHECK_PTR(ws, true);
+    HD_REQUIRE(tensor_scale != nullptr && ((uintptr_t)tensor_scale & 3u) == 0, "tensor_scale is NULL or misaligned");
+    if (scales == nullptr) return fail(HD_ERR_INVALID_ARG, "scales is NULL");
+    if ((uintptr_t)scales & 3u) return fail(HD_ERR_INVALID_ARG, "scales is not 4-byte aligned");
+    if (h != nullptr && !aligned16(h)) return fail(HD_ERR_INVALID_ARG, "h is not 16-byte aligned");
+    if (block_obj != nullptr && ((uintptr_t)block_obj & 3u)) return fail(HD_ERR_INVALID_ARG, "block_obj misaligned");
+    HD_REQUIRE(ws_bytes >= quantize_blocks_tensor_scaled_workspace_size(N, K), "workspace too small");
+    hipStream_t st = (hipStream_t)stream;
+    float *Wp = reinterpret_cast<float *>(static_cast<char *>(ws) + 256);
+    hipError_t e = hd::launch_tensor_scale(fmt, W, wt, N, K, tensor_scale, Wp, ws, st);
+    if (e != hipSuccess) return hip_status(e, "quantize_blocks_tensor_scaled(scale)");
+    if (method == HD_NAIVE)
+        return hip_status(hd::launch_encode(fmt, B, Wp, HD_F32, N, K, h, nullptr, codes, scales, block_obj, 0, st),
+                          "quantize_blocks_tensor_scaled(naive)");
+    const float *hh = method == HD_H_OPT ? h : nullptr;
+    return hip_status(hd::launch_search(fmt, B, Wp, HD_F32, N, K, hh, codes, scales, block_obj, st),
+                      "quantize_blocks_tensor_scaled(search)");
+}
+
+hd_status dequantize_tensor_scaled(hd_format fmt, int32_t B, const uint8_t *codes, const uint8_t *scales,
+                                   const float *tensor_scale, int64_t N, int64_t K, void *Wq, hd_dtype out_t,
+                                   void *stream)
+{
+    HD_REQUIRE(valid_dtype(out_t), "unknown dtype %d", (int)out_t);
+    hd_status s = check_quant_shape(fmt, B, N, K);
+    if (s != HD_OK) return s;
+    HD_REQUIRE(is_e4m3_scaled(fmt), "per-tensor scaling needs an E4M3 block-scale format");
+    if (N == 0 || K == 0) return ok();
+    HD_CHECK_PTR(codes, true);
+    HD_CHECK_PTR(Wq, true);
+    if (scales == nullptr) return fail(HD_ERR_INVALID_ARG, "scales is NULL");
+    HD_REQUIRE(tensor_scale != nullptr && ((uintptr_t)tensor_scale & 3u) == 0, "tensor_scale is NULL or misaligned");
+    return hip_status(hd::launch_dequant(fmt, B, codes, scales, N, K, Wq, out_t, tensor_scale, (hipStream_t)stream),
+                      "dequantize_tensor_scaled");
 }
 
 size_t gptq_hessian_workspace_size(int64_t M, int64_t K)

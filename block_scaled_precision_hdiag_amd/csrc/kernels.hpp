@@ -39,8 +39,9 @@ hipError_t launch_search_nvint4(int B, const void *W, int wdt, int64_t N, int64_
 hipError_t launch_alt_f16(int fmt, int B, const void *W, int wdt, int64_t N, int64_t K, const float *h,
                           uint8_t *codes, uint8_t *scales, float *block_obj, hipStream_t st);
 
+// tscale (device float, may be NULL): a per-tensor scale multiplying every value.
 hipError_t launch_dequant(int fmt, int B, const uint8_t *codes, const uint8_t *scales, int64_t N, int64_t K,
-                          void *out, int out_t, hipStream_t st);
+                          void *out, int out_t, const float *tscale, hipStream_t st);
 
 size_t weight_error_ws(int64_t N, int64_t K);
 hipError_t launch_weight_error(const void *W, int wdt, const void *Wq, int qdt, int64_t N, int64_t K,
@@ -86,5 +87,10 @@ int64_t gptq_ws(int B, int64_t N, int64_t K);
 hipError_t launch_gptq(int method, int fmt, int B, const void *W, int wdt, int64_t N, int64_t K, const float *H,
                        double damp, int ordered, uint8_t *codes, uint8_t *scales, int32_t *block_order, int *info,
                        void *ws, hipStream_t st);
+
+// Per-tensor scaling over E4M3 block scales (tscale.hip): the tensor scale
+// into *tscale and W / tscale (float32 [N][K]) into Wp.
+hipError_t launch_tensor_scale(int fmt, const void *W, int wdt, int64_t N, int64_t K, float *tscale, float *Wp,
+                               void *ws, hipStream_t st);
 
 }  // namespace hd

@@ -218,10 +218,12 @@ hipError_t launch_encode(int fmt, int B, const void *W, int wdt, int64_t N, int6
 
 // ------------------------------------------------------------ dequantize ---
 // x^ = s q ("Is Finer Better?" §2.1): sign * fl32(s * val(index)).
+// With a per-tensor scale t (tscale != NULL): t * fl32(s * val(index)).
 template <int EK, int SK, int OUT_BF16>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict__ codes,
                                                       const uint8_t *__restrict__ scales, int64_t total,
-                                                      int B, void *__restrict__ out)
+                                                      int B, void *__restrict__ out,
+                                                      const float *__restrict__ tscale)
 {
     const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
     if (e0 >= total) return;
@@ -263,7 +265,8 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict_
             idx = c[j] & 0x7Fu;
             ok = idx != 0x7Fu;
         }
-        const float mag = ok ? s * elem_value<EK>(idx) : 0.0f;
+        float mag = ok ? s * elem_value<EK>(idx) : 0.0f;
+        if (tscale) mag = tscale[0] * mag;
         o[j] = neg ? -mag : mag;
     }
     if (OUT_BF16) {
@@ -282,23 +285,23 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict_
 
 template <int EK, int SK>
 static hipError_t dequant_f(int B, const uint8_t *codes, const uint8_t *scales, int64_t total, void *out,
-                            int out_t, hipStream_t st)
+                            int out_t, const float *tscale, hipStream_t st)
 {
     const dim3 grid((unsigned)((total / 8 + 255) / 256));
     if (out_t == 1)
-        dequant_kernel<EK, SK, 1><<<grid, 256, 0, st>>>(codes, scales, total, B, out);
+        dequant_kernel<EK, SK, 1><<<grid, 256, 0, st>>>(codes, scales, total, B, out, tscale);
     else
-        dequant_kernel<EK, SK, 0><<<grid, 256, 0, st>>>(codes, scales, total, B, out);
+        dequant_kernel<EK, SK, 0><<<grid, 256, 0, st>>>(codes, scales, total, B, out, tscale);
     return hipGetLastError();
 }
 
 hipError_t launch_dequant(int fmt, int B, const uint8_t *codes, const uint8_t *scales, int64_t N, int64_t K,
-                          void *out, int out_t, hipStream_t st)
+                          void *out, int out_t, const float *tscale, hipStream_t st)
 {
     const int64_t total = N * K;
 #define HD_DEQ_FMT(F)                                                                                      \
     case F:                                                                                                \
-        return dequant_f<elem_kind(F), scale_kind(F)>(B, codes, scales, total, out, out_t, st);
+        return dequant_f<elem_kind(F), scale_kind(F)>(B, codes, scales, total, out, out_t, tscale, st);
     switch (fmt) {
         HD_DEQ_FMT(HD_INT8_E4M3)
         HD_DEQ_FMT(HD_NVFP4)

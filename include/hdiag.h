@@ -264,6 +264,32 @@ hd_status output_error_codes(hd_format fmt, int32_t B, const void *X, hd_dtype x
                              const void *ref, size_t ref_bytes, double *out, double *sums, void *ws,
                              size_t ws_bytes, void *stream);
 
+/* ------------------------------------------------ per-tensor scaling --- */
+
+/* Two-level scales for the E4M3 block-scale formats (HD_INT8_E4M3, HD_NVFP4,
+ * HD_FP8_E4M3S, HD_NVINT4): "Is Finer Better?" §5.1 and Table 1 (UE4M3-S,
+ * per-tensor scaling on top of UE4M3 block scales; the page's formula for the
+ * tensor scale is not legible, the reading here is the one documented):
+ *   s_T = fl32(amax_T / (C * 448)), C the element maximum (6 E2M1, 7 INT4,
+ *   448 E4M3; 1 for INT8, whose block scale is amax itself), 1 for an all-zero
+ *   tensor - the largest block scale lands on the top of the E4M3 grid;
+ *   the blocks quantise W' = fl32(W / s_T) exactly as quantize_blocks does
+ *   (codes, scales and block_obj refer to W');
+ *   dequantize_tensor_scaled gives x^ = fl32(s_T * fl32(s * val(q))).
+ * tensor_scale: one device float (written by quantize, read by dequantize).
+ * Workspace: quantize_blocks_tensor_scaled_workspace_size(N, K) bytes (W' is
+ * staged there in float32).  Errors as quantize_blocks / dequantize, plus
+ * HD_ERR_INVALID_ARG for a format without E4M3 block scales and for
+ * HD_NAIVE_OCP. */
+size_t quantize_blocks_tensor_scaled_workspace_size(int64_t N, int64_t K);
+hd_status quantize_blocks_tensor_scaled(hd_method method, hd_format fmt, int32_t B, const void *W, hd_dtype wt,
+                                        int64_t N, int64_t K, const float *h, uint8_t *codes, uint8_t *scales,
+                                        float *tensor_scale, float *block_obj, void *ws, size_t ws_bytes,
+                                        void *stream);
+hd_status dequantize_tensor_scaled(hd_format fmt, int32_t B, const uint8_t *codes, const uint8_t *scales,
+                                   const float *tensor_scale, int64_t N, int64_t K, void *Wq, hd_dtype out_t,
+                                   void *stream);
+
 /* ----------------------------------------------------------------- GPTQ --- */
 
 /* GPTQ on top of a scale choice (qwantize "Results", "GPTQ Quantization": GPTQ
