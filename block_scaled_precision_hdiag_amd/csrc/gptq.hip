@@ -366,11 +366,86 @@ __global__ __launch_bounds__(256) void gptq_dgemm_kernel(int64_t M, int64_t N, i
     }
 }
 
+// The same product with 128 x 128 output tiles and 8 x 8 outputs per thread
+// (64 fused multiply-adds per 16 LDS reads), k in steps of 8, the next step's
+// operands loaded into registers while the current one is multiplied; for
+// operands of at least 256 x 256.
+template <bool TB>
+__global__ __launch_bounds__(256) void gptq_dgemm_big_kernel(int64_t M, int64_t N, int64_t K, double alpha,
+                                                             const double *__restrict__ A, int64_t lda,
+                                                             const double *__restrict__ Bm, int64_t ldb,
+                                                             double beta, double *__restrict__ C, int64_t ldc, int tri)
+{
+    __shared__ double As[8][128 + 1];
+    __shared__ double Bs[8][128 + 1];
+    const int tid = threadIdx.x, tx = tid % 16, ty = tid / 16;
+    const int64_t m0 = (int64_t)blockIdx.y * 128, n0 = (int64_t)blockIdx.x * 128;
+    if ((tri & TRI_C_LOWER) && n0 > m0 + 127) return;
+    int64_t kb = 0, ke = K;
+    if (tri & TRI_B_KGE_N) kb = n0;
+    if (tri & TRI_B_KLE_N) ke = min(ke, n0 + 128);
+    if (tri & TRI_A_KLE_M) ke = min(ke, m0 + 128);
+    double acc[8][8] = {};
+    double ra[4], rb[4];
+    auto fetch = [&](int64_t k0) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = tid + 256 * q;
+            const int64_t m = m0 + e / 8, k = k0 + e % 8;
+            ra[q] = (m < M && k < ke) ? A[m * lda + k] : 0.0;
+            int64_t n, kq;
+            if (TB) { n = n0 + e / 8; kq = k0 + e % 8; } else { kq = k0 + e / 128; n = n0 + e % 128; }
+            rb[q] = (n < N && kq < ke) ? (TB ? Bm[n * ldb + kq] : Bm[kq * ldb + n]) : 0.0;
+        }
+    };
+    if (kb < ke) fetch(kb);
+    for (int64_t k0 = kb; k0 < ke; k0 += 8) {
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = tid + 256 * q;
+            As[e % 8][e / 8] = ra[q];
+            if (TB) Bs[e % 8][e / 8] = rb[q]; else Bs[e / 128][e % 128] = rb[q];
+        }
+        __syncthreads();
+        if (k0 + 8 < ke) fetch(k0 + 8);
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+            double av[8], bv[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) av[i] = As[kk][ty + 16 * i];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) bv[j] = Bs[kk][tx + 16 * j];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_fma(av[i], bv[j], acc[i][j]);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int64_t m = m0 + ty + 16 * i;
+        if (m >= M) continue;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int64_t n = n0 + tx + 16 * j;
+            if (n >= N) continue;
+            double *c = C + m * ldc + n;
+            *c = beta == 0.0 ? alpha * acc[i][j] : beta * *c + alpha * acc[i][j];
+        }
+    }
+}
+
 template <bool TB>
 static void dgemm(int64_t M, int64_t N, int64_t K, double alpha, const double *A, int64_t lda, const double *Bm,
                   int64_t ldb, double beta, double *C, int64_t ldc, int tri, hipStream_t st)
 {
     if (M <= 0 || N <= 0) return;
+    if (M >= 256 && N >= 256) {
+        const dim3 grid((unsigned)((N + 127) / 128), (unsigned)((M + 127) / 128));
+        gptq_dgemm_big_kernel<TB><<<grid, 256, 0, st>>>(M, N, K, alpha, A, lda, Bm, ldb, beta, C, ldc, tri);
+        return;
+    }
     const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 63) / 64));
     gptq_dgemm_kernel<TB><<<grid, 256, 0, st>>>(M, N, K, alpha, A, lda, Bm, ldb, beta, C, ldc, tri);
 }
