@@ -187,18 +187,26 @@ __global__ __launch_bounds__(256) void gptq_build_v_kernel(const double *__restr
 // ---------------------------------------------- float64 factorisation ---
 
 // Leaf: L = chol(P block), n <= 64, then Li = L^-1 (lower); only Li is kept.
-// Thread t owns the 4 x 4 tile rows 4 (t / 16) .., columns 4 (t % 16) .. of
-// the 64 x 64 block in registers; each step publishes one column (or row)
-// through LDS and every thread updates its tile.  Rows / columns >= n are
+// Thread t owns the 4 x 4 tile rows 4 (t % 16) .., columns 4 (t / 16) .. of
+// the 64 x 64 block in registers, so the 16 owners of a tile column (the
+// diagonal tile's owner among them) share one wave.  Factorisation step j:
+// the owners of column j take the pivot from the diagonal owner by a lane
+// shuffle, scale the column and publish it through LDS; after one barrier
+// every thread subtracts its outer product.  Inverse step k: the owners of
+// row k of X scale it and publish it; after one barrier every later row
+// subtracts its multiple.  Published vectors alternate between two LDS slots,
+// so one barrier a step suffices; step loops are unrolled by four so that
+// register indices are compile-time constants.  Rows / columns >= n are
 // padded with the identity.  info[0] gets the first non-positive pivot's
 // global index + 1 (the pivot is then replaced by 1 so the factorisation
 // still finishes).
 __global__ __launch_bounds__(256) void gptq_chol_leaf_kernel(const double *__restrict__ P, int64_t ld, int64_t off,
                                                              int n, double *__restrict__ Li, int *__restrict__ info)
 {
-    __shared__ double colv[64];     // the current column of L (or row of X)
+    __shared__ double colv[2][64];  // column j of L below the pivot, or row k of X
     __shared__ double Ls[64][65];   // L, for the inverse
-    const int tid = threadIdx.x, ti = tid / 16, tk = tid % 16;
+    __shared__ double rdiag[64];    // 1 / L_kk
+    const int tid = threadIdx.x, ti = tid % 16, tk = tid / 16;
     double a[4][4];
 #pragma unroll
     for (int u = 0; u < 4; ++u)
@@ -208,46 +216,41 @@ __global__ __launch_bounds__(256) void gptq_chol_leaf_kernel(const double *__res
             a[u][v] = (i < n && k <= i) ? P[(off + i) * ld + off + k] : (i == k ? 1.0 : 0.0);
         }
     // Cholesky: step j scales column j below the pivot by 1 / sqrt(pivot) and
-    // subtracts the outer product from the trailing lower triangle
-    for (int j = 0; j < 64; ++j) {
-        const int tj = j / 4, vj = j % 4;
-        if (tk == tj && ti == tj) {
-            double d = a[vj][vj];
-            if (!(d > 0.0)) {
-                if (info && j < n) atomicCAS(info, 0, (int)(off + j + 1));
-                d = 1.0;
+    // subtracts its outer product from the trailing lower triangle
+    for (int jt = 0; jt < 16; ++jt) {
+#pragma unroll
+        for (int vj = 0; vj < 4; ++vj) {
+            const int j = 4 * jt + vj, b = j & 1;
+            if (tk == jt) {
+                // lanes 16 (jt % 4) .. + 15 of wave jt / 4; the diagonal owner is ti == jt
+                double d = __shfl(a[vj][vj], (jt & 3) * 16 + jt, 64);
+                if (!(d > 0.0)) {
+                    if (ti == jt && info && j < n) atomicCAS(info, 0, (int)(off + j + 1));
+                    d = 1.0;
+                }
+                const double p = sqrt(d), r = 1.0 / p;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int i = 4 * ti + u;
+                    if (i > j) a[u][vj] *= r;
+                    if (i == j) a[u][vj] = p;
+                    colv[b][i] = i > j ? a[u][vj] : 0.0;
+                }
             }
-            colv[j] = sqrt(d);
-        }
-        __syncthreads();
-        const double piv = colv[j];
-        __syncthreads();
-        if (tk == tj) {
+            __syncthreads();
+            if (ti >= jt) {
+                double ci[4], ck[4];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int i = 4 * ti + u;
-                if (i > j) a[u][vj] /= piv;
-                if (i == j) a[u][vj] = piv;
-                if (i >= j) colv[i] = i == j ? 0.0 : a[u][vj];
+                for (int u = 0; u < 4; ++u) ci[u] = colv[b][4 * ti + u];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) ck[v] = colv[b][4 * tk + v];
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        if (4 * tk + v > j && 4 * tk + v <= 4 * ti + u) a[u][v] -= ci[u] * ck[v];
             }
         }
-        if (ti < tj) {
-            // rows above the pivot hold nothing of column j
-        }
-        __syncthreads();
-        if (ti >= tj) {
-            double ci[4], ck[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) ci[u] = 4 * ti + u > j ? colv[4 * ti + u] : 0.0;
-#pragma unroll
-            for (int v = 0; v < 4; ++v) ck[v] = 4 * tk + v > j ? colv[4 * tk + v] : 0.0;
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-#pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    if (4 * tk + v > j && 4 * tk + v <= 4 * ti + u) a[u][v] -= ci[u] * ck[v];
-        }
-        __syncthreads();
     }
     // L (lower) to LDS; X = identity tile
 #pragma unroll
@@ -259,34 +262,38 @@ __global__ __launch_bounds__(256) void gptq_chol_leaf_kernel(const double *__res
             a[u][v] = i == k ? 1.0 : 0.0;
         }
     __syncthreads();
+    if (tid < 64) rdiag[tid] = 1.0 / Ls[tid][tid];
+    __syncthreads();
     // L^-1 by a right-looking solve of L X = I: at step k row k of X is final
-    // once divided by L_kk, and every later row subtracts L_ik times it
-    for (int k = 0; k < 64; ++k) {
-        const int tkk = k / 4, uk = k % 4;
-        if (ti == tkk) {
-            const double rk = 1.0 / Ls[k][k];
+    // once scaled by 1 / L_kk, and every later row subtracts L_ik times it
+    for (int kt = 0; kt < 16; ++kt) {
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                a[uk][v] *= rk;
-                colv[4 * tk + v] = a[uk][v];
+        for (int uk = 0; uk < 4; ++uk) {
+            const int k = 4 * kt + uk, b = k & 1;
+            if (ti == kt) {
+                const double rk = rdiag[k];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    a[uk][v] *= rk;
+                    colv[b][4 * tk + v] = a[uk][v];
+                }
             }
-        }
-        __syncthreads();
-        if (ti >= tkk) {
-            double xr[4];
+            __syncthreads();
+            if (ti >= kt) {
+                double xr[4];
 #pragma unroll
-            for (int v = 0; v < 4; ++v) xr[v] = colv[4 * tk + v];
+                for (int v = 0; v < 4; ++v) xr[v] = colv[b][4 * tk + v];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int i = 4 * ti + u;
-                if (i > k) {
-                    const double lik = Ls[i][k];
+                for (int u = 0; u < 4; ++u) {
+                    const int i = 4 * ti + u;
+                    if (i > k) {
+                        const double lik = Ls[i][k];
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) a[u][v] -= lik * xr[v];
+                        for (int v = 0; v < 4; ++v) a[u][v] -= lik * xr[v];
+                    }
                 }
             }
         }
-        __syncthreads();
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u)
@@ -309,16 +316,17 @@ enum {
 
 // C[m][n] = alpha sum_k A[m][k] Bop[k][n] + beta C[m][n] in float64 (row-major,
 // leading dimensions lda / ldb / ldc; Bop = B or, with TB, B^T).  64 x 64
-// output tile per workgroup, 4 x 4 per thread, k in steps of 16 through LDS;
-// `tri` (TRI_* flags) limits the k range and the tiles.
+// output tile per workgroup, 4 x 4 per thread, k in steps of 32 through LDS
+// with the next step's operands loaded into registers during the current
+// one; `tri` (TRI_* flags) limits the k range and the tiles.
 template <bool TB>
 __global__ __launch_bounds__(256) void gptq_dgemm_kernel(int64_t M, int64_t N, int64_t K, double alpha,
                                                          const double *__restrict__ A, int64_t lda,
                                                          const double *__restrict__ Bm, int64_t ldb, double beta,
                                                          double *__restrict__ C, int64_t ldc, int tri)
 {
-    __shared__ double As[16][64 + 1];
-    __shared__ double Bs[16][64 + 1];
+    __shared__ double As[32][64 + 1];
+    __shared__ double Bs[32][64 + 1];
     const int tid = threadIdx.x, tx = tid % 16, ty = tid / 16;
     const int64_t m0 = (int64_t)blockIdx.y * 64, n0 = (int64_t)blockIdx.x * 64;
     if ((tri & TRI_C_LOWER) && n0 > m0 + 63) return;
@@ -327,19 +335,31 @@ __global__ __launch_bounds__(256) void gptq_dgemm_kernel(int64_t M, int64_t N, i
     if (tri & TRI_B_KLE_N) ke = min(ke, n0 + 64);
     if (tri & TRI_A_KLE_M) ke = min(ke, m0 + 64);
     double acc[4][4] = {};
-    for (int64_t k0 = kb; k0 < ke; k0 += 16) {
-        for (int e = tid; e < 64 * 16; e += 256) {
-            const int mm = e / 16, kk = e % 16;
-            const int64_t m = m0 + mm, k = k0 + kk;
-            As[kk][mm] = (m < M && k < K) ? A[m * lda + k] : 0.0;
-            int nn, kb;
-            if (TB) { nn = e / 16; kb = e % 16; } else { kb = e / 64; nn = e % 64; }
-            const int64_t n = n0 + nn, kq = k0 + kb;
-            Bs[kb][nn] = (n < N && kq < K) ? (TB ? Bm[n * ldb + kq] : Bm[kq * ldb + n]) : 0.0;
+    double ra[8], rb[8];
+    auto fetch = [&](int64_t k0) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int e = tid + 256 * q;
+            const int64_t m = m0 + e / 32, k = k0 + e % 32;
+            ra[q] = (m < M && k < ke) ? A[m * lda + k] : 0.0;
+            int64_t n, kq;
+            if (TB) { n = n0 + e / 32; kq = k0 + e % 32; } else { kq = k0 + e / 64; n = n0 + e % 64; }
+            rb[q] = (n < N && kq < ke) ? (TB ? Bm[n * ldb + kq] : Bm[kq * ldb + n]) : 0.0;
         }
+    };
+    if (kb < ke) fetch(kb);
+    for (int64_t k0 = kb; k0 < ke; k0 += 32) {
         __syncthreads();
 #pragma unroll
-        for (int kk = 0; kk < 16; ++kk) {
+        for (int q = 0; q < 8; ++q) {
+            const int e = tid + 256 * q;
+            As[e % 32][e / 32] = ra[q];
+            if (TB) Bs[e % 32][e / 32] = rb[q]; else Bs[e / 64][e % 64] = rb[q];
+        }
+        __syncthreads();
+        if (k0 + 32 < ke) fetch(k0 + 32);
+#pragma unroll
+        for (int kk = 0; kk < 32; ++kk) {
             double av[4], bv[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) av[i] = As[kk][ty + 16 * i];
@@ -350,7 +370,6 @@ __global__ __launch_bounds__(256) void gptq_dgemm_kernel(int64_t M, int64_t N, i
 #pragma unroll
                 for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fma(av[i], bv[j], acc[i][j]);
         }
-        __syncthreads();
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -366,74 +385,117 @@ __global__ __launch_bounds__(256) void gptq_dgemm_kernel(int64_t M, int64_t N, i
     }
 }
 
-// The same product with 128 x 128 output tiles and 8 x 8 outputs per thread
-// (64 fused multiply-adds per 16 LDS reads), k in steps of 8, the next step's
-// operands loaded into registers while the current one is multiplied; for
-// operands of at least 256 x 256.
-template <bool TB>
-__global__ __launch_bounds__(256) void gptq_dgemm_big_kernel(int64_t M, int64_t N, int64_t K, double alpha,
-                                                             const double *__restrict__ A, int64_t lda,
-                                                             const double *__restrict__ Bm, int64_t ldb,
-                                                             double beta, double *__restrict__ C, int64_t ldc, int tri)
+// The same product on the float64 matrix cores (v_mfma_f64_16x16x4f64: lane l
+// supplies A[l % 16][l / 16] and Bop[l / 16][l % 16] of a 16 x 4 by 4 x 16
+// step and holds C[l / 16 + 4 v][l % 16], v = 0..3).  TILE x TILE output tile
+// per workgroup of four waves (TILE = 128, or 64 for products too small to
+// fill the chip with 128-tiles), TILE/2 x TILE/2 per wave as NB x NB MFMA
+// blocks; k in steps of 16 through LDS (k-major rows, pitch TILE + 16
+// doubles: the four k rows of one fragment read fall on alternate halves of
+// the banks), the next step's operands loaded into registers while the
+// current one is multiplied.  Operands are read in aligned 16-byte pairs:
+// K, lda, ldb (and N when Bop = B) multiples of 8 and 2 doubles, base
+// pointers 16-byte aligned.
+typedef double gq_d4 __attribute__((ext_vector_type(4)));
+
+template <bool TB, int TILE>
+__global__ __launch_bounds__(256, 2) void gptq_dgemm_mfma_kernel(int64_t M, int64_t N, int64_t K, double alpha,
+                                                              const double *__restrict__ A, int64_t lda,
+                                                              const double *__restrict__ Bm, int64_t ldb,
+                                                              double beta, double *__restrict__ C, int64_t ldc,
+                                                              int tri)
 {
-    __shared__ double As[8][128 + 1];
-    __shared__ double Bs[8][128 + 1];
-    const int tid = threadIdx.x, tx = tid % 16, ty = tid / 16;
-    const int64_t m0 = (int64_t)blockIdx.y * 128, n0 = (int64_t)blockIdx.x * 128;
-    if ((tri & TRI_C_LOWER) && n0 > m0 + 127) return;
+    constexpr int PITCH = TILE + 16, NB = TILE / 32, CH = TILE / 16, CPR = 16 / CH, NP = CH / 2;
+    __shared__ __attribute__((aligned(16))) double As[16 * PITCH];
+    __shared__ __attribute__((aligned(16))) double Bs[16 * PITCH];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, wm = wv & 1, wn = wv >> 1;
+    const int64_t m0 = (int64_t)blockIdx.y * TILE, n0 = (int64_t)blockIdx.x * TILE;
+    if ((tri & TRI_C_LOWER) && n0 > m0 + TILE - 1) return;
     int64_t kb = 0, ke = K;
     if (tri & TRI_B_KGE_N) kb = n0;
-    if (tri & TRI_B_KLE_N) ke = min(ke, n0 + 128);
-    if (tri & TRI_A_KLE_M) ke = min(ke, m0 + 128);
-    double acc[8][8] = {};
-    double ra[4], rb[4];
+    if (tri & TRI_B_KLE_N) ke = min(ke, n0 + TILE);
+    if (tri & TRI_A_KLE_M) ke = min(ke, m0 + TILE);
+
+    // staging: thread t loads CH consecutive doubles (NP 16-byte pairs) of
+    // A row t / CPR, k chunk t % CPR; of Bop likewise with TB (B row = n),
+    // else of B row k = t / 16, n chunk t % 16.  Every k bound above is a
+    // multiple of 8, so a chunk is wholly inside or wholly outside [kb, ke).
+    const int sr = tid / CPR, sc = (tid % CPR) * CH, br = tid >> 4, bc = (tid & 15) * CH;
+    double2 ra[NP], rb[NP];
     auto fetch = [&](int64_t k0) {
+        {
+            const int64_t m = m0 + sr, k = k0 + sc;
+            const bool ok = m < M && k < ke;
+            const double2 *p = reinterpret_cast<const double2 *>(A + (ok ? m * lda + k : 0));
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int e = tid + 256 * q;
-            const int64_t m = m0 + e / 8, k = k0 + e % 8;
-            ra[q] = (m < M && k < ke) ? A[m * lda + k] : 0.0;
-            int64_t n, kq;
-            if (TB) { n = n0 + e / 8; kq = k0 + e % 8; } else { kq = k0 + e / 128; n = n0 + e % 128; }
-            rb[q] = (n < N && kq < ke) ? (TB ? Bm[n * ldb + kq] : Bm[kq * ldb + n]) : 0.0;
+            for (int q = 0; q < NP; ++q) ra[q] = ok ? p[q] : make_double2(0.0, 0.0);
+        }
+        if (TB) {
+            const int64_t n = n0 + sr, k = k0 + sc;
+            const bool ok = n < N && k < ke;
+            const double2 *p = reinterpret_cast<const double2 *>(Bm + (ok ? n * ldb + k : 0));
+#pragma unroll
+            for (int q = 0; q < NP; ++q) rb[q] = ok ? p[q] : make_double2(0.0, 0.0);
+        } else {
+            const int64_t k = k0 + br, n = n0 + bc;
+            const bool ok = k < ke && n < N;
+            const double2 *p = reinterpret_cast<const double2 *>(Bm + (ok ? k * ldb + n : 0));
+#pragma unroll
+            for (int q = 0; q < NP; ++q) rb[q] = ok ? p[q] : make_double2(0.0, 0.0);
         }
     };
+
+    gq_d4 acc[NB][NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j] = gq_d4{0.0, 0.0, 0.0, 0.0};
+
     if (kb < ke) fetch(kb);
-    for (int64_t k0 = kb; k0 < ke; k0 += 8) {
+    const int fr = lane & 15, fk = lane >> 4;
+    for (int64_t k0 = kb; k0 < ke; k0 += 16) {
         __syncthreads();
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int e = tid + 256 * q;
-            As[e % 8][e / 8] = ra[q];
-            if (TB) Bs[e % 8][e / 8] = rb[q]; else Bs[e / 128][e % 128] = rb[q];
+        for (int q = 0; q < NP; ++q) {
+            As[(sc + 2 * q) * PITCH + sr] = ra[q].x;
+            As[(sc + 2 * q + 1) * PITCH + sr] = ra[q].y;
+            if (TB) {
+                Bs[(sc + 2 * q) * PITCH + sr] = rb[q].x;
+                Bs[(sc + 2 * q + 1) * PITCH + sr] = rb[q].y;
+            } else {
+                *reinterpret_cast<double2 *>(&Bs[br * PITCH + bc + 2 * q]) = rb[q];
+            }
         }
         __syncthreads();
-        if (k0 + 8 < ke) fetch(k0 + 8);
+        if (k0 + 16 < ke) fetch(k0 + 16);
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-            double av[8], bv[8];
+        for (int k4 = 0; k4 < 4; ++k4) {
+            const int kr = (4 * k4 + fk) * PITCH;
+            double av[NB], bv[NB];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) av[i] = As[kk][ty + 16 * i];
+            for (int i = 0; i < NB; ++i) av[i] = As[kr + wm * (TILE / 2) + i * 16 + fr];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) bv[j] = Bs[kk][tx + 16 * j];
+            for (int j = 0; j < NB; ++j) bv[j] = Bs[kr + wn * (TILE / 2) + j * 16 + fr];
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
+            for (int i = 0; i < NB; ++i)
 #pragma unroll
-                for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_fma(av[i], bv[j], acc[i][j]);
+                for (int j = 0; j < NB; ++j) acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[i], bv[j], acc[i][j], 0, 0, 0);
         }
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int64_t m = m0 + ty + 16 * i;
-        if (m >= M) continue;
+    for (int i = 0; i < NB; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int64_t n = n0 + tx + 16 * j;
-            if (n >= N) continue;
-            double *c = C + m * ldc + n;
-            *c = beta == 0.0 ? alpha * acc[i][j] : beta * *c + alpha * acc[i][j];
+        for (int v = 0; v < 4; ++v) {
+            const int64_t m = m0 + wm * (TILE / 2) + i * 16 + fk + 4 * v;
+            if (m >= M) continue;
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                const int64_t n = n0 + wn * (TILE / 2) + j * 16 + fr;
+                if (n >= N) continue;
+                double *c = C + m * ldc + n;
+                *c = beta == 0.0 ? alpha * acc[i][j][v] : beta * *c + alpha * acc[i][j][v];
+            }
         }
-    }
 }
 
 template <bool TB>
@@ -441,9 +503,18 @@ static void dgemm(int64_t M, int64_t N, int64_t K, double alpha, const double *A
                   int64_t ldb, double beta, double *C, int64_t ldc, int tri, hipStream_t st)
 {
     if (M <= 0 || N <= 0) return;
-    if (M >= 256 && N >= 256) {
-        const dim3 grid((unsigned)((N + 127) / 128), (unsigned)((M + 127) / 128));
-        gptq_dgemm_big_kernel<TB><<<grid, 256, 0, st>>>(M, N, K, alpha, A, lda, Bm, ldb, beta, C, ldc, tri);
+    const bool aligned = K % 8 == 0 && lda % 2 == 0 && ldb % 2 == 0 && (TB || N % 8 == 0) &&
+                         reinterpret_cast<uintptr_t>(A) % 16 == 0 && reinterpret_cast<uintptr_t>(Bm) % 16 == 0;
+    if (M >= 256 && N >= 256 && aligned) {
+        // 128-tiles when they give at least two rounds of workgroups
+        const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
+        if (t128 >= 2 * 256) {
+            const dim3 grid((unsigned)((N + 127) / 128), (unsigned)((M + 127) / 128));
+            gptq_dgemm_mfma_kernel<TB, 128><<<grid, 256, 0, st>>>(M, N, K, alpha, A, lda, Bm, ldb, beta, C, ldc, tri);
+        } else {
+            const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 63) / 64));
+            gptq_dgemm_mfma_kernel<TB, 64><<<grid, 256, 0, st>>>(M, N, K, alpha, A, lda, Bm, ldb, beta, C, ldc, tri);
+        }
         return;
     }
     const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 63) / 64));
