@@ -84,7 +84,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=8, help="rows of W in the CPU sample")
-    ap.add_argument("--suite", choices=["headline", "formats", "gptq", "sigma"], default="headline",
+    ap.add_argument("--suite", choices=["headline", "formats", "gptq", "sigma", "gemm"], default="headline",
                     help="headline: the step above (one JSON line, the default); formats: every element / "
                          "scale format x B in {16, 32} x scale choice on the same W and h (one JSON line)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -116,6 +116,8 @@ def main():
         return gptq_suite(args, dev)
     if args.suite == "sigma":
         return sigma_suite(args, dev)
+    if args.suite == "gemm":
+        return gemm_suite(args, dev)
 
     cfg = synth.CONFIGS[2]
     W_cpu, X_cpu = synth.config_inputs(2)
@@ -458,6 +460,53 @@ def sigma_suite(args, dev):
                                                                "E2M1 elements, Naive scales", "sigmas": len(sigmas)},
                       "data": "synthetic", "quantizations": len(rows), "total_ms": round(t0.elapsed_time(t1), 3),
                       "b8_b16_crossing_sigma": crossings, "rows": out}), flush=True)
+
+
+def gemm_suite(args, dev):
+    """The MFMA products of the step on their own (X 16384x9728, W 2560x9728
+    bf16): output_reference (Y = X W^T stored, fp32), output_error_codes for
+    INT8 codes (fp16 operands) and NVFP4 codes (bf16 operands), and torch's
+    matmul of the same bf16 product (the vendor library) for comparison.
+    Median of 9 timed calls after 2 warm-ups, HIP events on torch's stream."""
+    import torch
+
+    import block_scaled_precision_hdiag_amd as hd
+    import synth
+
+    W_cpu, X_cpu = synth.config_inputs(2)
+    N, K = W_cpu.shape
+    M = X_cpu.shape[0]
+    W, X = W_cpu.to(dev), X_cpu.to(dev)
+    flops = 2.0 * M * N * K
+
+    def timed(f, reps=9):
+        for _ in range(2):
+            f()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            f()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return sorted(ts)[reps // 2]
+
+    res = {}
+    ref = hd.output_reference(X, W)
+    res["output_reference"] = timed(lambda: hd.output_reference(X, W, ref=ref))
+    ws = torch.empty(hd.output_error_codes_workspace_size(M, N, K), dtype=torch.uint8, device=dev)
+    for name, fmt, B in (("output_error_codes_int8", hd.INT8_E4M3, 32), ("output_error_codes_nvfp4", hd.NVFP4, 16)):
+        c, sc, _ = hd.quantize_blocks(hd.SSE_OPT, fmt, B, W)
+        res[name] = timed(lambda: hd.output_error_codes(fmt, B, X, c, sc, ref, N, K, workspace=ws))
+    Wc = W.contiguous()
+    res["torch_matmul_bf16"] = timed(lambda: torch.matmul(X, Wc.t()))
+    out = {k: {"ms": round(v, 4), "tflops": round(flops / v / 1e9, 1), "frac": round(flops / v / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4)}
+           for k, v in res.items()}
+    print(json.dumps({"suite": "gemm", "config": {"workload": "X W^T products, X 16384x9728 bf16, W 2560x9728 bf16",
+                                                  "M": M, "N": N, "K": K}, "data": "synthetic",
+                      "peak_tflops": MFMA_BF16_PEAK_TFLOPS, "results": out}), flush=True)
 
 
 def cpu_baseline(W_cpu, X_cpu, blocks, methods, fmt, rows, gpu_value):
