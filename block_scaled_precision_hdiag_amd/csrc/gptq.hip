@@ -31,6 +31,7 @@
 //      the panel's errors to every later column (an fp32 tiled GEMM).
 // Codes and scales are written at the original column / block positions.
 #include <algorithm>
+#include <cstdlib>
 
 #include "encode.hpp"
 #include "kernels.hpp"
@@ -506,9 +507,12 @@ static void dgemm(int64_t M, int64_t N, int64_t K, double alpha, const double *A
     const bool aligned = K % 8 == 0 && lda % 2 == 0 && ldb % 2 == 0 && (TB || N % 8 == 0) &&
                          reinterpret_cast<uintptr_t>(A) % 16 == 0 && reinterpret_cast<uintptr_t>(Bm) % 16 == 0;
     if (M >= 256 && N >= 256 && aligned) {
-        // 128-tiles when they give at least two rounds of workgroups
+        // 128-tiles when they give at least two rounds of workgroups, unless
+        // HD_GPTQ_GEMM_TILE (64 or 128) names the width
+        const char *env = getenv("HD_GPTQ_GEMM_TILE");
+        const int forced = env ? atoi(env) : 0;
         const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
-        if (t128 >= 2 * 256) {
+        if (forced == 128 || (forced != 64 && t128 >= 2 * 256)) {
             const dim3 grid((unsigned)((N + 127) / 128), (unsigned)((M + 127) / 128));
             gptq_dgemm_mfma_kernel<TB, 128><<<grid, 256, 0, st>>>(M, N, K, alpha, A, lda, Bm, ldb, beta, C, ldc, tri);
         } else {

@@ -322,7 +322,12 @@ hd_status dequantize_tensor_scaled(hd_format fmt, int32_t B, const uint8_t *code
  *     damped Hessian was not positive definite (that pivot is replaced by 1).
  * Workspace: gptq_workspace_size(B, N, K) bytes, about 2.6 K^2 doubles +
  * 1.5 K^2 floats + 4 N K bytes (2 GB for K = 9728).  Errors as
- * quantize_blocks, plus K > 65535 and a negative or non-finite damp. */
+ * quantize_blocks, plus K > 65535 and a negative or non-finite damp.
+ * Tuning: the environment variable HD_GPTQ_GEMM_TILE = 64 or 128, read at
+ * each call, fixes the output tile width of the factorisation's float64
+ * matrix-core products of 256 rows and columns and up; otherwise 128 is used
+ * when it gives at least two rounds of workgroups.  Results agree to float64
+ * rounding either way. */
 size_t gptq_hessian_workspace_size(int64_t M, int64_t K);
 hd_status gptq_hessian(const void *X, hd_dtype xt, int64_t M, int64_t K, float *H, void *ws, size_t ws_bytes,
                        void *stream);

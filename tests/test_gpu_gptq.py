@@ -103,6 +103,19 @@ def test_gptq_parity(fmt, B, method, ordered):
     compare(fmt, B, method, ordered, W, X, Hd)
 
 
+@pytest.mark.parametrize("tile", ["64", "128"])
+def test_gptq_parity_each_fp64_gemm_tile(tile, monkeypatch):
+    """K = 1024: the recursion's top products are 512 x 512, small enough that
+    the automatic choice takes 64-wide tiles; HD_GPTQ_GEMM_TILE forces each
+    width of the float64 matrix-core kernel, and both must meet the parity bar
+    (ragged N, GPTQ-Ord, H-Optimal)."""
+    monkeypatch.setenv("HD_GPTQ_GEMM_TILE", tile)
+    N, K, M = 45, 1024, 2048
+    W, X = gptq_inputs(N, K, M, 31)
+    Hd = hd.gptq_hessian(dev(X))
+    compare(hd.NVFP4, 16, hd.H_OPT, True, W, X, Hd)
+
+
 def test_gptq_parity_two_panels_and_fp32_weights():
     """K spans several 128-column panels with a short last one (K % 128 != 0),
     float32 weights, the OCP rule as the scale choice."""
