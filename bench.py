@@ -40,13 +40,22 @@ TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "int8_down_proj_2560x9728_hbm_t
 COUNTERS_PROFILE = os.path.join(ROOT, "profiles", "int8_down_proj_2560x9728_counters.md")
 
 
+# sources whose kernels the INT8 step never launches (other formats' searches,
+# the FP16-scale alternation, GPTQ, per-tensor scaling)
+_NOT_IN_STEP = {"alt_f16.hip", "gptq.hip", "tscale.hip", "search_fp8s.hip", "search_mxfp4.hip", "search_mxfp8.hip",
+                "search_nvfp4.hip", "search_nvfp4_ue4m4.hip", "search_nvfp4_ue5m3.hip", "search_nvint4.hip"}
+
+
 def source_hash():
-    """Hash of the HIP sources; counter-derived traffic is valid only for the
-    kernels it was measured on."""
+    """Hash of the HIP sources the step's kernels are built from (every file of
+    csrc/ but those listed above); counter-derived traffic is valid only for
+    the kernels it was measured on."""
     import glob
     import hashlib
     h = hashlib.sha256()
     for f in sorted(glob.glob(os.path.join(ROOT, "block_scaled_precision_hdiag_amd", "csrc", "*"))):
+        if os.path.basename(f) in _NOT_IN_STEP:
+            continue
         h.update(os.path.basename(f).encode())
         with open(f, "rb") as fh:
             h.update(fh.read())
