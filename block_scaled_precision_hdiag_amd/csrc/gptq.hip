@@ -725,51 +725,90 @@ __global__ __launch_bounds__(256) void gptq_panel_kernel(float *__restrict__ Wp,
     }
 }
 
-// Wp[n][k] -= sum_{c in panel} E[n][c - p0] V[c][k] for k >= pe (float32):
-// 64 x 64 output tiles, 4 x 4 per thread, the panel in steps of 16 via LDS.
+// Wp[n][k] -= sum_{c in panel} E[n][c - p0] V[c][k] for k >= pe, on the
+// float32 matrix cores (v_mfma_f32_32x32x2f32: lane l supplies A[l % 32][l / 32]
+// and B[l / 32][l % 32] of a 32 x 2 by 2 x 32 step and holds
+// C[8 (v / 4) + 4 (l / 32) + v % 4][l % 32], v = 0..15).  128 rows of W x 128
+// columns per workgroup of four waves, 64 x 64 (2 x 2 MFMA tiles) per wave;
+// the panel's BL errors in chunks of 32 through LDS (E chunk stored
+// panel-column-major, both with a pitch of 160 floats so the two half-waves
+// of a fragment read hit different bank halves), the next chunk loaded into
+// registers while the current one is multiplied.  BL, K and the panel end pe
+// are multiples of 4 (the loads are 16-byte vectors).
+typedef float gq_f16v __attribute__((ext_vector_type(16)));
+static constexpr int TR_PITCH = 160;
+
 __global__ __launch_bounds__(256) void gptq_trail_kernel(float *__restrict__ Wp, const float *__restrict__ V,
                                                          const float *__restrict__ E, int64_t N, int64_t K,
                                                          int64_t p0, int BL, int64_t pe)
 {
-    __shared__ float Es[16][64 + 1];
-    __shared__ float Vs[16][64 + 1];
-    const int tid = threadIdx.x, tx = tid % 16, ty = tid / 16;
-    const int64_t m0 = (int64_t)blockIdx.y * 64, k0 = pe + (int64_t)blockIdx.x * 64;
-    float acc[4][4] = {};
-    for (int q0 = 0; q0 < BL; q0 += 16) {
-        for (int e = tid; e < 64 * 16; e += 256) {
-            const int mm = e / 16, qq = e % 16;
-            const int64_t m = m0 + mm;
-            Es[qq][mm] = m < N ? E[m * BL + q0 + qq] : 0.0f;
-            const int qv = e / 64, kk = e % 64;
-            const int64_t k = k0 + kk;
-            Vs[qv][kk] = k < K ? V[(p0 + q0 + qv) * K + k] : 0.0f;
+    __shared__ __attribute__((aligned(16))) float Es[32 * TR_PITCH];
+    __shared__ __attribute__((aligned(16))) float Vs[32 * TR_PITCH];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, wm = wv & 1, wn = wv >> 1;
+    const int64_t n0 = (int64_t)blockIdx.y * 128, k0 = pe + (int64_t)blockIdx.x * 128;
+    // staging: E rows n0 + t / 2, chunk columns 16 (t % 2) ..; V chunk rows
+    // t / 8, columns k0 + 16 (t % 8) ..
+    const int er = tid >> 1, ec = (tid & 1) * 16, vr = tid >> 3, vc = (tid & 7) * 16;
+    float4 re[4], rv[4];
+    auto fetch = [&](int c0) {
+        const int64_t n = n0 + er;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            re[q] = n < N ? *reinterpret_cast<const float4 *>(E + n * BL + c0 + ec + 4 * q) : make_float4(0, 0, 0, 0);
+        const float *vrow = V + (p0 + c0 + vr) * K;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int64_t k = k0 + vc + 4 * q;
+            rv[q] = k < K ? *reinterpret_cast<const float4 *>(vrow + k) : make_float4(0, 0, 0, 0);
         }
+    };
+    gq_f16v acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+    fetch(0);
+    const int fr = lane & 31, fk = lane >> 5;
+    for (int c0 = 0; c0 < BL; c0 += 32) {
         __syncthreads();
 #pragma unroll
-        for (int qq = 0; qq < 16; ++qq) {
-            float av[4], bv[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) av[i] = Es[qq][ty + 16 * i];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) bv[j] = Vs[qq][tx + 16 * j];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(av[i], bv[j], acc[i][j]);
+        for (int q = 0; q < 4; ++q) {
+            Es[(ec + 4 * q + 0) * TR_PITCH + er] = re[q].x;
+            Es[(ec + 4 * q + 1) * TR_PITCH + er] = re[q].y;
+            Es[(ec + 4 * q + 2) * TR_PITCH + er] = re[q].z;
+            Es[(ec + 4 * q + 3) * TR_PITCH + er] = re[q].w;
+            *reinterpret_cast<float4 *>(&Vs[vr * TR_PITCH + vc + 4 * q]) = rv[q];
         }
         __syncthreads();
-    }
+        if (c0 + 32 < BL) fetch(c0 + 32);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int64_t m = m0 + ty + 16 * i;
-        if (m >= N) continue;
+        for (int kk = 0; kk < 16; ++kk) {
+            const int row = (2 * kk + fk) * TR_PITCH;
+            float a[2], bv[2];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t k = k0 + tx + 16 * j;
-            if (k < K) Wp[m * K + k] -= acc[i][j];
+            for (int i = 0; i < 2; ++i) a[i] = Es[row + wm * 64 + i * 32 + fr];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) bv[j] = Vs[row + wn * 64 + j * 32 + fr];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], bv[j], acc[i][j], 0, 0, 0);
         }
     }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int64_t n = n0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * fk + (v & 3);
+            if (n >= N) continue;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int64_t k = k0 + wn * 64 + j * 32 + fr;
+                if (k < K) Wp[n * K + k] -= acc[i][j][v];
+            }
+        }
 }
 
 // ------------------------------------------------------------ launchers ---
@@ -926,7 +965,7 @@ static hipError_t gq_run(int method, int B, const void *W, int wdt, int64_t N, i
         const int64_t pe = std::min<int64_t>(p0 + BL, K);
         gq_panel_m<EK, SK>(method, Wp, V, hp, col, N, K, B, p0, codes, scales, E, st);
         if (pe < K) {
-            const dim3 g((unsigned)((K - pe + 63) / 64), (unsigned)((N + 63) / 64));
+            const dim3 g((unsigned)((K - pe + 127) / 128), (unsigned)((N + 127) / 128));
             gptq_trail_kernel<<<g, 256, 0, st>>>(Wp, V, E, N, K, p0, (int)(pe - p0), pe);
         }
     }
