@@ -187,122 +187,148 @@ __global__ __launch_bounds__(256) void gptq_build_v_kernel(const double *__restr
 
 // ---------------------------------------------- float64 factorisation ---
 
+// Lane l's value of v, for a compile-time lane index (two 32-bit readlanes).
+__device__ __forceinline__ double gq_lane(double v, int l)
+{
+    const long long b = __double_as_longlong(v);
+    const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(b & 0xffffffff), l);
+    const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(b >> 32), l);
+    return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
 // Leaf: L = chol(P block), n <= 64, then Li = L^-1 (lower); only Li is kept.
-// Thread t owns the 4 x 4 tile rows 4 (t % 16) .., columns 4 (t / 16) .. of
-// the 64 x 64 block in registers, so the 16 owners of a tile column (the
-// diagonal tile's owner among them) share one wave.  Factorisation step j:
-// the owners of column j take the pivot from the diagonal owner by a lane
-// shuffle, scale the column and publish it through LDS; after one barrier
-// every thread subtracts its outer product.  Inverse step k: the owners of
-// row k of X scale it and publish it; after one barrier every later row
-// subtracts its multiple.  Published vectors alternate between two LDS slots,
-// so one barrier a step suffices; step loops are unrolled by four so that
-// register indices are compile-time constants.  Rows / columns >= n are
-// padded with the identity.  info[0] gets the first non-positive pivot's
-// global index + 1 (the pivot is then replaced by 1 so the factorisation
-// still finishes).
+// The block sits in LDS (rows / columns >= n padded with the identity) and is
+// factored in four panels of 16 columns:
+//   (a) one wave factors the panel's 16 x 16 diagonal block in registers,
+//       lane i holding row i (right-looking; pivots and column entries are
+//       passed between lanes by readlane, so the 16 steps need no barrier);
+//   (b) one thread per row below solves that row of the panel by forward
+//       substitution against the diagonal factor;
+//   (c) all threads subtract the panel's outer product from the trailing
+//       lower triangle.
+// Then each wave inverts one diagonal 16 x 16 factor the same way (lane i
+// holding row i of the inverse), and block forward substitution fills the
+// off-diagonal blocks: X_pq = -X_pp sum_{q <= m < p} L_pm X_mq.  Eighteen
+// barriers in all, against two per column for a column-at-a-time scheme.
+// info[0] gets the first non-positive pivot's global index + 1 (the pivot is
+// then replaced by 1 so the factorisation still finishes).
 __global__ __launch_bounds__(256) void gptq_chol_leaf_kernel(const double *__restrict__ P, int64_t ld, int64_t off,
                                                              int n, double *__restrict__ Li, int *__restrict__ info)
 {
-    __shared__ double colv[2][64];  // column j of L below the pivot, or row k of X
-    __shared__ double Ls[64][65];   // L, for the inverse
-    __shared__ double rdiag[64];    // 1 / L_kk
-    const int tid = threadIdx.x, ti = tid % 16, tk = tid / 16;
-    double a[4][4];
+    __shared__ double A[64][65];       // the block, then L (lower)
+    __shared__ double X[64][65];       // L^-1 (lower)
+    __shared__ double St[16][3 * 16 + 1];  // sums of the substitution
+    __shared__ double rdg[64];         // 1 / L_kk
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, li = lane & 15;
+    for (int e = tid; e < 64 * 64; e += 256) {
+        const int i = e >> 6, k = e & 63;
+        A[i][k] = (i < n && k <= i) ? P[(off + i) * ld + off + k] : (i == k ? 1.0 : 0.0);
+    }
+    __syncthreads();
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int p = 0; p < 4; ++p) {
+        const int c0 = 16 * p, T = 48 - 16 * p;
+        // (a) diagonal block: lanes 0..15 of wave 0 (the others repeat them)
+        if (wv == 0) {
+            double d[16];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int i = 4 * ti + u, k = 4 * tk + v;
-            a[u][v] = (i < n && k <= i) ? P[(off + i) * ld + off + k] : (i == k ? 1.0 : 0.0);
+            for (int k = 0; k < 16; ++k) d[k] = k <= li ? A[c0 + li][c0 + k] : 0.0;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                double piv = gq_lane(d[j], j);
+                if (!(piv > 0.0)) {
+                    if (lane == j && info && c0 + j < n) atomicCAS(info, 0, (int)(off + c0 + j + 1));
+                    piv = 1.0;
+                }
+                const double pv = sqrt(piv), r = 1.0 / pv;
+                d[j] = li > j ? d[j] * r : (li == j ? pv : 0.0);
+#pragma unroll
+                for (int k = j + 1; k < 16; ++k) d[k] -= d[j] * gq_lane(d[j], k);
+            }
+            if (lane < 16) {
+#pragma unroll
+                for (int k = 0; k < 16; ++k) A[c0 + li][c0 + k] = k <= li ? d[k] : 0.0;
+                rdg[c0 + li] = 1.0 / d[li];
+            }
         }
-    // Cholesky: step j scales column j below the pivot by 1 / sqrt(pivot) and
-    // subtracts its outer product from the trailing lower triangle
-    for (int jt = 0; jt < 16; ++jt) {
+        __syncthreads();
+        if (T == 0) break;
+        // (b) rows below: L[r][c0 + q] = (A[r][c0 + q] - sum_{m < q} L[r][c0 + m] L[c0 + q][c0 + m]) / L_qq
+        if (tid < T) {
+            const int r = c0 + 16 + tid;
+            double x[16];
 #pragma unroll
-        for (int vj = 0; vj < 4; ++vj) {
-            const int j = 4 * jt + vj, b = j & 1;
-            if (tk == jt) {
-                // lanes 16 (jt % 4) .. + 15 of wave jt / 4; the diagonal owner is ti == jt
-                double d = __shfl(a[vj][vj], (jt & 3) * 16 + jt, 64);
-                if (!(d > 0.0)) {
-                    if (ti == jt && info && j < n) atomicCAS(info, 0, (int)(off + j + 1));
-                    d = 1.0;
-                }
-                const double p = sqrt(d), r = 1.0 / p;
+            for (int q = 0; q < 16; ++q) {
+                double sq = A[r][c0 + q];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int i = 4 * ti + u;
-                    if (i > j) a[u][vj] *= r;
-                    if (i == j) a[u][vj] = p;
-                    colv[b][i] = i > j ? a[u][vj] : 0.0;
-                }
+                for (int m = 0; m < q; ++m) sq -= x[m] * A[c0 + q][c0 + m];
+                x[q] = sq * rdg[c0 + q];
             }
-            __syncthreads();
-            if (ti >= jt) {
-                double ci[4], ck[4];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) ci[u] = colv[b][4 * ti + u];
+            for (int q = 0; q < 16; ++q) A[r][c0 + q] = x[q];
+        }
+        __syncthreads();
+        // (c) trailing lower triangle
+        for (int e = tid; e < T * T; e += 256) {
+            const int r = c0 + 16 + e / T, q = c0 + 16 + e % T;
+            if (q > r) continue;
+            double acc = 0.0;
 #pragma unroll
-                for (int v = 0; v < 4; ++v) ck[v] = colv[b][4 * tk + v];
+            for (int m = 0; m < 16; ++m) acc += A[r][c0 + m] * A[q][c0 + m];
+            A[r][q] -= acc;
+        }
+        __syncthreads();
+    }
+    // inverses of the diagonal factors: wave p, lanes 0..15 (lane i: row i)
+    {
+        const int c0 = 16 * wv;
+        double x[16];
 #pragma unroll
-                for (int u = 0; u < 4; ++u)
+        for (int m = 0; m < 16; ++m) x[m] = m == li ? 1.0 : 0.0;
 #pragma unroll
-                    for (int v = 0; v < 4; ++v)
-                        if (4 * tk + v > j && 4 * tk + v <= 4 * ti + u) a[u][v] -= ci[u] * ck[v];
+        for (int k = 0; k < 16; ++k) {
+            const double rk = rdg[c0 + k];
+            if (li == k) {
+#pragma unroll
+                for (int m = 0; m <= k; ++m) x[m] *= rk;
             }
+            const double lik = li > k ? A[c0 + li][c0 + k] : 0.0;
+#pragma unroll
+            for (int m = 0; m <= k; ++m) x[m] -= lik * gq_lane(x[m], k);
+        }
+        if (lane < 16) {
+#pragma unroll
+            for (int m = 0; m < 16; ++m) X[c0 + li][c0 + m] = m <= li ? x[m] : 0.0;
         }
     }
-    // L (lower) to LDS; X = identity tile
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int i = 4 * ti + u, k = 4 * tk + v;
-            Ls[i][k] = k <= i ? a[u][v] : 0.0;
-            a[u][v] = i == k ? 1.0 : 0.0;
-        }
     __syncthreads();
-    if (tid < 64) rdiag[tid] = 1.0 / Ls[tid][tid];
-    __syncthreads();
-    // L^-1 by a right-looking solve of L X = I: at step k row k of X is final
-    // once scaled by 1 / L_kk, and every later row subtracts L_ik times it
-    for (int kt = 0; kt < 16; ++kt) {
+    // block forward substitution, block rows 1..3
 #pragma unroll
-        for (int uk = 0; uk < 4; ++uk) {
-            const int k = 4 * kt + uk, b = k & 1;
-            if (ti == kt) {
-                const double rk = rdiag[k];
+    for (int p = 1; p < 4; ++p) {
+        // St[a][16 q + b] = sum_{m = q}^{p-1} sum_t L[16p + a][16m + t] X[16m + t][16q + b]
+        for (int e = tid; e < 256 * p; e += 256) {
+            const int q = e >> 8, a = (e >> 4) & 15, b = e & 15;
+            double acc = 0.0;
+            for (int m = q; m < p; ++m)
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    a[uk][v] *= rk;
-                    colv[b][4 * tk + v] = a[uk][v];
-                }
-            }
-            __syncthreads();
-            if (ti >= kt) {
-                double xr[4];
-#pragma unroll
-                for (int v = 0; v < 4; ++v) xr[v] = colv[b][4 * tk + v];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int i = 4 * ti + u;
-                    if (i > k) {
-                        const double lik = Ls[i][k];
-#pragma unroll
-                        for (int v = 0; v < 4; ++v) a[u][v] -= lik * xr[v];
-                    }
-                }
-            }
+                for (int t = 0; t < 16; ++t) acc += A[16 * p + a][16 * m + t] * X[16 * m + t][16 * q + b];
+            St[a][16 * q + b] = acc;
         }
+        __syncthreads();
+        // X_pq[a][b] = -sum_{t <= a} X_pp[a][t] St[t][16 q + b]
+        for (int e = tid; e < 256 * p; e += 256) {
+            const int q = e >> 8, a = (e >> 4) & 15, b = e & 15;
+            double acc = 0.0;
+#pragma unroll
+            for (int t = 0; t < 16; ++t) acc += t <= a ? X[16 * p + a][16 * p + t] * St[t][16 * q + b] : 0.0;
+            X[16 * p + a][16 * q + b] = -acc;
+        }
+        __syncthreads();
     }
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int i = 4 * ti + u, k = 4 * tk + v;
-            if (i < n && k < n) Li[(off + i) * ld + off + k] = k <= i ? a[u][v] : 0.0;
-        }
+    for (int e = tid; e < 64 * 64; e += 256) {
+        const int i = e >> 6, k = e & 63;
+        if (i < n && k < n) Li[(off + i) * ld + off + k] = k <= i ? X[i][k] : 0.0;
+    }
 }
 
 // Structure flags of the float64 GEMM: operands known to be zero outside a
