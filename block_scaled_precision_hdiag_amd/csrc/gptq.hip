@@ -243,7 +243,7 @@ __global__ __launch_bounds__(256) void gptq_chol_leaf_kernel(const double *__res
                 const double pv = sqrt(piv), r = 1.0 / pv;
                 d[j] = li > j ? d[j] * r : (li == j ? pv : 0.0);
 #pragma unroll
-                for (int k = j + 1; k < 16; ++k) d[k] -= d[j] * gq_lane(d[j], k);
+                for (int k = j + 1; k < 16; ++k) d[k] = __builtin_fma(-d[j], gq_lane(d[j], k), d[k]);
             }
             if (lane < 16) {
 #pragma unroll
@@ -261,7 +261,7 @@ __global__ __launch_bounds__(256) void gptq_chol_leaf_kernel(const double *__res
             for (int q = 0; q < 16; ++q) {
                 double sq = A[r][c0 + q];
 #pragma unroll
-                for (int m = 0; m < q; ++m) sq -= x[m] * A[c0 + q][c0 + m];
+                for (int m = 0; m < q; ++m) sq = __builtin_fma(-x[m], A[c0 + q][c0 + m], sq);
                 x[q] = sq * rdg[c0 + q];
             }
 #pragma unroll
@@ -274,7 +274,7 @@ __global__ __launch_bounds__(256) void gptq_chol_leaf_kernel(const double *__res
             if (q > r) continue;
             double acc = 0.0;
 #pragma unroll
-            for (int m = 0; m < 16; ++m) acc += A[r][c0 + m] * A[q][c0 + m];
+            for (int m = 0; m < 16; ++m) acc = __builtin_fma(A[r][c0 + m], A[q][c0 + m], acc);
             A[r][q] -= acc;
         }
         __syncthreads();
@@ -294,7 +294,7 @@ __global__ __launch_bounds__(256) void gptq_chol_leaf_kernel(const double *__res
             }
             const double lik = li > k ? A[c0 + li][c0 + k] : 0.0;
 #pragma unroll
-            for (int m = 0; m <= k; ++m) x[m] -= lik * gq_lane(x[m], k);
+            for (int m = 0; m <= k; ++m) x[m] = __builtin_fma(-lik, gq_lane(x[m], k), x[m]);
         }
         if (lane < 16) {
 #pragma unroll
@@ -311,7 +311,7 @@ __global__ __launch_bounds__(256) void gptq_chol_leaf_kernel(const double *__res
             double acc = 0.0;
             for (int m = q; m < p; ++m)
 #pragma unroll
-                for (int t = 0; t < 16; ++t) acc += A[16 * p + a][16 * m + t] * X[16 * m + t][16 * q + b];
+                for (int t = 0; t < 16; ++t) acc = __builtin_fma(A[16 * p + a][16 * m + t], X[16 * m + t][16 * q + b], acc);
             St[a][16 * q + b] = acc;
         }
         __syncthreads();
@@ -320,7 +320,7 @@ __global__ __launch_bounds__(256) void gptq_chol_leaf_kernel(const double *__res
             const int q = e >> 8, a = (e >> 4) & 15, b = e & 15;
             double acc = 0.0;
 #pragma unroll
-            for (int t = 0; t < 16; ++t) acc += t <= a ? X[16 * p + a][16 * p + t] * St[t][16 * q + b] : 0.0;
+            for (int t = 0; t <= a; ++t) acc = __builtin_fma(X[16 * p + a][16 * p + t], St[t][16 * q + b], acc);
             X[16 * p + a][16 * q + b] = -acc;
         }
         __syncthreads();
