@@ -341,21 +341,35 @@ enum {
     TRI_C_LOWER = 8   // only entries with n <= m are needed
 };
 
-// C[m][n] = alpha sum_k A[m][k] Bop[k][n] + beta C[m][n] in float64 (row-major,
-// leading dimensions lda / ldb / ldc; Bop = B or, with TB, B^T).  64 x 64
-// output tile per workgroup, 4 x 4 per thread, k in steps of 32 through LDS
-// with the next step's operands loaded into registers during the current
-// one; `tri` (TRI_* flags) limits the k range and the tiles.
+// One float64 product C[m][n] = alpha sum_k A[m][k] Bop[k][n] + beta C[m][n]
+// (row-major, leading dimensions lda / ldb / ldc; Bop = B or, with TB, B^T);
+// `tri` (TRI_* flags) limits the k range and the tiles; gx = output tiles
+// along N at the kernel's tile width.
+struct GqGemm {
+    int64_t M, N, K;
+    double alpha;
+    const double *A;
+    int64_t lda;
+    const double *B;
+    int64_t ldb;
+    double beta;
+    double *C;
+    int64_t ldc;
+    int tri, gx;
+};
+
+// 64 x 64 output tile (bx, by) on the VALU: 4 x 4 per thread of 256, k in
+// steps of 32 through LDS with the next step's operands loaded into
+// registers during the current one.
 template <bool TB>
-__global__ __launch_bounds__(256) void gptq_dgemm_kernel(int64_t M, int64_t N, int64_t K, double alpha,
-                                                         const double *__restrict__ A, int64_t lda,
-                                                         const double *__restrict__ Bm, int64_t ldb, double beta,
-                                                         double *__restrict__ C, int64_t ldc, int tri)
+__device__ __forceinline__ void gq_fma_tile(const GqGemm &g, int bx, int by, double (*As)[65], double (*Bs)[65])
 {
-    __shared__ double As[32][64 + 1];
-    __shared__ double Bs[32][64 + 1];
+    const int64_t M = g.M, N = g.N, K = g.K, lda = g.lda, ldb = g.ldb;
+    const double *__restrict__ A = g.A;
+    const double *__restrict__ Bm = g.B;
+    const int tri = g.tri;
     const int tid = threadIdx.x, tx = tid % 16, ty = tid / 16;
-    const int64_t m0 = (int64_t)blockIdx.y * 64, n0 = (int64_t)blockIdx.x * 64;
+    const int64_t m0 = (int64_t)by * 64, n0 = (int64_t)bx * 64;
     if ((tri & TRI_C_LOWER) && n0 > m0 + 63) return;
     int64_t kb = 0, ke = K;
     if (tri & TRI_B_KGE_N) kb = n0;
@@ -406,10 +420,31 @@ __global__ __launch_bounds__(256) void gptq_dgemm_kernel(int64_t M, int64_t N, i
         for (int j = 0; j < 4; ++j) {
             const int64_t n = n0 + tx + 16 * j;
             if (n >= N) continue;
-            double *c = C + m * ldc + n;
-            *c = beta == 0.0 ? alpha * acc[i][j] : beta * *c + alpha * acc[i][j];
+            double *c = g.C + m * g.ldc + n;
+            *c = g.beta == 0.0 ? g.alpha * acc[i][j] : g.beta * *c + g.alpha * acc[i][j];
         }
     }
+}
+
+template <bool TB>
+__global__ __launch_bounds__(256) void gptq_dgemm_kernel(GqGemm g)
+{
+    __shared__ double As[32][65];
+    __shared__ double Bs[32][65];
+    gq_fma_tile<TB>(g, blockIdx.x, blockIdx.y, As, Bs);
+}
+
+// Two independent products in one launch (the first with Bop = B^T, the
+// second with Bop = B): workgroups 0 .. nb1 - 1 take the first's tiles.
+__global__ __launch_bounds__(256) void gptq_dgemm_pair_kernel(GqGemm g1, GqGemm g2, int nb1)
+{
+    __shared__ double As[32][65];
+    __shared__ double Bs[32][65];
+    const int b = blockIdx.x;
+    if (b < nb1)
+        gq_fma_tile<true>(g1, b % g1.gx, b / g1.gx, As, Bs);
+    else
+        gq_fma_tile<false>(g2, (b - nb1) % g2.gx, (b - nb1) / g2.gx, As, Bs);
 }
 
 // The same product on the float64 matrix cores (v_mfma_f64_16x16x4f64: lane l
@@ -426,17 +461,15 @@ __global__ __launch_bounds__(256) void gptq_dgemm_kernel(int64_t M, int64_t N, i
 typedef double gq_d4 __attribute__((ext_vector_type(4)));
 
 template <bool TB, int TILE>
-__global__ __launch_bounds__(256, 2) void gptq_dgemm_mfma_kernel(int64_t M, int64_t N, int64_t K, double alpha,
-                                                              const double *__restrict__ A, int64_t lda,
-                                                              const double *__restrict__ Bm, int64_t ldb,
-                                                              double beta, double *__restrict__ C, int64_t ldc,
-                                                              int tri)
+__device__ __forceinline__ void gq_mfma_tile(const GqGemm &g, int bx, int by, double *As, double *Bs)
 {
     constexpr int PITCH = TILE + 16, NB = TILE / 32, CH = TILE / 16, CPR = 16 / CH, NP = CH / 2;
-    __shared__ __attribute__((aligned(16))) double As[16 * PITCH];
-    __shared__ __attribute__((aligned(16))) double Bs[16 * PITCH];
+    const int64_t M = g.M, N = g.N, K = g.K, lda = g.lda, ldb = g.ldb;
+    const double *__restrict__ A = g.A;
+    const double *__restrict__ Bm = g.B;
+    const int tri = g.tri;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, wm = wv & 1, wn = wv >> 1;
-    const int64_t m0 = (int64_t)blockIdx.y * TILE, n0 = (int64_t)blockIdx.x * TILE;
+    const int64_t m0 = (int64_t)by * TILE, n0 = (int64_t)bx * TILE;
     if ((tri & TRI_C_LOWER) && n0 > m0 + TILE - 1) return;
     int64_t kb = 0, ke = K;
     if (tri & TRI_B_KGE_N) kb = n0;
@@ -519,10 +552,63 @@ __global__ __launch_bounds__(256, 2) void gptq_dgemm_mfma_kernel(int64_t M, int6
             for (int j = 0; j < NB; ++j) {
                 const int64_t n = n0 + wn * (TILE / 2) + j * 16 + fr;
                 if (n >= N) continue;
-                double *c = C + m * ldc + n;
-                *c = beta == 0.0 ? alpha * acc[i][j][v] : beta * *c + alpha * acc[i][j][v];
+                double *c = g.C + m * g.ldc + n;
+                *c = g.beta == 0.0 ? g.alpha * acc[i][j][v] : g.beta * *c + g.alpha * acc[i][j][v];
             }
         }
+}
+
+template <bool TB, int TILE>
+__global__ __launch_bounds__(256, 2) void gptq_dgemm_mfma_kernel(GqGemm g)
+{
+    __shared__ __attribute__((aligned(16))) double As[16 * (TILE + 16)];
+    __shared__ __attribute__((aligned(16))) double Bs[16 * (TILE + 16)];
+    gq_mfma_tile<TB, TILE>(g, blockIdx.x, blockIdx.y, As, Bs);
+}
+
+template <int TILE>
+__global__ __launch_bounds__(256, 2) void gptq_dgemm_mfma_pair_kernel(GqGemm g1, GqGemm g2, int nb1)
+{
+    __shared__ __attribute__((aligned(16))) double As[16 * (TILE + 16)];
+    __shared__ __attribute__((aligned(16))) double Bs[16 * (TILE + 16)];
+    const int b = blockIdx.x;
+    if (b < nb1)
+        gq_mfma_tile<true, TILE>(g1, b % g1.gx, b / g1.gx, As, Bs);
+    else
+        gq_mfma_tile<false, TILE>(g2, (b - nb1) % g2.gx, (b - nb1) / g2.gx, As, Bs);
+}
+
+static GqGemm gq_gemm(int64_t M, int64_t N, int64_t K, double alpha, const double *A, int64_t lda, const double *Bm,
+                      int64_t ldb, double beta, double *C, int64_t ldc, int tri)
+{
+    GqGemm g;
+    g.M = M; g.N = N; g.K = K; g.alpha = alpha; g.A = A; g.lda = lda; g.B = Bm; g.ldb = ldb;
+    g.beta = beta; g.C = C; g.ldc = ldc; g.tri = tri; g.gx = 0;
+    return g;
+}
+
+// Which kernel a product takes: 0 the VALU 64-tiles, else the matrix-core
+// tile width.  Products of 256 rows and columns and up (with aligned
+// operands) go to the matrix cores, with 128-tiles when they give at least
+// two rounds of workgroups, unless HD_GPTQ_GEMM_TILE (64 or 128) names the
+// width.
+template <bool TB>
+static int gq_tile(const GqGemm &g)
+{
+    const bool aligned = g.K % 8 == 0 && g.lda % 2 == 0 && g.ldb % 2 == 0 && (TB || g.N % 8 == 0) &&
+                         reinterpret_cast<uintptr_t>(g.A) % 16 == 0 && reinterpret_cast<uintptr_t>(g.B) % 16 == 0;
+    if (!(g.M >= 256 && g.N >= 256 && aligned)) return 0;
+    const char *env = getenv("HD_GPTQ_GEMM_TILE");
+    const int forced = env ? atoi(env) : 0;
+    const int64_t t128 = ((g.M + 127) / 128) * ((g.N + 127) / 128);
+    return (forced == 128 || (forced != 64 && t128 >= 2 * 256)) ? 128 : 64;
+}
+
+static int64_t gq_tiles(GqGemm &g, int tile)
+{
+    const int t = tile ? tile : 64;
+    g.gx = (int)((g.N + t - 1) / t);
+    return (int64_t)g.gx * ((g.M + t - 1) / t);
 }
 
 template <bool TB>
@@ -530,25 +616,38 @@ static void dgemm(int64_t M, int64_t N, int64_t K, double alpha, const double *A
                   int64_t ldb, double beta, double *C, int64_t ldc, int tri, hipStream_t st)
 {
     if (M <= 0 || N <= 0) return;
-    const bool aligned = K % 8 == 0 && lda % 2 == 0 && ldb % 2 == 0 && (TB || N % 8 == 0) &&
-                         reinterpret_cast<uintptr_t>(A) % 16 == 0 && reinterpret_cast<uintptr_t>(Bm) % 16 == 0;
-    if (M >= 256 && N >= 256 && aligned) {
-        // 128-tiles when they give at least two rounds of workgroups, unless
-        // HD_GPTQ_GEMM_TILE (64 or 128) names the width
-        const char *env = getenv("HD_GPTQ_GEMM_TILE");
-        const int forced = env ? atoi(env) : 0;
-        const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
-        if (forced == 128 || (forced != 64 && t128 >= 2 * 256)) {
-            const dim3 grid((unsigned)((N + 127) / 128), (unsigned)((M + 127) / 128));
-            gptq_dgemm_mfma_kernel<TB, 128><<<grid, 256, 0, st>>>(M, N, K, alpha, A, lda, Bm, ldb, beta, C, ldc, tri);
-        } else {
-            const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 63) / 64));
-            gptq_dgemm_mfma_kernel<TB, 64><<<grid, 256, 0, st>>>(M, N, K, alpha, A, lda, Bm, ldb, beta, C, ldc, tri);
-        }
+    GqGemm g = gq_gemm(M, N, K, alpha, A, lda, Bm, ldb, beta, C, ldc, tri);
+    const int tile = gq_tile<TB>(g);
+    gq_tiles(g, tile);
+    const int t = tile ? tile : 64;
+    const dim3 grid((unsigned)g.gx, (unsigned)((M + t - 1) / t));
+    if (tile == 128)
+        gptq_dgemm_mfma_kernel<TB, 128><<<grid, 256, 0, st>>>(g);
+    else if (tile == 64)
+        gptq_dgemm_mfma_kernel<TB, 64><<<grid, 256, 0, st>>>(g);
+    else
+        gptq_dgemm_kernel<TB><<<grid, 256, 0, st>>>(g);
+}
+
+// Two independent products (g1 with Bop = B^T, g2 with Bop = B) in one launch
+// when both take the same kernel family and tile width, else one after the
+// other.
+static void dgemm_pair(GqGemm g1, GqGemm g2, hipStream_t st)
+{
+    const int t1 = gq_tile<true>(g1), t2 = gq_tile<false>(g2);
+    if (t1 != t2 || g1.M <= 0 || g1.N <= 0 || g2.M <= 0 || g2.N <= 0) {
+        dgemm<true>(g1.M, g1.N, g1.K, g1.alpha, g1.A, g1.lda, g1.B, g1.ldb, g1.beta, g1.C, g1.ldc, g1.tri, st);
+        dgemm<false>(g2.M, g2.N, g2.K, g2.alpha, g2.A, g2.lda, g2.B, g2.ldb, g2.beta, g2.C, g2.ldc, g2.tri, st);
         return;
     }
-    const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 63) / 64));
-    gptq_dgemm_kernel<TB><<<grid, 256, 0, st>>>(M, N, K, alpha, A, lda, Bm, ldb, beta, C, ldc, tri);
+    const int64_t nb1 = gq_tiles(g1, t1), nb2 = gq_tiles(g2, t2);
+    const unsigned grid = (unsigned)(nb1 + nb2);
+    if (t1 == 128)
+        gptq_dgemm_mfma_pair_kernel<128><<<grid, 256, 0, st>>>(g1, g2, (int)nb1);
+    else if (t1 == 64)
+        gptq_dgemm_mfma_pair_kernel<64><<<grid, 256, 0, st>>>(g1, g2, (int)nb1);
+    else
+        gptq_dgemm_pair_kernel<<<grid, 256, 0, st>>>(g1, g2, (int)nb1);
 }
 
 // Recursive Cholesky-with-inverse of the n x n diagonal block of P at `off`
@@ -570,10 +669,11 @@ static void cholinv(double *P, double *Li, int64_t ld, int64_t off, int64_t n, d
     // L21 = P21 L11^-T  (T: n2 x n1; L11^-T is upper triangular)
     dgemm<true>(n2, n1, n1, 1.0, P21, ld, Li11, ld, 0.0, T, n1, TRI_B_KLE_N, st);
     // S22 = P22 - L21 L21^T (symmetric: the recursion reads its lower triangle)
-    dgemm<true>(n2, n2, n1, -1.0, T, n1, T, n1, 1.0, P22, ld, TRI_C_LOWER, st);
-    // L21 L11^-1 (T2: n2 x n1), kept across the recursion on S22
+    // and L21 L11^-1 (T2: n2 x n1, kept across the recursion on S22): both
+    // read only T and L11^-1, so they share one launch
     double *Tm = T2;
-    dgemm<false>(n2, n1, n1, 1.0, T, n1, Li11, ld, 0.0, Tm, n1, TRI_B_KGE_N, st);
+    dgemm_pair(gq_gemm(n2, n2, n1, -1.0, T, n1, T, n1, 1.0, P22, ld, TRI_C_LOWER),
+               gq_gemm(n2, n1, n1, 1.0, T, n1, Li11, ld, 0.0, Tm, n1, TRI_B_KGE_N), st);
     cholinv(P, Li, ld, off + n1, n2, T, T2 + n2 * n1, info, st);
     // (L^-1)21 = -L22^-1 (L21 L11^-1), L22^-1 lower triangular
     dgemm<false>(n2, n1, n2, -1.0, Li22, ld, Tm, n1, 0.0, Li21, ld, TRI_A_KLE_M, st);
