@@ -758,6 +758,15 @@ __global__ __launch_bounds__(256) void gptq_panel_kernel(float *__restrict__ Wp,
         const int64_t c = p0 + l * SEGP + i;
         w[i] = (active && c < pe) ? Wp[n * K + c] : 0.0f;
     }
+    // vp[u][i]: V[c][p0 + l SEGP + i] for the next column c = u (mod 4)
+    float vp[4][SEGP];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int i = 0; i < SEGP; ++i) {
+            const int64_t c = p0 + u, k = p0 + l * SEGP + i;
+            vp[u][i] = (c < pe && k > c && k < pe) ? V[c * K + k] : 0.0f;
+        }
     for (int64_t cs = p0; cs < pe; cs += B) {
         // the block's current values, and its h
         __syncthreads();
@@ -811,41 +820,52 @@ __global__ __launch_bounds__(256) void gptq_panel_kernel(float *__restrict__ Wp,
         const float rs = s != 0.0f ? 1.0f / s : 0.0f;
         if (active && l == 0) store_scale<SK>(scales, n * nb + col[cs] / B, code);
         // encode the block's columns in order; each error goes to the later
-        // columns of the panel held by the row's lanes
+        // columns of the panel held by the row's lanes.  The row of V each
+        // column needs is loaded four columns ahead (B is a multiple of 4).
         uint32_t lo = 0;
-        for (int64_t c = cs; c < cs + B; ++c) {
-            const int own = (int)((c - p0) / SEGP), slot = (int)((c - p0) % SEGP);
-            float e = 0.0f;
-            if (l == own) {
-                float wv = 0.0f;
+        for (int64_t c4 = cs; c4 < cs + B; c4 += 4) {
 #pragma unroll
-                for (int i = 0; i < SEGP; ++i)
-                    if (i == slot) wv = w[i];
-                const float a = fabsf(wv);
-                const float x = s != 0.0f ? quotient<SK, false>(a, s, rs) : 0.0f;
-                const float y = round_elem<EK>(x);
-                const float wq = s * y;
-                e = wv - (__builtin_signbitf(wv) ? -wq : wq);
-                const uint32_t cd = elem_code<EK>(elem_index<EK>(y), __builtin_signbitf(wv) != 0);
-                if (active) {
-                    E[n * BL + (c - p0)] = e;
-                    const int64_t oc = col[c];
-                    if (elem_4bit(EK)) {
-                        if ((c & 1) == 0)
-                            lo = cd & 15u;
-                        else
-                            codes[n * (K / 2) + oc / 2] = (uint8_t)(lo | ((cd & 15u) << 4));
-                    } else {
-                        codes[n * K + oc] = (uint8_t)cd;
+            for (int u = 0; u < 4; ++u) {
+                const int64_t c = c4 + u;
+                const int own = (int)((c - p0) / SEGP), slot = (int)((c - p0) % SEGP);
+                float e = 0.0f;
+                if (l == own) {
+                    float wv = 0.0f;
+#pragma unroll
+                    for (int i = 0; i < SEGP; ++i)
+                        if (i == slot) wv = w[i];
+                    const float a = fabsf(wv);
+                    const float x = s != 0.0f ? quotient<SK, false>(a, s, rs) : 0.0f;
+                    const float y = round_elem<EK>(x);
+                    const float wq = s * y;
+                    e = wv - (__builtin_signbitf(wv) ? -wq : wq);
+                    const uint32_t cd = elem_code<EK>(elem_index<EK>(y), __builtin_signbitf(wv) != 0);
+                    if (active) {
+                        E[n * BL + (c - p0)] = e;
+                        const int64_t oc = col[c];
+                        if (elem_4bit(EK)) {
+                            if ((c & 1) == 0)
+                                lo = cd & 15u;
+                            else
+                                codes[n * (K / 2) + oc / 2] = (uint8_t)(lo | ((cd & 15u) << 4));
+                        } else {
+                            codes[n * K + oc] = (uint8_t)cd;
+                        }
                     }
                 }
-            }
-            e = __shfl(e, own, 64);
-            const float *vr = V + c * K;
+                e = __shfl(e, own, 64);
 #pragma unroll
-            for (int i = 0; i < SEGP; ++i) {
-                const int64_t k = p0 + l * SEGP + i;
-                if (k > c && k < pe) w[i] = __builtin_fmaf(-e, vr[k], w[i]);
+                for (int i = 0; i < SEGP; ++i) {
+                    const int64_t k = p0 + l * SEGP + i;
+                    if (k > c && k < pe) w[i] = __builtin_fmaf(-e, vp[u][i], w[i]);
+                }
+                // the V row of column c + 4
+                const int64_t cn = c + 4;
+#pragma unroll
+                for (int i = 0; i < SEGP; ++i) {
+                    const int64_t k = p0 + l * SEGP + i;
+                    vp[u][i] = (cn < pe && k > cn && k < pe) ? V[cn * K + k] : 0.0f;
+                }
             }
         }
     }
