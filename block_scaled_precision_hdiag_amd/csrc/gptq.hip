@@ -17,7 +17,8 @@
 //      order and J the reversal, in float64; a recursive Cholesky gives
 //      L^-1 for P = L L^T directly (leaves of 64 x 64 factored and inverted
 //      in LDS; above them L21 = P21 L11^-T, S22 = P22 - L21 L21^T,
-//      (L^-1)21 = -(L22^-1) L21 (L11^-1), all float64 GEMMs).  Then
+//      (L^-1)21 = -(L22^-1) L21 (L11^-1), all float64 GEMMs, on the matrix
+//      cores from 256 rows and columns up).  Then
 //      (Hp + lambda I)^-1 = U^T U with U = J L^-1 J (upper triangular), and the
 //      loop uses V[c][k] = U[c][k] / U[c][c] in float32.
 //   5. The column loop over panels of BL = 128 (256 for B = 256) columns:
@@ -28,7 +29,7 @@
 //      candidates, or the FP16 alternation), then encodes the block's columns
 //      one by one, broadcasting each error e = w - q to the row's lanes, which
 //      apply w_k -= e V[c][k] inside the panel; gptq_trail_kernel then applies
-//      the panel's errors to every later column (an fp32 tiled GEMM).
+//      the panel's errors to every later column (an fp32 matrix-core GEMM).
 // Codes and scales are written at the original column / block positions.
 #include <algorithm>
 #include <cstdlib>
