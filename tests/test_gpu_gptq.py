@@ -116,6 +116,25 @@ def test_gptq_parity_each_fp64_gemm_tile(tile, monkeypatch):
     compare(hd.NVFP4, 16, hd.H_OPT, True, W, X, Hd)
 
 
+@pytest.mark.parametrize("N,K,B,fmt", [(1, 8, 8, hd.NVFP4), (3, 24, 8, hd.INT8_E4M3), (5, 40, 8, hd.MXFP4),
+                                       (2, 16, 16, hd.NVINT4), (7, 200, 8, hd.NVFP4)])
+def test_gptq_tiny(N, K, B, fmt):
+    """Leaves smaller than one 16-column panel, a single row, K below one
+    64-wide leaf and a ragged leaf (K = 200: leaves of 64 and 8 columns)."""
+    W, X = gptq_inputs(N, K, 64, 41 + K)
+    Hd = hd.gptq_hessian(dev(X))
+    for ordered in (False, True):
+        c, s, order, info = hd.gptq_quantize(hd.SSE_OPT, fmt, B, dev(W), Hd, ordered=ordered)
+        torch.cuda.synchronize()
+        assert int(info.item()) == 0
+        c_o, s_o, order_o = oracle.gptq(hd.SSE_OPT, fmt, B, synth.bits(W), npy(Hd).astype(np.float64),
+                                        ordered=ordered)
+        np.testing.assert_array_equal(npy(order), order_o)
+        np.testing.assert_array_equal(scales_np(s), s_o)
+        np.testing.assert_array_equal(npy(hd.dequantize(fmt, B, c, s, N, K)),
+                                      oracle.dequantize(fmt, B, c_o, s_o, N, K))
+
+
 def test_gptq_parity_two_panels_and_fp32_weights():
     """K spans several 128-column panels with a short last one (K % 128 != 0),
     float32 weights, the OCP rule as the scale choice."""
