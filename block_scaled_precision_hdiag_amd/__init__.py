@@ -111,6 +111,21 @@ def _strerror(status):
     return lib().hdiag_strerror(status).decode()
 
 
+def hdiag_strerror(status):
+    """Static description of a status code; host-only."""
+    return _strerror(status)
+
+
+def hdiag_last_error():
+    """Description of the calling thread's last failure ("" if none); host-only."""
+    return lib().hdiag_last_error().decode()
+
+
+def hdiag_version():
+    """Library version string; host-only."""
+    return lib().hdiag_version().decode()
+
+
 def _check(status, what):
     if status != HD_OK:
         raise HdiagError(status, what, lib().hdiag_last_error().decode())
@@ -195,6 +210,10 @@ def dequantize(fmt, B, codes, scales, N, K, dtype=torch.float32, out=None):
     _check(lib().dequantize(fmt, B, _ptr(codes), _ptr(scales), N, K, _ptr(out), _dt(out), _stream(d)),
            "dequantize")
     return out
+
+
+def weight_error_workspace_size(N, K):
+    return int(lib().weight_error_workspace_size(N, K))
 
 
 def weight_error(W, Wq, sums=False, workspace=None, out=None):

@@ -28,6 +28,15 @@ def test_header_declares_the_binding_exports():
     assert sorted(declared_functions()) == sorted(hd.EXPORTS)
 
 
+def test_binding_has_every_declared_call():
+    """The Python binding offers each C entry point under the same name."""
+    missing = [n for n in hd.EXPORTS if not callable(getattr(hd, n, None))]
+    assert not missing
+    assert hd.hdiag_version().startswith("hdiag ")
+    assert hd.hdiag_strerror(hd.HD_OK)
+    assert hd.weight_error_workspace_size(64, 256) > 0
+
+
 def test_library_exports_every_declared_symbol():
     L = hd.lib()
     for name in declared_functions():
