@@ -93,7 +93,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=8, help="rows of W in the CPU sample")
-    ap.add_argument("--suite", choices=["headline", "formats", "gptq", "sigma", "gemm"], default="headline",
+    ap.add_argument("--suite", choices=["headline", "formats", "gptq", "sigma", "gemm", "hbm"], default="headline",
                     help="headline: the step above (one JSON line, the default); formats: every element / "
                          "scale format x B in {16, 32} x scale choice on the same W and h (one JSON line)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -127,6 +127,8 @@ def main():
         return sigma_suite(args, dev)
     if args.suite == "gemm":
         return gemm_suite(args, dev)
+    if args.suite == "hbm":
+        return hbm_suite(args, dev)
 
     cfg = synth.CONFIGS[2]
     W_cpu, X_cpu = synth.config_inputs(2)
@@ -469,6 +471,79 @@ def sigma_suite(args, dev):
                                                                "E2M1 elements, Naive scales", "sigmas": len(sigmas)},
                       "data": "synthetic", "quantizations": len(rows), "total_ms": round(t0.elapsed_time(t1), 3),
                       "b8_b16_crossing_sigma": crossings, "rows": out}), flush=True)
+
+
+def hbm_suite(args, dev):
+    """The HBM-bound stages at the large layer's size (W 8192x28672 bf16,
+    470 MB; X 65536x28672 bf16, 3.76 GB), each timed launch preceded by a
+    512 MB scratch write so the 256 MB Infinity Cache holds none of its input:
+    hdiag, Naive quantize (NVFP4 B = 16, INT8 B = 128), dequantize (to float32
+    and to bfloat16) and the weight error; median of 10 launches (HIP events
+    around the launch alone), algorithmic bytes / time against 8 TB/s, beside
+    a 4 GiB device-to-device copy as the measured ceiling."""
+    import torch
+
+    import block_scaled_precision_hdiag_amd as hd
+    import synth
+
+    W = synth.config_inputs(5, x_rows=0)[0].to(dev)
+    cfg = synth.CONFIGS[5]["X"]
+    M, K = cfg["M"], cfg["K"]
+    X = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    r = 0
+    for ch in synth.activation_chunks(M, K, cfg["seed"], cfg["n_out"], cfg["out_gain"], cfg["idx_seed"],
+                                      rows_per_chunk=8192):
+        X[r:r + ch.shape[0]] = ch.to(dev)
+        r += ch.shape[0]
+    N = W.shape[0]
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    def timed(f, reps=10):
+        f()
+        ts = []
+        for _ in range(reps):
+            scratch.fill_(1)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            f()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return sorted(ts)[reps // 2]
+
+    res = {}
+
+    def put(name, ms, nbytes):
+        res[name] = {"ms": round(ms, 4), "bytes": int(nbytes), "gbs": round(nbytes / ms / 1e6, 1),
+                     "frac": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
+
+    src = torch.empty(4 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    put("device_copy_4GiB", timed(lambda: dst.copy_(src)), 2 * src.numel())
+    del src, dst
+    h = torch.empty(K, dtype=torch.float32, device=dev)
+    ws_h = torch.empty(hd.hdiag_workspace_size(M, K), dtype=torch.uint8, device=dev)
+    put("hdiag", timed(lambda: hd.hdiag(X, out=h, workspace=ws_h)), M * K * 2 + K * 4)
+    del X
+    nw = N * K
+    for fmt, B, name, cbytes in ((hd.NVFP4, 16, "nvfp4_b16", 0.5), (hd.INT8_E4M3, 128, "int8_b128", 1.0)):
+        codes, scales, _ = hd.quantize_blocks(hd.NAIVE, fmt, B, W)
+        put("naive_" + name, timed(lambda: hd.quantize_blocks(hd.NAIVE, fmt, B, W, codes=codes, scales=scales)),
+            nw * (2 + cbytes) + nw // B)
+        Wq = torch.empty((N, K), dtype=torch.float32, device=dev)
+        put("dequantize_f32_" + name, timed(lambda: hd.dequantize(fmt, B, codes, scales, N, K, out=Wq)),
+            nw * (cbytes + 4) + nw // B)
+        Wb = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+        put("dequantize_bf16_" + name, timed(lambda: hd.dequantize(fmt, B, codes, scales, N, K, dtype=torch.bfloat16,
+                                                                  out=Wb)),
+            nw * (cbytes + 2) + nw // B)
+        ws_e = torch.empty(hd.weight_error_workspace_size(N, K), dtype=torch.uint8, device=dev)
+        put("weight_error_" + name, timed(lambda: hd.weight_error(W, Wq, workspace=ws_e)), nw * (2 + 4))
+        del Wq, Wb
+    print(json.dumps({"suite": "hbm", "config": {"workload": "HBM-bound stages, W 8192x28672 bf16, X 65536x28672 bf16, "
+                                                             "Infinity Cache flushed before each launch",
+                                                 "W": [N, K], "X": [M, K]},
+                      "data": "synthetic", "peak_gbs": HBM_PEAK_GBS, "results": res}), flush=True)
 
 
 def gemm_suite(args, dev):

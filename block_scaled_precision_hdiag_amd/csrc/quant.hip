@@ -37,9 +37,10 @@ __global__ __launch_bounds__(256) void encode_kernel(const T *__restrict__ W, in
     const int nv8 = left >= ENC_EPT ? ENC_EPT / 8 : (left > 0 ? (int)(left / 8) : 0);  // valid 8-chunks
     float w[ENC_EPT];
     if (nv8 == ENC_EPT / 8) {
-        // all four 16-byte loads issued back to back (no per-chunk branch)
+        // all four 16-byte loads issued back to back (no per-chunk branch),
+        // non-temporal: W is streamed once here
 #pragma unroll
-        for (int c = 0; c < ENC_EPT / 8; ++c) load8<T>(W + e0 + 8 * c, w + 8 * c);
+        for (int c = 0; c < ENC_EPT / 8; ++c) load8_nt<T>(W + e0 + 8 * c, w + 8 * c);
     } else {
 #pragma unroll
         for (int c = 0; c < ENC_EPT / 8; ++c) {
@@ -219,67 +220,90 @@ hipError_t launch_encode(int fmt, int B, const void *W, int wdt, int64_t N, int6
 // ------------------------------------------------------------ dequantize ---
 // x^ = s q ("Is Finer Better?" §2.1): sign * fl32(s * val(index)).
 // With a per-tensor scale t (tscale != NULL): t * fl32(s * val(index)).
+// Every store is one 16-byte vector per lane with the lanes of a wave on
+// consecutive addresses (VPS = 4 float32 or 8 bfloat16 outputs per lane and
+// store): lane l of a wave takes, in each of DQ_G groups, the VPS outputs
+// starting at wave_base + g 64 VPS + l VPS, whose codes it loads as one
+// 2- to 8-byte word and whose block scale (VPS divides B) it loads once.
+static constexpr int DQ_G = 4;
+
+template <int EK>
+__device__ __forceinline__ float dq_value(uint32_t code, float s, const float *tscale)
+{
+    uint32_t idx;
+    bool neg, ok = true;
+    if (EK == ELEM_INT8) {
+        const int q = (int)(int8_t)(uint8_t)code;
+        ok = q != -128;
+        neg = q < 0;
+        idx = (uint32_t)(q < 0 ? -q : q);
+    } else if (EK == ELEM_INT4) {
+        const int q = (int)((code ^ 8u) & 15u) - 8;  // two's complement nibble
+        ok = q != -8;
+        neg = q < 0;
+        idx = (uint32_t)(q < 0 ? -q : q);
+    } else if (EK == ELEM_E2M1) {
+        neg = (code & 8u) != 0;
+        idx = code & 7u;
+    } else {
+        neg = (code & 0x80u) != 0;
+        idx = code & 0x7Fu;
+        ok = idx != 0x7Fu;
+    }
+    float mag = ok ? s * elem_value<EK>(idx) : 0.0f;
+    if (tscale) mag = tscale[0] * mag;
+    return neg ? -mag : mag;
+}
+
 template <int EK, int SK, int OUT_BF16>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict__ codes,
                                                       const uint8_t *__restrict__ scales, int64_t total,
                                                       int B, void *__restrict__ out,
                                                       const float *__restrict__ tscale)
 {
-    const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
-    if (e0 >= total) return;
-    const int sc = load_scale<SK>(scales, e0 / B);
-    const float s = scale_code_valid(SK, sc) ? scale_value(SK, sc) : 0.0f;
-    uint32_t c[8];
-    if (elem_4bit(EK)) {
-        const uint32_t v = *reinterpret_cast<const uint32_t *>(codes + e0 / 2);
+    constexpr int VPS = OUT_BF16 ? 8 : 4;
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6;
+    const int64_t base = wave * (64 * VPS * DQ_G) + (int64_t)lane * VPS;
+    // all loads first (codes and scales of the DQ_G groups), then the stores
+    uint64_t cw[DQ_G];
+    int sc[DQ_G];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) c[j] = (v >> (4 * j)) & 15u;
-    } else {
-        const uint2 v = *reinterpret_cast<const uint2 *>(codes + e0);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            c[j] = (v.x >> (8 * j)) & 255u;
-            c[4 + j] = (v.y >> (8 * j)) & 255u;
+    for (int g = 0; g < DQ_G; ++g) {
+        const int64_t e = base + (int64_t)g * 64 * VPS;
+        cw[g] = 0;
+        sc[g] = 0;
+        if (e < total) {  // total % 8 == 0: a group starting inside is whole
+            if (elem_4bit(EK))
+                cw[g] = VPS == 8 ? *reinterpret_cast<const uint32_t *>(codes + e / 2)
+                                 : *reinterpret_cast<const uint16_t *>(codes + e / 2);
+            else
+                cw[g] = VPS == 8 ? *reinterpret_cast<const uint64_t *>(codes + e)
+                                 : *reinterpret_cast<const uint32_t *>(codes + e);
+            sc[g] = load_scale<SK>(scales, e / B);
         }
     }
-    float o[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        uint32_t idx;
-        bool neg, ok = true;
-        if (EK == ELEM_INT8) {
-            const int q = (int)(int8_t)(uint8_t)c[j];
-            ok = q != -128;
-            neg = q < 0;
-            idx = (uint32_t)(q < 0 ? -q : q);
-        } else if (EK == ELEM_INT4) {
-            const int q = (int)((c[j] ^ 8u) & 15u) - 8;  // two's complement nibble
-            ok = q != -8;
-            neg = q < 0;
-            idx = (uint32_t)(q < 0 ? -q : q);
-        } else if (EK == ELEM_E2M1) {
-            neg = (c[j] & 8u) != 0;
-            idx = c[j] & 7u;
+    for (int g = 0; g < DQ_G; ++g) {
+        const int64_t e = base + (int64_t)g * 64 * VPS;
+        if (e >= total) break;
+        const float s = scale_code_valid(SK, sc[g]) ? scale_value(SK, sc[g]) : 0.0f;
+        float o[VPS];
+#pragma unroll
+        for (int j = 0; j < VPS; ++j) {
+            const uint32_t code = elem_4bit(EK) ? (uint32_t)(cw[g] >> (4 * j)) & 15u : (uint32_t)(cw[g] >> (8 * j)) & 255u;
+            o[j] = dq_value<EK>(code, s, tscale);
+        }
+        if (OUT_BF16) {
+            uint4 v;
+            v.x = f32_to_bf16(o[0]) | (f32_to_bf16(o[1]) << 16);
+            v.y = f32_to_bf16(o[2]) | (f32_to_bf16(o[3]) << 16);
+            v.z = f32_to_bf16(o[4 % VPS]) | (f32_to_bf16(o[5 % VPS]) << 16);
+            v.w = f32_to_bf16(o[6 % VPS]) | (f32_to_bf16(o[7 % VPS]) << 16);
+            *reinterpret_cast<uint4 *>(static_cast<bf16_t *>(out) + e) = v;
         } else {
-            neg = (c[j] & 0x80u) != 0;
-            idx = c[j] & 0x7Fu;
-            ok = idx != 0x7Fu;
+            *reinterpret_cast<float4 *>(static_cast<float *>(out) + e) = make_float4(o[0], o[1], o[2], o[3]);
         }
-        float mag = ok ? s * elem_value<EK>(idx) : 0.0f;
-        if (tscale) mag = tscale[0] * mag;
-        o[j] = neg ? -mag : mag;
-    }
-    if (OUT_BF16) {
-        uint4 v;
-        v.x = f32_to_bf16(o[0]) | (f32_to_bf16(o[1]) << 16);
-        v.y = f32_to_bf16(o[2]) | (f32_to_bf16(o[3]) << 16);
-        v.z = f32_to_bf16(o[4]) | (f32_to_bf16(o[5]) << 16);
-        v.w = f32_to_bf16(o[6]) | (f32_to_bf16(o[7]) << 16);
-        *reinterpret_cast<uint4 *>(static_cast<bf16_t *>(out) + e0) = v;
-    } else {
-        float4 *p = reinterpret_cast<float4 *>(static_cast<float *>(out) + e0);
-        p[0] = make_float4(o[0], o[1], o[2], o[3]);
-        p[1] = make_float4(o[4], o[5], o[6], o[7]);
     }
 }
 
@@ -287,7 +311,9 @@ template <int EK, int SK>
 static hipError_t dequant_f(int B, const uint8_t *codes, const uint8_t *scales, int64_t total, void *out,
                             int out_t, const float *tscale, hipStream_t st)
 {
-    const dim3 grid((unsigned)((total / 8 + 255) / 256));
+    // one wave per 64 DQ_G VPS outputs (VPS = 8 for bfloat16, 4 for float32)
+    const int64_t per_wave = 64 * DQ_G * (out_t == 1 ? 8 : 4);
+    const dim3 grid((unsigned)(((total + per_wave - 1) / per_wave + 3) / 4));
     if (out_t == 1)
         dequant_kernel<EK, SK, 1><<<grid, 256, 0, st>>>(codes, scales, total, B, out, tscale);
     else
