@@ -30,30 +30,34 @@ __device__ __forceinline__ double encode8(const float *w, float s, float r, cons
         }
         return obj;
     }
-    // E2M1 / E4M3 elements: fl32(|w| / m) into the conversion instruction with
-    // the power of two p2 (s = m p2); the same arithmetic as the search
+    // E2M1 / E4M3 elements: fl32(w / m) into the conversion instruction with
+    // the power of two p2 (s = m p2); the same arithmetic as the search.  The
+    // quotient is an odd function of w (its sign is copied back because the
+    // correction steps turn -0 into +0) and the conversion keeps the sign,
+    // zero included, so its codes already carry the sign bits.
     const ScaleParts sp = scale_parts<SK>(s);
     float x[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        const float a = fabsf(w[j]);
         // (an FP16 scale's mantissa m is one of 1024: both quotient corrections)
-        float v = (s == 0.0f) ? 0.0f
-                              : (SK == SCALE_E8M0 ? a : quotient<SCALE_E4M3, ONE_STEP && SK != SCALE_F16>(a, sp.m, sp.rm));
-        if (EK == ELEM_E4M3) v = fminf(v, 448.0f * sp.p2);
+        float v = (s == 0.0f) ? w[j] * 0.0f
+                              : (SK == SCALE_E8M0 ? w[j]
+                                                  : __builtin_copysignf(quotient<SCALE_E4M3, ONE_STEP && SK != SCALE_F16>(
+                                                                            w[j], sp.m, sp.rm),
+                                                                        w[j]));
+        if (EK == ELEM_E4M3) v = fminf(fmaxf(v, -448.0f * sp.p2), 448.0f * sp.p2);
         x[j] = v;
     }
 #pragma unroll
     for (int j = 0; j < 8; j += 2) {
         const uint32_t c2 = EK == ELEM_E2M1 ? fp4x2(x[j], x[j + 1], sp.p2) : fp8x2(x[j], x[j + 1], sp.p2);
-        const uint32_t sh = EK == ELEM_E2M1 ? 4u : 8u, mask = EK == ELEM_E2M1 ? 7u : 0x7Fu;
-        const uint32_t sb = EK == ELEM_E2M1 ? 8u : 0x80u;
-        code[j] = (c2 & mask) | (__builtin_signbitf(w[j]) ? sb : 0u);
-        code[j + 1] = ((c2 >> sh) & mask) | (__builtin_signbitf(w[j + 1]) ? sb : 0u);
+        const uint32_t sh = EK == ELEM_E2M1 ? 4u : 8u, mask = EK == ELEM_E2M1 ? 15u : 0xFFu;
+        code[j] = c2 & mask;
+        code[j + 1] = (c2 >> sh) & mask;
         if (WANT_OBJ) {
             const hd_v2f v = EK == ELEM_E2M1 ? fp4x2_val(c2) : fp8x2_val(c2);
-            const double d0 = (double)fabsf(w[j]) - (double)(s * v.x);
-            const double d1 = (double)fabsf(w[j + 1]) - (double)(s * v.y);
+            const double d0 = (double)w[j] - (double)(s * v.x);
+            const double d1 = (double)w[j + 1] - (double)(s * v.y);
             obj += (om ? om[j] : 1.0) * (d0 * d0);
             obj += (om ? om[j + 1] : 1.0) * (d1 * d1);
         }

@@ -139,7 +139,8 @@ __host__ __device__ inline float scale_value(int sk, int c)
     return sk == SCALE_INT8 ? v / 127.0f : v;  // IEEE division (INT8 section)
 }
 
-// fl32(a / s) for a >= 0, s > 0, given r = fl32(1 / s).
+// fl32(a / s) for s > 0, given r = fl32(1 / s) (any sign of a: every step is
+// an odd function of a).
 //  - E8M0 grids: s is a power of two, so a * r is the exactly rounded quotient.
 //  - Otherwise: q0 = fl32(a r) is within two ulps of a/s; one correction
 //    q1 = fl32(q0 + fl32(a - s q0) r) (Markstein's residual step, both FMAs)
@@ -147,7 +148,7 @@ __host__ __device__ inline float scale_value(int sk, int c)
 //    residual, returns the correctly rounded quotient.  bfloat16 inputs need
 //    only the first correction: checked exhaustively (every bf16 value against
 //    every candidate scale) by the encode parity test, which runs this code.
-//  - a is clamped to 2^100 first: any quotient that large saturates the
+//  - |a| is clamped to 2^100 first: any quotient that large saturates the
 //    element grid for every E4M3-grid scale, and the FMAs stay finite.
 //  - FP16 scales take both corrections whatever the input type (the one-step
 //    check covered only the scale grids above).
@@ -155,7 +156,7 @@ template <int SK, bool ONE_STEP>
 __device__ __forceinline__ float quotient(float a, float s, float r)
 {
     if (SK == SCALE_E8M0) return a * r;
-    a = fminf(a, 0x1p100f);
+    a = __builtin_amdgcn_fmed3f(a, -0x1p100f, 0x1p100f);
     float q = a * r;
     float e = __builtin_fmaf(-q, s, a);
     q = __builtin_fmaf(e, r, q);
