@@ -11,12 +11,14 @@ namespace hd {
 // INT8: the amax itself stored as E4M3 and divided by 127) when GIVEN is false;
 // otherwise the scale code of each block comes from scales_in.
 //
-// Each thread owns 32 consecutive weights (four 16-byte bf16 loads) and writes
-// their codes as whole 16-byte stores (32 bytes for INT8 / E4M3, 16 for E2M1):
-// narrower per-lane stores were measured to multiply the bytes written to HBM.
-// Blocks of B <= 32 lie inside one thread (32 / B of them); a block of B > 32
-// spans B / 32 adjacent lanes, combined with shuffles.
-static constexpr int ENC_EPT = 32;
+// Each wave covers 2048 consecutive weights in four sub-chunks of 512: lane
+// l takes weights 512 k + 8 l .. + 7 of sub-chunk k (one 16-byte bf16 or two
+// float32 loads, the lanes of a wave on consecutive addresses: loads strided
+// across lanes were measured to cut the read rate), so a block of B weights
+// is B / 8 adjacent lanes of one sub-chunk (512 % B == 0), combined with
+// shuffles.  Codes go out as 4 (4-bit) or 8 bytes per lane and sub-chunk,
+// again on consecutive addresses; the first lane of a block writes its scale.
+static constexpr int ENC_SUB = 4;
 
 template <int EK, int SK, typename T, int B, bool GIVEN, bool OBJ>
 __global__ __launch_bounds__(256) void encode_kernel(const T *__restrict__ W, int64_t total, int64_t K,
@@ -25,132 +27,70 @@ __global__ __launch_bounds__(256) void encode_kernel(const T *__restrict__ W, in
                                                      uint8_t *__restrict__ codes, uint8_t *__restrict__ scales,
                                                      float *__restrict__ block_obj, int ocp)
 {
-    constexpr int TPB = B > ENC_EPT ? B / ENC_EPT : 1;  // lanes per block
-    constexpr int NBT = B < ENC_EPT ? ENC_EPT / B : 1;  // blocks per lane
-    constexpr int EB = B < ENC_EPT ? B : ENC_EPT;       // weights of one block in this lane
+    constexpr int LPB = B / 8;  // lanes per block
     constexpr bool ONE_STEP = sizeof(T) == 2;
-    const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * ENC_EPT;
-    // total % 8 == 0 and total % B == 0: the last thread may own fewer than 32
-    // weights, but whole blocks (and for B > 32 every lane of a block agrees)
-    const int64_t left = total - e0;
-    const bool active = left > 0;
-    const int nv8 = left >= ENC_EPT ? ENC_EPT / 8 : (left > 0 ? (int)(left / 8) : 0);  // valid 8-chunks
-    float w[ENC_EPT];
-    if (nv8 == ENC_EPT / 8) {
-        // all four 16-byte loads issued back to back (no per-chunk branch),
-        // non-temporal: W is streamed once here
+    const int lane = threadIdx.x & 63;
+    const int64_t wbase = (((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6) * (64 * 8 * ENC_SUB);
+    // total % B == 0 and B % 8 == 0: a sub-chunk starting below total is
+    // whole, and the lanes of one block are all in or all out
+    float w[ENC_SUB][8];
 #pragma unroll
-        for (int c = 0; c < ENC_EPT / 8; ++c) load8_nt<T>(W + e0 + 8 * c, w + 8 * c);
-    } else {
+    for (int k = 0; k < ENC_SUB; ++k) {
+        const int64_t e = wbase + 512 * k + 8 * lane;
+        if (e < total)
+            load8_nt<T>(W + e, w[k]);
+        else
 #pragma unroll
-        for (int c = 0; c < ENC_EPT / 8; ++c) {
-            if (c < nv8)
-                load8<T>(W + e0 + 8 * c, w + 8 * c);
-            else
-                for (int j = 0; j < 8; ++j) w[8 * c + j] = 0.0f;
-        }
+            for (int j = 0; j < 8; ++j) w[k][j] = 0.0f;
     }
-    double om[OBJ ? ENC_EPT : 1];
     const bool weighted = OBJ && h != nullptr;
-    if (OBJ && weighted && active) {
-        // rows hold K % 8 == 0 weights: an 8-chunk never crosses a row end
 #pragma unroll
-        for (int c = 0; c < ENC_EPT / 8; ++c) {
-            const int64_t k0 = (e0 + 8 * c) % K;
+    for (int k = 0; k < ENC_SUB; ++k) {
+        const int64_t e = wbase + 512 * k + 8 * lane;
+        const bool in = e < total;
+        double om[OBJ ? 8 : 1];
+        if (OBJ && weighted && in) {
+            const int64_t k0 = e % K;  // rows hold K % 8 == 0 weights: no row end inside
 #pragma unroll
-            for (int j = 0; j < 8; ++j) om[OBJ ? 8 * c + j : 0] = c < nv8 ? (double)h[k0 + j] : 0.0;
+            for (int j = 0; j < 8; ++j) om[OBJ ? j : 0] = (double)h[k0 + j];
         }
-    }
-    uint32_t c[ENC_EPT];
-    int code[NBT];
-    double obj[NBT];
-#pragma unroll
-    for (int bb = 0; bb < NBT; ++bb) {
         float amax = 0.0f;
 #pragma unroll
-        for (int j = 0; j < EB; ++j) amax = fmaxf(amax, fabsf(w[bb * EB + j]));
-        amax = group_max<TPB>(amax);
-        const int64_t blk = (e0 + bb * EB) / B;
+        for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(w[k][j]));
+        amax = group_max<LPB>(amax);
+        const int64_t blk = e / B;
+        int code;
         float s;
         if (GIVEN) {
-            code[bb] = (bb * EB < 8 * nv8) ? load_scale<SK>(scales_in, blk) : 0;
-            s = scale_code_valid(SK, code[bb]) ? scale_value(SK, code[bb]) : 0.0f;
+            code = in ? load_scale<SK>(scales_in, blk) : 0;
+            s = scale_code_valid(SK, code) ? scale_value(SK, code) : 0.0f;
         } else {
             // ocp (E8M0 grids only): the OCP MX floor rule instead of the snap
             if constexpr (SK == SCALE_E8M0)
-                code[bb] = ocp ? ocp_code<EK>(amax) : naive_code<EK, SK>(amax);
+                code = ocp ? ocp_code<EK>(amax) : naive_code<EK, SK>(amax);
             else
-                code[bb] = naive_code<EK, SK>(amax);
-            s = scale_value(SK, code[bb]);
+                code = naive_code<EK, SK>(amax);
+            s = scale_value(SK, code);
         }
         const float r = (s != 0.0f) ? 1.0f / s : 0.0f;
-        double o = 0.0;
+        uint32_t c[8];
+        double o = encode8<EK, SK, ONE_STEP, OBJ>(w[k], s, r, (weighted && in) ? om : nullptr, c);
+        if (OBJ) o = group_sum<LPB>(o);
+        if (!in) continue;
+        if (elem_4bit(EK)) {
+            uint32_t v = 0;
 #pragma unroll
-        for (int q = 0; q < EB / 8; ++q) {
-            const int j0 = bb * EB + 8 * q;
-            o += encode8<EK, SK, ONE_STEP, OBJ>(w + j0, s, r, (weighted && active) ? om + (OBJ ? j0 : 0) : nullptr,
-                                                c + j0);
+            for (int j = 0; j < 8; ++j) v |= (c[j] & 15u) << (4 * j);
+            *reinterpret_cast<uint32_t *>(codes + e / 2) = v;
+        } else {
+            uint2 v;
+            v.x = (c[0] & 255u) | ((c[1] & 255u) << 8) | ((c[2] & 255u) << 16) | ((c[3] & 255u) << 24);
+            v.y = (c[4] & 255u) | ((c[5] & 255u) << 8) | ((c[6] & 255u) << 16) | ((c[7] & 255u) << 24);
+            *reinterpret_cast<uint2 *>(codes + e) = v;
         }
-        obj[bb] = OBJ ? group_sum<TPB>(o) : 0.0;
-    }
-    if (!active) return;
-    if (nv8 < ENC_EPT / 8) {  // tail thread: 8-weight stores, then its whole blocks
-        for (int cc = 0; cc < nv8; ++cc) store_codes8<EK>(codes, e0 + 8 * cc, c + 8 * cc);
-        for (int bb = 0; bb < NBT; ++bb) {
-            if (bb * EB >= 8 * nv8) break;
-            const int64_t blk = (e0 + bb * EB) / B;
-            if (!GIVEN) store_scale<SK>(scales, blk, code[bb]);
-            if (OBJ) block_obj[blk] = (float)obj[bb];
-        }
-        return;
-    }
-    if (elem_4bit(EK)) {
-        uint32_t v[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            v[i] = 0;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) v[i] |= (c[8 * i + j] & 15u) << (4 * j);
-        }
-        // non-temporal stores: the codes are not read again by this kernel
-        __builtin_nontemporal_store(hd_u32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<hd_u32x4 *>(codes + e0 / 2));
-    } else {
-        uint32_t v[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            v[i] = (c[4 * i] & 255u) | ((c[4 * i + 1] & 255u) << 8) | ((c[4 * i + 2] & 255u) << 16) |
-                   ((c[4 * i + 3] & 255u) << 24);
-        hd_u32x4 *p = reinterpret_cast<hd_u32x4 *>(codes + e0);
-        __builtin_nontemporal_store(hd_u32x4{v[0], v[1], v[2], v[3]}, p);
-        __builtin_nontemporal_store(hd_u32x4{v[4], v[5], v[6], v[7]}, p + 1);
-    }
-    if ((threadIdx.x % TPB) == 0) {
-        const int64_t blk0 = e0 / B;
-        if (!GIVEN && SK == SCALE_F16) {
-            // 2-byte codes
-            uint16_t *p = reinterpret_cast<uint16_t *>(scales) + blk0;
-            if (NBT == 4) {  // two 4-byte stores: the scales need only 4-byte alignment
-                uint32_t *q = reinterpret_cast<uint32_t *>(p);
-                q[0] = (uint32_t)code[0] | ((uint32_t)code[NBT > 1 ? 1 : 0] << 16);
-                q[1] = (uint32_t)code[NBT > 2 ? 2 : 0] | ((uint32_t)code[NBT > 3 ? 3 : 0] << 16);
-            } else if (NBT == 2)
-                *reinterpret_cast<uint32_t *>(p) = (uint32_t)code[0] | ((uint32_t)code[NBT > 1 ? 1 : 0] << 16);
-            else
-                *p = (uint16_t)code[0];
-        } else if (!GIVEN) {
-            if (NBT == 4)
-                *reinterpret_cast<uint32_t *>(scales + blk0) =
-                    (uint32_t)code[0] | ((uint32_t)code[NBT > 1 ? 1 : 0] << 8) |
-                    ((uint32_t)code[NBT > 2 ? 2 : 0] << 16) | ((uint32_t)code[NBT > 3 ? 3 : 0] << 24);
-            else if (NBT == 2)
-                *reinterpret_cast<uint16_t *>(scales + blk0) =
-                    (uint16_t)((uint32_t)code[0] | ((uint32_t)code[NBT > 1 ? 1 : 0] << 8));
-            else
-                scales[blk0] = (uint8_t)code[0];
-        }
-        if (OBJ) {
-#pragma unroll
-            for (int bb = 0; bb < NBT; ++bb) block_obj[blk0 + bb] = (float)obj[bb];
+        if (lane % LPB == 0) {
+            if (!GIVEN) store_scale<SK>(scales, blk, code);
+            if (OBJ) block_obj[blk] = (float)o;
         }
     }
 }
@@ -160,7 +100,8 @@ static hipError_t encode_b(int B, const void *W, int64_t N, int64_t K, const flo
                            uint8_t *codes, uint8_t *scales, float *bo, int ocp, hipStream_t st)
 {
     const int64_t total = N * K;
-    const dim3 grid((unsigned)((total / ENC_EPT + 255) / 256));
+    const int64_t waves = (total + 64 * 8 * ENC_SUB - 1) / (64 * 8 * ENC_SUB);
+    const dim3 grid((unsigned)((waves + 3) / 4));
     const T *w = static_cast<const T *>(W);
 #define HD_ENC_CASE(BB)                                                                                      \
     case BB:                                                                                                 \
