@@ -168,32 +168,52 @@ hipError_t launch_encode(int fmt, int B, const void *W, int wdt, int64_t N, int6
 // 2- to 8-byte word and whose block scale (VPS divides B) it loads once.
 static constexpr int DQ_G = 4;
 
-template <int EK>
-__device__ __forceinline__ float dq_value(uint32_t code, float s, const float *tscale)
+// VPS outputs from VPS codes packed in cw (4 or 8 bits each): the signed grid
+// values times s (exact products), times the tensor scale if given.  E2M1 and
+// E4M3 codes go through the gfx950 conversions (two values per instruction,
+// sign and signed zero kept); the integer grids sign-extend.  Codes outside
+// a grid (E4M3 0x7F / 0xFF, INT8 -128, INT4 -8) give a zero of their sign.
+template <int EK, int VPS>
+__device__ __forceinline__ void dq_group(uint64_t cw, float s, const float *tscale, float *o)
 {
-    uint32_t idx;
-    bool neg, ok = true;
-    if (EK == ELEM_INT8) {
-        const int q = (int)(int8_t)(uint8_t)code;
-        ok = q != -128;
-        neg = q < 0;
-        idx = (uint32_t)(q < 0 ? -q : q);
-    } else if (EK == ELEM_INT4) {
-        const int q = (int)((code ^ 8u) & 15u) - 8;  // two's complement nibble
-        ok = q != -8;
-        neg = q < 0;
-        idx = (uint32_t)(q < 0 ? -q : q);
-    } else if (EK == ELEM_E2M1) {
-        neg = (code & 8u) != 0;
-        idx = code & 7u;
+    if (EK == ELEM_E2M1) {
+        hd_v2f v[4];
+        v[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4((uint32_t)cw, 1.0f, 0);
+        v[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4((uint32_t)cw, 1.0f, 1);
+        if constexpr (VPS == 8) {
+            v[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4((uint32_t)cw, 1.0f, 2);
+            v[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4((uint32_t)cw, 1.0f, 3);
+        }
+#pragma unroll
+        for (int p = 0; p < VPS / 2; ++p) {
+            o[2 * p] = s * v[p].x;
+            o[2 * p + 1] = s * v[p].y;
+        }
+    } else if (EK == ELEM_E4M3) {
+#pragma unroll
+        for (int p = 0; p < VPS / 2; ++p) {
+            const uint32_t word = (uint32_t)(cw >> (32 * (p / 2))) >> (16 * (p & 1));
+            const hd_v2f v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(word, 1.0f, false);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t code = (uint32_t)(cw >> (8 * (2 * p + h))) & 255u;
+                const float z = (code & 0x80u) ? -0.0f : 0.0f;
+                o[2 * p + h] = (code & 0x7Fu) == 0x7Fu ? z : s * (h ? v.y : v.x);
+            }
+        }
     } else {
-        neg = (code & 0x80u) != 0;
-        idx = code & 0x7Fu;
-        ok = idx != 0x7Fu;
+        constexpr int BITS = EK == ELEM_INT8 ? 8 : 4;
+#pragma unroll
+        for (int j = 0; j < VPS; ++j) {
+            const int q = __builtin_amdgcn_sbfe((int)(uint32_t)(cw >> (BITS * j)), 0, BITS);
+            o[j] = q == -(1 << (BITS - 1)) ? -0.0f : s * (float)q;
+        }
     }
-    float mag = ok ? s * elem_value<EK>(idx) : 0.0f;
-    if (tscale) mag = tscale[0] * mag;
-    return neg ? -mag : mag;
+    if (tscale) {
+        const float t = tscale[0];
+#pragma unroll
+        for (int j = 0; j < VPS; ++j) o[j] = t * o[j];
+    }
 }
 
 template <int EK, int SK, int OUT_BF16>
@@ -230,11 +250,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict_
         if (e >= total) break;
         const float s = scale_code_valid(SK, sc[g]) ? scale_value(SK, sc[g]) : 0.0f;
         float o[VPS];
-#pragma unroll
-        for (int j = 0; j < VPS; ++j) {
-            const uint32_t code = elem_4bit(EK) ? (uint32_t)(cw[g] >> (4 * j)) & 15u : (uint32_t)(cw[g] >> (8 * j)) & 255u;
-            o[j] = dq_value<EK>(code, s, tscale);
-        }
+        dq_group<EK, VPS>(cw[g], s, tscale, o);
         if (OUT_BF16) {
             uint4 v;
             v.x = f32_to_bf16(o[0]) | (f32_to_bf16(o[1]) << 16);
