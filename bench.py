@@ -5,11 +5,15 @@ Workload (one "step"): the INT8 / E4M3-scale case on the qwantize "Results"
 page's layer shape -- W 2560 x 9728 bf16 (a seeded Student-t(4) x 0.02 stand-in
 with per-row lognormal gain for the down_proj weight) and calibration X
 16384 x 9728 bf16 (N(0,1), 8 outlier channels x 50):
-    hdiag(X) and output_reference(X, W) (Y = X W^T and ||Y||^2, which every
-    output error of the step is measured against), then for B in
+    hdiag(X), output_gram(X) (G = X^T X, stored as float16 correlations) and
+    output_reference_gram (||X W^T||^2 from G), then for B in
     {32, 64, 128, 256} and each of Naive, SSE-Optimal, H-Optimal:
     quantize_blocks (scale choice + encode), dequantize, weight error and
-    output error (output_error_codes: one MFMA product from the codes).
+    output error (output_error_gram: sum_n d_n^T G d_n for D = Wq - W, one
+    N x K x K MFMA product over G's lower block triangle).
+    --output-route direct measures the output error with X instead:
+    output_reference (Y = X W^T) once and output_error_codes (X Wq^T - Y, one
+    M x N x K MFMA product) per quantisation.
 value = 12 quantisations x 2560 x 9728 weights / step time, in Gweights/s.
 Inputs are resident in HBM before timing starts.  Per-call GPU times come from
 HIP events recorded on the stream the kernels run on, over the timed steps.
@@ -96,6 +100,8 @@ def parse():
     ap.add_argument("--suite", choices=["headline", "formats", "gptq", "sigma", "gemm", "hbm"], default="headline",
                     help="headline: the step above (one JSON line, the default); formats: every element / "
                          "scale format x B in {16, 32} x scale choice on the same W and h (one JSON line)")
+    ap.add_argument("--output-route", choices=["gram", "direct"], default="gram",
+                    help="output error through G = X^T X (gram) or through X W^T (direct)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="before timing, run one device copy of this many MB (a known-size kernel that "
                          "calibrates HBM byte counters)")
@@ -145,8 +151,15 @@ def main():
     h = torch.empty(K, dtype=torch.float32, device=dev)
     ws_h = torch.empty(hd.hdiag_workspace_size(M, K), dtype=torch.uint8, device=dev)
     ws_w = torch.empty(hd.lib().weight_error_workspace_size(N, K), dtype=torch.uint8, device=dev)
-    ref = torch.empty(hd.output_reference_size(M, N, K), dtype=torch.uint8, device=dev)
-    ws_o = torch.empty(hd.output_error_codes_workspace_size(M, N, K), dtype=torch.uint8, device=dev)
+    gram_route = args.output_route == "gram"
+    if gram_route:
+        gram = torch.empty(hd.output_gram_size(K), dtype=torch.uint8, device=dev)
+        ws_g = torch.empty(hd.output_gram_workspace_size(M, K), dtype=torch.uint8, device=dev)
+        ws_o = torch.empty(hd.output_error_gram_workspace_size(N, K), dtype=torch.uint8, device=dev)
+        ysq = torch.empty(1, dtype=torch.float64, device=dev)
+    else:
+        ref = torch.empty(hd.output_reference_size(M, N, K), dtype=torch.uint8, device=dev)
+        ws_o = torch.empty(hd.output_error_codes_workspace_size(M, N, K), dtype=torch.uint8, device=dev)
     codes = {B: torch.empty((N, K), dtype=torch.uint8, device=dev) for B in blocks}
     scales = {B: torch.empty((N, K // B), dtype=torch.uint8, device=dev) for B in blocks}
     Wq = torch.empty((N, K), dtype=torch.float32, device=dev)
@@ -178,7 +191,11 @@ def main():
 
     def step(rec):
         timed("hdiag", 0, lambda: hd.hdiag(X, out=h, workspace=ws_h), rec)
-        timed("output_reference", 0, lambda: hd.output_reference(X, W, ref=ref), rec)
+        if gram_route:
+            timed("output_gram", 0, lambda: hd.output_gram(X, h=h, gram=gram, workspace=ws_g), rec)
+            timed("output_reference", 0, lambda: hd.output_reference_gram(W, gram, workspace=ws_o, out=ysq), rec)
+        else:
+            timed("output_reference", 0, lambda: hd.output_reference(X, W, ref=ref), rec)
         for bi, B in enumerate(blocks):
             for mi, (mname, m) in enumerate(methods):
                 stage = "naive" if m == hd.NAIVE else "search_" + mname
@@ -187,9 +204,14 @@ def main():
                 timed("dequantize", B, lambda: hd.dequantize(fmt, B, codes[B], scales[B], N, K, out=Wq), rec)
                 timed("weight_error", B, lambda: hd.weight_error(W, Wq, workspace=ws_w, out=werr[bi, mi:mi + 1]),
                       rec)
-                timed("output_error", B,
-                      lambda: hd.output_error_codes(fmt, B, X, codes[B], scales[B], ref, N, K, workspace=ws_o,
-                                                    out=oerr[bi, mi:mi + 1]), rec)
+                if gram_route:
+                    timed("output_error", B,
+                          lambda: hd.output_error_gram(fmt, B, codes[B], scales[B], W, gram, ysq, workspace=ws_o,
+                                                       out=oerr[bi, mi:mi + 1]), rec)
+                else:
+                    timed("output_error", B,
+                          lambda: hd.output_error_codes(fmt, B, X, codes[B], scales[B], ref, N, K, workspace=ws_o,
+                                                        out=oerr[bi, mi:mi + 1]), rec)
 
     for _ in range(args.warmup):
         step(False)
@@ -216,8 +238,11 @@ def main():
         "naive": ("hbm", sum(bytes_w + N * K + N * K // B for B in blocks) / len(blocks)),
         "dequantize": ("hbm", sum(N * K + N * K // B + N * K * 4 for B in blocks) / len(blocks)),
         "weight_error": ("hbm", bytes_w + N * K * 4),
-        "output_reference": ("mfma", 2.0 * M * N * K),
-        "output_error": ("mfma", 2.0 * M * N * K),
+        # the gram route: G's K (K + 1) / 2 distinct entries (2 M flops each),
+        # and the quadratic forms d^T G d over G's symmetric halves (N K^2)
+        "output_gram": ("mfma", 1.0 * M * K * (K + 1)),
+        "output_reference": ("mfma", 1.0 * N * K * K if gram_route else 2.0 * M * N * K),
+        "output_error": ("mfma", 1.0 * N * K * K if gram_route else 2.0 * M * N * K),
         "search_sse": ("alu", N * K * n_cand * SEARCH_OPS["sse"]),
         "search_h": ("alu", N * K * n_cand * SEARCH_OPS["h"]),
     }
@@ -272,8 +297,11 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "INT8 (E4M3 scales) on W 2560x9728 bf16, h from X 16384x9728 bf16; "
-                               "B in {32,64,128,256}; Naive + SSE-Optimal + H-Optimal; hdiag, X W^T reference, "
-                               "quantize, dequantize, weight and output error per step",
+                               "B in {32,64,128,256}; Naive + SSE-Optimal + H-Optimal; hdiag, "
+                               + ("X^T X Gram matrix and ||X W^T||^2 from it, " if gram_route else
+                                  "X W^T reference, ")
+                               + "quantize, dequantize, weight and output error per step",
+                   "output_route": args.output_route,
                    "W": [N, K], "X": [M, K], "format": "INT8_E4M3", "blocks": blocks,
                    "quantizations_per_step": len(blocks) * len(methods)},
         "roofline": roofline,

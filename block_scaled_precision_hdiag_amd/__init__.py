@@ -9,7 +9,8 @@ computing anything some other way: build it with
 
 Names follow the C ABI: ``hdiag``, ``quantize_blocks``, ``encode_blocks``,
 ``dequantize``, ``weight_error``, ``output_error``, ``output_error_given_ref``,
-``output_reference``, ``output_error_codes``, ``gptq_hessian``, ``gptq_quantize``,
+``output_reference``, ``output_error_codes``, ``output_gram``, ``output_reference_gram``,
+``output_error_gram``, ``gptq_hessian``, ``gptq_quantize``,
 ``hdiag_format_info``.
 """
 import ctypes
@@ -38,7 +39,9 @@ F16_SCALES = (FP4_F16, INT4_F16)
 EXPORTS = ["hdiag", "hdiag_workspace_size", "quantize_blocks", "encode_blocks", "dequantize",
            "weight_error", "weight_error_workspace_size", "output_error", "output_error_workspace_size",
            "output_error_given_ref", "output_reference", "output_reference_size", "output_error_codes",
-           "output_error_codes_workspace_size", "quantize_blocks_tensor_scaled",
+           "output_error_codes_workspace_size", "output_gram", "output_gram_size", "output_gram_workspace_size",
+           "output_reference_gram", "output_error_gram", "output_error_gram_workspace_size",
+           "quantize_blocks_tensor_scaled",
            "quantize_blocks_tensor_scaled_workspace_size", "dequantize_tensor_scaled", "gptq_hessian", "gptq_hessian_workspace_size", "gptq_quantize",
            "gptq_workspace_size",
            "hdiag_strerror", "hdiag_last_error", "hdiag_format_info", "hdiag_version"]
@@ -81,6 +84,15 @@ def lib():
         L.output_error_codes_workspace_size.argtypes = [i64, i64, i64]
         L.output_error_codes_workspace_size.restype = sz
         L.output_error_codes.argtypes = [i32, i32, P, i32, i64, P, P, i64, i64, P, sz, P, P, P, sz, P]
+        L.output_gram_size.argtypes = [i64]
+        L.output_gram_size.restype = sz
+        L.output_gram_workspace_size.argtypes = [i64, i64]
+        L.output_gram_workspace_size.restype = sz
+        L.output_gram.argtypes = [P, i32, i64, i64, P, P, sz, P, sz, P]
+        L.output_error_gram_workspace_size.argtypes = [i64, i64]
+        L.output_error_gram_workspace_size.restype = sz
+        L.output_reference_gram.argtypes = [P, i32, i64, i64, P, sz, P, P, sz, P]
+        L.output_error_gram.argtypes = [i32, i32, P, P, P, i32, i64, i64, P, sz, P, P, P, P, sz, P]
         L.hdiag_strerror.argtypes = [i32]
         L.hdiag_strerror.restype = ctypes.c_char_p
         L.hdiag_last_error.argtypes = []
@@ -100,7 +112,7 @@ def lib():
         L.gptq_quantize.argtypes = [i32, i32, i32, P, i32, i64, i64, P, ctypes.c_double, i32, P, P, P, P, P, sz, P]
         for name in ("hdiag", "quantize_blocks", "encode_blocks", "dequantize", "weight_error",
                      "output_error", "output_error_given_ref", "output_reference", "output_error_codes",
-                     "hdiag_format_info", "gptq_hessian", "gptq_quantize", "quantize_blocks_tensor_scaled",
+                     "output_gram", "output_reference_gram", "output_error_gram", "hdiag_format_info", "gptq_hessian", "gptq_quantize", "quantize_blocks_tensor_scaled",
                      "dequantize_tensor_scaled"):
             getattr(L, name).restype = i32
         _lib = L
@@ -313,6 +325,62 @@ def output_error_codes(fmt, B, X, codes, scales, ref, N, K, sums=False, workspac
     _check(lib().output_error_codes(fmt, B, _ptr(X), _dt(X), M, _ptr(codes), _ptr(scales), N, K, _ptr(ref),
                                     ref.numel(), _ptr(out), _ptr(s), _ptr(ws), ws.numel(), _stream(d)),
            "output_error_codes")
+    return (out, s) if sums else out
+
+
+def output_gram_size(K):
+    return int(lib().output_gram_size(K))
+
+
+def output_gram_workspace_size(M, K):
+    return int(lib().output_gram_workspace_size(M, K))
+
+
+def output_gram(X, h=None, gram=None, workspace=None):
+    """Fill (or allocate) the Gram buffer of X (bfloat16 [M, K]) for
+    output_reference_gram / output_error_gram.  h: hdiag(X) if already
+    computed.  Returns it as a uint8 device tensor."""
+    d = _dev(X)
+    M, K = X.shape
+    if gram is None:
+        gram = torch.empty(max(output_gram_size(K), 16), dtype=torch.uint8, device=d)
+    need = output_gram_workspace_size(M, K)
+    ws = workspace if workspace is not None else torch.empty(max(need, 16), dtype=torch.uint8, device=d)
+    _check(lib().output_gram(_ptr(X), _dt(X), M, K, _ptr(h), _ptr(gram), gram.numel(), _ptr(ws), ws.numel(),
+                             _stream(d)), "output_gram")
+    return gram
+
+
+def output_error_gram_workspace_size(N, K):
+    return int(lib().output_error_gram_workspace_size(N, K))
+
+
+def output_reference_gram(W, gram, workspace=None, out=None):
+    """||X W^T||_F^2 from the Gram buffer of X, as a float64 device tensor [1]."""
+    d = _dev(W)
+    N, K = W.shape
+    if out is None:
+        out = torch.empty(1, dtype=torch.float64, device=d)
+    need = output_error_gram_workspace_size(N, K)
+    ws = workspace if workspace is not None else torch.empty(max(need, 16), dtype=torch.uint8, device=d)
+    _check(lib().output_reference_gram(_ptr(W), _dt(W), N, K, _ptr(gram), gram.numel(), _ptr(out), _ptr(ws),
+                                       ws.numel(), _stream(d)), "output_reference_gram")
+    return out
+
+
+def output_error_gram(fmt, B, codes, scales, W, gram, ysq, sums=False, workspace=None, out=None):
+    """||X Wq^T - X W^T||_F / sqrt(ysq) for Wq = dequantize(fmt, B, codes,
+    scales), from the Gram buffer of X; ysq from output_reference_gram."""
+    d = _dev(W)
+    N, K = W.shape
+    if out is None:
+        out = torch.empty(1, dtype=torch.float64, device=d)
+    s = torch.empty(2, dtype=torch.float64, device=d) if sums else None
+    need = output_error_gram_workspace_size(N, K)
+    ws = workspace if workspace is not None else torch.empty(max(need, 16), dtype=torch.uint8, device=d)
+    _check(lib().output_error_gram(fmt, B, _ptr(codes), _ptr(scales), _ptr(W), _dt(W), N, K, _ptr(gram),
+                                   gram.numel(), _ptr(ysq), _ptr(out), _ptr(s), _ptr(ws), ws.numel(), _stream(d)),
+           "output_error_gram")
     return (out, s) if sums else out
 
 

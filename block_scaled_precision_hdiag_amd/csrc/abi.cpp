@@ -309,6 +309,81 @@ hd_status output_error_codes(hd_format fmt, int32_t B, const void *X, hd_dtype x
                       "output_error_codes");
 }
 
+size_t output_gram_size(int64_t K)
+{
+    if (K < 0) return 0;
+    return (size_t)hd::output_gram_layout(K).bytes;
+}
+
+size_t output_gram_workspace_size(int64_t M, int64_t K)
+{
+    if (M < 0 || K < 0) return 0;
+    return hd::output_gram_ws(M, K);
+}
+
+hd_status output_gram(const void *X, hd_dtype xt, int64_t M, int64_t K, const float *h, void *gram,
+                      size_t gram_bytes, void *ws, size_t ws_bytes, void *stream)
+{
+    HD_REQUIRE(valid_dtype(xt), "unknown dtype %d", (int)xt);
+    HD_REQUIRE(M >= 0 && K >= 0, "negative size");
+    HD_REQUIRE(M <= (int64_t)1 << 31 && K <= (int64_t)1 << 17, "size too large");
+    HD_REQUIRE(K % 8 == 0, "K=%lld is not a multiple of 8", (long long)K);
+    if (xt != HD_BF16) return fail(HD_ERR_UNSUPPORTED, "output_gram needs bfloat16 X (the MFMA product)");
+    HD_CHECK_PTR(gram, true);
+    HD_REQUIRE(gram_bytes >= (size_t)hd::output_gram_layout(K).bytes, "gram buffer too small");
+    HD_CHECK_PTR(ws, true);
+    HD_REQUIRE(ws_bytes >= hd::output_gram_ws(M, K), "workspace too small");
+    HD_CHECK_PTR(X, M * K > 0);
+    HD_CHECK_PTR(h, h != nullptr);
+    return hip_status(hd::launch_output_gram(X, M, K, h, gram, ws, (hipStream_t)stream), "output_gram");
+}
+
+size_t output_error_gram_workspace_size(int64_t N, int64_t K)
+{
+    if (N < 0 || K < 0) return 0;
+    return hd::output_error_gram_ws(N, K);
+}
+
+hd_status output_reference_gram(const void *W, hd_dtype wt, int64_t N, int64_t K, const void *gram,
+                                size_t gram_bytes, double *ysq, void *ws, size_t ws_bytes, void *stream)
+{
+    HD_REQUIRE(valid_dtype(wt), "unknown dtype %d", (int)wt);
+    HD_REQUIRE(N >= 0 && K >= 0, "negative size");
+    HD_REQUIRE(N <= (int64_t)1 << 31 && K <= (int64_t)1 << 17, "size too large");
+    HD_REQUIRE(K % 8 == 0, "K=%lld is not a multiple of 8", (long long)K);
+    HD_REQUIRE(ysq != nullptr, "ysq is NULL");
+    HD_CHECK_PTR(gram, true);
+    HD_REQUIRE(gram_bytes >= (size_t)hd::output_gram_layout(K).bytes, "gram buffer too small");
+    HD_CHECK_PTR(ws, true);
+    HD_REQUIRE(ws_bytes >= hd::output_error_gram_ws(N, K), "workspace too small");
+    HD_CHECK_PTR(W, N * K > 0);
+    return hip_status(hd::launch_output_error_gram(-1, 8, nullptr, nullptr, W, wt, N, K, gram, nullptr, ysq,
+                                                   nullptr, nullptr, ws, (hipStream_t)stream),
+                      "output_reference_gram");
+}
+
+hd_status output_error_gram(hd_format fmt, int32_t B, const uint8_t *codes, const uint8_t *scales, const void *W,
+                            hd_dtype wt, int64_t N, int64_t K, const void *gram, size_t gram_bytes,
+                            const double *ysq, double *out, double *sums, void *ws, size_t ws_bytes, void *stream)
+{
+    hd_status s = check_quant_shape(fmt, B, N, K);
+    if (s != HD_OK) return s;
+    HD_REQUIRE(valid_dtype(wt), "unknown dtype %d", (int)wt);
+    HD_REQUIRE(N <= (int64_t)1 << 31 && K <= (int64_t)1 << 17, "size too large");
+    HD_REQUIRE(out != nullptr, "out is NULL");
+    HD_REQUIRE(ysq != nullptr, "ysq is NULL");
+    HD_CHECK_PTR(gram, true);
+    HD_REQUIRE(gram_bytes >= (size_t)hd::output_gram_layout(K).bytes, "gram buffer too small");
+    HD_CHECK_PTR(ws, true);
+    HD_REQUIRE(ws_bytes >= hd::output_error_gram_ws(N, K), "workspace too small");
+    HD_CHECK_PTR(W, N * K > 0);
+    HD_CHECK_PTR(codes, N * K > 0);
+    if (N * K > 0 && scales == nullptr) return fail(HD_ERR_INVALID_ARG, "scales is NULL");
+    return hip_status(hd::launch_output_error_gram(fmt, B, codes, scales, W, wt, N, K, gram, ysq, nullptr, out,
+                                                   sums, ws, (hipStream_t)stream),
+                      "output_error_gram");
+}
+
 bool is_e4m3_scaled(int f) { return f == HD_INT8_E4M3 || f == HD_NVFP4 || f == HD_FP8_E4M3S || f == HD_NVINT4; }
 
 size_t quantize_blocks_tensor_scaled_workspace_size(int64_t N, int64_t K)

@@ -72,6 +72,24 @@ hipError_t launch_output_error_codes(int fmt, int B, const void *X, int64_t M, c
                                      const uint8_t *scales, int64_t N, int64_t K, const void *ref, double *out,
                                      double *sums, void *ws, hipStream_t st);
 
+// Output error through G = X^T X (outref.hip).  The gram buffer holds, at
+// these byte offsets: h (float [K]), sqrt(h) (sq), 1/sqrt(h) or 0 (r) and the
+// lower block triangle of C = G / sqrt(h h^T) with zero diagonal, off-diagonal
+// 256 x 256 blocks doubled (float16 [K][K], offset c).
+struct GramLayout {
+    int64_t h, sq, r, c, bytes;
+};
+GramLayout output_gram_layout(int64_t K);
+size_t output_gram_ws(int64_t M, int64_t K);
+// h: float [K] = hdiag(X), or NULL to compute it here.
+hipError_t launch_output_gram(const void *X, int64_t M, int64_t K, const float *h, void *gram, void *ws,
+                              hipStream_t st);
+size_t output_error_gram_ws(int64_t N, int64_t K);
+// fmt >= 0: *out = ||X (Wq - W)^T|| / sqrt(*ysq); fmt < 0: *ysq_out = ||X W^T||^2.
+hipError_t launch_output_error_gram(int fmt, int B, const uint8_t *codes, const uint8_t *scales, const void *W,
+                                    int wdt, int64_t N, int64_t K, const void *gram, const double *ysq,
+                                    double *ysq_out, double *out, double *sums, void *ws, hipStream_t st);
+
 // Y = A B^T (bf16 A [M][K], B [N][K], float32 Y [M][N]) on the MFMA product of
 // outref.hip; part: output_gemm_parts_bytes(M, N) bytes of scratch.
 int64_t output_gemm_parts_bytes(int64_t M, int64_t N);

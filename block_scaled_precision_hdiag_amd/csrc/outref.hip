@@ -36,6 +36,9 @@
 //   - when the last round of tiles would fill at most half of the CUs, those
 //     tiles run as 256 x 128 halves (a second launch), so that round takes
 //     about half a tile's time.
+#include <algorithm>
+#include <cstdlib>
+
 #include "common.hpp"
 #include "formats.hpp"
 #include "kernels.hpp"
@@ -79,7 +82,7 @@ struct GeCfg {
     static_assert(LDS <= 160 * 1024, "LDS");
 };
 
-enum { GE_STORE_Y = 0, GE_SUB_Y = 1 };
+enum { GE_STORE_Y = 0, GE_SUB_Y = 1, GE_GRAM = 2, GE_QUAD = 3 };
 
 template <bool F16>
 struct Mfma16;
@@ -127,49 +130,117 @@ __device__ __forceinline__ void ge_wait_copies(int n)
     }
 }
 
-// Tiles: the X x W product is cut into 256 x 256 tiles, numbered in a grouped
-// order (GE_GROUP_M X tiles per weight tile).  A launch covers the tile
-// numbers lin0 .. lin0 + nlin - 1: one workgroup per tile, with an XCD-aware
-// remap of the workgroup index (consecutive workgroups go to different XCDs;
-// the remap gives each XCD a contiguous run of tile numbers), or, when
-// `split` is set (half-width configuration), two workgroups per tile, each
-// taking 128 of its 256 weight rows (the last, partial round of tiles then
-// fills twice as many CUs).
-// Each workgroup computes acc = A B^T for its tile (A [M][K], B [N][K],
-// 16-bit, K % 8 == 0), then
-//   MODE GE_STORE_Y: Y[m][n] = acc, partial {0, sum acc^2};
-//   MODE GE_SUB_Y:   d = acc f_m - Y[m][n] with f_m = fscale 2^erow[m]
-//                    (f_m = 1 when erow is NULL), partial {sum d^2, 0};
-// workgroup w writes its partial to part[2 (pbase + w) .. + 1].
+// Arguments of gemm_err_kernel.  acc = A B^T over the K range of a work item,
+// for 16-bit A [M][K] and B [N][K] (row pitch K, K % 8 == 0).
+struct GeArgs {
+    const uint16_t *A, *B;
+    int64_t M, N, K;
+    int mt, nt;        // 256-row tiles of A and of B
+    int lin0, nlin;    // work items of this launch: lin0 .. lin0 + nlin - 1
+    int split;         // STORE_Y / SUB_Y: two half-width workgroups per tile
+    int ch;            // QUAD: K blocks of 256 per work item
+    float *Y;          // STORE_Y (written) / SUB_Y (read): float [M][N]
+    const int *erow;   // SUB_Y (may be NULL) / QUAD: power-of-two exponent per row of A
+    double fscale;     // SUB_Y
+    const float *r;    // GRAM: 1 / sqrt(h) per row of A (A = B)
+    uint16_t *C;       // GRAM: float16 [N][N] output
+    double *part;      // per-workgroup partials, pairs of doubles (not GRAM)
+    int pbase;
+};
+
+// Work items and their epilogues, by MODE.
+//   STORE_Y, SUB_Y: the A x B product is cut into 256 x 256 tiles, numbered in
+//     a grouped order (GE_GROUP_M A tiles per B tile); one workgroup per tile,
+//     or, when `split` is set (half-width configuration), two workgroups per
+//     tile, each taking 128 of its 256 B rows (the last, partial round of
+//     tiles then fills twice as many CUs).  Epilogue:
+//       STORE_Y: Y[m][n] = acc, partial {0, sum acc^2};
+//       SUB_Y:   d = acc f_m - Y[m][n] with f_m = fscale 2^erow[m] (f_m = 1
+//                when erow is NULL), partial {sum d^2, 0}.
+//   GRAM (A = B = X^T, so acc = X^T X): the tiles (tm, tn) with tn <= tm of
+//     the lower triangle, in groups of GE_GROUP_M tile rows (column-major
+//     inside a group).  Epilogue: C[m][n] = fp16(f acc r[m] r[n]), with f = 2
+//     off the diagonal tiles, 1 on them, and C[m][m] = 0.
+//   QUAD (A = E [M][K], B = the C of GRAM, N = K): item (c, tk, ti) covers the
+//     K blocks [c ch, min(c ch + ch, tk + 1)) of 256 for A tile ti and B tile
+//     tk (ti fastest, then tk, then c).  Epilogue: partial
+//     {sum_mn acc[m][n] E[m][n] 4^erow[m], 0}: summed over all items this is
+//     E C E^T's trace with C's lower block triangle standing for both halves.
+// Consecutive workgroup indices go to different XCDs; the index is remapped
+// so that each XCD runs a contiguous run of item numbers.  Workgroup w writes
+// its partial to part[2 (pbase + w) .. + 1].
 template <bool F16, int MODE, int TK, int S, int WN, int NJ>
-__global__ __launch_bounds__(128 * WN, 1) void gemm_err_kernel(const uint16_t *__restrict__ A,
-                                                                 const uint16_t *__restrict__ Bm, int64_t M,
-                                                                 int64_t N, int64_t K, int mt, int nt, int lin0,
-                                                                 int nlin, int split, float *__restrict__ Y,
-                                                                 const int *__restrict__ erow, double fscale,
-                                                                 double *__restrict__ part, int pbase)
+__global__ __launch_bounds__(128 * WN, 1) void gemm_err_kernel(const GeArgs ga)
 {
     typedef GeCfg<TK, S, WN, NJ> C;
     typedef typename Mfma16<F16>::v V;
     extern __shared__ __attribute__((aligned(16))) uint16_t glds[];
     __shared__ double red[2][C::NW];
+    const uint16_t *__restrict__ A = ga.A;
+    const uint16_t *__restrict__ Bm = ga.B;
+    const int64_t M = ga.M, N = ga.N, K = ga.K;
 
     const int hw = blockIdx.x;
     int lin, half = 0;
-    if (split) {
-        lin = lin0 + hw / 2;
+    if (ga.split) {
+        lin = ga.lin0 + hw / 2;
         half = hw & 1;
     } else {
-        const int per = nlin / 8;
-        lin = lin0 + (hw < per * 8 ? (hw % 8) * per + hw / 8 : hw);
+        const int per = ga.nlin / 8;
+        lin = ga.lin0 + (hw < per * 8 ? (hw % 8) * per + hw / 8 : hw);
     }
-    const int group = lin / (GE_GROUP_M * nt);
-    const int first_m = group * GE_GROUP_M;
-    const int gm = min(mt - first_m, GE_GROUP_M);
-    const int within = lin % (GE_GROUP_M * nt);
-    const int tm = first_m + within % gm;
-    const int tn = within / gm;
-    const int64_t m0 = (int64_t)tm * GE_TM, n0 = (int64_t)tn * GE_TN + (int64_t)half * C::TN;
+    int64_t m0, n0, kb = 0, ke = K;
+    float fold = 1.0f;
+    if (MODE == GE_GRAM) {
+        int g0 = 0, base = 0, gm = 0;
+        for (;;) {
+            gm = min(GE_GROUP_M, ga.mt - g0);
+            const int cnt = g0 * gm + gm * (gm + 1) / 2;
+            if (lin < base + cnt) break;
+            base += cnt;
+            g0 += GE_GROUP_M;
+        }
+        int w = lin - base, tm, tn;
+        if (w < g0 * gm) {
+            tn = w / gm;
+            tm = g0 + w % gm;
+        } else {
+            w -= g0 * gm;
+            int c = 0;
+            while (w >= gm - c) {
+                w -= gm - c;
+                ++c;
+            }
+            tn = g0 + c;
+            tm = tn + w;
+        }
+        m0 = (int64_t)tm * GE_TM;
+        n0 = (int64_t)tn * GE_TN;
+        fold = tm != tn ? 2.0f : 1.0f;
+    } else if (MODE == GE_QUAD) {
+        const int p = lin / ga.mt, ti = lin % ga.mt;
+        int c = 0, base = 0;
+        for (;;) {
+            const int cnt = ga.nt - c * ga.ch;
+            if (p < base + cnt) break;
+            base += cnt;
+            ++c;
+        }
+        const int tk = c * ga.ch + (p - base);
+        m0 = (int64_t)ti * GE_TM;
+        n0 = (int64_t)tk * GE_TN;
+        kb = (int64_t)c * ga.ch * GE_TN;
+        ke = min(min((int64_t)(c + 1) * ga.ch, (int64_t)tk + 1) * GE_TN, K);
+    } else {
+        const int group = lin / (GE_GROUP_M * ga.nt);
+        const int first_m = group * GE_GROUP_M;
+        const int gm = min(ga.mt - first_m, GE_GROUP_M);
+        const int within = lin % (GE_GROUP_M * ga.nt);
+        const int tm = first_m + within % gm;
+        const int tn = within / gm;
+        m0 = (int64_t)tm * GE_TM;
+        n0 = (int64_t)tn * GE_TN + (int64_t)half * C::TN;
+    }
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int wm = wv & 1, wn = wv >> 1;
@@ -246,15 +317,15 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_err_kernel(const uint16_t *_
     // has finished reading the buffer they overwrite, the one of stage ks - 1).
     // Before the barrier each wave waits for its own copies of stage ks (the
     // copies of later stages may stay in flight) and for its LDS reads.
-    const int ksteps = (int)((K + TK - 1) / TK);
+    const int ksteps = (int)((ke - kb + TK - 1) / TK);
     constexpr int D = C::DA + C::DB;
 #pragma unroll
     for (int p = 0; p < S - 1; ++p)
-        if (p < ksteps) GE_ISSUE((int64_t)p * TK, p);
+        if (p < ksteps) GE_ISSUE(kb + (int64_t)p * TK, p);
     for (int ks = 0; ks < ksteps; ++ks) {
         ge_wait_copies(min(S - 2, ksteps - 1 - ks) * D);
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        if (ks + S - 1 < ksteps) GE_ISSUE((int64_t)(ks + S - 1) * TK, (ks + S - 1) % S);
+        if (ks + S - 1 < ksteps) GE_ISSUE(kb + (int64_t)(ks + S - 1) * TK, (ks + S - 1) % S);
         const uint16_t *base = glds + (ks % S) * C::STAGE;
         GE_FRAG(0, base, 0);
 #pragma unroll
@@ -277,11 +348,16 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_err_kernel(const uint16_t *_
     const int64_t mb0 = m0 + wm * 128 + 4 * (lane >> 5);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        // row exponents of this lane's 16 rows in tile row i (SUB with erow)
+        // row exponents (SUB_Y with erow, QUAD) or row factors r (GRAM) of
+        // this lane's 16 rows in tile row i
         int ev[16];
+        float rv[16];
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-            ev[v] = (MODE == GE_SUB_Y && erow != nullptr) ? erow[min(mb0 + i * 32 + 8 * (v >> 2) + (v & 3), M - 1)] : 0;
+        for (int v = 0; v < 16; ++v) {
+            const int64_t mc = min(mb0 + i * 32 + 8 * (v >> 2) + (v & 3), M - 1);
+            ev[v] = ((MODE == GE_SUB_Y && ga.erow != nullptr) || MODE == GE_QUAD) ? ga.erow[mc] : 0;
+            rv[v] = MODE == GE_GRAM ? ga.r[mc] * fold : 0.0f;
+        }
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             const int64_t n = nb0 + j * 32;
@@ -291,27 +367,51 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_err_kernel(const uint16_t *_
                 for (int v = 0; v < 16; ++v) {
                     const int64_t m = mb0 + i * 32 + 8 * (v >> 2) + (v & 3);
                     if (m < M && nin) {
-                        const float a = acc[i][j][v];
-                        Y[m * N + n] = a;
-                        sy = __builtin_fma((double)a, (double)a, sy);
+                        const float y = acc[i][j][v];
+                        ga.Y[m * N + n] = y;
+                        sy = __builtin_fma((double)y, (double)y, sy);
                     }
+                }
+            } else if (MODE == GE_GRAM) {
+                const float rn = nin ? ga.r[n] : 0.0f;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int64_t m = mb0 + i * 32 + 8 * (v >> 2) + (v & 3);
+                    if (m < M && nin) {
+                        const float c = m == n ? 0.0f : acc[i][j][v] * rv[v] * rn;
+                        ga.C[m * N + n] = __builtin_bit_cast(uint16_t, (_Float16)c);
+                    }
+                }
+            } else if (MODE == GE_QUAD) {
+                // E[m][n] = A[m][n] (N = K); the 16 reads are in flight together
+                const int64_t nc = min(n, N - 1);
+                _Float16 ev16[16];
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    ev16[v] = __builtin_bit_cast(_Float16, A[min(mb0 + i * 32 + 8 * (v >> 2) + (v & 3), M - 1) * K + nc]);
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int64_t m = mb0 + i * 32 + 8 * (v >> 2) + (v & 3);
+                    const double t = ldexp((double)acc[i][j][v] * (double)(float)ev16[v], 2 * ev[v]);
+                    sd = (m < M && nin) ? sd + t : sd;
                 }
             } else {
                 // the 16 reads of Y for this 32 x 32 tile are in flight together
                 const int64_t nc = min(n, N - 1);
                 float yv[16];
 #pragma unroll
-                for (int v = 0; v < 16; ++v) yv[v] = Y[min(mb0 + i * 32 + 8 * (v >> 2) + (v & 3), M - 1) * N + nc];
+                for (int v = 0; v < 16; ++v) yv[v] = ga.Y[min(mb0 + i * 32 + 8 * (v >> 2) + (v & 3), M - 1) * N + nc];
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int64_t m = mb0 + i * 32 + 8 * (v >> 2) + (v & 3);
-                    const double f = ldexp(fscale, ev[v]);
+                    const double f = ldexp(ga.fscale, ev[v]);
                     const double d = (double)acc[i][j][v] * f - (double)yv[v];
                     sd = (m < M && nin) ? __builtin_fma(d, d, sd) : sd;
                 }
             }
         }
     }
+    if (MODE == GE_GRAM) return;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
         sd += __shfl_xor(sd, o, 64);
@@ -329,8 +429,8 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_err_kernel(const uint16_t *_
             a += red[0][w];
             b += red[1][w];
         }
-        part[2 * (int64_t)(pbase + hw)] = a;
-        part[2 * (int64_t)(pbase + hw) + 1] = b;
+        ga.part[2 * (int64_t)(ga.pbase + hw)] = a;
+        ga.part[2 * (int64_t)(ga.pbase + hw) + 1] = b;
     }
 }
 
@@ -501,40 +601,67 @@ static int device_cus()
 // the last round would fill at most half of the CUs, its tiles run as
 // 256 x 128 halves instead (the round then takes half a tile's time).
 // Returns the number of workgroup partials written.
+template <bool F16, int MODE, int NJ>
+static hipError_t ge_launch(const GeArgs &ga, int64_t grid, hipStream_t st)
+{
+    typedef GeCfg<HD_GE_TK, HD_GE_STAGES, HD_GE_WN, NJ> C;
+    if (grid <= 0) return hipSuccess;
+    const hipError_t e = hipFuncSetAttribute((const void *)gemm_err_kernel<F16, MODE, HD_GE_TK, HD_GE_STAGES, HD_GE_WN, NJ>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS);
+    if (e != hipSuccess) return e;
+    gemm_err_kernel<F16, MODE, HD_GE_TK, HD_GE_STAGES, HD_GE_WN, NJ><<<(unsigned)grid, C::THREADS, C::LDS, st>>>(ga);
+    return hipGetLastError();
+}
+
+static GeArgs ge_args(const uint16_t *A, const uint16_t *Bm, int64_t M, int64_t N, int64_t K)
+{
+    GeArgs ga = {};
+    ga.A = A;
+    ga.B = Bm;
+    ga.M = M;
+    ga.N = N;
+    ga.K = K;
+    ga.mt = (int)((M + GE_TM - 1) / GE_TM);
+    ga.nt = (int)((N + GE_TN - 1) / GE_TN);
+    ga.fscale = 1.0;
+    return ga;
+}
+
 template <bool F16, int MODE>
 static hipError_t launch_gemm_err(const uint16_t *A, const uint16_t *Bm, int64_t M, int64_t N, int64_t K,
                                   float *Y, const int *erow, double fscale, double *part, int64_t *nparts,
                                   hipStream_t st)
 {
-    constexpr int TK = HD_GE_TK, S = HD_GE_STAGES, WN = HD_GE_WN, NJF = 8 / WN, NJH = 4 / WN;
-    typedef GeCfg<TK, S, WN, NJF> CF;
-    typedef GeCfg<TK, S, WN, NJH> CH;
-    static_assert(CF::TN == GE_TN && 2 * CH::TN == GE_TN, "tile widths");
-    const int mt = (int)((M + GE_TM - 1) / GE_TM), nt = (int)((N + GE_TN - 1) / GE_TN);
-    const int64_t T = (int64_t)mt * nt;
+    constexpr int WN = HD_GE_WN, NJF = 8 / WN, NJH = 4 / WN;
+    static_assert(GeCfg<HD_GE_TK, HD_GE_STAGES, WN, NJF>::TN == GE_TN &&
+                      2 * GeCfg<HD_GE_TK, HD_GE_STAGES, WN, NJH>::TN == GE_TN,
+                  "tile widths");
+    GeArgs ga = ge_args(A, Bm, M, N, K);
+    ga.Y = Y;
+    ga.erow = erow;
+    ga.fscale = fscale;
+    ga.part = part;
+    const int64_t T = (int64_t)ga.mt * ga.nt;
     *nparts = 0;
     if (T == 0) return hipSuccess;
     const int cus = device_cus();
     const int64_t rem = T % cus;
     const bool split = rem > 0 && 2 * rem <= cus;
     const int64_t nfull = split ? T - rem : T;
-    hipError_t e;
-    if (nfull > 0) {
-        e = hipFuncSetAttribute((const void *)gemm_err_kernel<F16, MODE, TK, S, WN, NJF>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)CF::LDS);
-        if (e != hipSuccess) return e;
-        gemm_err_kernel<F16, MODE, TK, S, WN, NJF><<<(unsigned)nfull, CF::THREADS, CF::LDS, st>>>(
-            A, Bm, M, N, K, mt, nt, 0, (int)nfull, 0, Y, erow, fscale, part, 0);
-    }
+    ga.lin0 = 0;
+    ga.nlin = (int)nfull;
+    hipError_t e = ge_launch<F16, MODE, NJF>(ga, nfull, st);
+    if (e != hipSuccess) return e;
     if (split) {
-        e = hipFuncSetAttribute((const void *)gemm_err_kernel<F16, MODE, TK, S, WN, NJH>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)CH::LDS);
+        ga.lin0 = (int)nfull;
+        ga.nlin = (int)rem;
+        ga.split = 1;
+        ga.pbase = (int)nfull;
+        e = ge_launch<F16, MODE, NJH>(ga, 2 * rem, st);
         if (e != hipSuccess) return e;
-        gemm_err_kernel<F16, MODE, TK, S, WN, NJH><<<(unsigned)(2 * rem), CH::THREADS, CH::LDS, st>>>(
-            A, Bm, M, N, K, mt, nt, (int)nfull, (int)rem, 1, Y, erow, fscale, part, (int)nfull);
     }
     *nparts = nfull + (split ? 2 * rem : 0);
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 // Y = A B^T in float32 for 16-bit bf16 operands A [M][K], B [N][K] (K % 8 == 0),
@@ -609,6 +736,376 @@ hipError_t launch_output_error_codes(int fmt, int B, const void *X, int64_t M, c
         e = launch_gemm_err<false, GE_SUB_Y>((const uint16_t *)X, opnd, M, N, K, Y, nullptr, 1.0, part, &np, st);
     if (e != hipSuccess) return e;
     outref_final<<<1, 256, 0, st>>>(part, np, ysq, nullptr, out, sums);
+    return hipGetLastError();
+}
+
+// ===================================================== output error by Gram ==
+// ||X D^T||_F^2 = sum_n d_n^T G d_n with G = X^T X (D = Wq - W, or W itself
+// for ||X W^T||^2): once G is known, each quantisation costs an N x K x K
+// product instead of an M x N x K one (M = rows of X), and G's symmetry halves
+// that.  With h = diag(G) and the scaled rows e_n = d_n sqrt(h):
+//   d^T G d = sum_j d_j^2 h_j + e^T C e,   C = G / sqrt(h h^T) off the diagonal,
+// where |C_jk| <= 1 (Cauchy-Schwarz).  The diagonal sum is taken exactly (in
+// float64 from the float32 d and h); only the off-diagonal part goes through
+// the float16 MFMA product, with C in float16 and e in float16 under one
+// power-of-two scale per row.
+//
+// output_gram():   h (hdiag), sqrt(h), 1/sqrt(h) (0 for h = 0); X^T in the
+//                  workspace; C's lower block triangle (256 x 256 blocks,
+//                  diagonal blocks whole) from one bf16 MFMA product over the
+//                  tiles tn <= tm, off-diagonal blocks stored as 2 C so that
+//                  the lower triangle stands for both halves;
+// output_error_gram(): e and the diagonal sums per row (one workgroup per
+//                  row), then E C over each item's K range with the epilogue
+//                  sum of acc * e, then a fixed-order final sum.
+
+// Xt[k][m] = X[m][k] for m < M, 0 for M <= m < M8 (16-bit values; K % 8 == 0,
+// M8 % 8 == 0).  64 x 64 tiles through LDS with 16-byte global loads and
+// stores on both sides.
+__global__ __launch_bounds__(256) void xt_transpose_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t K,
+                                                           int64_t M8, uint16_t *__restrict__ Xt)
+{
+    __shared__ uint16_t t[64][66];
+    const int64_t m0 = (int64_t)blockIdx.y * 64, k0 = (int64_t)blockIdx.x * 64;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int c = tid + 256 * q, r = c >> 3, kc = (c & 7) * 8;
+        const int64_t m = m0 + r, k = k0 + kc;
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (m < M && k < K) v = *reinterpret_cast<const uint4 *>(X + m * K + k);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            t[r][kc + 2 * j] = (uint16_t)(w[j] & 0xFFFFu);
+            t[r][kc + 2 * j + 1] = (uint16_t)(w[j] >> 16);
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int c = tid + 256 * q, kr = c >> 3, mc = (c & 7) * 8;
+        const int64_t k = k0 + kr, m = m0 + mc;
+        if (k < K && m < M8) {
+            uint32_t o[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) o[j] = (uint32_t)t[mc + 2 * j][kr] | ((uint32_t)t[mc + 2 * j + 1][kr] << 16);
+            *reinterpret_cast<uint4 *>(Xt + k * M8 + m) = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+    }
+}
+
+// h (copied unless it already is the buffer's), sqrt(h) and 1/sqrt(h) (0 for h = 0).
+__global__ __launch_bounds__(256) void gram_prep_kernel(const float *__restrict__ hin, int64_t K, float *__restrict__ h,
+                                                        float *__restrict__ sq, float *__restrict__ r)
+{
+    const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (k >= K) return;
+    const float v = hin[k];
+    if (hin != h) h[k] = v;
+    const float q = sqrtf(v);
+    sq[k] = q;
+    r[k] = v > 0.0f ? 1.0f / q : 0.0f;
+}
+
+__global__ __launch_bounds__(256) void gram_zero_kernel(uint16_t *__restrict__ p, int64_t n)
+{
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0;
+}
+
+// d = Wq - W for the 8 weights k .. k + 7 of row n (REF: d = W), with Wq the
+// float32 value dequantize() gives (fl32(s val(q)); invalid codes give 0).
+template <int EK, int SK, typename WT, bool REF>
+__device__ __forceinline__ void gram_diff(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales,
+                                          int B, const WT *__restrict__ W, int64_t n, int64_t K, int64_t k,
+                                          float d[8])
+{
+    const int64_t e0 = n * K + k;
+    float w[8];
+    if (sizeof(WT) == 2) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(W + e0);
+        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            w[2 * j] = bf16_to_f32(u[j] & 0xFFFFu);
+            w[2 * j + 1] = bf16_to_f32(u[j] >> 16);
+        }
+    } else {
+        const float4 a = *reinterpret_cast<const float4 *>(W + e0);
+        const float4 b = *reinterpret_cast<const float4 *>(W + e0 + 4);
+        w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+        w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+    }
+    if (REF) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) d[j] = w[j];
+        return;
+    }
+    const int64_t bi = e0 / B;
+    const int sc = scale_bytes(SK) == 2 ? (int)reinterpret_cast<const uint16_t *>(scales)[bi] : (int)scales[bi];
+    const float s = scale_code_valid(SK, sc) ? scale_value(SK, sc) : 0.0f;
+    uint32_t c[8];
+    if (elem_4bit(EK)) {
+        const uint32_t v = *reinterpret_cast<const uint32_t *>(codes + e0 / 2);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) c[j] = (v >> (4 * j)) & 15u;
+    } else {
+        const uint2 v = *reinterpret_cast<const uint2 *>(codes + e0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            c[j] = (v.x >> (8 * j)) & 255u;
+            c[4 + j] = (v.y >> (8 * j)) & 255u;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        float q;
+        if (EK == ELEM_INT8) {
+            const int i = (int)(int8_t)(uint8_t)c[j];
+            q = i == -128 ? 0.0f : s * (float)i;
+        } else if (EK == ELEM_INT4) {
+            const int i = (int)((c[j] ^ 8u) & 15u) - 8;
+            q = i == -8 ? 0.0f : s * (float)i;
+        } else {
+            bool neg, ok = true;
+            uint32_t idx;
+            if (EK == ELEM_E2M1) {
+                neg = (c[j] & 8u) != 0;
+                idx = c[j] & 7u;
+            } else {
+                neg = (c[j] & 0x80u) != 0;
+                idx = c[j] & 0x7Fu;
+                ok = idx != 0x7Fu;
+            }
+            const float mag = ok ? s * elem_value<EK>(idx) : 0.0f;
+            q = neg ? -mag : mag;
+        }
+        d[j] = q - w[j];
+    }
+}
+
+// One workgroup per row n: e = d sqrt(h) as float16 under the row exponent
+// erow[n] (largest |e| scaled into [2^14, 2^15); 0 for a zero row), and
+// dsum[n] = sum_j d_j^2 h_j in float64.
+template <int EK, int SK, typename WT, bool REF>
+__global__ __launch_bounds__(256) void gram_operand_kernel(const uint8_t *__restrict__ codes,
+                                                           const uint8_t *__restrict__ scales, int B,
+                                                           const WT *__restrict__ W, int64_t K,
+                                                           const float *__restrict__ sq, const float *__restrict__ h,
+                                                           uint16_t *__restrict__ E, int *__restrict__ erow,
+                                                           double *__restrict__ dsum)
+{
+    __shared__ double sh[4];
+    __shared__ int shm[4];
+    const int64_t n = blockIdx.x;
+    const int64_t nch = K / 8;
+    int mx = 0;  // largest |e| as float bits (monotone for non-negative floats)
+    double ds = 0.0;
+    for (int64_t c = threadIdx.x; c < nch; c += 256) {
+        float d[8];
+        gram_diff<EK, SK, WT, REF>(codes, scales, B, W, n, K, c * 8, d);
+        const float4 q0 = *reinterpret_cast<const float4 *>(sq + c * 8);
+        const float4 q1 = *reinterpret_cast<const float4 *>(sq + c * 8 + 4);
+        const float4 h0 = *reinterpret_cast<const float4 *>(h + c * 8);
+        const float4 h1 = *reinterpret_cast<const float4 *>(h + c * 8 + 4);
+        const float qv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+        const float hv[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            mx = max(mx, __builtin_bit_cast(int, fabsf(d[j] * qv[j])));
+            ds = __builtin_fma((double)d[j] * (double)d[j], (double)hv[j], ds);
+        }
+    }
+    mx = wave_max_int(mx);
+    if ((threadIdx.x & 63) == 0) shm[threadIdx.x >> 6] = mx;
+    ds = block_sum_256(ds, sh);  // synchronises, so shm is complete
+    mx = max(max(shm[0], shm[1]), max(shm[2], shm[3]));
+    int ex = 0;
+    if (mx != 0) {
+        int f;
+        frexpf(__builtin_bit_cast(float, mx), &f);  // max = g 2^f, g in [0.5, 1)
+        ex = f - 1 - 14;
+    }
+    if (threadIdx.x == 0) {
+        erow[n] = ex;
+        dsum[n] = ds;
+    }
+    uint16_t *orow = E + n * K;
+    for (int64_t c = threadIdx.x; c < nch; c += 256) {
+        float d[8];
+        gram_diff<EK, SK, WT, REF>(codes, scales, B, W, n, K, c * 8, d);
+        uint32_t o[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const _Float16 lo = (_Float16)ldexpf(d[2 * j] * sq[c * 8 + 2 * j], -ex);
+            const _Float16 hi = (_Float16)ldexpf(d[2 * j + 1] * sq[c * 8 + 2 * j + 1], -ex);
+            o[j] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+        }
+        *reinterpret_cast<uint4 *>(orow + c * 8) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+}
+
+// total = sum part[2 i] + sum dsum[n] in a fixed order; ysq == NULL: *ysq_out
+// = total.  Otherwise *out = sqrt(total) / sqrt(*ysq), sums = {total, *ysq}.
+__global__ __launch_bounds__(256) void gram_final(const double *__restrict__ part, int64_t np,
+                                                  const double *__restrict__ dsum, int64_t nr,
+                                                  const double *__restrict__ ysq, double *__restrict__ ysq_out,
+                                                  double *__restrict__ out, double *__restrict__ sums)
+{
+    __shared__ double sh[4];
+    double a = 0.0, b = 0.0;
+    for (int64_t i = threadIdx.x; i < np; i += 256) a += part[2 * i];
+    for (int64_t i = threadIdx.x; i < nr; i += 256) b += dsum[i];
+    a = block_sum_256(a, sh);
+    b = block_sum_256(b, sh);
+    if (threadIdx.x == 0) {
+        const double t = a + b;
+        if (ysq == nullptr) {
+            *ysq_out = t;
+        } else {
+            const double y = *ysq;
+            *out = sqrt(t) / sqrt(y);
+            if (sums) {
+                sums[0] = t;
+                sums[1] = y;
+            }
+        }
+    }
+}
+
+GramLayout output_gram_layout(int64_t K)
+{
+    GramLayout L;
+    L.h = 0;
+    L.sq = al256(K * 4);
+    L.r = L.sq + al256(K * 4);
+    L.c = L.r + al256(K * 4);
+    L.bytes = L.c + al256(K * K * 2);
+    return L;
+}
+
+size_t output_gram_ws(int64_t M, int64_t K)
+{
+    const int64_t M8 = (M + 7) / 8 * 8;
+    return (size_t)std::max(al256(K * M8 * 2), (int64_t)hdiag_ws(M, K));
+}
+
+// K blocks of 256 per work item of the E C product (HD_GRAM_CHUNK overrides).
+static int gram_chunk()
+{
+    const char *e = getenv("HD_GRAM_CHUNK");
+    const int v = e ? atoi(e) : 0;
+    return v >= 1 && v <= 1024 ? v : 4;
+}
+
+static int64_t gram_items(int64_t N, int64_t K, int ch)
+{
+    const int64_t mt = (N + GE_TM - 1) / GE_TM, nt = (K + GE_TN - 1) / GE_TN;
+    int64_t pairs = 0;
+    for (int64_t c = 0; c * ch < nt; ++c) pairs += nt - c * ch;
+    return mt * pairs;
+}
+
+size_t output_error_gram_ws(int64_t N, int64_t K)
+{
+    return (size_t)(al256(N * K * 2) + al256(N * 4) + al256(N * 8) + al256(gram_items(N, K, 1) * 16));
+}
+
+hipError_t launch_output_gram(const void *X, int64_t M, int64_t K, const float *h, void *gram, void *ws,
+                              hipStream_t st)
+{
+    const GramLayout L = output_gram_layout(K);
+    char *g = static_cast<char *>(gram);
+    float *gh = reinterpret_cast<float *>(g + L.h);
+    float *sq = reinterpret_cast<float *>(g + L.sq);
+    float *r = reinterpret_cast<float *>(g + L.r);
+    uint16_t *C = reinterpret_cast<uint16_t *>(g + L.c);
+    if (K == 0) return hipSuccess;
+    hipError_t e;
+    if (h == nullptr) {
+        e = launch_hdiag(X, HD_BF16, M, K, gh, ws, st);
+        if (e != hipSuccess) return e;
+        h = gh;
+    }
+    gram_prep_kernel<<<(unsigned)((K + 255) / 256), 256, 0, st>>>(h, K, gh, sq, r);
+    const int64_t M8 = (M + 7) / 8 * 8;
+    if (M8 == 0) {
+        gram_zero_kernel<<<1024, 256, 0, st>>>(C, K * K);
+        return hipGetLastError();
+    }
+    uint16_t *Xt = static_cast<uint16_t *>(ws);
+    const dim3 tg((unsigned)((K + 63) / 64), (unsigned)((M8 + 63) / 64));
+    xt_transpose_kernel<<<tg, 256, 0, st>>>(static_cast<const uint16_t *>(X), M, K, M8, Xt);
+    GeArgs ga = ge_args(Xt, Xt, K, K, M8);
+    const int64_t items = (int64_t)ga.mt * (ga.mt + 1) / 2;
+    ga.nlin = (int)items;
+    ga.r = r;
+    ga.C = C;
+    return ge_launch<false, GE_GRAM, 8 / HD_GE_WN>(ga, items, st);
+}
+
+template <int EK, int SK, bool REF>
+static void launch_gram_operand(const uint8_t *codes, const uint8_t *scales, int B, const void *W, int wdt, int64_t N,
+                                int64_t K, const float *sq, const float *h, uint16_t *E, int *erow, double *dsum,
+                                hipStream_t st)
+{
+    if (wdt == HD_BF16)
+        gram_operand_kernel<EK, SK, uint16_t, REF><<<(unsigned)N, 256, 0, st>>>(
+            codes, scales, B, static_cast<const uint16_t *>(W), K, sq, h, E, erow, dsum);
+    else
+        gram_operand_kernel<EK, SK, float, REF><<<(unsigned)N, 256, 0, st>>>(
+            codes, scales, B, static_cast<const float *>(W), K, sq, h, E, erow, dsum);
+}
+
+template <int F>
+static void gram_operand_fmt(const uint8_t *codes, const uint8_t *scales, int B, const void *W, int wdt, int64_t N,
+                             int64_t K, const float *sq, const float *h, uint16_t *E, int *erow, double *dsum,
+                             hipStream_t st)
+{
+    launch_gram_operand<elem_kind(F), scale_kind(F), false>(codes, scales, B, W, wdt, N, K, sq, h, E, erow, dsum, st);
+}
+
+// fmt < 0: the reference ||X W^T||^2 into *ysq_out.
+hipError_t launch_output_error_gram(int fmt, int B, const uint8_t *codes, const uint8_t *scales, const void *W,
+                                    int wdt, int64_t N, int64_t K, const void *gram, const double *ysq,
+                                    double *ysq_out, double *out, double *sums, void *ws, hipStream_t st)
+{
+    const GramLayout L = output_gram_layout(K);
+    const char *g = static_cast<const char *>(gram);
+    const float *gh = reinterpret_cast<const float *>(g + L.h);
+    const float *sq = reinterpret_cast<const float *>(g + L.sq);
+    const uint16_t *C = reinterpret_cast<const uint16_t *>(g + L.c);
+    char *w = static_cast<char *>(ws);
+    uint16_t *E = reinterpret_cast<uint16_t *>(w);
+    int *erow = reinterpret_cast<int *>(w + al256(N * K * 2));
+    double *dsum = reinterpret_cast<double *>(w + al256(N * K * 2) + al256(N * 4));
+    double *part = reinterpret_cast<double *>(w + al256(N * K * 2) + al256(N * 4) + al256(N * 8));
+    const int ch = gram_chunk();
+    const int64_t items = N > 0 && K > 0 ? gram_items(N, K, ch) : 0;
+    if (items > 0) {
+        switch (fmt) {
+        case -1: launch_gram_operand<ELEM_INT8, SCALE_INT8, true>(codes, scales, B, W, wdt, N, K, sq, gh, E, erow, dsum, st); break;
+        case HD_INT8_E4M3: gram_operand_fmt<HD_INT8_E4M3>(codes, scales, B, W, wdt, N, K, sq, gh, E, erow, dsum, st); break;
+        case HD_NVFP4: gram_operand_fmt<HD_NVFP4>(codes, scales, B, W, wdt, N, K, sq, gh, E, erow, dsum, st); break;
+        case HD_MXFP4: gram_operand_fmt<HD_MXFP4>(codes, scales, B, W, wdt, N, K, sq, gh, E, erow, dsum, st); break;
+        case HD_MXFP8: gram_operand_fmt<HD_MXFP8>(codes, scales, B, W, wdt, N, K, sq, gh, E, erow, dsum, st); break;
+        case HD_FP8_E4M3S: gram_operand_fmt<HD_FP8_E4M3S>(codes, scales, B, W, wdt, N, K, sq, gh, E, erow, dsum, st); break;
+        case HD_NVFP4_UE4M4: gram_operand_fmt<HD_NVFP4_UE4M4>(codes, scales, B, W, wdt, N, K, sq, gh, E, erow, dsum, st); break;
+        case HD_NVFP4_UE5M3: gram_operand_fmt<HD_NVFP4_UE5M3>(codes, scales, B, W, wdt, N, K, sq, gh, E, erow, dsum, st); break;
+        case HD_NVINT4: gram_operand_fmt<HD_NVINT4>(codes, scales, B, W, wdt, N, K, sq, gh, E, erow, dsum, st); break;
+        case HD_FP4_F16: gram_operand_fmt<HD_FP4_F16>(codes, scales, B, W, wdt, N, K, sq, gh, E, erow, dsum, st); break;
+        case HD_INT4_F16: gram_operand_fmt<HD_INT4_F16>(codes, scales, B, W, wdt, N, K, sq, gh, E, erow, dsum, st); break;
+        default: return hipErrorInvalidValue;
+        }
+        GeArgs ga = ge_args(E, C, N, K, K);
+        ga.ch = ch;
+        ga.nlin = (int)items;
+        ga.erow = erow;
+        ga.part = part;
+        const hipError_t e = ge_launch<true, GE_QUAD, 8 / HD_GE_WN>(ga, items, st);
+        if (e != hipSuccess) return e;
+    }
+    gram_final<<<1, 256, 0, st>>>(part, items, dsum, items > 0 ? N : 0, fmt < 0 ? nullptr : ysq, ysq_out, out, sums);
     return hipGetLastError();
 }
 

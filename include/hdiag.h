@@ -264,6 +264,59 @@ hd_status output_error_codes(hd_format fmt, int32_t B, const void *X, hd_dtype x
                              const void *ref, size_t ref_bytes, double *out, double *sums, void *ws,
                              size_t ws_bytes, void *stream);
 
+/* ----------------------------------------- output error through X^T X --- */
+
+/* The output error of qwantize "Results" (metric definitions), computed from
+ * the Gram matrix G = X^T X: ||X D^T||_F^2 = sum_n d_n^T G d_n for the rows
+ * d_n of D = Wq - W (and of W itself for ||X W^T||_F^2), an identity of the
+ * definition.  G depends on X alone, so once it is formed each quantisation
+ * costs about N K^2 multiply-adds (the symmetry of G halves N K K) instead of
+ * the 2 M N K of two products with X: the cheaper order whenever several
+ * quantisations of weights of width K are scored against more than about K/2
+ * rows of X.
+ *
+ * output_gram() fills a caller-allocated device buffer `gram` of at least
+ * output_gram_size(K) bytes (16-byte aligned) with data private to the
+ * library: h = diag(G), and C = G / sqrt(h_j h_k) off the diagonal (0 where h
+ * is 0), as float16, lower triangle only.  X: bfloat16 [M, K], K % 8 == 0;
+ * the products run on the bf16 MFMA units with float32 accumulation.
+ * h (optional, device, float [K]): hdiag(X) already computed on the same X;
+ * NULL computes it here.  The buffer stays valid as long as X is unchanged.
+ * workspace: ws_bytes >= output_gram_workspace_size(M, K) (X^T is staged
+ * there).
+ *
+ * output_reference_gram() writes ||X W^T||_F^2 (double) to the device scalar
+ * *ysq; output_error_gram() writes ||X Wq^T - X W^T||_F / sqrt(*ysq) to *out,
+ * for Wq = dequantize(fmt, B, codes, scales) (every format, FP16 scales
+ * included) without forming Wq, and sums (optional, device, 2 doubles) gets
+ * {||X (Wq - W)^T||_F^2, *ysq}.  W: bfloat16 or float32 [N, K], the weights
+ * the codes quantise.
+ * Accuracy: with e_n = d_n sqrt(h), d^T G d = sum_j d_j^2 h_j + e^T C e; the
+ * diagonal sum is taken in float64 from float32 d and h, the off-diagonal part
+ * is the float16 MFMA product of e (one power-of-two scale per row, rounded
+ * to 11 significant bits) with the float16 C, in float32 accumulation.  Both
+ * roundings are relative to 2^-11 per term and unbiased, so their effect on
+ * the sum is far smaller than 2^-11 unless the off-diagonal part dominates and
+ * is dominated by a few terms; on Gaussian X with outlier channels it is
+ * about 1e-6 relative.  output_error_codes() / output_error() form X Wq^T
+ * itself.
+ * workspace: ws_bytes >= output_error_gram_workspace_size(N, K); each call
+ * needs its own.  Calls that share `gram` may run concurrently (it is only
+ * read).
+ * Errors: HD_ERR_INVALID_ARG as quantize_blocks for fmt / B / N / K, NULL or
+ * misaligned pointers, a short buffer or workspace, K % 8 != 0 for
+ * output_gram; HD_ERR_UNSUPPORTED for a float32 X. */
+size_t output_gram_size(int64_t K);
+size_t output_gram_workspace_size(int64_t M, int64_t K);
+hd_status output_gram(const void *X, hd_dtype xt, int64_t M, int64_t K, const float *h, void *gram,
+                      size_t gram_bytes, void *ws, size_t ws_bytes, void *stream);
+size_t output_error_gram_workspace_size(int64_t N, int64_t K);
+hd_status output_reference_gram(const void *W, hd_dtype wt, int64_t N, int64_t K, const void *gram,
+                                size_t gram_bytes, double *ysq, void *ws, size_t ws_bytes, void *stream);
+hd_status output_error_gram(hd_format fmt, int32_t B, const uint8_t *codes, const uint8_t *scales, const void *W,
+                            hd_dtype wt, int64_t N, int64_t K, const void *gram, size_t gram_bytes,
+                            const double *ysq, double *out, double *sums, void *ws, size_t ws_bytes, void *stream);
+
 /* ------------------------------------------------ per-tensor scaling --- */
 
 /* Two-level scales for the E4M3 block-scale formats (HD_INT8_E4M3, HD_NVFP4,

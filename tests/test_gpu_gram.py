@@ -1,0 +1,219 @@
+"""GPU parity of the output error through G = X^T X (output_gram,
+output_reference_gram, output_error_gram) against the oracle.
+
+The output error of every format's codes is compared with the oracle's output
+error of the dequantised weights (the definition, ||X Wq^T - X W^T||_F /
+||X W^T||_F in float64), within 1e-4 relative; ||X W^T||^2 likewise.  The
+library's Gram buffer is also checked entry by entry: h bit for bit against
+hdiag(), and the stored correlations C = G / sqrt(h_j h_k) (lower block
+triangle, off-diagonal 256 x 256 blocks doubled, zero diagonal) against the
+oracle's float64 X^T X within the float16 rounding plus the float32
+accumulation bound.  Shapes span several 256 x 256 tiles with ragged edges and
+K tails that are not multiples of 256.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import block_scaled_precision_hdiag_amd as hd
+
+pytestmark = pytest.mark.gpu
+
+FMTS = [hd.INT8_E4M3, hd.NVFP4, hd.MXFP4, hd.MXFP8, hd.FP8_E4M3S, hd.NVFP4_UE4M4, hd.NVFP4_UE5M3, hd.NVINT4,
+        hd.FP4_F16, hd.INT4_F16]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    hd.lib()
+
+
+def dev(t):
+    return t.contiguous().cuda()
+
+
+def npy(t):
+    return t.detach().cpu().numpy()
+
+
+def weights_for(fmt, N, K, seed, dtype=torch.bfloat16):
+    std = {hd.FP8_E4M3S: 4.0, hd.MXFP8: 0.05}.get(fmt, 0.02)
+    return synth.weights("t4", N, K, std=std, seed=seed, gain_seed=seed + 1, dtype=dtype)
+
+
+def acts(M, K, seed):
+    return synth.activations(M, K, seed, n_out=3, out_gain=50.0, idx_seed=seed + 1, dtype=torch.bfloat16)
+
+
+def method_for(fmt):
+    return hd.SSE_OPT
+
+
+def sc_np(s):
+    """Scales for the oracle: uint8 codes, or the binary16 bits of float16 scales."""
+    if s.dtype == torch.float16:
+        return npy(s.view(torch.int16)).view(np.uint16)
+    return npy(s)
+
+
+def al256(x):
+    return (x + 255) // 256 * 256
+
+
+def gram_parts(gram, K):
+    """h, C (float16 [K, K]) of a Gram buffer, at the library's offsets."""
+    g = gram.cpu()
+    h = g[:4 * K].view(torch.float32).numpy()
+    c0 = 3 * al256(4 * K)
+    C = g[c0:c0 + 2 * K * K].view(torch.float16).float().numpy().reshape(K, K)
+    return h, C
+
+
+@pytest.mark.parametrize("M,K", [(700, 600), (300, 512), (1, 8), (513, 1032)])
+def test_gram_buffer(M, K):
+    X = acts(M, K, 60 + K)
+    Xf = X.float()
+    Xf[:, 3] = 0.0  # a zero column: its h is 0 and its row and column of C are 0
+    X = Xf.to(torch.bfloat16)
+    Xd = dev(X)
+    gram = hd.output_gram(Xd)
+    h_dev = hd.hdiag(Xd)
+    gram2 = hd.output_gram(Xd, h=h_dev)
+    torch.cuda.synchronize()
+    h, C = gram_parts(gram, K)
+    h2, C2 = gram_parts(gram2, K)
+    blk = np.arange(K) // 256
+    lower = blk[:, None] >= blk[None, :]  # the part of C the library writes and reads
+    np.testing.assert_array_equal(h, h2)
+    np.testing.assert_array_equal(C[lower], C2[lower])
+    np.testing.assert_array_equal(h, oracle.hdiag(synth.bits(X)))
+    Xt = np.ascontiguousarray(synth.bits(X).T)
+    G = oracle.matmul_nt(Xt, Xt)
+    hg = np.diag(G).copy()
+    r = np.where(hg > 0, 1.0 / np.sqrt(np.where(hg > 0, hg, 1.0)), 0.0)
+    Ct = G * r[:, None] * r[None, :]
+    fold = np.where(blk[:, None] > blk[None, :], 2.0, 1.0)
+    np.fill_diagonal(Ct, 0.0)
+    exp = (fold * Ct)[lower]
+    got = C[lower].astype(np.float64)
+    tol = fold[lower] * (2.0 ** -11 * np.abs(Ct[lower]) + 1e-4) + 2.0 ** -24
+    assert np.all(np.abs(got - exp) <= tol), float(np.max(np.abs(got - exp) - tol))
+    assert np.all(np.diag(C) == 0.0)
+    assert np.all(C[3, :3] == 0.0) and np.all(C[4:, 3][blk[4:] >= blk[3]] == 0.0)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("B,M,N,K", [(16, 300, 200, 512), (256, 257, 300, 1024), (8, 700, 40, 520)])
+def test_output_error_gram_parity(fmt, B, M, N, K):
+    X, W = acts(M, K, 40 + B), weights_for(fmt, N, K, 950 + B)
+    Xd, Wd = dev(X), dev(W)
+    c, s, _ = hd.quantize_blocks(method_for(fmt), fmt, B, Wd)
+    gram = hd.output_gram(Xd)
+    ysq = hd.output_reference_gram(Wd, gram)
+    out, sums = hd.output_error_gram(fmt, B, c, s, Wd, gram, ysq, sums=True)
+    torch.cuda.synchronize()
+    oe_o, d_o, y_o = oracle.output_error(synth.bits(X), synth.bits(W), oracle.dequantize(fmt, B, npy(c), sc_np(s), N, K),
+                                         sums=True)
+    assert out.item() == pytest.approx(oe_o, rel=1e-4)
+    np.testing.assert_allclose(npy(sums), [d_o, y_o], rtol=1e-4)
+    assert ysq.item() == pytest.approx(y_o, rel=1e-4)
+
+
+@pytest.mark.parametrize("fmt,B", [(hd.INT8_E4M3, 32), (hd.NVFP4, 16)])
+def test_output_error_gram_float32_weights(fmt, B):
+    M, N, K = 400, 260, 768
+    X, W = acts(M, K, 3), weights_for(fmt, N, K, 4, dtype=torch.float32)
+    Xd, Wd = dev(X), dev(W)
+    c, s, _ = hd.quantize_blocks(hd.H_OPT, fmt, B, Wd, h=hd.hdiag(Xd))
+    gram = hd.output_gram(Xd)
+    ysq = hd.output_reference_gram(Wd, gram)
+    out = hd.output_error_gram(fmt, B, c, s, Wd, gram, ysq).item()
+    Wq = oracle.dequantize(fmt, B, npy(c), sc_np(s), N, K)
+    assert out == pytest.approx(oracle.output_error(synth.bits(X), synth.bits(W), Wq), rel=1e-4)
+
+
+def test_output_error_gram_x_dynamic_range():
+    """A 1e4 outlier channel, a zero channel and rows over 2^-30 .. 2^30: the
+    diagonal term is exact and C is scale-free."""
+    M, N, K = 384, 80, 512
+    X = acts(M, K, 5).float()
+    X *= torch.from_numpy(np.exp2(np.linspace(-30, 30, M)).astype(np.float32))[:, None]
+    X[:, 11] *= 1e4
+    X[:, 12] = 0.0
+    X = X.to(torch.bfloat16)
+    for fmt, B in ((hd.INT8_E4M3, 32), (hd.NVFP4, 16), (hd.MXFP8, 32)):
+        W = weights_for(fmt, N, K, 77)
+        Xd, Wd = dev(X), dev(W)
+        c, s, _ = hd.quantize_blocks(hd.NAIVE, fmt, B, Wd)
+        gram = hd.output_gram(Xd)
+        ysq = hd.output_reference_gram(Wd, gram)
+        out = hd.output_error_gram(fmt, B, c, s, Wd, gram, ysq).item()
+        Wq = oracle.dequantize(fmt, B, npy(c), sc_np(s), N, K)
+        assert out == pytest.approx(oracle.output_error(synth.bits(X), synth.bits(W), Wq), rel=1e-4)
+
+
+def test_output_error_gram_on_grid_is_zero():
+    """W on the NVFP4 grid: D = 0, so the error is exactly 0."""
+    M, N, K, B = 300, 260, 512, 16
+    W0 = weights_for(hd.NVFP4, N, K, 3)
+    c, s, _ = hd.quantize_blocks(hd.NAIVE, hd.NVFP4, B, dev(W0))
+    Wg = hd.dequantize(hd.NVFP4, B, c, s, N, K, dtype=torch.bfloat16)
+    X = dev(acts(M, K, 9))
+    gram = hd.output_gram(X)
+    ysq = hd.output_reference_gram(Wg, gram)
+    out, sums = hd.output_error_gram(hd.NVFP4, B, c, s, Wg, gram, ysq, sums=True)
+    torch.cuda.synchronize()
+    assert out.item() == 0.0 and sums[0].item() == 0.0 and ysq.item() > 0.0
+
+
+def test_output_error_gram_no_rows():
+    """M = 0: G = 0, so both norms are 0 and the quotient is NaN, as the
+    definition gives."""
+    N, K, B = 64, 256, 32
+    W = dev(weights_for(hd.INT8_E4M3, N, K, 1))
+    X = torch.empty((0, K), dtype=torch.bfloat16, device="cuda")
+    gram = hd.output_gram(X)
+    ysq = hd.output_reference_gram(W, gram)
+    c, s, _ = hd.quantize_blocks(hd.NAIVE, hd.INT8_E4M3, B, W)
+    out, sums = hd.output_error_gram(hd.INT8_E4M3, B, c, s, W, gram, ysq, sums=True)
+    torch.cuda.synchronize()
+    assert ysq.item() == 0.0 and sums[0].item() == 0.0 and np.isnan(out.item())
+
+
+def test_output_error_gram_chunking_and_repeat(monkeypatch):
+    """The K range of each work item (HD_GRAM_CHUNK blocks of 256) changes
+    only the summation order; repeated calls agree bit for bit."""
+    M, N, K, B = 600, 300, 1536, 32
+    X, W = dev(acts(M, K, 21)), dev(weights_for(hd.INT8_E4M3, N, K, 22))
+    c, s, _ = hd.quantize_blocks(hd.SSE_OPT, hd.INT8_E4M3, B, W)
+    gram = hd.output_gram(X)
+    ysq = hd.output_reference_gram(W, gram)
+    vals = []
+    for ch in ("1", "2", "4", "64"):
+        monkeypatch.setenv("HD_GRAM_CHUNK", ch)
+        a = hd.output_error_gram(hd.INT8_E4M3, B, c, s, W, gram, ysq).item()
+        b = hd.output_error_gram(hd.INT8_E4M3, B, c, s, W, gram, ysq).item()
+        assert a == b
+        vals.append(a)
+    assert max(vals) == pytest.approx(min(vals), rel=1e-9)
+    generic = hd.output_error(X, W, hd.dequantize(hd.INT8_E4M3, B, c, s, N, K)).item()
+    assert vals[0] == pytest.approx(generic, rel=1e-4)
+
+
+def test_output_gram_errors():
+    X = torch.randn(8, 16, device="cuda")
+    with pytest.raises(hd.HdiagError) as e:
+        hd.output_gram(X)
+    assert e.value.status == hd.HD_ERR_UNSUPPORTED
+    Xb = torch.randn(8, 12, device="cuda").bfloat16()
+    with pytest.raises(hd.HdiagError) as e:
+        hd.output_gram(Xb, gram=torch.empty(hd.output_gram_size(12), dtype=torch.uint8, device="cuda"))
+    assert e.value.status == hd.HD_ERR_INVALID_ARG
+    Xb = torch.randn(8, 16, device="cuda").bfloat16()
+    with pytest.raises(hd.HdiagError) as e:
+        hd.output_gram(Xb, gram=torch.empty(16, dtype=torch.uint8, device="cuda"))
+    assert e.value.status == hd.HD_ERR_INVALID_ARG
