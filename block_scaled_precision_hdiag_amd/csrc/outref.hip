@@ -138,7 +138,6 @@ struct GeArgs {
     int mt, nt;        // 256-row tiles of A and of B
     int lin0, nlin;    // work items of this launch: lin0 .. lin0 + nlin - 1
     int split;         // STORE_Y / SUB_Y: two half-width workgroups per tile
-    int ch;            // QUAD: K blocks of 256 per work item
     float *Y;          // STORE_Y (written) / SUB_Y (read): float [M][N]
     const int *erow;   // SUB_Y (may be NULL) / QUAD: power-of-two exponent per row of A
     double fscale;     // SUB_Y
@@ -159,13 +158,17 @@ struct GeArgs {
 //                when erow is NULL), partial {sum d^2, 0}.
 //   GRAM (A = B = X^T, so acc = X^T X): the tiles (tm, tn) with tn <= tm of
 //     the lower triangle, in groups of GE_GROUP_M tile rows (column-major
-//     inside a group).  Epilogue: C[m][n] = fp16(f acc r[m] r[n]), with f = 2
-//     off the diagonal tiles, 1 on them, and C[m][m] = 0.
-//   QUAD (A = E [M][K], B = the C of GRAM, N = K): item (c, tk, ti) covers the
-//     K blocks [c ch, min(c ch + ch, tk + 1)) of 256 for A tile ti and B tile
-//     tk (ti fastest, then tk, then c).  Epilogue: partial
-//     {sum_mn acc[m][n] E[m][n] 4^erow[m], 0}: summed over all items this is
-//     E C E^T's trace with C's lower block triangle standing for both halves.
+//     inside a group).  Epilogue: C[n][m] = fp16(f acc[m][n] r[m] r[n]) (the
+//     transposed position, so C holds the upper block triangle), f = 2 off
+//     the diagonal tiles, 1 on them, and C[m][m] = 0.
+//   QUAD (A = the C of GRAM, M = K; B = E [N][K]): nlin = nq nt persistent
+//     workgroups; workgroup (q, ti) takes E tile ti and the q-th of nq equal
+//     runs of the K-block pairs (tk, J), J >= tk, in band-major order, so the
+//     nt workgroups of a group read the same C blocks at the same time.
+//     acc[m][e] = (E C)[e][m] for the C rows m of band tk; when the band
+//     changes or the run ends: partial += sum acc[m][e] E[e][m] 4^erow[e],
+//     and acc restarts at zero.  Summed over all workgroups this is
+//     E C E^T's trace with C's upper block triangle standing for both halves.
 // Consecutive workgroup indices go to different XCDs; the index is remapped
 // so that each XCD runs a contiguous run of item numbers.  Workgroup w writes
 // its partial to part[2 (pbase + w) .. + 1].
@@ -191,6 +194,8 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_err_kernel(const GeArgs ga)
     }
     int64_t m0, n0, kb = 0, ke = K;
     float fold = 1.0f;
+    int64_t qp0 = 0, qp1 = 0;  // QUAD: this workgroup's pairs
+    int qtk = 0, qJ = 0;       // QUAD: the first pair's (tk, J)
     if (MODE == GE_GRAM) {
         int g0 = 0, base = 0, gm = 0;
         for (;;) {
@@ -218,19 +223,18 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_err_kernel(const GeArgs ga)
         n0 = (int64_t)tn * GE_TN;
         fold = tm != tn ? 2.0f : 1.0f;
     } else if (MODE == GE_QUAD) {
-        const int p = lin / ga.mt, ti = lin % ga.mt;
-        int c = 0, base = 0;
-        for (;;) {
-            const int cnt = ga.nt - c * ga.ch;
-            if (p < base + cnt) break;
-            base += cnt;
-            ++c;
-        }
-        const int tk = c * ga.ch + (p - base);
-        m0 = (int64_t)ti * GE_TM;
-        n0 = (int64_t)tk * GE_TN;
-        kb = (int64_t)c * ga.ch * GE_TN;
-        ke = min(min((int64_t)(c + 1) * ga.ch, (int64_t)tk + 1) * GE_TN, K);
+        // workgroup (q, ti) of nq = nlin / nt groups: E tile ti, the pairs
+        // [p0, p1) of group q; pair p = (tk, J), J = tk .. mt - 1, in tk-major
+        // order (band tk starts at pair tk mt - tk (tk - 1) / 2)
+        const int nq = ga.nlin / ga.nt, q = lin / ga.nt, ti = lin % ga.nt;
+        const int64_t P = (int64_t)ga.mt * (ga.mt + 1) / 2;
+        qp0 = q * P / nq;
+        qp1 = (q + 1) * P / nq;
+        qtk = 0;
+        while (qtk + 1 < ga.mt && (int64_t)(qtk + 1) * ga.mt - (int64_t)(qtk + 1) * qtk / 2 <= qp0) ++qtk;
+        qJ = qtk + (int)(qp0 - ((int64_t)qtk * ga.mt - (int64_t)qtk * (qtk - 1) / 2));
+        m0 = (int64_t)qtk * GE_TM;
+        n0 = (int64_t)ti * GE_TN;
     } else {
         const int group = lin / (GE_GROUP_M * ga.nt);
         const int first_m = group * GE_GROUP_M;
@@ -317,47 +321,185 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_err_kernel(const GeArgs ga)
     // has finished reading the buffer they overwrite, the one of stage ks - 1).
     // Before the barrier each wave waits for its own copies of stage ks (the
     // copies of later stages may stay in flight) and for its LDS reads.
-    const int ksteps = (int)((ke - kb + TK - 1) / TK);
     constexpr int D = C::DA + C::DB;
+#define GE_COMPUTE(stage)                                                                              \
+    do {                                                                                               \
+        const uint16_t *base = glds + (stage) * C::STAGE;                                              \
+        GE_FRAG(0, base, 0);                                                                           \
+        _Pragma("unroll") for (int kk = 0; kk < TK / 16; ++kk)                                         \
+        {                                                                                              \
+            const int cur = kk & 1;                                                                    \
+            if (kk + 1 < TK / 16) GE_FRAG(cur ^ 1, base, kk + 1);                                      \
+            _Pragma("unroll") for (int i = 0; i < 4; ++i)                                              \
+                _Pragma("unroll") for (int j = 0; j < NJ; ++j) acc[i][j] =                             \
+                    Mfma16<F16>::op(fa[cur][i], fb[cur][j], acc[i][j]);                                \
+        }                                                                                              \
+    } while (0)
+    double sd = 0.0, sy = 0.0;
+    if (MODE == GE_QUAD) {
+        // Persistent walk over the pairs [qp0, qp1): the copies run S - 1
+        // k-steps ahead across pair and band boundaries; when the band tk
+        // changes (or the range ends) the accumulators of tile (tk, ti) go
+        // through the epilogue and restart at zero.  K block J has `full`
+        // k-steps, the last one (J = mt - 1) `last`.
+        const int full = GE_TN / TK;
+        const int last = (int)((K - (int64_t)(ga.mt - 1) * GE_TN + TK - 1) / TK);
+        int ctk = qtk, cJ = qJ, ckk = 0, itk = qtk, iJ = qJ, ikk = 0, atk = qtk;
+        int64_t cp = qp0, ip = qp0;
+#define GE_QISSUE(buf)                                                                                 \
+    do {                                                                                               \
+        if (itk != atk) {                                                                              \
+            atk = itk;                                                                                 \
+            _Pragma("unroll") for (int i = 0; i < C::DA; ++i)                                          \
+            {                                                                                          \
+                const int r_ = (C::NW * i + wv) * C::RPI + lrow;                                       \
+                aoff[i] = min((int64_t)itk * GE_TM + r_, M - 1) * K + acs[i];                          \
+            }                                                                                          \
+        }                                                                                              \
+        GE_ISSUE((int64_t)iJ * GE_TN + (int64_t)ikk * TK, buf);                                        \
+        if (++ikk == (iJ < ga.mt - 1 ? full : last)) {                                                 \
+            ikk = 0;                                                                                   \
+            ++ip;                                                                                      \
+            if (++iJ == ga.mt) {                                                                       \
+                ++itk;                                                                                 \
+                iJ = itk;                                                                              \
+            }                                                                                          \
+        }                                                                                              \
+    } while (0)
+        int inflight = 0, st = 0;
 #pragma unroll
-    for (int p = 0; p < S - 1; ++p)
-        if (p < ksteps) GE_ISSUE(kb + (int64_t)p * TK, p);
-    for (int ks = 0; ks < ksteps; ++ks) {
-        ge_wait_copies(min(S - 2, ksteps - 1 - ks) * D);
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        if (ks + S - 1 < ksteps) GE_ISSUE(kb + (int64_t)(ks + S - 1) * TK, (ks + S - 1) % S);
-        const uint16_t *base = glds + (ks % S) * C::STAGE;
-        GE_FRAG(0, base, 0);
+        for (int b = 0; b < S - 1; ++b)
+            if (ip < qp1) {
+                GE_QISSUE(b);
+                ++inflight;
+            }
+        while (cp < qp1) {
+            ge_wait_copies((inflight - 1) * D);
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            if (ip < qp1) {
+                GE_QISSUE((st + S - 1) % S);
+                ++inflight;
+            }
+            GE_COMPUTE(st % S);
+            --inflight;
+            ++st;
+            if (++ckk == (cJ < ga.mt - 1 ? full : last)) {
+                ckk = 0;
+                ++cp;
+                int ntk = ctk;
+                if (++cJ == ga.mt) {
+                    ++ntk;
+                    cJ = ntk;
+                }
+                if (ntk != ctk || cp == qp1) {
+                    // epilogue of tile (ctk, ti): acc[i][j][4 g + u] = (E C)[e][m + u]
+                    // for the C rows m = mb0 + 32 i + 8 g and the E row
+                    // e = nb0 + 32 j; times E[e][m .. m + 3] (one 8-byte load;
+                    // the 16 loads of a row are in flight together), scaled by
+                    // 4^erow[e]
+                    const int64_t mb0 = (int64_t)ctk * GE_TM + wm * 128 + 4 * (lane >> 5);
+                    const int64_t nb0 = n0 + wn * 32 * NJ + (lane & 31);
 #pragma unroll
-        for (int kk = 0; kk < TK / 16; ++kk) {
-            const int cur = kk & 1;
-            if (kk + 1 < TK / 16) GE_FRAG(cur ^ 1, base, kk + 1);
+                    for (int j = 0; j < NJ; ++j) {
+                        const int64_t e = nb0 + j * 32;
+                        const int64_t ec = min(e, N - 1);
+                        const uint16_t *er = Bm + ec * K;
+                        uint2 ld[4][4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+                        for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < NJ; ++j) acc[i][j] = Mfma16<F16>::op(fa[cur][i], fb[cur][j], acc[i][j]);
+                            for (int g = 0; g < 4; ++g)
+                                ld[i][g] = *reinterpret_cast<const uint2 *>(er + min(mb0 + i * 32 + 8 * g, M - 4));
+                        double t = 0.0;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+#pragma unroll
+                            for (int g = 0; g < 4; ++g) {
+                                const uint32_t w2[2] = {ld[i][g].x, ld[i][g].y};
+                                double q = 0.0;
+#pragma unroll
+                                for (int u = 0; u < 4; ++u) {
+                                    const _Float16 ev =
+                                        __builtin_bit_cast(_Float16, (uint16_t)(w2[u >> 1] >> (16 * (u & 1))));
+                                    q += (double)acc[i][j][4 * g + u] * (double)(float)ev;
+                                }
+                                t = mb0 + i * 32 + 8 * g < M ? t + q : t;
+                            }
+                        if (e < N) sd += ldexp(t, 2 * ga.erow[ec]);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+                    ctk = ntk;
+                }
+            }
+        }
+#undef GE_QISSUE
+    } else {
+        // Pipeline: the copies of stage ks + S - 1 are issued right after the
+        // barrier that opens stage ks (that barrier also certifies that every
+        // wave has finished reading the buffer they overwrite, the one of
+        // stage ks - 1).  Before the barrier each wave waits for its own copies
+        // of stage ks (the copies of later stages may stay in flight) and for
+        // its LDS reads.
+        const int ksteps = (int)((ke - kb + TK - 1) / TK);
+#pragma unroll
+        for (int p = 0; p < S - 1; ++p)
+            if (p < ksteps) GE_ISSUE(kb + (int64_t)p * TK, p);
+        for (int ks = 0; ks < ksteps; ++ks) {
+            ge_wait_copies(min(S - 2, ksteps - 1 - ks) * D);
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            if (ks + S - 1 < ksteps) GE_ISSUE(kb + (int64_t)(ks + S - 1) * TK, (ks + S - 1) % S);
+            GE_COMPUTE(ks % S);
         }
     }
+#undef GE_COMPUTE
 #undef GE_FRAG
 #undef GE_ISSUE
 
     // epilogue: accumulator v of lane l in a 32 x 32 tile is row
     // 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32
-    double sd = 0.0, sy = 0.0;
     const int64_t nb0 = n0 + wn * 32 * NJ + (lane & 31);
     const int64_t mb0 = m0 + wm * 128 + 4 * (lane >> 5);
+    if (MODE == GE_GRAM) {
+        // acc[i][j][4 g + u] = G[m + u][n] for m = mb0 + 32 i + 8 g (a multiple
+        // of 4; M % 8 == 0, so m < M covers m + 3) and n = nb0 + 32 j: one
+        // 8-byte store of C[n][m .. m + 3], the transposed position.
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int64_t n = nb0 + j * 32;
+            if (n >= N) continue;
+            const float rn = ga.r[n] * fold;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int64_t m = mb0 + i * 32 + 8 * g;
+                    if (m >= M) continue;
+                    const float4 rm = *reinterpret_cast<const float4 *>(ga.r + m);
+                    const float rr[4] = {rm.x, rm.y, rm.z, rm.w};
+                    uint32_t hv[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const float c = m + u == n ? 0.0f : acc[i][j][4 * g + u] * rr[u] * rn;
+                        hv[u] = __builtin_bit_cast(uint16_t, (_Float16)c);
+                    }
+                    *reinterpret_cast<uint2 *>(ga.C + n * M + m) = make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
+                }
+        }
+        return;
+    }
+    if (MODE != GE_QUAD) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        // row exponents (SUB_Y with erow, QUAD) or row factors r (GRAM) of
-        // this lane's 16 rows in tile row i
+        // row exponents of this lane's 16 rows in tile row i (SUB with erow)
         int ev[16];
-        float rv[16];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int64_t mc = min(mb0 + i * 32 + 8 * (v >> 2) + (v & 3), M - 1);
-            ev[v] = ((MODE == GE_SUB_Y && ga.erow != nullptr) || MODE == GE_QUAD) ? ga.erow[mc] : 0;
-            rv[v] = MODE == GE_GRAM ? ga.r[mc] * fold : 0.0f;
-        }
+        for (int v = 0; v < 16; ++v)
+            ev[v] = (MODE == GE_SUB_Y && ga.erow != nullptr) ? ga.erow[min(mb0 + i * 32 + 8 * (v >> 2) + (v & 3), M - 1)] : 0;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             const int64_t n = nb0 + j * 32;
@@ -371,29 +513,6 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_err_kernel(const GeArgs ga)
                         ga.Y[m * N + n] = y;
                         sy = __builtin_fma((double)y, (double)y, sy);
                     }
-                }
-            } else if (MODE == GE_GRAM) {
-                const float rn = nin ? ga.r[n] : 0.0f;
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int64_t m = mb0 + i * 32 + 8 * (v >> 2) + (v & 3);
-                    if (m < M && nin) {
-                        const float c = m == n ? 0.0f : acc[i][j][v] * rv[v] * rn;
-                        ga.C[m * N + n] = __builtin_bit_cast(uint16_t, (_Float16)c);
-                    }
-                }
-            } else if (MODE == GE_QUAD) {
-                // E[m][n] = A[m][n] (N = K); the 16 reads are in flight together
-                const int64_t nc = min(n, N - 1);
-                _Float16 ev16[16];
-#pragma unroll
-                for (int v = 0; v < 16; ++v)
-                    ev16[v] = __builtin_bit_cast(_Float16, A[min(mb0 + i * 32 + 8 * (v >> 2) + (v & 3), M - 1) * K + nc]);
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int64_t m = mb0 + i * 32 + 8 * (v >> 2) + (v & 3);
-                    const double t = ldexp((double)acc[i][j][v] * (double)(float)ev16[v], 2 * ev[v]);
-                    sd = (m < M && nin) ? sd + t : sd;
                 }
             } else {
                 // the 16 reads of Y for this 32 x 32 tile are in flight together
@@ -411,7 +530,7 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_err_kernel(const GeArgs ga)
             }
         }
     }
-    if (MODE == GE_GRAM) return;
+    }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
         sd += __shfl_xor(sd, o, 64);
@@ -601,15 +720,15 @@ static int device_cus()
 // the last round would fill at most half of the CUs, its tiles run as
 // 256 x 128 halves instead (the round then takes half a tile's time).
 // Returns the number of workgroup partials written.
-template <bool F16, int MODE, int NJ>
+template <bool F16, int MODE, int NJ, int TK = HD_GE_TK, int S = HD_GE_STAGES>
 static hipError_t ge_launch(const GeArgs &ga, int64_t grid, hipStream_t st)
 {
-    typedef GeCfg<HD_GE_TK, HD_GE_STAGES, HD_GE_WN, NJ> C;
+    typedef GeCfg<TK, S, HD_GE_WN, NJ> C;
     if (grid <= 0) return hipSuccess;
-    const hipError_t e = hipFuncSetAttribute((const void *)gemm_err_kernel<F16, MODE, HD_GE_TK, HD_GE_STAGES, HD_GE_WN, NJ>,
+    const hipError_t e = hipFuncSetAttribute((const void *)gemm_err_kernel<F16, MODE, TK, S, HD_GE_WN, NJ>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS);
     if (e != hipSuccess) return e;
-    gemm_err_kernel<F16, MODE, HD_GE_TK, HD_GE_STAGES, HD_GE_WN, NJ><<<(unsigned)grid, C::THREADS, C::LDS, st>>>(ga);
+    gemm_err_kernel<F16, MODE, TK, S, HD_GE_WN, NJ><<<(unsigned)grid, C::THREADS, C::LDS, st>>>(ga);
     return hipGetLastError();
 }
 
@@ -751,13 +870,13 @@ hipError_t launch_output_error_codes(int fmt, int B, const void *X, int64_t M, c
 // power-of-two scale per row.
 //
 // output_gram():   h (hdiag), sqrt(h), 1/sqrt(h) (0 for h = 0); X^T in the
-//                  workspace; C's lower block triangle (256 x 256 blocks,
-//                  diagonal blocks whole) from one bf16 MFMA product over the
-//                  tiles tn <= tm, off-diagonal blocks stored as 2 C so that
-//                  the lower triangle stands for both halves;
+//                  workspace; C's upper block triangle (256 x 256 blocks,
+//                  diagonal blocks whole) from one bf16 MFMA product over
+//                  half of the tiles, off-diagonal blocks stored as 2 C so
+//                  that the upper triangle stands for both halves;
 // output_error_gram(): e and the diagonal sums per row (one workgroup per
-//                  row), then E C over each item's K range with the epilogue
-//                  sum of acc * e, then a fixed-order final sum.
+//                  row), then C E^T over each item's K range with the
+//                  epilogue sum of acc * e, then a fixed-order final sum.
 
 // Xt[k][m] = X[m][k] for m < M, 0 for M <= m < M8 (16-bit values; K % 8 == 0,
 // M8 % 8 == 0).  64 x 64 tiles through LDS with 16-byte global loads and
@@ -886,8 +1005,10 @@ __device__ __forceinline__ void gram_diff(const uint8_t *__restrict__ codes, con
 
 // One workgroup per row n: e = d sqrt(h) as float16 under the row exponent
 // erow[n] (largest |e| scaled into [2^14, 2^15); 0 for a zero row), and
-// dsum[n] = sum_j d_j^2 h_j in float64.
-template <int EK, int SK, typename WT, bool REF>
+// dsum[n] = sum_j d_j^2 h_j in float64.  RC > 0: the row's e values stay in
+// registers (RC chunks of 8 per thread, K <= 2048 RC) between the row maximum
+// and the float16 stores; RC = 0: a second pass recomputes them.
+template <int EK, int SK, typename WT, bool REF, int RC>
 __global__ __launch_bounds__(256) void gram_operand_kernel(const uint8_t *__restrict__ codes,
                                                            const uint8_t *__restrict__ scales, int B,
                                                            const WT *__restrict__ W, int64_t K,
@@ -901,7 +1022,8 @@ __global__ __launch_bounds__(256) void gram_operand_kernel(const uint8_t *__rest
     const int64_t nch = K / 8;
     int mx = 0;  // largest |e| as float bits (monotone for non-negative floats)
     double ds = 0.0;
-    for (int64_t c = threadIdx.x; c < nch; c += 256) {
+    float ek[RC > 0 ? RC : 1][8];
+    auto chunk = [&](int64_t c, float *e) {
         float d[8];
         gram_diff<EK, SK, WT, REF>(codes, scales, B, W, n, K, c * 8, d);
         const float4 q0 = *reinterpret_cast<const float4 *>(sq + c * 8);
@@ -912,9 +1034,19 @@ __global__ __launch_bounds__(256) void gram_operand_kernel(const uint8_t *__rest
         const float hv[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            mx = max(mx, __builtin_bit_cast(int, fabsf(d[j] * qv[j])));
+            e[j] = d[j] * qv[j];
+            mx = max(mx, __builtin_bit_cast(int, fabsf(e[j])));
             ds = __builtin_fma((double)d[j] * (double)d[j], (double)hv[j], ds);
         }
+    };
+    if (RC > 0) {
+#pragma unroll
+        for (int it = 0; it < RC; ++it) {
+            const int64_t c = threadIdx.x + 256 * it;
+            if (c < nch) chunk(c, ek[it]);
+        }
+    } else {
+        for (int64_t c = threadIdx.x; c < nch; c += 256) chunk(c, ek[0]);
     }
     mx = wave_max_int(mx);
     if ((threadIdx.x & 63) == 0) shm[threadIdx.x >> 6] = mx;
@@ -931,17 +1063,32 @@ __global__ __launch_bounds__(256) void gram_operand_kernel(const uint8_t *__rest
         dsum[n] = ds;
     }
     uint16_t *orow = E + n * K;
-    for (int64_t c = threadIdx.x; c < nch; c += 256) {
-        float d[8];
-        gram_diff<EK, SK, WT, REF>(codes, scales, B, W, n, K, c * 8, d);
+    auto store = [&](int64_t c, const float *e) {
         uint32_t o[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const _Float16 lo = (_Float16)ldexpf(d[2 * j] * sq[c * 8 + 2 * j], -ex);
-            const _Float16 hi = (_Float16)ldexpf(d[2 * j + 1] * sq[c * 8 + 2 * j + 1], -ex);
+            const _Float16 lo = (_Float16)ldexpf(e[2 * j], -ex);
+            const _Float16 hi = (_Float16)ldexpf(e[2 * j + 1], -ex);
             o[j] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
         }
         *reinterpret_cast<uint4 *>(orow + c * 8) = make_uint4(o[0], o[1], o[2], o[3]);
+    };
+    if (RC > 0) {
+#pragma unroll
+        for (int it = 0; it < RC; ++it) {
+            const int64_t c = threadIdx.x + 256 * it;
+            if (c < nch) store(c, ek[it]);
+        }
+    } else {
+        for (int64_t c = threadIdx.x; c < nch; c += 256) {
+            float e[8];
+            const int mx0 = mx;
+            const double ds0 = ds;
+            chunk(c, e);  // recomputes e (mx and ds are not used again)
+            mx = mx0;
+            ds = ds0;
+            store(c, e);
+        }
     }
 }
 
@@ -990,25 +1137,29 @@ size_t output_gram_ws(int64_t M, int64_t K)
     return (size_t)std::max(al256(K * M8 * 2), (int64_t)hdiag_ws(M, K));
 }
 
-// K blocks of 256 per work item of the E C product (HD_GRAM_CHUNK overrides).
-static int gram_chunk()
+// Workgroups of the C E^T walk: nq groups of nt (one per 256-row tile of E),
+// nq = CUs / nt (at least 1, at most the number of pairs); HD_GRAM_GROUPS
+// overrides nq.
+static int64_t gram_groups(int64_t N, int64_t K)
 {
-    const char *e = getenv("HD_GRAM_CHUNK");
-    const int v = e ? atoi(e) : 0;
-    return v >= 1 && v <= 1024 ? v : 4;
+    const int64_t nt = (N + GE_TN - 1) / GE_TN, mt = (K + GE_TM - 1) / GE_TM;
+    const int64_t P = mt * (mt + 1) / 2;
+    const char *e = getenv("HD_GRAM_GROUPS");
+    int64_t nq = e ? atoll(e) : 0;
+    if (nq <= 0) nq = device_cus() / std::max<int64_t>(nt, 1);
+    return std::max<int64_t>(1, std::min(nq, P));
 }
 
-static int64_t gram_items(int64_t N, int64_t K, int ch)
+// Upper bound of the partials: one per workgroup.
+static int64_t gram_items(int64_t N, int64_t K)
 {
-    const int64_t mt = (N + GE_TM - 1) / GE_TM, nt = (K + GE_TN - 1) / GE_TN;
-    int64_t pairs = 0;
-    for (int64_t c = 0; c * ch < nt; ++c) pairs += nt - c * ch;
-    return mt * pairs;
+    const int64_t nt = (N + GE_TN - 1) / GE_TN, mt = (K + GE_TM - 1) / GE_TM;
+    return nt * mt * (mt + 1) / 2;
 }
 
 size_t output_error_gram_ws(int64_t N, int64_t K)
 {
-    return (size_t)(al256(N * K * 2) + al256(N * 4) + al256(N * 8) + al256(gram_items(N, K, 1) * 16));
+    return (size_t)(al256(N * K * 2) + al256(N * 4) + al256(N * 8) + al256(gram_items(N, K) * 16));
 }
 
 hipError_t launch_output_gram(const void *X, int64_t M, int64_t K, const float *h, void *gram, void *ws,
@@ -1049,12 +1200,22 @@ static void launch_gram_operand(const uint8_t *codes, const uint8_t *scales, int
                                 int64_t K, const float *sq, const float *h, uint16_t *E, int *erow, double *dsum,
                                 hipStream_t st)
 {
-    if (wdt == HD_BF16)
-        gram_operand_kernel<EK, SK, uint16_t, REF><<<(unsigned)N, 256, 0, st>>>(
-            codes, scales, B, static_cast<const uint16_t *>(W), K, sq, h, E, erow, dsum);
-    else
-        gram_operand_kernel<EK, SK, float, REF><<<(unsigned)N, 256, 0, st>>>(
-            codes, scales, B, static_cast<const float *>(W), K, sq, h, E, erow, dsum);
+    const bool regs = K <= 2048 * 8;
+    if (wdt == HD_BF16) {
+        if (regs)
+            gram_operand_kernel<EK, SK, uint16_t, REF, 8><<<(unsigned)N, 256, 0, st>>>(
+                codes, scales, B, static_cast<const uint16_t *>(W), K, sq, h, E, erow, dsum);
+        else
+            gram_operand_kernel<EK, SK, uint16_t, REF, 0><<<(unsigned)N, 256, 0, st>>>(
+                codes, scales, B, static_cast<const uint16_t *>(W), K, sq, h, E, erow, dsum);
+    } else {
+        if (regs)
+            gram_operand_kernel<EK, SK, float, REF, 8><<<(unsigned)N, 256, 0, st>>>(
+                codes, scales, B, static_cast<const float *>(W), K, sq, h, E, erow, dsum);
+        else
+            gram_operand_kernel<EK, SK, float, REF, 0><<<(unsigned)N, 256, 0, st>>>(
+                codes, scales, B, static_cast<const float *>(W), K, sq, h, E, erow, dsum);
+    }
 }
 
 template <int F>
@@ -1080,8 +1241,7 @@ hipError_t launch_output_error_gram(int fmt, int B, const uint8_t *codes, const 
     int *erow = reinterpret_cast<int *>(w + al256(N * K * 2));
     double *dsum = reinterpret_cast<double *>(w + al256(N * K * 2) + al256(N * 4));
     double *part = reinterpret_cast<double *>(w + al256(N * K * 2) + al256(N * 4) + al256(N * 8));
-    const int ch = gram_chunk();
-    const int64_t items = N > 0 && K > 0 ? gram_items(N, K, ch) : 0;
+    const int64_t items = N > 0 && K > 0 ? gram_groups(N, K) * ((N + GE_TN - 1) / GE_TN) : 0;
     if (items > 0) {
         switch (fmt) {
         case -1: launch_gram_operand<ELEM_INT8, SCALE_INT8, true>(codes, scales, B, W, wdt, N, K, sq, gh, E, erow, dsum, st); break;
@@ -1097,8 +1257,7 @@ hipError_t launch_output_error_gram(int fmt, int B, const uint8_t *codes, const 
         case HD_INT4_F16: gram_operand_fmt<HD_INT4_F16>(codes, scales, B, W, wdt, N, K, sq, gh, E, erow, dsum, st); break;
         default: return hipErrorInvalidValue;
         }
-        GeArgs ga = ge_args(E, C, N, K, K);
-        ga.ch = ch;
+        GeArgs ga = ge_args(C, E, K, N, K);
         ga.nlin = (int)items;
         ga.erow = erow;
         ga.part = part;

@@ -5,7 +5,7 @@ The output error of every format's codes is compared with the oracle's output
 error of the dequantised weights (the definition, ||X Wq^T - X W^T||_F /
 ||X W^T||_F in float64), within 1e-4 relative; ||X W^T||^2 likewise.  The
 library's Gram buffer is also checked entry by entry: h bit for bit against
-hdiag(), and the stored correlations C = G / sqrt(h_j h_k) (lower block
+hdiag(), and the stored correlations C = G / sqrt(h_j h_k) (upper block
 triangle, off-diagonal 256 x 256 blocks doubled, zero diagonal) against the
 oracle's float64 X^T X within the float16 rounding plus the float32
 accumulation bound.  Shapes span several 256 x 256 tiles with ragged edges and
@@ -87,23 +87,23 @@ def test_gram_buffer(M, K):
     h, C = gram_parts(gram, K)
     h2, C2 = gram_parts(gram2, K)
     blk = np.arange(K) // 256
-    lower = blk[:, None] >= blk[None, :]  # the part of C the library writes and reads
+    upper = blk[:, None] <= blk[None, :]  # the part of C the library writes and reads
     np.testing.assert_array_equal(h, h2)
-    np.testing.assert_array_equal(C[lower], C2[lower])
+    np.testing.assert_array_equal(C[upper], C2[upper])
     np.testing.assert_array_equal(h, oracle.hdiag(synth.bits(X)))
     Xt = np.ascontiguousarray(synth.bits(X).T)
     G = oracle.matmul_nt(Xt, Xt)
     hg = np.diag(G).copy()
     r = np.where(hg > 0, 1.0 / np.sqrt(np.where(hg > 0, hg, 1.0)), 0.0)
     Ct = G * r[:, None] * r[None, :]
-    fold = np.where(blk[:, None] > blk[None, :], 2.0, 1.0)
+    fold = np.where(blk[:, None] < blk[None, :], 2.0, 1.0)
     np.fill_diagonal(Ct, 0.0)
-    exp = (fold * Ct)[lower]
-    got = C[lower].astype(np.float64)
-    tol = fold[lower] * (2.0 ** -11 * np.abs(Ct[lower]) + 1e-4) + 2.0 ** -24
+    exp = (fold * Ct)[upper]
+    got = C[upper].astype(np.float64)
+    tol = fold[upper] * (2.0 ** -11 * np.abs(Ct[upper]) + 1e-4) + 2.0 ** -24
     assert np.all(np.abs(got - exp) <= tol), float(np.max(np.abs(got - exp) - tol))
     assert np.all(np.diag(C) == 0.0)
-    assert np.all(C[3, :3] == 0.0) and np.all(C[4:, 3][blk[4:] >= blk[3]] == 0.0)
+    assert np.all(C[:3, 3] == 0.0) and np.all(C[3, 4:][blk[4:] >= blk[3]] == 0.0)
 
 
 @pytest.mark.parametrize("fmt", FMTS)
@@ -184,17 +184,18 @@ def test_output_error_gram_no_rows():
     assert ysq.item() == 0.0 and sums[0].item() == 0.0 and np.isnan(out.item())
 
 
-def test_output_error_gram_chunking_and_repeat(monkeypatch):
-    """The K range of each work item (HD_GRAM_CHUNK blocks of 256) changes
-    only the summation order; repeated calls agree bit for bit."""
+def test_output_error_gram_partition_and_repeat(monkeypatch):
+    """How the K-block pairs are split between workgroups (HD_GRAM_GROUPS
+    runs) changes only the summation order; repeated calls agree bit for
+    bit."""
     M, N, K, B = 600, 300, 1536, 32
     X, W = dev(acts(M, K, 21)), dev(weights_for(hd.INT8_E4M3, N, K, 22))
     c, s, _ = hd.quantize_blocks(hd.SSE_OPT, hd.INT8_E4M3, B, W)
     gram = hd.output_gram(X)
     ysq = hd.output_reference_gram(W, gram)
     vals = []
-    for ch in ("1", "2", "4", "64"):
-        monkeypatch.setenv("HD_GRAM_CHUNK", ch)
+    for nq in ("1", "2", "5", "21", "1000"):
+        monkeypatch.setenv("HD_GRAM_GROUPS", nq)
         a = hd.output_error_gram(hd.INT8_E4M3, B, c, s, W, gram, ysq).item()
         b = hd.output_error_gram(hd.INT8_E4M3, B, c, s, W, gram, ysq).item()
         assert a == b
@@ -217,3 +218,20 @@ def test_output_gram_errors():
     with pytest.raises(hd.HdiagError) as e:
         hd.output_gram(Xb, gram=torch.empty(16, dtype=torch.uint8, device="cuda"))
     assert e.value.status == hd.HD_ERR_INVALID_ARG
+
+
+def test_output_error_gram_wide_rows():
+    """K = 16640 > 16384: the operand kernel's two-pass path (the row does not
+    stay in registers)."""
+    M, N, K, B = 96, 24, 16640, 32
+    X, W = acts(M, K, 31), weights_for(hd.INT8_E4M3, N, K, 32)
+    Xd, Wd = dev(X), dev(W)
+    c, s, _ = hd.quantize_blocks(hd.SSE_OPT, hd.INT8_E4M3, B, Wd)
+    gram = hd.output_gram(Xd)
+    ysq = hd.output_reference_gram(Wd, gram)
+    out, sums = hd.output_error_gram(hd.INT8_E4M3, B, c, s, Wd, gram, ysq, sums=True)
+    torch.cuda.synchronize()
+    oe_o, d_o, y_o = oracle.output_error(synth.bits(X), synth.bits(W),
+                                         oracle.dequantize(hd.INT8_E4M3, B, npy(c), sc_np(s), N, K), sums=True)
+    assert out.item() == pytest.approx(oe_o, rel=1e-4)
+    np.testing.assert_allclose(npy(sums), [d_o, y_o], rtol=1e-4)
