@@ -144,6 +144,8 @@ struct GeArgs {
     const float *r;    // GRAM: 1 / sqrt(h) per row of A (A = B)
     uint16_t *C;       // GRAM: float16 [N][N] output
     double *part;      // per-workgroup partials, pairs of doubles (not GRAM)
+    int qa, qg, qper;  // QUAD: bands per panel, gangs, workgroup slots per gang
+    int64_t qcols;     // QUAD: panel columns in all
     int pbase;
 };
 
@@ -161,11 +163,16 @@ struct GeArgs {
 //     inside a group).  Epilogue: C[n][m] = fp16(f acc[m][n] r[m] r[n]) (the
 //     transposed position, so C holds the upper block triangle), f = 2 off
 //     the diagonal tiles, 1 on them, and C[m][m] = 0.
-//   QUAD (A = the C of GRAM, M = K; B = E [N][K]): nlin = nq nt persistent
-//     workgroups; workgroup (q, ti) takes E tile ti and the q-th of nq equal
-//     runs of the K-block pairs (tk, J), J >= tk, in band-major order, so the
-//     nt workgroups of a group read the same C blocks at the same time.
-//     acc[m][e] = (E C)[e][m] for the C rows m of band tk; when the band
+//   QUAD (A = the C of GRAM, M = K; B = E [N][K]): persistent workgroups in
+//     qg gangs of qper slots; slot sl of a gang is band offset qb = sl / nt
+//     and E tile ti = sl % nt (slots past qa nt idle).  The K-block pairs
+//     (tk, J >= tk) are cut into panels of qa bands; panel i has the columns
+//     J = qa i .. mt - 1, and gang x walks the x-th of qg equal runs of the
+//     qcols panel columns in order, each member doing band qa i + qb at the
+//     columns where J >= that band.  The members of a gang thus read the same
+//     qa C blocks and nt E blocks of a column at the same time (a gang is one
+//     XCD's worth of workgroups when qa > 1; qa = 1 gives gangs of nt).
+//     acc[m][e] = (E C)[e][m] for the C rows m of the band; when the panel
 //     changes or the run ends: partial += sum acc[m][e] E[e][m] 4^erow[e],
 //     and acc restarts at zero.  Summed over all workgroups this is
 //     E C E^T's trace with C's upper block triangle standing for both halves.
@@ -194,8 +201,8 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_err_kernel(const GeArgs ga)
     }
     int64_t m0, n0, kb = 0, ke = K;
     float fold = 1.0f;
-    int64_t qp0 = 0, qp1 = 0;  // QUAD: this workgroup's pairs
-    int qtk = 0, qJ = 0;       // QUAD: the first pair's (tk, J)
+    int64_t qc0 = 0, qc1 = 0;  // QUAD: this workgroup's panel columns
+    int qb = 0;                // QUAD: band offset within a panel
     if (MODE == GE_GRAM) {
         int g0 = 0, base = 0, gm = 0;
         for (;;) {
@@ -223,17 +230,14 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_err_kernel(const GeArgs ga)
         n0 = (int64_t)tn * GE_TN;
         fold = tm != tn ? 2.0f : 1.0f;
     } else if (MODE == GE_QUAD) {
-        // workgroup (q, ti) of nq = nlin / nt groups: E tile ti, the pairs
-        // [p0, p1) of group q; pair p = (tk, J), J = tk .. mt - 1, in tk-major
-        // order (band tk starts at pair tk mt - tk (tk - 1) / 2)
-        const int nq = ga.nlin / ga.nt, q = lin / ga.nt, ti = lin % ga.nt;
-        const int64_t P = (int64_t)ga.mt * (ga.mt + 1) / 2;
-        qp0 = q * P / nq;
-        qp1 = (q + 1) * P / nq;
-        qtk = 0;
-        while (qtk + 1 < ga.mt && (int64_t)(qtk + 1) * ga.mt - (int64_t)(qtk + 1) * qtk / 2 <= qp0) ++qtk;
-        qJ = qtk + (int)(qp0 - ((int64_t)qtk * ga.mt - (int64_t)qtk * (qtk - 1) / 2));
-        m0 = (int64_t)qtk * GE_TM;
+        // gang x = lin / qper, slot sl: band offset qb = sl / nt, E tile
+        // ti = sl % nt (slots past qa nt idle); the gang's run of panel
+        // columns is [qc0, qc1)
+        const int x = lin / ga.qper, sl = lin % ga.qper, ti = sl % ga.nt;
+        qb = sl / ga.nt;
+        qc0 = ga.qcols * x / ga.qg;
+        qc1 = sl < ga.qa * ga.nt ? ga.qcols * (x + 1) / ga.qg : qc0;
+        m0 = 0;
         n0 = (int64_t)ti * GE_TN;
     } else {
         const int group = lin / (GE_GROUP_M * ga.nt);
@@ -337,61 +341,77 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_err_kernel(const GeArgs ga)
     } while (0)
     double sd = 0.0, sy = 0.0;
     if (MODE == GE_QUAD) {
-        // Persistent walk over the pairs [qp0, qp1): the copies run S - 1
-        // k-steps ahead across pair and band boundaries; when the band tk
-        // changes (or the range ends) the accumulators of tile (tk, ti) go
-        // through the epilogue and restart at zero.  K block J has `full`
-        // k-steps, the last one (J = mt - 1) `last`.
+        // Persistent walk over this member's columns of [qc0, qc1): the
+        // copies run S - 1 k-steps ahead across column and panel boundaries;
+        // when the panel changes (or the run ends) the accumulators of tile
+        // (band, ti) go through the epilogue and restart at zero.  K block J
+        // has `full` k-steps, the last one (J = mt - 1) `last`.
         const int full = GE_TN / TK;
         const int last = (int)((K - (int64_t)(ga.mt - 1) * GE_TN + TK - 1) / TK);
-        int ctk = qtk, cJ = qJ, ckk = 0, itk = qtk, iJ = qJ, ikk = 0, atk = qtk;
-        int64_t cp = qp0, ip = qp0;
+        const int mt = ga.mt, qa = ga.qa;
+        // cursor (c, panel i, K block J) on this member's valid columns:
+        // band tk = qa i + qb exists and J >= tk
+#define GE_QVALID(i, J) (qa * (i) + qb < mt && (J) >= qa * (i) + qb)
+#define GE_QNEXT(c, i, J)                                                                              \
+    do {                                                                                               \
+        ++(c);                                                                                         \
+        if (++(J) == mt) {                                                                             \
+            ++(i);                                                                                     \
+            (J) = qa * (i);                                                                            \
+        }                                                                                              \
+    } while ((c) < qc1 && !GE_QVALID(i, J))
+        int64_t cc = qc0;
+        int ci = 0, cJ = 0;
+        {
+            int64_t r = qc0;
+            while (ci * qa < mt && r >= mt - qa * ci) {
+                r -= mt - qa * ci;
+                ++ci;
+            }
+            cJ = qa * ci + (int)r;
+            if (cc < qc1 && !GE_QVALID(ci, cJ)) GE_QNEXT(cc, ci, cJ);
+        }
+        int64_t ic = cc;
+        int ii = ci, iJ = cJ, ikk = 0, ckk = 0, atk = -1;
 #define GE_QISSUE(buf)                                                                                 \
     do {                                                                                               \
-        if (itk != atk) {                                                                              \
-            atk = itk;                                                                                 \
+        const int itk_ = qa * ii + qb;                                                                 \
+        if (itk_ != atk) {                                                                             \
+            atk = itk_;                                                                                \
             _Pragma("unroll") for (int i = 0; i < C::DA; ++i)                                          \
             {                                                                                          \
                 const int r_ = (C::NW * i + wv) * C::RPI + lrow;                                       \
-                aoff[i] = min((int64_t)itk * GE_TM + r_, M - 1) * K + acs[i];                          \
+                aoff[i] = min((int64_t)itk_ * GE_TM + r_, M - 1) * K + acs[i];                         \
             }                                                                                          \
         }                                                                                              \
         GE_ISSUE((int64_t)iJ * GE_TN + (int64_t)ikk * TK, buf);                                        \
-        if (++ikk == (iJ < ga.mt - 1 ? full : last)) {                                                 \
+        if (++ikk == (iJ < mt - 1 ? full : last)) {                                                    \
             ikk = 0;                                                                                   \
-            ++ip;                                                                                      \
-            if (++iJ == ga.mt) {                                                                       \
-                ++itk;                                                                                 \
-                iJ = itk;                                                                              \
-            }                                                                                          \
+            GE_QNEXT(ic, ii, iJ);                                                                      \
         }                                                                                              \
     } while (0)
         int inflight = 0, st = 0;
 #pragma unroll
         for (int b = 0; b < S - 1; ++b)
-            if (ip < qp1) {
+            if (ic < qc1) {
                 GE_QISSUE(b);
                 ++inflight;
             }
-        while (cp < qp1) {
+        while (cc < qc1) {
             ge_wait_copies((inflight - 1) * D);
             asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-            if (ip < qp1) {
+            if (ic < qc1) {
                 GE_QISSUE((st + S - 1) % S);
                 ++inflight;
             }
             GE_COMPUTE(st % S);
             --inflight;
             ++st;
-            if (++ckk == (cJ < ga.mt - 1 ? full : last)) {
+            if (++ckk == (cJ < mt - 1 ? full : last)) {
                 ckk = 0;
-                ++cp;
-                int ntk = ctk;
-                if (++cJ == ga.mt) {
-                    ++ntk;
-                    cJ = ntk;
-                }
-                if (ntk != ctk || cp == qp1) {
+                const int ctk = qa * ci + qb;
+                GE_QNEXT(cc, ci, cJ);
+                if (cc >= qc1 || qa * ci + qb != ctk) {
                     // epilogue of tile (ctk, ti): acc[i][j][4 g + u] = (E C)[e][m + u]
                     // for the C rows m = mb0 + 32 i + 8 g and the E row
                     // e = nb0 + 32 j; times E[e][m .. m + 3] (one 8-byte load;
@@ -433,11 +453,12 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_err_kernel(const GeArgs ga)
                         for (int j = 0; j < NJ; ++j)
 #pragma unroll
                             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-                    ctk = ntk;
                 }
             }
         }
 #undef GE_QISSUE
+#undef GE_QNEXT
+#undef GE_QVALID
     } else {
         // Pipeline: the copies of stage ks + S - 1 are issued right after the
         // barrier that opens stage ks (that barrier also certifies that every
@@ -1137,24 +1158,44 @@ size_t output_gram_ws(int64_t M, int64_t K)
     return (size_t)std::max(al256(K * M8 * 2), (int64_t)hdiag_ws(M, K));
 }
 
-// Workgroups of the C E^T walk: nq groups of nt (one per 256-row tile of E),
-// nq = CUs / nt (at least 1, at most the number of pairs); HD_GRAM_GROUPS
-// overrides nq.
-static int64_t gram_groups(int64_t N, int64_t K)
+// Schedule of the C E^T walk (the QUAD mode's gangs).  With nt E tiles and
+// P = CUs / 8 workgroups per XCD: when qa = P / nt bands per panel (at most 4)
+// fill at least 90% of an XCD, 8 gangs of P slots (one per XCD, qa nt busy);
+// otherwise gangs of nt (qa = 1), CUs / nt of them.  HD_GRAM_GROUPS = g
+// forces the second form with g gangs.
+struct GramPlan {
+    int qa, qg, qper;
+    int64_t qcols, wgs;
+};
+static GramPlan gram_plan(int64_t N, int64_t K)
 {
     const int64_t nt = (N + GE_TN - 1) / GE_TN, mt = (K + GE_TM - 1) / GE_TM;
-    const int64_t P = mt * (mt + 1) / 2;
+    const int64_t per = device_cus() / 8;
     const char *e = getenv("HD_GRAM_GROUPS");
-    int64_t nq = e ? atoll(e) : 0;
-    if (nq <= 0) nq = device_cus() / std::max<int64_t>(nt, 1);
-    return std::max<int64_t>(1, std::min(nq, P));
+    const int64_t forced = e ? atoll(e) : 0;
+    GramPlan g;
+    const int64_t qa = nt <= per ? per / nt : 0;
+    if (forced <= 0 && qa >= 1 && qa <= 4 && 10 * qa * nt >= 9 * per) {
+        g.qa = (int)qa;
+        g.qg = 8;
+        g.qper = (int)per;
+    } else {
+        g.qa = 1;
+        g.qg = (int)std::max<int64_t>(1, forced > 0 ? forced : device_cus() / std::max<int64_t>(nt, 1));
+        g.qper = (int)nt;
+    }
+    g.qcols = 0;
+    for (int64_t i = 0; i * g.qa < mt; ++i) g.qcols += mt - g.qa * i;
+    g.qg = (int)std::min<int64_t>(g.qg, g.qcols);
+    g.wgs = (int64_t)g.qg * g.qper;
+    return g;
 }
 
 // Upper bound of the partials: one per workgroup.
 static int64_t gram_items(int64_t N, int64_t K)
 {
     const int64_t nt = (N + GE_TN - 1) / GE_TN, mt = (K + GE_TM - 1) / GE_TM;
-    return nt * mt * (mt + 1) / 2;
+    return std::max<int64_t>(nt * mt * (mt + 1) / 2, device_cus());
 }
 
 size_t output_error_gram_ws(int64_t N, int64_t K)
@@ -1241,7 +1282,8 @@ hipError_t launch_output_error_gram(int fmt, int B, const uint8_t *codes, const 
     int *erow = reinterpret_cast<int *>(w + al256(N * K * 2));
     double *dsum = reinterpret_cast<double *>(w + al256(N * K * 2) + al256(N * 4));
     double *part = reinterpret_cast<double *>(w + al256(N * K * 2) + al256(N * 4) + al256(N * 8));
-    const int64_t items = N > 0 && K > 0 ? gram_groups(N, K) * ((N + GE_TN - 1) / GE_TN) : 0;
+    const GramPlan plan = gram_plan(N, K);
+    const int64_t items = N > 0 && K > 0 ? plan.wgs : 0;
     if (items > 0) {
         switch (fmt) {
         case -1: launch_gram_operand<ELEM_INT8, SCALE_INT8, true>(codes, scales, B, W, wdt, N, K, sq, gh, E, erow, dsum, st); break;
@@ -1259,6 +1301,10 @@ hipError_t launch_output_error_gram(int fmt, int B, const uint8_t *codes, const 
         }
         GeArgs ga = ge_args(C, E, K, N, K);
         ga.nlin = (int)items;
+        ga.qa = plan.qa;
+        ga.qg = plan.qg;
+        ga.qper = plan.qper;
+        ga.qcols = plan.qcols;
         ga.erow = erow;
         ga.part = part;
         const hipError_t e = ge_launch<true, GE_QUAD, 8 / HD_GE_WN>(ga, items, st);
