@@ -278,7 +278,7 @@ hd_status output_error_codes(hd_format fmt, int32_t B, const void *X, hd_dtype x
  * output_gram() fills a caller-allocated device buffer `gram` of at least
  * output_gram_size(K) bytes (16-byte aligned) with data private to the
  * library: h = diag(G), and C = G / sqrt(h_j h_k) off the diagonal (0 where h
- * is 0), as float16, lower triangle only.  X: bfloat16 [M, K], K % 8 == 0;
+ * is 0), as float16, one triangle only.  X: bfloat16 [M, K], K % 8 == 0;
  * the products run on the bf16 MFMA units with float32 accumulation.
  * h (optional, device, float [K]): hdiag(X) already computed on the same X;
  * NULL computes it here.  The buffer stays valid as long as X is unchanged.
