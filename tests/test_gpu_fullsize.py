@@ -87,6 +87,38 @@ def test_config2_int8_full():
     full_x_checks(X, W, Wq)
 
 
+def test_config2_gram_route_full():
+    """The bench step's output error (through G = X^T X) at config 2's full
+    size: against the direct route (X Wq^T - Y, an independent product) over
+    the whole X for every quantisation of the step, and against the oracle on
+    the first R rows of X (G of that row subset).  W = Wq gives exactly 0."""
+    W, X = synth.config_inputs(2)
+    Xd, Wd = X.cuda(), W.cuda()
+    N, K = W.shape
+    h = hd.hdiag(Xd)
+    gram = hd.output_gram(Xd, h=h)
+    ysq = hd.output_reference_gram(Wd, gram)
+    ref = hd.output_reference(Xd, Wd)
+    assert ysq.item() == pytest.approx(hd.reference_ysq(ref).item(), rel=1e-4)
+    for B in (32, 64, 128, 256):
+        for m in (hd.NAIVE, hd.SSE_OPT, hd.H_OPT):
+            c, s, _ = hd.quantize_blocks(m, hd.INT8_E4M3, B, Wd, h=h)
+            g = hd.output_error_gram(hd.INT8_E4M3, B, c, s, Wd, gram, ysq).item()
+            d = hd.output_error_codes(hd.INT8_E4M3, B, Xd, c, s, ref, N, K).item()
+            assert g == pytest.approx(d, rel=1e-4), (B, m)
+    R = 192
+    Xs = Xd[:R].contiguous()
+    gram_s = hd.output_gram(Xs)
+    ysq_s = hd.output_reference_gram(Wd, gram_s)
+    sub = hd.output_error_gram(hd.INT8_E4M3, 256, c, s, Wd, gram_s, ysq_s).item()
+    Wq = hd.dequantize(hd.INT8_E4M3, 256, c, s, N, K)
+    sub_o = oracle.output_error(synth.bits(X[:R]), synth.bits(W), Wq.cpu().numpy())
+    assert sub == pytest.approx(sub_o, rel=1e-4)
+    # W = the codes' own float32 dequantisation: D = 0 exactly
+    ysq_q = hd.output_reference_gram(Wq, gram)
+    assert hd.output_error_gram(hd.INT8_E4M3, 256, c, s, Wq, gram, ysq_q).item() == 0.0
+
+
 def test_config3_nvfp4_full_x():
     W, _ = synth.config_inputs(3, x_rows=0)
     cfg = synth.CONFIGS[3]["X"]
