@@ -15,8 +15,12 @@ with per-row lognormal gain for the down_proj weight) and calibration X
     output_reference (Y = X W^T) once and output_error_codes (X Wq^T - Y, one
     M x N x K MFMA product) per quantisation.
 value = 12 quantisations x 2560 x 9728 weights / step time, in Gweights/s.
-Inputs are resident in HBM before timing starts.  Per-call GPU times come from
-HIP events recorded on the stream the kernels run on, over the timed steps.
+Inputs are resident in HBM before timing starts.  The step is timed twice:
+as individual launches (per-call GPU times from HIP events recorded on the
+stream the kernels run on: the per-stage figures and the roofline) and as
+replays of the same step captured once in a HIP graph (no host launch gaps;
+a replay must first reproduce the eager step's errors bit for bit), which
+gives ms_per_step and value unless --eager is given.
 
 Prints one JSON line (the metric, per-stage figures, the roofline of the
 dominant kernel and the CPU oracle timed on a bounded sample).
@@ -100,6 +104,8 @@ def parse():
     ap.add_argument("--suite", choices=["headline", "formats", "gptq", "sigma", "gemm", "hbm"], default="headline",
                     help="headline: the step above (one JSON line, the default); formats: every element / "
                          "scale format x B in {16, 32} x scale choice on the same W and h (one JSON line)")
+    ap.add_argument("--eager", action="store_true",
+                    help="time the step as individual launches instead of replays of one captured HIP graph")
     ap.add_argument("--output-route", choices=["gram", "direct"], default="gram",
                     help="output error through G = X^T X (gram) or through X W^T (direct)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -221,7 +227,31 @@ def main():
         step(True)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    ms_eager = (t1 - t0) * 1e3 / args.steps
+    ms_per_step, launch = ms_eager, "eager"
+    if not args.eager:
+        # the same step captured once as a HIP graph (every launch of the step,
+        # same buffers) and replayed: a replay must reproduce the eager errors
+        # bit for bit before its time is used
+        eager_w, eager_o = werr.clone(), oerr.clone()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step(False)
+        werr.zero_()
+        oerr.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        if not (torch.equal(werr, eager_w) and torch.equal(oerr, eager_o)):
+            raise SystemExit("graph replay does not reproduce the eager step")
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        ms_per_step, launch = (t1 - t0) * 1e3 / args.steps, "hip_graph"
     value = len(blocks) * len(methods) * N * K / (ms_per_step * 1e-3) / 1e9
 
     # per-stage GPU times (ms per launch), from the events
@@ -294,6 +324,7 @@ def main():
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": "Gweights/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3),
+        "launch": launch, "ms_per_step_eager": round(ms_eager, 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "INT8 (E4M3 scales) on W 2560x9728 bf16, h from X 16384x9728 bf16; "
