@@ -303,6 +303,10 @@ hd_status output_error_codes(hd_format fmt, int32_t B, const void *X, hd_dtype x
  * workspace: ws_bytes >= output_error_gram_workspace_size(N, K); each call
  * needs its own.  Calls that share `gram` may run concurrently (it is only
  * read).
+ * Tuning: the environment variable HD_GRAM_GROUPS = g (read per call) makes
+ * the C E^T product use g groups of one workgroup per 256-row tile of E
+ * instead of its default schedule; it changes only the order of the fp64
+ * partial sums.
  * Errors: HD_ERR_INVALID_ARG as quantize_blocks for fmt / B / N / K, NULL or
  * misaligned pointers, a short buffer or workspace, K % 8 != 0 for
  * output_gram; HD_ERR_UNSUPPORTED for a float32 X. */
