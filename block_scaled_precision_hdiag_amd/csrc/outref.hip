@@ -139,7 +139,7 @@ struct GeArgs {
     int lin0, nlin;    // work items of this launch: lin0 .. lin0 + nlin - 1
     int split;         // STORE_Y / SUB_Y: two half-width workgroups per tile
     float *Y;          // STORE_Y (written) / SUB_Y (read): float [M][N]
-    const int *erow;   // SUB_Y (may be NULL) / QUAD: power-of-two exponent per row of A
+    const int *erow;   // SUB_Y: exponent per row of A (may be NULL); QUAD: per row of B (E)
     double fscale;     // SUB_Y
     const float *r;    // GRAM: 1 / sqrt(h) per row of A (A = B)
     uint16_t *C;       // GRAM: float16 [N][N] output
@@ -1192,7 +1192,7 @@ static GramPlan gram_plan(int64_t N, int64_t K)
 }
 
 // Upper bound of the partials: one per workgroup.
-static int64_t gram_items(int64_t N, int64_t K)
+static int64_t gram_parts_max(int64_t N, int64_t K)
 {
     const int64_t nt = (N + GE_TN - 1) / GE_TN, mt = (K + GE_TM - 1) / GE_TM;
     return std::max<int64_t>(nt * mt * (mt + 1) / 2, device_cus());
@@ -1200,7 +1200,7 @@ static int64_t gram_items(int64_t N, int64_t K)
 
 size_t output_error_gram_ws(int64_t N, int64_t K)
 {
-    return (size_t)(al256(N * K * 2) + al256(N * 4) + al256(N * 8) + al256(gram_items(N, K) * 16));
+    return (size_t)(al256(N * K * 2) + al256(N * 4) + al256(N * 8) + al256(gram_parts_max(N, K) * 16));
 }
 
 hipError_t launch_output_gram(const void *X, int64_t M, int64_t K, const float *h, void *gram, void *ws,
