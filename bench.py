@@ -9,8 +9,9 @@ with per-row lognormal gain for the down_proj weight) and calibration X
     output_reference_gram (||X W^T||^2 from G), then for B in
     {32, 64, 128, 256} and each of Naive, SSE-Optimal, H-Optimal:
     quantize_blocks (scale choice + encode), dequantize, weight error and
-    output error (output_error_gram: sum_n d_n^T G d_n for D = Wq - W, one
-    N x K x K MFMA product over G's lower block triangle).
+    output error (output_error_gram_batch after the loop: sum_n d_n^T G d_n
+    for D = Wq - W of all 12 quantisations, one MFMA walk of 12 N x K x K over
+    G's upper block triangle).
     --output-route direct measures the output error with X instead:
     output_reference (Y = X W^T) once and output_error_codes (X Wq^T - Y, one
     M x N x K MFMA product) per quantisation.
@@ -161,13 +162,16 @@ def main():
     if gram_route:
         gram = torch.empty(hd.output_gram_size(K), dtype=torch.uint8, device=dev)
         ws_g = torch.empty(hd.output_gram_workspace_size(M, K), dtype=torch.uint8, device=dev)
-        ws_o = torch.empty(hd.output_error_gram_workspace_size(N, K), dtype=torch.uint8, device=dev)
+        ws_o = torch.empty(hd.output_error_gram_batch_workspace_size(len(blocks) * len(methods), N, K),
+                           dtype=torch.uint8, device=dev)
         ysq = torch.empty(1, dtype=torch.float64, device=dev)
     else:
         ref = torch.empty(hd.output_reference_size(M, N, K), dtype=torch.uint8, device=dev)
         ws_o = torch.empty(hd.output_error_codes_workspace_size(M, N, K), dtype=torch.uint8, device=dev)
-    codes = {B: torch.empty((N, K), dtype=torch.uint8, device=dev) for B in blocks}
-    scales = {B: torch.empty((N, K // B), dtype=torch.uint8, device=dev) for B in blocks}
+    # one code / scale buffer per quantisation (B, method): the Gram route
+    # scores all of them together after the loop
+    codes = {(B, m): torch.empty((N, K), dtype=torch.uint8, device=dev) for B in blocks for _, m in methods}
+    scales = {(B, m): torch.empty((N, K // B), dtype=torch.uint8, device=dev) for B in blocks for _, m in methods}
     Wq = torch.empty((N, K), dtype=torch.float32, device=dev)
     werr = torch.empty((len(blocks), 3), dtype=torch.float64, device=dev)
     oerr = torch.empty((len(blocks), 3), dtype=torch.float64, device=dev)
@@ -205,19 +209,20 @@ def main():
         for bi, B in enumerate(blocks):
             for mi, (mname, m) in enumerate(methods):
                 stage = "naive" if m == hd.NAIVE else "search_" + mname
-                timed(stage, B, lambda: hd.quantize_blocks(m, fmt, B, W, h=h, codes=codes[B], scales=scales[B]),
-                      rec)
-                timed("dequantize", B, lambda: hd.dequantize(fmt, B, codes[B], scales[B], N, K, out=Wq), rec)
+                cb, sb = codes[(B, m)], scales[(B, m)]
+                timed(stage, B, lambda: hd.quantize_blocks(m, fmt, B, W, h=h, codes=cb, scales=sb), rec)
+                timed("dequantize", B, lambda: hd.dequantize(fmt, B, cb, sb, N, K, out=Wq), rec)
                 timed("weight_error", B, lambda: hd.weight_error(W, Wq, workspace=ws_w, out=werr[bi, mi:mi + 1]),
                       rec)
-                if gram_route:
+                if not gram_route:
                     timed("output_error", B,
-                          lambda: hd.output_error_gram(fmt, B, codes[B], scales[B], W, gram, ysq, workspace=ws_o,
-                                                       out=oerr[bi, mi:mi + 1]), rec)
-                else:
-                    timed("output_error", B,
-                          lambda: hd.output_error_codes(fmt, B, X, codes[B], scales[B], ref, N, K, workspace=ws_o,
+                          lambda: hd.output_error_codes(fmt, B, X, cb, sb, ref, N, K, workspace=ws_o,
                                                         out=oerr[bi, mi:mi + 1]), rec)
+        if gram_route:
+            # the 12 output errors in one call (one MFMA walk over their stacked operand)
+            items = [(fmt, B, codes[(B, m)], scales[(B, m)]) for B in blocks for _, m in methods]
+            timed("output_error", 0,
+                  lambda: hd.output_error_gram_batch(items, W, gram, ysq, workspace=ws_o, out=oerr.view(-1)), rec)
 
     for _ in range(args.warmup):
         step(False)
@@ -272,7 +277,7 @@ def main():
         # and the quadratic forms d^T G d over G's symmetric halves (N K^2)
         "output_gram": ("mfma", 1.0 * M * K * (K + 1)),
         "output_reference": ("mfma", 1.0 * N * K * K if gram_route else 2.0 * M * N * K),
-        "output_error": ("mfma", 1.0 * N * K * K if gram_route else 2.0 * M * N * K),
+        "output_error": ("mfma", len(blocks) * len(methods) * 1.0 * N * K * K if gram_route else 2.0 * M * N * K),
         "search_sse": ("alu", N * K * n_cand * SEARCH_OPS["sse"]),
         "search_h": ("alu", N * K * n_cand * SEARCH_OPS["h"]),
     }

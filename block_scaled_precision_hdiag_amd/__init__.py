@@ -41,6 +41,7 @@ EXPORTS = ["hdiag", "hdiag_workspace_size", "quantize_blocks", "encode_blocks", 
            "output_error_given_ref", "output_reference", "output_reference_size", "output_error_codes",
            "output_error_codes_workspace_size", "output_gram", "output_gram_size", "output_gram_workspace_size",
            "output_reference_gram", "output_error_gram", "output_error_gram_workspace_size",
+           "output_error_gram_batch", "output_error_gram_batch_workspace_size",
            "quantize_blocks_tensor_scaled",
            "quantize_blocks_tensor_scaled_workspace_size", "dequantize_tensor_scaled", "gptq_hessian", "gptq_hessian_workspace_size", "gptq_quantize",
            "gptq_workspace_size",
@@ -93,6 +94,9 @@ def lib():
         L.output_error_gram_workspace_size.restype = sz
         L.output_reference_gram.argtypes = [P, i32, i64, i64, P, sz, P, P, sz, P]
         L.output_error_gram.argtypes = [i32, i32, P, P, P, i32, i64, i64, P, sz, P, P, P, P, sz, P]
+        L.output_error_gram_batch_workspace_size.argtypes = [i32, i64, i64]
+        L.output_error_gram_batch_workspace_size.restype = sz
+        L.output_error_gram_batch.argtypes = [i32, P, P, P, P, P, i32, i64, i64, P, sz, P, P, P, P, sz, P]
         L.hdiag_strerror.argtypes = [i32]
         L.hdiag_strerror.restype = ctypes.c_char_p
         L.hdiag_last_error.argtypes = []
@@ -112,7 +116,8 @@ def lib():
         L.gptq_quantize.argtypes = [i32, i32, i32, P, i32, i64, i64, P, ctypes.c_double, i32, P, P, P, P, P, sz, P]
         for name in ("hdiag", "quantize_blocks", "encode_blocks", "dequantize", "weight_error",
                      "output_error", "output_error_given_ref", "output_reference", "output_error_codes",
-                     "output_gram", "output_reference_gram", "output_error_gram", "hdiag_format_info", "gptq_hessian", "gptq_quantize", "quantize_blocks_tensor_scaled",
+                     "output_gram", "output_reference_gram", "output_error_gram", "output_error_gram_batch",
+                     "hdiag_format_info", "gptq_hessian", "gptq_quantize", "quantize_blocks_tensor_scaled",
                      "dequantize_tensor_scaled"):
             getattr(L, name).restype = i32
         _lib = L
@@ -381,6 +386,32 @@ def output_error_gram(fmt, B, codes, scales, W, gram, ysq, sums=False, workspace
     _check(lib().output_error_gram(fmt, B, _ptr(codes), _ptr(scales), _ptr(W), _dt(W), N, K, _ptr(gram),
                                    gram.numel(), _ptr(ysq), _ptr(out), _ptr(s), _ptr(ws), ws.numel(), _stream(d)),
            "output_error_gram")
+    return (out, s) if sums else out
+
+
+def output_error_gram_batch_workspace_size(count, N, K):
+    return int(lib().output_error_gram_batch_workspace_size(count, N, K))
+
+
+def output_error_gram_batch(items, W, gram, ysq, sums=False, workspace=None, out=None):
+    """output_error_gram for several quantisations of W in one call: items is a
+    sequence of (fmt, B, codes, scales).  Returns a float64 device tensor
+    [len(items)] (and [len(items), 2] sums)."""
+    d = _dev(W)
+    N, K = W.shape
+    n = len(items)
+    if out is None:
+        out = torch.empty(n, dtype=torch.float64, device=d)
+    s = torch.empty((n, 2), dtype=torch.float64, device=d) if sums else None
+    fm = (ctypes.c_int * n)(*[int(it[0]) for it in items])
+    bs = (ctypes.c_int32 * n)(*[int(it[1]) for it in items])
+    cs = (ctypes.c_void_p * n)(*[it[2].data_ptr() for it in items])
+    ss = (ctypes.c_void_p * n)(*[it[3].data_ptr() for it in items])
+    need = output_error_gram_batch_workspace_size(n, N, K)
+    ws = workspace if workspace is not None else torch.empty(max(need, 16), dtype=torch.uint8, device=d)
+    _check(lib().output_error_gram_batch(n, fm, bs, cs, ss, _ptr(W), _dt(W), N, K, _ptr(gram), gram.numel(),
+                                         _ptr(ysq), _ptr(out), _ptr(s), _ptr(ws), ws.numel(), _stream(d)),
+           "output_error_gram_batch")
     return (out, s) if sums else out
 
 

@@ -341,7 +341,13 @@ hd_status output_gram(const void *X, hd_dtype xt, int64_t M, int64_t K, const fl
 size_t output_error_gram_workspace_size(int64_t N, int64_t K)
 {
     if (N < 0 || K < 0) return 0;
-    return hd::output_error_gram_ws(N, K);
+    return hd::output_error_gram_ws(1, N, K);
+}
+
+size_t output_error_gram_batch_workspace_size(int32_t count, int64_t N, int64_t K)
+{
+    if (count < 1 || N < 0 || K < 0) return 0;
+    return hd::output_error_gram_ws(count, N, K);
 }
 
 hd_status output_reference_gram(const void *W, hd_dtype wt, int64_t N, int64_t K, const void *gram,
@@ -355,19 +361,31 @@ hd_status output_reference_gram(const void *W, hd_dtype wt, int64_t N, int64_t K
     HD_CHECK_PTR(gram, true);
     HD_REQUIRE(gram_bytes >= (size_t)hd::output_gram_layout(K).bytes, "gram buffer too small");
     HD_CHECK_PTR(ws, true);
-    HD_REQUIRE(ws_bytes >= hd::output_error_gram_ws(N, K), "workspace too small");
+    HD_REQUIRE(ws_bytes >= hd::output_error_gram_ws(1, N, K), "workspace too small");
     HD_CHECK_PTR(W, N * K > 0);
-    return hip_status(hd::launch_output_error_gram(-1, 8, nullptr, nullptr, W, wt, N, K, gram, nullptr, ysq,
-                                                   nullptr, nullptr, ws, (hipStream_t)stream),
+    return hip_status(hd::launch_output_error_gram(1, nullptr, nullptr, nullptr, nullptr, W, wt, N, K, gram, nullptr,
+                                                   ysq, nullptr, nullptr, ws, (hipStream_t)stream),
                       "output_reference_gram");
 }
 
-hd_status output_error_gram(hd_format fmt, int32_t B, const uint8_t *codes, const uint8_t *scales, const void *W,
-                            hd_dtype wt, int64_t N, int64_t K, const void *gram, size_t gram_bytes,
-                            const double *ysq, double *out, double *sums, void *ws, size_t ws_bytes, void *stream)
+hd_status output_error_gram_batch(int32_t count, const hd_format *fmts, const int32_t *Bs,
+                                  const uint8_t *const *codes, const uint8_t *const *scales, const void *W,
+                                  hd_dtype wt, int64_t N, int64_t K, const void *gram, size_t gram_bytes,
+                                  const double *ysq, double *out, double *sums, void *ws, size_t ws_bytes,
+                                  void *stream)
 {
-    hd_status s = check_quant_shape(fmt, B, N, K);
-    if (s != HD_OK) return s;
+    HD_REQUIRE(count >= 1 && count <= 4096, "count=%d is not in 1..4096", (int)count);
+    HD_REQUIRE(fmts != nullptr && Bs != nullptr && codes != nullptr && scales != nullptr,
+               "fmts, Bs, codes and scales must be host arrays of count entries");
+    int f[4096], b[4096];
+    for (int32_t q = 0; q < count; ++q) {
+        hd_status s = check_quant_shape(fmts[q], Bs[q], N, K);
+        if (s != HD_OK) return s;
+        f[q] = (int)fmts[q];
+        b[q] = (int)Bs[q];
+        HD_CHECK_PTR(codes[q], N * K > 0);
+        if (N * K > 0 && scales[q] == nullptr) return fail(HD_ERR_INVALID_ARG, "scales[%d] is NULL", (int)q);
+    }
     HD_REQUIRE(valid_dtype(wt), "unknown dtype %d", (int)wt);
     HD_REQUIRE(N <= (int64_t)1 << 31 && K <= (int64_t)1 << 17, "size too large");
     HD_REQUIRE(out != nullptr, "out is NULL");
@@ -375,13 +393,23 @@ hd_status output_error_gram(hd_format fmt, int32_t B, const uint8_t *codes, cons
     HD_CHECK_PTR(gram, true);
     HD_REQUIRE(gram_bytes >= (size_t)hd::output_gram_layout(K).bytes, "gram buffer too small");
     HD_CHECK_PTR(ws, true);
-    HD_REQUIRE(ws_bytes >= hd::output_error_gram_ws(N, K), "workspace too small");
+    HD_REQUIRE(ws_bytes >= hd::output_error_gram_ws(count, N, K), "workspace too small");
     HD_CHECK_PTR(W, N * K > 0);
-    HD_CHECK_PTR(codes, N * K > 0);
-    if (N * K > 0 && scales == nullptr) return fail(HD_ERR_INVALID_ARG, "scales is NULL");
-    return hip_status(hd::launch_output_error_gram(fmt, B, codes, scales, W, wt, N, K, gram, ysq, nullptr, out,
+    return hip_status(hd::launch_output_error_gram(count, f, b, codes, scales, W, wt, N, K, gram, ysq, nullptr, out,
                                                    sums, ws, (hipStream_t)stream),
-                      "output_error_gram");
+                      "output_error_gram_batch");
+}
+
+hd_status output_error_gram(hd_format fmt, int32_t B, const uint8_t *codes, const uint8_t *scales, const void *W,
+                            hd_dtype wt, int64_t N, int64_t K, const void *gram, size_t gram_bytes,
+                            const double *ysq, double *out, double *sums, void *ws, size_t ws_bytes, void *stream)
+{
+    if (codes == nullptr && N * K > 0) return fail(HD_ERR_INVALID_ARG, "codes is NULL");
+    const uint8_t *cs[1] = {codes}, *ss[1] = {scales};
+    const hd_format fs[1] = {fmt};
+    const int32_t bs[1] = {B};
+    return output_error_gram_batch(1, fs, bs, cs, ss, W, wt, N, K, gram, gram_bytes, ysq, out, sums, ws, ws_bytes,
+                                   stream);
 }
 
 bool is_e4m3_scaled(int f) { return f == HD_INT8_E4M3 || f == HD_NVFP4 || f == HD_FP8_E4M3S || f == HD_NVINT4; }

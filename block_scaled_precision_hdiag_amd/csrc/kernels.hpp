@@ -84,11 +84,13 @@ size_t output_gram_ws(int64_t M, int64_t K);
 // h: float [K] = hdiag(X), or NULL to compute it here.
 hipError_t launch_output_gram(const void *X, int64_t M, int64_t K, const float *h, void *gram, void *ws,
                               hipStream_t st);
-size_t output_error_gram_ws(int64_t N, int64_t K);
-// fmt >= 0: *out = ||X (Wq - W)^T|| / sqrt(*ysq); fmt < 0: *ysq_out = ||X W^T||^2.
-hipError_t launch_output_error_gram(int fmt, int B, const uint8_t *codes, const uint8_t *scales, const void *W,
-                                    int wdt, int64_t N, int64_t K, const void *gram, const double *ysq,
-                                    double *ysq_out, double *out, double *sums, void *ws, hipStream_t st);
+size_t output_error_gram_ws(int64_t count, int64_t N, int64_t K);
+// count quantisations (host arrays fmt, B, codes, scales) of one W:
+// out[q] = ||X (Wq_q - W)^T|| / sqrt(*ysq); fmt == NULL: ysq_out[0] = ||X W^T||^2.
+hipError_t launch_output_error_gram(int count, const int *fmt, const int *B, const uint8_t *const *codes,
+                                    const uint8_t *const *scales, const void *W, int wdt, int64_t N, int64_t K,
+                                    const void *gram, const double *ysq, double *ysq_out, double *out, double *sums,
+                                    void *ws, hipStream_t st);
 
 // Y = A B^T (bf16 A [M][K], B [N][K], float32 Y [M][N]) on the MFMA product of
 // outref.hip; part: output_gemm_parts_bytes(M, N) bytes of scratch.

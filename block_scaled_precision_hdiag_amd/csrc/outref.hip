@@ -144,8 +144,10 @@ struct GeArgs {
     const float *r;    // GRAM: 1 / sqrt(h) per row of A (A = B)
     uint16_t *C;       // GRAM: float16 [N][N] output
     double *part;      // per-workgroup partials, pairs of doubles (not GRAM)
-    int qa, qg, qper;  // QUAD: bands per panel, gangs, workgroup slots per gang
-    int64_t qcols;     // QUAD: panel columns in all
+    int qa, qe;        // QUAD: bands per panel, E tiles per E group
+    int qg, qper;      // QUAD: gangs, workgroup slots per gang
+    int64_t qcpg;      // QUAD: panel columns per E group
+    int64_t qcols;     // QUAD: panel columns in all (E groups x qcpg)
     int pbase;
 };
 
@@ -163,19 +165,22 @@ struct GeArgs {
 //     inside a group).  Epilogue: C[n][m] = fp16(f acc[m][n] r[m] r[n]) (the
 //     transposed position, so C holds the upper block triangle), f = 2 off
 //     the diagonal tiles, 1 on them, and C[m][m] = 0.
-//   QUAD (A = the C of GRAM, M = K; B = E [N][K]): persistent workgroups in
-//     qg gangs of qper slots; slot sl of a gang is band offset qb = sl / nt
-//     and E tile ti = sl % nt (slots past qa nt idle).  The K-block pairs
-//     (tk, J >= tk) are cut into panels of qa bands; panel i has the columns
-//     J = qa i .. mt - 1, and gang x walks the x-th of qg equal runs of the
-//     qcols panel columns in order, each member doing band qa i + qb at the
-//     columns where J >= that band.  The members of a gang thus read the same
-//     qa C blocks and nt E blocks of a column at the same time (a gang is one
-//     XCD's worth of workgroups when qa > 1; qa = 1 gives gangs of nt).
-//     acc[m][e] = (E C)[e][m] for the C rows m of the band; when the panel
-//     changes or the run ends: partial += sum acc[m][e] E[e][m] 4^erow[e],
-//     and acc restarts at zero.  Summed over all workgroups this is
-//     E C E^T's trace with C's upper block triangle standing for both halves.
+//   QUAD (A = the C of GRAM, M = K; B = E [N][K], the rows of one or more
+//     quantisations): persistent workgroups in qg gangs of qper slots; slot
+//     sl of a gang is band offset qb = sl / qe and E tile offset qu = sl % qe
+//     (slots past qa qe idle).  The work is cut into E groups of qe E tiles
+//     and, within each, panels of qa bands of C; panel i has the columns
+//     (K blocks) J = qa i .. mt - 1.  Gang x walks the x-th of qg equal runs
+//     of all (E group, panel, column) in order, each member doing band
+//     qa i + qb of E tile g qe + qu at the columns where J >= band, so the
+//     members read the same qa C blocks and qe E blocks of a column at the
+//     same time (a gang is one XCD's worth of workgroups).  acc[m][e] =
+//     (E C)[e][m] for the C rows m of the band; when the tile (band, E tile)
+//     changes or the run ends, sum acc[m][e] E[e][m] 4^erow[e] over the tile
+//     goes to part[(E tile mt + band) qg + gang] (zeroed beforehand) and acc
+//     restarts at zero.  Summed over an E row range, the slots give that
+//     range's E C E^T trace with C's upper block triangle standing for both
+//     halves.  Returns without the partial pair below.
 // Consecutive workgroup indices go to different XCDs; the index is remapped
 // so that each XCD runs a contiguous run of item numbers.  Workgroup w writes
 // its partial to part[2 (pbase + w) .. + 1].
@@ -202,7 +207,7 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_err_kernel(const GeArgs ga)
     int64_t m0, n0, kb = 0, ke = K;
     float fold = 1.0f;
     int64_t qc0 = 0, qc1 = 0;  // QUAD: this workgroup's panel columns
-    int qb = 0;                // QUAD: band offset within a panel
+    int qb = 0, qu = 0, qx = 0;  // QUAD: band offset, E tile offset, gang
     if (MODE == GE_GRAM) {
         int g0 = 0, base = 0, gm = 0;
         for (;;) {
@@ -230,15 +235,17 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_err_kernel(const GeArgs ga)
         n0 = (int64_t)tn * GE_TN;
         fold = tm != tn ? 2.0f : 1.0f;
     } else if (MODE == GE_QUAD) {
-        // gang x = lin / qper, slot sl: band offset qb = sl / nt, E tile
-        // ti = sl % nt (slots past qa nt idle); the gang's run of panel
-        // columns is [qc0, qc1)
-        const int x = lin / ga.qper, sl = lin % ga.qper, ti = sl % ga.nt;
-        qb = sl / ga.nt;
-        qc0 = ga.qcols * x / ga.qg;
-        qc1 = sl < ga.qa * ga.nt ? ga.qcols * (x + 1) / ga.qg : qc0;
+        // gang qx = lin / qper, slot sl: band offset qb = sl / qe, E tile
+        // offset qu = sl % qe (slots past qa qe idle); the gang's run of
+        // panel columns is [qc0, qc1)
+        const int sl = lin % ga.qper;
+        qx = lin / ga.qper;
+        qb = sl / ga.qe;
+        qu = sl % ga.qe;
+        qc0 = ga.qcols * qx / ga.qg;
+        qc1 = sl < ga.qa * ga.qe ? ga.qcols * (qx + 1) / ga.qg : qc0;
         m0 = 0;
-        n0 = (int64_t)ti * GE_TN;
+        n0 = 0;
     } else {
         const int group = lin / (GE_GROUP_M * ga.nt);
         const int first_m = group * GE_GROUP_M;
@@ -342,40 +349,48 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_err_kernel(const GeArgs ga)
     double sd = 0.0, sy = 0.0;
     if (MODE == GE_QUAD) {
         // Persistent walk over this member's columns of [qc0, qc1): the
-        // copies run S - 1 k-steps ahead across column and panel boundaries;
-        // when the panel changes (or the run ends) the accumulators of tile
-        // (band, ti) go through the epilogue and restart at zero.  K block J
-        // has `full` k-steps, the last one (J = mt - 1) `last`.
+        // copies run S - 1 k-steps ahead across column, panel and E group
+        // boundaries; when the tile (band, E tile) changes or the run ends,
+        // the accumulators go through the epilogue, the workgroup's sum goes
+        // to part[(E tile * mt + band) * qg + gang], and acc restarts at zero.
+        // K block J has `full` k-steps, the last one (J = mt - 1) `last`.
         const int full = GE_TN / TK;
         const int last = (int)((K - (int64_t)(ga.mt - 1) * GE_TN + TK - 1) / TK);
-        const int mt = ga.mt, qa = ga.qa;
-        // cursor (c, panel i, K block J) on this member's valid columns:
-        // band tk = qa i + qb exists and J >= tk
-#define GE_QVALID(i, J) (qa * (i) + qb < mt && (J) >= qa * (i) + qb)
-#define GE_QNEXT(c, i, J)                                                                              \
+        const int mt = ga.mt, qa = ga.qa, qe = ga.qe, nte = ga.nt;
+        // cursor (c, E group g, panel i, K block J) on this member's valid
+        // columns: band qa i + qb exists, J >= band, E tile g qe + qu exists
+#define GE_QBAND(i) (qa * (i) + qb)
+#define GE_QTILE(g) ((g) * qe + qu)
+#define GE_QVALID(g, i, J) (GE_QBAND(i) < mt && (J) >= GE_QBAND(i) && GE_QTILE(g) < nte)
+#define GE_QNEXT(c, g, i, J)                                                                           \
     do {                                                                                               \
         ++(c);                                                                                         \
         if (++(J) == mt) {                                                                             \
             ++(i);                                                                                     \
             (J) = qa * (i);                                                                            \
+            if ((J) >= mt) {                                                                           \
+                (i) = 0;                                                                               \
+                (J) = 0;                                                                               \
+                ++(g);                                                                                 \
+            }                                                                                          \
         }                                                                                              \
-    } while ((c) < qc1 && !GE_QVALID(i, J))
+    } while ((c) < qc1 && !GE_QVALID(g, i, J))
         int64_t cc = qc0;
-        int ci = 0, cJ = 0;
+        int cg = (int)(qc0 / ga.qcpg), ci = 0, cJ = 0;
         {
-            int64_t r = qc0;
+            int64_t r = qc0 % ga.qcpg;
             while (ci * qa < mt && r >= mt - qa * ci) {
                 r -= mt - qa * ci;
                 ++ci;
             }
             cJ = qa * ci + (int)r;
-            if (cc < qc1 && !GE_QVALID(ci, cJ)) GE_QNEXT(cc, ci, cJ);
+            if (cc < qc1 && !GE_QVALID(cg, ci, cJ)) GE_QNEXT(cc, cg, ci, cJ);
         }
         int64_t ic = cc;
-        int ii = ci, iJ = cJ, ikk = 0, ckk = 0, atk = -1;
+        int ig = cg, ii = ci, iJ = cJ, ikk = 0, ckk = 0, atk = -1, btl = -1;
 #define GE_QISSUE(buf)                                                                                 \
     do {                                                                                               \
-        const int itk_ = qa * ii + qb;                                                                 \
+        const int itk_ = GE_QBAND(ii), itl_ = GE_QTILE(ig);                                            \
         if (itk_ != atk) {                                                                             \
             atk = itk_;                                                                                \
             _Pragma("unroll") for (int i = 0; i < C::DA; ++i)                                          \
@@ -384,10 +399,18 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_err_kernel(const GeArgs ga)
                 aoff[i] = min((int64_t)itk_ * GE_TM + r_, M - 1) * K + acs[i];                         \
             }                                                                                          \
         }                                                                                              \
+        if (itl_ != btl) {                                                                             \
+            btl = itl_;                                                                                \
+            _Pragma("unroll") for (int i = 0; i < C::DB; ++i)                                          \
+            {                                                                                          \
+                const int r_ = (C::NW * i + wv) * C::RPI + lrow;                                       \
+                boff[i] = min((int64_t)itl_ * GE_TN + r_, N - 1) * K + bcs[i];                         \
+            }                                                                                          \
+        }                                                                                              \
         GE_ISSUE((int64_t)iJ * GE_TN + (int64_t)ikk * TK, buf);                                        \
         if (++ikk == (iJ < mt - 1 ? full : last)) {                                                    \
             ikk = 0;                                                                                   \
-            GE_QNEXT(ic, ii, iJ);                                                                      \
+            GE_QNEXT(ic, ig, ii, iJ);                                                                  \
         }                                                                                              \
     } while (0)
         int inflight = 0, st = 0;
@@ -409,16 +432,17 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_err_kernel(const GeArgs ga)
             ++st;
             if (++ckk == (cJ < mt - 1 ? full : last)) {
                 ckk = 0;
-                const int ctk = qa * ci + qb;
-                GE_QNEXT(cc, ci, cJ);
-                if (cc >= qc1 || qa * ci + qb != ctk) {
-                    // epilogue of tile (ctk, ti): acc[i][j][4 g + u] = (E C)[e][m + u]
+                const int ctk = GE_QBAND(ci), ctl = GE_QTILE(cg);
+                GE_QNEXT(cc, cg, ci, cJ);
+                if (cc >= qc1 || GE_QBAND(ci) != ctk || GE_QTILE(cg) != ctl) {
+                    // epilogue of tile (ctk, ctl): acc[i][j][4 g + u] = (E C)[e][m + u]
                     // for the C rows m = mb0 + 32 i + 8 g and the E row
                     // e = nb0 + 32 j; times E[e][m .. m + 3] (one 8-byte load;
                     // the 16 loads of a row are in flight together), scaled by
                     // 4^erow[e]
                     const int64_t mb0 = (int64_t)ctk * GE_TM + wm * 128 + 4 * (lane >> 5);
-                    const int64_t nb0 = n0 + wn * 32 * NJ + (lane & 31);
+                    const int64_t nb0 = (int64_t)ctl * GE_TN + wn * 32 * NJ + (lane & 31);
+                    double sdl = 0.0;
 #pragma unroll
                     for (int j = 0; j < NJ; ++j) {
                         const int64_t e = nb0 + j * 32;
@@ -445,7 +469,17 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_err_kernel(const GeArgs ga)
                                 }
                                 t = mb0 + i * 32 + 8 * g < M ? t + q : t;
                             }
-                        if (e < N) sd += ldexp(t, 2 * ga.erow[ec]);
+                        if (e < N) sdl += ldexp(t, 2 * ga.erow[ec]);
+                    }
+#pragma unroll
+                    for (int o = 32; o >= 1; o >>= 1) sdl += __shfl_xor(sdl, o, 64);
+                    if (lane == 0) red[0][wv] = sdl;
+                    __syncthreads();
+                    if (tid == 0) {
+                        double a = 0.0;
+#pragma unroll
+                        for (int w = 0; w < C::NW; ++w) a += red[0][w];
+                        ga.part[((int64_t)ctl * mt + ctk) * ga.qg + qx] = a;
                     }
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
@@ -459,6 +493,9 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_err_kernel(const GeArgs ga)
 #undef GE_QISSUE
 #undef GE_QNEXT
 #undef GE_QVALID
+#undef GE_QTILE
+#undef GE_QBAND
+        return;
     } else {
         // Pipeline: the copies of stage ks + S - 1 are issued right after the
         // barrier that opens stage ks (that barrier also certifies that every
@@ -1026,7 +1063,8 @@ __device__ __forceinline__ void gram_diff(const uint8_t *__restrict__ codes, con
 
 // One workgroup per row n: e = d sqrt(h) as float16 under the row exponent
 // erow[n] (largest |e| scaled into [2^14, 2^15); 0 for a zero row), and
-// dsum[n] = sum_j d_j^2 h_j in float64.  RC > 0: the row's e values stay in
+// dsum[n] = sum_j d_j^2 h_j in float64; rows n >= nvalid (the padding of E
+// to whole 256-row tiles) are written as zeros.  RC > 0: the row's e values stay in
 // registers (RC chunks of 8 per thread, K <= 2048 RC) between the row maximum
 // and the float16 stores; RC = 0: a second pass recomputes them.
 template <int EK, int SK, typename WT, bool REF, int RC>
@@ -1035,11 +1073,20 @@ __global__ __launch_bounds__(256) void gram_operand_kernel(const uint8_t *__rest
                                                            const WT *__restrict__ W, int64_t K,
                                                            const float *__restrict__ sq, const float *__restrict__ h,
                                                            uint16_t *__restrict__ E, int *__restrict__ erow,
-                                                           double *__restrict__ dsum)
+                                                           double *__restrict__ dsum, int64_t nvalid)
 {
     __shared__ double sh[4];
     __shared__ int shm[4];
     const int64_t n = blockIdx.x;
+    if (n >= nvalid) {  // padding row of E: zeros
+        for (int64_t c = threadIdx.x; c < K / 8; c += 256)
+            *reinterpret_cast<uint4 *>(E + n * K + c * 8) = make_uint4(0u, 0u, 0u, 0u);
+        if (threadIdx.x == 0) {
+            erow[n] = 0;
+            dsum[n] = 0.0;
+        }
+        return;
+    }
     const int64_t nch = K / 8;
     int mx = 0;  // largest |e| as float bits (monotone for non-negative floats)
     double ds = 0.0;
@@ -1113,32 +1160,43 @@ __global__ __launch_bounds__(256) void gram_operand_kernel(const uint8_t *__rest
     }
 }
 
-// total = sum part[2 i] + sum dsum[n] in a fixed order; ysq == NULL: *ysq_out
-// = total.  Otherwise *out = sqrt(total) / sqrt(*ysq), sums = {total, *ysq}.
-__global__ __launch_bounds__(256) void gram_final(const double *__restrict__ part, int64_t np,
-                                                  const double *__restrict__ dsum, int64_t nr,
+// One workgroup per quantisation q: total = the slots part[(t mt + band) qg
+// + x] of its E tiles t = q tpq .. q tpq + tpq - 1 (every band and gang) plus
+// dsum of its rows q rpq .. q rpq + nvalid - 1, in a fixed order.  ysq ==
+// NULL: ysq_out[q] = total.  Otherwise out[q] = sqrt(total) / sqrt(*ysq) and
+// sums[2 q .. 2 q + 1] = {total, *ysq}.
+__global__ __launch_bounds__(256) void gram_final(const double *__restrict__ part, int tpq, int mt, int qg,
+                                                  const double *__restrict__ dsum, int64_t rpq, int64_t nvalid,
                                                   const double *__restrict__ ysq, double *__restrict__ ysq_out,
                                                   double *__restrict__ out, double *__restrict__ sums)
 {
     __shared__ double sh[4];
+    const int q = blockIdx.x;
+    const int64_t ns = (int64_t)tpq * mt * qg;
+    const double *ps = part + (int64_t)q * ns;
     double a = 0.0, b = 0.0;
-    for (int64_t i = threadIdx.x; i < np; i += 256) a += part[2 * i];
-    for (int64_t i = threadIdx.x; i < nr; i += 256) b += dsum[i];
+    for (int64_t i = threadIdx.x; i < ns; i += 256) a += ps[i];
+    for (int64_t i = threadIdx.x; i < nvalid; i += 256) b += dsum[q * rpq + i];
     a = block_sum_256(a, sh);
     b = block_sum_256(b, sh);
     if (threadIdx.x == 0) {
         const double t = a + b;
         if (ysq == nullptr) {
-            *ysq_out = t;
+            ysq_out[q] = t;
         } else {
             const double y = *ysq;
-            *out = sqrt(t) / sqrt(y);
+            out[q] = sqrt(t) / sqrt(y);
             if (sums) {
-                sums[0] = t;
-                sums[1] = y;
+                sums[2 * q] = t;
+                sums[2 * q + 1] = y;
             }
         }
     }
+}
+
+__global__ __launch_bounds__(256) void gram_zero_f64(double *__restrict__ p, int64_t n)
+{
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.0;
 }
 
 GramLayout output_gram_layout(int64_t K)
@@ -1158,49 +1216,60 @@ size_t output_gram_ws(int64_t M, int64_t K)
     return (size_t)std::max(al256(K * M8 * 2), (int64_t)hdiag_ws(M, K));
 }
 
-// Schedule of the C E^T walk (the QUAD mode's gangs).  With nt E tiles and
-// P = CUs / 8 workgroups per XCD: when qa = P / nt bands per panel (at most 4)
-// fill at least 90% of an XCD, 8 gangs of P slots (one per XCD, qa nt busy);
-// otherwise gangs of nt (qa = 1), CUs / nt of them.  HD_GRAM_GROUPS = g
-// forces the second form with g gangs.
+// Schedule of the C E^T walk (the QUAD mode's gangs) over nt E tiles: with
+// P = CUs / 8 workgroups per XCD, the E tiles per group qe (and qa = min(4,
+// P / qe) bands per panel) that keep the largest share of the XCD busy on
+// real tiles, 8 gangs of P slots, when that share is at least 90%;
+// otherwise gangs of all nt tiles with one band per panel, CUs / nt of them.
+// HD_GRAM_GROUPS = g forces the second form with g gangs.
 struct GramPlan {
-    int qa, qg, qper;
-    int64_t qcols, wgs;
+    int qa, qe, qg, qper;
+    int64_t qcpg, qcols, wgs;
 };
-static GramPlan gram_plan(int64_t N, int64_t K)
+static GramPlan gram_plan(int64_t nt, int64_t K)
 {
-    const int64_t nt = (N + GE_TN - 1) / GE_TN, mt = (K + GE_TM - 1) / GE_TM;
-    const int64_t per = device_cus() / 8;
-    const char *e = getenv("HD_GRAM_GROUPS");
-    const int64_t forced = e ? atoll(e) : 0;
+    const int64_t mt = (K + GE_TM - 1) / GE_TM, cus = device_cus(), per = cus / 8;
+    const char *env = getenv("HD_GRAM_GROUPS");
+    const int64_t forced = env ? std::min<int64_t>(atoll(env), cus) : 0;
     GramPlan g;
-    const int64_t qa = nt <= per ? per / nt : 0;
-    if (forced <= 0 && qa >= 1 && qa <= 4 && 10 * qa * nt >= 9 * per) {
-        g.qa = (int)qa;
+    double best = 0.0;
+    int64_t bqe = 0, bqa = 0;
+    for (int64_t qe = 1; qe <= per; ++qe) {
+        const int64_t qa = std::min<int64_t>(4, per / qe), ngr = (nt + qe - 1) / qe;
+        const double eff = (double)nt / (double)(ngr * qe) * (double)(qa * qe) / (double)per;
+        if (eff > best + 1e-9) {
+            best = eff;
+            bqe = qe;
+            bqa = qa;
+        }
+    }
+    if (forced <= 0 && best >= 0.9) {
+        g.qa = (int)bqa;
+        g.qe = (int)bqe;
         g.qg = 8;
         g.qper = (int)per;
     } else {
         g.qa = 1;
-        g.qg = (int)std::max<int64_t>(1, forced > 0 ? forced : device_cus() / std::max<int64_t>(nt, 1));
+        g.qe = (int)nt;
+        g.qg = (int)std::max<int64_t>(1, forced > 0 ? forced : cus / std::max<int64_t>(nt, 1));
         g.qper = (int)nt;
     }
-    g.qcols = 0;
-    for (int64_t i = 0; i * g.qa < mt; ++i) g.qcols += mt - g.qa * i;
+    g.qcpg = 0;
+    for (int64_t i = 0; i * g.qa < mt; ++i) g.qcpg += mt - g.qa * i;
+    g.qcols = g.qcpg * ((nt + g.qe - 1) / g.qe);
     g.qg = (int)std::min<int64_t>(g.qg, g.qcols);
     g.wgs = (int64_t)g.qg * g.qper;
     return g;
 }
 
-// Upper bound of the partials: one per workgroup.
-static int64_t gram_parts_max(int64_t N, int64_t K)
-{
-    const int64_t nt = (N + GE_TN - 1) / GE_TN, mt = (K + GE_TM - 1) / GE_TM;
-    return std::max<int64_t>(nt * mt * (mt + 1) / 2, device_cus());
-}
+// Rows of E per quantisation (N padded to whole 256-row tiles).
+static int64_t gram_rows(int64_t N) { return (N + GE_TN - 1) / GE_TN * GE_TN; }
 
-size_t output_error_gram_ws(int64_t N, int64_t K)
+size_t output_error_gram_ws(int64_t count, int64_t N, int64_t K)
 {
-    return (size_t)(al256(N * K * 2) + al256(N * 4) + al256(N * 8) + al256(gram_parts_max(N, K) * 16));
+    const int64_t R = count * gram_rows(N), nt = R / GE_TN, mt = (K + GE_TM - 1) / GE_TM;
+    const int64_t slots = nt * mt * std::max<int64_t>(device_cus(), 8);
+    return (size_t)(al256(R * K * 2) + al256(R * 4) + al256(R * 8) + al256(slots * 8));
 }
 
 hipError_t launch_output_gram(const void *X, int64_t M, int64_t K, const float *h, void *gram, void *ws,
@@ -1238,79 +1307,96 @@ hipError_t launch_output_gram(const void *X, int64_t M, int64_t K, const float *
 
 template <int EK, int SK, bool REF>
 static void launch_gram_operand(const uint8_t *codes, const uint8_t *scales, int B, const void *W, int wdt, int64_t N,
-                                int64_t K, const float *sq, const float *h, uint16_t *E, int *erow, double *dsum,
-                                hipStream_t st)
+                                int64_t rows, int64_t K, const float *sq, const float *h, uint16_t *E, int *erow,
+                                double *dsum, hipStream_t st)
 {
     const bool regs = K <= 2048 * 8;
     if (wdt == HD_BF16) {
         if (regs)
-            gram_operand_kernel<EK, SK, uint16_t, REF, 8><<<(unsigned)N, 256, 0, st>>>(
-                codes, scales, B, static_cast<const uint16_t *>(W), K, sq, h, E, erow, dsum);
+            gram_operand_kernel<EK, SK, uint16_t, REF, 8><<<(unsigned)rows, 256, 0, st>>>(
+                codes, scales, B, static_cast<const uint16_t *>(W), K, sq, h, E, erow, dsum, N);
         else
-            gram_operand_kernel<EK, SK, uint16_t, REF, 0><<<(unsigned)N, 256, 0, st>>>(
-                codes, scales, B, static_cast<const uint16_t *>(W), K, sq, h, E, erow, dsum);
+            gram_operand_kernel<EK, SK, uint16_t, REF, 0><<<(unsigned)rows, 256, 0, st>>>(
+                codes, scales, B, static_cast<const uint16_t *>(W), K, sq, h, E, erow, dsum, N);
     } else {
         if (regs)
-            gram_operand_kernel<EK, SK, float, REF, 8><<<(unsigned)N, 256, 0, st>>>(
-                codes, scales, B, static_cast<const float *>(W), K, sq, h, E, erow, dsum);
+            gram_operand_kernel<EK, SK, float, REF, 8><<<(unsigned)rows, 256, 0, st>>>(
+                codes, scales, B, static_cast<const float *>(W), K, sq, h, E, erow, dsum, N);
         else
-            gram_operand_kernel<EK, SK, float, REF, 0><<<(unsigned)N, 256, 0, st>>>(
-                codes, scales, B, static_cast<const float *>(W), K, sq, h, E, erow, dsum);
+            gram_operand_kernel<EK, SK, float, REF, 0><<<(unsigned)rows, 256, 0, st>>>(
+                codes, scales, B, static_cast<const float *>(W), K, sq, h, E, erow, dsum, N);
     }
 }
 
 template <int F>
 static void gram_operand_fmt(const uint8_t *codes, const uint8_t *scales, int B, const void *W, int wdt, int64_t N,
-                             int64_t K, const float *sq, const float *h, uint16_t *E, int *erow, double *dsum,
-                             hipStream_t st)
+                             int64_t rows, int64_t K, const float *sq, const float *h, uint16_t *E, int *erow,
+                             double *dsum, hipStream_t st)
 {
-    launch_gram_operand<elem_kind(F), scale_kind(F), false>(codes, scales, B, W, wdt, N, K, sq, h, E, erow, dsum, st);
+    launch_gram_operand<elem_kind(F), scale_kind(F), false>(codes, scales, B, W, wdt, N, rows, K, sq, h, E, erow,
+                                                            dsum, st);
 }
 
-// fmt < 0: the reference ||X W^T||^2 into *ysq_out.
-hipError_t launch_output_error_gram(int fmt, int B, const uint8_t *codes, const uint8_t *scales, const void *W,
-                                    int wdt, int64_t N, int64_t K, const void *gram, const double *ysq,
-                                    double *ysq_out, double *out, double *sums, void *ws, hipStream_t st)
+// count quantisations (fmt[q], B[q], codes[q], scales[q]) of one W: out[q] =
+// sqrt(||X (Wq_q - W)^T||^2) / sqrt(*ysq); fmt == NULL: the reference
+// ||X W^T||^2 into ysq_out[0] (count 1).
+hipError_t launch_output_error_gram(int count, const int *fmt, const int *B, const uint8_t *const *codes,
+                                    const uint8_t *const *scales, const void *W, int wdt, int64_t N, int64_t K,
+                                    const void *gram, const double *ysq, double *ysq_out, double *out, double *sums,
+                                    void *ws, hipStream_t st)
 {
     const GramLayout L = output_gram_layout(K);
     const char *g = static_cast<const char *>(gram);
     const float *gh = reinterpret_cast<const float *>(g + L.h);
     const float *sq = reinterpret_cast<const float *>(g + L.sq);
     const uint16_t *C = reinterpret_cast<const uint16_t *>(g + L.c);
+    const int64_t rpq = gram_rows(N), R = count * rpq, nt = R / GE_TN, mt = (K + GE_TM - 1) / GE_TM;
     char *w = static_cast<char *>(ws);
     uint16_t *E = reinterpret_cast<uint16_t *>(w);
-    int *erow = reinterpret_cast<int *>(w + al256(N * K * 2));
-    double *dsum = reinterpret_cast<double *>(w + al256(N * K * 2) + al256(N * 4));
-    double *part = reinterpret_cast<double *>(w + al256(N * K * 2) + al256(N * 4) + al256(N * 8));
-    const GramPlan plan = gram_plan(N, K);
-    const int64_t items = N > 0 && K > 0 ? plan.wgs : 0;
-    if (items > 0) {
-        switch (fmt) {
-        case -1: launch_gram_operand<ELEM_INT8, SCALE_INT8, true>(codes, scales, B, W, wdt, N, K, sq, gh, E, erow, dsum, st); break;
-        case HD_INT8_E4M3: gram_operand_fmt<HD_INT8_E4M3>(codes, scales, B, W, wdt, N, K, sq, gh, E, erow, dsum, st); break;
-        case HD_NVFP4: gram_operand_fmt<HD_NVFP4>(codes, scales, B, W, wdt, N, K, sq, gh, E, erow, dsum, st); break;
-        case HD_MXFP4: gram_operand_fmt<HD_MXFP4>(codes, scales, B, W, wdt, N, K, sq, gh, E, erow, dsum, st); break;
-        case HD_MXFP8: gram_operand_fmt<HD_MXFP8>(codes, scales, B, W, wdt, N, K, sq, gh, E, erow, dsum, st); break;
-        case HD_FP8_E4M3S: gram_operand_fmt<HD_FP8_E4M3S>(codes, scales, B, W, wdt, N, K, sq, gh, E, erow, dsum, st); break;
-        case HD_NVFP4_UE4M4: gram_operand_fmt<HD_NVFP4_UE4M4>(codes, scales, B, W, wdt, N, K, sq, gh, E, erow, dsum, st); break;
-        case HD_NVFP4_UE5M3: gram_operand_fmt<HD_NVFP4_UE5M3>(codes, scales, B, W, wdt, N, K, sq, gh, E, erow, dsum, st); break;
-        case HD_NVINT4: gram_operand_fmt<HD_NVINT4>(codes, scales, B, W, wdt, N, K, sq, gh, E, erow, dsum, st); break;
-        case HD_FP4_F16: gram_operand_fmt<HD_FP4_F16>(codes, scales, B, W, wdt, N, K, sq, gh, E, erow, dsum, st); break;
-        case HD_INT4_F16: gram_operand_fmt<HD_INT4_F16>(codes, scales, B, W, wdt, N, K, sq, gh, E, erow, dsum, st); break;
-        default: return hipErrorInvalidValue;
+    int *erow = reinterpret_cast<int *>(w + al256(R * K * 2));
+    double *dsum = reinterpret_cast<double *>(w + al256(R * K * 2) + al256(R * 4));
+    double *part = reinterpret_cast<double *>(w + al256(R * K * 2) + al256(R * 4) + al256(R * 8));
+    const bool work = N > 0 && K > 0;
+    const GramPlan plan = gram_plan(nt, K);
+    if (work) {
+        for (int q = 0; q < count; ++q) {
+            uint16_t *Eq = E + q * rpq * K;
+            int *eq = erow + q * rpq;
+            double *dq = dsum + q * rpq;
+            const uint8_t *cq = codes ? codes[q] : nullptr;
+            const uint8_t *sq8 = scales ? scales[q] : nullptr;
+            switch (fmt ? fmt[q] : -1) {
+            case -1: launch_gram_operand<ELEM_INT8, SCALE_INT8, true>(cq, sq8, 8, W, wdt, N, rpq, K, sq, gh, Eq, eq, dq, st); break;
+            case HD_INT8_E4M3: gram_operand_fmt<HD_INT8_E4M3>(cq, sq8, B[q], W, wdt, N, rpq, K, sq, gh, Eq, eq, dq, st); break;
+            case HD_NVFP4: gram_operand_fmt<HD_NVFP4>(cq, sq8, B[q], W, wdt, N, rpq, K, sq, gh, Eq, eq, dq, st); break;
+            case HD_MXFP4: gram_operand_fmt<HD_MXFP4>(cq, sq8, B[q], W, wdt, N, rpq, K, sq, gh, Eq, eq, dq, st); break;
+            case HD_MXFP8: gram_operand_fmt<HD_MXFP8>(cq, sq8, B[q], W, wdt, N, rpq, K, sq, gh, Eq, eq, dq, st); break;
+            case HD_FP8_E4M3S: gram_operand_fmt<HD_FP8_E4M3S>(cq, sq8, B[q], W, wdt, N, rpq, K, sq, gh, Eq, eq, dq, st); break;
+            case HD_NVFP4_UE4M4: gram_operand_fmt<HD_NVFP4_UE4M4>(cq, sq8, B[q], W, wdt, N, rpq, K, sq, gh, Eq, eq, dq, st); break;
+            case HD_NVFP4_UE5M3: gram_operand_fmt<HD_NVFP4_UE5M3>(cq, sq8, B[q], W, wdt, N, rpq, K, sq, gh, Eq, eq, dq, st); break;
+            case HD_NVINT4: gram_operand_fmt<HD_NVINT4>(cq, sq8, B[q], W, wdt, N, rpq, K, sq, gh, Eq, eq, dq, st); break;
+            case HD_FP4_F16: gram_operand_fmt<HD_FP4_F16>(cq, sq8, B[q], W, wdt, N, rpq, K, sq, gh, Eq, eq, dq, st); break;
+            case HD_INT4_F16: gram_operand_fmt<HD_INT4_F16>(cq, sq8, B[q], W, wdt, N, rpq, K, sq, gh, Eq, eq, dq, st); break;
+            default: return hipErrorInvalidValue;
+            }
         }
-        GeArgs ga = ge_args(C, E, K, N, K);
-        ga.nlin = (int)items;
+        const int64_t slots = nt * mt * plan.qg;
+        gram_zero_f64<<<(unsigned)std::min<int64_t>((slots + 255) / 256, 1024), 256, 0, st>>>(part, slots);
+        GeArgs ga = ge_args(C, E, K, R, K);
+        ga.nlin = (int)plan.wgs;
         ga.qa = plan.qa;
+        ga.qe = plan.qe;
         ga.qg = plan.qg;
         ga.qper = plan.qper;
+        ga.qcpg = plan.qcpg;
         ga.qcols = plan.qcols;
         ga.erow = erow;
         ga.part = part;
-        const hipError_t e = ge_launch<true, GE_QUAD, 8 / HD_GE_WN>(ga, items, st);
+        const hipError_t e = ge_launch<true, GE_QUAD, 8 / HD_GE_WN>(ga, plan.wgs, st);
         if (e != hipSuccess) return e;
     }
-    gram_final<<<1, 256, 0, st>>>(part, items, dsum, items > 0 ? N : 0, fmt < 0 ? nullptr : ysq, ysq_out, out, sums);
+    gram_final<<<(unsigned)count, 256, 0, st>>>(part, work ? (int)(rpq / GE_TN) : 0, (int)mt, plan.qg, dsum, rpq,
+                                                work ? N : 0, fmt ? ysq : nullptr, ysq_out, out, sums);
     return hipGetLastError();
 }
 

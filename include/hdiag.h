@@ -321,6 +321,25 @@ hd_status output_error_gram(hd_format fmt, int32_t B, const uint8_t *codes, cons
                             hd_dtype wt, int64_t N, int64_t K, const void *gram, size_t gram_bytes,
                             const double *ysq, double *out, double *sums, void *ws, size_t ws_bytes, void *stream);
 
+/* output_error_gram for count quantisations of the same W [N, K] in one call:
+ * fmts[q], Bs[q], codes[q], scales[q] (q < count) are HOST arrays holding,
+ * for each quantisation, its format, block size and the device pointers of
+ * its codes and scales (each as for output_error_gram).  out: device
+ * double[count], out[q] = ||X Wq_q^T - X W^T||_F / sqrt(*ysq); sums (optional,
+ * device, 2 count doubles): {||X (Wq_q - W)^T||_F^2, *ysq} for each q.
+ * The results are those of count output_error_gram calls up to the order of
+ * the float64 partial sums; one MFMA walk over the stacked operand of all
+ * count quantisations reads each C block for several of them at once.
+ * workspace: ws_bytes >= output_error_gram_batch_workspace_size(count, N, K)
+ * (count x the single call's operand).  1 <= count <= 4096.  Errors as
+ * output_error_gram, for each q. */
+size_t output_error_gram_batch_workspace_size(int32_t count, int64_t N, int64_t K);
+hd_status output_error_gram_batch(int32_t count, const hd_format *fmts, const int32_t *Bs,
+                                  const uint8_t *const *codes, const uint8_t *const *scales, const void *W,
+                                  hd_dtype wt, int64_t N, int64_t K, const void *gram, size_t gram_bytes,
+                                  const double *ysq, double *out, double *sums, void *ws, size_t ws_bytes,
+                                  void *stream);
+
 /* ------------------------------------------------ per-tensor scaling --- */
 
 /* Two-level scales for the E4M3 block-scale formats (HD_INT8_E4M3, HD_NVFP4,

@@ -235,3 +235,48 @@ def test_output_error_gram_wide_rows():
                                          oracle.dequantize(hd.INT8_E4M3, B, npy(c), sc_np(s), N, K), sums=True)
     assert out.item() == pytest.approx(oe_o, rel=1e-4)
     np.testing.assert_allclose(npy(sums), [d_o, y_o], rtol=1e-4)
+
+
+@pytest.mark.parametrize("N,K", [(300, 512), (2560, 1536), (40, 520)])
+def test_output_error_gram_batch(N, K):
+    """A batch of mixed formats and block sizes (N padded to whole 256-row
+    tiles inside) gives each quantisation's output error as the single call
+    does (up to summation order) and as the oracle does."""
+    M = 600
+    X = acts(M, K, 70 + N)
+    W = weights_for(hd.NVFP4, N, K, 71 + N)
+    Xd, Wd = dev(X), dev(W)
+    h = hd.hdiag(Xd)
+    gram = hd.output_gram(Xd, h=h)
+    ysq = hd.output_reference_gram(Wd, gram)
+    items = []
+    for fmt, B, m in ((hd.INT8_E4M3, 32, hd.SSE_OPT), (hd.NVFP4, 16, hd.H_OPT), (hd.MXFP4, 32, hd.NAIVE),
+                      (hd.INT8_E4M3, 8, hd.H_OPT), (hd.FP4_F16, 16, hd.SSE_OPT)):
+        if K % B:
+            continue
+        c, s, _ = hd.quantize_blocks(m, fmt, B, Wd, h=h)
+        items.append((fmt, B, c, s))
+    out, sums = hd.output_error_gram_batch(items, Wd, gram, ysq, sums=True)
+    torch.cuda.synchronize()
+    for q, (fmt, B, c, s) in enumerate(items):
+        single = hd.output_error_gram(fmt, B, c, s, Wd, gram, ysq).item()
+        # the two schedules cut the K blocks into different runs, each summed
+        # in float32 accumulators before the float64 partials
+        assert out[q].item() == pytest.approx(single, rel=1e-6)
+        oe_o = oracle.output_error(synth.bits(X), synth.bits(W), oracle.dequantize(fmt, B, npy(c), sc_np(s), N, K))
+        assert out[q].item() == pytest.approx(oe_o, rel=1e-4)
+        assert sums[q, 1].item() == ysq.item()
+
+
+def test_output_error_gram_batch_errors():
+    W = torch.zeros((64, 256), dtype=torch.bfloat16, device="cuda")
+    X = torch.zeros((32, 256), dtype=torch.bfloat16, device="cuda")
+    gram = hd.output_gram(X)
+    ysq = hd.output_reference_gram(W, gram)
+    c, s, _ = hd.quantize_blocks(hd.NAIVE, hd.INT8_E4M3, 32, W)
+    with pytest.raises(hd.HdiagError) as e:
+        hd.output_error_gram_batch([(hd.INT8_E4M3, 32, c, s), (hd.INT8_E4M3, 24, c, s)], W, gram, ysq)
+    assert e.value.status == hd.HD_ERR_INVALID_ARG
+    with pytest.raises(hd.HdiagError) as e:
+        hd.output_error_gram_batch([], W, gram, ysq)
+    assert e.value.status == hd.HD_ERR_INVALID_ARG

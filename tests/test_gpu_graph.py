@@ -1,6 +1,6 @@
 """A captured HIP graph of one step of the path (hdiag, output_gram,
 output_reference_gram, quantize_blocks, dequantize, weight_error,
-output_error_gram) replayed several times, with eager work and
+output_error_gram_batch) replayed several times, with eager work and
 synchronisations between the replays: every replay reproduces the eager
 results bit for bit (the library issues no memset or allocation inside the
 step, so nothing in the graph depends on state left by an earlier replay)."""
@@ -29,7 +29,7 @@ def test_step_graph_replays_match_eager():
     ws_h = torch.empty(max(hd.hdiag_workspace_size(M, K), 16), dtype=torch.uint8, device=dev)
     gram = torch.empty(hd.output_gram_size(K), dtype=torch.uint8, device=dev)
     ws_g = torch.empty(hd.output_gram_workspace_size(M, K), dtype=torch.uint8, device=dev)
-    ws_o = torch.empty(hd.output_error_gram_workspace_size(N, K), dtype=torch.uint8, device=dev)
+    ws_o = torch.empty(hd.output_error_gram_batch_workspace_size(3, N, K), dtype=torch.uint8, device=dev)
     ws_w = torch.empty(hd.weight_error_workspace_size(N, K), dtype=torch.uint8, device=dev)
     ysq = torch.empty(1, dtype=torch.float64, device=dev)
     plan = [(hd.NAIVE, 32), (hd.SSE_OPT, 64), (hd.H_OPT, 128)]
@@ -47,8 +47,8 @@ def test_step_graph_replays_match_eager():
             hd.quantize_blocks(m, hd.INT8_E4M3, B, W, h=h, codes=codes[i], scales=scales[i])
             hd.dequantize(hd.INT8_E4M3, B, codes[i], scales[i], N, K, out=Wq)
             hd.weight_error(W, Wq, workspace=ws_w, out=werr[i:i + 1])
-            hd.output_error_gram(hd.INT8_E4M3, B, codes[i], scales[i], W, gram, ysq, workspace=ws_o,
-                                 out=oerr[i:i + 1])
+        hd.output_error_gram_batch([(hd.INT8_E4M3, B, codes[i], scales[i]) for i, (_, B) in enumerate(plan)], W,
+                                   gram, ysq, workspace=ws_o, out=oerr)
 
     step()
     torch.cuda.synchronize()
