@@ -990,34 +990,12 @@ __global__ __launch_bounds__(256) void gram_zero_kernel(uint16_t *__restrict__ p
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0;
 }
 
-// d = Wq - W for the 8 weights k .. k + 7 of row n (REF: d = W), with Wq the
-// float32 value dequantize() gives (fl32(s val(q)); invalid codes give 0).
-template <int EK, int SK, typename WT, bool REF>
-__device__ __forceinline__ void gram_diff(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales,
-                                          int B, const WT *__restrict__ W, int64_t n, int64_t K, int64_t k,
-                                          float d[8])
+// The float32 values dequantize() gives (fl32(s val(q)); invalid codes give
+// 0) for the 8 weights at flat index e0 (a multiple of 8) of the codes.
+template <int EK, int SK>
+__device__ __forceinline__ void gram_wq(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales, int B,
+                                        int64_t e0, float q[8])
 {
-    const int64_t e0 = n * K + k;
-    float w[8];
-    if (sizeof(WT) == 2) {
-        const uint4 v = *reinterpret_cast<const uint4 *>(W + e0);
-        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            w[2 * j] = bf16_to_f32(u[j] & 0xFFFFu);
-            w[2 * j + 1] = bf16_to_f32(u[j] >> 16);
-        }
-    } else {
-        const float4 a = *reinterpret_cast<const float4 *>(W + e0);
-        const float4 b = *reinterpret_cast<const float4 *>(W + e0 + 4);
-        w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
-        w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
-    }
-    if (REF) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) d[j] = w[j];
-        return;
-    }
     const int64_t bi = e0 / B;
     const int sc = scale_bytes(SK) == 2 ? (int)reinterpret_cast<const uint16_t *>(scales)[bi] : (int)scales[bi];
     const float s = scale_code_valid(SK, sc) ? scale_value(SK, sc) : 0.0f;
@@ -1036,13 +1014,12 @@ __device__ __forceinline__ void gram_diff(const uint8_t *__restrict__ codes, con
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        float q;
         if (EK == ELEM_INT8) {
             const int i = (int)(int8_t)(uint8_t)c[j];
-            q = i == -128 ? 0.0f : s * (float)i;
+            q[j] = i == -128 ? 0.0f : s * (float)i;
         } else if (EK == ELEM_INT4) {
             const int i = (int)((c[j] ^ 8u) & 15u) - 8;
-            q = i == -8 ? 0.0f : s * (float)i;
+            q[j] = i == -8 ? 0.0f : s * (float)i;
         } else {
             bool neg, ok = true;
             uint32_t idx;
@@ -1055,10 +1032,49 @@ __device__ __forceinline__ void gram_diff(const uint8_t *__restrict__ codes, con
                 ok = idx != 0x7Fu;
             }
             const float mag = ok ? s * elem_value<EK>(idx) : 0.0f;
-            q = neg ? -mag : mag;
+            q[j] = neg ? -mag : mag;
         }
-        d[j] = q - w[j];
     }
+}
+
+// The 8 weights at flat index e0 of W as float32.
+template <typename WT>
+__device__ __forceinline__ void gram_w(const WT *__restrict__ W, int64_t e0, float w[8])
+{
+    if (sizeof(WT) == 2) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(W + e0);
+        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            w[2 * j] = bf16_to_f32(u[j] & 0xFFFFu);
+            w[2 * j + 1] = bf16_to_f32(u[j] >> 16);
+        }
+    } else {
+        const float4 a = *reinterpret_cast<const float4 *>(W + e0);
+        const float4 b = *reinterpret_cast<const float4 *>(W + e0 + 4);
+        w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+        w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+    }
+}
+
+// d = Wq - W for the 8 weights k .. k + 7 of row n (REF: d = W).
+template <int EK, int SK, typename WT, bool REF>
+__device__ __forceinline__ void gram_diff(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales,
+                                          int B, const WT *__restrict__ W, int64_t n, int64_t K, int64_t k,
+                                          float d[8])
+{
+    const int64_t e0 = n * K + k;
+    float w[8];
+    gram_w<WT>(W, e0, w);
+    if (REF) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) d[j] = w[j];
+        return;
+    }
+    float q[8];
+    gram_wq<EK, SK>(codes, scales, B, e0, q);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) d[j] = q[j] - w[j];
 }
 
 // One workgroup per row n: e = d sqrt(h) as float16 under the row exponent
@@ -1068,16 +1084,14 @@ __device__ __forceinline__ void gram_diff(const uint8_t *__restrict__ codes, con
 // registers (RC chunks of 8 per thread, K <= 2048 RC) between the row maximum
 // and the float16 stores; RC = 0: a second pass recomputes them.
 template <int EK, int SK, typename WT, bool REF, int RC>
-__global__ __launch_bounds__(256) void gram_operand_kernel(const uint8_t *__restrict__ codes,
-                                                           const uint8_t *__restrict__ scales, int B,
-                                                           const WT *__restrict__ W, int64_t K,
-                                                           const float *__restrict__ sq, const float *__restrict__ h,
-                                                           uint16_t *__restrict__ E, int *__restrict__ erow,
-                                                           double *__restrict__ dsum, int64_t nvalid)
+__device__ __forceinline__ void gram_operand_row(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales,
+                                                 int B, const WT *__restrict__ W, int64_t K,
+                                                 const float *__restrict__ sq, const float *__restrict__ h,
+                                                 uint16_t *__restrict__ E, int *__restrict__ erow,
+                                                 double *__restrict__ dsum, int64_t nvalid, int64_t n)
 {
     __shared__ double sh[4];
     __shared__ int shm[4];
-    const int64_t n = blockIdx.x;
     if (n >= nvalid) {  // padding row of E: zeros
         for (int64_t c = threadIdx.x; c < K / 8; c += 256)
             *reinterpret_cast<uint4 *>(E + n * K + c * 8) = make_uint4(0u, 0u, 0u, 0u);
@@ -1158,6 +1172,41 @@ __global__ __launch_bounds__(256) void gram_operand_kernel(const uint8_t *__rest
             store(c, e);
         }
     }
+}
+
+template <int EK, int SK, typename WT, bool REF, int RC>
+__global__ __launch_bounds__(256) void gram_operand_kernel(const uint8_t *__restrict__ codes,
+                                                           const uint8_t *__restrict__ scales, int B,
+                                                           const WT *__restrict__ W, int64_t K,
+                                                           const float *__restrict__ sq, const float *__restrict__ h,
+                                                           uint16_t *__restrict__ E, int *__restrict__ erow,
+                                                           double *__restrict__ dsum, int64_t nvalid)
+{
+    gram_operand_row<EK, SK, WT, REF, RC>(codes, scales, B, W, K, sq, h, E, erow, dsum, nvalid, blockIdx.x);
+}
+
+// Up to GRAM_OPS quantisations of one format in one launch: workgroup
+// (n, q) = (blockIdx / n_q, blockIdx % n_q) does row n of quantisation q, so
+// the workgroups of one row of W run next to each other and share it in L2;
+// quantisation q's E, erow and dsum start at row q rpq.
+constexpr int GRAM_OPS = 16;
+struct GramOps {
+    const uint8_t *codes[GRAM_OPS];
+    const uint8_t *scales[GRAM_OPS];
+    int B[GRAM_OPS];
+    int n;
+};
+template <int EK, int SK, typename WT>
+__global__ __launch_bounds__(256) void gram_operand_multi_kernel(const GramOps ob, const WT *__restrict__ W, int64_t K,
+                                                                 const float *__restrict__ sq,
+                                                                 const float *__restrict__ h, uint16_t *__restrict__ E,
+                                                                 int *__restrict__ erow, double *__restrict__ dsum,
+                                                                 int64_t nvalid, int64_t rpq)
+{
+    const int q = (int)(blockIdx.x % (unsigned)ob.n);
+    const int64_t n = blockIdx.x / (unsigned)ob.n, o = q * rpq;
+    gram_operand_row<EK, SK, WT, false, 8>(ob.codes[q], ob.scales[q], ob.B[q], W, K, sq, h, E + o * K, erow + o,
+                                           dsum + o, nvalid, n);
 }
 
 // One workgroup per quantisation q: total = the slots part[(t mt + band) qg
@@ -1337,6 +1386,19 @@ static void gram_operand_fmt(const uint8_t *codes, const uint8_t *scales, int B,
                                                             dsum, st);
 }
 
+template <int F>
+static void gram_operand_multi_fmt(const GramOps &ob, const void *W, int wdt, int64_t N, int64_t rows, int64_t K,
+                                   const float *sq, const float *h, uint16_t *E, int *erow, double *dsum,
+                                   hipStream_t st)
+{
+    if (wdt == HD_BF16)
+        gram_operand_multi_kernel<elem_kind(F), scale_kind(F), uint16_t><<<(unsigned)(rows * ob.n), 256, 0, st>>>(
+            ob, static_cast<const uint16_t *>(W), K, sq, h, E, erow, dsum, N, rows);
+    else
+        gram_operand_multi_kernel<elem_kind(F), scale_kind(F), float><<<(unsigned)(rows * ob.n), 256, 0, st>>>(
+            ob, static_cast<const float *>(W), K, sq, h, E, erow, dsum, N, rows);
+}
+
 // count quantisations (fmt[q], B[q], codes[q], scales[q]) of one W: out[q] =
 // sqrt(||X (Wq_q - W)^T||^2) / sqrt(*ysq); fmt == NULL: the reference
 // ||X W^T||^2 into ysq_out[0] (count 1).
@@ -1358,8 +1420,40 @@ hipError_t launch_output_error_gram(int count, const int *fmt, const int *B, con
     double *part = reinterpret_cast<double *>(w + al256(R * K * 2) + al256(R * 4) + al256(R * 8));
     const bool work = N > 0 && K > 0;
     const GramPlan plan = gram_plan(nt, K);
+    bool fused = false;
+    if (work && fmt != nullptr && K <= 2048 * 8 && rpq * GRAM_OPS < ((int64_t)1 << 31)) {
+        fused = true;
+        for (int q = 1; q < count; ++q) fused = fused && fmt[q] == fmt[0];
+    }
+    if (work && fused) {
+        for (int q0 = 0; q0 < count; q0 += GRAM_OPS) {
+            GramOps ob = {};
+            ob.n = std::min(GRAM_OPS, count - q0);
+            for (int k = 0; k < ob.n; ++k) {
+                ob.codes[k] = codes[q0 + k];
+                ob.scales[k] = scales[q0 + k];
+                ob.B[k] = B[q0 + k];
+            }
+            uint16_t *Eq = E + q0 * rpq * K;
+            int *eq = erow + q0 * rpq;
+            double *dq = dsum + q0 * rpq;
+            switch (fmt[0]) {
+            case HD_INT8_E4M3: gram_operand_multi_fmt<HD_INT8_E4M3>(ob, W, wdt, N, rpq, K, sq, gh, Eq, eq, dq, st); break;
+            case HD_NVFP4: gram_operand_multi_fmt<HD_NVFP4>(ob, W, wdt, N, rpq, K, sq, gh, Eq, eq, dq, st); break;
+            case HD_MXFP4: gram_operand_multi_fmt<HD_MXFP4>(ob, W, wdt, N, rpq, K, sq, gh, Eq, eq, dq, st); break;
+            case HD_MXFP8: gram_operand_multi_fmt<HD_MXFP8>(ob, W, wdt, N, rpq, K, sq, gh, Eq, eq, dq, st); break;
+            case HD_FP8_E4M3S: gram_operand_multi_fmt<HD_FP8_E4M3S>(ob, W, wdt, N, rpq, K, sq, gh, Eq, eq, dq, st); break;
+            case HD_NVFP4_UE4M4: gram_operand_multi_fmt<HD_NVFP4_UE4M4>(ob, W, wdt, N, rpq, K, sq, gh, Eq, eq, dq, st); break;
+            case HD_NVFP4_UE5M3: gram_operand_multi_fmt<HD_NVFP4_UE5M3>(ob, W, wdt, N, rpq, K, sq, gh, Eq, eq, dq, st); break;
+            case HD_NVINT4: gram_operand_multi_fmt<HD_NVINT4>(ob, W, wdt, N, rpq, K, sq, gh, Eq, eq, dq, st); break;
+            case HD_FP4_F16: gram_operand_multi_fmt<HD_FP4_F16>(ob, W, wdt, N, rpq, K, sq, gh, Eq, eq, dq, st); break;
+            case HD_INT4_F16: gram_operand_multi_fmt<HD_INT4_F16>(ob, W, wdt, N, rpq, K, sq, gh, Eq, eq, dq, st); break;
+            default: return hipErrorInvalidValue;
+            }
+        }
+    }
     if (work) {
-        for (int q = 0; q < count; ++q) {
+        for (int q = 0; q < count && !fused; ++q) {
             uint16_t *Eq = E + q * rpq * K;
             int *eq = erow + q * rpq;
             double *dq = dsum + q * rpq;

@@ -280,3 +280,23 @@ def test_output_error_gram_batch_errors():
     with pytest.raises(hd.HdiagError) as e:
         hd.output_error_gram_batch([], W, gram, ysq)
     assert e.value.status == hd.HD_ERR_INVALID_ARG
+
+
+def test_output_error_gram_batch_same_format_over_16():
+    """18 quantisations of one format: the fused operand pass runs as two
+    launches (16 + 2); each result equals its single call."""
+    M, N, K = 400, 300, 768
+    X, W = dev(acts(M, K, 81)), dev(weights_for(hd.NVFP4, N, K, 82))
+    h = hd.hdiag(X)
+    gram = hd.output_gram(X, h=h)
+    ysq = hd.output_reference_gram(W, gram)
+    items = []
+    for k in range(18):
+        B = (16, 32, 64)[k % 3]
+        m = (hd.NAIVE, hd.SSE_OPT, hd.H_OPT)[(k // 3) % 3]
+        c, s, _ = hd.quantize_blocks(m, hd.NVFP4, B, W, h=h)
+        items.append((hd.NVFP4, B, c, s))
+    out = hd.output_error_gram_batch(items, W, gram, ysq)
+    torch.cuda.synchronize()
+    for q, (fmt, B, c, s) in enumerate(items):
+        assert out[q].item() == pytest.approx(hd.output_error_gram(fmt, B, c, s, W, gram, ysq).item(), rel=1e-6)
