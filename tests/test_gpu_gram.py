@@ -300,3 +300,25 @@ def test_output_error_gram_batch_same_format_over_16():
     torch.cuda.synchronize()
     for q, (fmt, B, c, s) in enumerate(items):
         assert out[q].item() == pytest.approx(hd.output_error_gram(fmt, B, c, s, W, gram, ysq).item(), rel=1e-6)
+
+
+def test_output_error_gram_correlated_x():
+    """Strongly correlated activations (rank-8 structure plus 30% noise and
+    two outlier channels): the off-diagonal part of d^T G d is large here,
+    and the float16 route still meets the 1e-4 bar against the oracle."""
+    M, N, K = 1024, 256, 1024
+    rng = np.random.default_rng(91)
+    Xf = rng.standard_normal((M, 8)) @ rng.standard_normal((8, K)) * 3.0 + 0.3 * rng.standard_normal((M, K))
+    Xf[:, [5, 700]] *= 100.0
+    X = torch.from_numpy(Xf.astype(np.float32)).to(torch.bfloat16)
+    Xd = dev(X)
+    h = hd.hdiag(Xd)
+    gram = hd.output_gram(Xd, h=h)
+    for fmt, B, m in ((hd.INT8_E4M3, 32, hd.H_OPT), (hd.NVFP4, 16, hd.H_OPT), (hd.MXFP8, 32, hd.SSE_OPT)):
+        W = weights_for(fmt, N, K, 92)
+        Wd = dev(W)
+        ysq = hd.output_reference_gram(Wd, gram)
+        c, s, _ = hd.quantize_blocks(m, fmt, B, Wd, h=h)
+        out = hd.output_error_gram(fmt, B, c, s, Wd, gram, ysq).item()
+        Wq = oracle.dequantize(fmt, B, npy(c), sc_np(s), N, K)
+        assert out == pytest.approx(oracle.output_error(synth.bits(X), synth.bits(W), Wq), rel=1e-4)
