@@ -168,3 +168,46 @@ def test_output_error_codes_validation():
         bad = list(args); bad[0] = f; bad[1] = 128
         assert L.output_error_codes(*bad) == hd.HD_ERR_UNSUPPORTED
         assert "FP16" in L.hdiag_last_error().decode()
+
+
+def test_gram_validation():
+    """Argument checks of the Gram-route calls, all taken before any GPU work."""
+    L = hd.lib()
+    K = 256
+    gb = L.output_gram_size(K)
+    assert gb >= 2 * K * K and L.output_gram_size(-1) == 0
+    assert L.output_gram_workspace_size(-1, K) == 0
+    ws1 = L.output_error_gram_workspace_size(300, K)
+    assert ws1 == L.output_error_gram_batch_workspace_size(1, 300, K) > 0
+    assert L.output_error_gram_batch_workspace_size(3, 300, K) >= 3 * 512 * K * 2  # 300 rows pad to 512
+    assert L.output_error_gram_batch_workspace_size(0, 300, K) == 0
+    # output_gram: float32 X is unsupported; K % 8; short buffer; misaligned pointers
+    rc = L.output_gram(A, hd.HD_F32, 8, K, None, A, gb, A, 1 << 30, None)
+    assert rc == hd.HD_ERR_UNSUPPORTED
+    rc = L.output_gram(A, hd.HD_BF16, 8, 12, None, A, gb, A, 1 << 30, None)
+    assert rc == hd.HD_ERR_INVALID_ARG and "multiple of 8" in L.hdiag_last_error().decode()
+    rc = L.output_gram(A, hd.HD_BF16, 8, K, None, A, gb - 1, A, 1 << 30, None)
+    assert rc == hd.HD_ERR_INVALID_ARG and "too small" in L.hdiag_last_error().decode()
+    rc = L.output_gram(A, hd.HD_BF16, 8, K, None, MIS, gb, A, 1 << 30, None)
+    assert rc == hd.HD_ERR_INVALID_ARG and "aligned" in L.hdiag_last_error().decode()
+    # output_reference_gram: NULL ysq, short workspace
+    rc = L.output_reference_gram(A, hd.HD_BF16, 4, K, A, gb, None, A, 1 << 30, None)
+    assert rc == hd.HD_ERR_INVALID_ARG and "ysq" in L.hdiag_last_error().decode()
+    rc = L.output_reference_gram(A, hd.HD_BF16, 4, K, A, gb, A, A, 16, None)
+    assert rc == hd.HD_ERR_INVALID_ARG and "workspace" in L.hdiag_last_error().decode()
+    # output_error_gram(_batch): count, block size, NULL arrays / pointers
+    n = 2
+    fm = (ctypes.c_int * n)(hd.INT8_E4M3, hd.NVFP4)
+    bs = (ctypes.c_int32 * n)(32, 24)
+    cs = (ctypes.c_void_p * n)(A.value, A.value)
+    ss = (ctypes.c_void_p * n)(A.value, A.value)
+    rc = L.output_error_gram_batch(n, fm, bs, cs, ss, A, hd.HD_BF16, 4, K, A, gb, A, A, None, A, 1 << 30, None)
+    assert rc == hd.HD_ERR_INVALID_ARG and "block size 24" in L.hdiag_last_error().decode()
+    rc = L.output_error_gram_batch(0, fm, bs, cs, ss, A, hd.HD_BF16, 4, K, A, gb, A, A, None, A, 1 << 30, None)
+    assert rc == hd.HD_ERR_INVALID_ARG and "count" in L.hdiag_last_error().decode()
+    rc = L.output_error_gram_batch(n, None, bs, cs, ss, A, hd.HD_BF16, 4, K, A, gb, A, A, None, A, 1 << 30, None)
+    assert rc == hd.HD_ERR_INVALID_ARG and "host arrays" in L.hdiag_last_error().decode()
+    rc = L.output_error_gram(hd.INT8_E4M3, 32, None, A, A, hd.HD_BF16, 4, K, A, gb, A, A, None, A, 1 << 30, None)
+    assert rc == hd.HD_ERR_INVALID_ARG and "codes" in L.hdiag_last_error().decode()
+    rc = L.output_error_gram(hd.INT8_E4M3, 32, A, A, A, hd.HD_BF16, 4, K, A, gb, A, None, None, A, 1 << 30, None)
+    assert rc == hd.HD_ERR_INVALID_ARG and "out" in L.hdiag_last_error().decode()
