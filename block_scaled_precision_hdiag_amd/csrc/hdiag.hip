@@ -121,14 +121,22 @@ __global__ __launch_bounds__(256) void hdiag_col(const T *__restrict__ X, int64_
     part[(int64_t)blockIdx.y * K + col] = acc;
 }
 
+// h[col] = sum of the R row-chunk partials of col, in float64: 64 columns per
+// workgroup, the four waves summing the chunks r = wave, wave + 4, ... (so
+// more loads are in flight than with one thread per column), combined in a
+// fixed order.
 __global__ __launch_bounds__(256) void hdiag_final(const double *__restrict__ part, int64_t R, int64_t K,
                                                    float *__restrict__ h)
 {
-    const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (col >= K) return;
+    __shared__ double sh[4][64];
+    const int c = threadIdx.x & 63, g = threadIdx.x >> 6;
+    const int64_t col = (int64_t)blockIdx.x * 64 + c;
     double s = 0.0;
-    for (int64_t r = 0; r < R; ++r) s += part[r * K + col];
-    h[col] = (float)s;
+    if (col < K)
+        for (int64_t r = g; r < R; r += 4) s += part[r * K + col];
+    sh[g][c] = s;
+    __syncthreads();
+    if (g == 0 && col < K) h[col] = (float)((sh[0][c] + sh[1][c]) + (sh[2][c] + sh[3][c]));
 }
 
 hipError_t launch_hdiag(const void *X, int xdt, int64_t M, int64_t K, float *h, void *ws, hipStream_t st)
@@ -149,7 +157,7 @@ hipError_t launch_hdiag(const void *X, int xdt, int64_t M, int64_t K, float *h, 
         else
             hdiag_col<float><<<grid, 256, 0, st>>>((const float *)X, M, K, rpc, part);
     }
-    hdiag_final<<<(unsigned)((K + 255) / 256), 256, 0, st>>>(part, R, K, h);
+    hdiag_final<<<(unsigned)((K + 63) / 64), 256, 0, st>>>(part, R, K, h);
     return hipGetLastError();
 }
 
