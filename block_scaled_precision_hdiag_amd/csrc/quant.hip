@@ -81,12 +81,12 @@ __global__ __launch_bounds__(256) void encode_kernel(const T *__restrict__ W, in
             uint32_t v = 0;
 #pragma unroll
             for (int j = 0; j < 8; ++j) v |= (c[j] & 15u) << (4 * j);
-            *reinterpret_cast<uint32_t *>(codes + e / 2) = v;
+            __builtin_nontemporal_store(v, reinterpret_cast<uint32_t *>(codes + e / 2));  // streamed out
         } else {
             uint2 v;
             v.x = (c[0] & 255u) | ((c[1] & 255u) << 8) | ((c[2] & 255u) << 16) | ((c[3] & 255u) << 24);
             v.y = (c[4] & 255u) | ((c[5] & 255u) << 8) | ((c[6] & 255u) << 16) | ((c[7] & 255u) << 24);
-            *reinterpret_cast<uint2 *>(codes + e) = v;
+            __builtin_nontemporal_store((uint64_t)v.x | ((uint64_t)v.y << 32), reinterpret_cast<uint64_t *>(codes + e));
         }
         if (lane % LPB == 0) {
             if (!GIVEN) store_scale<SK>(scales, blk, code);
