@@ -39,7 +39,7 @@ METRIC = "Gweights/s for SSE/H-Optimal block-scale search; % of VALU & HBM peak"
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 # 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz: VALU lane-operations per second
-# without packed FP32 (which this build does not use).
+# without packed FP32 (the kernels are compiled without packed FP32 instructions).
 VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 # counting convention for the search: VALU lane-ops per (weight, candidate)
 SEARCH_OPS = {"sse": 6, "h": 7}
@@ -118,8 +118,8 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the work shards by rows "
-              "of W and X; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (the work would shard by rows "
+              "of W and X). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
