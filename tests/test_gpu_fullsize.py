@@ -181,11 +181,16 @@ def test_config5_large_layer():
     torch.cuda.synchronize()
     np.testing.assert_allclose(h.cpu().numpy(), h_o, rtol=1e-6)
     rows = sample_rows(W.shape[0], 12, 5)
+    Wd = W.cuda()
+    # the output error through G = X^T X at this size too (K = 28672: the
+    # operand's two-pass path, 112 bands of C)
+    gram = hd.output_gram(Xd, h=h)
+    ysq = hd.output_reference_gram(Wd, gram)
     for fmt, B in ((hd.NVFP4, 16), (hd.INT8_E4M3, 128)):
         c, s = check_rows(hd.H_OPT, fmt, B, W, h_o, h, rows)
         Wq = hd.dequantize(fmt, B, c, s, *W.shape)
-        Wd = W.cuda()
         full = hd.output_error(Xd, Wd, Wq).item()
+        assert hd.output_error_gram(fmt, B, c, s, Wd, gram, ysq).item() == pytest.approx(full, rel=1e-4)
         sub = hd.output_error(Xd[:64].contiguous(), Wd, Wq).item()
         sub_o = oracle.output_error(synth.bits(Xh[:64]), synth.bits(W), Wq.cpu().numpy())
         assert sub == pytest.approx(sub_o, rel=1e-4)
