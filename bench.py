@@ -422,7 +422,9 @@ def gptq_suite(args, dev):
     MXFP4 and NVINT4 at B = 16 and 32, each of Naive / SSE-Optimal /
     H-Optimal without GPTQ, with GPTQ-Seq and with GPTQ-Ord: the call's time
     (HIP events, one warm-up) and the weight / output error of the result.
-    H = X^T X is computed once (its time is reported separately)."""
+    H = X^T X is computed once (its time is reported separately), and so is
+    the sequential order's factor of H (gptq_factor): "seq_factored" rows are
+    GPTQ-Seq from it (gptq_quantize_factored, the same results as "seq")."""
     import torch
 
     import block_scaled_precision_hdiag_amd as hd
@@ -449,15 +451,23 @@ def gptq_suite(args, dev):
     H = torch.empty((K, K), dtype=torch.float32, device=dev)
     h_ms, _ = timed(lambda: hd.gptq_hessian(X, H=H, workspace=ws_h))
     h = hd.hdiag(X)
+    ws_f = torch.empty(hd.gptq_factor_workspace_size(K), dtype=torch.uint8, device=dev)
+    factor = torch.empty(hd.gptq_factor_size(K), dtype=torch.uint8, device=dev)
+    f_ms, (_, finfo) = timed(lambda: hd.gptq_factor(H, factor=factor, workspace=ws_f))
+    assert int(finfo.item()) == 0
     names = {v: k for k, v in hd.FORMATS.items()}
     rows = []
     for fmt in (hd.NVFP4, hd.MXFP4, hd.NVINT4):
         for B in (16, 32):
             ws = torch.empty(hd.gptq_workspace_size(B, N, K), dtype=torch.uint8, device=dev)
             for mname, m in (("naive", hd.NAIVE), ("sse", hd.SSE_OPT), ("h", hd.H_OPT)):
-                for mode in ("none", "seq", "ord"):
+                for mode in ("none", "seq", "ord", "seq_factored"):
                     if mode == "none":
                         ms, (c, sc, _) = timed(lambda: hd.quantize_blocks(m, fmt, B, W, h=h))
+                    elif mode == "seq_factored":
+                        ms, (c, sc, _, info) = timed(lambda: hd.gptq_quantize_factored(m, fmt, B, W, H, factor,
+                                                                                       workspace=ws))
+                        assert int(info.item()) == 0
                     else:
                         ms, (c, sc, _, info) = timed(lambda: hd.gptq_quantize(m, fmt, B, W, H, ordered=mode == "ord",
                                                                               workspace=ws))
@@ -471,7 +481,8 @@ def gptq_suite(args, dev):
     print(json.dumps({"suite": "gptq", "config": {"workload": "GPTQ on W 2560x9728 bf16 with H = X^T X from X "
                                                               "16384x9728 bf16 (synthetic stand-ins)",
                                                   "W": [N, K], "X": [M, K]},
-                      "hessian_ms": round(h_ms, 3), "data": "synthetic", "rows": rows}), flush=True)
+                      "hessian_ms": round(h_ms, 3), "factor_ms": round(f_ms, 3), "data": "synthetic", "rows": rows}),
+          flush=True)
 
 
 def sigma_suite(args, dev):

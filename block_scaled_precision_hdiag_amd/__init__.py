@@ -44,7 +44,8 @@ EXPORTS = ["hdiag", "hdiag_workspace_size", "quantize_blocks", "encode_blocks", 
            "output_error_gram_batch", "output_error_gram_batch_workspace_size",
            "quantize_blocks_tensor_scaled",
            "quantize_blocks_tensor_scaled_workspace_size", "dequantize_tensor_scaled", "gptq_hessian", "gptq_hessian_workspace_size", "gptq_quantize",
-           "gptq_workspace_size",
+           "gptq_workspace_size", "gptq_factor", "gptq_factor_size", "gptq_factor_workspace_size",
+           "gptq_quantize_factored",
            "hdiag_strerror", "hdiag_last_error", "hdiag_format_info", "hdiag_version"]
 
 
@@ -114,10 +115,16 @@ def lib():
         L.gptq_workspace_size.argtypes = [i32, i64, i64]
         L.gptq_workspace_size.restype = sz
         L.gptq_quantize.argtypes = [i32, i32, i32, P, i32, i64, i64, P, ctypes.c_double, i32, P, P, P, P, P, sz, P]
+        L.gptq_factor_size.argtypes = [i64]
+        L.gptq_factor_size.restype = sz
+        L.gptq_factor_workspace_size.argtypes = [i64]
+        L.gptq_factor_workspace_size.restype = sz
+        L.gptq_factor.argtypes = [P, i64, ctypes.c_double, P, sz, P, P, sz, P]
+        L.gptq_quantize_factored.argtypes = [i32, i32, i32, P, i32, i64, i64, P, P, sz, P, P, P, P, P, sz, P]
         for name in ("hdiag", "quantize_blocks", "encode_blocks", "dequantize", "weight_error",
                      "output_error", "output_error_given_ref", "output_reference", "output_error_codes",
                      "output_gram", "output_reference_gram", "output_error_gram", "output_error_gram_batch",
-                     "hdiag_format_info", "gptq_hessian", "gptq_quantize", "quantize_blocks_tensor_scaled",
+                     "hdiag_format_info", "gptq_hessian", "gptq_quantize", "gptq_factor", "gptq_quantize_factored", "quantize_blocks_tensor_scaled",
                      "dequantize_tensor_scaled"):
             getattr(L, name).restype = i32
         _lib = L
@@ -478,6 +485,46 @@ def gptq_quantize(method, fmt, B, W, H, damp=0.01, ordered=False, codes=None, sc
     _check(lib().gptq_quantize(method, fmt, B, _ptr(W), _dt(W), N, K, _ptr(H), float(damp), int(bool(ordered)),
                                _ptr(codes), _ptr(scales), _ptr(order), _ptr(info), _ptr(ws), ws.numel(), _stream(d)),
            "gptq_quantize")
+    return codes, scales, order, info
+
+
+def gptq_factor_size(K):
+    return int(lib().gptq_factor_size(K))
+
+
+def gptq_factor_workspace_size(K):
+    return int(lib().gptq_factor_workspace_size(K))
+
+
+def gptq_factor(H, damp=0.01, factor=None, workspace=None):
+    """The sequential-order GPTQ factor of H (float32 [K, K]) and damp, as a
+    uint8 device tensor, and its status (int32 [1])."""
+    d = _dev(H)
+    K = H.shape[0]
+    if factor is None:
+        factor = torch.empty(max(gptq_factor_size(K), 16), dtype=torch.uint8, device=d)
+    info = torch.zeros(1, dtype=torch.int32, device=d)
+    need = gptq_factor_workspace_size(K)
+    ws = workspace if workspace is not None else torch.empty(max(need, 16), dtype=torch.uint8, device=d)
+    _check(lib().gptq_factor(_ptr(H), K, float(damp), _ptr(factor), factor.numel(), _ptr(info), _ptr(ws), ws.numel(),
+                             _stream(d)), "gptq_factor")
+    return factor, info
+
+
+def gptq_quantize_factored(method, fmt, B, W, H, factor, codes=None, scales=None, workspace=None):
+    """GPTQ-Seq from a factor made by gptq_factor(H, damp): the results of
+    gptq_quantize(method, fmt, B, W, H, damp, ordered=False)."""
+    d = _dev(W)
+    N, K = W.shape
+    codes = codes if codes is not None else torch.empty(codes_shape(fmt, N, K), dtype=torch.uint8, device=d)
+    scales = scales if scales is not None else torch.empty((N, K // B), dtype=scale_dtype(fmt), device=d)
+    order = torch.empty(K // B, dtype=torch.int32, device=d)
+    info = torch.zeros(1, dtype=torch.int32, device=d)
+    need = gptq_workspace_size(B, N, K)
+    ws = workspace if workspace is not None else torch.empty(max(need, 16), dtype=torch.uint8, device=d)
+    _check(lib().gptq_quantize_factored(method, fmt, B, _ptr(W), _dt(W), N, K, _ptr(H), _ptr(factor), factor.numel(),
+                                        _ptr(codes), _ptr(scales), _ptr(order), _ptr(info), _ptr(ws), ws.numel(),
+                                        _stream(d)), "gptq_quantize_factored")
     return codes, scales, order, info
 
 

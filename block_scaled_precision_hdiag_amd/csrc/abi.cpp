@@ -412,6 +412,61 @@ hd_status output_error_gram(hd_format fmt, int32_t B, const uint8_t *codes, cons
                                    stream);
 }
 
+size_t gptq_factor_size(int64_t K)
+{
+    if (K < 0) return 0;
+    return (size_t)hd::gptq_factor_bytes(K);
+}
+
+size_t gptq_factor_workspace_size(int64_t K)
+{
+    if (K < 0) return 0;
+    return (size_t)hd::gptq_factor_ws(K);
+}
+
+hd_status gptq_factor(const float *H, int64_t K, double damp, void *factor, size_t factor_bytes, int32_t *info,
+                      void *ws, size_t ws_bytes, void *stream)
+{
+    HD_REQUIRE(K >= 0 && K <= 65535, "size too large (K <= 65535)");
+    HD_REQUIRE(damp >= 0.0 && damp < 1e300, "damp must be a finite non-negative number");
+    if (K == 0) return ok();
+    HD_CHECK_PTR(H, true);
+    HD_CHECK_PTR(factor, true);
+    HD_REQUIRE(factor_bytes >= (size_t)hd::gptq_factor_bytes(K), "factor buffer too small");
+    HD_CHECK_PTR(ws, true);
+    HD_REQUIRE(ws_bytes >= (size_t)hd::gptq_factor_ws(K), "workspace too small");
+    if (info != nullptr && ((uintptr_t)info & 3u)) return fail(HD_ERR_INVALID_ARG, "info misaligned");
+    return hip_status(hd::launch_gptq_factor(H, K, damp, factor, info, ws, (hipStream_t)stream), "gptq_factor");
+}
+
+hd_status gptq_quantize_factored(hd_method method, hd_format fmt, int32_t B, const void *W, hd_dtype wt, int64_t N,
+                                 int64_t K, const float *H, const void *factor, size_t factor_bytes, uint8_t *codes,
+                                 uint8_t *scales, int32_t *block_order, int32_t *info, void *ws, size_t ws_bytes,
+                                 void *stream)
+{
+    HD_REQUIRE(method >= HD_NAIVE && method <= HD_NAIVE_OCP, "unknown method %d", (int)method);
+    HD_REQUIRE(valid_dtype(wt), "unknown dtype %d", (int)wt);
+    hd_status s = check_quant_shape(fmt, B, N, K);
+    if (s != HD_OK) return s;
+    HD_REQUIRE(K <= 65535 && N <= (int64_t)1 << 31, "size too large (K <= 65535)");
+    HD_REQUIRE(method != HD_NAIVE_OCP || is_e8m0(fmt), "the OCP rule needs a power-of-two (E8M0) scale grid");
+    if (N == 0 || K == 0) return ok();
+    HD_CHECK_PTR(W, true);
+    HD_CHECK_PTR(H, true);
+    HD_CHECK_PTR(factor, true);
+    HD_REQUIRE(factor_bytes >= (size_t)hd::gptq_factor_bytes(K), "factor buffer too small");
+    HD_CHECK_PTR(codes, true);
+    HD_CHECK_PTR(ws, true);
+    if (scales == nullptr) return fail(HD_ERR_INVALID_ARG, "scales is NULL");
+    if ((uintptr_t)scales & 3u) return fail(HD_ERR_INVALID_ARG, "scales is not 4-byte aligned");
+    if (block_order != nullptr && ((uintptr_t)block_order & 3u)) return fail(HD_ERR_INVALID_ARG, "block_order misaligned");
+    if (info != nullptr && ((uintptr_t)info & 3u)) return fail(HD_ERR_INVALID_ARG, "info misaligned");
+    HD_REQUIRE(ws_bytes >= (size_t)hd::gptq_ws(B, N, K), "workspace too small");
+    return hip_status(hd::launch_gptq_factored(method, fmt, B, W, wt, N, K, H, factor, codes, scales, block_order,
+                                               info, ws, (hipStream_t)stream),
+                      "gptq_quantize_factored");
+}
+
 bool is_e4m3_scaled(int f) { return f == HD_INT8_E4M3 || f == HD_NVFP4 || f == HD_FP8_E4M3S || f == HD_NVINT4; }
 
 size_t quantize_blocks_tensor_scaled_workspace_size(int64_t N, int64_t K)

@@ -968,6 +968,19 @@ int64_t gptq_hessian_ws(int64_t M, int64_t K)
     return al256(K * M8 * 2) + al256(output_gemm_parts_bytes(K, K));
 }
 
+// col[k] = k (the sequential order); info[0] = 0.
+__global__ __launch_bounds__(256) void gptq_iota_kernel(int *__restrict__ col, int64_t K, int *__restrict__ info)
+{
+    const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (k < K) col[k] = (int)k;
+    if (k == 0) info[0] = 0;
+}
+
+__global__ void gptq_copy_int_kernel(const int *__restrict__ src, int *__restrict__ dst)
+{
+    if (threadIdx.x == 0) dst[0] = src[0];
+}
+
 __global__ __launch_bounds__(256) void gptq_zero_kernel(float *__restrict__ p, int64_t n)
 {
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.0f;
@@ -1061,7 +1074,7 @@ static void gq_loss(const void *W, int wdt, int64_t N, int64_t K, int B, const f
 template <int EK, int SK>
 static hipError_t gq_run(int method, int B, const void *W, int wdt, int64_t N, int64_t K, const float *H, double damp,
                          int ordered, uint8_t *codes, uint8_t *scales, int32_t *block_order, int *info_out, void *ws,
-                         int fmt, hipStream_t st)
+                         int fmt, const float *Vg, const int *info_g, hipStream_t st)
 {
     const GqLayout L = gq_layout(B, N, K);
     char *base = static_cast<char *>(ws);
@@ -1101,12 +1114,18 @@ static hipError_t gq_run(int method, int B, const void *W, int wdt, int64_t N, i
             gptq_gather_kernel<float><<<g, 256, 0, st>>>(static_cast<const float *>(W), N, K, B, perm, h, col, hp,
                                                          Wp);
     }
-    gptq_build_p_kernel<<<dim3((unsigned)((K + 255) / 256), (unsigned)K), 256, 0, st>>>(H, K, col, stat, P);
-    // the recursion multiplies by whole diagonal blocks of L^-1, whose upper
-    // off-diagonal parts it never writes: they must read as zero
-    gptq_zero_kernel<<<2048, 256, 0, st>>>(reinterpret_cast<float *>(Li), 2 * K * K);
-    cholinv(P, Li, K, 0, K, T, T2, info, st);
-    gptq_build_v_kernel<<<dim3((unsigned)((K + 255) / 256), (unsigned)K), 256, 0, st>>>(Li, K, V);
+    if (Vg != nullptr) {
+        // a factor of the sequential order made by gptq_factor: its status, its V
+        gptq_copy_int_kernel<<<1, 64, 0, st>>>(info_g, info);
+        V = const_cast<float *>(Vg);
+    } else {
+        gptq_build_p_kernel<<<dim3((unsigned)((K + 255) / 256), (unsigned)K), 256, 0, st>>>(H, K, col, stat, P);
+        // the recursion multiplies by whole diagonal blocks of L^-1, whose upper
+        // off-diagonal parts it never writes: they must read as zero
+        gptq_zero_kernel<<<2048, 256, 0, st>>>(reinterpret_cast<float *>(Li), 2 * K * K);
+        cholinv(P, Li, K, 0, K, T, T2, info, st);
+        gptq_build_v_kernel<<<dim3((unsigned)((K + 255) / 256), (unsigned)K), 256, 0, st>>>(Li, K, V);
+    }
     const int BL = B > 128 ? 256 : 128;
     for (int64_t p0 = 0; p0 < K; p0 += BL) {
         const int64_t pe = std::min<int64_t>(p0 + BL, K);
@@ -1119,14 +1138,68 @@ static hipError_t gq_run(int method, int B, const void *W, int wdt, int64_t N, i
     return hipGetLastError();
 }
 
+// The float32 factor V of the sequential order, made once for every GPTQ
+// call that shares H and the damping: V = fl32((L^-1)^T) (what the column
+// loop reads) at byte GQ_FACTOR_V of the factor buffer, the factorisation's
+// status (0, or 1 + the first non-positive pivot) at byte 0.
+static constexpr int64_t GQ_FACTOR_V = 256;
+int64_t gptq_factor_bytes(int64_t K) { return GQ_FACTOR_V + al256(K * K * 4); }
+int64_t gptq_factor_ws(int64_t K) { return gptq_ws(32, 0, K); }
+
+hipError_t launch_gptq_factor(const float *H, int64_t K, double damp, void *factor, int *info_out, void *ws,
+                              hipStream_t st)
+{
+    const GqLayout L = gq_layout(32, 0, K);
+    char *base = static_cast<char *>(ws);
+    double *P = reinterpret_cast<double *>(base + L.P), *Li = reinterpret_cast<double *>(base + L.Li);
+    double *T = reinterpret_cast<double *>(base + L.T), *T2 = reinterpret_cast<double *>(base + L.T2);
+    float *h = reinterpret_cast<float *>(base + L.h);
+    int *col = reinterpret_cast<int *>(base + L.col);
+    double *stat = reinterpret_cast<double *>(base + L.stat);
+    int *info = static_cast<int *>(factor);
+    float *V = reinterpret_cast<float *>(static_cast<char *>(factor) + GQ_FACTOR_V);
+    gptq_diag_kernel<<<1, 256, 0, st>>>(H, K, damp, h, stat);
+    gptq_iota_kernel<<<(unsigned)((K + 255) / 256), 256, 0, st>>>(col, K, info);
+    gptq_build_p_kernel<<<dim3((unsigned)((K + 255) / 256), (unsigned)K), 256, 0, st>>>(H, K, col, stat, P);
+    gptq_zero_kernel<<<2048, 256, 0, st>>>(reinterpret_cast<float *>(Li), 2 * K * K);
+    cholinv(P, Li, K, 0, K, T, T2, info, st);
+    gptq_build_v_kernel<<<dim3((unsigned)((K + 255) / 256), (unsigned)K), 256, 0, st>>>(Li, K, V);
+    if (info_out) gptq_copy_int_kernel<<<1, 64, 0, st>>>(info, info_out);
+    return hipGetLastError();
+}
+
+static hipError_t gq_dispatch(int method, int fmt, int B, const void *W, int wdt, int64_t N, int64_t K,
+                              const float *H, double damp, int ordered, uint8_t *codes, uint8_t *scales,
+                              int32_t *block_order, int *info, void *ws, const float *Vg, const int *info_g,
+                              hipStream_t st);
+
 hipError_t launch_gptq(int method, int fmt, int B, const void *W, int wdt, int64_t N, int64_t K, const float *H,
                        double damp, int ordered, uint8_t *codes, uint8_t *scales, int32_t *block_order, int *info,
                        void *ws, hipStream_t st)
 {
+    return gq_dispatch(method, fmt, B, W, wdt, N, K, H, damp, ordered, codes, scales, block_order, info, ws, nullptr,
+                       nullptr, st);
+}
+
+hipError_t launch_gptq_factored(int method, int fmt, int B, const void *W, int wdt, int64_t N, int64_t K,
+                                const float *H, const void *factor, uint8_t *codes, uint8_t *scales,
+                                int32_t *block_order, int *info, void *ws, hipStream_t st)
+{
+    const int *info_g = static_cast<const int *>(factor);
+    const float *Vg = reinterpret_cast<const float *>(static_cast<const char *>(factor) + GQ_FACTOR_V);
+    return gq_dispatch(method, fmt, B, W, wdt, N, K, H, 0.0, 0, codes, scales, block_order, info, ws, Vg, info_g,
+                       st);
+}
+
+static hipError_t gq_dispatch(int method, int fmt, int B, const void *W, int wdt, int64_t N, int64_t K,
+                              const float *H, double damp, int ordered, uint8_t *codes, uint8_t *scales,
+                              int32_t *block_order, int *info, void *ws, const float *Vg, const int *info_g,
+                              hipStream_t st)
+{
 #define HD_GQ_FMT(F)                                                                                          \
     case F:                                                                                                   \
         return gq_run<elem_kind(F), scale_kind(F)>(method, B, W, wdt, N, K, H, damp, ordered, codes, scales, \
-                                                   block_order, info, ws, F, st);
+                                                   block_order, info, ws, F, Vg, info_g, st);
     switch (fmt) {
         HD_GQ_FMT(HD_INT8_E4M3)
         HD_GQ_FMT(HD_NVFP4)

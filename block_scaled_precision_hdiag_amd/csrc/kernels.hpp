@@ -107,6 +107,14 @@ int64_t gptq_ws(int B, int64_t N, int64_t K);
 hipError_t launch_gptq(int method, int fmt, int B, const void *W, int wdt, int64_t N, int64_t K, const float *H,
                        double damp, int ordered, uint8_t *codes, uint8_t *scales, int32_t *block_order, int *info,
                        void *ws, hipStream_t st);
+// The sequential order's factor, made once per (H, damp), and GPTQ-Seq from it.
+int64_t gptq_factor_bytes(int64_t K);
+int64_t gptq_factor_ws(int64_t K);
+hipError_t launch_gptq_factor(const float *H, int64_t K, double damp, void *factor, int *info, void *ws,
+                              hipStream_t st);
+hipError_t launch_gptq_factored(int method, int fmt, int B, const void *W, int wdt, int64_t N, int64_t K,
+                                const float *H, const void *factor, uint8_t *codes, uint8_t *scales,
+                                int32_t *block_order, int *info, void *ws, hipStream_t st);
 
 // Per-tensor scaling over E4M3 block scales (tscale.hip): the tensor scale
 // into *tscale and W / tscale (float32 [N][K]) into Wp.

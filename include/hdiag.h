@@ -412,6 +412,28 @@ hd_status gptq_quantize(hd_method method, hd_format fmt, int32_t B, const void *
                         const float *H, double damp, int32_t ordered, uint8_t *codes, uint8_t *scales,
                         int32_t *block_order, int32_t *info, void *ws, size_t ws_bytes, void *stream);
 
+/* GPTQ-Seq with the factor made once: the column loop of sequential-order
+ * GPTQ reads only V = (L^-1)^T of the damped Hessian H + lambda I (lambda as
+ * gptq_quantize takes it from damp), which depends on H and damp alone, so
+ * every call on one layer (any format, block size and method) can share it.
+ * gptq_factor() writes it, with the factorisation's status, to a caller
+ * buffer of gptq_factor_size(K) bytes (16-byte aligned; workspace
+ * gptq_factor_workspace_size(K)); info (optional, device int32) gets the
+ * status as gptq_quantize reports it.  gptq_quantize_factored() is
+ * gptq_quantize(..., ordered = 0) with the factor's V in place of its own
+ * factorisation: the same codes, scales, block_order and info bit for bit.
+ * H is still read (its diagonal weights H-Optimal); workspace as
+ * gptq_quantize.  Errors as gptq_quantize, plus HD_ERR_INVALID_ARG for a
+ * short factor buffer. */
+size_t gptq_factor_size(int64_t K);
+size_t gptq_factor_workspace_size(int64_t K);
+hd_status gptq_factor(const float *H, int64_t K, double damp, void *factor, size_t factor_bytes, int32_t *info,
+                      void *ws, size_t ws_bytes, void *stream);
+hd_status gptq_quantize_factored(hd_method method, hd_format fmt, int32_t B, const void *W, hd_dtype wt, int64_t N,
+                                 int64_t K, const float *H, const void *factor, size_t factor_bytes, uint8_t *codes,
+                                 uint8_t *scales, int32_t *block_order, int32_t *info, void *ws, size_t ws_bytes,
+                                 void *stream);
+
 /* ------------------------------------------------------------ utilities --- */
 
 /* Static description of a status code. */

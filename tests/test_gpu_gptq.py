@@ -210,3 +210,33 @@ def test_invalid_calls():
     with pytest.raises(hd.HdiagError) as e:
         hd.gptq_hessian(dev(torch.zeros(8, 64)))
     assert e.value.status == hd.HD_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("fmt,B,method", [(hd.INT8_E4M3, 32, hd.H_OPT), (hd.NVFP4, 16, hd.SSE_OPT),
+                                          (hd.MXFP4, 32, hd.NAIVE), (hd.FP4_F16, 64, hd.H_OPT)])
+def test_gptq_factored_matches_gptq_seq(fmt, B, method):
+    """One factor of (H, damp) serves every sequential-order call: the same
+    codes, scales, block order and status as gptq_quantize, bit for bit."""
+    N, K, M = 96, 512, 1024
+    X = synth.activations(M, K, 61, n_out=3, out_gain=20.0, idx_seed=62, dtype=torch.bfloat16)
+    W = synth.weights("t4", N, K, std=0.02, seed=63, gain_seed=64, dtype=torch.bfloat16)
+    Hd = hd.gptq_hessian(dev(X))
+    factor, finfo = hd.gptq_factor(Hd, damp=0.01)
+    c0, s0, o0, i0 = hd.gptq_quantize(method, fmt, B, dev(W), Hd, damp=0.01, ordered=False)
+    c1, s1, o1, i1 = hd.gptq_quantize_factored(method, fmt, B, dev(W), Hd, factor)
+    torch.cuda.synchronize()
+    assert torch.equal(c0, c1) and torch.equal(s0, s1) and torch.equal(o0, o1)
+    assert int(i0.item()) == int(i1.item()) == int(finfo.item()) == 0
+
+
+def test_gptq_factor_reports_an_indefinite_hessian():
+    K = 256
+    h = torch.ones(K)
+    h[7] = -1.0
+    Hd = dev(torch.diag(h))
+    factor, finfo = hd.gptq_factor(Hd, damp=0.0)
+    W = dev(synth.weights("t4", 32, K, std=0.02, seed=1, gain_seed=2, dtype=torch.bfloat16))
+    _, _, _, info = hd.gptq_quantize_factored(hd.NAIVE, hd.NVFP4, 16, W, Hd, factor)
+    _, _, _, info0 = hd.gptq_quantize(hd.NAIVE, hd.NVFP4, 16, W, Hd, damp=0.0)
+    torch.cuda.synchronize()
+    assert int(finfo.item()) > 0 and int(info.item()) == int(finfo.item()) == int(info0.item())
