@@ -50,9 +50,11 @@ COUNTERS_PROFILE = os.path.join(ROOT, "profiles", "int8_down_proj_2560x9728_coun
 
 
 # sources whose kernels the INT8 step never launches (other formats' searches,
-# the FP16-scale alternation, GPTQ, per-tensor scaling)
+# the FP16-scale alternation, GPTQ, per-tensor scaling), and the host-only C
+# ABI wrapper and launcher declarations (no device code)
 _NOT_IN_STEP = {"alt_f16.hip", "gptq.hip", "tscale.hip", "search_fp8s.hip", "search_mxfp4.hip", "search_mxfp8.hip",
-                "search_nvfp4.hip", "search_nvfp4_ue4m4.hip", "search_nvfp4_ue5m3.hip", "search_nvint4.hip"}
+                "search_nvfp4.hip", "search_nvfp4_ue4m4.hip", "search_nvfp4_ue5m3.hip", "search_nvint4.hip",
+                "abi.cpp", "kernels.hpp"}
 
 
 def source_hash():
