@@ -7,8 +7,10 @@
 // chunk.  Each lane streams 16-byte row segments (8 columns) down the chunk,
 // one row in four per wave, four rows in flight, with non-temporal loads
 // (X is read once), and keeps 8 float64
-// sums (a bf16 square is exact in fp32, an fp32 square in fp64), so the only
-// rounding is float64 addition.  The four waves' sums are added through LDS
+// sums of float64 squares (exact for every bf16 and fp32 value: a float64
+// product of two 24-bit significands needs 48 bits, and its exponent range
+// covers squares of the smallest subnormal and the largest finite fp32), so
+// the only rounding is float64 addition.  The four waves' sums are added through LDS
 // in a fixed order and stored as a float64 partial [R][K] in the workspace.
 // Pass 2: h[j] = fl32(sum over the R partials, in chunk order).
 // A one-column-per-lane variant covers K % 8 != 0.
@@ -50,11 +52,12 @@ size_t hdiag_ws(int64_t M, int64_t K)
     return (size_t)r * (size_t)K * sizeof(double);
 }
 
+// x^2 in float64, exact for every finite float32 (hence bf16) value; a float32
+// square would flush or round below 2^-126 and overflow above 2^64.
 template <typename T>
 __device__ __forceinline__ double sq(float x)
 {
-    if (sizeof(T) == 2) return (double)(x * x);  // bf16: 8-bit significand, the fp32 square is exact
-    return (double)x * (double)x;                // fp32: exact in float64
+    return (double)x * (double)x;
 }
 
 template <typename T>

@@ -196,6 +196,15 @@ def test_hdiag_exact_cases():
     Xi = torch.randint(-3, 4, (2049, 64), generator=torch.Generator().manual_seed(1)).float()
     want = (Xi.double() ** 2).sum(0).float()
     assert torch.equal(hd.hdiag(dev(Xi)).cpu(), want)
+    # bf16 values whose squares lie below float32's normal range (2^-136 here)
+    # or near its top: the squares are summed in float64, as in the oracle
+    g = torch.Generator().manual_seed(2)
+    mant = 1.0 + torch.randint(0, 128, (4096, 24), generator=g).double() / 128.0
+    ex = torch.tensor([-68.0] * 8 + [-75.0] * 8 + [56.0] * 8, dtype=torch.float64)
+    Xs = (mant * torch.pow(2.0, ex)).to(torch.bfloat16)
+    want = oracle.hdiag(synth.bits(Xs))
+    assert np.isfinite(want).all() and (want[:16] > 0).all()
+    np.testing.assert_allclose(npy(hd.hdiag(dev(Xs))), want, rtol=1e-6)
 
 
 @pytest.mark.parametrize("fmt", FMTS)
