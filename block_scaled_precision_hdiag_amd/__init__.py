@@ -36,7 +36,7 @@ FOUR_BIT = (NVFP4, MXFP4, NVFP4_UE4M4, NVFP4_UE5M3, NVINT4, FP4_F16, INT4_F16)
 # formats whose block scales are binary16 values (stored as torch.float16)
 F16_SCALES = (FP4_F16, INT4_F16)
 
-EXPORTS = ["hdiag", "hdiag_workspace_size", "quantize_blocks", "encode_blocks", "dequantize",
+EXPORTS = ["hdiag", "hdiag_workspace_size", "hdiag_noalloc", "quantize_blocks", "encode_blocks", "dequantize",
            "weight_error", "weight_error_workspace_size", "output_error", "output_error_workspace_size",
            "output_error_given_ref", "output_reference", "output_reference_size", "output_error_codes",
            "output_error_codes_workspace_size", "output_gram", "output_gram_size", "output_gram_workspace_size",
@@ -69,6 +69,7 @@ def lib():
         P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
         L.hdiag.argtypes = [P, i32, i64, i64, P, P, sz, P]
         L.hdiag_workspace_size.argtypes = [i64, i64]
+        L.hdiag_noalloc.argtypes = [P, i32, i64, i64, P, P]
         L.hdiag_workspace_size.restype = sz
         L.quantize_blocks.argtypes = [i32, i32, i32, P, i32, i64, i64, P, P, P, P, P]
         L.encode_blocks.argtypes = [i32, i32, P, i32, i64, i64, P, P, P, P, P]
@@ -121,7 +122,7 @@ def lib():
         L.gptq_factor_workspace_size.restype = sz
         L.gptq_factor.argtypes = [P, i64, ctypes.c_double, P, sz, P, P, sz, P]
         L.gptq_quantize_factored.argtypes = [i32, i32, i32, P, i32, i64, i64, P, P, sz, P, P, P, P, P, sz, P]
-        for name in ("hdiag", "quantize_blocks", "encode_blocks", "dequantize", "weight_error",
+        for name in ("hdiag", "hdiag_noalloc", "quantize_blocks", "encode_blocks", "dequantize", "weight_error",
                      "output_error", "output_error_given_ref", "output_reference", "output_error_codes",
                      "output_gram", "output_reference_gram", "output_error_gram", "output_error_gram_batch",
                      "hdiag_format_info", "gptq_hessian", "gptq_quantize", "gptq_factor", "gptq_quantize_factored", "quantize_blocks_tensor_scaled",
@@ -202,6 +203,20 @@ def hdiag(X, out=None, workspace=None):
     ws = workspace if workspace is not None else torch.empty(max(need, 16), dtype=torch.uint8, device=d)
     _check(lib().hdiag(_ptr(X), _dt(X), M, K, _ptr(h), _ptr(ws), ws.numel(), _stream(d)), "hdiag")
     return h
+
+
+# bytes of the static device scratch behind hdiag_noalloc (HD_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def hdiag_noalloc(X, out):
+    """hdiag() into a caller-given float32 [K] tensor `out`, with the library's
+    static per-GPU scratch instead of a workspace: the call allocates nothing.
+    Calls that overlap on one GPU race (they share the scratch)."""
+    d = _dev(X)
+    M, K = X.shape
+    _check(lib().hdiag_noalloc(_ptr(X), _dt(X), M, K, _ptr(out), _stream(d)), "hdiag_noalloc")
+    return out
 
 
 def quantize_blocks(method, fmt, B, W, h=None, block_obj=False, codes=None, scales=None):

@@ -130,6 +130,23 @@ hd_status hdiag(const void *X, hd_dtype xt, int64_t M, int64_t K, float *h, void
     return hip_status(hd::launch_hdiag(X, xt, M, K, h, ws, (hipStream_t)stream), "hdiag");
 }
 
+hd_status hdiag_noalloc(const void *X, hd_dtype xt, int64_t M, int64_t K, float *h, void *stream)
+{
+    HD_REQUIRE(valid_dtype(xt), "unknown dtype %d", (int)xt);
+    HD_REQUIRE(M >= 0 && K >= 0, "negative size M=%lld K=%lld", (long long)M, (long long)K);
+    if (K == 0) return ok();
+    HD_CHECK_PTR(h, true);
+    HD_CHECK_PTR(X, M > 0);
+    const size_t need = hd::hdiag_ws(M, K), have = hd::hdiag_noalloc_limit();
+    if (need > have)
+        return fail(HD_ERR_UNSUPPORTED, "hdiag_noalloc: X [%lld, %lld] needs %zu bytes of partials, beyond the %zu-byte static scratch; use hdiag() with a workspace",
+                    (long long)M, (long long)K, need, have);
+    void *ws = nullptr;
+    hd_status s = hip_status(hd::hdiag_scratch_address((hipStream_t)stream, &ws), "hdiag_noalloc (scratch address)");
+    if (s != HD_OK) return s;
+    return hip_status(hd::launch_hdiag(X, xt, M, K, h, ws, (hipStream_t)stream), "hdiag_noalloc");
+}
+
 hd_status quantize_blocks(hd_method method, hd_format fmt, int32_t B, const void *W, hd_dtype wt, int64_t N,
                           int64_t K, const float *h, uint8_t *codes, uint8_t *scales, float *block_obj,
                           void *stream)

@@ -14,7 +14,10 @@
 // in a fixed order and stored as a float64 partial [R][K] in the workspace.
 // Pass 2: h[j] = fl32(sum over the R partials, in chunk order).
 // A one-column-per-lane variant covers K % 8 != 0.
+#include <mutex>
+
 #include "common.hpp"
+#include "hdiag.h"
 #include "kernels.hpp"
 
 namespace hd {
@@ -162,6 +165,52 @@ hipError_t launch_hdiag(const void *X, int xdt, int64_t M, int64_t K, float *h, 
     }
     hdiag_final<<<(unsigned)((K + 63) / 64), 256, 0, st>>>(part, R, K, h);
     return hipGetLastError();
+}
+
+// ------------------------------------------------------ hdiag_noalloc ---
+// The row-chunk partials of hdiag_noalloc() live in this file-scope array, one
+// copy per GPU for the life of the process, instead of a caller workspace.
+// Host code never passes the symbol itself to a kernel (on the host it names a
+// stand-in, not device memory): each device's address comes from
+// hipGetSymbolAddress, taken once per device with that device current, and
+// only that address is used.  Every partial is written by pass 1 before pass 2
+// reads it, so nothing has to be cleared between calls.
+static __device__ __align__(256) double scratch[HD_NOALLOC_SCRATCH_BYTES / sizeof(double)];
+
+static constexpr int HD_MAX_DEVICES = 64;
+static std::mutex g_scratch_mu;
+static void *g_scratch_ptr[HD_MAX_DEVICES];
+
+size_t hdiag_noalloc_limit() { return sizeof(scratch); }
+
+hipError_t hdiag_scratch_address(hipStream_t st, void **ptr)
+{
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    int dev = cur;
+    if (st != nullptr) {
+        hipDevice_t d = 0;
+        e = hipStreamGetDevice(st, &d);
+        if (e != hipSuccess) return e;
+        dev = (int)d;
+    }
+    if (dev < 0 || dev >= HD_MAX_DEVICES) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur) {
+            const hipError_t r = hipSetDevice(cur);
+            if (e == hipSuccess) e = r;
+        }
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 }  // namespace hd

@@ -49,6 +49,11 @@ hipError_t launch_weight_error(const void *W, int wdt, const void *Wq, int qdt, 
 
 size_t hdiag_ws(int64_t M, int64_t K);
 hipError_t launch_hdiag(const void *X, int xdt, int64_t M, int64_t K, float *h, void *ws, hipStream_t st);
+// hdiag_noalloc's static scratch: its size in bytes, and its device address on
+// the device of `st` (the current device for the null stream), looked up once
+// per device.
+size_t hdiag_noalloc_limit();
+hipError_t hdiag_scratch_address(hipStream_t st, void **ptr);
 
 size_t output_error_ws(int64_t M, int64_t N, int64_t K, bool mfma);
 bool output_error_uses_mfma(int xdt, int wdt, int64_t K);

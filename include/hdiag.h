@@ -132,6 +132,30 @@ size_t hdiag_workspace_size(int64_t M, int64_t K);
 hd_status hdiag(const void *X, hd_dtype xt, int64_t M, int64_t K, float *h, void *ws,
                 size_t ws_bytes, void *stream);
 
+/* Bytes of the static device scratch behind hdiag_noalloc(). */
+#define HD_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+/* hdiag() for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, kernels and results as hdiag() (bit for bit), but the float64
+ * row-chunk partials go to a static __device__ scratch array of
+ * HD_NOALLOC_SCRATCH_BYTES held by every GPU the library runs on until the
+ * process ends, so no workspace is passed and nothing is allocated
+ * (no hipMalloc / hipFree, no allocating library call).  The device is the
+ * stream's (the current device for the null stream); the first call on a
+ * device looks up that device's scratch address once.
+ * Limit: hdiag_workspace_size(M, K) <= HD_NOALLOC_SCRATCH_BYTES (every M for
+ * K up to about 10^6 columns); larger shapes return HD_ERR_UNSUPPORTED and
+ * launch nothing.
+ * Concurrency: every call on one GPU shares that GPU's scratch.  Calls that
+ * overlap on one GPU (on different streams, or from different threads without
+ * ordering) race and give undefined h; calls on one stream are ordered and
+ * safe.  No part of the scratch must start at zero: each call writes every
+ * partial it reads.
+ * Errors: those of hdiag(), plus HD_ERR_UNSUPPORTED for a shape beyond the
+ * limit and HD_ERR_HIP if the scratch address cannot be looked up. */
+hd_status hdiag_noalloc(const void *X, hd_dtype xt, int64_t M, int64_t K, float *h, void *stream);
+
 /* ------------------------------------------------------ quantize_blocks --- */
 
 /* Choose the scale of every block and encode W with it.

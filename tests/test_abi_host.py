@@ -127,6 +127,21 @@ def test_workspace_queries():
     assert rc == hd.HD_ERR_INVALID_ARG and "workspace" in L.hdiag_last_error().decode()
 
 
+def test_hdiag_noalloc_validation():
+    """hdiag_noalloc refuses shapes whose partials exceed its static scratch,
+    and bad arguments, before any HIP call."""
+    L = hd.lib()
+    assert hd.hdiag_workspace_size(1, 4 << 20) > hd.NOALLOC_SCRATCH_BYTES
+    assert hd.hdiag_workspace_size(244449, 9728) <= hd.NOALLOC_SCRATCH_BYTES
+    assert hd.hdiag_workspace_size(65536, 28672) <= hd.NOALLOC_SCRATCH_BYTES
+    rc = L.hdiag_noalloc(A, hd.HD_BF16, 1, 4 << 20, A, None)
+    assert rc == hd.HD_ERR_UNSUPPORTED and "static scratch" in L.hdiag_last_error().decode()
+    assert L.hdiag_noalloc(A, 7, 10, 64, A, None) == hd.HD_ERR_INVALID_ARG
+    assert L.hdiag_noalloc(A, hd.HD_BF16, 10, 64, None, None) == hd.HD_ERR_INVALID_ARG
+    assert L.hdiag_noalloc(MIS, hd.HD_BF16, 10, 64, A, None) == hd.HD_ERR_INVALID_ARG
+    assert L.hdiag_noalloc(None, hd.HD_BF16, 10, 0, None, None) == hd.HD_OK
+
+
 def test_output_reference_validation():
     L = hd.lib()
     M, N, K = 300, 200, 512
