@@ -24,6 +24,7 @@ LIB_PATH = os.path.join(_HERE, "libhdiag.so")
 # enums of include/hdiag.h
 HD_OK, HD_ERR_INVALID_ARG, HD_ERR_UNSUPPORTED, HD_ERR_HIP = 0, -1, -2, -3
 HD_F32, HD_BF16 = 0, 1
+SCHED_GRAM_GANGS, SCHED_GPTQ_TILE = 0, 1
 NAIVE, SSE_OPT, H_OPT, NAIVE_OCP = 0, 1, 2, 3
 INT8_E4M3, NVFP4, MXFP4, MXFP8, FP8_E4M3S = 0, 1, 2, 3, 4
 NVFP4_UE4M4, NVFP4_UE5M3, NVINT4 = 5, 6, 7
@@ -36,7 +37,7 @@ FOUR_BIT = (NVFP4, MXFP4, NVFP4_UE4M4, NVFP4_UE5M3, NVINT4, FP4_F16, INT4_F16)
 # formats whose block scales are binary16 values (stored as torch.float16)
 F16_SCALES = (FP4_F16, INT4_F16)
 
-EXPORTS = ["hdiag", "hdiag_workspace_size", "hdiag_noalloc", "quantize_blocks", "encode_blocks", "dequantize",
+EXPORTS = ["hdiag_set_schedule", "hdiag", "hdiag_workspace_size", "hdiag_noalloc", "quantize_blocks", "encode_blocks", "dequantize",
            "weight_error", "weight_error_workspace_size", "output_error", "output_error_workspace_size",
            "output_error_given_ref", "output_reference", "output_reference_size", "output_error_codes",
            "output_error_codes_workspace_size", "output_gram", "output_gram_size", "output_gram_workspace_size",
@@ -70,6 +71,7 @@ def lib():
         L.hdiag.argtypes = [P, i32, i64, i64, P, P, sz, P]
         L.hdiag_workspace_size.argtypes = [i64, i64]
         L.hdiag_noalloc.argtypes = [P, i32, i64, i64, P, P]
+        L.hdiag_set_schedule.argtypes = [i32, i32]
         L.hdiag_workspace_size.restype = sz
         L.quantize_blocks.argtypes = [i32, i32, i32, P, i32, i64, i64, P, P, P, P, P]
         L.encode_blocks.argtypes = [i32, i32, P, i32, i64, i64, P, P, P, P, P]
@@ -122,7 +124,7 @@ def lib():
         L.gptq_factor_workspace_size.restype = sz
         L.gptq_factor.argtypes = [P, i64, ctypes.c_double, P, sz, P, P, sz, P]
         L.gptq_quantize_factored.argtypes = [i32, i32, i32, P, i32, i64, i64, P, P, sz, P, P, P, P, P, sz, P]
-        for name in ("hdiag", "hdiag_noalloc", "quantize_blocks", "encode_blocks", "dequantize", "weight_error",
+        for name in ("hdiag_set_schedule", "hdiag", "hdiag_noalloc", "quantize_blocks", "encode_blocks", "dequantize", "weight_error",
                      "output_error", "output_error_given_ref", "output_reference", "output_error_codes",
                      "output_gram", "output_reference_gram", "output_error_gram", "output_error_gram_batch",
                      "hdiag_format_info", "gptq_hessian", "gptq_quantize", "gptq_factor", "gptq_quantize_factored", "quantize_blocks_tensor_scaled",
@@ -188,6 +190,12 @@ def scale_dtype(fmt):
     """torch dtype of a scale tensor: float16 (the binary16 scale itself) for
     the FP16-scale formats, uint8 codes otherwise."""
     return torch.float16 if fmt in F16_SCALES else torch.uint8
+
+
+def hdiag_set_schedule(knob, value):
+    """Set a process-wide schedule setting (SCHED_GRAM_GANGS, SCHED_GPTQ_TILE;
+    0 = automatic); host-only."""
+    _check(lib().hdiag_set_schedule(knob, value), "hdiag_set_schedule")
 
 
 def hdiag_workspace_size(M, K):
@@ -402,7 +410,7 @@ def output_error_gram(fmt, B, codes, scales, W, gram, ysq, sums=False, workspace
     N, K = W.shape
     if out is None:
         out = torch.empty(1, dtype=torch.float64, device=d)
-    s = torch.empty(2, dtype=torch.float64, device=d) if sums else None
+    s = torch.empty(3, dtype=torch.float64, device=d) if sums else None
     need = output_error_gram_workspace_size(N, K)
     ws = workspace if workspace is not None else torch.empty(max(need, 16), dtype=torch.uint8, device=d)
     _check(lib().output_error_gram(fmt, B, _ptr(codes), _ptr(scales), _ptr(W), _dt(W), N, K, _ptr(gram),
@@ -418,13 +426,19 @@ def output_error_gram_batch_workspace_size(count, N, K):
 def output_error_gram_batch(items, W, gram, ysq, sums=False, workspace=None, out=None):
     """output_error_gram for several quantisations of W in one call: items is a
     sequence of (fmt, B, codes, scales).  Returns a float64 device tensor
-    [len(items)] (and [len(items), 2] sums)."""
+    [len(items)] (and [len(items), 3] sums: ||X D^T||^2, ||X W^T||^2 and the
+    diagonal sum of each; `sums` may be such a float64 tensor to fill)."""
     d = _dev(W)
     N, K = W.shape
     n = len(items)
     if out is None:
         out = torch.empty(n, dtype=torch.float64, device=d)
-    s = torch.empty((n, 2), dtype=torch.float64, device=d) if sums else None
+    if isinstance(sums, torch.Tensor):
+        if sums.dtype != torch.float64 or sums.numel() < 3 * n or not sums.is_contiguous():
+            raise ValueError("sums must be a contiguous float64 tensor of 3 x %d values" % n)
+        s = sums
+    else:
+        s = torch.empty((n, 3), dtype=torch.float64, device=d) if sums else None
     fm = (ctypes.c_int * n)(*[int(it[0]) for it in items])
     bs = (ctypes.c_int32 * n)(*[int(it[1]) for it in items])
     cs = (ctypes.c_void_p * n)(*[it[2].data_ptr() for it in items])
@@ -434,7 +448,7 @@ def output_error_gram_batch(items, W, gram, ysq, sums=False, workspace=None, out
     _check(lib().output_error_gram_batch(n, fm, bs, cs, ss, _ptr(W), _dt(W), N, K, _ptr(gram), gram.numel(),
                                          _ptr(ysq), _ptr(out), _ptr(s), _ptr(ws), ws.numel(), _stream(d)),
            "output_error_gram_batch")
-    return (out, s) if sums else out
+    return (out, s) if s is not None else out
 
 
 def quantize_blocks_tensor_scaled_workspace_size(N, K):

@@ -1,5 +1,7 @@
 // abi.cpp - the C ABI of libhdiag.so: argument validation, error reporting and
 // dispatch to the kernel launchers.  Nothing here allocates device memory.
+#include <atomic>
+
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -76,9 +78,26 @@ hd_status check_quant_shape(int fmt, int32_t B, int64_t N, int64_t K)
     return HD_OK;
 }
 
+std::atomic<int> g_schedule[HD_SCHED_COUNT];
+
 }  // namespace
 
+int hd::schedule_setting(int knob)
+{
+    return knob >= 0 && knob < HD_SCHED_COUNT ? g_schedule[knob].load(std::memory_order_relaxed) : 0;
+}
+
 extern "C" {
+
+hd_status hdiag_set_schedule(hd_schedule knob, int32_t value)
+{
+    HD_REQUIRE(knob >= 0 && knob < HD_SCHED_COUNT, "unknown schedule setting %d", (int)knob);
+    HD_REQUIRE(value >= 0, "schedule value %d is negative", (int)value);
+    if (knob == HD_SCHED_GPTQ_TILE)
+        HD_REQUIRE(value == 0 || value == 64 || value == 128, "GPTQ tile %d is not 0, 64 or 128", (int)value);
+    g_schedule[knob].store(value, std::memory_order_relaxed);
+    return ok();
+}
 
 const char *hdiag_version(void) { return "hdiag 0.1 (gfx950)"; }
 

@@ -35,6 +35,7 @@
 #include <cstdlib>
 
 #include "encode.hpp"
+#include "hdiag.h"
 #include "kernels.hpp"
 
 namespace hd {
@@ -591,16 +592,15 @@ static GqGemm gq_gemm(int64_t M, int64_t N, int64_t K, double alpha, const doubl
 // Which kernel a product takes: 0 the VALU 64-tiles, else the matrix-core
 // tile width.  Products of 256 rows and columns and up (with aligned
 // operands) go to the matrix cores, with 128-tiles when they give at least
-// two rounds of workgroups, unless HD_GPTQ_GEMM_TILE (64 or 128) names the
-// width.
+// two rounds of workgroups, unless the schedule setting HD_SCHED_GPTQ_TILE
+// (64 or 128) names the width.
 template <bool TB>
 static int gq_tile(const GqGemm &g)
 {
     const bool aligned = g.K % 8 == 0 && g.lda % 2 == 0 && g.ldb % 2 == 0 && (TB || g.N % 8 == 0) &&
                          reinterpret_cast<uintptr_t>(g.A) % 16 == 0 && reinterpret_cast<uintptr_t>(g.B) % 16 == 0;
     if (!(g.M >= 256 && g.N >= 256 && aligned)) return 0;
-    const char *env = getenv("HD_GPTQ_GEMM_TILE");
-    const int forced = env ? atoi(env) : 0;
+    const int forced = schedule_setting(HD_SCHED_GPTQ_TILE);
     const int64_t t128 = ((g.M + 127) / 128) * ((g.N + 127) / 128);
     return (forced == 128 || (forced != 64 && t128 >= 2 * 256)) ? 128 : 64;
 }

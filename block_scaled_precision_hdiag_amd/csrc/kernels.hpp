@@ -7,6 +7,9 @@
 
 namespace hd {
 
+// Current value of a schedule setting (hdiag_set_schedule; 0 = automatic).
+int schedule_setting(int knob);
+
 // Naive scale + encode (scales_in == NULL), or encode with given scale codes.
 // ocp != 0 (E8M0 grids): the OCP MX floor rule instead of the Naive snap.
 hipError_t launch_encode(int fmt, int B, const void *W, int wdt, int64_t N, int64_t K, const float *h,

@@ -41,6 +41,7 @@
 
 #include "common.hpp"
 #include "formats.hpp"
+#include "hdiag.h"
 #include "kernels.hpp"
 
 namespace hd {
@@ -1211,9 +1212,11 @@ __global__ __launch_bounds__(256) void gram_operand_multi_kernel(const GramOps o
 
 // One workgroup per quantisation q: total = the slots part[(t mt + band) qg
 // + x] of its E tiles t = q tpq .. q tpq + tpq - 1 (every band and gang) plus
-// dsum of its rows q rpq .. q rpq + nvalid - 1, in a fixed order.  ysq ==
-// NULL: ysq_out[q] = total.  Otherwise out[q] = sqrt(total) / sqrt(*ysq) and
-// sums[2 q .. 2 q + 1] = {total, *ysq}.
+// the diagonal sum b = dsum of its rows q rpq .. q rpq + nvalid - 1, in a
+// fixed order.  ysq == NULL: ysq_out[q] = total.  Otherwise out[q] =
+// sqrt(total) / sqrt(*ysq) and sums[3 q .. 3 q + 2] = {total, *ysq, b} (b /
+// total says how much the float16 off-diagonal part cancels the exact
+// diagonal one).
 __global__ __launch_bounds__(256) void gram_final(const double *__restrict__ part, int tpq, int mt, int qg,
                                                   const double *__restrict__ dsum, int64_t rpq, int64_t nvalid,
                                                   const double *__restrict__ ysq, double *__restrict__ ysq_out,
@@ -1236,8 +1239,9 @@ __global__ __launch_bounds__(256) void gram_final(const double *__restrict__ par
             const double y = *ysq;
             out[q] = sqrt(t) / sqrt(y);
             if (sums) {
-                sums[2 * q] = t;
-                sums[2 * q + 1] = y;
+                sums[3 * q] = t;
+                sums[3 * q + 1] = y;
+                sums[3 * q + 2] = b;
             }
         }
     }
@@ -1270,7 +1274,8 @@ size_t output_gram_ws(int64_t M, int64_t K)
 // P / qe) bands per panel) that keep the largest share of the XCD busy on
 // real tiles, 8 gangs of P slots, when that share is at least 90%;
 // otherwise gangs of all nt tiles with one band per panel, CUs / nt of them.
-// HD_GRAM_GROUPS = g forces the second form with g gangs.
+// The schedule setting HD_SCHED_GRAM_GANGS = g > 0 forces the second form
+// with g gangs.
 struct GramPlan {
     int qa, qe, qg, qper;
     int64_t qcpg, qcols, wgs;
@@ -1278,8 +1283,7 @@ struct GramPlan {
 static GramPlan gram_plan(int64_t nt, int64_t K)
 {
     const int64_t mt = (K + GE_TM - 1) / GE_TM, cus = device_cus(), per = cus / 8;
-    const char *env = getenv("HD_GRAM_GROUPS");
-    const int64_t forced = env ? std::min<int64_t>(atoll(env), cus) : 0;
+    const int64_t forced = std::min<int64_t>(schedule_setting(HD_SCHED_GRAM_GANGS), cus);
     GramPlan g;
     double best = 0.0;
     int64_t bqe = 0, bqa = 0;

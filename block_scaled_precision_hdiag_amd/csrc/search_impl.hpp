@@ -18,8 +18,14 @@
 //     every lane of a wave and is loaded once) and walk the candidates in
 //     lock-step, reading each candidate's (s, 1/s) from an LDS table; the
 //     running argmin is per lane and needs no cross-lane reduction;
-//   - each residual is exact in fp32 and squared / accumulated in float64, so
-//     the objective differs from its exact value only by float64 rounding;
+//   - each residual is formed in fp32 and squared / accumulated in float64.
+//     It is exact (Sterbenz) for every element that does not saturate, and
+//     for elements that encode to zero; for a saturated element
+//     (a > 2 fl32(Q s)) the fp32 subtraction rounds once, at most 2^-24
+//     relative, so the objective of a candidate that clips is within 2^-23
+//     relative of its exact value (the oracle subtracts in float64).  A block
+//     whose choice this could move has two candidates within 2^-23 of each
+//     other, inside the 1e-6 tie tolerance of the parity bar;
 //   - candidates at and above the first scale that rounds the block's amax to
 //     zero all give sum_j om_j w_j^2 (every element encodes to 0): they could
 //     only tie, and ties keep the lower code, so they are never evaluated;

@@ -116,6 +116,23 @@ typedef enum {
     HD_INT4_F16 = 9
 } hd_format;
 
+/* ------------------------------------------------------------- schedule --- */
+
+/* Process-wide schedule settings of kernels whose work split does not change
+ * what they compute, only the order of floating-point partial sums or the
+ * tile shape of an intermediate product.  Value 0 (the initial state) is the
+ * automatic choice.  Meant for tests and tuning; a setting applies to calls
+ * made after it on any thread.
+ *   HD_SCHED_GRAM_GANGS - output_error_gram(_batch): g > 0 runs the C E^T walk
+ *                         as g gangs of one workgroup per 256-row tile of E
+ *                         instead of its per-XCD schedule (the order of the
+ *                         float64 partial sums changes);
+ *   HD_SCHED_GPTQ_TILE  - gptq_*: 64 or 128 forces the tile width of the
+ *                         factorisation's matrix-core products.
+ * Errors: HD_ERR_INVALID_ARG for an unknown setting or value. */
+typedef enum { HD_SCHED_GRAM_GANGS = 0, HD_SCHED_GPTQ_TILE = 1, HD_SCHED_COUNT = 2 } hd_schedule;
+hd_status hdiag_set_schedule(hd_schedule knob, int32_t value);
+
 /* ---------------------------------------------------------------- hdiag --- */
 
 /* Bytes of workspace hdiag() needs for X [M, K]. */
@@ -312,25 +329,27 @@ hd_status output_error_codes(hd_format fmt, int32_t B, const void *X, hd_dtype x
  * output_reference_gram() writes ||X W^T||_F^2 (double) to the device scalar
  * *ysq; output_error_gram() writes ||X Wq^T - X W^T||_F / sqrt(*ysq) to *out,
  * for Wq = dequantize(fmt, B, codes, scales) (every format, FP16 scales
- * included) without forming Wq, and sums (optional, device, 2 doubles) gets
- * {||X (Wq - W)^T||_F^2, *ysq}.  W: bfloat16 or float32 [N, K], the weights
- * the codes quantise.
+ * included) without forming Wq, and sums (optional, device, 3 doubles) gets
+ * {t = ||X (Wq - W)^T||_F^2, *ysq, b = sum_n sum_j d_nj^2 h_j}.  W: bfloat16
+ * or float32 [N, K], the weights the codes quantise.
  * Accuracy: with e_n = d_n sqrt(h), d^T G d = sum_j d_j^2 h_j + e^T C e; the
- * diagonal sum is taken in float64 from float32 d and h, the off-diagonal part
- * is the float16 MFMA product of e (one power-of-two scale per row, rounded
- * to 11 significant bits) with the float16 C, in float32 accumulation.  Both
- * roundings are relative to 2^-11 per term and unbiased, so their effect on
- * the sum is far smaller than 2^-11 unless the off-diagonal part dominates and
- * is dominated by a few terms; on Gaussian X with outlier channels it is
- * about 1e-6 relative.  output_error_codes() / output_error() form X Wq^T
- * itself.
+ * diagonal sum b is taken in float64 from float32 d and h, the off-diagonal
+ * part t - b is the float16 MFMA product of e (one power-of-two scale per
+ * row, rounded to 11 significant bits) with the float16 C (|C| <= 1), in
+ * float32 accumulation.  Those roundings are relative to the off-diagonal
+ * terms, whose size is set by b, not by t, so the metric's relative error
+ * grows with b / t: on Gaussian X with outlier channels (b / t about 1) it
+ * is about 1e-6; where the error cancels across correlated channels (as
+ * GPTQ's compensation makes it do) it reaches about 4e-5 (b / t) in the
+ * worst constructions tested (channel pairs of correlation 0.5 ... 0.999
+ * with errors of opposite sign, K = 16 ... 1024), so it meets a 1e-4 bar for
+ * b / t <= 2.  sums[2] / sums[0] reports b / t; above 2, use
+ * output_error_codes() or output_error(), which form X Wq^T itself.
  * workspace: ws_bytes >= output_error_gram_workspace_size(N, K); each call
  * needs its own.  Calls that share `gram` may run concurrently (it is only
  * read).
- * Tuning: the environment variable HD_GRAM_GROUPS = g (read per call) makes
- * the C E^T product use g groups of one workgroup per 256-row tile of E
- * instead of its default schedule; it changes only the order of the fp64
- * partial sums.
+ * Schedule: HD_SCHED_GRAM_GANGS (hdiag_set_schedule) changes only the order
+ * of the float64 partial sums.
  * Errors: HD_ERR_INVALID_ARG as quantize_blocks for fmt / B / N / K, NULL or
  * misaligned pointers, a short buffer or workspace, K % 8 != 0 for
  * output_gram; HD_ERR_UNSUPPORTED for a float32 X. */
@@ -350,7 +369,7 @@ hd_status output_error_gram(hd_format fmt, int32_t B, const uint8_t *codes, cons
  * for each quantisation, its format, block size and the device pointers of
  * its codes and scales (each as for output_error_gram).  out: device
  * double[count], out[q] = ||X Wq_q^T - X W^T||_F / sqrt(*ysq); sums (optional,
- * device, 2 count doubles): {||X (Wq_q - W)^T||_F^2, *ysq} for each q.
+ * device, 3 count doubles): {t_q, *ysq, b_q} for each q, as output_error_gram's.
  * The results are those of count output_error_gram calls up to the order of
  * the float64 partial sums; one MFMA walk over the stacked operand of all
  * count quantisations reads each C block for several of them at once.
@@ -423,8 +442,8 @@ hd_status dequantize_tensor_scaled(hd_format fmt, int32_t B, const uint8_t *code
  * Workspace: gptq_workspace_size(B, N, K) bytes, about 2.6 K^2 doubles +
  * 1.5 K^2 floats + 4 N K bytes (2 GB for K = 9728).  Errors as
  * quantize_blocks, plus K > 65535 and a negative or non-finite damp.
- * Tuning: the environment variable HD_GPTQ_GEMM_TILE = 64 or 128, read at
- * each call, fixes the output tile width of the factorisation's float64
+ * Schedule: HD_SCHED_GPTQ_TILE (hdiag_set_schedule) = 64 or 128 fixes the
+ * output tile width of the factorisation's float64
  * matrix-core products of 256 rows and columns and up; otherwise 128 is used
  * when it gives at least two rounds of workgroups.  Results agree to float64
  * rounding either way. */

@@ -142,6 +142,19 @@ def test_hdiag_noalloc_validation():
     assert L.hdiag_noalloc(None, hd.HD_BF16, 10, 0, None, None) == hd.HD_OK
 
 
+def test_schedule_settings():
+    """hdiag_set_schedule validates the setting and value on the host."""
+    L = hd.lib()
+    assert L.hdiag_set_schedule(hd.SCHED_GRAM_GANGS, 0) == hd.HD_OK
+    assert L.hdiag_set_schedule(hd.SCHED_GPTQ_TILE, 0) == hd.HD_OK
+    assert L.hdiag_set_schedule(2, 0) == hd.HD_ERR_INVALID_ARG
+    assert "unknown schedule" in L.hdiag_last_error().decode()
+    assert L.hdiag_set_schedule(hd.SCHED_GRAM_GANGS, -1) == hd.HD_ERR_INVALID_ARG
+    assert L.hdiag_set_schedule(hd.SCHED_GPTQ_TILE, 96) == hd.HD_ERR_INVALID_ARG
+    for v in (64, 128, 0):
+        hd.hdiag_set_schedule(hd.SCHED_GPTQ_TILE, v)
+
+
 def test_output_reference_validation():
     L = hd.lib()
     M, N, K = 300, 200, 512

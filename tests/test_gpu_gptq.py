@@ -103,17 +103,20 @@ def test_gptq_parity(fmt, B, method, ordered):
     compare(fmt, B, method, ordered, W, X, Hd)
 
 
-@pytest.mark.parametrize("tile", ["64", "128"])
-def test_gptq_parity_each_fp64_gemm_tile(tile, monkeypatch):
+@pytest.mark.parametrize("tile", [64, 128])
+def test_gptq_parity_each_fp64_gemm_tile(tile):
     """K = 1024: the recursion's top products are 512 x 512, small enough that
-    the automatic choice takes 64-wide tiles; HD_GPTQ_GEMM_TILE forces each
-    width of the float64 matrix-core kernel, and both must meet the parity bar
-    (ragged N, GPTQ-Ord, H-Optimal)."""
-    monkeypatch.setenv("HD_GPTQ_GEMM_TILE", tile)
-    N, K, M = 45, 1024, 2048
-    W, X = gptq_inputs(N, K, M, 31)
-    Hd = hd.gptq_hessian(dev(X))
-    compare(hd.NVFP4, 16, hd.H_OPT, True, W, X, Hd)
+    the automatic choice takes 64-wide tiles; the schedule setting
+    SCHED_GPTQ_TILE forces each width of the float64 matrix-core kernel, and
+    both must meet the parity bar (ragged N, GPTQ-Ord, H-Optimal)."""
+    hd.hdiag_set_schedule(hd.SCHED_GPTQ_TILE, tile)
+    try:
+        N, K, M = 45, 1024, 2048
+        W, X = gptq_inputs(N, K, M, 31)
+        Hd = hd.gptq_hessian(dev(X))
+        compare(hd.NVFP4, 16, hd.H_OPT, True, W, X, Hd)
+    finally:
+        hd.hdiag_set_schedule(hd.SCHED_GPTQ_TILE, 0)
 
 
 @pytest.mark.parametrize("N,K,B,fmt", [(1, 8, 8, hd.NVFP4), (3, 24, 8, hd.INT8_E4M3), (5, 40, 8, hd.MXFP4),

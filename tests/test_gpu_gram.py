@@ -119,8 +119,32 @@ def test_output_error_gram_parity(fmt, B, M, N, K):
     oe_o, d_o, y_o = oracle.output_error(synth.bits(X), synth.bits(W), oracle.dequantize(fmt, B, npy(c), sc_np(s), N, K),
                                          sums=True)
     assert out.item() == pytest.approx(oe_o, rel=1e-4)
-    np.testing.assert_allclose(npy(sums), [d_o, y_o], rtol=1e-4)
+    np.testing.assert_allclose(npy(sums)[:2], [d_o, y_o], rtol=1e-4)
     assert ysq.item() == pytest.approx(y_o, rel=1e-4)
+    # the third value is the exact diagonal part sum_j d_j^2 h_j
+    Wq = oracle.dequantize(fmt, B, npy(c), sc_np(s), N, K).astype(np.float64)
+    Dd = Wq - W.float().numpy().astype(np.float64)
+    b_o = float((Dd ** 2 @ oracle.hdiag(synth.bits(X)).astype(np.float64)).sum())
+    assert sums[2].item() == pytest.approx(b_o, rel=1e-6)
+
+
+@pytest.mark.parametrize("fmt", [hd.FP8_E4M3S, hd.MXFP8])
+@pytest.mark.parametrize("method", [hd.NAIVE, hd.SSE_OPT, hd.H_OPT])
+def test_output_error_gram_configs_width(fmt, method):
+    """E4M3 elements on weights of the configs' width (std 0.02), where the
+    E4M3-scale Naive collapses most blocks to the zero scale: all three scale
+    choices, Gram route against the oracle's direct fp64 product."""
+    M, N, K, B = 300, 200, 512, 32
+    X = acts(M, K, 61)
+    W = synth.weights("t4", N, K, std=0.02, seed=62, gain_seed=63)
+    Xd, Wd = dev(X), dev(W)
+    h = hd.hdiag(Xd)
+    c, s, _ = hd.quantize_blocks(method, fmt, B, Wd, h=h if method == hd.H_OPT else None)
+    gram = hd.output_gram(Xd, h=h)
+    ysq = hd.output_reference_gram(Wd, gram)
+    out = hd.output_error_gram(fmt, B, c, s, Wd, gram, ysq).item()
+    Wq = oracle.dequantize(fmt, B, npy(c), sc_np(s), N, K)
+    assert out == pytest.approx(oracle.output_error(synth.bits(X), synth.bits(W), Wq), rel=1e-4)
 
 
 @pytest.mark.parametrize("fmt,B", [(hd.INT8_E4M3, 32), (hd.NVFP4, 16)])
@@ -184,22 +208,25 @@ def test_output_error_gram_no_rows():
     assert ysq.item() == 0.0 and sums[0].item() == 0.0 and np.isnan(out.item())
 
 
-def test_output_error_gram_partition_and_repeat(monkeypatch):
-    """How the K-block pairs are split between workgroups (HD_GRAM_GROUPS
-    runs) changes only the summation order; repeated calls agree bit for
-    bit."""
+def test_output_error_gram_partition_and_repeat():
+    """How the K-block pairs are split between workgroups (the schedule
+    setting SCHED_GRAM_GANGS) changes only the summation order; repeated
+    calls agree bit for bit."""
     M, N, K, B = 600, 300, 1536, 32
     X, W = dev(acts(M, K, 21)), dev(weights_for(hd.INT8_E4M3, N, K, 22))
     c, s, _ = hd.quantize_blocks(hd.SSE_OPT, hd.INT8_E4M3, B, W)
     gram = hd.output_gram(X)
     ysq = hd.output_reference_gram(W, gram)
     vals = []
-    for nq in ("1", "2", "5", "21", "1000"):
-        monkeypatch.setenv("HD_GRAM_GROUPS", nq)
-        a = hd.output_error_gram(hd.INT8_E4M3, B, c, s, W, gram, ysq).item()
-        b = hd.output_error_gram(hd.INT8_E4M3, B, c, s, W, gram, ysq).item()
-        assert a == b
-        vals.append(a)
+    try:
+        for nq in (1, 2, 5, 21, 1000, 0):
+            hd.hdiag_set_schedule(hd.SCHED_GRAM_GANGS, nq)
+            a = hd.output_error_gram(hd.INT8_E4M3, B, c, s, W, gram, ysq).item()
+            b = hd.output_error_gram(hd.INT8_E4M3, B, c, s, W, gram, ysq).item()
+            assert a == b
+            vals.append(a)
+    finally:
+        hd.hdiag_set_schedule(hd.SCHED_GRAM_GANGS, 0)
     assert max(vals) == pytest.approx(min(vals), rel=1e-9)
     generic = hd.output_error(X, W, hd.dequantize(hd.INT8_E4M3, B, c, s, N, K)).item()
     assert vals[0] == pytest.approx(generic, rel=1e-4)
@@ -234,7 +261,7 @@ def test_output_error_gram_wide_rows():
     oe_o, d_o, y_o = oracle.output_error(synth.bits(X), synth.bits(W),
                                          oracle.dequantize(hd.INT8_E4M3, B, npy(c), sc_np(s), N, K), sums=True)
     assert out.item() == pytest.approx(oe_o, rel=1e-4)
-    np.testing.assert_allclose(npy(sums), [d_o, y_o], rtol=1e-4)
+    np.testing.assert_allclose(npy(sums)[:2], [d_o, y_o], rtol=1e-4)
 
 
 @pytest.mark.parametrize("N,K", [(300, 512), (2560, 1536), (40, 520)])
@@ -322,3 +349,79 @@ def test_output_error_gram_correlated_x():
         out = hd.output_error_gram(fmt, B, c, s, Wd, gram, ysq).item()
         Wq = oracle.dequantize(fmt, B, npy(c), sc_np(s), N, K)
         assert out == pytest.approx(oracle.output_error(synth.bits(X), synth.bits(W), Wq), rel=1e-4)
+
+
+def _paired_x(M, K, rho, seed):
+    rng = np.random.default_rng(seed)
+    Z = rng.standard_normal((M, K))
+    X = Z.copy()
+    X[:, 1::2] = rho * Z[:, 0::2] + np.sqrt(1.0 - rho * rho) * Z[:, 1::2]
+    return torch.from_numpy(X.astype(np.float32)).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("rho", [0.5, 0.875, 0.99])
+def test_output_error_gram_cancellation(rho):
+    """Quantisation errors of opposite sign on channel pairs of correlation
+    rho, so t = ||X D^T||^2 falls to about b (1 - rho), b the diagonal sum:
+    the route's float16 error scales with b / t, which sums[2] / sums[0]
+    reports.  W is built as W' - D with W' on the INT8 grid of fixed scales
+    and |D| under half a step, so the codes give Wq = W' and D exactly."""
+    M, N, K, B, fmt = 2048, 64, 256, 32, hd.INT8_E4M3
+    X = _paired_x(M, K, rho, 11)
+    rng = np.random.default_rng(12)
+    sc = np.full((N, K // B), 0x38, dtype=np.uint8)  # E4M3 1.0: s = fl32(1 / 127)
+    s = np.float32(oracle.scale_value(fmt, 0x38))
+    Wp = (s * rng.integers(-100, 101, (N, K)).astype(np.float32)).astype(np.float32)
+    Dp = np.zeros((N, K), dtype=np.float32)
+    Dp[:, 0::2] = rng.uniform(-0.3, 0.3, (N, K // 2)).astype(np.float32) * s
+    Dp[:, 1::2] = -Dp[:, 0::2]
+    W = (Wp - Dp).astype(np.float32)
+    Wd, Xd = dev(torch.from_numpy(W)), dev(X)
+    c, _ = hd.encode_blocks(fmt, B, Wd, dev(torch.from_numpy(sc)))
+    Wq = oracle.dequantize(fmt, B, npy(c), sc, N, K)
+    np.testing.assert_array_equal(Wq, Wp)
+    gram = hd.output_gram(Xd)
+    ysq = hd.output_reference_gram(Wd, gram)
+    out, sums = hd.output_error_gram(fmt, B, c, dev(torch.from_numpy(sc)), Wd, gram, ysq, sums=True)
+    torch.cuda.synchronize()
+    oe_o, t_o, _ = oracle.output_error(synth.bits(X), W, Wq, sums=True)
+    ratio = sums[2].item() / sums[0].item()
+    assert ratio == pytest.approx(1.0 / (1.0 - rho), rel=0.15)
+    err = abs(out.item() - oe_o) / oe_o
+    assert err <= 5e-5 * ratio + 1e-6, (err, ratio)
+    if ratio <= 2.0:
+        assert err <= 1e-4
+    # the direct product has no such dependence
+    direct = hd.output_error(Xd, Wd, dev(torch.from_numpy(Wq))).item()
+    assert direct == pytest.approx(oe_o, rel=1e-4)
+
+
+def test_output_error_gram_after_gptq_on_correlated_x():
+    """GPTQ-quantised W on correlated activations: GPTQ pushes each error
+    against the channels correlated with it, which lowers t below b.  The
+    Gram route stays within its stated bound (4e-5 per unit of the b / t it
+    reports) and within 1e-4 whenever b / t <= 2; the direct route within 1e-4."""
+    M, N, K, B = 2048, 128, 512, 16
+    rng = np.random.default_rng(93)
+    Xf = rng.standard_normal((M, 16)) @ rng.standard_normal((16, K)) + 0.3 * rng.standard_normal((M, K))
+    X = torch.from_numpy(Xf.astype(np.float32)).to(torch.bfloat16)
+    W = weights_for(hd.NVFP4, N, K, 94)
+    Xd, Wd = dev(X), dev(W)
+    H = hd.gptq_hessian(Xd)
+    gram = hd.output_gram(Xd)
+    ysq = hd.output_reference_gram(Wd, gram)
+    for fmt, m in ((hd.NVFP4, hd.H_OPT), (hd.INT8_E4M3, hd.SSE_OPT)):
+        c, s, _, info = hd.gptq_quantize(m, fmt, B, Wd, H)
+        out, sums = hd.output_error_gram(fmt, B, c, s, Wd, gram, ysq, sums=True)
+        Wq = hd.dequantize(fmt, B, c, s, N, K)
+        direct = hd.output_error(Xd, Wd, Wq).item()
+        torch.cuda.synchronize()
+        assert info.item() == 0
+        oe_o = oracle.output_error(synth.bits(X), synth.bits(W), npy(Wq))
+        ratio = sums[2].item() / sums[0].item()
+        assert ratio > 1.0  # GPTQ's errors cancel across correlated channels
+        err = abs(out.item() - oe_o) / oe_o
+        assert err <= 5e-5 * ratio + 1e-6, (fmt, err, ratio)
+        if ratio <= 2.0:
+            assert err <= 1e-4
+        assert direct == pytest.approx(oe_o, rel=1e-4)

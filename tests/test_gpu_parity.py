@@ -148,6 +148,46 @@ def test_search_parity(fmt, B, method):
     check_search(fmt, B, W, h_for(K, 11), method)
 
 
+@pytest.mark.parametrize("fmt", [hd.FP8_E4M3S, hd.MXFP8])
+@pytest.mark.parametrize("B", BLOCKS)
+@pytest.mark.parametrize("method", [hd.SSE_OPT, hd.H_OPT])
+def test_search_parity_configs_width(fmt, B, method):
+    """E4M3 elements at the configs' weight width (std 0.02, Student-t with a
+    per-row gain), where the Naive E4M3 scale of most blocks falls into the
+    zero bin and the search walks down to the grid's small-scale end."""
+    N, K = 300, 1024
+    W = synth.weights("t4", N, K, std=0.02, seed=2500 + fmt * 10 + B, gain_seed=2501 + B)
+    if fmt == hd.FP8_E4M3S:
+        _, s_n, _ = oracle.quantize(hd.NAIVE, fmt, B, synth.bits(W))
+        assert (s_n == 0).mean() > 0.5  # the Naive collapse the pages describe
+    check_search(fmt, B, W, h_for(K, 13), method)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("method", [hd.SSE_OPT, hd.H_OPT])
+def test_search_parity_near_saturation(fmt, method):
+    """Blocks with one outlier 6-40x the rest, so the optimum clips it: the
+    chosen scale saturates an element in many blocks, where the kernel's
+    float32 residual of the clipped element is rounded (at most 2^-24
+    relative; the oracle subtracts exactly)."""
+    N, K, B = 256, 1024, 32
+    rng = np.random.default_rng(6000 + fmt)
+    W = rng.standard_normal((N, K)) * 0.02
+    col = rng.integers(0, B, (N, K // B)) + np.arange(K // B) * B
+    W[np.arange(N)[:, None], col] *= rng.uniform(6.0, 40.0, (N, K // B))
+    Wt = torch.from_numpy(W.astype(np.float32)).to(torch.bfloat16)
+    frac = check_search(fmt, B, Wt, h_for(K, 14), method)
+    assert frac >= 0.9999
+    # the case is exercised: in some blocks the chosen scale clips the
+    # outlier (|w| / s beyond the largest element)
+    _, s_g, _ = hd.quantize_blocks(method, fmt, B, dev(Wt), h=dev(torch.from_numpy(h_for(K, 14))))
+    sv = np.array([oracle.scale_value(fmt, int(c)) for c in range(256)])[npy(s_g).astype(np.int64)]
+    qmax = {hd.INT8_E4M3: 127.0, hd.NVINT4: 7.0, hd.MXFP8: 448.0, hd.FP8_E4M3S: 448.0}.get(fmt, 6.0)
+    amax = np.abs(Wt.float().numpy()).reshape(N, K // B, B).max(axis=2)
+    if fmt != hd.FP8_E4M3S:  # E4M3 elements on E4M3 scales almost never clip
+        assert (amax > qmax * sv).mean() > 0.01
+
+
 @pytest.mark.parametrize("fmt", [hd.INT8_E4M3, hd.NVFP4])
 def test_search_parity_fp32_inputs(fmt):
     W = weights_for(fmt, 100, 512, 31, dtype=torch.float32)
