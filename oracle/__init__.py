@@ -69,6 +69,7 @@ def lib():
         L.orc_quantize_tensor_scaled.argtypes = [i32, i32, i32, P, i32, i64, i64, P, P, P, P, P, i32]
         L.orc_dequantize_tensor_scaled.argtypes = [i32, i32, P, P, ctypes.c_float, i64, i64, P, i32]
         L.orc_gptq.argtypes = [i32, i32, i32, P, i32, i64, i64, P, dbl, i32, P, P, P, i32]
+        L.orc_gptq_emulated.argtypes = [i32, i32, i32, P, i32, i64, i64, P, dbl, i32, P, P, P, i32, i32]
         L.orc_max_threads.argtypes = []
         _lib = L
     return _lib
@@ -263,6 +264,25 @@ def gptq(method, fmt, B, W, H, damp=0.01, ordered=False, nthreads=0):
     rc = lib().orc_gptq(method, fmt, B, _ptr(W), _dt(W), N, K, _ptr(H), float(damp), int(bool(ordered)),
                         _ptr(codes), _ptr(scales), _ptr(order), nthreads)
     _check(rc, "gptq")
+    return codes, scales, order
+
+
+# precision experiment flags of gptq_emulated (see oracle.c)
+GPTQ_EMUL_H32, GPTQ_EMUL_U32, GPTQ_EMUL_W32, GPTQ_EMUL_HULP = 1, 2, 4, 8
+
+
+def gptq_emulated(method, fmt, B, W, H, emul, damp=0.01, ordered=False, nthreads=0):
+    """gptq() with selected quantities rounded to float32 or perturbed by one
+    float64 ulp (flags above): a precision experiment, not a reference."""
+    W = np.ascontiguousarray(W)
+    N, K = W.shape
+    H = np.ascontiguousarray(H, np.float64)
+    codes = np.zeros(codes_shape(fmt, N, K), np.uint8)
+    scales = np.zeros((N, K // B), scale_dtype(fmt))
+    order = np.zeros(K // B, np.int32)
+    rc = lib().orc_gptq_emulated(method, fmt, B, _ptr(W), _dt(W), N, K, _ptr(H), float(damp), int(bool(ordered)),
+                                 _ptr(codes), _ptr(scales), _ptr(order), nthreads, int(emul))
+    _check(rc, "gptq_emulated")
     return codes, scales, order
 
 

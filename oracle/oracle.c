@@ -942,8 +942,36 @@ static int inverse_upper_factor(const double *H, double *U, int64_t n)
  *             later column k: w_k -= e U_jk.  Working weights are float64.
  * Outputs codes / scales in the original column order; block_order[i] is the
  * original index of the i-th block column processed (may be NULL). */
+/* Precision experiment (test infrastructure, not a reference): GPTQ as
+ * orc_gptq, with selected quantities carried in float32 or perturbed, to
+ * measure how far the column loop's decisions move under rounding alone.
+ *   GPTQ_EMUL_H32  : H rounded to float32 (an H formed in float32);
+ *   GPTQ_EMUL_U32  : the factor U rounded to float32;
+ *   GPTQ_EMUL_W32  : working weights stored in float32 after every update,
+ *                    the propagated error e and each product e U_ck in float32;
+ *   GPTQ_EMUL_HULP : every off-diagonal H_ij with i + j odd moved by one
+ *                    float64 ulp (a float64 computation in another order). */
+enum { GPTQ_EMUL_H32 = 1, GPTQ_EMUL_U32 = 2, GPTQ_EMUL_W32 = 4, GPTQ_EMUL_HULP = 8 };
+static int gptq_impl(int method, int fmt, int B, const void *W, int wdt, int64_t N, int64_t K, const double *H,
+                     double damp, int ordered, uint8_t *codes, uint8_t *scales, int32_t *block_order, int nthreads,
+                     int emul);
+
 int orc_gptq(int method, int fmt, int B, const void *W, int wdt, int64_t N, int64_t K, const double *H,
              double damp, int ordered, uint8_t *codes, uint8_t *scales, int32_t *block_order, int nthreads)
+{
+    return gptq_impl(method, fmt, B, W, wdt, N, K, H, damp, ordered, codes, scales, block_order, nthreads, 0);
+}
+
+int orc_gptq_emulated(int method, int fmt, int B, const void *W, int wdt, int64_t N, int64_t K, const double *H,
+                      double damp, int ordered, uint8_t *codes, uint8_t *scales, int32_t *block_order, int nthreads,
+                      int emul)
+{
+    return gptq_impl(method, fmt, B, W, wdt, N, K, H, damp, ordered, codes, scales, block_order, nthreads, emul);
+}
+
+static int gptq_impl(int method, int fmt, int B, const void *W, int wdt, int64_t N, int64_t K, const double *H,
+                     double damp, int ordered, uint8_t *codes, uint8_t *scales, int32_t *block_order, int nthreads,
+                     int emul)
 {
     init_tables();
     if (check_common(fmt, B, N, K) != ORC_OK || (wdt != DT_F32 && wdt != DT_BF16) || !H || damp < 0.0 || B > 256)
@@ -1017,14 +1045,23 @@ int orc_gptq(int method, int fmt, int B, const void *W, int wdt, int64_t N, int6
         for (int64_t i = 0; i < nb; i++)
             block_order[i] = (int32_t)perm[i];
     for (int64_t i = 0; i < K; i++) {
-        for (int64_t j = 0; j < K; j++)
-            Hp[i * K + j] = H[col[i] * K + col[j]];
+        for (int64_t j = 0; j < K; j++) {
+            double v = H[col[i] * K + col[j]];
+            if (emul & GPTQ_EMUL_H32)
+                v = (double)(float)v;
+            if ((emul & GPTQ_EMUL_HULP) && col[i] != col[j] && ((col[i] + col[j]) & 1))
+                v = nextafter(v, v > 0.0 ? INFINITY : -INFINITY);
+            Hp[i * K + j] = v;
+        }
         Hp[i * K + i] += lambda;
         om[i] = (double)h[col[i]];
     }
     rc = inverse_upper_factor(Hp, U, K);
     if (rc != ORC_OK)
         goto done;
+    if (emul & GPTQ_EMUL_U32)
+        for (int64_t i = 0; i < K * K; i++)
+            U[i] = (double)(float)U[i];
     for (int64_t n = 0; n < N; n++)
         for (int64_t i = 0; i < K; i++)
             Wc[n * K + i] = (double)widen(W, wdt, n * K + col[i]);
@@ -1054,8 +1091,14 @@ int orc_gptq(int method, int fmt, int B, const void *W, int wdt, int64_t N, int6
                     const int cb = enc_elem(fmt, s, (float)wr[c], &wq);
                     put_code(fmt, codes, N, K, n, col[c], cb);
                     const double e = (wr[c] - (double)wq) / U[c * K + c];
-                    for (int64_t k = c + 1; k < K; k++)
-                        wr[k] -= e * U[c * K + k];
+                    if (emul & GPTQ_EMUL_W32) {
+                        const float ef = (float)e;
+                        for (int64_t k = c + 1; k < K; k++)
+                            wr[k] = (double)((float)wr[k] - ef * (float)U[c * K + k]);
+                    } else {
+                        for (int64_t k = c + 1; k < K; k++)
+                            wr[k] -= e * U[c * K + k];
+                    }
                 }
             }
         }
