@@ -20,16 +20,22 @@
 //      (L^-1)21 = -(L22^-1) L21 (L11^-1), all float64 GEMMs, on the matrix
 //      cores from 256 rows and columns up).  Then
 //      (Hp + lambda I)^-1 = U^T U with U = J L^-1 J (upper triangular), and the
-//      loop uses V[c][k] = U[c][k] / U[c][c] in float32.
+//      loop uses V[c][k] = U[c][k] / U[c][c] in float64.
 //   5. The column loop over panels of BL = 128 (256 for B = 256) columns:
 //      gptq_panel_kernel walks a panel with one wave per row (each lane
 //      holding BL / 64 working values in registers): at each
 //      quantisation block it picks every row's scale with the method from the
-//      current values (the full-grid argmin with the lanes splitting the
-//      candidates, or the FP16 alternation), then encodes the block's columns
-//      one by one, broadcasting each error e = w - q to the row's lanes, which
-//      apply w_k -= e V[c][k] inside the panel; gptq_trail_kernel then applies
-//      the panel's errors to every later column (an fp32 matrix-core GEMM).
+//      current values rounded to float32 (the quantiser's input; the
+//      full-grid argmin with the lanes splitting the candidates, or the FP16
+//      alternation), then encodes the block's columns one by one,
+//      broadcasting each error e = w - q to the row's lanes, which apply
+//      w_k -= e V[c][k] inside the panel; then W[:, pe:] -= E V[panel, pe:]
+//      applies the panel's errors to every later column (the float64
+//      matrix-core GEMM of the factorisation).  Working weights, V and the
+//      errors are float64: GPTQ's decisions cascade along a row (a flipped
+//      element changes every later compensation), and with float32 working
+//      weights about 0.3% of INT8 elements moved against a float64 loop,
+//      while float64 rounding in another order moved none.
 // Codes and scales are written at the original column / block positions.
 #include <algorithm>
 #include <cstdlib>
@@ -142,12 +148,12 @@ __global__ __launch_bounds__(256) void gptq_rank_kernel(const double *__restrict
 }
 
 // Processing-order maps: col[i] = original column of processed column i,
-// hp[i] = h[col[i]]; Wp[n][i] = W[n][col[i]] as float32.
+// hp[i] = h[col[i]]; Wp[n][i] = W[n][col[i]] as float64.
 template <typename T>
 __global__ __launch_bounds__(256) void gptq_gather_kernel(const T *__restrict__ W, int64_t N, int64_t K, int B,
                                                           const int *__restrict__ perm, const float *__restrict__ h,
                                                           int *__restrict__ col, float *__restrict__ hp,
-                                                          float *__restrict__ Wp)
+                                                          double *__restrict__ Wp)
 {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= K) return;
@@ -158,8 +164,8 @@ __global__ __launch_bounds__(256) void gptq_gather_kernel(const T *__restrict__ 
     }
     for (int64_t n = blockIdx.y; n < N; n += gridDim.y) {
         const int64_t e = n * K + c;
-        Wp[n * K + i] = sizeof(T) == 2 ? __uint_as_float((uint32_t)((const uint16_t *)W)[e] << 16)
-                                       : ((const float *)W)[e];
+        Wp[n * K + i] = (double)(sizeof(T) == 2 ? __uint_as_float((uint32_t)((const uint16_t *)W)[e] << 16)
+                                                : ((const float *)W)[e]);
     }
 }
 
@@ -177,14 +183,14 @@ __global__ __launch_bounds__(256) void gptq_build_p_kernel(const float *__restri
     P[i * K + j] = v;
 }
 
-// V[c][k] = U[c][k] / U[c][c] for k > c, U[c][k] = Li[K-1-c][K-1-k] (float32).
+// V[c][k] = U[c][k] / U[c][c] for k > c, U[c][k] = Li[K-1-c][K-1-k] (float64).
 __global__ __launch_bounds__(256) void gptq_build_v_kernel(const double *__restrict__ Li, int64_t K,
-                                                           float *__restrict__ V)
+                                                           double *__restrict__ V)
 {
     const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x, c = blockIdx.y;
     if (k >= K) return;
     const int64_t rc = K - 1 - c;
-    V[c * K + k] = k > c ? (float)(Li[rc * K + (K - 1 - k)] / Li[rc * K + rc]) : 0.0f;
+    V[c * K + k] = k > c ? Li[rc * K + (K - 1 - k)] / Li[rc * K + rc] : 0.0;
 }
 
 // ---------------------------------------------- float64 factorisation ---
@@ -736,13 +742,15 @@ __device__ int gq_alternation(const float *v, const float *om, int B)
 }
 
 // One panel [p0, p0 + 64 SEGP) of the column loop: one wave per row, four
-// rows per workgroup, each lane holding SEGP consecutive working values.
+// rows per workgroup, each lane holding SEGP consecutive float64 working
+// values.  A column is encoded from its working value rounded to float32 (as
+// the scale choice sees it); its error e = w - q is taken in float64.
 template <int EK, int SK, int KIND, bool WEIGHTED, int SEGP>
-__global__ __launch_bounds__(256) void gptq_panel_kernel(float *__restrict__ Wp, const float *__restrict__ V,
+__global__ __launch_bounds__(256) void gptq_panel_kernel(double *__restrict__ Wp, const double *__restrict__ V,
                                                          const float *__restrict__ hp, const int *__restrict__ col,
                                                          int64_t N, int64_t K, int B, int64_t p0, int ocp,
                                                          uint8_t *__restrict__ codes, uint8_t *__restrict__ scales,
-                                                         float *__restrict__ E)
+                                                         double *__restrict__ E)
 {
     constexpr int BL = 64 * SEGP;
     __shared__ float blk[4][256 + 4];
@@ -753,20 +761,20 @@ __global__ __launch_bounds__(256) void gptq_panel_kernel(float *__restrict__ Wp,
     const int64_t pe = min(p0 + BL, K);
     const int64_t nb = K / B;
 
-    float w[SEGP];
+    double w[SEGP];
 #pragma unroll
     for (int i = 0; i < SEGP; ++i) {
         const int64_t c = p0 + l * SEGP + i;
-        w[i] = (active && c < pe) ? Wp[n * K + c] : 0.0f;
+        w[i] = (active && c < pe) ? Wp[n * K + c] : 0.0;
     }
     // vp[u][i]: V[c][p0 + l SEGP + i] for the next column c = u (mod 4)
-    float vp[4][SEGP];
+    double vp[4][SEGP];
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int i = 0; i < SEGP; ++i) {
             const int64_t c = p0 + u, k = p0 + l * SEGP + i;
-            vp[u][i] = (c < pe && k > c && k < pe) ? V[c * K + k] : 0.0f;
+            vp[u][i] = (c < pe && k > c && k < pe) ? V[c * K + k] : 0.0;
         }
     for (int64_t cs = p0; cs < pe; cs += B) {
         // the block's current values, and its h
@@ -774,7 +782,7 @@ __global__ __launch_bounds__(256) void gptq_panel_kernel(float *__restrict__ Wp,
 #pragma unroll
         for (int i = 0; i < SEGP; ++i) {
             const int64_t c = p0 + l * SEGP + i;
-            if (c >= cs && c < cs + B) blk[r][c - cs] = w[i];
+            if (c >= cs && c < cs + B) blk[r][c - cs] = (float)w[i];
         }
         if (WEIGHTED)
             for (int j = tid; j < B; j += 256) oms[j] = hp[cs + j];
@@ -829,17 +837,18 @@ __global__ __launch_bounds__(256) void gptq_panel_kernel(float *__restrict__ Wp,
             for (int u = 0; u < 4; ++u) {
                 const int64_t c = c4 + u;
                 const int own = (int)((c - p0) / SEGP), slot = (int)((c - p0) % SEGP);
-                float e = 0.0f;
+                double e = 0.0;
                 if (l == own) {
-                    float wv = 0.0f;
+                    double wd = 0.0;
 #pragma unroll
                     for (int i = 0; i < SEGP; ++i)
-                        if (i == slot) wv = w[i];
+                        if (i == slot) wd = w[i];
+                    const float wv = (float)wd;
                     const float a = fabsf(wv);
                     const float x = s != 0.0f ? quotient<SK, false>(a, s, rs) : 0.0f;
                     const float y = round_elem<EK>(x);
                     const float wq = s * y;
-                    e = wv - (__builtin_signbitf(wv) ? -wq : wq);
+                    e = wd - (double)(__builtin_signbitf(wv) ? -wq : wq);
                     const uint32_t cd = elem_code<EK>(elem_index<EK>(y), __builtin_signbitf(wv) != 0);
                     if (active) {
                         E[n * BL + (c - p0)] = e;
@@ -858,104 +867,18 @@ __global__ __launch_bounds__(256) void gptq_panel_kernel(float *__restrict__ Wp,
 #pragma unroll
                 for (int i = 0; i < SEGP; ++i) {
                     const int64_t k = p0 + l * SEGP + i;
-                    if (k > c && k < pe) w[i] = __builtin_fmaf(-e, vp[u][i], w[i]);
+                    if (k > c && k < pe) w[i] = __builtin_fma(-e, vp[u][i], w[i]);
                 }
                 // the V row of column c + 4
                 const int64_t cn = c + 4;
 #pragma unroll
                 for (int i = 0; i < SEGP; ++i) {
                     const int64_t k = p0 + l * SEGP + i;
-                    vp[u][i] = (cn < pe && k > cn && k < pe) ? V[cn * K + k] : 0.0f;
+                    vp[u][i] = (cn < pe && k > cn && k < pe) ? V[cn * K + k] : 0.0;
                 }
             }
         }
     }
-}
-
-// Wp[n][k] -= sum_{c in panel} E[n][c - p0] V[c][k] for k >= pe, on the
-// float32 matrix cores (v_mfma_f32_32x32x2f32: lane l supplies A[l % 32][l / 32]
-// and B[l / 32][l % 32] of a 32 x 2 by 2 x 32 step and holds
-// C[8 (v / 4) + 4 (l / 32) + v % 4][l % 32], v = 0..15).  128 rows of W x 128
-// columns per workgroup of four waves, 64 x 64 (2 x 2 MFMA tiles) per wave;
-// the panel's BL errors in chunks of 32 through LDS (E chunk stored
-// panel-column-major, both with a pitch of 160 floats so the two half-waves
-// of a fragment read hit different bank halves), the next chunk loaded into
-// registers while the current one is multiplied.  BL, K and the panel end pe
-// are multiples of 4 (the loads are 16-byte vectors).
-typedef float gq_f16v __attribute__((ext_vector_type(16)));
-static constexpr int TR_PITCH = 160;
-
-__global__ __launch_bounds__(256) void gptq_trail_kernel(float *__restrict__ Wp, const float *__restrict__ V,
-                                                         const float *__restrict__ E, int64_t N, int64_t K,
-                                                         int64_t p0, int BL, int64_t pe)
-{
-    __shared__ __attribute__((aligned(16))) float Es[32 * TR_PITCH];
-    __shared__ __attribute__((aligned(16))) float Vs[32 * TR_PITCH];
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, wm = wv & 1, wn = wv >> 1;
-    const int64_t n0 = (int64_t)blockIdx.y * 128, k0 = pe + (int64_t)blockIdx.x * 128;
-    // staging: E rows n0 + t / 2, chunk columns 16 (t % 2) ..; V chunk rows
-    // t / 8, columns k0 + 16 (t % 8) ..
-    const int er = tid >> 1, ec = (tid & 1) * 16, vr = tid >> 3, vc = (tid & 7) * 16;
-    float4 re[4], rv[4];
-    auto fetch = [&](int c0) {
-        const int64_t n = n0 + er;
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            re[q] = n < N ? *reinterpret_cast<const float4 *>(E + n * BL + c0 + ec + 4 * q) : make_float4(0, 0, 0, 0);
-        const float *vrow = V + (p0 + c0 + vr) * K;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int64_t k = k0 + vc + 4 * q;
-            rv[q] = k < K ? *reinterpret_cast<const float4 *>(vrow + k) : make_float4(0, 0, 0, 0);
-        }
-    };
-    gq_f16v acc[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-    fetch(0);
-    const int fr = lane & 31, fk = lane >> 5;
-    for (int c0 = 0; c0 < BL; c0 += 32) {
-        __syncthreads();
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            Es[(ec + 4 * q + 0) * TR_PITCH + er] = re[q].x;
-            Es[(ec + 4 * q + 1) * TR_PITCH + er] = re[q].y;
-            Es[(ec + 4 * q + 2) * TR_PITCH + er] = re[q].z;
-            Es[(ec + 4 * q + 3) * TR_PITCH + er] = re[q].w;
-            *reinterpret_cast<float4 *>(&Vs[vr * TR_PITCH + vc + 4 * q]) = rv[q];
-        }
-        __syncthreads();
-        if (c0 + 32 < BL) fetch(c0 + 32);
-#pragma unroll
-        for (int kk = 0; kk < 16; ++kk) {
-            const int row = (2 * kk + fk) * TR_PITCH;
-            float a[2], bv[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) a[i] = Es[row + wm * 64 + i * 32 + fr];
-#pragma unroll
-            for (int j = 0; j < 2; ++j) bv[j] = Vs[row + wn * 64 + j * 32 + fr];
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], bv[j], acc[i][j], 0, 0, 0);
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int64_t n = n0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * fk + (v & 3);
-            if (n >= N) continue;
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int64_t k = k0 + wn * 64 + j * 32 + fr;
-                if (k < K) Wp[n * K + k] -= acc[i][j][v];
-            }
-        }
 }
 
 // ------------------------------------------------------------ launchers ---
@@ -1013,9 +936,9 @@ static GqLayout gq_layout(int B, int64_t N, int64_t K)
     L.Li = o; o += al256(K * K * 8);
     L.T = o; o += al256(h1 * h1 * 8);
     L.T2 = o; o += al256(K * K * 8 / 2);
-    L.V = o; o += al256(K * K * 4);
-    L.Wp = o; o += al256(N * K * 4);
-    L.E = o; o += al256(N * BL * 4);
+    L.V = o; o += al256(K * K * 8);
+    L.Wp = o; o += al256(N * K * 8);
+    L.E = o; o += al256(N * BL * 8);
     L.h = o; o += al256(K * 4);
     L.hp = o; o += al256(K * 4);
     L.col = o; o += al256(K * 4);
@@ -1030,8 +953,8 @@ static GqLayout gq_layout(int B, int64_t N, int64_t K)
 int64_t gptq_ws(int B, int64_t N, int64_t K) { return gq_layout(B, N, K).bytes; }
 
 template <int EK, int SK, int KIND, bool WEIGHTED>
-static void gq_panel(float *Wp, const float *V, const float *hp, const int *col, int64_t N, int64_t K, int B,
-                     int64_t p0, int ocp, uint8_t *codes, uint8_t *scales, float *E, hipStream_t st)
+static void gq_panel(double *Wp, const double *V, const float *hp, const int *col, int64_t N, int64_t K, int B,
+                     int64_t p0, int ocp, uint8_t *codes, uint8_t *scales, double *E, hipStream_t st)
 {
     const unsigned g = (unsigned)((N + 3) / 4);
     if (B > 128)
@@ -1043,8 +966,8 @@ static void gq_panel(float *Wp, const float *V, const float *hp, const int *col,
 }
 
 template <int EK, int SK>
-static void gq_panel_m(int method, float *Wp, const float *V, const float *hp, const int *col, int64_t N, int64_t K,
-                       int B, int64_t p0, uint8_t *codes, uint8_t *scales, float *E, hipStream_t st)
+static void gq_panel_m(int method, double *Wp, const double *V, const float *hp, const int *col, int64_t N,
+                       int64_t K, int B, int64_t p0, uint8_t *codes, uint8_t *scales, double *E, hipStream_t st)
 {
     if (method == HD_NAIVE || method == HD_NAIVE_OCP) {
         gq_panel<EK, SK, GQ_NAIVE, false>(Wp, V, hp, col, N, K, B, p0, method == HD_NAIVE_OCP, codes, scales, E,
@@ -1074,14 +997,15 @@ static void gq_loss(const void *W, int wdt, int64_t N, int64_t K, int B, const f
 template <int EK, int SK>
 static hipError_t gq_run(int method, int B, const void *W, int wdt, int64_t N, int64_t K, const float *H, double damp,
                          int ordered, uint8_t *codes, uint8_t *scales, int32_t *block_order, int *info_out, void *ws,
-                         int fmt, const float *Vg, const int *info_g, hipStream_t st)
+                         int fmt, const double *Vg, const int *info_g, hipStream_t st)
 {
     const GqLayout L = gq_layout(B, N, K);
     char *base = static_cast<char *>(ws);
     double *P = reinterpret_cast<double *>(base + L.P), *Li = reinterpret_cast<double *>(base + L.Li);
     double *T = reinterpret_cast<double *>(base + L.T), *T2 = reinterpret_cast<double *>(base + L.T2);
-    float *V = reinterpret_cast<float *>(base + L.V), *Wp = reinterpret_cast<float *>(base + L.Wp);
-    float *E = reinterpret_cast<float *>(base + L.E), *h = reinterpret_cast<float *>(base + L.h);
+    double *V = reinterpret_cast<double *>(base + L.V), *Wp = reinterpret_cast<double *>(base + L.Wp);
+    double *E = reinterpret_cast<double *>(base + L.E);
+    float *h = reinterpret_cast<float *>(base + L.h);
     float *hp = reinterpret_cast<float *>(base + L.hp);
     int *col = reinterpret_cast<int *>(base + L.col), *perm = reinterpret_cast<int *>(base + L.perm);
     double *loss = reinterpret_cast<double *>(base + L.loss), *stat = reinterpret_cast<double *>(base + L.stat);
@@ -1117,7 +1041,7 @@ static hipError_t gq_run(int method, int B, const void *W, int wdt, int64_t N, i
     if (Vg != nullptr) {
         // a factor of the sequential order made by gptq_factor: its status, its V
         gptq_copy_int_kernel<<<1, 64, 0, st>>>(info_g, info);
-        V = const_cast<float *>(Vg);
+        V = const_cast<double *>(Vg);
     } else {
         gptq_build_p_kernel<<<dim3((unsigned)((K + 255) / 256), (unsigned)K), 256, 0, st>>>(H, K, col, stat, P);
         // the recursion multiplies by whole diagonal blocks of L^-1, whose upper
@@ -1130,20 +1054,20 @@ static hipError_t gq_run(int method, int B, const void *W, int wdt, int64_t N, i
     for (int64_t p0 = 0; p0 < K; p0 += BL) {
         const int64_t pe = std::min<int64_t>(p0 + BL, K);
         gq_panel_m<EK, SK>(method, Wp, V, hp, col, N, K, B, p0, codes, scales, E, st);
-        if (pe < K) {
-            const dim3 g((unsigned)((K - pe + 127) / 128), (unsigned)((N + 127) / 128));
-            gptq_trail_kernel<<<g, 256, 0, st>>>(Wp, V, E, N, K, p0, (int)(pe - p0), pe);
-        }
+        // the panel's errors into every later column: Wp[:, pe:] -= E V[p0:pe, pe:]
+        // (beta = 1, alpha = -1: one float64 rounding per entry)
+        if (pe < K)
+            dgemm<false>(N, K - pe, pe - p0, -1.0, E, pe - p0, V + p0 * K + pe, K, 1.0, Wp + pe, K, 0, st);
     }
     return hipGetLastError();
 }
 
-// The float32 factor V of the sequential order, made once for every GPTQ
-// call that shares H and the damping: V = fl32((L^-1)^T) (what the column
-// loop reads) at byte GQ_FACTOR_V of the factor buffer, the factorisation's
-// status (0, or 1 + the first non-positive pivot) at byte 0.
+// The float64 factor V of the sequential order, made once for every GPTQ
+// call that shares H and the damping: V (what the column loop reads) at byte
+// GQ_FACTOR_V of the factor buffer, the factorisation's status (0, or 1 + the
+// first non-positive pivot) at byte 0.
 static constexpr int64_t GQ_FACTOR_V = 256;
-int64_t gptq_factor_bytes(int64_t K) { return GQ_FACTOR_V + al256(K * K * 4); }
+int64_t gptq_factor_bytes(int64_t K) { return GQ_FACTOR_V + al256(K * K * 8); }
 int64_t gptq_factor_ws(int64_t K) { return gptq_ws(32, 0, K); }
 
 hipError_t launch_gptq_factor(const float *H, int64_t K, double damp, void *factor, int *info_out, void *ws,
@@ -1157,7 +1081,7 @@ hipError_t launch_gptq_factor(const float *H, int64_t K, double damp, void *fact
     int *col = reinterpret_cast<int *>(base + L.col);
     double *stat = reinterpret_cast<double *>(base + L.stat);
     int *info = static_cast<int *>(factor);
-    float *V = reinterpret_cast<float *>(static_cast<char *>(factor) + GQ_FACTOR_V);
+    double *V = reinterpret_cast<double *>(static_cast<char *>(factor) + GQ_FACTOR_V);
     gptq_diag_kernel<<<1, 256, 0, st>>>(H, K, damp, h, stat);
     gptq_iota_kernel<<<(unsigned)((K + 255) / 256), 256, 0, st>>>(col, K, info);
     gptq_build_p_kernel<<<dim3((unsigned)((K + 255) / 256), (unsigned)K), 256, 0, st>>>(H, K, col, stat, P);
@@ -1170,7 +1094,7 @@ hipError_t launch_gptq_factor(const float *H, int64_t K, double damp, void *fact
 
 static hipError_t gq_dispatch(int method, int fmt, int B, const void *W, int wdt, int64_t N, int64_t K,
                               const float *H, double damp, int ordered, uint8_t *codes, uint8_t *scales,
-                              int32_t *block_order, int *info, void *ws, const float *Vg, const int *info_g,
+                              int32_t *block_order, int *info, void *ws, const double *Vg, const int *info_g,
                               hipStream_t st);
 
 hipError_t launch_gptq(int method, int fmt, int B, const void *W, int wdt, int64_t N, int64_t K, const float *H,
@@ -1186,14 +1110,14 @@ hipError_t launch_gptq_factored(int method, int fmt, int B, const void *W, int w
                                 int32_t *block_order, int *info, void *ws, hipStream_t st)
 {
     const int *info_g = static_cast<const int *>(factor);
-    const float *Vg = reinterpret_cast<const float *>(static_cast<const char *>(factor) + GQ_FACTOR_V);
+    const double *Vg = reinterpret_cast<const double *>(static_cast<const char *>(factor) + GQ_FACTOR_V);
     return gq_dispatch(method, fmt, B, W, wdt, N, K, H, 0.0, 0, codes, scales, block_order, info, ws, Vg, info_g,
                        st);
 }
 
 static hipError_t gq_dispatch(int method, int fmt, int B, const void *W, int wdt, int64_t N, int64_t K,
                               const float *H, double damp, int ordered, uint8_t *codes, uint8_t *scales,
-                              int32_t *block_order, int *info, void *ws, const float *Vg, const int *info_g,
+                              int32_t *block_order, int *info, void *ws, const double *Vg, const int *info_g,
                               hipStream_t st)
 {
 #define HD_GQ_FMT(F)                                                                                          \

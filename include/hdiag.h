@@ -435,12 +435,14 @@ hd_status dequantize_tensor_scaled(hd_format fmt, int32_t B, const uint8_t *code
  *     order, each block's scales are chosen by `method` from the block's
  *     current (compensated) values, then its columns are encoded in order and
  *     each error (w_c - q_c) / U_cc is subtracted, times U_ck, from every later
- *     column k (the working weights are float32; the factorisation is
- *     float64);
+ *     column k (scales and codes are taken from the working values rounded to
+ *     float32, the quantiser's input; the working weights, the errors, the
+ *     factor and the updates are float64, so decisions follow a float64
+ *     computation of the loop);
  *   - info (optional, device int32): 0, or 1 + the first pivot at which the
  *     damped Hessian was not positive definite (that pivot is replaced by 1).
- * Workspace: gptq_workspace_size(B, N, K) bytes, about 2.6 K^2 doubles +
- * 1.5 K^2 floats + 4 N K bytes (2 GB for K = 9728).  Errors as
+ * Workspace: gptq_workspace_size(B, N, K) bytes, about 3.8 K^2 doubles +
+ * 8 N K bytes (3.1 GB for K = 9728, N = 2560).  Errors as
  * quantize_blocks, plus K > 65535 and a negative or non-finite damp.
  * Schedule: HD_SCHED_GPTQ_TILE (hdiag_set_schedule) = 64 or 128 fixes the
  * output tile width of the factorisation's float64

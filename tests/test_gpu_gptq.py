@@ -4,18 +4,18 @@ Quantization") with the oracle.
 - gptq_hessian: H = X^T X against the oracle's float64 product, entry by entry
   within the float32-accumulation bound 2e-6 * sum_t |x_ti x_tj|.
 - gptq_quantize: the oracle runs on the GPU's own H (widened to float64), so
-  the comparison isolates the column loop: the GPU carries the working weights
-  in float32 (the oracle in float64) and its factor of (H + lambda I)^-1 in
-  float64 by a different algorithm, so a quantisation decision may flip where
-  a value sits within rounding of a decision boundary, and a flip changes the
-  compensation of the rest of that row.  Bars: block order identical (GPTQ-Ord),
-  scales identical on >= 99.5% of blocks, dequantised weights identical on
-  >= 99.5% of elements, weight and output error within 1e-3 relative.  For the
-  binary16 scales (1024 codes per binade) the snapped least-squares scale of a
-  block moves by a code under much smaller perturbations, and one such block
-  changes all of its elements: there the two agreement bars are 98.5%.  With a
-  diagonal H there is nothing to compensate and the result must equal
-  quantize_blocks bit for bit.
+  the comparison isolates the column loop.  Both carry the working weights,
+  the errors and the factor of (H + lambda I)^-1 in float64 (the GPU by a
+  recursive Cholesky-with-inverse and panel-blocked updates, the oracle
+  column by column), so they differ only by float64 rounding order.  GPTQ's
+  decisions cascade along a row, but a float64-order perturbation moves no
+  decision on the oracle's own precision experiment
+  (tests/test_oracle_gptq_precision.py: with float32 working weights about
+  0.3% of INT8 elements move).  Bars, as the search's: block order identical
+  (GPTQ-Ord), scales identical on >= 99.99% of blocks, dequantised weights
+  identical on >= 99.99% of elements, weight and output error within 1e-4
+  relative.  With a diagonal H there is nothing to compensate and the result
+  must equal quantize_blocks bit for bit.
 """
 import numpy as np
 import pytest
@@ -79,13 +79,15 @@ def compare(fmt, B, method, ordered, W, X, Hd):
     sg = scales_np(s)
     Wq = npy(hd.dequantize(fmt, B, c, s, N, K))
     Wq_o = oracle.dequantize(fmt, B, c_o, s_o, N, K)
-    bar = 0.985 if fmt in hd.F16_SCALES else 0.995
-    assert (sg == s_o).mean() >= bar, (sg == s_o).mean()
-    assert (Wq == Wq_o).mean() >= bar, (Wq == Wq_o).mean()
+    fs, fe = (sg == s_o).mean(), (Wq == Wq_o).mean()
+    print("gptq agreement fmt %d B %d method %d ordered %d: scales %.6f elements %.6f"
+          % (fmt, B, method, int(ordered), fs, fe), flush=True)
+    assert fs >= 0.9999, fs
+    assert fe >= 0.9999, fe
     Xb = synth.bits(X)
-    assert oracle.weight_error(Wb, Wq) == pytest.approx(oracle.weight_error(Wb, Wq_o), rel=1e-3)
+    assert oracle.weight_error(Wb, Wq) == pytest.approx(oracle.weight_error(Wb, Wq_o), rel=1e-4)
     oe, oe_o = oracle.output_error(Xb, Wb, Wq), oracle.output_error(Xb, Wb, Wq_o)
-    assert oe == pytest.approx(oe_o, rel=1e-3)
+    assert oe == pytest.approx(oe_o, rel=1e-4)
     return oe
 
 
@@ -147,9 +149,19 @@ def test_gptq_parity_two_panels_and_fp32_weights():
     for fmt, B, m in ((hd.MXFP4, 32, hd.NAIVE_OCP), (hd.NVFP4, 16, hd.H_OPT)):
         c, s, _, info = hd.gptq_quantize(m, fmt, B, dev(W.float()), Hd)
         c_o, s_o, _ = oracle.gptq(m, fmt, B, synth.bits(W.float()), npy(Hd).astype(np.float64))
-        assert (scales_np(s) == s_o).mean() >= 0.995
+        assert (scales_np(s) == s_o).mean() >= 0.9999
         Wq = npy(hd.dequantize(fmt, B, c, s, N, K))
-        assert (Wq == oracle.dequantize(fmt, B, c_o, s_o, N, K)).mean() >= 0.995
+        assert (Wq == oracle.dequantize(fmt, B, c_o, s_o, N, K)).mean() >= 0.9999
+
+
+@pytest.mark.parametrize("fmt,B,method", [(hd.INT8_E4M3, 32, hd.SSE_OPT), (hd.NVFP4, 16, hd.H_OPT)])
+def test_gptq_parity_many_panels(fmt, B, method):
+    """K = 2048: sixteen 128-column panels, so each row's decisions cascade
+    through fifteen trailing updates on the float64 matrix cores."""
+    N, K, M = 256, 2048, 4096
+    W, X = gptq_inputs(N, K, M, 17)
+    Hd = hd.gptq_hessian(dev(X))
+    compare(fmt, B, method, False, W, X, Hd)
 
 
 @pytest.mark.parametrize("fmt,B", [(hd.NVFP4, 16), (hd.INT8_E4M3, 128), (hd.FP4_F16, 128), (hd.MXFP4, 32)])
