@@ -40,6 +40,8 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 bool valid_dtype(int d) { return d == HD_F32 || d == HD_BF16; }
 bool valid_fmt(int f) { return f >= HD_INT8_E4M3 && f <= HD_INT4_F16; }
 bool valid_block(int32_t B) { return B == 8 || B == 16 || B == 32 || B == 64 || B == 128 || B == 256; }
+// B = 4 (two blocks per 8-weight lane chunk): Naive, encode and dequantize only
+bool valid_block4(int32_t B) { return B == 4 || valid_block(B); }
 bool is_4bit(int f)
 {
     return f == HD_NVFP4 || f == HD_MXFP4 || f == HD_NVFP4_UE4M4 || f == HD_NVFP4_UE5M3 || f == HD_NVINT4 ||
@@ -67,10 +69,13 @@ hd_status check_ptr(const void *p, const char *name, bool needed)
         if (s_ != HD_OK) return s_;                                   \
     } while (0)
 
-hd_status check_quant_shape(int fmt, int32_t B, int64_t N, int64_t K)
+hd_status check_quant_shape(int fmt, int32_t B, int64_t N, int64_t K, bool naive_path = false)
 {
     HD_REQUIRE(valid_fmt(fmt), "unknown format %d", fmt);
-    HD_REQUIRE(valid_block(B), "block size %d is not one of 8, 16, 32, 64, 128, 256", (int)B);
+    if (B == 4 && !naive_path)
+        return fail(HD_ERR_UNSUPPORTED, "block size 4 is supported by Naive scales, encode_blocks and dequantize only");
+    HD_REQUIRE(valid_block4(B), "block size %d is not one of 4, 8, 16, 32, 64, 128, 256", (int)B);
+    HD_REQUIRE(B != 4 || K % 8 == 0, "block size 4 needs K %% 8 == 0 (K=%lld)", (long long)K);
     HD_REQUIRE(N >= 0 && K >= 0, "negative size N=%lld K=%lld", (long long)N, (long long)K);
     HD_REQUIRE(K % B == 0, "K=%lld is not a multiple of B=%d", (long long)K, (int)B);
     HD_REQUIRE(N <= (int64_t)1 << 40 && K <= (int64_t)1 << 31, "size too large");
@@ -172,7 +177,7 @@ hd_status quantize_blocks(hd_method method, hd_format fmt, int32_t B, const void
 {
     HD_REQUIRE(method >= HD_NAIVE && method <= HD_NAIVE_OCP, "unknown method %d", (int)method);
     HD_REQUIRE(valid_dtype(wt), "unknown dtype %d", (int)wt);
-    hd_status s = check_quant_shape(fmt, B, N, K);
+    hd_status s = check_quant_shape(fmt, B, N, K, method == HD_NAIVE || method == HD_NAIVE_OCP);
     if (s != HD_OK) return s;
     HD_REQUIRE(method != HD_H_OPT || h != nullptr, "H-Optimal needs h");
     if (N == 0 || K == 0) return ok();
@@ -200,7 +205,7 @@ hd_status encode_blocks(hd_format fmt, int32_t B, const void *W, hd_dtype wt, in
                         const uint8_t *scales_in, const float *h, uint8_t *codes, float *block_obj, void *stream)
 {
     HD_REQUIRE(valid_dtype(wt), "unknown dtype %d", (int)wt);
-    hd_status s = check_quant_shape(fmt, B, N, K);
+    hd_status s = check_quant_shape(fmt, B, N, K, true);
     if (s != HD_OK) return s;
     if (N == 0 || K == 0) return ok();
     HD_CHECK_PTR(W, true);
@@ -218,7 +223,7 @@ hd_status dequantize(hd_format fmt, int32_t B, const uint8_t *codes, const uint8
                      void *Wq, hd_dtype out_t, void *stream)
 {
     HD_REQUIRE(valid_dtype(out_t), "unknown dtype %d", (int)out_t);
-    hd_status s = check_quant_shape(fmt, B, N, K);
+    hd_status s = check_quant_shape(fmt, B, N, K, true);
     if (s != HD_OK) return s;
     if (N == 0 || K == 0) return ok();
     HD_CHECK_PTR(codes, true);
@@ -519,7 +524,7 @@ hd_status quantize_blocks_tensor_scaled(hd_method method, hd_format fmt, int32_t
     HD_REQUIRE(method >= HD_NAIVE && method <= HD_H_OPT, "unknown method %d (the OCP rule needs E8M0 scales)",
                (int)method);
     HD_REQUIRE(valid_dtype(wt), "unknown dtype %d", (int)wt);
-    hd_status s = check_quant_shape(fmt, B, N, K);
+    hd_status s = check_quant_shape(fmt, B, N, K, method == HD_NAIVE);
     if (s != HD_OK) return s;
     HD_REQUIRE(is_e4m3_scaled(fmt), "per-tensor scaling needs an E4M3 block-scale format");
     HD_REQUIRE(method != HD_H_OPT || h != nullptr, "H-Optimal needs h");
@@ -550,7 +555,7 @@ hd_status dequantize_tensor_scaled(hd_format fmt, int32_t B, const uint8_t *code
                                    void *stream)
 {
     HD_REQUIRE(valid_dtype(out_t), "unknown dtype %d", (int)out_t);
-    hd_status s = check_quant_shape(fmt, B, N, K);
+    hd_status s = check_quant_shape(fmt, B, N, K, true);
     if (s != HD_OK) return s;
     HD_REQUIRE(is_e4m3_scaled(fmt), "per-tensor scaling needs an E4M3 block-scale format");
     if (N == 0 || K == 0) return ok();

@@ -16,9 +16,20 @@ namespace hd {
 // float32 loads, the lanes of a wave on consecutive addresses: loads strided
 // across lanes were measured to cut the read rate), so a block of B weights
 // is B / 8 adjacent lanes of one sub-chunk (512 % B == 0), combined with
-// shuffles.  Codes go out as 4 (4-bit) or 8 bytes per lane and sub-chunk,
-// again on consecutive addresses; the first lane of a block writes its scale.
+// shuffles; for B = 4 a lane's eight weights are two whole blocks.  Codes go
+// out as 4 (4-bit) or 8 bytes per lane and sub-chunk, again on consecutive
+// addresses; the first lane of a block writes its scale.
 static constexpr int ENC_SUB = 4;
+
+// Scale code of one block with largest magnitude amax: given, or the Naive
+// snap (the OCP floor rule on E8M0 grids when ocp is set).
+template <int EK, int SK, bool GIVEN>
+__device__ __forceinline__ int enc_scale_code(float amax, const uint8_t *scales_in, int64_t blk, bool in, int ocp)
+{
+    if (GIVEN) return in ? load_scale<SK>(scales_in, blk) : 0;
+    if constexpr (SK == SCALE_E8M0) return ocp ? ocp_code<EK>(amax) : naive_code<EK, SK>(amax);
+    return naive_code<EK, SK>(amax);
+}
 
 template <int EK, int SK, typename T, int B, bool GIVEN, bool OBJ>
 __global__ __launch_bounds__(256) void encode_kernel(const T *__restrict__ W, int64_t total, int64_t K,
@@ -27,11 +38,11 @@ __global__ __launch_bounds__(256) void encode_kernel(const T *__restrict__ W, in
                                                      uint8_t *__restrict__ codes, uint8_t *__restrict__ scales,
                                                      float *__restrict__ block_obj, int ocp)
 {
-    constexpr int LPB = B / 8;  // lanes per block
+    constexpr int LPB = B >= 8 ? B / 8 : 1;  // lanes per block (B = 4: two blocks per lane)
     constexpr bool ONE_STEP = sizeof(T) == 2;
     const int lane = threadIdx.x & 63;
     const int64_t wbase = (((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6) * (64 * 8 * ENC_SUB);
-    // total % B == 0 and B % 8 == 0: a sub-chunk starting below total is
+    // total % 8 == 0 and total % B == 0: a sub-chunk starting below total is
     // whole, and the lanes of one block are all in or all out
     float w[ENC_SUB][8];
 #pragma unroll
@@ -53,6 +64,46 @@ __global__ __launch_bounds__(256) void encode_kernel(const T *__restrict__ W, in
             const int64_t k0 = e % K;  // rows hold K % 8 == 0 weights: no row end inside
 #pragma unroll
             for (int j = 0; j < 8; ++j) om[OBJ ? j : 0] = (double)h[k0 + j];
+        }
+        if constexpr (B == 4) {
+            // two blocks: each half is encoded as eight weights of which the
+            // last four are zeros (they encode to 0 and add nothing)
+            uint32_t c[8];
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb) {
+                float wh[8], amax = 0.0f;
+                double omh[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    wh[j] = j < 4 ? w[k][4 * hb + j] : 0.0f;
+                    omh[j] = (OBJ && weighted && in && j < 4) ? om[OBJ ? 4 * hb + j : 0] : 0.0;
+                    amax = fmaxf(amax, fabsf(wh[j]));
+                }
+                const int64_t blk = e / 4 + hb;
+                const int code = enc_scale_code<EK, SK, GIVEN>(amax, scales_in, blk, in, ocp);
+                const float s = (GIVEN ? scale_code_valid(SK, code) : true) ? scale_value(SK, code) : 0.0f;
+                const float r = (s != 0.0f) ? 1.0f / s : 0.0f;
+                uint32_t ch[8];
+                const double o = encode8<EK, SK, ONE_STEP, OBJ>(wh, s, r, (weighted && in) ? omh : nullptr, ch);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) c[4 * hb + j] = ch[j];
+                if (in) {
+                    if (!GIVEN) store_scale<SK>(scales, blk, code);
+                    if (OBJ) block_obj[blk] = (float)o;
+                }
+            }
+            if (!in) continue;
+            if (elem_4bit(EK)) {
+                uint32_t v = 0;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) v |= (c[j] & 15u) << (4 * j);
+                __builtin_nontemporal_store(v, reinterpret_cast<uint32_t *>(codes + e / 2));
+            } else {
+                const uint32_t lo = (c[0] & 255u) | ((c[1] & 255u) << 8) | ((c[2] & 255u) << 16) | ((c[3] & 255u) << 24);
+                const uint32_t hi = (c[4] & 255u) | ((c[5] & 255u) << 8) | ((c[6] & 255u) << 16) | ((c[7] & 255u) << 24);
+                __builtin_nontemporal_store((uint64_t)lo | ((uint64_t)hi << 32), reinterpret_cast<uint64_t *>(codes + e));
+            }
+            continue;
         }
         float amax = 0.0f;
 #pragma unroll
@@ -111,6 +162,7 @@ static hipError_t encode_b(int B, const void *W, int64_t N, int64_t K, const flo
             encode_kernel<EK, SK, T, BB, GIVEN, false><<<grid, 256, 0, st>>>(w, total, K, h, si, codes, scales, bo, ocp); \
         break;
     switch (B) {
+        HD_ENC_CASE(4)
         HD_ENC_CASE(8)
         HD_ENC_CASE(16)
         HD_ENC_CASE(32)
@@ -228,12 +280,13 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict_
     const int64_t base = wave * (64 * VPS * DQ_G) + (int64_t)lane * VPS;
     // all loads first (codes and scales of the DQ_G groups), then the stores
     uint64_t cw[DQ_G];
-    int sc[DQ_G];
+    int sc[DQ_G], sc2[DQ_G];
 #pragma unroll
     for (int g = 0; g < DQ_G; ++g) {
         const int64_t e = base + (int64_t)g * 64 * VPS;
         cw[g] = 0;
         sc[g] = 0;
+        sc2[g] = 0;
         if (e < total) {  // total % 8 == 0: a group starting inside is whole
             if (elem_4bit(EK))
                 cw[g] = VPS == 8 ? *reinterpret_cast<const uint32_t *>(codes + e / 2)
@@ -242,6 +295,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict_
                 cw[g] = VPS == 8 ? *reinterpret_cast<const uint64_t *>(codes + e)
                                  : *reinterpret_cast<const uint32_t *>(codes + e);
             sc[g] = load_scale<SK>(scales, e / B);
+            if (VPS > B) sc2[g] = load_scale<SK>(scales, e / B + 1);  // B = 4, bfloat16: two blocks
         }
     }
 #pragma unroll
@@ -251,6 +305,13 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict_
         const float s = scale_code_valid(SK, sc[g]) ? scale_value(SK, sc[g]) : 0.0f;
         float o[VPS];
         dq_group<EK, VPS>(cw[g], s, tscale, o);
+        if (VPS > B) {  // the second block's four outputs at its own scale
+            const float s2 = scale_code_valid(SK, sc2[g]) ? scale_value(SK, sc2[g]) : 0.0f;
+            float o2[VPS];
+            dq_group<EK, VPS>(cw[g], s2, tscale, o2);
+#pragma unroll
+            for (int j = VPS / 2; j < VPS; ++j) o[j] = o2[j];
+        }
         if (OUT_BF16) {
             uint4 v;
             v.x = f32_to_bf16(o[0]) | (f32_to_bf16(o[1]) << 16);

@@ -178,6 +178,10 @@ hd_status hdiag_noalloc(const void *X, hd_dtype xt, int64_t M, int64_t K, float 
 /* Choose the scale of every block and encode W with it.
  *   W      : [N, K] of dtype wt (float32 or bfloat16).
  *   B      : block size along K, one of 8, 16, 32, 64, 128, 256; K % B == 0.
+ *            B = 4 (the smallest block of "Is Finer Better?" App. F) is
+ *            accepted by the Naive methods, encode_blocks, dequantize and the
+ *            per-tensor-scaled pair, with K % 8 == 0; every other call
+ *            returns HD_ERR_UNSUPPORTED for it.
  *   h      : [K] float32, required for HD_H_OPT.  For HD_NAIVE it only weights
  *            the reported block objective (NULL: unweighted); ignored by
  *            HD_SSE_OPT.

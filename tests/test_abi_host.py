@@ -142,6 +142,25 @@ def test_hdiag_noalloc_validation():
     assert L.hdiag_noalloc(None, hd.HD_BF16, 10, 0, None, None) == hd.HD_OK
 
 
+def test_block4_only_on_the_naive_path():
+    """B = 4 is accepted by Naive / encode / dequantize (K % 8 == 0) and
+    refused as unsupported by the search and the codes-to-operand routes."""
+    L = hd.lib()
+    for m in (hd.SSE_OPT, hd.H_OPT):
+        rc = L.quantize_blocks(m, hd.NVFP4, 4, A, hd.HD_BF16, 4, 32, A, A, A, None, None)
+        assert rc == hd.HD_ERR_UNSUPPORTED and "block size 4" in L.hdiag_last_error().decode()
+    rc = L.quantize_blocks(hd.NAIVE, hd.NVFP4, 4, A, hd.HD_BF16, 4, 12, None, A, A, None, None)
+    assert rc == hd.HD_ERR_INVALID_ARG and "K % 8" in L.hdiag_last_error().decode()
+    assert L.quantize_blocks(hd.NAIVE, hd.NVFP4, 4, A, hd.HD_BF16, 0, 32, None, A, A, None, None) == hd.HD_OK
+    assert L.dequantize(hd.NVFP4, 4, A, A, 0, 32, A, hd.HD_F32, None) == hd.HD_OK
+    M, N, K = 300, 200, 512
+    rb = hd.output_reference_size(M, N, K)
+    ws = hd.output_error_codes_workspace_size(M, N, K)
+    rc = L.output_error_codes(hd.NVFP4, 4, A, hd.HD_BF16, M, A, A, N, K, A, rb, A, None, A, ws, None)
+    assert rc == hd.HD_ERR_UNSUPPORTED
+    assert L.gptq_workspace_size(4, 8, 64) == 0
+
+
 def test_schedule_settings():
     """hdiag_set_schedule validates the setting and value on the host."""
     L = hd.lib()

@@ -85,6 +85,66 @@ def test_naive_bit_exact(fmt, B, dtype):
     np.testing.assert_allclose(npy(obj_g), obj_o.astype(np.float32), rtol=2e-6)
 
 
+ALL_FMTS = FMTS + [hd.FP4_F16, hd.INT4_F16]
+
+
+def scales_np(s):
+    return npy(s.view(torch.int16)).view(np.uint16) if s.dtype == torch.float16 else npy(s)
+
+
+@pytest.mark.parametrize("fmt", ALL_FMTS)
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_block4_naive_encode_dequantize_bit_exact(fmt, dtype):
+    """B = 4 ("Is Finer Better?" App. F's smallest block): two blocks per
+    8-weight lane chunk.  Naive scales, codes and (h-weighted) objectives,
+    encode with given scales, and dequantize to float32 and bfloat16, all
+    bit-exact with the oracle; all-zero and single-nonzero blocks included."""
+    N, K, B = 37, 1032, 4  # ragged rows, K % 512 != 0
+    W = weights_for(fmt, N, K, 7000 + fmt, dtype).float()
+    W[2, :4] = 0.0
+    W[3, 4:8] = 0.0
+    W[3, 5] = 1.0
+    W = W.to(dtype)
+    h = h_for(K, 17)
+    hd_h = dev(torch.from_numpy(h))
+    c_o, s_o, obj_o = oracle.quantize(hd.NAIVE, fmt, B, synth.bits(W), h=h)
+    c_g, s_g, obj_g = hd.quantize_blocks(hd.NAIVE, fmt, B, dev(W), h=hd_h, block_obj=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(scales_np(s_g), s_o)
+    np.testing.assert_array_equal(npy(c_g), c_o)
+    np.testing.assert_allclose(npy(obj_g), obj_o.astype(np.float32), rtol=2e-6)
+    # encode at given scales (every block at a scale shifted from its Naive one)
+    s_in = s_g.clone()
+    if s_in.dtype == torch.uint8:
+        s_in = torch.clamp(s_in.to(torch.int16) - 3, 1, 126).to(torch.uint8)
+    c_e, _ = hd.encode_blocks(fmt, B, dev(W), s_in)
+    c_eo, _, _ = oracle.quantize(hd.NAIVE, fmt, B, synth.bits(W), scales_in=scales_np(s_in))
+    np.testing.assert_array_equal(npy(c_e), c_eo)
+    deq_o = oracle.dequantize(fmt, B, c_o, s_o, N, K)
+    np.testing.assert_array_equal(npy(hd.dequantize(fmt, B, c_g, s_g, N, K)), deq_o)
+    deq_b = hd.dequantize(fmt, B, c_g, s_g, N, K, dtype=torch.bfloat16)
+    assert torch.equal(deq_b.cpu(), torch.from_numpy(deq_o).to(torch.bfloat16))
+
+
+@pytest.mark.parametrize("fmt", [hd.MXFP4, hd.MXFP8])
+def test_block4_ocp_and_tensor_scaled(fmt):
+    N, K, B = 20, 512, 4
+    W = weights_for(fmt, N, K, 7100 + fmt)
+    c_o, s_o, _ = oracle.quantize(oracle.NAIVE_OCP, fmt, B, synth.bits(W))
+    c_g, s_g, _ = hd.quantize_blocks(hd.NAIVE_OCP, fmt, B, dev(W))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(npy(s_g), s_o)
+    np.testing.assert_array_equal(npy(c_g), c_o)
+    Wn = weights_for(hd.NVFP4, N, K, 7200)
+    c_t, s_t, ts, _ = hd.quantize_blocks_tensor_scaled(hd.NAIVE, hd.NVFP4, B, dev(Wn))
+    c_to, s_to, ts_o, _ = oracle.quantize_tensor_scaled(hd.NAIVE, hd.NVFP4, B, synth.bits(Wn))
+    np.testing.assert_array_equal(npy(s_t), s_to)
+    np.testing.assert_array_equal(npy(c_t), c_to)
+    assert ts.item() == ts_o
+    np.testing.assert_array_equal(npy(hd.dequantize_tensor_scaled(hd.NVFP4, B, c_t, s_t, ts, N, K)),
+                                  oracle.dequantize_tensor_scaled(hd.NVFP4, B, c_to, s_to, ts_o, N, K))
+
+
 @pytest.mark.parametrize("fmt", [hd.MXFP4, hd.MXFP8])
 @pytest.mark.parametrize("B", [8, 32, 256])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
