@@ -104,7 +104,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=8, help="rows of W in the CPU sample")
-    ap.add_argument("--suite", choices=["headline", "formats", "gptq", "sigma", "gemm", "hbm"], default="headline",
+    ap.add_argument("--suite", choices=["headline", "formats", "gptq", "sigma", "gemm", "hbm", "config3", "config5"],
+                    default="headline",
                     help="headline: the step above (one JSON line, the default); formats: every element / "
                          "scale format x B in {16, 32} x scale choice on the same W and h (one JSON line)")
     ap.add_argument("--eager", action="store_true",
@@ -144,6 +145,8 @@ def main():
         return gemm_suite(args, dev)
     if args.suite == "hbm":
         return hbm_suite(args, dev)
+    if args.suite in ("config3", "config5"):
+        return layer_suite(args, dev, int(args.suite[-1]))
 
     cfg = synth.CONFIGS[2]
     W_cpu, X_cpu = synth.config_inputs(2)
@@ -167,6 +170,7 @@ def main():
         ws_o = torch.empty(hd.output_error_gram_batch_workspace_size(len(blocks) * len(methods), N, K),
                            dtype=torch.uint8, device=dev)
         ysq = torch.empty(1, dtype=torch.float64, device=dev)
+        osums = torch.empty((len(blocks) * len(methods), 3), dtype=torch.float64, device=dev)
     else:
         ref = torch.empty(hd.output_reference_size(M, N, K), dtype=torch.uint8, device=dev)
         ws_o = torch.empty(hd.output_error_codes_workspace_size(M, N, K), dtype=torch.uint8, device=dev)
@@ -224,7 +228,8 @@ def main():
             # the 12 output errors in one call (one MFMA walk over their stacked operand)
             items = [(fmt, B, codes[(B, m)], scales[(B, m)]) for B in blocks for _, m in methods]
             timed("output_error", 0,
-                  lambda: hd.output_error_gram_batch(items, W, gram, ysq, workspace=ws_o, out=oerr.view(-1)), rec)
+                  lambda: hd.output_error_gram_batch(items, W, gram, ysq, sums=osums, workspace=ws_o,
+                                                     out=oerr.view(-1)), rec)
 
     for _ in range(args.warmup):
         step(False)
@@ -327,6 +332,12 @@ def main():
         for mi, (mname, _) in enumerate(methods):
             errs["B%d_%s" % (B, mname)] = {"weight_error": round(float(we[bi, mi]), 6),
                                            "output_error": round(float(oe[bi, mi]), 6)}
+
+    if gram_route:
+        # b / t of each quantisation (the diagonal part over the total): the
+        # Gram route meets the 1e-4 bar for b / t <= 2
+        sm = osums.cpu().numpy()
+        errs["gram_max_diag_over_total"] = round(float(np.max(sm[:, 2] / sm[:, 0])), 4)
 
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": "Gweights/s", "n_gpus": 1,
@@ -487,14 +498,65 @@ def gptq_suite(args, dev):
           flush=True)
 
 
+# relative tolerance under which two per-block objectives count as equal:
+# block_obj values are float64 sums rounded once to float32 (2^-24), so a
+# pair of B = 8 objectives and one B = 16 objective of the same elements
+# agree to a few 2^-24 when both blocks took the same codes
+BLOCK_TIE = 2.0 ** -20
+
+
+def block_pair_comparison(obj8, obj16):
+    """Per 16-weight block: the B = 8 error (its two 8-blocks' objectives
+    added) against the B = 16 error, both from quantize_blocks' block_obj
+    ("Is Finer Better?" §3.2, Fig. 2(a): the same tensor quantised at both
+    block sizes, MSE taken over the larger block).  Returns the fractions of
+    blocks above the diagonal (B = 8 worse), on it (within BLOCK_TIE) and
+    below.  Works on torch tensors [N, K/8] and [N, K/16] on any device."""
+    import torch
+    e8 = obj8.double().reshape(obj16.shape[0], -1, 2).sum(-1)
+    e16 = obj16.double()
+    tol = BLOCK_TIE * torch.maximum(e8, e16)
+    above = (e8 - e16 > tol).double().mean().item()
+    below = (e16 - e8 > tol).double().mean().item()
+    return {"above": above, "equal": 1.0 - above - below, "below": below}
+
+
+def mse_decomposition(W, Wq, scale_zero, B):
+    """The three parts of the per-tensor MSE that "Is Finer Better?" App. F
+    (Fig. 12) separates, from one quantisation: blocks whose scale is zero
+    (every element rounded to zero), the maximum-magnitude element of every
+    other block (the first one on ties), and the remaining elements.  W, Wq:
+    [N, K] tensors; scale_zero: bool [N, K/B].  Returns the three sums of
+    squared errors divided by N K (they add up to the MSE), in float64."""
+    import torch
+    N, K = W.shape
+    d2 = (Wq.double() - W.double()) ** 2
+    d2b = d2.reshape(N, K // B, B)
+    zero = scale_zero.reshape(N, K // B)
+    imax = W.abs().reshape(N, K // B, B).argmax(dim=-1, keepdim=True)
+    at_max = torch.gather(d2b, 2, imax).squeeze(-1)
+    total_b = d2b.sum(-1)
+    n = float(N * K)
+    s0 = total_b[zero].sum().item() / n
+    smax = at_max[~zero].sum().item() / n
+    srest = (total_b[~zero] - at_max[~zero]).sum().item() / n
+    return {"s_zero": s0, "x_max": smax, "x_other": srest}
+
+
 def sigma_suite(args, dev):
-    """Block size against tensor width ("Is Finer Better?", §3.2, §4.3,
-    §5.2): a seeded N(0, 1) tensor of 4096 x 4096 is scaled by sigma (40
-    values, 1e-4 .. 1) and quantised with E2M1 elements and Naive scales on
-    the UE4M3 (E4M3), UE4M4, UE5M3 and binary16 grids and UE4M3 under a
-    per-tensor scale (UE4M3-S, §5.1) at B = 8 .. 64; the
-    per-tensor MSE (from weight_error's sums) is reported as MSE / sigma^2,
-    with the sigma where B = 8 and B = 16 cross for each grid."""
+    """Block size against tensor width ("Is Finer Better?" §3.2 and Fig. 2,
+    §4.3, App. F, §5.2): a seeded N(0, 1) tensor of 4096 x 4096 is scaled by
+    sigma (40 values, 1e-4 .. 1) and quantised with E2M1 elements and Naive
+    scales on the UE4M3 (E4M3), UE4M4, UE5M3 and binary16 grids and UE4M3
+    under a per-tensor scale (UE4M3-S, §5.1) at B = 4 .. 64.  Reported:
+      - the per-tensor MSE (from weight_error's sums) as MSE / sigma^2, with
+        the sigma where B = 8 and B = 16 cross for each grid;
+      - per 16-weight block, the B = 8 against the B = 16 error (Fig. 2(a)):
+        the fractions of blocks above, on and below the diagonal, for every
+        sigma and grid and for the config-4 weights (4096 x 4096 Laplace,
+        std 0.02, per-row lognormal gain);
+      - for UE4M3 at B = 4, 8, 16, 32, the three parts of the MSE App. F
+        separates (zero-scale blocks, block maxima, other elements)."""
     import numpy as np
     import torch
 
@@ -506,11 +568,11 @@ def sigma_suite(args, dev):
     sigmas = [float(x) for x in np.geomspace(1e-4, 1.0, 40)]
     fmts = (hd.NVFP4, hd.NVFP4_UE4M4, hd.NVFP4_UE5M3, hd.FP4_F16)
     TS = -1  # marker: NVFP4 with a per-tensor scale (UE4M3-S)
-    blocks = (8, 16, 32, 64)
+    blocks = (4, 8, 16, 32, 64)
     names = {v: k for k, v in hd.FORMATS.items()}
     names[TS] = "NVFP4_TENSOR_SCALED"
     Wq = torch.empty((N, K), dtype=torch.float32, device=dev)
-    rows = []
+    rows, pairs, decomp = [], [], []
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
@@ -518,15 +580,22 @@ def sigma_suite(args, dev):
     for sg in sigmas:
         W = (Z * sg).contiguous()  # the synthetic input at this width
         for fmt in fmts + (TS,):
+            objs = {}
             for B in blocks:
                 if fmt == TS:  # UE4M3 block scales under a per-tensor scale
-                    c, sc, ts, _ = hd.quantize_blocks_tensor_scaled(hd.NAIVE, hd.NVFP4, B, W, workspace=ws_t)
+                    c, sc, ts, obj = hd.quantize_blocks_tensor_scaled(hd.NAIVE, hd.NVFP4, B, W, block_obj=True,
+                                                                      workspace=ws_t)
                     hd.dequantize_tensor_scaled(hd.NVFP4, B, c, sc, ts, N, K, out=Wq)
                 else:
-                    c, sc, _ = hd.quantize_blocks(hd.NAIVE, fmt, B, W)
+                    c, sc, obj = hd.quantize_blocks(hd.NAIVE, fmt, B, W, block_obj=True)
                     hd.dequantize(fmt, B, c, sc, N, K, out=Wq)
+                objs[B] = obj
                 _, sums = hd.weight_error(W, Wq, sums=True)
                 rows.append((sg, fmt, B, sums))
+                if fmt == hd.NVFP4 and B <= 32:
+                    decomp.append((sg, B, mse_decomposition(W, Wq, sc == 0, B)))
+            # (tensor-scaled objectives refer to W / s_T: the same comparison in other units)
+            pairs.append((sg, fmt, block_pair_comparison(objs[8], objs[16])))
     t1.record()
     torch.cuda.synchronize()
     out = []
@@ -544,10 +613,188 @@ def sigma_suite(args, dev):
                 f = d[i - 1] / (d[i - 1] - d[i])
                 xs.append(float(np.exp(np.log(sigmas[i - 1]) + f * (np.log(sigmas[i]) - np.log(sigmas[i - 1])))))
         crossings[names[fmt]] = xs
+    # the config-4 weights (the MX block-size sweep's tensor) at B = 8 / 16
+    W4 = synth.config_inputs(4)[0].to(dev)
+    cfg4 = {}
+    for fmt in fmts:
+        o8 = hd.quantize_blocks(hd.NAIVE, fmt, 8, W4, block_obj=True)[2]
+        o16 = hd.quantize_blocks(hd.NAIVE, fmt, 16, W4, block_obj=True)[2]
+        cfg4[names[fmt]] = block_pair_comparison(o8, o16)
     print(json.dumps({"suite": "sigma", "config": {"workload": "N(0, sigma^2) 4096x4096 fp32 (one seeded draw scaled), "
-                                                               "E2M1 elements, Naive scales", "sigmas": len(sigmas)},
+                                                               "E2M1 elements, Naive scales", "sigmas": len(sigmas),
+                                                   "blocks": list(blocks)},
                       "data": "synthetic", "quantizations": len(rows), "total_ms": round(t0.elapsed_time(t1), 3),
-                      "b8_b16_crossing_sigma": crossings, "rows": out}), flush=True)
+                      "b8_b16_crossing_sigma": crossings,
+                      "b8_vs_b16_per_block": [{"sigma": round(sg, 8), "format": names[f], **p} for sg, f, p in pairs],
+                      "b8_vs_b16_per_block_config4": cfg4,
+                      "ue4m3_mse_parts": [{"sigma": round(sg, 8), "B": B, **p} for sg, B, p in decomp],
+                      "rows": out}), flush=True)
+
+
+def _roof(bound, units, ms):
+    """Roofline figures of one stage from its algorithmic work per launch."""
+    t = ms * 1e-3
+    if bound == "hbm":
+        ach, peak, unit = units / t / 1e9, HBM_PEAK_GBS, "GB/s"
+    elif bound == "mfma":
+        ach, peak, unit = units / t / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
+    else:
+        ach, peak, unit = units / t / 1e12, VALU_PEAK_TOPS, "Tops/s"
+    return {"bound": bound, "achieved": round(ach, 3), "peak": round(peak, 3), "unit": unit,
+            "frac": round(ach / peak, 4), "avg_ms": round(ms, 4)}
+
+
+def layer_suite(args, dev, ci):
+    """Configuration 3 (NVFP4 on the down_proj stand-in W 2560x9728 with the
+    pages' full calibration X 244449x9728) or 5 (W 8192x28672, X
+    65536x28672): one pass of the hot path over the full X - hdiag, the scale
+    choices (config 3: NVFP4 B = 16, 32 x Naive / SSE / H-Optimal; config 5:
+    NVFP4 B = 16 and INT8 B = 128, Naive and H-Optimal), dequantize, weight
+    error, and the output error of every quantisation through G = X^T X
+    (output_gram, output_reference_gram, one output_error_gram_batch) and,
+    timed separately, through X W^T (output_reference, then one
+    output_error_codes per quantisation).  X is streamed to the GPU in row
+    chunks; per-stage GPU times are HIP-event averages over `steps` passes
+    after one warm-up."""
+    import numpy as np
+    import torch
+
+    import block_scaled_precision_hdiag_amd as hd
+    import synth
+
+    cfg = synth.CONFIGS[ci]
+    W = synth.config_inputs(ci, x_rows=0)[0].to(dev)
+    N, K = W.shape
+    xc = cfg["X"]
+    M = xc["M"]
+    X = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    r0 = 0
+    for ch in synth.activation_chunks(M, K, xc["seed"], xc["n_out"], xc["out_gain"], xc["idx_seed"]):
+        X[r0:r0 + ch.shape[0]].copy_(ch)
+        r0 += ch.shape[0]
+    torch.cuda.synchronize()
+    print("config %d: X %dx%d on the GPU" % (ci, M, K), file=sys.stderr, flush=True)
+    if ci == 3:
+        quants = [(hd.NVFP4, B, m) for B in (16, 32) for m in (hd.NAIVE, hd.SSE_OPT, hd.H_OPT)]
+    else:
+        quants = [(f, B, m) for f, B in ((hd.NVFP4, 16), (hd.INT8_E4M3, 128)) for m in (hd.NAIVE, hd.H_OPT)]
+    mname = {hd.NAIVE: "naive", hd.SSE_OPT: "sse", hd.H_OPT: "h"}
+    fname = {v: k for k, v in hd.FORMATS.items()}
+    nq = len(quants)
+    qstage = ["%s_%s_b%d" % ("naive" if m == hd.NAIVE else "search_" + mname[m], fname[f], B) for f, B, m in quants]
+    qmeta = {qstage[q]: quants[q] for q in range(nq)}
+    h = torch.empty(K, dtype=torch.float32, device=dev)
+    ws_h = torch.empty(hd.hdiag_workspace_size(M, K), dtype=torch.uint8, device=dev)
+    gram = torch.empty(hd.output_gram_size(K), dtype=torch.uint8, device=dev)
+    ws_g = torch.empty(hd.output_gram_workspace_size(M, K), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(hd.output_error_gram_batch_workspace_size(nq, N, K), dtype=torch.uint8, device=dev)
+    ysq = torch.empty(1, dtype=torch.float64, device=dev)
+    osums = torch.empty((nq, 3), dtype=torch.float64, device=dev)
+    codes = [torch.empty(hd.codes_shape(f, N, K), dtype=torch.uint8, device=dev) for f, _, _ in quants]
+    scales = [torch.empty((N, K // B), dtype=torch.uint8, device=dev) for _, B, _ in quants]
+    Wq = torch.empty((N, K), dtype=torch.float32, device=dev)
+    ws_w = torch.empty(hd.weight_error_workspace_size(N, K), dtype=torch.uint8, device=dev)
+    werr = torch.empty(nq, dtype=torch.float64, device=dev)
+    oerr = torch.empty(nq, dtype=torch.float64, device=dev)
+    events = []
+
+    def timed(stage, fn, rec):
+        if not rec:
+            return fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        events.append((stage, a, b))
+
+    def gram_pass(rec):
+        timed("hdiag", lambda: hd.hdiag(X, out=h, workspace=ws_h), rec)
+        timed("output_gram", lambda: hd.output_gram(X, h=h, gram=gram, workspace=ws_g), rec)
+        timed("output_reference_gram", lambda: hd.output_reference_gram(W, gram, workspace=ws_b, out=ysq), rec)
+        for q, (f, B, m) in enumerate(quants):
+            timed(qstage[q], lambda: hd.quantize_blocks(m, f, B, W, h=h, codes=codes[q], scales=scales[q]), rec)
+            timed("dequantize", lambda: hd.dequantize(f, B, codes[q], scales[q], N, K, out=Wq), rec)
+            timed("weight_error", lambda: hd.weight_error(W, Wq, workspace=ws_w, out=werr[q:q + 1]), rec)
+        items = [(f, B, codes[q], scales[q]) for q, (f, B, _) in enumerate(quants)]
+        timed("output_error_gram_batch",
+              lambda: hd.output_error_gram_batch(items, W, gram, ysq, sums=osums, workspace=ws_b, out=oerr), rec)
+
+    gram_pass(False)
+    torch.cuda.synchronize()
+    print("config %d: warm-up pass done" % ci, file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        gram_pass(True)
+    torch.cuda.synchronize()
+    pass_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    print("config %d: %d timed passes, %.2f ms each" % (ci, args.steps, pass_ms), file=sys.stderr, flush=True)
+    o_gram = oerr.cpu().numpy().copy()
+    w_err = werr.cpu().numpy().copy()
+    ratios = (osums[:, 2] / osums[:, 0]).cpu().numpy()
+
+    # the direct route: Y = X W^T stored once, then X Wq^T - Y per quantisation
+    ref = torch.empty(hd.output_reference_size(M, N, K), dtype=torch.uint8, device=dev)
+    ws_c = torch.empty(hd.output_error_codes_workspace_size(M, N, K), dtype=torch.uint8, device=dev)
+    o_dir = torch.empty(nq, dtype=torch.float64, device=dev)
+
+    def direct_pass(rec):
+        timed("output_reference", lambda: hd.output_reference(X, W, ref=ref), rec)
+        for q, (f, B, _) in enumerate(quants):
+            timed("output_error_codes", lambda: hd.output_error_codes(f, B, X, codes[q], scales[q], ref, N, K,
+                                                                      workspace=ws_c, out=o_dir[q:q + 1]), rec)
+
+    direct_pass(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        direct_pass(True)
+    torch.cuda.synchronize()
+    direct_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    o_direct = o_dir.cpu().numpy()
+
+    per = {}
+    for st, a, b in events:
+        per.setdefault(st, []).append(a.elapsed_time(b))
+    avg = {k: sum(v) / len(v) for k, v in per.items()}
+    nw = N * K
+    work = {"hdiag": ("hbm", M * K * 2 + K * 4), "output_gram": ("mfma", 1.0 * M * K * (K + 1)),
+            "output_reference_gram": ("mfma", 1.0 * N * K * K), "dequantize": ("hbm", None),
+            "weight_error": ("hbm", nw * 6), "output_error_gram_batch": ("mfma", nq * 1.0 * N * K * K),
+            "output_reference": ("mfma", 2.0 * M * N * K), "output_error_codes": ("mfma", 2.0 * M * N * K)}
+    stages = {}
+    for st, ms in avg.items():
+        if st in qmeta and qmeta[st][2] == hd.NAIVE:
+            f, B, _ = qmeta[st]
+            cb = 0.5 if f in hd.FOUR_BIT else 1.0
+            stages[st] = _roof("hbm", nw * (2 + cb) + nw // B, ms)
+        elif st in qmeta:
+            f, B, m = qmeta[st]
+            nc = hd.hdiag_format_info(f, 16)[2]
+            r = _roof("alu", nw * nc * SEARCH_OPS[mname[m]], ms)
+            r["basis"] = "full-grid equivalent"
+            r["gweights_per_s"] = round(nw / (ms * 1e-3) / 1e9, 2)
+            stages[st] = r
+        elif st == "dequantize":
+            stages[st] = {"avg_ms": round(ms, 4)}
+        else:
+            bound, units = work[st]
+            stages[st] = _roof(bound, units, ms)
+    errors = {}
+    for q, (f, B, m) in enumerate(quants):
+        errors["%s_b%d_%s" % (fname[f], B, mname[m])] = {
+            "weight_error": round(float(w_err[q]), 6), "output_error_gram": round(float(o_gram[q]), 6),
+            "output_error_direct": round(float(o_direct[q]), 6),
+            "gram_diag_over_total": round(float(ratios[q]), 4),
+            "gram_vs_direct_rel": float(abs(o_gram[q] - o_direct[q]) / o_direct[q])}
+    print(json.dumps({"suite": "config%d" % ci, "unit": "Gweights/s",
+                      "config": {"workload": "%s: W %dx%d bf16, X %dx%d bf16 (seeded synthetic stand-ins); %d "
+                                             "quantisations, hdiag, scale choice, dequantize, weight error and "
+                                             "output error per pass" % (cfg["name"], N, K, M, K, nq),
+                                 "W": [N, K], "X": [M, K]},
+                      "data": "synthetic", "steps": args.steps, "pass_ms_gram_route": round(pass_ms, 3),
+                      "direct_route_ms": round(direct_ms, 3),
+                      "value": round(nq * nw / (pass_ms * 1e-3) / 1e9, 3),
+                      "stages": stages, "errors": errors}), flush=True)
 
 
 def hbm_suite(args, dev):

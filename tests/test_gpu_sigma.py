@@ -43,7 +43,7 @@ def gpu_mse(fmt, B, W):
 
 @pytest.mark.parametrize("sigma", [3e-4, 1e-2, 5e-2])
 @pytest.mark.parametrize("fmt", [hd.NVFP4, hd.NVFP4_UE5M3, hd.FP4_F16])
-@pytest.mark.parametrize("B", [8, 16])
+@pytest.mark.parametrize("B", [4, 8, 16])
 def test_sigma_mse_parity(sigma, fmt, B):
     W = tensor(sigma)
     c, s, m = gpu_mse(fmt, B, W)
@@ -65,3 +65,28 @@ def test_crossover_and_collapse_on_the_gpu():
         assert gpu_mse(fmt, 8, lo)[2] < gpu_mse(fmt, 16, lo)[2]
     m = gpu_mse(hd.NVFP4, 16, tiny)[2]
     assert m == pytest.approx(float((tiny.double() ** 2).mean()), rel=1e-12)
+
+
+@pytest.mark.parametrize("sigma", [3e-3, 1e-2, 5e-2])
+@pytest.mark.parametrize("fmt", [hd.NVFP4, hd.NVFP4_UE5M3, hd.FP4_F16])
+def test_block_pair_comparison_parity(sigma, fmt):
+    """Fig. 2(a) of "Is Finer Better?": the per-block objectives at B = 8 and
+    B = 16 from the kernels match the oracle's (float32 of the float64 sum,
+    2e-6), and the fractions of 16-weight blocks above / on / below the
+    diagonal come out the same from both."""
+    import bench
+
+    W = tensor(sigma)
+    Wd = W.cuda()
+    r = {}
+    for src in ("gpu", "oracle"):
+        o = {}
+        for B in (8, 16):
+            if src == "gpu":
+                o[B] = hd.quantize_blocks(hd.NAIVE, fmt, B, Wd, block_obj=True)[2].cpu()
+            else:
+                o[B] = torch.from_numpy(oracle.quantize(oracle.NAIVE, fmt, B, W.numpy())[2])
+        r[src] = (bench.block_pair_comparison(o[8], o[16]), o)
+    for B in (8, 16):
+        np.testing.assert_allclose(r["gpu"][1][B].numpy(), r["oracle"][1][B].numpy().astype(np.float32), rtol=2e-6)
+    assert r["gpu"][0] == r["oracle"][0]
