@@ -37,7 +37,7 @@ FOUR_BIT = (NVFP4, MXFP4, NVFP4_UE4M4, NVFP4_UE5M3, NVINT4, FP4_F16, INT4_F16)
 # formats whose block scales are binary16 values (stored as torch.float16)
 F16_SCALES = (FP4_F16, INT4_F16)
 
-EXPORTS = ["hdiag_set_schedule", "hdiag", "hdiag_workspace_size", "hdiag_noalloc", "quantize_blocks", "encode_blocks", "dequantize",
+EXPORTS = ["hdiag_set_schedule", "hdiag", "hdiag_workspace_size", "hdiag_noalloc", "quantize_blocks", "quantize_blocks_instrumented", "encode_blocks", "dequantize",
            "weight_error", "weight_error_workspace_size", "output_error", "output_error_workspace_size",
            "output_error_given_ref", "output_reference", "output_reference_size", "output_error_codes",
            "output_error_codes_workspace_size", "output_gram", "output_gram_size", "output_gram_workspace_size",
@@ -74,6 +74,7 @@ def lib():
         L.hdiag_set_schedule.argtypes = [i32, i32]
         L.hdiag_workspace_size.restype = sz
         L.quantize_blocks.argtypes = [i32, i32, i32, P, i32, i64, i64, P, P, P, P, P]
+        L.quantize_blocks_instrumented.argtypes = [i32, i32, i32, P, i32, i64, i64, P, P, P, P, P, P]
         L.encode_blocks.argtypes = [i32, i32, P, i32, i64, i64, P, P, P, P, P]
         L.dequantize.argtypes = [i32, i32, P, P, i64, i64, P, i32, P]
         L.weight_error_workspace_size.argtypes = [i64, i64]
@@ -124,7 +125,7 @@ def lib():
         L.gptq_factor_workspace_size.restype = sz
         L.gptq_factor.argtypes = [P, i64, ctypes.c_double, P, sz, P, P, sz, P]
         L.gptq_quantize_factored.argtypes = [i32, i32, i32, P, i32, i64, i64, P, P, sz, P, P, P, P, P, sz, P]
-        for name in ("hdiag_set_schedule", "hdiag", "hdiag_noalloc", "quantize_blocks", "encode_blocks", "dequantize", "weight_error",
+        for name in ("hdiag_set_schedule", "hdiag", "hdiag_noalloc", "quantize_blocks", "quantize_blocks_instrumented", "encode_blocks", "dequantize", "weight_error",
                      "output_error", "output_error_given_ref", "output_reference", "output_error_codes",
                      "output_gram", "output_reference_gram", "output_error_gram", "output_error_gram_batch",
                      "hdiag_format_info", "gptq_hessian", "gptq_quantize", "gptq_factor", "gptq_quantize_factored", "quantize_blocks_tensor_scaled",
@@ -237,6 +238,23 @@ def quantize_blocks(method, fmt, B, W, h=None, block_obj=False, codes=None, scal
     obj = torch.empty((N, K // B if B else 0), dtype=torch.float32, device=d) if block_obj else None
     _check(lib().quantize_blocks(method, fmt, B, _ptr(W), _dt(W), N, K, _ptr(h), _ptr(codes), _ptr(scales),
                                  _ptr(obj), _stream(d)), "quantize_blocks")
+    return codes, scales, obj
+
+
+def quantize_blocks_instrumented(method, fmt, B, W, evaluated, h=None, block_obj=False, codes=None, scales=None):
+    """quantize_blocks, adding to `evaluated` (a device int64 tensor of one
+    element, cleared by the caller) the (weight, candidate) pairs the search
+    evaluated.  Returns what quantize_blocks returns."""
+    d = _dev(W)
+    N, K = W.shape
+    if evaluated.dtype != torch.int64 or evaluated.numel() != 1:
+        raise ValueError("evaluated must be a device int64 tensor of one element")
+    codes = codes if codes is not None else torch.empty(codes_shape(fmt, N, K), dtype=torch.uint8, device=d)
+    scales = scales if scales is not None else torch.empty((N, K // B), dtype=scale_dtype(fmt), device=d)
+    obj = torch.empty((N, K // B), dtype=torch.float32, device=d) if block_obj else None
+    _check(lib().quantize_blocks_instrumented(method, fmt, B, _ptr(W), _dt(W), N, K, _ptr(h), _ptr(codes),
+                                              _ptr(scales), _ptr(obj), _ptr(evaluated), _stream(d)),
+           "quantize_blocks_instrumented")
     return codes, scales, obj
 
 

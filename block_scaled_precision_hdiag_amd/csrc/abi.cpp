@@ -175,6 +175,15 @@ hd_status quantize_blocks(hd_method method, hd_format fmt, int32_t B, const void
                           int64_t K, const float *h, uint8_t *codes, uint8_t *scales, float *block_obj,
                           void *stream)
 {
+    return quantize_blocks_instrumented(method, fmt, B, W, wt, N, K, h, codes, scales, block_obj, nullptr, stream);
+}
+
+hd_status quantize_blocks_instrumented(hd_method method, hd_format fmt, int32_t B, const void *W, hd_dtype wt,
+                                       int64_t N, int64_t K, const float *h, uint8_t *codes, uint8_t *scales,
+                                       float *block_obj, uint64_t *evaluated, void *stream)
+{
+    if (evaluated != nullptr && ((uintptr_t)evaluated & 7u))
+        return fail(HD_ERR_INVALID_ARG, "evaluated is not 8-byte aligned");
     HD_REQUIRE(method >= HD_NAIVE && method <= HD_NAIVE_OCP, "unknown method %d", (int)method);
     HD_REQUIRE(valid_dtype(wt), "unknown dtype %d", (int)wt);
     hd_status s = check_quant_shape(fmt, B, N, K, method == HD_NAIVE || method == HD_NAIVE_OCP);
@@ -197,7 +206,8 @@ hd_status quantize_blocks(hd_method method, hd_format fmt, int32_t B, const void
     if (is_f16(fmt))
         return hip_status(hd::launch_alt_f16(fmt, B, W, wt, N, K, hh, codes, scales, block_obj, st),
                           "quantize_blocks(alternation)");
-    return hip_status(hd::launch_search(fmt, B, W, wt, N, K, hh, codes, scales, block_obj, st),
+    return hip_status(hd::launch_search(fmt, B, W, wt, N, K, hh, codes, scales, block_obj,
+                                        reinterpret_cast<unsigned long long *>(evaluated), st),
                       "quantize_blocks(search)");
 }
 
@@ -546,7 +556,7 @@ hd_status quantize_blocks_tensor_scaled(hd_method method, hd_format fmt, int32_t
         return hip_status(hd::launch_encode(fmt, B, Wp, HD_F32, N, K, h, nullptr, codes, scales, block_obj, 0, st),
                           "quantize_blocks_tensor_scaled(naive)");
     const float *hh = method == HD_H_OPT ? h : nullptr;
-    return hip_status(hd::launch_search(fmt, B, Wp, HD_F32, N, K, hh, codes, scales, block_obj, st),
+    return hip_status(hd::launch_search(fmt, B, Wp, HD_F32, N, K, hh, codes, scales, block_obj, nullptr, st),
                       "quantize_blocks_tensor_scaled(search)");
 }
 
@@ -625,17 +635,18 @@ hd_status gptq_quantize(hd_method method, hd_format fmt, int32_t B, const void *
 namespace hd {
 
 hipError_t launch_search(int fmt, int B, const void *W, int wdt, int64_t N, int64_t K, const float *h,
-                         uint8_t *codes, uint8_t *scales, float *block_obj, hipStream_t st)
+                         uint8_t *codes, uint8_t *scales, float *block_obj, unsigned long long *evals,
+                         hipStream_t st)
 {
     switch (fmt) {
-    case HD_INT8_E4M3: return launch_search_int8(B, W, wdt, N, K, h, codes, scales, block_obj, st);
-    case HD_NVFP4: return launch_search_nvfp4(B, W, wdt, N, K, h, codes, scales, block_obj, st);
-    case HD_MXFP4: return launch_search_mxfp4(B, W, wdt, N, K, h, codes, scales, block_obj, st);
-    case HD_MXFP8: return launch_search_mxfp8(B, W, wdt, N, K, h, codes, scales, block_obj, st);
-    case HD_FP8_E4M3S: return launch_search_fp8s(B, W, wdt, N, K, h, codes, scales, block_obj, st);
-    case HD_NVFP4_UE4M4: return launch_search_nvfp4_ue4m4(B, W, wdt, N, K, h, codes, scales, block_obj, st);
-    case HD_NVFP4_UE5M3: return launch_search_nvfp4_ue5m3(B, W, wdt, N, K, h, codes, scales, block_obj, st);
-    case HD_NVINT4: return launch_search_nvint4(B, W, wdt, N, K, h, codes, scales, block_obj, st);
+    case HD_INT8_E4M3:
+    case HD_NVINT4: return launch_search_int_elems(fmt, B, W, wdt, N, K, h, codes, scales, block_obj, evals, st);
+    case HD_NVFP4:
+    case HD_MXFP4:
+    case HD_NVFP4_UE4M4:
+    case HD_NVFP4_UE5M3: return launch_search_e2m1_elems(fmt, B, W, wdt, N, K, h, codes, scales, block_obj, evals, st);
+    case HD_MXFP8:
+    case HD_FP8_E4M3S: return launch_search_e4m3_elems(fmt, B, W, wdt, N, K, h, codes, scales, block_obj, evals, st);
     }
     return hipErrorInvalidValue;
 }

@@ -1024,7 +1024,7 @@ static hipError_t gq_run(int method, int B, const void *W, int wdt, int64_t N, i
         else if (SK == SCALE_F16)
             e = launch_alt_f16(fmt, B, W, wdt, N, K, hh, codes, sc, nullptr, st);
         else
-            e = launch_search(fmt, B, W, wdt, N, K, hh, codes, sc, nullptr, st);
+            e = launch_search(fmt, B, W, wdt, N, K, hh, codes, sc, nullptr, nullptr, st);
         if (e != hipSuccess) return e;
         gq_loss<EK, SK>(W, wdt, N, K, B, h, sc, loss, st);
     }

@@ -16,26 +16,21 @@ hipError_t launch_encode(int fmt, int B, const void *W, int wdt, int64_t N, int6
                          const uint8_t *scales_in, uint8_t *codes, uint8_t *scales, float *block_obj, int ocp,
                          hipStream_t st);
 
-// SSE-Optimal (h == NULL) or H-Optimal search + encode.
+// SSE-Optimal (h == NULL) or H-Optimal search + encode.  evals (optional,
+// device): incremented by the number of (weight, candidate) pairs evaluated.
 hipError_t launch_search(int fmt, int B, const void *W, int wdt, int64_t N, int64_t K, const float *h,
-                         uint8_t *codes, uint8_t *scales, float *block_obj, hipStream_t st);
-// per-format instantiations (one translation unit each)
-hipError_t launch_search_int8(int B, const void *W, int wdt, int64_t N, int64_t K, const float *h,
-                              uint8_t *codes, uint8_t *scales, float *block_obj, hipStream_t st);
-hipError_t launch_search_nvfp4(int B, const void *W, int wdt, int64_t N, int64_t K, const float *h,
-                               uint8_t *codes, uint8_t *scales, float *block_obj, hipStream_t st);
-hipError_t launch_search_mxfp4(int B, const void *W, int wdt, int64_t N, int64_t K, const float *h,
-                               uint8_t *codes, uint8_t *scales, float *block_obj, hipStream_t st);
-hipError_t launch_search_mxfp8(int B, const void *W, int wdt, int64_t N, int64_t K, const float *h,
-                               uint8_t *codes, uint8_t *scales, float *block_obj, hipStream_t st);
-hipError_t launch_search_fp8s(int B, const void *W, int wdt, int64_t N, int64_t K, const float *h,
-                              uint8_t *codes, uint8_t *scales, float *block_obj, hipStream_t st);
-hipError_t launch_search_nvfp4_ue4m4(int B, const void *W, int wdt, int64_t N, int64_t K, const float *h,
-                                     uint8_t *codes, uint8_t *scales, float *block_obj, hipStream_t st);
-hipError_t launch_search_nvfp4_ue5m3(int B, const void *W, int wdt, int64_t N, int64_t K, const float *h,
-                                     uint8_t *codes, uint8_t *scales, float *block_obj, hipStream_t st);
-hipError_t launch_search_nvint4(int B, const void *W, int wdt, int64_t N, int64_t K, const float *h,
-                                uint8_t *codes, uint8_t *scales, float *block_obj, hipStream_t st);
+                         uint8_t *codes, uint8_t *scales, float *block_obj, unsigned long long *evals,
+                         hipStream_t st);
+// per element family (one translation unit each)
+hipError_t launch_search_int_elems(int fmt, int B, const void *W, int wdt, int64_t N, int64_t K, const float *h,
+                                   uint8_t *codes, uint8_t *scales, float *block_obj, unsigned long long *evals,
+                                   hipStream_t st);
+hipError_t launch_search_e2m1_elems(int fmt, int B, const void *W, int wdt, int64_t N, int64_t K, const float *h,
+                                    uint8_t *codes, uint8_t *scales, float *block_obj, unsigned long long *evals,
+                                    hipStream_t st);
+hipError_t launch_search_e4m3_elems(int fmt, int B, const void *W, int wdt, int64_t N, int64_t K, const float *h,
+                                    uint8_t *codes, uint8_t *scales, float *block_obj, unsigned long long *evals,
+                                    hipStream_t st);
 
 // SSE-Optimal (h == NULL) or H-Optimal binary16 block scales by alternation
 // (HD_FP4_F16, HD_INT4_F16) + encode.

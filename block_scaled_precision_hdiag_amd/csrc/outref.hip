@@ -1403,13 +1403,14 @@ static void gram_operand_multi_fmt(const GramOps &ob, const void *W, int wdt, in
             ob, static_cast<const float *>(W), K, sq, h, E, erow, dsum, N, rows);
 }
 
-// count quantisations (fmt[q], B[q], codes[q], scales[q]) of one W: out[q] =
-// sqrt(||X (Wq_q - W)^T||^2) / sqrt(*ysq); fmt == NULL: the reference
-// ||X W^T||^2 into ysq_out[0] (count 1).
-hipError_t launch_output_error_gram(int count, const int *fmt, const int *B, const uint8_t *const *codes,
-                                    const uint8_t *const *scales, const void *W, int wdt, int64_t N, int64_t K,
-                                    const void *gram, const double *ysq, double *ysq_out, double *out, double *sums,
-                                    void *ws, hipStream_t st)
+// One walk over `count` quantisations (fmt[q], B[q], codes[q], scales[q]) of
+// one W: out[q] = sqrt(||X (Wq_q - W)^T||^2) / sqrt(*ysq); fmt == NULL: the
+// reference ||X W^T||^2 into ysq_out[0] (count 1).  E, erow and dsum are the
+// walk's rows, part its slots.
+static hipError_t gram_walk(int count, const int *fmt, const int *B, const uint8_t *const *codes,
+                            const uint8_t *const *scales, const void *W, int wdt, int64_t N, int64_t K,
+                            const void *gram, const double *ysq, double *ysq_out, double *out, double *sums,
+                            uint16_t *E, int *erow, double *dsum, double *part, hipStream_t st)
 {
     const GramLayout L = output_gram_layout(K);
     const char *g = static_cast<const char *>(gram);
@@ -1417,11 +1418,6 @@ hipError_t launch_output_error_gram(int count, const int *fmt, const int *B, con
     const float *sq = reinterpret_cast<const float *>(g + L.sq);
     const uint16_t *C = reinterpret_cast<const uint16_t *>(g + L.c);
     const int64_t rpq = gram_rows(N), R = count * rpq, nt = R / GE_TN, mt = (K + GE_TM - 1) / GE_TM;
-    char *w = static_cast<char *>(ws);
-    uint16_t *E = reinterpret_cast<uint16_t *>(w);
-    int *erow = reinterpret_cast<int *>(w + al256(R * K * 2));
-    double *dsum = reinterpret_cast<double *>(w + al256(R * K * 2) + al256(R * 4));
-    double *part = reinterpret_cast<double *>(w + al256(R * K * 2) + al256(R * 4) + al256(R * 8));
     const bool work = N > 0 && K > 0;
     const GramPlan plan = gram_plan(nt, K);
     bool fused = false;
@@ -1496,6 +1492,50 @@ hipError_t launch_output_error_gram(int count, const int *fmt, const int *B, con
     gram_final<<<(unsigned)count, 256, 0, st>>>(part, work ? (int)(rpq / GE_TN) : 0, (int)mt, plan.qg, dsum, rpq,
                                                 work ? N : 0, fmt ? ysq : nullptr, ysq_out, out, sums);
     return hipGetLastError();
+}
+
+// Quantisations per walk: the walk re-reads the stacked operand E once per
+// panel of C's bands and C once per group of E tiles, from the Infinity Cache
+// when C's upper block triangle and the walk's E fit in it together
+// (GRAM_CACHE_BYTES); a batch whose whole E does not fit is cut into walks of
+// as many quantisations as do (at least one).  When C alone does not fit
+// there is nothing to gain and the batch stays one walk.
+static constexpr int64_t GRAM_CACHE_BYTES = (int64_t)224 << 20;
+static int gram_sub_batch(int count, int64_t N, int64_t K)
+{
+    const int64_t mt = (K + GE_TM - 1) / GE_TM;
+    const int64_t cbytes = mt * (mt + 1) / 2 * (int64_t)GE_TM * GE_TM * 2;
+    const int64_t ebytes = gram_rows(N) * K * 2;
+    if (cbytes + ebytes > GRAM_CACHE_BYTES || ebytes == 0) return count;
+    return (int)std::max<int64_t>(1, std::min<int64_t>(count, (GRAM_CACHE_BYTES - cbytes) / ebytes));
+}
+
+// count quantisations of one W, in walks of gram_sub_batch quantisations
+// that take consecutive slices of the workspace (E rows, row exponents,
+// diagonal sums, partial slots); fmt == NULL: the reference (count 1).
+hipError_t launch_output_error_gram(int count, const int *fmt, const int *B, const uint8_t *const *codes,
+                                    const uint8_t *const *scales, const void *W, int wdt, int64_t N, int64_t K,
+                                    const void *gram, const double *ysq, double *ysq_out, double *out, double *sums,
+                                    void *ws, hipStream_t st)
+{
+    const int64_t rpq = gram_rows(N), R = count * rpq, mt = (K + GE_TM - 1) / GE_TM;
+    char *w = static_cast<char *>(ws);
+    uint16_t *E = reinterpret_cast<uint16_t *>(w);
+    int *erow = reinterpret_cast<int *>(w + al256(R * K * 2));
+    double *dsum = reinterpret_cast<double *>(w + al256(R * K * 2) + al256(R * 4));
+    double *part = reinterpret_cast<double *>(w + al256(R * K * 2) + al256(R * 4) + al256(R * 8));
+    const int64_t slots_per_q = rpq / GE_TN * mt * std::max<int64_t>(device_cus(), 8);
+    const int sb = fmt == nullptr ? 1 : gram_sub_batch(count, N, K);
+    for (int q0 = 0; q0 < count; q0 += sb) {
+        const int n = std::min(sb, count - q0);
+        const hipError_t e = gram_walk(n, fmt ? fmt + q0 : nullptr, B ? B + q0 : nullptr,
+                                       codes ? codes + q0 : nullptr, scales ? scales + q0 : nullptr, W, wdt, N, K,
+                                       gram, ysq, ysq_out, out ? out + q0 : nullptr, sums ? sums + 3 * q0 : nullptr,
+                                       E + q0 * rpq * K, erow + q0 * rpq, dsum + q0 * rpq, part + q0 * slots_per_q,
+                                       st);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace hd

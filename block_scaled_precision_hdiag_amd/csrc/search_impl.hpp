@@ -105,10 +105,13 @@ __device__ __forceinline__ float search_resid(float a, float s, float r)
     return __builtin_fmaf(-y, s, a);
 }
 
+// evals (optional): the kernel adds the number of (weight, candidate) pairs it
+// evaluated, counting the weights of active lanes only (one atomic per wave).
 template <int EK, int SK, typename T, int SEG, int LPB, bool WEIGHTED>
 __global__ __launch_bounds__(256) void search_kernel(const T *__restrict__ W, int64_t N, int64_t K,
                                                      const float *__restrict__ h, uint8_t *__restrict__ codes,
-                                                     uint8_t *__restrict__ scales, float *__restrict__ block_obj)
+                                                     uint8_t *__restrict__ scales, float *__restrict__ block_obj,
+                                                     unsigned long long *__restrict__ evals)
 {
     constexpr int B = SEG * LPB;
     constexpr int ROWS = 256 / LPB;
@@ -228,6 +231,11 @@ __global__ __launch_bounds__(256) void search_kernel(const T *__restrict__ W, in
         olo -= SEARCH_STEP;
     }
 
+    if (evals != nullptr) {
+        // the wave evaluated offsets olo..ohi for each active lane's SEG weights
+        const unsigned long long nact = (unsigned long long)__popcll(__ballot(active));
+        if ((tid & 63) == 0) atomicAdd(evals, (unsigned long long)(ohi - olo + 1) * nact * SEG);
+    }
     // encode the segment with the chosen scale
     const float s = cand[best_c].x, r = cand[best_c].y;
     if (!active) return;
@@ -250,7 +258,7 @@ __global__ __launch_bounds__(256) void search_kernel(const T *__restrict__ W, in
 
 template <int EK, int SK, typename T, int SEG, int LPB>
 static hipError_t search_go(const void *W, int64_t N, int64_t K, const float *h, uint8_t *codes,
-                            uint8_t *scales, float *bo, hipStream_t st)
+                            uint8_t *scales, float *bo, unsigned long long *ev, hipStream_t st)
 {
     constexpr int ROWS = 256 / LPB;
     const dim3 grid((unsigned)((N + ROWS - 1) / ROWS), (unsigned)(K / (SEG * LPB)));
@@ -259,11 +267,12 @@ static hipError_t search_go(const void *W, int64_t N, int64_t K, const float *h,
     constexpr bool MAY_W = SEG <= 16, MAY_U = !(SEG == 16 && LPB > 1);
     if constexpr (MAY_W) {
         if (h) {
-            search_kernel<EK, SK, T, SEG, LPB, true><<<grid, 256, 0, st>>>(w, N, K, h, codes, scales, bo);
+            search_kernel<EK, SK, T, SEG, LPB, true><<<grid, 256, 0, st>>>(w, N, K, h, codes, scales, bo, ev);
             return hipGetLastError();
         }
     }
-    if constexpr (MAY_U) search_kernel<EK, SK, T, SEG, LPB, false><<<grid, 256, 0, st>>>(w, N, K, h, codes, scales, bo);
+    if constexpr (MAY_U)
+        search_kernel<EK, SK, T, SEG, LPB, false><<<grid, 256, 0, st>>>(w, N, K, h, codes, scales, bo, ev);
     return hipGetLastError();
 }
 
@@ -271,36 +280,36 @@ static hipError_t search_go(const void *W, int64_t N, int64_t K, const float *h,
 // registers (so the H kernels keep two waves per SIMD).
 template <int EK, int SK, typename T>
 static hipError_t search_b(int B, const void *W, int64_t N, int64_t K, const float *h, uint8_t *codes,
-                           uint8_t *scales, float *bo, hipStream_t st)
+                           uint8_t *scales, float *bo, unsigned long long *ev, hipStream_t st)
 {
     if (h) {
         switch (B) {
-        case 8: return search_go<EK, SK, T, 8, 1>(W, N, K, h, codes, scales, bo, st);
-        case 16: return search_go<EK, SK, T, 16, 1>(W, N, K, h, codes, scales, bo, st);
-        case 32: return search_go<EK, SK, T, 16, 2>(W, N, K, h, codes, scales, bo, st);
-        case 64: return search_go<EK, SK, T, 16, 4>(W, N, K, h, codes, scales, bo, st);
-        case 128: return search_go<EK, SK, T, 16, 8>(W, N, K, h, codes, scales, bo, st);
-        case 256: return search_go<EK, SK, T, 16, 16>(W, N, K, h, codes, scales, bo, st);
+        case 8: return search_go<EK, SK, T, 8, 1>(W, N, K, h, codes, scales, bo, ev, st);
+        case 16: return search_go<EK, SK, T, 16, 1>(W, N, K, h, codes, scales, bo, ev, st);
+        case 32: return search_go<EK, SK, T, 16, 2>(W, N, K, h, codes, scales, bo, ev, st);
+        case 64: return search_go<EK, SK, T, 16, 4>(W, N, K, h, codes, scales, bo, ev, st);
+        case 128: return search_go<EK, SK, T, 16, 8>(W, N, K, h, codes, scales, bo, ev, st);
+        case 256: return search_go<EK, SK, T, 16, 16>(W, N, K, h, codes, scales, bo, ev, st);
         }
         return hipErrorInvalidValue;
     }
     switch (B) {
-    case 8: return search_go<EK, SK, T, 8, 1>(W, N, K, h, codes, scales, bo, st);
-    case 16: return search_go<EK, SK, T, 16, 1>(W, N, K, h, codes, scales, bo, st);
-    case 32: return search_go<EK, SK, T, 32, 1>(W, N, K, h, codes, scales, bo, st);
-    case 64: return search_go<EK, SK, T, 32, 2>(W, N, K, h, codes, scales, bo, st);
-    case 128: return search_go<EK, SK, T, 32, 4>(W, N, K, h, codes, scales, bo, st);
-    case 256: return search_go<EK, SK, T, 32, 8>(W, N, K, h, codes, scales, bo, st);
+    case 8: return search_go<EK, SK, T, 8, 1>(W, N, K, h, codes, scales, bo, ev, st);
+    case 16: return search_go<EK, SK, T, 16, 1>(W, N, K, h, codes, scales, bo, ev, st);
+    case 32: return search_go<EK, SK, T, 32, 1>(W, N, K, h, codes, scales, bo, ev, st);
+    case 64: return search_go<EK, SK, T, 32, 2>(W, N, K, h, codes, scales, bo, ev, st);
+    case 128: return search_go<EK, SK, T, 32, 4>(W, N, K, h, codes, scales, bo, ev, st);
+    case 256: return search_go<EK, SK, T, 32, 8>(W, N, K, h, codes, scales, bo, ev, st);
     }
     return hipErrorInvalidValue;
 }
 
 template <int EK, int SK>
 static hipError_t search_fmt(int B, const void *W, int wdt, int64_t N, int64_t K, const float *h,
-                             uint8_t *codes, uint8_t *scales, float *bo, hipStream_t st)
+                             uint8_t *codes, uint8_t *scales, float *bo, unsigned long long *ev, hipStream_t st)
 {
-    return wdt == 1 ? search_b<EK, SK, bf16_t>(B, W, N, K, h, codes, scales, bo, st)
-                    : search_b<EK, SK, float>(B, W, N, K, h, codes, scales, bo, st);
+    return wdt == 1 ? search_b<EK, SK, bf16_t>(B, W, N, K, h, codes, scales, bo, ev, st)
+                    : search_b<EK, SK, float>(B, W, N, K, h, codes, scales, bo, ev, st);
 }
 
 }  // namespace hd

@@ -209,6 +209,17 @@ hd_status quantize_blocks(hd_method method, hd_format fmt, int32_t B, const void
                           int64_t N, int64_t K, const float *h, uint8_t *codes, uint8_t *scales,
                           float *block_obj, void *stream);
 
+/* quantize_blocks() with instrumentation, for measurement and tests: when
+ * `evaluated` (device uint64, 8-byte aligned, may be NULL) is given, the
+ * SSE / H-Optimal searches of the 8-bit scale grids add to it the number of
+ * (weight, candidate) pairs they evaluated (every candidate a block's lanes
+ * walk, repeats at the grid ends included; the zero tail the search proves
+ * tied is not walked).  The caller clears it; Naive and the FP16-scale
+ * alternation add nothing.  Results are those of quantize_blocks(). */
+hd_status quantize_blocks_instrumented(hd_method method, hd_format fmt, int32_t B, const void *W, hd_dtype wt,
+                                       int64_t N, int64_t K, const float *h, uint8_t *codes, uint8_t *scales,
+                                       float *block_obj, uint64_t *evaluated, void *stream);
+
 /* Encode W with caller-given scale codes (the encode step alone).  Arguments
  * as quantize_blocks; scales_in [N, K/B] is read, not written.  A NaN scale
  * code (E4M3 0x7F..., E8M0 0xFF, binary16 above 0x7BFF) encodes its block
@@ -375,8 +386,10 @@ hd_status output_error_gram(hd_format fmt, int32_t B, const uint8_t *codes, cons
  * double[count], out[q] = ||X Wq_q^T - X W^T||_F / sqrt(*ysq); sums (optional,
  * device, 3 count doubles): {t_q, *ysq, b_q} for each q, as output_error_gram's.
  * The results are those of count output_error_gram calls up to the order of
- * the float64 partial sums; one MFMA walk over the stacked operand of all
- * count quantisations reads each C block for several of them at once.
+ * the float64 partial sums; one MFMA walk over the stacked operand of several
+ * quantisations reads each C block for all of them at once, and a batch is
+ * cut into walks of as many quantisations as fit the Infinity Cache together
+ * with C (two for K = 9728; the whole batch when C alone does not fit).
  * workspace: ws_bytes >= output_error_gram_batch_workspace_size(count, N, K)
  * (count x the single call's operand).  1 <= count <= 4096.  Errors as
  * output_error_gram, for each q. */

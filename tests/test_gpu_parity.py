@@ -402,3 +402,32 @@ def test_invalid_call_raises():
     W = dev(torch.zeros(4, 40, dtype=torch.bfloat16))
     with pytest.raises(hd.HdiagError):
         hd.quantize_blocks(hd.SSE_OPT, hd.NVFP4, 16, W)
+
+
+@pytest.mark.parametrize("fmt", [hd.INT8_E4M3, hd.NVFP4, hd.MXFP4, hd.FP8_E4M3S])
+@pytest.mark.parametrize("method", [hd.SSE_OPT, hd.H_OPT])
+def test_instrumented_search_counts(fmt, method):
+    """quantize_blocks_instrumented gives quantize_blocks' results bit for bit
+    and counts the (weight, candidate) pairs the search walked: the same on
+    every run, at least the first window per weight and at most the grid
+    plus one widening step per weight; Naive adds nothing."""
+    N, K, B = 300, 1024, 32
+    W = dev(weights_for(fmt, N, K, 8000 + fmt))
+    h = dev(torch.from_numpy(h_for(K, 21)))
+    hh = h if method == hd.H_OPT else None
+    c0, s0, o0 = hd.quantize_blocks(method, fmt, B, W, h=hh, block_obj=True)
+    counts = []
+    for _ in range(2):
+        ev = torch.zeros(1, dtype=torch.int64, device="cuda")
+        c1, s1, o1 = hd.quantize_blocks_instrumented(method, fmt, B, W, ev, h=hh, block_obj=True)
+        torch.cuda.synchronize()
+        assert torch.equal(c0, c1) and torch.equal(s0, s1) and torch.equal(o0, o1)
+        counts.append(ev.item())
+    assert counts[0] == counts[1]
+    ncand = hd.hdiag_format_info(fmt, B)[2]
+    first = 10 if fmt == hd.INT8_E4M3 else 13 if fmt != hd.MXFP4 else 2
+    assert N * K * first <= counts[0] <= N * K * (ncand + 24)
+    ev = torch.zeros(1, dtype=torch.int64, device="cuda")
+    hd.quantize_blocks_instrumented(hd.NAIVE, fmt, B, W, ev)
+    torch.cuda.synchronize()
+    assert ev.item() == 0
