@@ -52,8 +52,7 @@ COUNTERS_PROFILE = os.path.join(ROOT, "profiles", "int8_down_proj_2560x9728_coun
 # sources whose kernels the INT8 step never launches (other formats' searches,
 # the FP16-scale alternation, GPTQ, per-tensor scaling), and the host-only C
 # ABI wrapper and launcher declarations (no device code)
-_NOT_IN_STEP = {"alt_f16.hip", "gptq.hip", "tscale.hip", "search_fp8s.hip", "search_mxfp4.hip", "search_mxfp8.hip",
-                "search_nvfp4.hip", "search_nvfp4_ue4m4.hip", "search_nvfp4_ue5m3.hip", "search_nvint4.hip",
+_NOT_IN_STEP = {"alt_f16.hip", "gptq.hip", "tscale.hip", "search_e2m1_elems.hip", "search_e4m3_elems.hip",
                 "abi.cpp", "kernels.hpp"}
 
 
@@ -103,7 +102,6 @@ def parse():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-rows", type=int, default=8, help="rows of W in the CPU sample")
     ap.add_argument("--suite", choices=["headline", "formats", "gptq", "sigma", "gemm", "hbm", "config3", "config5"],
                     default="headline",
                     help="headline: the step above (one JSON line, the default); formats: every element / "
@@ -112,14 +110,32 @@ def parse():
                     help="time the step as individual launches instead of replays of one captured HIP graph")
     ap.add_argument("--output-route", choices=["gram", "direct"], default="gram",
                     help="output error through G = X^T X (gram) or through X W^T (direct)")
+    ap.add_argument("--summarize-profile", metavar="DIR", default=None,
+                    help="no GPU: write the step's profile summaries under profiles/ from rocprofv3 csv output in "
+                         "DIR/{trace,valu,fetch,write} (the runs made with --copy-probe-mb 1024)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="before timing, run one device copy of this many MB (a known-size kernel that "
                          "calibrates HBM byte counters)")
     return ap.parse_args()
 
 
+PROFILE_CMDS = {
+    "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof/trace -o step -- python3 bench.py "
+             "--steps 2 --warmup 1 --no-cpu --eager --copy-probe-mb 1024",
+    "valu": "rocprofv3 --pmc SQ_INSTS_VALU SQ_ACTIVE_INST_VALU SQ_WAVE_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE "
+            "SQ_INSTS_SALU SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA --output-format csv -d gpurun_out/prof/valu -o step "
+            "-- python3 bench.py --steps 1 --warmup 0 --no-cpu --eager --copy-probe-mb 1024",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof/fetch -o step -- python3 bench.py "
+             "--steps 1 --warmup 0 --no-cpu --eager --copy-probe-mb 1024",
+    "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof/write -o step -- python3 bench.py "
+             "--steps 1 --warmup 0 --no-cpu --eager --copy-probe-mb 1024",
+}
+
+
 def main():
     args = parse()
+    if args.summarize_profile:
+        return summarize_profile(args.summarize_profile, 1024, PROFILE_CMDS)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the library has no multi-GPU path (the work would shard by rows "
               "of W and X). Run with --gpus 1.", file=sys.stderr)
@@ -231,6 +247,19 @@ def main():
                   lambda: hd.output_error_gram_batch(items, W, gram, ysq, sums=osums, workspace=ws_o,
                                                      out=oerr.view(-1)), rec)
 
+    # (weight, candidate) pairs the searches evaluate per launch: one
+    # instrumented call per (B, method) before the warm-up (outside the timed region, and before the profiled step)
+    evals = {"search_sse": [], "search_h": []}
+    for B in blocks:
+        for mname, m in methods:
+            if m == hd.NAIVE:
+                continue
+            ev = torch.zeros(1, dtype=torch.int64, device=dev)
+            hd.quantize_blocks_instrumented(m, fmt, B, W, ev, h=h if m == hd.H_OPT else None)
+            evals["search_" + mname].append(ev)
+    torch.cuda.synchronize()
+    evals = {k: sum(e.item() for e in v) / len(v) for k, v in evals.items()}
+
     for _ in range(args.warmup):
         step(False)
     torch.cuda.synchronize()
@@ -294,25 +323,36 @@ def main():
     def roof(stage):
         bound, units = work[stage]
         t = avg[stage] * 1e-3
-        if bound == "hbm":
-            ach, peak, unit = units / t / 1e9, HBM_PEAK_GBS, "GB/s"
-        elif bound == "mfma":
-            ach, peak, unit = units / t / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
-        else:
-            ach, peak, unit = units / t / 1e12, VALU_PEAK_TOPS, "Tops/s"
-        r = {"bound": bound, "achieved": round(ach, 3), "peak": round(peak, 3), "unit": unit,
-             "frac": round(ach / peak, 4), "avg_ms": round(avg[stage], 4)}
         c = counters.get(stage)
         if bound == "alu":
-            # the full-grid count above is a convention (the search evaluates a
-            # fraction of the grid); the executed VALU rate comes from counters
-            r["basis"] = "full-grid equivalent (%d lane-ops per weight and candidate)" % SEARCH_OPS[stage[7:]]
+            # the search: its work is the (weight, candidate) pairs it evaluated
+            # (counted by the instrumented call); what a pair costs in VALU
+            # lane-instructions comes from the counters, so `achieved` is the
+            # executed VALU lane-op rate against the non-packed FP32 peak
+            pairs = evals[stage]
+            r = {"bound": "alu", "unit": "Tops/s", "peak": round(VALU_PEAK_TOPS, 3), "avg_ms": round(avg[stage], 4),
+                 "evaluated_pairs_per_launch": int(pairs), "candidates_per_weight": round(pairs / (N * K), 3),
+                 "gpairs_per_s": round(pairs / t / 1e9, 2),
+                 "full_grid_equivalent_tops": round(units / t / 1e12, 3)}
             if c:
-                ex = c["SQ_INSTS_VALU"] * 64 / t / 1e12
-                r["executed_valu_tops"] = round(ex, 3)
-                r["executed_valu_frac"] = round(ex / VALU_PEAK_TOPS, 4)
-        elif bound == "mfma" and c:
-            r["mfma_busy_frac"] = round(c["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * t * 2.4e9), 4)
+                lane_ops = c["SQ_INSTS_VALU"] * 64
+                r["achieved"] = round(lane_ops / t / 1e12, 3)
+                r["frac"] = round(lane_ops / t / 1e12 / VALU_PEAK_TOPS, 4)
+                r["valu_lane_ops_per_pair"] = round(lane_ops / pairs, 2)
+                r["valu_busy"] = round(c["valu_busy"], 4)
+                r["clock_ghz"] = round(c["clock_ghz"], 3)
+            else:
+                r["achieved"] = r["frac"] = None
+            return r
+        if bound == "hbm":
+            ach, peak, unit = units / t / 1e9, HBM_PEAK_GBS, "GB/s"
+        else:
+            ach, peak, unit = units / t / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
+        r = {"bound": bound, "achieved": round(ach, 3), "peak": round(peak, 3), "unit": unit,
+             "frac": round(ach / peak, 4), "avg_ms": round(avg[stage], 4)}
+        if bound == "mfma" and c:
+            r["mfma_util"] = round(c["mfma_util"], 4)
+            r["clock_ghz"] = round(c["clock_ghz"], 3)
         return r
 
     stages = {s: roof(s) for s in avg}
@@ -321,7 +361,8 @@ def main():
     roofline["kernel"] = dominant
     tr = measured_traffic().get(dominant)
     roofline["traffic"] = round(tr["read_bytes"] + tr["write_bytes"]) if tr else None
-    roofline["traffic_unit"] = "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated)"
+    roofline["traffic_unit"] = ("bytes per call between the L2s and the memory fabric (rocprofv3 FETCH_SIZE + "
+                                "WRITE_SIZE, calibrated on a device copy; Infinity Cache hits included)")
     roofline.pop("avg_ms")
 
     search_gwps = {s: round(N * K / (avg[s] * 1e-3) / 1e9, 3) for s in avg if s.startswith("search") or s == "naive"}
@@ -341,6 +382,7 @@ def main():
 
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": "Gweights/s", "n_gpus": 1,
+        "profiles_source_hash": source_hash(),
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3),
         "launch": launch, "ms_per_step_eager": round(ms_eager, 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
@@ -361,7 +403,7 @@ def main():
     }
 
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(W_cpu, X_cpu, blocks, methods, fmt, args.cpu_rows, value)
+        out["cpu_baseline"] = cpu_baseline(W_cpu, X_cpu, blocks, methods, fmt, value, search_gwps)
     print(json.dumps(out), flush=True)
 
 
@@ -917,10 +959,239 @@ def gemm_suite(args, dev):
                       "peak_tflops": MFMA_BF16_PEAK_TFLOPS, "results": out}), flush=True)
 
 
-def cpu_baseline(W_cpu, X_cpu, blocks, methods, fmt, rows, gpu_value):
-    """The CPU oracle on a bounded sample of the same step, extrapolated stage
-    by stage to the full workload (blocks are independent, so each stage's
-    time is linear in the rows it covers)."""
+# ------------------------------------------------------------------------
+# Profile summaries: rocprofv3 CSV output of the headline step -> the
+# committed summaries under profiles/ (no GPU needed).
+
+def _stage_of(name, state):
+    """Step stage of one dispatch from its kernel name; state carries which
+    operand kernel ran last, which tells the C E^T walk of the reference
+    (||X W^T||^2) from the walk of the quantisations' batch."""
+    n = name.split("(")[0]
+    if "hdiag_vec" in n or "hdiag_col" in n or "hdiag_final" in n:
+        return "hdiag"
+    if "gram_prep_kernel" in n or "xt_transpose_kernel" in n or "gemm_err_kernel<false, 2," in n:
+        return "output_gram"
+    if "gram_operand_kernel" in n:
+        state["walk"] = "output_reference"
+        return "output_reference"
+    if "gram_operand_multi_kernel" in n:
+        state["walk"] = "output_error"
+        return "output_error"
+    if "gemm_err_kernel<true, 3," in n or "gram_zero_f64" in n or "gram_final" in n:
+        return state.get("walk", "output_error")
+    if "encode_kernel" in n:
+        return "naive"
+    if "search_kernel" in n:
+        return "search_h" if n.rstrip().endswith("true>") else "search_sse"
+    if "dequant_kernel" in n:
+        return "dequantize"
+    if "werr_partial" in n or "ratio_final" in n:
+        return "weight_error"
+    if "__amd_rocclr_copyBuffer" in n:
+        return "copy"
+    return "other"
+
+
+def _read_csv(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _find(d, suffix):
+    import glob
+    hits = sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True))
+    if not hits:
+        raise SystemExit("no *%s under %s" % (suffix, d))
+    return hits[0]
+
+
+def _dispatches(rows, with_counters):
+    """Per dispatch (in dispatch order): kernel name, stage, duration (ns) and
+    counters.  The copy probe is the largest __amd_rocclr_copyBuffer."""
+    by = {}
+    for r in rows:
+        k = int(r["Dispatch_Id"])
+        e = by.setdefault(k, {"name": r["Kernel_Name"], "t": int(r["End_Timestamp"]) - int(r["Start_Timestamp"]),
+                              "c": {}})
+        if with_counters:
+            e["c"][r["Counter_Name"]] = float(r["Counter_Value"])
+    state = {}
+    out = []
+    started = False  # dispatches before the first step's hdiag are set-up work
+    for k in sorted(by):
+        e = by[k]
+        e["stage"] = _stage_of(e["name"], state)
+        started = started or e["stage"] == "hdiag"
+        if not started and e["stage"] not in ("copy",):
+            e["stage"] = "setup"
+        out.append(e)
+    copies = [e for e in out if e["stage"] == "copy"]
+    if copies:
+        max(copies, key=lambda e: e["t"])["stage"] = "copy_probe"
+    return out
+
+
+STAGE_ORDER = ["hdiag", "output_gram", "output_reference", "naive", "search_sse", "search_h", "dequantize",
+               "weight_error", "output_error"]
+# calls of each stage in one step (a call may launch several kernels)
+STAGE_CALLS = {"hdiag": 1, "output_gram": 1, "output_reference": 1, "naive": 4, "search_sse": 4, "search_h": 4,
+               "dequantize": 12, "weight_error": 12, "output_error": 1}
+
+
+def summarize_profile(d, probe_mb, cmds):
+    """Write the kernel-stats, counters and traffic summaries of the step from
+    rocprofv3 output under d (trace/, valu/, fetch/, write/ subdirectories)
+    into profiles/."""
+    sh = source_hash()
+    tr = _dispatches(_read_csv(_find(os.path.join(d, "trace"), "kernel_trace.csv")), False)
+    steps = sum(1 for e in tr if "hdiag_final" in e["name"])
+    # kernel statistics, one row per (kernel, stage)
+    agg = {}
+    for e in tr:
+        if e["stage"] in ("other", "copy", "copy_probe", "setup"):
+            continue
+        key = (e["name"].split("(")[0], e["stage"])
+        agg.setdefault(key, []).append(e["t"] / 1e3)
+    tot = sum(sum(v) for v in agg.values())
+    per_stage = {}
+    for e in tr:
+        if e["stage"] in STAGE_ORDER:
+            per_stage.setdefault(e["stage"], 0.0)
+            per_stage[e["stage"]] += e["t"] / 1e3
+    lines = ["# Kernel statistics: the bench.py step (INT8 / E4M3 scales, W 2560x9728 bf16, X 16384x9728 bf16)", "",
+             "One MI355X (gfx950).  Command, from the repository root:", "", "    " + cmds["trace"], "",
+             "%d steps ran (warm-up included).  Rows are split by the step stage a dispatch belongs to: the C E^T "
+             "walk `gemm_err_kernel<true, 3, ...>` serves output_reference_gram (one E, the reference ||X W^T||^2) "
+             "and the output errors of the quantisations (output_error_gram_batch, in walks of two "
+             "quantisations); `gemm_err_kernel<false, 2, ...>` is the X^T X product of output_gram.  Summary made "
+             "by `python bench.py --summarize-profile DIR`; step sources' hash (bench.py source_hash): %s." % (steps, sh),
+             "", "| kernel | stage | calls | avg (us) | min (us) | max (us) | % time |", "|---|---|---:|---:|---:|---:|---:|"]
+    for (k, st), v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+        lines.append("| `%s` | %s | %d | %.1f | %.1f | %.1f | %.2f |" % (k[:90], st, len(v), sum(v) / len(v), min(v),
+                                                                        max(v), 100 * sum(v) / tot))
+    lines += ["", "Per stage (all kernels of the stage, per step):", "", "| stage | us per step |", "|---|---:|"]
+    for st in STAGE_ORDER:
+        if st in per_stage:
+            lines.append("| %s | %.1f |" % (st, per_stage[st] / steps))
+    with open(os.path.join(ROOT, "profiles", "int8_down_proj_2560x9728_kernel_stats.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    # counters: executed VALU / MFMA work per stage, clocks from GRBM_GUI_ACTIVE
+    va = _dispatches(_read_csv(_find(os.path.join(d, "valu"), "counter_collection.csv")), True)
+    cs = {}
+    for e in va:
+        if e["stage"] not in STAGE_ORDER:
+            continue
+        c = cs.setdefault(e["stage"], {"launches": 0, "ns": 0.0})
+        c["launches"] += 1
+        c["ns"] += e["t"]
+        for k, v in e["c"].items():
+            c[k] = c.get(k, 0.0) + v
+    csteps = sum(1 for e in va if "hdiag_final" in e["name"])
+    rec = {}
+    lines = ["# Executed VALU / MFMA work per call: the bench.py step (INT8 / E4M3 scales, W 2560x9728, X 16384x9728)",
+             "", "One MI355X (gfx950).  One counter pass, from the repository root:", "", "    " + cmds["valu"], "",
+             "Per stage: summed over all kernels of its calls in the step and divided by the calls (the search and "
+             "Naive stages are one kernel per call; output_error is the batch call with its operand, walk and final "
+             "kernels).  GRBM_GUI_ACTIVE is reported summed over the 8 XCDs, so GRBM_GUI_ACTIVE / 8 / duration is "
+             "the shader clock during the call's kernels (meaningful for calls of 100 us and more; for shorter ones "
+             "the counter's activity window exceeds the kernels' run time).  VALUBusy = "
+             "SQ_ACTIVE_INST_VALU / CU_NUM / (GRBM_GUI_ACTIVE / 8) and MfmaUtil = SQ_VALU_MFMA_BUSY_CYCLES / "
+             "(SIMD_NUM x GRBM_GUI_ACTIVE / 8) are the vendor's derived metrics (rocprofv3 -L), here with CU_NUM = "
+             "256 and SIMD_NUM = 1024; both are taken against the cycles the clock actually ran.  SQ_ACTIVE_INST_VALU "
+             "counts one quad-cycle per wave64 VALU instruction (it equals SQ_INSTS_VALU here), so VALUBusy assumes "
+             "four shader cycles per instruction; readings above 1 mean the SIMDs issue more than one VALU "
+             "instruction per four cycles on average (gfx950 finishes some VALU instructions in fewer than four), "
+             "i.e. the VALU issue port is saturated.  Durations are those of this counter pass.",
+             "", "| stage | calls | kernels | us per call | clock GHz | VALU instr / call | VALUBusy | MFMA instr / call | MfmaUtil |",
+             "|---|---:|---:|---:|---:|---:|---:|---:|---:|"]
+    for st in STAGE_ORDER:
+        if st not in cs:
+            continue
+        c = cs[st]
+        n = STAGE_CALLS[st] * max(csteps, 1)
+        grbm = c.get("GRBM_GUI_ACTIVE", 0.0) / 8.0
+        clk = grbm / (c["ns"] * 1e-9) / 1e9 if c["ns"] else 0.0
+        vb = c.get("SQ_ACTIVE_INST_VALU", 0.0) / 256.0 / grbm if grbm else 0.0
+        mu = c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (1024.0 * grbm) if grbm else 0.0
+        rec[st] = {"calls": n, "kernels": c["launches"], "avg_us": c["ns"] / n / 1e3, "clock_ghz": clk,
+                   "valu_busy": vb, "mfma_util": mu,
+                   "SQ_INSTS_VALU": c.get("SQ_INSTS_VALU", 0.0) / n, "SQ_INSTS_MFMA": c.get("SQ_INSTS_MFMA", 0.0) / n,
+                   "SQ_VALU_MFMA_BUSY_CYCLES": c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / n,
+                   "GRBM_GUI_ACTIVE": c.get("GRBM_GUI_ACTIVE", 0.0) / n}
+        lines.append("| %s | %d | %d | %.1f | %.2f | %.4g | %.3f | %.4g | %.3f |" % (
+            st, n, c["launches"], c["ns"] / n / 1e3, clk, rec[st]["SQ_INSTS_VALU"], vb, rec[st]["SQ_INSTS_MFMA"], mu))
+    lines += ["", "Machine-readable record read by bench.py (used only while the step's sources in csrc/ still hash "
+                  "to source_hash):", "", "counters-json: " + json.dumps({"source_hash": sh, "stages": rec})]
+    with open(os.path.join(ROOT, "profiles", "int8_down_proj_2560x9728_counters.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    # HBM traffic: FETCH_SIZE / WRITE_SIZE (KiB per dispatch), calibrated on the
+    # copy probe of probe_mb MiB (it reads and writes probe_mb MiB)
+    rd = _dispatches(_read_csv(_find(os.path.join(d, "fetch"), "counter_collection.csv")), True)
+    wr = _dispatches(_read_csv(_find(os.path.join(d, "write"), "counter_collection.csv")), True)
+    probe = float(probe_mb) * (1 << 20)
+    fr = [e for e in rd if e["stage"] == "copy_probe"][0]["c"]["FETCH_SIZE"] * 1024.0
+    fw = [e for e in wr if e["stage"] == "copy_probe"][0]["c"]["WRITE_SIZE"] * 1024.0
+    kr, kw = probe / fr, probe / fw
+    tr_rec = {}
+    for lst, key, fac, col in ((rd, "FETCH_SIZE", kr, "read_bytes"), (wr, "WRITE_SIZE", kw, "write_bytes")):
+        n = {}
+        for e in lst:
+            if e["stage"] in STAGE_ORDER:
+                t = tr_rec.setdefault(e["stage"], {"read_bytes": 0.0, "write_bytes": 0.0, "launches": 0})
+                t[col] += e["c"].get(key, 0.0) * 1024.0 * fac
+                n[e["stage"]] = n.get(e["stage"], 0) + 1
+        for st, cnt in n.items():
+            tr_rec[st]["launches"] = cnt
+    launches = STAGE_CALLS
+    lines = ["# HBM traffic per launch: the bench.py step (INT8 / E4M3 scales, W 2560x9728, X 16384x9728)", "",
+             "One MI355X (gfx950).  Two counter passes, from the repository root:", "", "    " + cmds["fetch"],
+             "    " + cmds["write"], "",
+             "FETCH_SIZE and WRITE_SIZE (KiB per dispatch) summed over each stage's kernels in one step and divided "
+             "by the stage's calls per step (output_error is one output_error_gram_batch call: its operand, walk "
+             "and final kernels for all 12 quantisations).  Both counters are taken where the L2 caches meet the "
+             "memory fabric: they count every L2 miss and write-back, whether the Infinity Cache or HBM serves it, "
+             "so they bound the HBM bytes from above.  Calibration: the same passes count a device copy of "
+             "%d MiB (the copy probe, which reads and writes %d MiB) as %.0f MiB fetched and %.0f MiB written, so "
+             "reads are scaled by %.3f and writes by %.3f." % (probe_mb, probe_mb, fr / (1 << 20), fw / (1 << 20), kr, kw),
+             "", "| stage | calls per step | read GB per call | write GB per call |", "|---|---:|---:|---:|"]
+    for st in STAGE_ORDER:
+        if st in tr_rec:
+            t = tr_rec[st]
+            L = launches[st]
+            t["read_bytes"] /= L
+            t["write_bytes"] /= L
+            lines.append("| %s | %d | %.4f | %.4f |" % (st, L, t["read_bytes"] / 1e9, t["write_bytes"] / 1e9))
+    lines += ["", "Machine-readable record read by bench.py (used only while the step's sources in csrc/ still hash "
+                  "to source_hash):", "", "traffic-json: " + json.dumps({"source_hash": sh, "read_scale": kr,
+                                                                         "write_scale": kw, "stages": tr_rec})]
+    with open(os.path.join(ROOT, "profiles", "int8_down_proj_2560x9728_hbm_traffic.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("wrote profiles/int8_down_proj_2560x9728_{kernel_stats,counters,hbm_traffic}.md (source hash %s)" % sh)
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(W_cpu, X_cpu, blocks, methods, fmt, gpu_value, gpu_search):
+    """The CPU oracle on bounded samples of the same step, each stage timed at
+    two sample sizes and extrapolated from the slope (so a call's fixed cost is
+    not multiplied up): hdiag over rows of X, the scale choice, dequantize and
+    weight error over rows of W, and the output error over rows of X for a
+    fixed block of W rows (its cost is rows of X x rows of W).  Every sample has
+    at least as many rows as the oracle has threads, so all of them work.  Run
+    with all threads and with one."""
     import numpy as np
 
     import oracle
@@ -928,35 +1199,74 @@ def cpu_baseline(W_cpu, X_cpu, blocks, methods, fmt, rows, gpu_value):
 
     N, K = W_cpu.shape
     M = X_cpu.shape[0]
-    nt = oracle.max_threads()
     Wb = synth.bits(W_cpu)
     Xb = synth.bits(X_cpu)
-    xr_h = 2048          # rows of X for hdiag
-    xr_o = 4             # rows of X for the output error
-    Ws = Wb[:rows]
-    t = time.perf_counter()
-    h = oracle.hdiag(Xb[:xr_h])
-    t_hdiag = (time.perf_counter() - t) * (M / xr_h)
-    h_full = h  # the sample's h weights the sample's search; the cost does not depend on its values
-    total = t_hdiag
-    for B in blocks:
-        for _, m in methods:
-            t = time.perf_counter()
-            c, s, _ = oracle.quantize(m, fmt, B, Ws, h=h_full if m == oracle.H_OPT else None)
-            t_q = time.perf_counter() - t
-            t = time.perf_counter()
-            Wq = oracle.dequantize(fmt, B, c, s, rows, K)
-            oracle.weight_error(Ws, Wq)
-            t_d = time.perf_counter() - t
-            t = time.perf_counter()
-            oracle.output_error(Xb[:xr_o], Ws, Wq)
-            t_o = time.perf_counter() - t
-            total += (t_q + t_d) * (N / rows) + t_o * (M / xr_o) * (N / rows)
-    value = len(blocks) * len(methods) * N * K / total / 1e9
+
+    def clock(f):
+        t = time.perf_counter()
+        f()
+        return time.perf_counter() - t
+
+    def fit(t1, n1, t2, n2):
+        b = max((t2 - t1) / (n2 - n1), 0.0)
+        return b, max(t1 - b * n1, 0.0)  # per-unit cost, fixed cost
+
+    def run(nt):
+        w1, w2 = 4 * nt, 16 * nt       # rows of W
+        x1, x2 = 16 * nt, 64 * nt      # rows of X (output error, with w2 rows of W)
+        h1, h2 = 256 * nt, 1024 * nt   # rows of X (hdiag)
+        st = {}
+        b, a = fit(clock(lambda: oracle.hdiag(Xb[:h1], nthreads=nt)), h1,
+                   clock(lambda: oracle.hdiag(Xb[:h2], nthreads=nt)), h2)
+        st["hdiag"] = a + b * M
+        h = oracle.hdiag(Xb[:h2], nthreads=nt)
+        st["quantize"], st["dequantize_weight_error"], st["output_error"] = 0.0, 0.0, 0.0
+        search = {"sse": 0.0, "h": 0.0}
+        for B in blocks:
+            for mname, m in methods:
+                tq, td = [], []
+                for r in (w1, w2):
+                    t = time.perf_counter()
+                    c, s, _ = oracle.quantize(m, fmt, B, Wb[:r], h=h if m == oracle.H_OPT else None, nthreads=nt)
+                    tq.append(time.perf_counter() - t)
+                    t = time.perf_counter()
+                    Wq = oracle.dequantize(fmt, B, c, s, r, K, nthreads=nt)
+                    oracle.weight_error(Wb[:r], Wq, nthreads=nt)
+                    td.append(time.perf_counter() - t)
+                b, a = fit(tq[0], w1, tq[1], w2)
+                st["quantize"] += a + b * N
+                if mname in search:
+                    search[mname] += (a + b * N) / len(blocks)
+                b, a = fit(td[0], w1, td[1], w2)
+                st["dequantize_weight_error"] += a + b * N
+                t1 = clock(lambda: oracle.output_error(Xb[:x1], Wb[:w2], Wq, nthreads=nt))
+                t2 = clock(lambda: oracle.output_error(Xb[:x2], Wb[:w2], Wq, nthreads=nt))
+                b, a = fit(t1, x1, t2, x2)
+                st["output_error"] += a + b * M * (N / w2)
+        return st, search
+
+    nt = oracle.max_threads()
+    t0 = time.perf_counter()
+    st_all, se_all = run(nt)
+    st_one, se_one = run(1)
+    wall = time.perf_counter() - t0
+    q = len(blocks) * len(methods)
+    tot_all, tot_one = sum(st_all.values()), sum(st_one.values())
+    value = q * N * K / tot_all / 1e9
     return {"value": value, "unit": "Gweights/s", "cores": nt, "kind": "oracle",
-            "sample": "oracle (C, fp64, OpenMP %d threads) on W rows 0..%d, X rows 0..%d for hdiag and 0..%d "
-                      "for the output error, every stage of the step, extrapolated linearly to the full "
-                      "2560x9728 / 16384-row workload: %.1f s per step" % (nt, rows - 1, xr_h - 1, xr_o - 1, total),
+            "sample": "oracle (C, fp64, OpenMP) on the step's own inputs, with t threads: W rows 0..4t-1 and "
+                      "0..16t-1 for the scale choice, dequantize and weight error, X rows 0..16t-1 and 0..64t-1 (with "
+                      "W rows 0..16t-1) for the output error, X rows 0..256t-1 and 0..1024t-1 for hdiag; each stage "
+                      "extrapolated from the slope between its two sample sizes to the full 2560x9728 / 16384-row "
+                      "step: %.1f s per step with t = %d, %.1f s with t = 1; %.1f s of host time in all"
+                      % (tot_all, nt, tot_one, wall),
+            "cpu_model": _cpu_model(), "nproc": os.cpu_count(),
+            "stage_seconds_per_step": {k: round(v, 3) for k, v in st_all.items()},
+            "stage_seconds_per_step_1thread": {k: round(v, 3) for k, v in st_one.items()},
+            "value_1thread": q * N * K / tot_one / 1e9,
+            "search_gweights_per_s": {k: round(N * K / v / 1e9, 5) for k, v in se_all.items()},
+            "search_gweights_per_s_1thread": {k: round(N * K / v / 1e9, 5) for k, v in se_one.items()},
+            "gpu_search_gweights_per_s": gpu_search,
             "gpu_over_cpu": gpu_value / value}
 
 
