@@ -7,19 +7,21 @@
 namespace hd {
 
 // Encode 8 elements w[0..7] with scale s (s == 0: the zero scale) and
-// r = fl32(1/s).  Writes the code of each element (sign included) and returns
-// the objective sum_j om_j (w_j - fl32(s q_j))^2 of the eight, in float64 and
-// element order (om == NULL: unweighted).
-template <int EK, int SK, bool ONE_STEP, bool WANT_OBJ = true>
+// r = fl32(1/s) (0 for s == 0).  Writes the code of each element (sign
+// included) and returns the objective sum_j om_j (w_j - fl32(s q_j))^2 of the
+// eight, in float64 and element order (om == NULL: unweighted).  rm_tab: see
+// scale_parts (TAB).  Branch-free: the zero scale multiplies the quotients by 0.
+template <int EK, int SK, bool ONE_STEP, bool WANT_OBJ = true, bool TAB = false>
 __device__ __forceinline__ double encode8(const float *w, float s, float r, const double *om,
-                                          uint32_t *code)
+                                          uint32_t *code, const float *rm_tab = nullptr)
 {
     double obj = 0.0;
     if (elem_int(EK)) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const float a = fabsf(w[j]);
-            const float x = (s != 0.0f) ? quotient<SK, ONE_STEP>(a, s, r) : 0.0f;
+            // s == 0 (r == 0): fl32(a 0) = 0, fma(-0, 0, a) = a, fma(a, 0, 0) = 0
+            const float x = quotient<SK, ONE_STEP>(a, s, r);
             const float y = round_elem<EK>(x);
             code[j] = elem_code<EK>(elem_index<EK>(y), __builtin_signbitf(w[j]) != 0);
             if (WANT_OBJ) {
@@ -35,16 +37,16 @@ __device__ __forceinline__ double encode8(const float *w, float s, float r, cons
     // quotient is an odd function of w (its sign is copied back because the
     // correction steps turn -0 into +0) and the conversion keeps the sign,
     // zero included, so its codes already carry the sign bits.
-    const ScaleParts sp = scale_parts<SK>(s);
+    const ScaleParts sp = scale_parts<SK, TAB>(s, rm_tab);
+    const float keep = s == 0.0f ? 0.0f : 1.0f;  // the zero scale: every element to +-0
     float x[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         // (an FP16 scale's mantissa m is one of 1024: both quotient corrections)
-        float v = (s == 0.0f) ? w[j] * 0.0f
-                              : (SK == SCALE_E8M0 ? w[j]
-                                                  : __builtin_copysignf(quotient<SCALE_E4M3, ONE_STEP && SK != SCALE_F16>(
-                                                                            w[j], sp.m, sp.rm),
-                                                                        w[j]));
+        float v = (SK == SCALE_E8M0 ? w[j]
+                                    : __builtin_copysignf(quotient_m<ONE_STEP && SK != SCALE_F16>(w[j], sp.m, sp.rm),
+                                                          w[j])) *
+                  keep;
         if (EK == ELEM_E4M3) v = fminf(fmaxf(v, -448.0f * sp.p2), 448.0f * sp.p2);
         x[j] = v;
     }

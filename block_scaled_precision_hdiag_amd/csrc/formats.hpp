@@ -167,6 +167,22 @@ __device__ __forceinline__ float quotient(float a, float s, float r)
     return q;
 }
 
+// fl32(a / m) for a scale mantissa m in [1, 2) with rm = fl32(1 / m): the
+// corrections of quotient() without its clamp (dividing by m >= 1 keeps every
+// FMA finite for finite a).  Elements this large saturate the grid either way.
+template <bool ONE_STEP>
+__device__ __forceinline__ float quotient_m(float a, float m, float rm)
+{
+    float q = a * rm;
+    float e = __builtin_fmaf(-q, m, a);
+    q = __builtin_fmaf(e, rm, q);
+    if (!ONE_STEP) {
+        e = __builtin_fmaf(-q, m, a);
+        q = __builtin_fmaf(e, rm, q);
+    }
+    return q;
+}
+
 // Round x >= 0 onto the element grid, saturating; returns the grid VALUE.
 // E2M1 / E4M3: add and subtract C = 2^(e + 23 - mbits) where e is the binade
 // of x floored at the smallest normal; the add rounds x to a multiple of that
@@ -262,22 +278,30 @@ __device__ __forceinline__ hd_v2f fp8x2_val(uint32_t half) { return __builtin_am
 struct ScaleParts {
     float s, m, rm, p2;
 };
-template <int SK>
-__device__ __forceinline__ ScaleParts scale_parts(float s)
+// TAB: rm comes from rm_tab[j] = fl32(1 / (1 + j / 16)), j = 0 .. 15 (an LDS
+// table), in place of a division: for the grids whose mantissas have at most
+// four bits (E4M3, UE4M4, UE5M3; not binary16).  Branch-free: s == 0 selects
+// m = 1, rm = 1, p2 = 1.
+template <int SK, bool TAB = false>
+__device__ __forceinline__ ScaleParts scale_parts(float s, const float *rm_tab = nullptr)
 {
     ScaleParts r;
     r.s = s;
-    if (SK == SCALE_E8M0 || s == 0.0f) {
+    if (SK == SCALE_E8M0) {
         r.m = 1.0f;
         r.rm = 1.0f;
         r.p2 = s == 0.0f ? 1.0f : s;
         return r;
     }
+    const bool z = s == 0.0f;
     int ex;
     const float f = __builtin_frexpf(s, &ex);  // s = f 2^ex, f in [0.5, 1)
-    r.m = 2.0f * f;
-    r.rm = 1.0f / r.m;
-    r.p2 = __builtin_ldexpf(1.0f, ex - 1);
+    r.m = z ? 1.0f : 2.0f * f;
+    if constexpr (TAB && SK != SCALE_F16)
+        r.rm = rm_tab[(f_bits(r.m) >> 19) & 15u];
+    else
+        r.rm = 1.0f / r.m;
+    r.p2 = z ? 1.0f : __builtin_ldexpf(1.0f, ex - 1);
     return r;
 }
 
@@ -336,17 +360,33 @@ __device__ __forceinline__ int ocp_code(float amax)
 // amax itself as E4M3).  E4M3 grids may return code 0 (the zero scale).
 // E8M0: nearest power of two in the linear domain, ties upward, clamped to
 // 2^[-127, 127].
+// fl32(amax / C), C = the element grid's largest value (6, 7 or 448), for
+// the non-power-of-two scale grids: two Markstein corrections of amax
+// RN(1 / C).  Checked exhaustively against IEEE division for every positive
+// float up to 2^100 (the quotient's clamp) and C = 6, 7, 448: they differ only
+// where the quotient is an fp32 subnormal (below 2^-126), which every one of
+// these grids (E4M3, UE4M4, UE5M3 and binary16, whose smallest values are
+// 2^-9 .. 2^-24) snaps to code 0 either way.  INT8 needs no quotient (the
+// scale is amax itself), and E8M0 keeps the division: its grid reaches 2^-127.
+template <int EK>
+__device__ __forceinline__ float div_elem_max(float amax)
+{
+    constexpr float C = EK == ELEM_E2M1 ? 6.0f : EK == ELEM_INT4 ? 7.0f : 448.0f;
+    constexpr float RC = EK == ELEM_E2M1 ? 0x1.555556p-3f : EK == ELEM_INT4 ? 0x1.24924ap-3f : 0x1.24924ap-9f;
+    return quotient<SCALE_E4M3, false>(amax, C, RC);
+}
+
 template <int EK, int SK>
 __device__ __forceinline__ int naive_code(float amax)
 {
     if (SK == SCALE_INT8 || SK == SCALE_E4M3) {
-        const float v = (SK == SCALE_INT8) ? amax : amax / elem_max(EK);  // IEEE division
+        const float v = (SK == SCALE_INT8) ? amax : div_elem_max<EK>(amax);
         const float y = round_elem<ELEM_E4M3>(v);
         return (int)elem_index<ELEM_E4M3>(y);
     }
-    if (SK == SCALE_UE4M4) return ue_round_code<4, 7>(amax / elem_max(EK));
-    if (SK == SCALE_UE5M3) return ue_round_code<3, 15>(amax / elem_max(EK));
-    if (SK == SCALE_F16) return f16_round_code((double)(amax / elem_max(EK)));  // fp16(fl32(amax / C))
+    if (SK == SCALE_UE4M4) return ue_round_code<4, 7>(div_elem_max<EK>(amax));
+    if (SK == SCALE_UE5M3) return ue_round_code<3, 15>(div_elem_max<EK>(amax));
+    if (SK == SCALE_F16) return f16_round_code((double)div_elem_max<EK>(amax));  // fp16(fl32(amax / C))
     const float v = amax / elem_max(EK);
     if (v == 0.0f) return 0;
     // v = f 2^E with f in [1, 2); frexp gives the exponent for subnormals too

@@ -19,7 +19,10 @@ namespace hd {
 // shuffles; for B = 4 a lane's eight weights are two whole blocks.  Codes go
 // out as 4 (4-bit) or 8 bytes per lane and sub-chunk, again on consecutive
 // addresses; the first lane of a block writes its scale.
-static constexpr int ENC_SUB = 4;
+#ifndef HD_ENC_SUB
+#define HD_ENC_SUB 4
+#endif
+static constexpr int ENC_SUB = HD_ENC_SUB;
 
 // Scale code of one block with largest magnitude amax: given, or the Naive
 // snap (the OCP floor rule on E8M0 grids when ocp is set).
@@ -31,6 +34,26 @@ __device__ __forceinline__ int enc_scale_code(float amax, const uint8_t *scales_
     return naive_code<EK, SK>(amax);
 }
 
+// fl32(1 / s) for the integer element grids (0 for s == 0): from the table
+// on the INT8 grid, by division on the others (INT4 elements); E2M1 / E4M3
+// elements do not use it (their quotients take scale_parts).
+// Scale value of a valid code: from the table on the INT8 grid (its values
+// are fl32(val / 127), a division each), by bit formula on the others.
+template <int SK>
+__device__ __forceinline__ float enc_scale_value(int code, const float *stab)
+{
+    if (SK == SCALE_INT8) return stab[code & 127];
+    return scale_value(SK, code);
+}
+
+template <int EK, int SK>
+__device__ __forceinline__ float enc_recip(float s, int code, const float *rtab)
+{
+    if (!elem_int(EK)) return 0.0f;
+    if (SK == SCALE_INT8) return s != 0.0f ? rtab[code & 127] : 0.0f;
+    return s != 0.0f ? 1.0f / s : 0.0f;
+}
+
 template <int EK, int SK, typename T, int B, bool GIVEN, bool OBJ>
 __global__ __launch_bounds__(256) void encode_kernel(const T *__restrict__ W, int64_t total, int64_t K,
                                                      const float *__restrict__ h,
@@ -40,19 +63,35 @@ __global__ __launch_bounds__(256) void encode_kernel(const T *__restrict__ W, in
 {
     constexpr int LPB = B >= 8 ? B / 8 : 1;  // lanes per block (B = 4: two blocks per lane)
     constexpr bool ONE_STEP = sizeof(T) == 2;
+    // reciprocals without a division per block: the INT8 grid's fl32(1 / s)
+    // per scale code (0 for code 0), else fl32(1 / (1 + j / 16)) for the
+    // mantissas of the E4M3 / UE4M4 / UE5M3 grids (see scale_parts)
+    constexpr bool RTAB = SK == SCALE_INT8 || SK == SCALE_E4M3 || SK == SCALE_UE4M4 || SK == SCALE_UE5M3;
+    __shared__ float rtab[128], stab[128];  // stab: the INT8 grid's scale values
+    if (RTAB) {
+        const int t = threadIdx.x;
+        if (SK == SCALE_INT8) {
+            if (t < 128) {
+                const float sv = (t >= 1 && t <= 126) ? scale_value(SCALE_INT8, t) : 0.0f;
+                stab[t] = sv;
+                rtab[t] = sv != 0.0f ? 1.0f / sv : 0.0f;
+            }
+        } else if (t < 16) {
+            rtab[t] = 1.0f / (1.0f + (float)t * 0.0625f);
+        }
+        __syncthreads();
+    }
     const int lane = threadIdx.x & 63;
     const int64_t wbase = (((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6) * (64 * 8 * ENC_SUB);
     // total % 8 == 0 and total % B == 0: a sub-chunk starting below total is
-    // whole, and the lanes of one block are all in or all out
+    // whole, and the lanes of one block are all in or all out.  Every lane
+    // loads (sub-chunks past the end read the last 8 weights and are dropped),
+    // so the waits can go sub-chunk by sub-chunk.
     float w[ENC_SUB][8];
 #pragma unroll
     for (int k = 0; k < ENC_SUB; ++k) {
         const int64_t e = wbase + 512 * k + 8 * lane;
-        if (e < total)
-            load8_nt<T>(W + e, w[k]);
-        else
-#pragma unroll
-            for (int j = 0; j < 8; ++j) w[k][j] = 0.0f;
+        load8_nt<T>(W + (e < total ? e : total - 8), w[k]);
     }
     const bool weighted = OBJ && h != nullptr;
 #pragma unroll
@@ -81,10 +120,11 @@ __global__ __launch_bounds__(256) void encode_kernel(const T *__restrict__ W, in
                 }
                 const int64_t blk = e / 4 + hb;
                 const int code = enc_scale_code<EK, SK, GIVEN>(amax, scales_in, blk, in, ocp);
-                const float s = (GIVEN ? scale_code_valid(SK, code) : true) ? scale_value(SK, code) : 0.0f;
-                const float r = (s != 0.0f) ? 1.0f / s : 0.0f;
+                const float s = (GIVEN ? scale_code_valid(SK, code) : true) ? enc_scale_value<SK>(code, stab) : 0.0f;
+                const float r = enc_recip<EK, SK>(s, code, rtab);
                 uint32_t ch[8];
-                const double o = encode8<EK, SK, ONE_STEP, OBJ>(wh, s, r, (weighted && in) ? omh : nullptr, ch);
+                const double o = encode8<EK, SK, ONE_STEP, OBJ, RTAB>(wh, s, r, (weighted && in) ? omh : nullptr,
+                                                                      ch, rtab);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) c[4 * hb + j] = ch[j];
                 if (in) {
@@ -114,18 +154,18 @@ __global__ __launch_bounds__(256) void encode_kernel(const T *__restrict__ W, in
         float s;
         if (GIVEN) {
             code = in ? load_scale<SK>(scales_in, blk) : 0;
-            s = scale_code_valid(SK, code) ? scale_value(SK, code) : 0.0f;
+            s = scale_code_valid(SK, code) ? enc_scale_value<SK>(code, stab) : 0.0f;
         } else {
             // ocp (E8M0 grids only): the OCP MX floor rule instead of the snap
             if constexpr (SK == SCALE_E8M0)
                 code = ocp ? ocp_code<EK>(amax) : naive_code<EK, SK>(amax);
             else
                 code = naive_code<EK, SK>(amax);
-            s = scale_value(SK, code);
+            s = enc_scale_value<SK>(code, stab);
         }
-        const float r = (s != 0.0f) ? 1.0f / s : 0.0f;
+        const float r = enc_recip<EK, SK>(s, code, rtab);
         uint32_t c[8];
-        double o = encode8<EK, SK, ONE_STEP, OBJ>(w[k], s, r, (weighted && in) ? om : nullptr, c);
+        double o = encode8<EK, SK, ONE_STEP, OBJ, RTAB>(w[k], s, r, (weighted && in) ? om : nullptr, c, rtab);
         if (OBJ) o = group_sum<LPB>(o);
         if (!in) continue;
         if (elem_4bit(EK)) {
@@ -275,6 +315,14 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict_
                                                       const float *__restrict__ tscale)
 {
     constexpr int VPS = OUT_BF16 ? 8 : 4;
+    // the INT8 grid's scale values fl32(val / 127), one division per code
+    // per workgroup instead of one per output group
+    __shared__ float stab[128];
+    if (SK == SCALE_INT8) {
+        if (threadIdx.x < 128)
+            stab[threadIdx.x] = scale_code_valid(SK, threadIdx.x) ? scale_value(SK, threadIdx.x) : 0.0f;
+        __syncthreads();
+    }
     const int lane = threadIdx.x & 63;
     const int64_t wave = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6;
     const int64_t base = wave * (64 * VPS * DQ_G) + (int64_t)lane * VPS;
@@ -302,11 +350,13 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict_
     for (int g = 0; g < DQ_G; ++g) {
         const int64_t e = base + (int64_t)g * 64 * VPS;
         if (e >= total) break;
-        const float s = scale_code_valid(SK, sc[g]) ? scale_value(SK, sc[g]) : 0.0f;
+        const float s = SK == SCALE_INT8 ? stab[sc[g] & 127] * (sc[g] < 128 ? 1.0f : 0.0f)
+                                         : (scale_code_valid(SK, sc[g]) ? scale_value(SK, sc[g]) : 0.0f);
         float o[VPS];
         dq_group<EK, VPS>(cw[g], s, tscale, o);
         if (VPS > B) {  // the second block's four outputs at its own scale
-            const float s2 = scale_code_valid(SK, sc2[g]) ? scale_value(SK, sc2[g]) : 0.0f;
+            const float s2 = SK == SCALE_INT8 ? stab[sc2[g] & 127] * (sc2[g] < 128 ? 1.0f : 0.0f)
+                                              : (scale_code_valid(SK, sc2[g]) ? scale_value(SK, sc2[g]) : 0.0f);
             float o2[VPS];
             dq_group<EK, VPS>(cw[g], s2, tscale, o2);
 #pragma unroll
