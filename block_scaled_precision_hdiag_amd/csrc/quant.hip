@@ -81,7 +81,19 @@ __global__ __launch_bounds__(256) void encode_kernel(const T *__restrict__ W, in
         }
         __syncthreads();
     }
-    const int lane = threadIdx.x & 63;
+    // A workgroup whose weights all lie inside W gathers its codes and scale
+    // codes in LDS and writes them out as 16-byte (codes) and 4-byte (scale)
+    // stores per lane, instead of one 4- or 8-byte store per lane and one
+    // scale per block: fewer, fuller write requests.  The last workgroup of
+    // a ragged grid, and B = 4, store directly.
+    constexpr int CW = elem_4bit(EK) ? 1 : 2;              // code dwords per lane and sub-chunk
+    constexpr int SB = SK == SCALE_F16 ? 2 : 1;            // bytes per scale code
+    constexpr int SCB = 512 * ENC_SUB / (B >= 8 ? B : 8) * SB;  // scale bytes per wave (a multiple of 8)
+    __shared__ uint32_t lcode[4][64 * ENC_SUB * CW];
+    __shared__ uint32_t lscale[4][SCB / 4];
+    const bool staged = B >= 8 && (int64_t)(blockIdx.x + 1) * (256 * 8 * ENC_SUB) <= total &&
+                        (GIVEN || ((uintptr_t)scales & 3u) == 0);
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int64_t wbase = (((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6) * (64 * 8 * ENC_SUB);
     // total % 8 == 0 and total % B == 0: a sub-chunk starting below total is
     // whole, and the lanes of one block are all in or all out.  Every lane
@@ -168,20 +180,44 @@ __global__ __launch_bounds__(256) void encode_kernel(const T *__restrict__ W, in
         double o = encode8<EK, SK, ONE_STEP, OBJ, RTAB>(w[k], s, r, (weighted && in) ? om : nullptr, c, rtab);
         if (OBJ) o = group_sum<LPB>(o);
         if (!in) continue;
+        uint32_t v[CW];
         if (elem_4bit(EK)) {
-            uint32_t v = 0;
+            v[0] = 0;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) v |= (c[j] & 15u) << (4 * j);
-            __builtin_nontemporal_store(v, reinterpret_cast<uint32_t *>(codes + e / 2));  // streamed out
+            for (int j = 0; j < 8; ++j) v[0] |= (c[j] & 15u) << (4 * j);
         } else {
-            uint2 v;
-            v.x = (c[0] & 255u) | ((c[1] & 255u) << 8) | ((c[2] & 255u) << 16) | ((c[3] & 255u) << 24);
-            v.y = (c[4] & 255u) | ((c[5] & 255u) << 8) | ((c[6] & 255u) << 16) | ((c[7] & 255u) << 24);
-            __builtin_nontemporal_store((uint64_t)v.x | ((uint64_t)v.y << 32), reinterpret_cast<uint64_t *>(codes + e));
+            v[0] = (c[0] & 255u) | ((c[1] & 255u) << 8) | ((c[2] & 255u) << 16) | ((c[3] & 255u) << 24);
+            v[CW - 1] = (c[4] & 255u) | ((c[5] & 255u) << 8) | ((c[6] & 255u) << 16) | ((c[7] & 255u) << 24);
+        }
+        if (staged) {
+            // dword (64 k + lane) CW of the wave's codes
+#pragma unroll
+            for (int j = 0; j < CW; ++j) lcode[wv][(64 * k + lane) * CW + j] = v[j];
+        } else if (elem_4bit(EK)) {
+            __builtin_nontemporal_store(v[0], reinterpret_cast<uint32_t *>(codes + e / 2));  // streamed out
+        } else {
+            __builtin_nontemporal_store((uint64_t)v[0] | ((uint64_t)v[CW - 1] << 32),
+                                        reinterpret_cast<uint64_t *>(codes + e));
         }
         if (lane % LPB == 0) {
-            if (!GIVEN) store_scale<SK>(scales, blk, code);
+            if (!GIVEN) {
+                if (staged)
+                    store_scale<SK>(reinterpret_cast<uint8_t *>(lscale[wv]), (512 * k + 8 * lane) / B, code);
+                else
+                    store_scale<SK>(scales, blk, code);
+            }
             if (OBJ) block_obj[blk] = (float)o;
+        }
+    }
+    if (B >= 8 && staged) {
+        __syncthreads();  // staged is uniform over the workgroup
+        const hd_u32x4 *src = reinterpret_cast<const hd_u32x4 *>(lcode[wv]);
+        hd_u32x4 *dst = reinterpret_cast<hd_u32x4 *>(codes + wbase * CW / 2);
+#pragma unroll
+        for (int i = lane; i < 16 * ENC_SUB * CW; i += 64) __builtin_nontemporal_store(src[i], dst + i);
+        if (!GIVEN) {
+            uint32_t *sdst = reinterpret_cast<uint32_t *>(scales + wbase / (B >= 8 ? B : 8) * SB);
+            for (int i = lane; i < SCB / 4; i += 64) sdst[i] = lscale[wv][i];
         }
     }
 }
