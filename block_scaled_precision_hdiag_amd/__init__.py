@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(_HERE, "libhdiag.so")
 # enums of include/hdiag.h
 HD_OK, HD_ERR_INVALID_ARG, HD_ERR_UNSUPPORTED, HD_ERR_HIP = 0, -1, -2, -3
 HD_F32, HD_BF16 = 0, 1
-SCHED_GRAM_GANGS, SCHED_GPTQ_TILE = 0, 1
+SCHED_GRAM_GANGS, SCHED_GPTQ_TILE, SCHED_GRAM_BANDS = 0, 1, 2
 NAIVE, SSE_OPT, H_OPT, NAIVE_OCP = 0, 1, 2, 3
 INT8_E4M3, NVFP4, MXFP4, MXFP8, FP8_E4M3S = 0, 1, 2, 3, 4
 NVFP4_UE4M4, NVFP4_UE5M3, NVINT4 = 5, 6, 7
@@ -194,8 +194,8 @@ def scale_dtype(fmt):
 
 
 def hdiag_set_schedule(knob, value):
-    """Set a process-wide schedule setting (SCHED_GRAM_GANGS, SCHED_GPTQ_TILE;
-    0 = automatic); host-only."""
+    """Set a process-wide schedule setting (SCHED_GRAM_GANGS, SCHED_GPTQ_TILE,
+    SCHED_GRAM_BANDS; 0 = automatic); host-only."""
     _check(lib().hdiag_set_schedule(knob, value), "hdiag_set_schedule")
 
 

@@ -31,6 +31,10 @@
 //     XOR-swizzled so the 16-byte fragment reads of 16 consecutive rows hit all
 //     64 banks (no conflicts, checked with SQ_LDS_BANK_CONFLICT); the fragments
 //     of the next 16-wide K slice are read while the current one multiplies;
+//   - the X^T X product of output_gram() stages rows of X itself (the
+//     reduction index) and reads the MFMA fragments with the LDS transpose
+//     read ds_read_b64_tr_b16 (two per fragment), so X needs no transposed
+//     copy;
 //   - tile order: the workgroups one XCD runs at once cover 8 X tiles for each
 //     weight tile, so they share X and weight panels in that XCD's L2;
 //   - when the last round of tiles would fill at most half of the CUs, those
@@ -49,6 +53,13 @@ namespace hd {
 typedef __bf16 ob16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 oh16x8_t __attribute__((ext_vector_type(8)));
 typedef float of32x16_t __attribute__((ext_vector_type(16)));
+typedef __bf16 ob16x4_t __attribute__((ext_vector_type(4)));
+
+// Permutation of the 32-byte pairs of a staged X row by its residue mod 4
+// (XOR with 0, 3, 5, 6): the 4 rows one 16-lane group reads at one pair
+// position land on 4 different pairs mod 4, and the 8 rows x 2 pairs of one
+// wave read on 8 different pairs mod 8.
+__device__ __forceinline__ constexpr int tr_sig(int r) { return (0x6530 >> (4 * r)) & 15; }
 
 static constexpr int GE_TM = 256;      // X rows per tile
 static constexpr int GE_TN = 256;      // weight rows per full tile
@@ -161,7 +172,8 @@ struct GeArgs {
 //       STORE_Y: Y[m][n] = acc, partial {0, sum acc^2};
 //       SUB_Y:   d = acc f_m - Y[m][n] with f_m = fscale 2^erow[m] (f_m = 1
 //                when erow is NULL), partial {sum d^2, 0}.
-//   GRAM (A = B = X^T, so acc = X^T X): the tiles (tm, tn) with tn <= tm of
+//   GRAM (A = B = X^T read from row-major X [K][M], K the reduction length
+//     and pitch M, so acc = X^T X): the tiles (tm, tn) with tn <= tm of
 //     the lower triangle, in groups of GE_GROUP_M tile rows (column-major
 //     inside a group).  Epilogue: C[n][m] = fp16(f acc[m][n] r[m] r[n]) (the
 //     transposed position, so C holds the upper block triangle), f = 2 off
@@ -269,20 +281,50 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_err_kernel(const GeArgs ga)
     // spreads the 16 rows of one fragment read over all 64 banks.  Chunks past
     // K come from ge_zero16; rows past M / N are clamped to the last row
     // (their outputs are never read).
+    //
+    // GRAM stages rows of X itself (A = B = X^T, read without a transposed
+    // copy): stage row r is X row k0 + r (the reduction index), 256 columns
+    // (m0 .. m0 + 255 for A, n0 .. n0 + 255 for B), 512 bytes.  Lane l of
+    // the wave's i-th instruction fills row r = 2 (NW i + wv) + l / 32,
+    // 16-byte slot l % 32, with chunk c = 2 ((slot / 2) ^ tr_sig(r % 4)) +
+    // slot % 2 of those columns: the 32-byte pairs of a row are permuted by
+    // the row's residue mod 4 so that the transposed fragment reads (GE_FRAG
+    // below: 4 rows x 32 bytes per 16 lanes, 8 rows x 64 bytes per wave)
+    // spread over the banks.  Rows past K (the reduction length) and columns
+    // past M / N are read as zeros.
     const int lrow = lane / C::CPR, slot = lane % C::CPR;
     int64_t aoff[C::DA], boff[C::DB];
     int acs[C::DA], bcs[C::DB];
+    // GRAM: the i-th instruction's row is tr_r0 + 2 NW i, a multiple of 4
+    // past tr_r0, so its chunk permutation, and hence its column, is the
+    // instruction-0 one: one column offset per operand (tr_ok*: not past M / N).
+    const int tr_r0 = 2 * wv + (lane >> 5);
+    int64_t tr_a = 0, tr_b = 0;
+    bool tr_oka = false, tr_okb = false;
+    const uintptr_t tr_zero = (uintptr_t)ge_zero16;
+    if (MODE == GE_GRAM) {
+        static_assert(MODE != GE_GRAM || (C::TN == GE_TN && C::DA * 2 * C::NW == TK && C::DB * 2 * C::NW == TK &&
+                                          (2 * C::NW) % 4 == 0),
+                      "GRAM staging: full 256 x 256 tiles, 2 rows per instruction");
+        const int ts = lane & 31;
+        const int c = (((ts >> 1) ^ tr_sig(tr_r0 & 3)) << 1) | (ts & 1);
+        tr_oka = m0 + 8 * c < M;
+        tr_okb = n0 + 8 * c < N;
+        tr_a = tr_oka ? (int64_t)tr_r0 * M + m0 + 8 * c : 0;
+        tr_b = tr_okb ? (int64_t)tr_r0 * N + n0 + 8 * c : 0;
+    } else {
 #pragma unroll
-    for (int i = 0; i < C::DA; ++i) {
-        const int r = (C::NW * i + wv) * C::RPI + lrow;
-        acs[i] = (slot ^ ((r / C::SWZ) % C::CPR)) * 8;
-        aoff[i] = min(m0 + r, M - 1) * K + acs[i];
-    }
+        for (int i = 0; i < C::DA; ++i) {
+            const int r = (C::NW * i + wv) * C::RPI + lrow;
+            acs[i] = (slot ^ ((r / C::SWZ) % C::CPR)) * 8;
+            aoff[i] = min(m0 + r, M - 1) * K + acs[i];
+        }
 #pragma unroll
-    for (int i = 0; i < C::DB; ++i) {
-        const int r = (C::NW * i + wv) * C::RPI + lrow;
-        bcs[i] = (slot ^ ((r / C::SWZ) % C::CPR)) * 8;
-        boff[i] = min(n0 + r, N - 1) * K + bcs[i];
+        for (int i = 0; i < C::DB; ++i) {
+            const int r = (C::NW * i + wv) * C::RPI + lrow;
+            bcs[i] = (slot ^ ((r / C::SWZ) % C::CPR)) * 8;
+            boff[i] = min(n0 + r, N - 1) * K + bcs[i];
+        }
     }
 #define GE_ISSUE(k0, buf)                                                                              \
     do {                                                                                               \
@@ -299,6 +341,36 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_err_kernel(const GeArgs ga)
             __builtin_amdgcn_global_load_lds((ge_gbl_void *)p_, (ge_lds_void *)(sb_ + C::NW * i * C::RPI * TK), 16, 0, 0); \
         }                                                                                              \
     } while (0)
+    // GRAM: X rows k0 + acs[i] (zeros past K, the reduction length, and for
+    // columns past M); the same LDS placement as GE_ISSUE (1 KB per
+    // instruction, 2 rows of 512 bytes)
+#define GE_ISSUE_T(k0, buf)                                                                            \
+    do {                                                                                               \
+        uint16_t *sa_ = glds + (buf) * C::STAGE + wv * C::RPI * TK;                                    \
+        uint16_t *sb_ = sa_ + GE_TM * TK;                                                              \
+        const int64_t kr_ = (int64_t)(k0) + tr_r0;                                                     \
+        const uint16_t *pa_ = A + tr_a + (int64_t)(k0) * M;                                            \
+        const uint16_t *pb_ = Bm + tr_b + (int64_t)(k0) * N;                                           \
+        _Pragma("unroll") for (int i = 0; i < C::DA; ++i)                                              \
+        {                                                                                              \
+            const bool ok_ = tr_oka & (kr_ + 2 * C::NW * i < K);                                       \
+            const uintptr_t p_ = ok_ ? (uintptr_t)(pa_ + (int64_t)(2 * C::NW * i) * M) : tr_zero;     \
+            __builtin_amdgcn_global_load_lds((ge_gbl_void *)p_, (ge_lds_void *)(sa_ + C::NW * i * C::RPI * TK), 16, 0, 0); \
+        }                                                                                              \
+        _Pragma("unroll") for (int i = 0; i < C::DB; ++i)                                              \
+        {                                                                                              \
+            const bool ok_ = tr_okb & (kr_ + 2 * C::NW * i < K);                                       \
+            const uintptr_t p_ = ok_ ? (uintptr_t)(pb_ + (int64_t)(2 * C::NW * i) * N) : tr_zero;     \
+            __builtin_amdgcn_global_load_lds((ge_gbl_void *)p_, (ge_lds_void *)(sb_ + C::NW * i * C::RPI * TK), 16, 0, 0); \
+        }                                                                                              \
+    } while (0)
+#define GE_STAGE_IN(k0, buf)                                                                           \
+    do {                                                                                               \
+        if constexpr (MODE == GE_GRAM)                                                                 \
+            GE_ISSUE_T(k0, buf);                                                                       \
+        else                                                                                           \
+            GE_ISSUE(k0, buf);                                                                         \
+    } while (0)
 
     of32x16_t acc[4][NJ];
 #pragma unroll
@@ -313,8 +385,34 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_err_kernel(const GeArgs ga)
     // multiplies.
     const int fr = lane & 31, fh = lane >> 5;
     V fa[2][4], fb[2][NJ];
+    // GRAM (stage rows = reduction index): one fragment is two LDS
+    // transpose reads (ds_read_b64_tr_b16).  In each 16-lane group g of the
+    // wave, source lane s reads 4 consecutive columns 4 (s % 4) of stage row
+    // 16 kk + 8 (g / 2) + 4 h + s / 4; the read hands output lane i the i-th
+    // column of the group's 16 from those 4 rows, i.e. the 4 reduction
+    // indices 8 (g / 2) + 4 h + 0..3 of MFMA row 16 (g % 2) + i: the A / B
+    // operand layout of v_mfma_f32_32x32x16 (lane l: row l % 32, reduction
+    // indices 8 (l / 32) .. + 7), h = 0 and 1 giving its two halves.
+    const int tg = lane >> 4, trow = 8 * (tg >> 1) + ((lane & 15) >> 2), tq = lane & 3;
+    const int tsig = tr_sig(((lane & 15) >> 2));
+#define GE_TRV(bufp, row, sl)                                                                          \
+    ({                                                                                                 \
+        const auto lo_ = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(                                    \
+            (__attribute__((address_space(3))) ob16x4_t *)((bufp) + (row) * 256 + (((sl) ^ tsig) * 16) + 4 * tq)); \
+        const auto hi_ = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(                                    \
+            (__attribute__((address_space(3))) ob16x4_t *)((bufp) + ((row) + 4) * 256 + (((sl) ^ tsig) * 16) + 4 * tq)); \
+        __builtin_shufflevector(lo_, hi_, 0, 1, 2, 3, 4, 5, 6, 7);                                   \
+    })
 #define GE_FRAG(set, bufp, kk)                                                                         \
     do {                                                                                               \
+        if constexpr (MODE == GE_GRAM) {                                                               \
+            const int row_ = 16 * (kk) + trow;                                                         \
+            _Pragma("unroll") for (int i = 0; i < 4; ++i)                                              \
+                fa[set][i] = GE_TRV(bufp, row_, (wm * 128 + i * 32) / 16 + (tg & 1));                   \
+            _Pragma("unroll") for (int j = 0; j < NJ; ++j)                                             \
+                fb[set][j] = GE_TRV((bufp) + GE_TM * TK, row_, (wn * 32 * NJ + j * 32) / 16 + (tg & 1)); \
+            break;                                                                                     \
+        }                                                                                              \
         const int c_ = 2 * (kk) + fh;                                                                  \
         _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                  \
         {                                                                                              \
@@ -507,16 +605,19 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_err_kernel(const GeArgs ga)
         const int ksteps = (int)((ke - kb + TK - 1) / TK);
 #pragma unroll
         for (int p = 0; p < S - 1; ++p)
-            if (p < ksteps) GE_ISSUE(kb + (int64_t)p * TK, p);
+            if (p < ksteps) GE_STAGE_IN(kb + (int64_t)p * TK, p);
         for (int ks = 0; ks < ksteps; ++ks) {
             ge_wait_copies(min(S - 2, ksteps - 1 - ks) * D);
             asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-            if (ks + S - 1 < ksteps) GE_ISSUE(kb + (int64_t)(ks + S - 1) * TK, (ks + S - 1) % S);
+            if (ks + S - 1 < ksteps) GE_STAGE_IN(kb + (int64_t)(ks + S - 1) * TK, (ks + S - 1) % S);
             GE_COMPUTE(ks % S);
         }
     }
 #undef GE_COMPUTE
 #undef GE_FRAG
+#undef GE_TRV
+#undef GE_STAGE_IN
+#undef GE_ISSUE_T
 #undef GE_ISSUE
 
     // epilogue: accumulator v of lane l in a 32 x 32 tile is row
@@ -779,15 +880,15 @@ static int device_cus()
 // the last round would fill at most half of the CUs, its tiles run as
 // 256 x 128 halves instead (the round then takes half a tile's time).
 // Returns the number of workgroup partials written.
-template <bool F16, int MODE, int NJ, int TK = HD_GE_TK, int S = HD_GE_STAGES>
+template <bool F16, int MODE, int NJ, int TK = HD_GE_TK, int S = HD_GE_STAGES, int WN = HD_GE_WN>
 static hipError_t ge_launch(const GeArgs &ga, int64_t grid, hipStream_t st)
 {
-    typedef GeCfg<TK, S, HD_GE_WN, NJ> C;
+    typedef GeCfg<TK, S, WN, NJ> C;
     if (grid <= 0) return hipSuccess;
-    const hipError_t e = hipFuncSetAttribute((const void *)gemm_err_kernel<F16, MODE, TK, S, HD_GE_WN, NJ>,
+    const hipError_t e = hipFuncSetAttribute((const void *)gemm_err_kernel<F16, MODE, TK, S, WN, NJ>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS);
     if (e != hipSuccess) return e;
-    gemm_err_kernel<F16, MODE, TK, S, HD_GE_WN, NJ><<<(unsigned)grid, C::THREADS, C::LDS, st>>>(ga);
+    gemm_err_kernel<F16, MODE, TK, S, WN, NJ><<<(unsigned)grid, C::THREADS, C::LDS, st>>>(ga);
     return hipGetLastError();
 }
 
@@ -936,42 +1037,6 @@ hipError_t launch_output_error_codes(int fmt, int B, const void *X, int64_t M, c
 // output_error_gram(): e and the diagonal sums per row (one workgroup per
 //                  row), then C E^T over each item's K range with the
 //                  epilogue sum of acc * e, then a fixed-order final sum.
-
-// Xt[k][m] = X[m][k] for m < M, 0 for M <= m < M8 (16-bit values; K % 8 == 0,
-// M8 % 8 == 0).  64 x 64 tiles through LDS with 16-byte global loads and
-// stores on both sides.
-__global__ __launch_bounds__(256) void xt_transpose_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t K,
-                                                           int64_t M8, uint16_t *__restrict__ Xt)
-{
-    __shared__ uint16_t t[64][66];
-    const int64_t m0 = (int64_t)blockIdx.y * 64, k0 = (int64_t)blockIdx.x * 64;
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int c = tid + 256 * q, r = c >> 3, kc = (c & 7) * 8;
-        const int64_t m = m0 + r, k = k0 + kc;
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (m < M && k < K) v = *reinterpret_cast<const uint4 *>(X + m * K + k);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            t[r][kc + 2 * j] = (uint16_t)(w[j] & 0xFFFFu);
-            t[r][kc + 2 * j + 1] = (uint16_t)(w[j] >> 16);
-        }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int c = tid + 256 * q, kr = c >> 3, mc = (c & 7) * 8;
-        const int64_t k = k0 + kr, m = m0 + mc;
-        if (k < K && m < M8) {
-            uint32_t o[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) o[j] = (uint32_t)t[mc + 2 * j][kr] | ((uint32_t)t[mc + 2 * j + 1][kr] << 16);
-            *reinterpret_cast<uint4 *>(Xt + k * M8 + m) = make_uint4(o[0], o[1], o[2], o[3]);
-        }
-    }
-}
 
 // h (copied unless it already is the buffer's), sqrt(h) and 1/sqrt(h) (0 for h = 0).
 __global__ __launch_bounds__(256) void gram_prep_kernel(const float *__restrict__ hin, int64_t K, float *__restrict__ h,
@@ -1263,11 +1328,7 @@ GramLayout output_gram_layout(int64_t K)
     return L;
 }
 
-size_t output_gram_ws(int64_t M, int64_t K)
-{
-    const int64_t M8 = (M + 7) / 8 * 8;
-    return (size_t)std::max(al256(K * M8 * 2), (int64_t)hdiag_ws(M, K));
-}
+size_t output_gram_ws(int64_t M, int64_t K) { return (size_t)std::max<int64_t>(256, (int64_t)hdiag_ws(M, K)); }
 
 // Schedule of the C E^T walk (the QUAD mode's gangs) over nt E tiles: with
 // P = CUs / 8 workgroups per XCD, the E tiles per group qe (and qa = min(4,
@@ -1275,7 +1336,8 @@ size_t output_gram_ws(int64_t M, int64_t K)
 // real tiles, 8 gangs of P slots, when that share is at least 90%;
 // otherwise gangs of all nt tiles with one band per panel, CUs / nt of them.
 // The schedule setting HD_SCHED_GRAM_GANGS = g > 0 forces the second form
-// with g gangs.
+// with g gangs; HD_SCHED_GRAM_BANDS = a > 0 the first with qa = a and qe =
+// max(1, P / a) (at most nt).
 struct GramPlan {
     int qa, qe, qg, qper;
     int64_t qcpg, qcols, wgs;
@@ -1295,6 +1357,12 @@ static GramPlan gram_plan(int64_t nt, int64_t K)
             bqe = qe;
             bqa = qa;
         }
+    }
+    const int64_t bands = std::min<int64_t>(schedule_setting(HD_SCHED_GRAM_BANDS), std::max<int64_t>(mt, 1));
+    if (forced <= 0 && bands > 0) {
+        best = 1.0;
+        bqa = bands;
+        bqe = std::min<int64_t>(std::max<int64_t>(1, per / bands), std::max<int64_t>(nt, 1));
     }
     if (forced <= 0 && best >= 0.9) {
         g.qa = (int)bqa;
@@ -1342,15 +1410,13 @@ hipError_t launch_output_gram(const void *X, int64_t M, int64_t K, const float *
         h = gh;
     }
     gram_prep_kernel<<<(unsigned)((K + 255) / 256), 256, 0, st>>>(h, K, gh, sq, r);
-    const int64_t M8 = (M + 7) / 8 * 8;
-    if (M8 == 0) {
+    if (M == 0) {
         gram_zero_kernel<<<1024, 256, 0, st>>>(C, K * K);
         return hipGetLastError();
     }
-    uint16_t *Xt = static_cast<uint16_t *>(ws);
-    const dim3 tg((unsigned)((K + 63) / 64), (unsigned)((M8 + 63) / 64));
-    xt_transpose_kernel<<<tg, 256, 0, st>>>(static_cast<const uint16_t *>(X), M, K, M8, Xt);
-    GeArgs ga = ge_args(Xt, Xt, K, K, M8);
+    // X^T X straight from row-major X (the GRAM mode's transposed LDS reads)
+    const uint16_t *Xb = static_cast<const uint16_t *>(X);
+    GeArgs ga = ge_args(Xb, Xb, K, K, M);
     const int64_t items = (int64_t)ga.mt * (ga.mt + 1) / 2;
     ga.nlin = (int)items;
     ga.r = r;

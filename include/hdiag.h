@@ -128,9 +128,19 @@ typedef enum {
  *                         instead of its per-XCD schedule (the order of the
  *                         float64 partial sums changes);
  *   HD_SCHED_GPTQ_TILE  - gptq_*: 64 or 128 forces the tile width of the
- *                         factorisation's matrix-core products.
+ *                         factorisation's matrix-core products;
+ *   HD_SCHED_GRAM_BANDS - output_error_gram(_batch): a > 0 runs the per-XCD
+ *                         walk with a bands of C per panel and
+ *                         max(1, CUs / 8 / a) tiles of E per group (ignored
+ *                         while HD_SCHED_GRAM_GANGS is set; the order of the
+ *                         float64 partial sums changes).
  * Errors: HD_ERR_INVALID_ARG for an unknown setting or value. */
-typedef enum { HD_SCHED_GRAM_GANGS = 0, HD_SCHED_GPTQ_TILE = 1, HD_SCHED_COUNT = 2 } hd_schedule;
+typedef enum {
+    HD_SCHED_GRAM_GANGS = 0,
+    HD_SCHED_GPTQ_TILE = 1,
+    HD_SCHED_GRAM_BANDS = 2,
+    HD_SCHED_COUNT = 3
+} hd_schedule;
 hd_status hdiag_set_schedule(hd_schedule knob, int32_t value);
 
 /* ---------------------------------------------------------------- hdiag --- */
@@ -338,8 +348,8 @@ hd_status output_error_codes(hd_format fmt, int32_t B, const void *X, hd_dtype x
  * the products run on the bf16 MFMA units with float32 accumulation.
  * h (optional, device, float [K]): hdiag(X) already computed on the same X;
  * NULL computes it here.  The buffer stays valid as long as X is unchanged.
- * workspace: ws_bytes >= output_gram_workspace_size(M, K) (X^T is staged
- * there).
+ * workspace: ws_bytes >= output_gram_workspace_size(M, K) (hdiag's partial
+ * sums when h is NULL; X itself is read in place).
  *
  * output_reference_gram() writes ||X W^T||_F^2 (double) to the device scalar
  * *ysq; output_error_gram() writes ||X Wq^T - X W^T||_F / sqrt(*ysq) to *out,
@@ -363,8 +373,8 @@ hd_status output_error_codes(hd_format fmt, int32_t B, const void *X, hd_dtype x
  * workspace: ws_bytes >= output_error_gram_workspace_size(N, K); each call
  * needs its own.  Calls that share `gram` may run concurrently (it is only
  * read).
- * Schedule: HD_SCHED_GRAM_GANGS (hdiag_set_schedule) changes only the order
- * of the float64 partial sums.
+ * Schedule: HD_SCHED_GRAM_GANGS and HD_SCHED_GRAM_BANDS (hdiag_set_schedule)
+ * change only the order of the float64 partial sums.
  * Errors: HD_ERR_INVALID_ARG as quantize_blocks for fmt / B / N / K, NULL or
  * misaligned pointers, a short buffer or workspace, K % 8 != 0 for
  * output_gram; HD_ERR_UNSUPPORTED for a float32 X. */

@@ -166,10 +166,12 @@ def test_schedule_settings():
     L = hd.lib()
     assert L.hdiag_set_schedule(hd.SCHED_GRAM_GANGS, 0) == hd.HD_OK
     assert L.hdiag_set_schedule(hd.SCHED_GPTQ_TILE, 0) == hd.HD_OK
-    assert L.hdiag_set_schedule(2, 0) == hd.HD_ERR_INVALID_ARG
+    assert L.hdiag_set_schedule(hd.SCHED_GRAM_BANDS, 0) == hd.HD_OK
+    assert L.hdiag_set_schedule(3, 0) == hd.HD_ERR_INVALID_ARG
     assert "unknown schedule" in L.hdiag_last_error().decode()
     assert L.hdiag_set_schedule(hd.SCHED_GRAM_GANGS, -1) == hd.HD_ERR_INVALID_ARG
     assert L.hdiag_set_schedule(hd.SCHED_GPTQ_TILE, 96) == hd.HD_ERR_INVALID_ARG
+    assert L.hdiag_set_schedule(hd.SCHED_GRAM_BANDS, -2) == hd.HD_ERR_INVALID_ARG
     for v in (64, 128, 0):
         hd.hdiag_set_schedule(hd.SCHED_GPTQ_TILE, v)
 

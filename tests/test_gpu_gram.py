@@ -210,8 +210,8 @@ def test_output_error_gram_no_rows():
 
 def test_output_error_gram_partition_and_repeat():
     """How the K-block pairs are split between workgroups (the schedule
-    setting SCHED_GRAM_GANGS) changes only the summation order; repeated
-    calls agree bit for bit."""
+    settings SCHED_GRAM_GANGS and SCHED_GRAM_BANDS) changes only the
+    summation order; repeated calls agree bit for bit."""
     M, N, K, B = 600, 300, 1536, 32
     X, W = dev(acts(M, K, 21)), dev(weights_for(hd.INT8_E4M3, N, K, 22))
     c, s, _ = hd.quantize_blocks(hd.SSE_OPT, hd.INT8_E4M3, B, W)
@@ -225,8 +225,15 @@ def test_output_error_gram_partition_and_repeat():
             b = hd.output_error_gram(hd.INT8_E4M3, B, c, s, W, gram, ysq).item()
             assert a == b
             vals.append(a)
+        for qa in (1, 2, 3, 5, 6, 8, 64):
+            hd.hdiag_set_schedule(hd.SCHED_GRAM_BANDS, qa)
+            a = hd.output_error_gram(hd.INT8_E4M3, B, c, s, W, gram, ysq).item()
+            b = hd.output_error_gram(hd.INT8_E4M3, B, c, s, W, gram, ysq).item()
+            assert a == b
+            vals.append(a)
     finally:
         hd.hdiag_set_schedule(hd.SCHED_GRAM_GANGS, 0)
+        hd.hdiag_set_schedule(hd.SCHED_GRAM_BANDS, 0)
     assert max(vals) == pytest.approx(min(vals), rel=1e-9)
     generic = hd.output_error(X, W, hd.dequantize(hd.INT8_E4M3, B, c, s, N, K)).item()
     assert vals[0] == pytest.approx(generic, rel=1e-4)
