@@ -250,6 +250,7 @@ def main():
     # (weight, candidate) pairs the searches evaluate per launch: one
     # instrumented call per (B, method) before the warm-up (outside the timed region, and before the profiled step)
     evals = {"search_sse": [], "search_h": []}
+    hd.hdiag(X, out=h, workspace=ws_h)  # the H search's weights (the step recomputes them)
     for B in blocks:
         for mname, m in methods:
             if m == hd.NAIVE:
