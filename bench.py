@@ -198,6 +198,21 @@ def main():
     werr = torch.empty((len(blocks), 3), dtype=torch.float64, device=dev)
     oerr = torch.empty((len(blocks), 3), dtype=torch.float64, device=dev)
 
+    # (weight, candidate) pairs the searches evaluate per launch: one
+    # instrumented call per (B, method) outside the timed region, before the
+    # copy probe that opens the profiled part
+    evals = {"search_sse": [], "search_h": []}
+    hd.hdiag(X, out=h, workspace=ws_h)  # the H search's weights (the step recomputes them)
+    for B in blocks:
+        for mname, m in methods:
+            if m == hd.NAIVE:
+                continue
+            ev = torch.zeros(1, dtype=torch.int64, device=dev)
+            hd.quantize_blocks_instrumented(m, fmt, B, W, ev, h=h if m == hd.H_OPT else None)
+            evals["search_" + mname].append(ev)
+    torch.cuda.synchronize()
+    evals = {k: sum(e.item() for e in v) / len(v) for k, v in evals.items()}
+
     if args.copy_probe_mb:
         # a plain device-to-device copy of a known size (hipMemcpyAsync runs it
         # as one copy kernel): reads and writes args.copy_probe_mb MiB
@@ -247,19 +262,6 @@ def main():
                   lambda: hd.output_error_gram_batch(items, W, gram, ysq, sums=osums, workspace=ws_o,
                                                      out=oerr.view(-1)), rec)
 
-    # (weight, candidate) pairs the searches evaluate per launch: one
-    # instrumented call per (B, method) before the warm-up (outside the timed region, and before the profiled step)
-    evals = {"search_sse": [], "search_h": []}
-    hd.hdiag(X, out=h, workspace=ws_h)  # the H search's weights (the step recomputes them)
-    for B in blocks:
-        for mname, m in methods:
-            if m == hd.NAIVE:
-                continue
-            ev = torch.zeros(1, dtype=torch.int64, device=dev)
-            hd.quantize_blocks_instrumented(m, fmt, B, W, ev, h=h if m == hd.H_OPT else None)
-            evals["search_" + mname].append(ev)
-    torch.cuda.synchronize()
-    evals = {k: sum(e.item() for e in v) / len(v) for k, v in evals.items()}
 
     for _ in range(args.warmup):
         step(False)
@@ -847,7 +849,8 @@ def hbm_suite(args, dev):
     hdiag, Naive quantize (NVFP4 B = 16, INT8 B = 128), dequantize (to float32
     and to bfloat16) and the weight error; median of 10 launches (HIP events
     around the launch alone), algorithmic bytes / time against 8 TB/s, beside
-    a 4 GiB device-to-device copy as the measured ceiling."""
+    a 4 GiB device-to-device copy and torch kernels with the stages' byte
+    mixes as references."""
     import torch
 
     import block_scaled_precision_hdiag_amd as hd
@@ -888,6 +891,20 @@ def hbm_suite(args, dev):
     dst = torch.empty_like(src)
     put("device_copy_4GiB", timed(lambda: dst.copy_(src)), 2 * src.numel())
     del src, dst
+    # torch's own kernels with the byte mixes of the stages, as references:
+    # a read of W alone (sum), 2 bytes read for 0.5 written per weight (a sum
+    # over groups of 4: the NVFP4 encode's code bytes) and 0.5 read for 2
+    # written (a broadcast of a quarter-size bf16 tensor: the dequantize to
+    # bfloat16)
+    N0, K0 = W.shape
+    o4 = torch.empty((N0, K0 // 4), dtype=torch.bfloat16, device=dev)
+    o1 = torch.empty((), dtype=torch.bfloat16, device=dev)
+    put("torch_sum_read_W", timed(lambda: torch.sum(W.view(-1), dim=0, out=o1)), W.numel() * 2)
+    put("torch_reduce4_W", timed(lambda: torch.sum(W.view(N0, K0 // 4, 4), dim=-1, out=o4)), W.numel() * 2.5)
+    wb = torch.empty_like(W)
+    put("torch_expand4_W", timed(lambda: wb.view(N0, K0 // 4, 4).copy_(o4.unsqueeze(-1).expand(N0, K0 // 4, 4))),
+        W.numel() * 2.5)
+    del o4, o1, wb
     h = torch.empty(K, dtype=torch.float32, device=dev)
     ws_h = torch.empty(hd.hdiag_workspace_size(M, K), dtype=torch.uint8, device=dev)
     put("hdiag", timed(lambda: hd.hdiag(X, out=h, workspace=ws_h)), M * K * 2 + K * 4)
@@ -1020,17 +1037,21 @@ def _dispatches(rows, with_counters):
             e["c"][r["Counter_Name"]] = float(r["Counter_Value"])
     state = {}
     out = []
-    started = False  # dispatches before the first step's hdiag are set-up work
     for k in sorted(by):
         e = by[k]
         e["stage"] = _stage_of(e["name"], state)
-        started = started or e["stage"] == "hdiag"
-        if not started and e["stage"] not in ("copy",):
-            e["stage"] = "setup"
         out.append(e)
-    copies = [e for e in out if e["stage"] == "copy"]
-    if copies:
-        max(copies, key=lambda e: e["t"])["stage"] = "copy_probe"
+    copies = [i for i, e in enumerate(out) if e["stage"] == "copy"]
+    probe = max(copies, key=lambda i: out[i]["t"]) if copies else -1
+    if probe >= 0:
+        out[probe]["stage"] = "copy_probe"
+    # set-up work (the instrumented search calls and their hdiag among it):
+    # every dispatch before the first hdiag that follows the copy probe
+    started = False
+    for i, e in enumerate(out):
+        started = started or (i > probe and e["stage"] == "hdiag")
+        if not started and e["stage"] not in ("copy", "copy_probe"):
+            e["stage"] = "setup"
     return out
 
 
@@ -1047,7 +1068,7 @@ def summarize_profile(d, probe_mb, cmds):
     into profiles/."""
     sh = source_hash()
     tr = _dispatches(_read_csv(_find(os.path.join(d, "trace"), "kernel_trace.csv")), False)
-    steps = sum(1 for e in tr if "hdiag_final" in e["name"])
+    steps = sum(1 for e in tr if "hdiag_final" in e["name"] and e["stage"] == "hdiag")
     # kernel statistics, one row per (kernel, stage)
     agg = {}
     for e in tr:
@@ -1090,7 +1111,7 @@ def summarize_profile(d, probe_mb, cmds):
         c["ns"] += e["t"]
         for k, v in e["c"].items():
             c[k] = c.get(k, 0.0) + v
-    csteps = sum(1 for e in va if "hdiag_final" in e["name"])
+    csteps = sum(1 for e in va if "hdiag_final" in e["name"] and e["stage"] == "hdiag")
     rec = {}
     lines = ["# Executed VALU / MFMA work per call: the bench.py step (INT8 / E4M3 scales, W 2560x9728, X 16384x9728)",
              "", "One MI355X (gfx950).  One counter pass, from the repository root:", "", "    " + cmds["valu"], "",
