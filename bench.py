@@ -52,7 +52,7 @@ COUNTERS_PROFILE = os.path.join(ROOT, "profiles", "int8_down_proj_2560x9728_coun
 # sources whose kernels the INT8 step never launches (other formats' searches,
 # the FP16-scale alternation, GPTQ, per-tensor scaling), and the host-only C
 # ABI wrapper and launcher declarations (no device code)
-_NOT_IN_STEP = {"alt_f16.hip", "gptq.hip", "tscale.hip", "search_e2m1_elems.hip", "search_e4m3_elems.hip",
+_NOT_IN_STEP = {"alt_f16.hip", "probe.hip", "gptq.hip", "tscale.hip", "search_e2m1_elems.hip", "search_e4m3_elems.hip",
                 "abi.cpp", "kernels.hpp"}
 
 
@@ -849,8 +849,9 @@ def hbm_suite(args, dev):
     hdiag, Naive quantize (NVFP4 B = 16, INT8 B = 128), dequantize (to float32
     and to bfloat16) and the weight error; median of 10 launches (HIP events
     around the launch alone), algorithmic bytes / time against 8 TB/s, beside
-    a 4 GiB device-to-device copy and torch kernels with the stages' byte
-    mixes as references."""
+    a 4 GiB device-to-device copy, torch kernels with the stages' byte mixes
+    and the library's streaming probes (the stages' loads and stores with
+    next to no arithmetic) as references."""
     import torch
 
     import block_scaled_precision_hdiag_amd as hd
@@ -904,7 +905,20 @@ def hbm_suite(args, dev):
     wb = torch.empty_like(W)
     put("torch_expand4_W", timed(lambda: wb.view(N0, K0 // 4, 4).copy_(o4.unsqueeze(-1).expand(N0, K0 // 4, 4))),
         W.numel() * 2.5)
-    del o4, o1, wb
+    # the library's streaming probes: the same loads and stores as the encode
+    # (NVFP4 B = 16) and the dequantize to bfloat16, and a pure read and a
+    # pure write, with next to no arithmetic
+    nW = W.numel()
+    pc = torch.empty(nW // 2, dtype=torch.uint8, device=dev)
+    ps = torch.empty(nW // 16, dtype=torch.uint8, device=dev)
+    pr = torch.empty(nW // 8192, dtype=torch.int32, device=dev)
+    put("probe_read_W", timed(lambda: hd.hdiag_stream_probe(hd.PROBE_READ, nW, in0=W, out0=pr)), nW * 2)
+    put("probe_encode_W", timed(lambda: hd.hdiag_stream_probe(hd.PROBE_ENCODE, nW, in0=W, out0=pc, out1=ps)),
+        nW * 2 + nW // 2 + nW // 16)
+    put("probe_write_W", timed(lambda: hd.hdiag_stream_probe(hd.PROBE_WRITE, nW, out0=wb)), nW * 2)
+    put("probe_dequant_W", timed(lambda: hd.hdiag_stream_probe(hd.PROBE_DEQUANT, nW, in0=pc, in1=ps, out0=wb)),
+        nW // 2 + nW // 16 + nW * 2)
+    del o4, o1, wb, pc, ps, pr
     h = torch.empty(K, dtype=torch.float32, device=dev)
     ws_h = torch.empty(hd.hdiag_workspace_size(M, K), dtype=torch.uint8, device=dev)
     put("hdiag", timed(lambda: hd.hdiag(X, out=h, workspace=ws_h)), M * K * 2 + K * 4)

@@ -25,6 +25,7 @@ LIB_PATH = os.path.join(_HERE, "libhdiag.so")
 HD_OK, HD_ERR_INVALID_ARG, HD_ERR_UNSUPPORTED, HD_ERR_HIP = 0, -1, -2, -3
 HD_F32, HD_BF16 = 0, 1
 SCHED_GRAM_GANGS, SCHED_GPTQ_TILE, SCHED_GRAM_BANDS = 0, 1, 2
+PROBE_READ, PROBE_ENCODE, PROBE_WRITE, PROBE_DEQUANT = 0, 1, 2, 3
 NAIVE, SSE_OPT, H_OPT, NAIVE_OCP = 0, 1, 2, 3
 INT8_E4M3, NVFP4, MXFP4, MXFP8, FP8_E4M3S = 0, 1, 2, 3, 4
 NVFP4_UE4M4, NVFP4_UE5M3, NVINT4 = 5, 6, 7
@@ -47,7 +48,7 @@ EXPORTS = ["hdiag_set_schedule", "hdiag", "hdiag_workspace_size", "hdiag_noalloc
            "quantize_blocks_tensor_scaled_workspace_size", "dequantize_tensor_scaled", "gptq_hessian", "gptq_hessian_workspace_size", "gptq_quantize",
            "gptq_workspace_size", "gptq_factor", "gptq_factor_size", "gptq_factor_workspace_size",
            "gptq_quantize_factored",
-           "hdiag_strerror", "hdiag_last_error", "hdiag_format_info", "hdiag_version"]
+           "hdiag_strerror", "hdiag_last_error", "hdiag_format_info", "hdiag_version", "hdiag_stream_probe"]
 
 
 class HdiagError(RuntimeError):
@@ -72,6 +73,7 @@ def lib():
         L.hdiag_workspace_size.argtypes = [i64, i64]
         L.hdiag_noalloc.argtypes = [P, i32, i64, i64, P, P]
         L.hdiag_set_schedule.argtypes = [i32, i32]
+        L.hdiag_stream_probe.argtypes = [i32, i64, P, P, P, P, P]
         L.hdiag_workspace_size.restype = sz
         L.quantize_blocks.argtypes = [i32, i32, i32, P, i32, i64, i64, P, P, P, P, P]
         L.quantize_blocks_instrumented.argtypes = [i32, i32, i32, P, i32, i64, i64, P, P, P, P, P, P]
@@ -197,6 +199,14 @@ def hdiag_set_schedule(knob, value):
     """Set a process-wide schedule setting (SCHED_GRAM_GANGS, SCHED_GPTQ_TILE,
     SCHED_GRAM_BANDS; 0 = automatic); host-only."""
     _check(lib().hdiag_set_schedule(knob, value), "hdiag_set_schedule")
+
+
+def hdiag_stream_probe(kind, n, in0=None, in1=None, out0=None, out1=None, device=None):
+    """One streaming probe of n 16-bit elements (PROBE_READ, PROBE_ENCODE,
+    PROBE_WRITE, PROBE_DEQUANT; buffers as include/hdiag.h gives them)."""
+    t = next(x for x in (in0, out0) if x is not None)
+    _check(lib().hdiag_stream_probe(kind, n, _ptr(in0), _ptr(in1), _ptr(out0), _ptr(out1), _stream(_dev(t))),
+           "hdiag_stream_probe")
 
 
 def hdiag_workspace_size(M, K):

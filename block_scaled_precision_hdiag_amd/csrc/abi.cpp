@@ -134,6 +134,21 @@ hd_status hdiag_format_info(hd_format fmt, int32_t B, int *elem_bits, int *scale
     return ok();
 }
 
+hd_status hdiag_stream_probe(hd_probe kind, int64_t n, const void *in0, const void *in1, void *out0, void *out1,
+                             void *stream)
+{
+    HD_REQUIRE(kind >= HD_PROBE_READ && kind <= HD_PROBE_DEQUANT, "unknown probe kind %d", (int)kind);
+    HD_REQUIRE(n >= 0 && n % 8192 == 0, "n=%lld is not a non-negative multiple of 8192", (long long)n);
+    if (n == 0) return ok();
+    HD_CHECK_PTR(in0, kind != HD_PROBE_WRITE);
+    HD_CHECK_PTR(out0, true);
+    if (kind == HD_PROBE_ENCODE)
+        HD_REQUIRE(out1 != nullptr && ((uintptr_t)out1 & 3u) == 0, "out1 is NULL or not 4-byte aligned");
+    if (kind == HD_PROBE_DEQUANT) HD_REQUIRE(in1 != nullptr, "in1 is NULL");
+    return hip_status(hd::launch_stream_probe(kind, n, in0, in1, out0, out1, (hipStream_t)stream),
+                      "hdiag_stream_probe");
+}
+
 size_t hdiag_workspace_size(int64_t M, int64_t K)
 {
     if (M < 0 || K <= 0) return 0;

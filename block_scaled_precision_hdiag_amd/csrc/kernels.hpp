@@ -124,4 +124,8 @@ hipError_t launch_gptq_factored(int method, int fmt, int B, const void *W, int w
 hipError_t launch_tensor_scale(int fmt, const void *W, int wdt, int64_t N, int64_t K, float *tscale, float *Wp,
                                void *ws, hipStream_t st);
 
+// measurement probes (probe.hip)
+hipError_t launch_stream_probe(int kind, int64_t n, const void *in0, const void *in1, void *out0, void *out1,
+                               hipStream_t st);
+
 }  // namespace hd

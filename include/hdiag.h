@@ -527,6 +527,32 @@ hd_status hdiag_format_info(hd_format fmt, int32_t B, int *elem_bits, int *scale
 /* Library version string.  Host-only. */
 const char *hdiag_version(void);
 
+/* ---------------------------------------------------------- measurement --- */
+
+/* Streaming probes: kernels with the memory access patterns of the
+ * HBM-bound stages and next to no arithmetic, for measuring the bandwidth a
+ * kernel with those loads and stores reaches at best (no passage of the
+ * pages defines them; they serve the measurement of the stages against the
+ * HBM roofline).  n counts 16-bit elements, n % 8192 == 0; every buffer is
+ * device memory, 16-byte aligned (out1 of ENCODE and in1 of DEQUANT:
+ * 4-byte), and caller-allocated:
+ *   HD_PROBE_READ:    in0 = n bf16 read; out0 = n / 8192 uint32, word w the
+ *                     XOR of the 32-bit words of elements 8192 w .. + 8191;
+ *   HD_PROBE_ENCODE:  in0 = n bf16; out0 = n / 2 bytes, one 32-bit word per
+ *                     8 elements (the XOR of their four words); out1 = n / 16
+ *                     bytes, per 16 elements the low byte of the first
+ *                     8-element word (the NVFP4 B = 16 encode's byte mix);
+ *   HD_PROBE_WRITE:   out0 = n bf16, 32-bit word i = i;
+ *   HD_PROBE_DEQUANT: in0 = n / 2 bytes (a 32-bit word c per 8 elements), in1
+ *                     = n / 16 bytes (a byte s per 16 elements); out0 = n bf16,
+ *                     per 8 elements the words {c ^ s, c + s, 3 c, c >> 3} (the
+ *                     dequantize-to-bfloat16 byte mix).
+ * Errors: HD_ERR_INVALID_ARG for an unknown kind, n < 0, n % 8192 != 0, or a
+ * NULL or misaligned buffer the kind uses. */
+typedef enum { HD_PROBE_READ = 0, HD_PROBE_ENCODE = 1, HD_PROBE_WRITE = 2, HD_PROBE_DEQUANT = 3 } hd_probe;
+hd_status hdiag_stream_probe(hd_probe kind, int64_t n, const void *in0, const void *in1, void *out0, void *out1,
+                             void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -260,3 +260,19 @@ def test_gram_validation():
     assert rc == hd.HD_ERR_INVALID_ARG and "codes" in L.hdiag_last_error().decode()
     rc = L.output_error_gram(hd.INT8_E4M3, 32, A, A, A, hd.HD_BF16, 4, K, A, gb, A, None, None, A, 1 << 30, None)
     assert rc == hd.HD_ERR_INVALID_ARG and "out" in L.hdiag_last_error().decode()
+
+
+def test_stream_probe_validation():
+    """hdiag_stream_probe rejects unknown kinds, sizes that are not whole
+    8192-element groups and missing buffers before launching anything."""
+    L = hd.lib()
+    buf = ctypes.c_void_p(4096)  # never dereferenced: every call below fails or is empty
+    assert L.hdiag_stream_probe(7, 8192, buf, None, buf, None, None) == hd.HD_ERR_INVALID_ARG
+    assert "unknown probe" in L.hdiag_last_error().decode()
+    assert L.hdiag_stream_probe(hd.PROBE_READ, 4096, buf, None, buf, None, None) == hd.HD_ERR_INVALID_ARG
+    assert L.hdiag_stream_probe(hd.PROBE_READ, -8192, buf, None, buf, None, None) == hd.HD_ERR_INVALID_ARG
+    assert L.hdiag_stream_probe(hd.PROBE_READ, 8192, None, None, buf, None, None) == hd.HD_ERR_INVALID_ARG
+    assert L.hdiag_stream_probe(hd.PROBE_ENCODE, 8192, buf, None, buf, None, None) == hd.HD_ERR_INVALID_ARG
+    assert L.hdiag_stream_probe(hd.PROBE_DEQUANT, 8192, buf, None, buf, None, None) == hd.HD_ERR_INVALID_ARG
+    assert L.hdiag_stream_probe(hd.PROBE_WRITE, 8192, None, None, None, None, None) == hd.HD_ERR_INVALID_ARG
+    assert L.hdiag_stream_probe(hd.PROBE_WRITE, 0, None, None, None, None, None) == hd.HD_OK
