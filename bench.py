@@ -767,6 +767,15 @@ def layer_suite(args, dev, ci):
     gram_pass(False)
     torch.cuda.synchronize()
     print("config %d: warm-up pass done" % ci, file=sys.stderr, flush=True)
+    # (weight, candidate) pairs each search evaluates (h is the warm-up's)
+    pairs = {}
+    for q, (f, B, m) in enumerate(quants):
+        if m != hd.NAIVE:
+            ev = torch.zeros(1, dtype=torch.int64, device=dev)
+            hd.quantize_blocks_instrumented(m, f, B, W, ev, h=h if m == hd.H_OPT else None)
+            pairs[qstage[q]] = ev
+    torch.cuda.synchronize()
+    pairs = {k: v.item() for k, v in pairs.items()}
     t0 = time.perf_counter()
     for _ in range(args.steps):
         gram_pass(True)
@@ -813,12 +822,19 @@ def layer_suite(args, dev, ci):
             cb = 0.5 if f in hd.FOUR_BIT else 1.0
             stages[st] = _roof("hbm", nw * (2 + cb) + nw // B, ms)
         elif st in qmeta:
+            # the search: its work is the pairs it evaluated; the executed VALU
+            # rate (and so the fraction of peak) needs counters, which this
+            # suite does not take
             f, B, m = qmeta[st]
             nc = hd.hdiag_format_info(f, 16)[2]
-            r = _roof("alu", nw * nc * SEARCH_OPS[mname[m]], ms)
-            r["basis"] = "full-grid equivalent"
-            r["gweights_per_s"] = round(nw / (ms * 1e-3) / 1e9, 2)
-            stages[st] = r
+            t = ms * 1e-3
+            stages[st] = {"bound": "alu", "unit": "Tops/s", "peak": round(VALU_PEAK_TOPS, 3), "avg_ms": round(ms, 4),
+                          "gweights_per_s": round(nw / t / 1e9, 2),
+                          "evaluated_pairs_per_launch": int(pairs[st]),
+                          "candidates_per_weight": round(pairs[st] / nw, 3),
+                          "gpairs_per_s": round(pairs[st] / t / 1e9, 2),
+                          "full_grid_equivalent_tops": round(nw * nc * SEARCH_OPS[mname[m]] / t / 1e12, 3),
+                          "achieved": None, "frac": None}
         elif st == "dequantize":
             stages[st] = {"avg_ms": round(ms, 4)}
         else:
