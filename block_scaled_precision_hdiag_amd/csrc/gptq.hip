@@ -6,8 +6,10 @@
 // propagated through H^-1).
 //
 // Pipeline (all on the caller's stream, no host synchronisation):
-//   1. H = X^T X (gptq_hessian): X is transposed into the workspace and the
-//      bf16 MFMA product of output_reference computes Xt Xt^T in float32
+//   1. H = X^T X (gptq_hessian): for K % 8 == 0 the bf16 MFMA product of
+//      output_gram read straight from row-major X, its lower tile triangle
+//      computed and each element stored with its mirror; otherwise X is
+//      transposed into the workspace and the full product computed; float32
 //      (bf16 products are exact; the sums carry float32 accumulation).
 //   2. h = diag(H), lambda = damp * mean(h) (1 if the mean is 0).
 //   3. GPTQ-Ord only: the method's own scales on W, the h-weighted loss of
@@ -48,7 +50,9 @@ namespace hd {
 
 // --------------------------------------------------------------- helpers ---
 
-// Xt[k][m] = X[m][k] for m < M, 0 for M <= m < M8 (bf16 bits).
+// Xt[k][m] = X[m][k] for m < M, 0 for M <= m < M8 (bf16 bits): the staging of
+// the Hessian's product when K % 8 != 0 (rows of X then are not whole 16-byte
+// chunks, which the in-place product reads).
 __global__ __launch_bounds__(256) void gptq_transpose_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t K,
                                                              int64_t M8, uint16_t *__restrict__ Xt)
 {
@@ -887,6 +891,7 @@ static int64_t al256(int64_t x) { return (x + 255) / 256 * 256; }
 
 int64_t gptq_hessian_ws(int64_t M, int64_t K)
 {
+    if (K % 8 == 0) return 256;  // nothing is staged: X is read in place
     const int64_t M8 = (M + 7) / 8 * 8;
     return al256(K * M8 * 2) + al256(output_gemm_parts_bytes(K, K));
 }
@@ -911,11 +916,15 @@ __global__ __launch_bounds__(256) void gptq_zero_kernel(float *__restrict__ p, i
 
 hipError_t launch_gptq_hessian(const void *X, int64_t M, int64_t K, float *H, void *ws, hipStream_t st)
 {
-    const int64_t M8 = (M + 7) / 8 * 8;
-    if (M8 == 0) {  // no rows: H = 0
+    if (M == 0) {  // no rows: H = 0
         gptq_zero_kernel<<<1024, 256, 0, st>>>(H, K * K);
         return hipGetLastError();
     }
+    // K % 8 == 0: the lower tile triangle of X^T X, read from row-major X,
+    // each element stored with its mirror; otherwise X^T is staged and the
+    // full product computed
+    if (K % 8 == 0) return launch_gram_store(X, M, K, H, st);
+    const int64_t M8 = (M + 7) / 8 * 8;
     uint16_t *Xt = static_cast<uint16_t *>(ws);
     double *part = reinterpret_cast<double *>(static_cast<char *>(ws) + al256(K * M8 * 2));
     const dim3 tg((unsigned)((K + 63) / 64), (unsigned)((M8 + 63) / 64));

@@ -98,6 +98,7 @@ hipError_t launch_output_error_gram(int count, const int *fmt, const int *B, con
 // Y = A B^T (bf16 A [M][K], B [N][K], float32 Y [M][N]) on the MFMA product of
 // outref.hip; part: output_gemm_parts_bytes(M, N) bytes of scratch.
 int64_t output_gemm_parts_bytes(int64_t M, int64_t N);
+hipError_t launch_gram_store(const void *X, int64_t M, int64_t K, float *H, hipStream_t st);
 hipError_t launch_gemm_store(const uint16_t *A, const uint16_t *Bm, int64_t M, int64_t N, int64_t K, float *Y,
                              double *part, hipStream_t st);
 

@@ -94,7 +94,10 @@ struct GeCfg {
     static_assert(LDS <= 160 * 1024, "LDS");
 };
 
-enum { GE_STORE_Y = 0, GE_SUB_Y = 1, GE_GRAM = 2, GE_QUAD = 3 };
+enum { GE_STORE_Y = 0, GE_SUB_Y = 1, GE_GRAM = 2, GE_QUAD = 3, GE_SYRK = 4 };
+// GRAM and SYRK read X^T from row-major X through the LDS transpose reads
+template <int MODE>
+static constexpr bool ge_tr = MODE == GE_GRAM || MODE == GE_SYRK;
 
 template <bool F16>
 struct Mfma16;
@@ -172,12 +175,13 @@ struct GeArgs {
 //       STORE_Y: Y[m][n] = acc, partial {0, sum acc^2};
 //       SUB_Y:   d = acc f_m - Y[m][n] with f_m = fscale 2^erow[m] (f_m = 1
 //                when erow is NULL), partial {sum d^2, 0}.
-//   GRAM (A = B = X^T read from row-major X [K][M], K the reduction length
-//     and pitch M, so acc = X^T X): the tiles (tm, tn) with tn <= tm of
+//   GRAM, SYRK (A = B = X^T read from row-major X [K][M], K the reduction
+//     length and pitch M, so acc = X^T X): the tiles (tm, tn) with tn <= tm of
 //     the lower triangle, in groups of GE_GROUP_M tile rows (column-major
-//     inside a group).  Epilogue: C[n][m] = fp16(f acc[m][n] r[m] r[n]) (the
-//     transposed position, so C holds the upper block triangle), f = 2 off
-//     the diagonal tiles, 1 on them, and C[m][m] = 0.
+//     inside a group).  Epilogue: GRAM: C[n][m] = fp16(f acc[m][n] r[m]
+//     r[n]) (the transposed position, so C holds the upper block triangle),
+//     f = 2 off the diagonal tiles, 1 on them, and C[m][m] = 0; SYRK:
+//     Y[m][n] = Y[n][m] = acc[m][n] (float32) from the elements with m >= n.
 //   QUAD (A = the C of GRAM, M = K; B = E [N][K], the rows of one or more
 //     quantisations): persistent workgroups in qg gangs of qper slots; slot
 //     sl of a gang is band offset qb = sl / qe and E tile offset qu = sl % qe
@@ -221,7 +225,7 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_err_kernel(const GeArgs ga)
     float fold = 1.0f;
     int64_t qc0 = 0, qc1 = 0;  // QUAD: this workgroup's panel columns
     int qb = 0, qu = 0, qx = 0;  // QUAD: band offset, E tile offset, gang
-    if (MODE == GE_GRAM) {
+    if (MODE == GE_GRAM || MODE == GE_SYRK) {
         int g0 = 0, base = 0, gm = 0;
         for (;;) {
             gm = min(GE_GROUP_M, ga.mt - g0);
@@ -302,8 +306,8 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_err_kernel(const GeArgs ga)
     int64_t tr_a = 0, tr_b = 0;
     bool tr_oka = false, tr_okb = false;
     const uintptr_t tr_zero = (uintptr_t)ge_zero16;
-    if (MODE == GE_GRAM) {
-        static_assert(MODE != GE_GRAM || (C::TN == GE_TN && C::DA * 2 * C::NW == TK && C::DB * 2 * C::NW == TK &&
+    if (ge_tr<MODE>) {
+        static_assert(!ge_tr<MODE> || (C::TN == GE_TN && C::DA * 2 * C::NW == TK && C::DB * 2 * C::NW == TK &&
                                           (2 * C::NW) % 4 == 0),
                       "GRAM staging: full 256 x 256 tiles, 2 rows per instruction");
         const int ts = lane & 31;
@@ -366,7 +370,7 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_err_kernel(const GeArgs ga)
     } while (0)
 #define GE_STAGE_IN(k0, buf)                                                                           \
     do {                                                                                               \
-        if constexpr (MODE == GE_GRAM)                                                                 \
+        if constexpr (ge_tr<MODE>)                                                                     \
             GE_ISSUE_T(k0, buf);                                                                       \
         else                                                                                           \
             GE_ISSUE(k0, buf);                                                                         \
@@ -405,7 +409,7 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_err_kernel(const GeArgs ga)
     })
 #define GE_FRAG(set, bufp, kk)                                                                         \
     do {                                                                                               \
-        if constexpr (MODE == GE_GRAM) {                                                               \
+        if constexpr (ge_tr<MODE>) {                                                                   \
             const int row_ = 16 * (kk) + trow;                                                         \
             _Pragma("unroll") for (int i = 0; i < 4; ++i)                                              \
                 fa[set][i] = GE_TRV(bufp, row_, (wm * 128 + i * 32) / 16 + (tg & 1));                   \
@@ -648,6 +652,37 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_err_kernel(const GeArgs ga)
                         hv[u] = __builtin_bit_cast(uint16_t, (_Float16)c);
                     }
                     *reinterpret_cast<uint2 *>(ga.C + n * M + m) = make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
+                }
+        }
+        return;
+    }
+    if (MODE == GE_SYRK) {
+        // acc[i][j][4 g + u] = H[m + u][n] (m, n as for GRAM): the element and
+        // its mirror H[n][m + u] are written from the lower triangle only
+        // (m + u >= n; on the diagonal tiles the upper elements come from their
+        // mirrors), so H is exactly symmetric.  Y: float [N][N].
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int64_t n = nb0 + j * 32;
+            if (n >= N) continue;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int64_t m = mb0 + i * 32 + 8 * g;
+                    if (m >= M || m + 3 < n) continue;
+                    const float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                                        acc[i][j][4 * g + 3]};
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        if (m + u >= n) ga.Y[(m + u) * N + n] = v[u];
+                    if (m > n) {
+                        *reinterpret_cast<float4 *>(ga.Y + n * N + m) = make_float4(v[0], v[1], v[2], v[3]);
+                    } else {
+#pragma unroll
+                        for (int u = 0; u < 4; ++u)
+                            if (m + u > n) ga.Y[n * N + m + u] = v[u];
+                    }
                 }
         }
         return;
@@ -1422,6 +1457,19 @@ hipError_t launch_output_gram(const void *X, int64_t M, int64_t K, const float *
     ga.r = r;
     ga.C = C;
     return ge_launch<false, GE_GRAM, 8 / HD_GE_WN>(ga, items, st);
+}
+
+// H = X^T X in float32 [K][K] for bf16 X [M][K] (K % 8 == 0, M > 0): the
+// lower tile triangle of the transposed-read product, each element written
+// with its mirror.
+hipError_t launch_gram_store(const void *X, int64_t M, int64_t K, float *H, hipStream_t st)
+{
+    const uint16_t *Xb = static_cast<const uint16_t *>(X);
+    GeArgs ga = ge_args(Xb, Xb, K, K, M);
+    const int64_t items = (int64_t)ga.mt * (ga.mt + 1) / 2;
+    ga.nlin = (int)items;
+    ga.Y = H;
+    return ge_launch<false, GE_SYRK, 8 / HD_GE_WN>(ga, items, st);
 }
 
 template <int EK, int SK, bool REF>

@@ -444,8 +444,10 @@ hd_status dequantize_tensor_scaled(hd_format fmt, int32_t B, const uint8_t *code
  * quantised in sequence with each residual propagated through H^-1).
  *
  * gptq_hessian: H = X^T X, float32 [K, K] row-major, for bfloat16 X [M, K]
- * (products exact, float32 accumulation on the MFMA units).  Workspace:
- * gptq_hessian_workspace_size(M, K) bytes (X^T is staged there).  Errors:
+ * (products exact, float32 accumulation on the MFMA units; for K % 8 == 0 the
+ * lower triangle is computed and mirrored, so H is exactly symmetric).
+ * Workspace: gptq_hessian_workspace_size(M, K) bytes (256 when K % 8 == 0, X
+ * being read in place; otherwise X^T is staged there).  Errors:
  * HD_ERR_UNSUPPORTED for float32 X; HD_ERR_INVALID_ARG for K > 65535, NULL or
  * misaligned pointers, a short workspace.
  *

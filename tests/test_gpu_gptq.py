@@ -47,7 +47,7 @@ def scales_np(s):
     return npy(s.view(torch.int16)).view(np.uint16) if s.dtype == torch.float16 else npy(s)
 
 
-@pytest.mark.parametrize("M,K", [(1000, 200), (4096, 512), (77, 64), (1, 8), (513, 130)])
+@pytest.mark.parametrize("M,K", [(1000, 200), (4096, 512), (77, 64), (1, 8), (513, 130), (700, 776)])
 def test_hessian(M, K):
     X = synth.activations(M, K, 3 + M, n_out=3, out_gain=50.0, idx_seed=4, dtype=torch.bfloat16)
     H = npy(hd.gptq_hessian(dev(X)))
@@ -56,6 +56,8 @@ def test_hessian(M, K):
     Xa = np.abs(X.float().numpy())
     bound = oracle.xtx(Xa)
     assert np.all(np.abs(H - Ho) <= 2e-6 * bound + 1e-30)
+    if K % 8 == 0:  # the lower triangle, mirrored
+        assert np.array_equal(H, H.T)
 
 
 def gptq_inputs(N, K, M, seed):
