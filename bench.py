@@ -56,10 +56,19 @@ _NOT_IN_STEP = {"alt_f16.hip", "probe.hip", "gptq.hip", "tscale.hip", "search_e2
                 "abi.cpp", "kernels.hpp"}
 
 
+def _code_only(text):
+    """C / C++ source without its comments and with runs of white space
+    collapsed (string literals kept as they are): what the compiler sees."""
+    import re
+    tok = re.compile(r'"(?:\\.|[^"\\\n])*"|//[^\n]*|/\*.*?\*/', re.S)
+    out = tok.sub(lambda m: m.group(0) if m.group(0).startswith('"') else " ", text)
+    return " ".join(out.split())
+
+
 def source_hash():
     """Hash of the HIP sources the step's kernels are built from (every file of
-    csrc/ but those listed above); counter-derived traffic is valid only for
-    the kernels it was measured on."""
+    csrc/ but those listed above), comments and layout left out; counter-derived
+    traffic is valid only for the kernels it was measured on."""
     import glob
     import hashlib
     h = hashlib.sha256()
@@ -67,8 +76,8 @@ def source_hash():
         if os.path.basename(f) in _NOT_IN_STEP:
             continue
         h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -1,6 +1,7 @@
 // outref.hip - output error of many quantisations of one W against one X
 // (qwantize "Results", metric definitions: ||X Wq^T - X W^T||_F / ||X W^T||_F),
-// one bf16/fp16 MFMA product per quantisation.
+// one bf16/fp16 MFMA product per quantisation, directly (X Wq^T - Y) or
+// through G = X^T X (output_gram and the C E^T walk below).
 //
 // output_reference() runs once per (X, W):
 //   - Y = X W^T on the bf16 MFMA units, stored as float32 [M][N], and ||Y||^2;
@@ -31,8 +32,9 @@
 //     XOR-swizzled so the 16-byte fragment reads of 16 consecutive rows hit all
 //     64 banks (no conflicts, checked with SQ_LDS_BANK_CONFLICT); the fragments
 //     of the next 16-wide K slice are read while the current one multiplies;
-//   - the X^T X product of output_gram() stages rows of X itself (the
-//     reduction index) and reads the MFMA fragments with the LDS transpose
+//   - the X^T X products (output_gram()'s scaled float16 triangle, and the
+//     GPTQ Hessian's mirrored float32 matrix) stage rows of X itself (the
+//     reduction index) and read the MFMA fragments with the LDS transpose
 //     read ds_read_b64_tr_b16 (two per fragment), so X needs no transposed
 //     copy;
 //   - tile order: the workgroups one XCD runs at once cover 8 X tiles for each
