@@ -16,13 +16,12 @@ namespace hd {
 // float32 loads, the lanes of a wave on consecutive addresses: loads strided
 // across lanes were measured to cut the read rate), so a block of B weights
 // is B / 8 adjacent lanes of one sub-chunk (512 % B == 0), combined with
-// shuffles; for B = 4 a lane's eight weights are two whole blocks.  Codes go
-// out as 4 (4-bit) or 8 bytes per lane and sub-chunk, again on consecutive
-// addresses; the first lane of a block writes its scale.
-#ifndef HD_ENC_SUB
-#define HD_ENC_SUB 4
-#endif
-static constexpr int ENC_SUB = HD_ENC_SUB;
+// shuffles; for B = 4 a lane's eight weights are two whole blocks.  A
+// workgroup inside W gathers its codes and scale codes in LDS and writes them
+// with 16-byte and 4-byte stores per lane; the last, ragged workgroup (and
+// B = 4) writes 4 (4-bit) or 8 bytes per lane and sub-chunk, on consecutive
+// addresses, and one scale per block from the block's first lane.
+static constexpr int ENC_SUB = 4;
 
 // Scale code of one block with largest magnitude amax: given, or the Naive
 // snap (the OCP floor rule on E8M0 grids when ocp is set).
@@ -34,9 +33,6 @@ __device__ __forceinline__ int enc_scale_code(float amax, const uint8_t *scales_
     return naive_code<EK, SK>(amax);
 }
 
-// fl32(1 / s) for the integer element grids (0 for s == 0): from the table
-// on the INT8 grid, by division on the others (INT4 elements); E2M1 / E4M3
-// elements do not use it (their quotients take scale_parts).
 // Scale value of a valid code: from the table on the INT8 grid (its values
 // are fl32(val / 127), a division each), by bit formula on the others.
 template <int SK>
@@ -46,6 +42,9 @@ __device__ __forceinline__ float enc_scale_value(int code, const float *stab)
     return scale_value(SK, code);
 }
 
+// fl32(1 / s) for the integer element grids (0 for s == 0): from the table
+// on the INT8 grid, by division on the others (INT4 elements); E2M1 / E4M3
+// elements do not use it (their quotients take scale_parts).
 template <int EK, int SK>
 __device__ __forceinline__ float enc_recip(float s, int code, const float *rtab)
 {
