@@ -1094,14 +1094,17 @@ __global__ __launch_bounds__(256) void gram_zero_kernel(uint16_t *__restrict__ p
 }
 
 // The float32 values dequantize() gives (fl32(s val(q)); invalid codes give
-// 0) for the 8 weights at flat index e0 (a multiple of 8) of the codes.
+// 0) for the 8 weights at flat index e0 (a multiple of 8) of the codes.  B
+// is a power of two (block index by shift); stab: the INT8 grid's scale
+// values per code (0 for invalid codes), unused on the other grids.
 template <int EK, int SK>
 __device__ __forceinline__ void gram_wq(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales, int B,
-                                        int64_t e0, float q[8])
+                                        int64_t e0, float q[8], const float *stab)
 {
-    const int64_t bi = e0 / B;
+    const int64_t bi = e0 >> (31 - __builtin_clz((unsigned)B));
     const int sc = scale_bytes(SK) == 2 ? (int)reinterpret_cast<const uint16_t *>(scales)[bi] : (int)scales[bi];
-    const float s = scale_code_valid(SK, sc) ? scale_value(SK, sc) : 0.0f;
+    const float s = SK == SCALE_INT8 ? stab[sc & 127] * (sc < 128 ? 1.0f : 0.0f)
+                                     : (scale_code_valid(SK, sc) ? scale_value(SK, sc) : 0.0f);
     uint32_t c[8];
     if (elem_4bit(EK)) {
         const uint32_t v = *reinterpret_cast<const uint32_t *>(codes + e0 / 2);
@@ -1164,7 +1167,7 @@ __device__ __forceinline__ void gram_w(const WT *__restrict__ W, int64_t e0, flo
 template <int EK, int SK, typename WT, bool REF>
 __device__ __forceinline__ void gram_diff(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales,
                                           int B, const WT *__restrict__ W, int64_t n, int64_t K, int64_t k,
-                                          float d[8])
+                                          float d[8], const float *stab)
 {
     const int64_t e0 = n * K + k;
     float w[8];
@@ -1175,7 +1178,7 @@ __device__ __forceinline__ void gram_diff(const uint8_t *__restrict__ codes, con
         return;
     }
     float q[8];
-    gram_wq<EK, SK>(codes, scales, B, e0, q);
+    gram_wq<EK, SK>(codes, scales, B, e0, q, stab);
 #pragma unroll
     for (int j = 0; j < 8; ++j) d[j] = q[j] - w[j];
 }
@@ -1195,6 +1198,7 @@ __device__ __forceinline__ void gram_operand_row(const uint8_t *__restrict__ cod
 {
     __shared__ double sh[4];
     __shared__ int shm[4];
+    __shared__ float stab[128];  // the INT8 grid's scale values fl32(val / 127)
     if (n >= nvalid) {  // padding row of E: zeros
         for (int64_t c = threadIdx.x; c < K / 8; c += 256)
             *reinterpret_cast<uint4 *>(E + n * K + c * 8) = make_uint4(0u, 0u, 0u, 0u);
@@ -1204,13 +1208,18 @@ __device__ __forceinline__ void gram_operand_row(const uint8_t *__restrict__ cod
         }
         return;
     }
+    if (SK == SCALE_INT8 && !REF) {
+        if (threadIdx.x < 128)
+            stab[threadIdx.x] = scale_code_valid(SK, threadIdx.x) ? scale_value(SK, threadIdx.x) : 0.0f;
+        __syncthreads();
+    }
     const int64_t nch = K / 8;
     int mx = 0;  // largest |e| as float bits (monotone for non-negative floats)
     double ds = 0.0;
     float ek[RC > 0 ? RC : 1][8];
     auto chunk = [&](int64_t c, float *e) {
         float d[8];
-        gram_diff<EK, SK, WT, REF>(codes, scales, B, W, n, K, c * 8, d);
+        gram_diff<EK, SK, WT, REF>(codes, scales, B, W, n, K, c * 8, d, stab);
         const float4 q0 = *reinterpret_cast<const float4 *>(sq + c * 8);
         const float4 q1 = *reinterpret_cast<const float4 *>(sq + c * 8 + 4);
         const float4 h0 = *reinterpret_cast<const float4 *>(h + c * 8);
