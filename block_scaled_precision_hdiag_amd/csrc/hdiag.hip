@@ -12,7 +12,7 @@
 // covers squares of the smallest subnormal and the largest finite fp32), so
 // the only rounding is float64 addition.  The four waves' sums are added through LDS
 // in a fixed order and stored as a float64 partial [R][K] in the workspace.
-// Pass 2: h[j] = fl32(sum over the R partials, in chunk order).
+// Pass 2: h[j] = fl32(sum over the R partials, in a fixed order).
 // A one-column-per-lane variant covers K % 8 != 0.
 #include <mutex>
 
@@ -128,19 +128,26 @@ __global__ __launch_bounds__(256) void hdiag_col(const T *__restrict__ X, int64_
 }
 
 // h[col] = sum of the R row-chunk partials of col, in float64: 64 columns per
-// workgroup, the four waves summing the chunks r = wave, wave + 4, ... (so
-// more loads are in flight than with one thread per column), combined in a
-// fixed order.
+// workgroup; wave g sums the chunks r = g + 4 i as four running sums over
+// i mod 4 (four loads in flight per lane and round; chunks past R are clamped
+// for the load and contribute 0), and the 16 sums are combined in a fixed
+// order.
 __global__ __launch_bounds__(256) void hdiag_final(const double *__restrict__ part, int64_t R, int64_t K,
                                                    float *__restrict__ h)
 {
     __shared__ double sh[4][64];
     const int c = threadIdx.x & 63, g = threadIdx.x >> 6;
     const int64_t col = (int64_t)blockIdx.x * 64 + c;
-    double s = 0.0;
+    double sv[4] = {0.0, 0.0, 0.0, 0.0};
     if (col < K)
-        for (int64_t r = g; r < R; r += 4) s += part[r * K + col];
-    sh[g][c] = s;
+        for (int64_t r0 = g; r0 < R; r0 += 16) {
+            double x[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) x[u] = part[min<int64_t>(r0 + 4 * u, R - 1) * K + col];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) sv[u] += r0 + 4 * u < R ? x[u] : 0.0;
+        }
+    sh[g][c] = (sv[0] + sv[1]) + (sv[2] + sv[3]);
     __syncthreads();
     if (g == 0 && col < K) h[col] = (float)((sh[0][c] + sh[1][c]) + (sh[2][c] + sh[3][c]));
 }

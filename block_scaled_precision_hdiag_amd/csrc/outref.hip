@@ -1093,39 +1093,79 @@ __global__ __launch_bounds__(256) void gram_zero_kernel(uint16_t *__restrict__ p
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0;
 }
 
-// The float32 values dequantize() gives (fl32(s val(q)); invalid codes give
-// 0) for the 8 weights at flat index e0 (a multiple of 8) of the codes.  B
-// is a power of two (block index by shift); stab: the INT8 grid's scale
-// values per code (0 for invalid codes), unused on the other grids.
-template <int EK, int SK>
-__device__ __forceinline__ void gram_wq(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales, int B,
-                                        int64_t e0, float q[8], const float *stab)
+// The raw memory of one 8-weight chunk at flat index e0 (a multiple of 8):
+// the weights (16 bytes of bf16 in w0, or 32 bytes of float32 in w0, w1),
+// the codes (8-bit: c.x, c.y; 4-bit: c.x) and the block's scale code (B is a
+// power of two: block index by shift).  REF: the weights only.  Loading every
+// chunk of a row before decoding any lets the row's loads overlap.
+struct GramRaw {
+    uint4 w0, w1;
+    uint2 c;
+    int sc;
+};
+template <int EK, int SK, typename WT, bool REF>
+__device__ __forceinline__ void gram_load(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales, int B,
+                                          const WT *__restrict__ W, int64_t e0, GramRaw &r)
 {
+    r.w0 = *reinterpret_cast<const uint4 *>(W + e0);
+    if (sizeof(WT) == 4) r.w1 = *reinterpret_cast<const uint4 *>(W + e0 + 4);
+    if (REF) return;
     const int64_t bi = e0 >> (31 - __builtin_clz((unsigned)B));
-    const int sc = scale_bytes(SK) == 2 ? (int)reinterpret_cast<const uint16_t *>(scales)[bi] : (int)scales[bi];
+    r.sc = scale_bytes(SK) == 2 ? (int)reinterpret_cast<const uint16_t *>(scales)[bi] : (int)scales[bi];
+    if (elem_4bit(EK))
+        r.c.x = *reinterpret_cast<const uint32_t *>(codes + e0 / 2);
+    else
+        r.c = *reinterpret_cast<const uint2 *>(codes + e0);
+}
+
+// d = Wq - W for a loaded chunk (REF: d = W), with Wq the float32 values
+// dequantize() gives (fl32(s val(q)); invalid codes give 0).  stab: the INT8
+// grid's scale values per code (0 for invalid codes), unused on the other
+// grids.
+template <int EK, int SK, typename WT, bool REF>
+__device__ __forceinline__ void gram_decode(const GramRaw &r, float d[8], const float *stab)
+{
+    float w[8];
+    if (sizeof(WT) == 2) {
+        const uint32_t u[4] = {r.w0.x, r.w0.y, r.w0.z, r.w0.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            w[2 * j] = bf16_to_f32(u[j] & 0xFFFFu);
+            w[2 * j + 1] = bf16_to_f32(u[j] >> 16);
+        }
+    } else {
+        const uint32_t u[8] = {r.w0.x, r.w0.y, r.w0.z, r.w0.w, r.w1.x, r.w1.y, r.w1.z, r.w1.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) w[j] = __builtin_bit_cast(float, u[j]);
+    }
+    if (REF) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) d[j] = w[j];
+        return;
+    }
+    const int sc = r.sc;
     const float s = SK == SCALE_INT8 ? stab[sc & 127] * (sc < 128 ? 1.0f : 0.0f)
                                      : (scale_code_valid(SK, sc) ? scale_value(SK, sc) : 0.0f);
     uint32_t c[8];
     if (elem_4bit(EK)) {
-        const uint32_t v = *reinterpret_cast<const uint32_t *>(codes + e0 / 2);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) c[j] = (v >> (4 * j)) & 15u;
+        for (int j = 0; j < 8; ++j) c[j] = (r.c.x >> (4 * j)) & 15u;
     } else {
-        const uint2 v = *reinterpret_cast<const uint2 *>(codes + e0);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            c[j] = (v.x >> (8 * j)) & 255u;
-            c[4 + j] = (v.y >> (8 * j)) & 255u;
+            c[j] = (r.c.x >> (8 * j)) & 255u;
+            c[4 + j] = (r.c.y >> (8 * j)) & 255u;
         }
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
+        float q;
         if (EK == ELEM_INT8) {
             const int i = (int)(int8_t)(uint8_t)c[j];
-            q[j] = i == -128 ? 0.0f : s * (float)i;
+            q = i == -128 ? 0.0f : s * (float)i;
         } else if (EK == ELEM_INT4) {
             const int i = (int)((c[j] ^ 8u) & 15u) - 8;
-            q[j] = i == -8 ? 0.0f : s * (float)i;
+            q = i == -8 ? 0.0f : s * (float)i;
         } else {
             bool neg, ok = true;
             uint32_t idx;
@@ -1138,49 +1178,10 @@ __device__ __forceinline__ void gram_wq(const uint8_t *__restrict__ codes, const
                 ok = idx != 0x7Fu;
             }
             const float mag = ok ? s * elem_value<EK>(idx) : 0.0f;
-            q[j] = neg ? -mag : mag;
+            q = neg ? -mag : mag;
         }
+        d[j] = q - w[j];
     }
-}
-
-// The 8 weights at flat index e0 of W as float32.
-template <typename WT>
-__device__ __forceinline__ void gram_w(const WT *__restrict__ W, int64_t e0, float w[8])
-{
-    if (sizeof(WT) == 2) {
-        const uint4 v = *reinterpret_cast<const uint4 *>(W + e0);
-        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            w[2 * j] = bf16_to_f32(u[j] & 0xFFFFu);
-            w[2 * j + 1] = bf16_to_f32(u[j] >> 16);
-        }
-    } else {
-        const float4 a = *reinterpret_cast<const float4 *>(W + e0);
-        const float4 b = *reinterpret_cast<const float4 *>(W + e0 + 4);
-        w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
-        w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
-    }
-}
-
-// d = Wq - W for the 8 weights k .. k + 7 of row n (REF: d = W).
-template <int EK, int SK, typename WT, bool REF>
-__device__ __forceinline__ void gram_diff(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales,
-                                          int B, const WT *__restrict__ W, int64_t n, int64_t K, int64_t k,
-                                          float d[8], const float *stab)
-{
-    const int64_t e0 = n * K + k;
-    float w[8];
-    gram_w<WT>(W, e0, w);
-    if (REF) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) d[j] = w[j];
-        return;
-    }
-    float q[8];
-    gram_wq<EK, SK>(codes, scales, B, e0, q, stab);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) d[j] = q[j] - w[j];
 }
 
 // One workgroup per row n: e = d sqrt(h) as float16 under the row exponent
@@ -1217,15 +1218,25 @@ __device__ __forceinline__ void gram_operand_row(const uint8_t *__restrict__ cod
     int mx = 0;  // largest |e| as float bits (monotone for non-negative floats)
     double ds = 0.0;
     float ek[RC > 0 ? RC : 1][8];
-    auto chunk = [&](int64_t c, float *e) {
+    // sqrt(h) and h of chunk c
+    struct SqH {
+        float4 q0, q1, h0, h1;
+    };
+    auto load_sqh = [&](int64_t c) {
+        SqH v;
+        v.q0 = *reinterpret_cast<const float4 *>(sq + c * 8);
+        v.q1 = *reinterpret_cast<const float4 *>(sq + c * 8 + 4);
+        v.h0 = *reinterpret_cast<const float4 *>(h + c * 8);
+        v.h1 = *reinterpret_cast<const float4 *>(h + c * 8 + 4);
+        return v;
+    };
+    // e = d sqrt(h) of a chunk from its loaded memory, into the row maximum
+    // and the diagonal sum
+    auto chunk = [&](const GramRaw &r, const SqH &v, float *e) {
         float d[8];
-        gram_diff<EK, SK, WT, REF>(codes, scales, B, W, n, K, c * 8, d, stab);
-        const float4 q0 = *reinterpret_cast<const float4 *>(sq + c * 8);
-        const float4 q1 = *reinterpret_cast<const float4 *>(sq + c * 8 + 4);
-        const float4 h0 = *reinterpret_cast<const float4 *>(h + c * 8);
-        const float4 h1 = *reinterpret_cast<const float4 *>(h + c * 8 + 4);
-        const float qv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-        const float hv[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+        gram_decode<EK, SK, WT, REF>(r, d, stab);
+        const float qv[8] = {v.q0.x, v.q0.y, v.q0.z, v.q0.w, v.q1.x, v.q1.y, v.q1.z, v.q1.w};
+        const float hv[8] = {v.h0.x, v.h0.y, v.h0.z, v.h0.w, v.h1.x, v.h1.y, v.h1.z, v.h1.w};
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             e[j] = d[j] * qv[j];
@@ -1234,13 +1245,29 @@ __device__ __forceinline__ void gram_operand_row(const uint8_t *__restrict__ cod
         }
     };
     if (RC > 0) {
+        // every chunk's weights, codes and scale first, then the chunks in
+        // order, each one's sqrt(h) and h loaded while the one before is
+        // decoded (chunk indices past the row are clamped to its last chunk
+        // for the loads; their values go unused)
+        GramRaw raw[RC > 0 ? RC : 1];
+#pragma unroll
+        for (int it = 0; it < RC; ++it)
+            if (256 * it < nch)
+                gram_load<EK, SK, WT, REF>(codes, scales, B, W, n * K + min<int64_t>(threadIdx.x + 256 * it, nch - 1) * 8,
+                                           raw[it]);
+        SqH nxt = load_sqh(min<int64_t>(threadIdx.x, nch - 1));
 #pragma unroll
         for (int it = 0; it < RC; ++it) {
-            const int64_t c = threadIdx.x + 256 * it;
-            if (c < nch) chunk(c, ek[it]);
+            const SqH cur = nxt;
+            if (it + 1 < RC && 256 * (it + 1) < nch) nxt = load_sqh(min<int64_t>(threadIdx.x + 256 * (it + 1), nch - 1));
+            if (threadIdx.x + 256 * it < nch) chunk(raw[it], cur, ek[it]);
         }
     } else {
-        for (int64_t c = threadIdx.x; c < nch; c += 256) chunk(c, ek[0]);
+        for (int64_t c = threadIdx.x; c < nch; c += 256) {
+            GramRaw r;
+            gram_load<EK, SK, WT, REF>(codes, scales, B, W, n * K + c * 8, r);
+            chunk(r, load_sqh(c), ek[0]);
+        }
     }
     mx = wave_max_int(mx);
     if ((threadIdx.x & 63) == 0) shm[threadIdx.x >> 6] = mx;
@@ -1278,7 +1305,9 @@ __device__ __forceinline__ void gram_operand_row(const uint8_t *__restrict__ cod
             float e[8];
             const int mx0 = mx;
             const double ds0 = ds;
-            chunk(c, e);  // recomputes e (mx and ds are not used again)
+            GramRaw r;
+            gram_load<EK, SK, WT, REF>(codes, scales, B, W, n * K + c * 8, r);
+            chunk(r, load_sqh(c), e);  // recomputes e (mx and ds are not used again)
             mx = mx0;
             ds = ds0;
             store(c, e);
@@ -1297,9 +1326,11 @@ __global__ __launch_bounds__(256) void gram_operand_kernel(const uint8_t *__rest
     gram_operand_row<EK, SK, WT, REF, RC>(codes, scales, B, W, K, sq, h, E, erow, dsum, nvalid, blockIdx.x);
 }
 
-// Up to GRAM_OPS quantisations of one format in one launch: workgroup
-// (n, q) = (blockIdx / n_q, blockIdx % n_q) does row n of quantisation q, so
-// the workgroups of one row of W run next to each other and share it in L2;
+// Up to GRAM_OPS quantisations of one format in one launch: workgroup b does
+// row n of quantisation q with, for b = 8 (n_q i + q) + x (x < 8),
+// n = 8 i + x: consecutive workgroups go to the 8 XCDs in turn, so the n_q
+// workgroups of one row of W run on one XCD, 8 dispatches apart, and share
+// the row in its L2.  rpq (a multiple of 256) rows per quantisation;
 // quantisation q's E, erow and dsum start at row q rpq.
 constexpr int GRAM_OPS = 16;
 struct GramOps {
@@ -1315,10 +1346,28 @@ __global__ __launch_bounds__(256) void gram_operand_multi_kernel(const GramOps o
                                                                  int *__restrict__ erow, double *__restrict__ dsum,
                                                                  int64_t nvalid, int64_t rpq)
 {
-    const int q = (int)(blockIdx.x % (unsigned)ob.n);
-    const int64_t n = blockIdx.x / (unsigned)ob.n, o = q * rpq;
+    const unsigned rest = blockIdx.x / 8u;
+    const int q = (int)(rest % (unsigned)ob.n);
+    const int64_t n = (int64_t)(rest / (unsigned)ob.n) * 8 + (blockIdx.x & 7u), o = q * rpq;
     gram_operand_row<EK, SK, WT, false, 8>(ob.codes[q], ob.scales[q], ob.B[q], W, K, sq, h, E + o * K, erow + o,
                                            dsum + o, nvalid, n);
+}
+
+// This thread's share of v[0 .. n - 1] in a 256-thread workgroup (elements
+// threadIdx.x + 256 i) as 8 running sums over i mod 8, added in a fixed order
+// at the end: the 8 loads of a round are in flight together (indices past n
+// are clamped for the load and contribute 0).
+__device__ __forceinline__ double strided_sum8(const double *__restrict__ v, int64_t n)
+{
+    double a[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+    for (int64_t i0 = threadIdx.x; i0 < n; i0 += 2048) {
+        double x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = v[min<int64_t>(i0 + 256 * u, n - 1)];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) a[u] += i0 + 256 * u < n ? x[u] : 0.0;
+    }
+    return ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
 }
 
 // One workgroup per quantisation q: total = the slots part[(t mt + band) qg
@@ -1337,9 +1386,7 @@ __global__ __launch_bounds__(256) void gram_final(const double *__restrict__ par
     const int q = blockIdx.x;
     const int64_t ns = (int64_t)tpq * mt * qg;
     const double *ps = part + (int64_t)q * ns;
-    double a = 0.0, b = 0.0;
-    for (int64_t i = threadIdx.x; i < ns; i += 256) a += ps[i];
-    for (int64_t i = threadIdx.x; i < nvalid; i += 256) b += dsum[q * rpq + i];
+    double a = strided_sum8(ps, ns), b = strided_sum8(dsum + q * rpq, nvalid);
     a = block_sum_256(a, sh);
     b = block_sum_256(b, sh);
     if (threadIdx.x == 0) {
@@ -1528,10 +1575,17 @@ static void gram_operand_multi_fmt(const GramOps &ob, const void *W, int wdt, in
             ob, static_cast<const float *>(W), K, sq, h, E, erow, dsum, N, rows);
 }
 
+// Partial slots of one walk over `count` quantisations of N x K weights.
+static int64_t gram_walk_slots(int count, int64_t N, int64_t K)
+{
+    const int64_t nt = count * gram_rows(N) / GE_TN, mt = (K + GE_TM - 1) / GE_TM;
+    return N > 0 && K > 0 ? nt * mt * gram_plan(nt, K).qg : 0;
+}
+
 // One walk over `count` quantisations (fmt[q], B[q], codes[q], scales[q]) of
 // one W: out[q] = sqrt(||X (Wq_q - W)^T||^2) / sqrt(*ysq); fmt == NULL: the
 // reference ||X W^T||^2 into ysq_out[0] (count 1).  E, erow and dsum are the
-// walk's rows, part its slots.
+// walk's rows, part its gram_walk_slots() slots, zeroed beforehand.
 static hipError_t gram_walk(int count, const int *fmt, const int *B, const uint8_t *const *codes,
                             const uint8_t *const *scales, const void *W, int wdt, int64_t N, int64_t K,
                             const void *gram, const double *ysq, double *ysq_out, double *out, double *sums,
@@ -1599,8 +1653,6 @@ static hipError_t gram_walk(int count, const int *fmt, const int *B, const uint8
             default: return hipErrorInvalidValue;
             }
         }
-        const int64_t slots = nt * mt * plan.qg;
-        gram_zero_f64<<<(unsigned)std::min<int64_t>((slots + 255) / 256, 1024), 256, 0, st>>>(part, slots);
         GeArgs ga = ge_args(C, E, K, R, K);
         ga.nlin = (int)plan.wgs;
         ga.qa = plan.qa;
@@ -1643,21 +1695,26 @@ hipError_t launch_output_error_gram(int count, const int *fmt, const int *B, con
                                     const void *gram, const double *ysq, double *ysq_out, double *out, double *sums,
                                     void *ws, hipStream_t st)
 {
-    const int64_t rpq = gram_rows(N), R = count * rpq, mt = (K + GE_TM - 1) / GE_TM;
+    const int64_t rpq = gram_rows(N), R = count * rpq;
     char *w = static_cast<char *>(ws);
     uint16_t *E = reinterpret_cast<uint16_t *>(w);
     int *erow = reinterpret_cast<int *>(w + al256(R * K * 2));
     double *dsum = reinterpret_cast<double *>(w + al256(R * K * 2) + al256(R * 4));
     double *part = reinterpret_cast<double *>(w + al256(R * K * 2) + al256(R * 4) + al256(R * 8));
-    const int64_t slots_per_q = rpq / GE_TN * mt * std::max<int64_t>(device_cus(), 8);
     const int sb = fmt == nullptr ? 1 : gram_sub_batch(count, N, K);
+    // the walks' slots packed one after another, all zeroed by one launch
+    const int last = count - (count - 1) / sb * sb;  // quantisations of the last walk
+    const int64_t full_slots = gram_walk_slots(sb, N, K), slots = (int64_t)((count - 1) / sb) * full_slots +
+                                                               gram_walk_slots(last, N, K);
+    if (slots > 0)
+        gram_zero_f64<<<(unsigned)std::min<int64_t>((slots + 255) / 256, 1024), 256, 0, st>>>(part, slots);
     for (int q0 = 0; q0 < count; q0 += sb) {
         const int n = std::min(sb, count - q0);
         const hipError_t e = gram_walk(n, fmt ? fmt + q0 : nullptr, B ? B + q0 : nullptr,
                                        codes ? codes + q0 : nullptr, scales ? scales + q0 : nullptr, W, wdt, N, K,
                                        gram, ysq, ysq_out, out ? out + q0 : nullptr, sums ? sums + 3 * q0 : nullptr,
-                                       E + q0 * rpq * K, erow + q0 * rpq, dsum + q0 * rpq, part + q0 * slots_per_q,
-                                       st);
+                                       E + q0 * rpq * K, erow + q0 * rpq, dsum + q0 * rpq,
+                                       part + (int64_t)(q0 / sb) * full_slots, st);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

@@ -496,15 +496,28 @@ __global__ __launch_bounds__(256) void werr_partial(const TW *__restrict__ W, co
 }
 
 // Sum `n` (num, den) partials in a fixed order; out = sqrt(num) / sqrt(den).
+// Each thread keeps 8 running pairs over its partials i = threadIdx.x + 256 j
+// (j mod 8), so 8 loads are in flight per round; indices past n are clamped
+// for the load and contribute 0.
 __global__ __launch_bounds__(256) void ratio_final(const double *__restrict__ part, int n,
                                                    double *__restrict__ out, double *__restrict__ sums)
 {
     __shared__ double sh[4];
-    double a = 0.0, b = 0.0;
-    for (int i = threadIdx.x; i < n; i += 256) {
-        a += part[2 * i];
-        b += part[2 * i + 1];
+    const double2 *pp = reinterpret_cast<const double2 *>(part);
+    double av[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0}, bv[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+    for (int i0 = threadIdx.x; i0 < n; i0 += 2048) {
+        double2 x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = pp[min(i0 + 256 * u, n - 1)];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const bool in = i0 + 256 * u < n;
+            av[u] += in ? x[u].x : 0.0;
+            bv[u] += in ? x[u].y : 0.0;
+        }
     }
+    double a = ((av[0] + av[1]) + (av[2] + av[3])) + ((av[4] + av[5]) + (av[6] + av[7]));
+    double b = ((bv[0] + bv[1]) + (bv[2] + bv[3])) + ((bv[4] + bv[5]) + (bv[6] + bv[7]));
     a = block_sum_256(a, sh);
     b = block_sum_256(b, sh);
     if (threadIdx.x == 0) {

@@ -100,12 +100,23 @@ def test_config2_gram_route_full():
     ysq = hd.output_reference_gram(Wd, gram)
     ref = hd.output_reference(Xd, Wd)
     assert ysq.item() == pytest.approx(hd.reference_ysq(ref).item(), rel=1e-4)
+    items, singles = [], []
     for B in (32, 64, 128, 256):
         for m in (hd.NAIVE, hd.SSE_OPT, hd.H_OPT):
             c, s, _ = hd.quantize_blocks(m, hd.INT8_E4M3, B, Wd, h=h)
             g = hd.output_error_gram(hd.INT8_E4M3, B, c, s, Wd, gram, ysq).item()
             d = hd.output_error_codes(hd.INT8_E4M3, B, Xd, c, s, ref, N, K).item()
             assert g == pytest.approx(d, rel=1e-4), (B, m)
+            items.append((hd.INT8_E4M3, B, c, s))
+            singles.append(g)
+    # the step's batch (walks of two quantisations at this size) and a batch of
+    # three (walks of two and one, with different walk schedules): each result
+    # as its single call gives it, up to summation order
+    for batch in (items, items[:3]):
+        out = hd.output_error_gram_batch(batch, Wd, gram, ysq)
+        torch.cuda.synchronize()
+        for q in range(len(batch)):
+            assert out[q].item() == pytest.approx(singles[q], rel=1e-6), q
     R = 192
     Xs = Xd[:R].contiguous()
     gram_s = hd.output_gram(Xs)
