@@ -21,12 +21,19 @@ as individual launches (per-call GPU times from HIP events recorded on the
 stream the kernels run on: the per-stage figures and the roofline) and as
 replays of the same step captured once in a HIP graph (no host launch gaps;
 a replay must first reproduce the eager step's errors bit for bit), which
-gives ms_per_step and value unless --eager is given.
+gives ms_per_step and value unless --eager is given.  The replayed step runs
+on two streams (--streams 2, the default; Gram route): after hdiag, the
+G = X^T X product and the reference on a second stream, beside the
+quantise / dequantize / weight-error chain of the 12 quantisations on the
+first (the two branches share no buffer; the first stream waits for the
+second before the output-error batch); the per-stage times come from the
+one-stream launches, and a one-stream replay is timed as well.
 
 Prints one JSON line (the metric, per-stage figures, the roofline of the
 dominant kernel and the CPU oracle timed on a bounded sample).
 """
 import argparse
+import contextlib
 import json
 import os
 import sys
@@ -117,6 +124,9 @@ def parse():
                          "scale format x B in {16, 32} x scale choice on the same W and h (one JSON line)")
     ap.add_argument("--eager", action="store_true",
                     help="time the step as individual launches instead of replays of one captured HIP graph")
+    ap.add_argument("--streams", type=int, choices=[1, 2], default=2,
+                    help="streams of the replayed step (2: G = X^T X and the reference beside the quantisation "
+                         "chain; Gram route only)")
     ap.add_argument("--output-route", choices=["gram", "direct"], default="gram",
                     help="output error through G = X^T X (gram) or through X W^T (direct)")
     ap.add_argument("--summarize-profile", metavar="DIR", default=None,
@@ -245,11 +255,19 @@ def main():
         else:
             fn()
 
-    def step(rec):
+    side = torch.cuda.Stream(device=dev)  # default priority
+
+    def step(rec, streams=1):
         timed("hdiag", 0, lambda: hd.hdiag(X, out=h, workspace=ws_h), rec)
+        two = gram_route and streams == 2
+        if two:
+            # G and the reference on the second stream, after hdiag
+            side.wait_stream(torch.cuda.current_stream())
         if gram_route:
-            timed("output_gram", 0, lambda: hd.output_gram(X, h=h, gram=gram, workspace=ws_g), rec)
-            timed("output_reference", 0, lambda: hd.output_reference_gram(W, gram, workspace=ws_o, out=ysq), rec)
+            with torch.cuda.stream(side) if two else contextlib.nullcontext():
+                timed("output_gram", 0, lambda: hd.output_gram(X, h=h, gram=gram, workspace=ws_g), rec)
+                timed("output_reference", 0, lambda: hd.output_reference_gram(W, gram, workspace=ws_o, out=ysq),
+                      rec)
         else:
             timed("output_reference", 0, lambda: hd.output_reference(X, W, ref=ref), rec)
         for bi, B in enumerate(blocks):
@@ -265,6 +283,8 @@ def main():
                           lambda: hd.output_error_codes(fmt, B, X, cb, sb, ref, N, K, workspace=ws_o,
                                                         out=oerr[bi, mi:mi + 1]), rec)
         if gram_route:
+            if two:
+                torch.cuda.current_stream().wait_stream(side)
             # the 12 output errors in one call (one MFMA walk over their stacked operand)
             items = [(fmt, B, codes[(B, m)], scales[(B, m)]) for B in blocks for _, m in methods]
             timed("output_error", 0,
@@ -282,29 +302,35 @@ def main():
     t1 = time.perf_counter()
     ms_eager = (t1 - t0) * 1e3 / args.steps
     ms_per_step, launch = ms_eager, "eager"
+    ms_graph = {}
     if not args.eager:
         # the same step captured once as a HIP graph (every launch of the step,
-        # same buffers) and replayed: a replay must reproduce the eager errors
-        # bit for bit before its time is used
+        # same buffers) on one stream and, with --streams 2, on two; each is
+        # replayed, and a replay must reproduce the eager errors bit for bit
+        # before its time is used
         eager_w, eager_o = werr.clone(), oerr.clone()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            step(False)
-        werr.zero_()
-        oerr.zero_()
-        graph.replay()
-        torch.cuda.synchronize()
-        if not (torch.equal(werr, eager_w) and torch.equal(oerr, eager_o)):
-            raise SystemExit("graph replay does not reproduce the eager step")
-        for _ in range(args.warmup):
+        for ns in sorted({1, args.streams if gram_route else 1}):
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                step(False, ns)
+            werr.zero_()
+            oerr.zero_()
             graph.replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            graph.replay()
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        ms_per_step, launch = (t1 - t0) * 1e3 / args.steps, "hip_graph"
+            torch.cuda.synchronize()
+            if not (torch.equal(werr, eager_w) and torch.equal(oerr, eager_o)):
+                raise SystemExit("graph replay (%d streams) does not reproduce the eager step" % ns)
+            for _ in range(args.warmup):
+                graph.replay()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(args.steps):
+                graph.replay()
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
+            ms_graph[ns] = (t1 - t0) * 1e3 / args.steps
+            del graph
+        ns = max(ms_graph)
+        ms_per_step, launch = ms_graph[ns], "hip_graph, %d stream%s" % (ns, "s" if ns > 1 else "")
     value = len(blocks) * len(methods) * N * K / (ms_per_step * 1e-3) / 1e9
 
     # per-stage GPU times (ms per launch), from the events
@@ -397,6 +423,7 @@ def main():
         "profiles_source_hash": source_hash(),
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3),
         "launch": launch, "ms_per_step_eager": round(ms_eager, 3),
+        "ms_per_step_graph_one_stream": round(ms_graph[1], 3) if ms_graph else None,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "INT8 (E4M3 scales) on W 2560x9728 bf16, h from X 16384x9728 bf16; "
