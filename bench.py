@@ -8,10 +8,11 @@ with per-row lognormal gain for the down_proj weight) and calibration X
     hdiag(X), output_gram(X) (G = X^T X, stored as float16 correlations) and
     output_reference_gram (||X W^T||^2 from G), then for B in
     {32, 64, 128, 256} and each of Naive, SSE-Optimal, H-Optimal:
-    quantize_blocks (scale choice + encode), dequantize, weight error and
-    output error (output_error_gram_batch after the loop: sum_n d_n^T G d_n
-    for D = Wq - W of all 12 quantisations, one MFMA walk of 12 N x K x K over
-    G's upper block triangle).
+    quantize_blocks (scale choice + encode), dequantize_weight_error (the
+    dequantised weights and the weight error in one pass) and output error
+    (output_error_gram_batch after the loop: sum_n d_n^T G d_n for D = Wq - W
+    of all 12 quantisations, one MFMA walk of 12 N x K x K over G's upper
+    block triangle).
     --output-route direct measures the output error with X instead:
     output_reference (Y = X W^T) once and output_error_codes (X Wq^T - Y, one
     M x N x K MFMA product) per quantisation.
@@ -24,7 +25,7 @@ a replay must first reproduce the eager step's errors bit for bit), which
 gives ms_per_step and value unless --eager is given.  The replayed step runs
 on two streams (--streams 2, the default; Gram route): after hdiag, the
 G = X^T X product and the reference on a second stream, beside the
-quantise / dequantize / weight-error chain of the 12 quantisations on the
+quantise / dequantize-and-weight-error chain of the 12 quantisations on the
 first (the two branches share no buffer; the first stream waits for the
 second before the output-error batch); the per-stage times come from the
 one-stream launches, and a one-stream replay is timed as well.
@@ -275,9 +276,10 @@ def main():
                 stage = "naive" if m == hd.NAIVE else "search_" + mname
                 cb, sb = codes[(B, m)], scales[(B, m)]
                 timed(stage, B, lambda: hd.quantize_blocks(m, fmt, B, W, h=h, codes=cb, scales=sb), rec)
-                timed("dequantize", B, lambda: hd.dequantize(fmt, B, cb, sb, N, K, out=Wq), rec)
-                timed("weight_error", B, lambda: hd.weight_error(W, Wq, workspace=ws_w, out=werr[bi, mi:mi + 1]),
-                      rec)
+                # the dequantised weights and the weight error in one pass
+                timed("dequantize_weight_error", B,
+                      lambda: hd.dequantize_weight_error(fmt, B, cb, sb, W, out=Wq, err=werr[bi, mi:mi + 1],
+                                                         workspace=ws_w), rec)
                 if not gram_route:
                     timed("output_error", B,
                           lambda: hd.output_error_codes(fmt, B, X, cb, sb, ref, N, K, workspace=ws_o,
@@ -345,8 +347,8 @@ def main():
     work = {
         "hdiag": ("hbm", M * K * 2 + K * 4),
         "naive": ("hbm", sum(bytes_w + N * K + N * K // B for B in blocks) / len(blocks)),
-        "dequantize": ("hbm", sum(N * K + N * K // B + N * K * 4 for B in blocks) / len(blocks)),
-        "weight_error": ("hbm", bytes_w + N * K * 4),
+        # codes and scales read, W read, float32 Wq written
+        "dequantize_weight_error": ("hbm", sum(N * K + N * K // B + bytes_w + N * K * 4 for B in blocks) / len(blocks)),
         # the gram route: G's K (K + 1) / 2 distinct entries (2 M flops each),
         # and the quadratic forms d^T G d over G's symmetric halves (N K^2)
         "output_gram": ("mfma", 1.0 * M * K * (K + 1)),
@@ -430,7 +432,7 @@ def main():
                                "B in {32,64,128,256}; Naive + SSE-Optimal + H-Optimal; hdiag, "
                                + ("X^T X Gram matrix and ||X W^T||^2 from it, " if gram_route else
                                   "X W^T reference, ")
-                               + "quantize, dequantize, weight and output error per step",
+                               + "quantize, dequantize with the weight error, output error per step",
                    "output_route": args.output_route,
                    "W": [N, K], "X": [M, K], "format": "INT8_E4M3", "blocks": blocks,
                    "quantizations_per_step": len(blocks) * len(methods)},
@@ -1068,10 +1070,16 @@ def _stage_of(name, state):
         return "naive"
     if "search_kernel" in n:
         return "search_h" if n.rstrip().endswith("true>") else "search_sse"
+    if "dqwe_partial" in n:
+        state["ratio"] = "dequantize_weight_error"
+        return "dequantize_weight_error"
     if "dequant_kernel" in n:
         return "dequantize"
-    if "werr_partial" in n or "ratio_final" in n:
+    if "werr_partial" in n:
+        state["ratio"] = "weight_error"
         return "weight_error"
+    if "ratio_final" in n:
+        return state.get("ratio", "weight_error")
     if "__amd_rocclr_copyBuffer" in n:
         return "copy"
     return "other"
@@ -1122,10 +1130,10 @@ def _dispatches(rows, with_counters):
 
 
 STAGE_ORDER = ["hdiag", "output_gram", "output_reference", "naive", "search_sse", "search_h", "dequantize",
-               "weight_error", "output_error"]
+               "weight_error", "dequantize_weight_error", "output_error"]
 # calls of each stage in one step (a call may launch several kernels)
 STAGE_CALLS = {"hdiag": 1, "output_gram": 1, "output_reference": 1, "naive": 4, "search_sse": 4, "search_h": 4,
-               "dequantize": 12, "weight_error": 12, "output_error": 1}
+               "dequantize": 12, "weight_error": 12, "dequantize_weight_error": 12, "output_error": 1}
 
 
 def summarize_profile(d, probe_mb, cmds):

@@ -39,7 +39,7 @@ FOUR_BIT = (NVFP4, MXFP4, NVFP4_UE4M4, NVFP4_UE5M3, NVINT4, FP4_F16, INT4_F16)
 F16_SCALES = (FP4_F16, INT4_F16)
 
 EXPORTS = ["hdiag_set_schedule", "hdiag", "hdiag_workspace_size", "hdiag_noalloc", "quantize_blocks", "quantize_blocks_instrumented", "encode_blocks", "dequantize",
-           "weight_error", "weight_error_workspace_size", "output_error", "output_error_workspace_size",
+           "weight_error", "weight_error_workspace_size", "dequantize_weight_error", "output_error", "output_error_workspace_size",
            "output_error_given_ref", "output_reference", "output_reference_size", "output_error_codes",
            "output_error_codes_workspace_size", "output_gram", "output_gram_size", "output_gram_workspace_size",
            "output_reference_gram", "output_error_gram", "output_error_gram_workspace_size",
@@ -82,6 +82,7 @@ def lib():
         L.weight_error_workspace_size.argtypes = [i64, i64]
         L.weight_error_workspace_size.restype = sz
         L.weight_error.argtypes = [P, i32, P, i32, i64, i64, P, P, P, sz, P]
+        L.dequantize_weight_error.argtypes = [i32, i32, P, P, i64, i64, P, i32, P, i32, P, P, P, sz, P]
         L.output_error_workspace_size.argtypes = [i64, i64, i64]
         L.output_error_workspace_size.restype = sz
         L.output_error.argtypes = [P, i32, i64, P, i32, P, i32, i64, i64, P, P, P, sz, P]
@@ -128,7 +129,7 @@ def lib():
         L.gptq_factor.argtypes = [P, i64, ctypes.c_double, P, sz, P, P, sz, P]
         L.gptq_quantize_factored.argtypes = [i32, i32, i32, P, i32, i64, i64, P, P, sz, P, P, P, P, P, sz, P]
         for name in ("hdiag_set_schedule", "hdiag", "hdiag_noalloc", "quantize_blocks", "quantize_blocks_instrumented", "encode_blocks", "dequantize", "weight_error",
-                     "output_error", "output_error_given_ref", "output_reference", "output_error_codes",
+                     "dequantize_weight_error", "output_error", "output_error_given_ref", "output_reference", "output_error_codes",
                      "output_gram", "output_reference_gram", "output_error_gram", "output_error_gram_batch",
                      "hdiag_format_info", "gptq_hessian", "gptq_quantize", "gptq_factor", "gptq_quantize_factored", "quantize_blocks_tensor_scaled",
                      "dequantize_tensor_scaled"):
@@ -303,6 +304,23 @@ def weight_error(W, Wq, sums=False, workspace=None, out=None):
     _check(lib().weight_error(_ptr(W), _dt(W), _ptr(Wq), _dt(Wq), N, K, _ptr(out), _ptr(s), _ptr(ws),
                               ws.numel(), _stream(d)), "weight_error")
     return (out, s) if sums else out
+
+
+def dequantize_weight_error(fmt, B, codes, scales, W, dtype=torch.float32, out=None, err=None, sums=False,
+                            workspace=None):
+    """dequantize() and weight_error() in one pass: (Wq, err[, sums]) with Wq
+    as dequantize writes it and err (float64 [1]) as weight_error(W, Wq) gives it."""
+    d = _dev(W)
+    N, K = W.shape
+    out = out if out is not None else torch.empty((N, K), dtype=dtype, device=d)
+    err = err if err is not None else torch.empty(1, dtype=torch.float64, device=d)
+    s = torch.empty(2, dtype=torch.float64, device=d) if sums else None
+    need = int(lib().weight_error_workspace_size(N, K))
+    ws = workspace if workspace is not None else torch.empty(max(need, 16), dtype=torch.uint8, device=d)
+    _check(lib().dequantize_weight_error(fmt, B, _ptr(codes), _ptr(scales), N, K, _ptr(out), _dt(out), _ptr(W),
+                                         _dt(W), _ptr(err), _ptr(s), _ptr(ws), ws.numel(), _stream(d)),
+           "dequantize_weight_error")
+    return (out, err, s) if sums else (out, err)
 
 
 def output_error_workspace_size(M, N, K):

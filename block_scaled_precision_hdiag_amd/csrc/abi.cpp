@@ -276,6 +276,28 @@ hd_status weight_error(const void *W, hd_dtype wt, const void *Wq, hd_dtype qt, 
                       "weight_error");
 }
 
+hd_status dequantize_weight_error(hd_format fmt, int32_t B, const uint8_t *codes, const uint8_t *scales, int64_t N,
+                                  int64_t K, void *Wq, hd_dtype out_t, const void *W, hd_dtype wt, double *out,
+                                  double *sums, void *ws, size_t ws_bytes, void *stream)
+{
+    HD_REQUIRE(valid_dtype(out_t) && valid_dtype(wt), "unknown dtype");
+    hd_status s = check_quant_shape(fmt, B, N, K, true);
+    if (s != HD_OK) return s;
+    HD_REQUIRE(K % 8 == 0, "K=%lld must be a multiple of 8", (long long)K);
+    HD_REQUIRE(out != nullptr, "out is NULL");
+    HD_CHECK_PTR(ws, true);
+    HD_REQUIRE(ws_bytes >= hd::weight_error_ws(N, K), "workspace too small");
+    const bool any = N * K > 0;
+    HD_CHECK_PTR(codes, any);
+    HD_CHECK_PTR(Wq, any);
+    HD_CHECK_PTR(W, any);
+    if (any && scales == nullptr) return fail(HD_ERR_INVALID_ARG, "scales is NULL");
+    if (any && is_f16(fmt) && ((uintptr_t)scales & 1u)) return fail(HD_ERR_INVALID_ARG, "scales is not 2-byte aligned");
+    return hip_status(hd::launch_dequant_weight_error(fmt, B, codes, scales, N, K, Wq, out_t, W, wt, out, sums, ws,
+                                                      (hipStream_t)stream),
+                      "dequantize_weight_error");
+}
+
 size_t output_error_workspace_size(int64_t M, int64_t N, int64_t K)
 {
     if (M < 0 || N < 0 || K < 0) return 0;

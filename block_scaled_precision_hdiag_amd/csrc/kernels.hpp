@@ -44,6 +44,10 @@ hipError_t launch_dequant(int fmt, int B, const uint8_t *codes, const uint8_t *s
 size_t weight_error_ws(int64_t N, int64_t K);
 hipError_t launch_weight_error(const void *W, int wdt, const void *Wq, int qdt, int64_t N, int64_t K,
                                double *out, double *sums, void *ws, hipStream_t st);
+// dequantize and weight error in one pass (workspace: weight_error_ws)
+hipError_t launch_dequant_weight_error(int fmt, int B, const uint8_t *codes, const uint8_t *scales, int64_t N,
+                                       int64_t K, void *Wq, int out_t, const void *W, int wdt, double *out,
+                                       double *sums, void *ws, hipStream_t st);
 
 size_t hdiag_ws(int64_t M, int64_t K);
 hipError_t launch_hdiag(const void *X, int xdt, int64_t M, int64_t K, float *h, void *ws, hipStream_t st);

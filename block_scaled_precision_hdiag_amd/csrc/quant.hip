@@ -529,6 +529,110 @@ __global__ __launch_bounds__(256) void ratio_final(const double *__restrict__ pa
     }
 }
 
+// ------------------------------------------- dequantize + weight error ---
+// dequantize() and weight_error() in one pass over the codes and W: each
+// 8-weight chunk is decoded exactly as dequant_kernel decodes it, stored in
+// the output dtype, and its stored values enter the error sums.  The grid,
+// the chunks each thread takes and their order are werr_partial's, so the
+// partial sums, and the ratio ratio_final makes of them, are those of
+// weight_error(W, Wq) on the Wq written here.
+template <int EK, int SK, int OUT_BF16, typename TW>
+__device__ __forceinline__ void dqwe_chunk(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales,
+                                           int B, const float *stab, int64_t e, void *__restrict__ out, const float *w,
+                                           double &num, double &den)
+{
+    uint64_t cw;
+    if (elem_4bit(EK))
+        cw = *reinterpret_cast<const uint32_t *>(codes + e / 2);
+    else
+        cw = *reinterpret_cast<const uint64_t *>(codes + e);
+    auto sval = [&](int c) {
+        return SK == SCALE_INT8 ? stab[c & 127] * (c < 128 ? 1.0f : 0.0f)
+                                : (scale_code_valid(SK, c) ? scale_value(SK, c) : 0.0f);
+    };
+    float o[8];
+    dq_group<EK, 8>(cw, sval(load_scale<SK>(scales, e / B)), nullptr, o);
+    if (B == 4) {  // the chunk's second block at its own scale
+        float o2[8];
+        dq_group<EK, 8>(cw, sval(load_scale<SK>(scales, e / B + 1)), nullptr, o2);
+#pragma unroll
+        for (int j = 4; j < 8; ++j) o[j] = o2[j];
+    }
+    float q[8];
+    if (OUT_BF16) {
+        uint32_t u[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t lo = f32_to_bf16(o[2 * j]), hi = f32_to_bf16(o[2 * j + 1]);
+            u[j] = lo | (hi << 16);
+            q[2 * j] = bf16_to_f32(lo);
+            q[2 * j + 1] = bf16_to_f32(hi);
+        }
+        *reinterpret_cast<uint4 *>(static_cast<bf16_t *>(out) + e) = make_uint4(u[0], u[1], u[2], u[3]);
+    } else {
+        float *op = static_cast<float *>(out) + e;
+        *reinterpret_cast<float4 *>(op) = make_float4(o[0], o[1], o[2], o[3]);
+        *reinterpret_cast<float4 *>(op + 4) = make_float4(o[4], o[5], o[6], o[7]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) q[j] = o[j];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const double d = (double)q[j] - (double)w[j];
+        num += d * d;
+        den += (double)w[j] * (double)w[j];
+    }
+}
+
+template <int EK, int SK, int OUT_BF16, typename TW>
+__global__ __launch_bounds__(256) void dqwe_partial(const uint8_t *__restrict__ codes,
+                                                    const uint8_t *__restrict__ scales, int B,
+                                                    const TW *__restrict__ W, int64_t total, void *__restrict__ out,
+                                                    double *__restrict__ part)
+{
+    __shared__ double sh[4];
+    __shared__ float stab[128];  // the INT8 grid's scale values fl32(val / 127)
+    if (SK == SCALE_INT8) {
+        if (threadIdx.x < 128)
+            stab[threadIdx.x] = scale_code_valid(SK, threadIdx.x) ? scale_value(SK, threadIdx.x) : 0.0f;
+        __syncthreads();
+    }
+    double num = 0.0, den = 0.0;
+    const int64_t stride = (int64_t)gridDim.x * 256 * 8;
+    for (int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8; e0 < total; e0 += 2 * stride) {
+        const int64_t e1 = e0 + stride;
+        const bool two = e1 < total;
+        float w[16];
+        load8_nt<TW>(W + e0, w);  // each weight is read once here
+        if (two) load8_nt<TW>(W + e1, w + 8);
+        dqwe_chunk<EK, SK, OUT_BF16, TW>(codes, scales, B, stab, e0, out, w, num, den);
+        if (two) dqwe_chunk<EK, SK, OUT_BF16, TW>(codes, scales, B, stab, e1, out, w + 8, num, den);
+    }
+    num = block_sum_256(num, sh);
+    den = block_sum_256(den, sh);
+    if (threadIdx.x == 0) {
+        part[2 * blockIdx.x] = num;
+        part[2 * blockIdx.x + 1] = den;
+    }
+}
+
+template <int EK, int SK>
+static void dqwe_f(int B, const uint8_t *codes, const uint8_t *scales, int64_t total, void *out, int out_t,
+                   const void *W, int wdt, int grid, double *part, hipStream_t st)
+{
+    if (wdt == 1) {
+        if (out_t == 1)
+            dqwe_partial<EK, SK, 1, bf16_t><<<grid, 256, 0, st>>>(codes, scales, B, (const bf16_t *)W, total, out, part);
+        else
+            dqwe_partial<EK, SK, 0, bf16_t><<<grid, 256, 0, st>>>(codes, scales, B, (const bf16_t *)W, total, out, part);
+    } else {
+        if (out_t == 1)
+            dqwe_partial<EK, SK, 1, float><<<grid, 256, 0, st>>>(codes, scales, B, (const float *)W, total, out, part);
+        else
+            dqwe_partial<EK, SK, 0, float><<<grid, 256, 0, st>>>(codes, scales, B, (const float *)W, total, out, part);
+    }
+}
+
 size_t weight_error_ws(int64_t, int64_t) { return sizeof(double) * 2 * WE_GRID; }
 
 hipError_t launch_weight_error(const void *W, int wdt, const void *Wq, int qdt, int64_t N, int64_t K,
@@ -546,6 +650,36 @@ hipError_t launch_weight_error(const void *W, int wdt, const void *Wq, int qdt, 
         werr_partial<float, bf16_t><<<grid, 256, 0, st>>>((const float *)W, (const bf16_t *)Wq, total, part);
     else
         werr_partial<float, float><<<grid, 256, 0, st>>>((const float *)W, (const float *)Wq, total, part);
+    ratio_final<<<1, 256, 0, st>>>(part, grid, out, sums);
+    return hipGetLastError();
+}
+
+hipError_t launch_dequant_weight_error(int fmt, int B, const uint8_t *codes, const uint8_t *scales, int64_t N,
+                                       int64_t K, void *Wq, int out_t, const void *W, int wdt, double *out,
+                                       double *sums, void *ws, hipStream_t st)
+{
+    const int64_t total = N * K;
+    int64_t g = (total / 8 + 255) / 256;
+    const int grid = (int)(g < WE_GRID ? (g > 0 ? g : 1) : WE_GRID);  // werr_partial's grid
+    double *part = static_cast<double *>(ws);
+#define HD_DQWE_FMT(F)                                                                                     \
+    case F:                                                                                                \
+        dqwe_f<elem_kind(F), scale_kind(F)>(B, codes, scales, total, Wq, out_t, W, wdt, grid, part, st);  \
+        break;
+    switch (fmt) {
+        HD_DQWE_FMT(HD_INT8_E4M3)
+        HD_DQWE_FMT(HD_NVFP4)
+        HD_DQWE_FMT(HD_MXFP4)
+        HD_DQWE_FMT(HD_MXFP8)
+        HD_DQWE_FMT(HD_FP8_E4M3S)
+        HD_DQWE_FMT(HD_NVFP4_UE4M4)
+        HD_DQWE_FMT(HD_NVFP4_UE5M3)
+        HD_DQWE_FMT(HD_NVINT4)
+        HD_DQWE_FMT(HD_FP4_F16)
+        HD_DQWE_FMT(HD_INT4_F16)
+    default: return hipErrorInvalidValue;
+    }
+#undef HD_DQWE_FMT
     ratio_final<<<1, 256, 0, st>>>(part, grid, out, sums);
     return hipGetLastError();
 }

@@ -258,6 +258,19 @@ size_t weight_error_workspace_size(int64_t N, int64_t K);
 hd_status weight_error(const void *W, hd_dtype wt, const void *Wq, hd_dtype qt, int64_t N, int64_t K,
                        double *out, double *sums, void *ws, size_t ws_bytes, void *stream);
 
+/* dequantize() and weight_error() in one pass ("Is Finer Better?" §2.1 for
+ * the dequantised values; qwantize "Results", metric definitions, for the
+ * ratio): Wq is written exactly as dequantize(fmt, B, codes, scales, N, K,
+ * Wq, out_t) writes it, and *out / sums are exactly what weight_error(W, wt,
+ * Wq, out_t, N, K, ...) gives for that Wq (the same partial sums in the same
+ * order), while the codes and W are read once and Wq is not read back.
+ * B as for dequantize (4 included); K % 8 == 0; W [N, K] float32 or
+ * bfloat16; workspace: ws_bytes >= weight_error_workspace_size(N, K).
+ * N * K = 0 writes nothing to Wq and gives the IEEE quotient 0 / 0. */
+hd_status dequantize_weight_error(hd_format fmt, int32_t B, const uint8_t *codes, const uint8_t *scales,
+                                  int64_t N, int64_t K, void *Wq, hd_dtype out_t, const void *W, hd_dtype wt,
+                                  double *out, double *sums, void *ws, size_t ws_bytes, void *stream);
+
 /* Output error ||X Wq^T - X W^T||_F / ||X W^T||_F (qwantize "Results", metric
  * definitions), written to the device scalar *out (float64).
  * sums (optional, device, 2 doubles): {||X (Wq-W)^T||^2, ||X W^T||^2}.

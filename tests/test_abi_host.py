@@ -161,6 +161,28 @@ def test_block4_only_on_the_naive_path():
     assert L.gptq_workspace_size(4, 8, 64) == 0
 
 
+def test_dequantize_weight_error_validation():
+    """The fused dequantize + weight error checks its arguments on the host."""
+    L = hd.lib()
+    ws = hd.weight_error_workspace_size(4, 32)
+    f = L.dequantize_weight_error
+    cases = [
+        ((hd.INT8_E4M3, 16, A, A, 4, 32, A, 7, A, hd.HD_BF16, A, None, A, ws, None), "dtype"),
+        ((hd.INT8_E4M3, 16, A, A, 4, 32, A, hd.HD_F32, A, hd.HD_BF16, None, None, A, ws, None), "out is NULL"),
+        ((hd.INT8_E4M3, 16, A, A, 4, 32, A, hd.HD_F32, A, hd.HD_BF16, A, None, A, 8, None), "workspace"),
+        ((hd.INT8_E4M3, 16, A, A, 4, 32, A, hd.HD_F32, None, hd.HD_BF16, A, None, A, ws, None), "W is NULL"),
+        ((hd.INT8_E4M3, 16, A, None, 4, 32, A, hd.HD_F32, A, hd.HD_BF16, A, None, A, ws, None), "scales"),
+        ((hd.INT8_E4M3, 12, A, A, 4, 48, A, hd.HD_F32, A, hd.HD_BF16, A, None, A, ws, None), "block size"),
+        ((hd.NVFP4, 4, A, A, 4, 12, A, hd.HD_F32, A, hd.HD_BF16, A, None, A, ws, None), "K % 8"),
+        ((hd.FP4_F16, 128, A, ctypes.c_void_p((1 << 20) + 1), 4, 128, A, hd.HD_F32, A, hd.HD_BF16, A, None, A,
+          ws, None), "2-byte aligned"),
+    ]
+    for args, needle in cases:
+        rc = f(*args)
+        assert rc == hd.HD_ERR_INVALID_ARG, needle
+        assert needle in L.hdiag_last_error().decode(), (needle, L.hdiag_last_error())
+
+
 def test_schedule_settings():
     """hdiag_set_schedule validates the setting and value on the host."""
     L = hd.lib()
