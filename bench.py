@@ -732,8 +732,8 @@ def layer_suite(args, dev, ci):
     pages' full calibration X 244449x9728) or 5 (W 8192x28672, X
     65536x28672): one pass of the hot path over the full X - hdiag, the scale
     choices (config 3: NVFP4 B = 16, 32 x Naive / SSE / H-Optimal; config 5:
-    NVFP4 B = 16 and INT8 B = 128, Naive and H-Optimal), dequantize, weight
-    error, and the output error of every quantisation through G = X^T X
+    NVFP4 B = 16 and INT8 B = 128, Naive and H-Optimal), dequantize with the
+    weight error in one pass, and the output error of every quantisation through G = X^T X
     (output_gram, output_reference_gram, one output_error_gram_batch) and,
     timed separately, through X W^T (output_reference, then one
     output_error_codes per quantisation).  X is streamed to the GPU in row
@@ -796,8 +796,9 @@ def layer_suite(args, dev, ci):
         timed("output_reference_gram", lambda: hd.output_reference_gram(W, gram, workspace=ws_b, out=ysq), rec)
         for q, (f, B, m) in enumerate(quants):
             timed(qstage[q], lambda: hd.quantize_blocks(m, f, B, W, h=h, codes=codes[q], scales=scales[q]), rec)
-            timed("dequantize", lambda: hd.dequantize(f, B, codes[q], scales[q], N, K, out=Wq), rec)
-            timed("weight_error", lambda: hd.weight_error(W, Wq, workspace=ws_w, out=werr[q:q + 1]), rec)
+            timed("dequantize_weight_error",
+                  lambda: hd.dequantize_weight_error(f, B, codes[q], scales[q], W, out=Wq, err=werr[q:q + 1],
+                                                     workspace=ws_w), rec)
         items = [(f, B, codes[q], scales[q]) for q, (f, B, _) in enumerate(quants)]
         timed("output_error_gram_batch",
               lambda: hd.output_error_gram_batch(items, W, gram, ysq, sums=osums, workspace=ws_b, out=oerr), rec)
@@ -850,8 +851,11 @@ def layer_suite(args, dev, ci):
     avg = {k: sum(v) / len(v) for k, v in per.items()}
     nw = N * K
     work = {"hdiag": ("hbm", M * K * 2 + K * 4), "output_gram": ("mfma", 1.0 * M * K * (K + 1)),
-            "output_reference_gram": ("mfma", 1.0 * N * K * K), "dequantize": ("hbm", None),
-            "weight_error": ("hbm", nw * 6), "output_error_gram_batch": ("mfma", nq * 1.0 * N * K * K),
+            "output_reference_gram": ("mfma", 1.0 * N * K * K),
+            # codes (0.5 or 1 B) and scales read, bf16 W read, float32 Wq written; averaged over the quantisations
+            "dequantize_weight_error": ("hbm", sum(nw * ((0.5 if f in hd.FOUR_BIT else 1.0) + 2 + 4) + nw // B
+                                                   for f, B, _ in quants) / nq),
+            "output_error_gram_batch": ("mfma", nq * 1.0 * N * K * K),
             "output_reference": ("mfma", 2.0 * M * N * K), "output_error_codes": ("mfma", 2.0 * M * N * K)}
     stages = {}
     for st, ms in avg.items():
@@ -873,8 +877,6 @@ def layer_suite(args, dev, ci):
                           "gpairs_per_s": round(pairs[st] / t / 1e9, 2),
                           "full_grid_equivalent_tops": round(nw * nc * SEARCH_OPS[mname[m]] / t / 1e12, 3),
                           "achieved": None, "frac": None}
-        elif st == "dequantize":
-            stages[st] = {"avg_ms": round(ms, 4)}
         else:
             bound, units = work[st]
             stages[st] = _roof(bound, units, ms)
@@ -887,7 +889,7 @@ def layer_suite(args, dev, ci):
             "gram_vs_direct_rel": float(abs(o_gram[q] - o_direct[q]) / o_direct[q])}
     print(json.dumps({"suite": "config%d" % ci, "unit": "Gweights/s",
                       "config": {"workload": "%s: W %dx%d bf16, X %dx%d bf16 (seeded synthetic stand-ins); %d "
-                                             "quantisations, hdiag, scale choice, dequantize, weight error and "
+                                             "quantisations, hdiag, scale choice, dequantize with the weight error, and "
                                              "output error per pass" % (cfg["name"], N, K, M, K, nq),
                                  "W": [N, K], "X": [M, K]},
                       "data": "synthetic", "steps": args.steps, "pass_ms_gram_route": round(pass_ms, 3),
