@@ -1004,8 +1004,11 @@ def gemm_suite(args, dev):
     """The MFMA products of the step on their own (X 16384x9728, W 2560x9728
     bf16): output_reference (Y = X W^T stored, fp32), output_error_codes for
     INT8 codes (fp16 operands) and NVFP4 codes (bf16 operands), and torch's
-    matmul of the same bf16 product (the vendor library) for comparison.
-    Median of 9 timed calls after 2 warm-ups, HIP events on torch's stream."""
+    matmul of the same bf16 product (the vendor library) for comparison; then
+    the Gram route's products: output_gram (G = X^T X, M K (K + 1) flop) and
+    output_error_gram_batch over the step's 12 INT8 quantisations (12 N K^2
+    flop, its operand and final kernels included).  Median of 9 timed calls
+    after 2 warm-ups, HIP events on torch's stream."""
     import torch
 
     import block_scaled_precision_hdiag_amd as hd
@@ -1040,9 +1043,26 @@ def gemm_suite(args, dev):
         res[name] = timed(lambda: hd.output_error_codes(fmt, B, X, c, sc, ref, N, K, workspace=ws))
     Wc = W.contiguous()
     res["torch_matmul_bf16"] = timed(lambda: torch.matmul(X, Wc.t()))
-    out = {k: {"ms": round(v, 4), "tflops": round(flops / v / 1e9, 1), "frac": round(flops / v / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4)}
-           for k, v in res.items()}
-    print(json.dumps({"suite": "gemm", "config": {"workload": "X W^T products, X 16384x9728 bf16, W 2560x9728 bf16",
+    fl = {k: flops for k in res}
+    h = hd.hdiag(X)
+    gram = torch.empty(hd.output_gram_size(K), dtype=torch.uint8, device=dev)
+    ws_g = torch.empty(hd.output_gram_workspace_size(M, K), dtype=torch.uint8, device=dev)
+    res["output_gram"] = timed(lambda: hd.output_gram(X, h=h, gram=gram, workspace=ws_g))
+    fl["output_gram"] = 1.0 * M * K * (K + 1)
+    ysq = hd.output_reference_gram(W, gram)
+    items = []
+    for B in (32, 64, 128, 256):
+        for m in (hd.NAIVE, hd.SSE_OPT, hd.H_OPT):
+            c, sc, _ = hd.quantize_blocks(m, hd.INT8_E4M3, B, W, h=h)
+            items.append((hd.INT8_E4M3, B, c, sc))
+    ws_b = torch.empty(hd.output_error_gram_batch_workspace_size(len(items), N, K), dtype=torch.uint8, device=dev)
+    ob = torch.empty(len(items), dtype=torch.float64, device=dev)
+    res["output_error_gram_batch_12"] = timed(lambda: hd.output_error_gram_batch(items, W, gram, ysq, workspace=ws_b,
+                                                                                 out=ob))
+    fl["output_error_gram_batch_12"] = len(items) * 1.0 * N * K * K
+    out = {k: {"ms": round(v, 4), "tflops": round(fl[k] / v / 1e9, 1),
+               "frac": round(fl[k] / v / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4)} for k, v in res.items()}
+    print(json.dumps({"suite": "gemm", "config": {"workload": "X W^T products and the Gram route (X^T X, the batch of 12), X 16384x9728 bf16, W 2560x9728 bf16",
                                                   "M": M, "N": N, "K": K}, "data": "synthetic",
                       "peak_tflops": MFMA_BF16_PEAK_TFLOPS, "results": out}), flush=True)
 
