@@ -200,6 +200,11 @@ def test_config5_large_layer():
     for fmt, B in ((hd.NVFP4, 16), (hd.INT8_E4M3, 128)):
         c, s = check_rows(hd.H_OPT, fmt, B, W, h_o, h, rows)
         Wq = hd.dequantize(fmt, B, c, s, *W.shape)
+        # the fused dequantize and weight error at this size (many chunk pairs per thread)
+        Wq_f, we_f = hd.dequantize_weight_error(fmt, B, c, s, Wd)
+        assert torch.equal(Wq_f.view(torch.int32), Wq.view(torch.int32))
+        assert we_f.item() == hd.weight_error(Wd, Wq).item()
+        del Wq_f
         full = hd.output_error(Xd, Wd, Wq).item()
         assert hd.output_error_gram(fmt, B, c, s, Wd, gram, ysq).item() == pytest.approx(full, rel=1e-4)
         sub = hd.output_error(Xd[:64].contiguous(), Wd, Wq).item()
